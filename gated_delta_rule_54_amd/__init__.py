@@ -1,0 +1,11 @@
+"""MI355X-native gated delta rule: forward and VJP behind the libgdr C ABI.
+
+The kernels are hand-written HIP for gfx950 (csrc/); ``binding`` marshals
+torch tensors to the C entry points declared in include/gdr.h.
+"""
+
+from .binding import (GdrError, gdr_backward, gdr_backward_workspace, gdr_forward,
+                      gdr_forward_workspace, lib)
+
+__all__ = ["GdrError", "gdr_forward", "gdr_backward", "gdr_forward_workspace",
+           "gdr_backward_workspace", "lib"]

@@ -1,0 +1,184 @@
+"""Thin ctypes binding of libgdr (include/gdr.h): argument marshalling only.
+
+Every function here has the name of the C entry point it wraps.  Torch is
+used for device memory (outputs and workspace are allocated as torch
+tensors) and for the current HIP stream; all arithmetic runs in libgdr's
+kernels.  If libgdr.so has not been built, loading fails loudly.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdr.so")
+
+GDR_OK = 0
+GDR_F32, GDR_BF16 = 0, 1
+GDR_ALGO_AUTO, GDR_ALGO_SEQUENTIAL, GDR_ALGO_CHUNKED = 0, 1, 2
+GDR_USE_QK_L2NORM, GDR_CHANNELWISE = 1, 2
+ALGOS = {"auto": GDR_ALGO_AUTO, "sequential": GDR_ALGO_SEQUENTIAL,
+         "chunked": GDR_ALGO_CHUNKED}
+
+# Every symbol include/gdr.h declares.
+SYMBOLS = ("gdr_forward_workspace", "gdr_backward_workspace", "gdr_forward",
+           "gdr_backward", "gdr_status_str", "gdr_last_hip_error",
+           "gdr_abi_version")
+
+
+class GdrProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("Hk", ctypes.c_int32), ("Hv", ctypes.c_int32),
+                ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("flags", ctypes.c_uint32), ("algo", ctypes.c_int32),
+                ("chunk_size", ctypes.c_int32)]
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = lib().gdr_status_str(status).decode()
+        if status == 6:
+            msg += ": " + lib().gdr_last_hip_error().decode()
+        super().__init__(f"{where}: status {status} ({msg})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libgdr.so (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(GdrProblem)
+        vp, fp, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t
+        L.gdr_forward_workspace.argtypes = [P, ctypes.POINTER(sz)]
+        L.gdr_backward_workspace.argtypes = [P, ctypes.POINTER(sz)]
+        L.gdr_forward.argtypes = [P, vp, vp, vp, fp, fp, fp, vp, fp, vp, sz, vp]
+        L.gdr_backward.argtypes = [P, vp, vp, vp, fp, fp, fp, vp, fp,
+                                   vp, vp, vp, fp, fp, fp, vp, sz, vp]
+        for name in ("gdr_forward_workspace", "gdr_backward_workspace",
+                     "gdr_forward", "gdr_backward"):
+            getattr(L, name).restype = ctypes.c_int
+        L.gdr_status_str.argtypes = [ctypes.c_int]
+        L.gdr_status_str.restype = ctypes.c_char_p
+        L.gdr_last_hip_error.restype = ctypes.c_char_p
+        L.gdr_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _dt(t):
+    if t == torch.float32:
+        return GDR_F32
+    if t == torch.bfloat16:
+        return GDR_BF16
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def make_problem(B, T, Hk, Hv, Dk, Dv, io_dtype, out_dtype, use_qk_l2norm=True,
+                 channelwise=False, algo="auto", chunk_size=0):
+    flags = (GDR_USE_QK_L2NORM if use_qk_l2norm else 0) | (GDR_CHANNELWISE if channelwise else 0)
+    return GdrProblem(B, T, Hk, Hv, Dk, Dv, _dt(io_dtype), _dt(out_dtype), flags,
+                      ALGOS[algo], chunk_size)
+
+
+def gdr_forward_workspace(prob):
+    n = ctypes.c_size_t(0)
+    st = lib().gdr_forward_workspace(ctypes.byref(prob), ctypes.byref(n))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_forward_workspace")
+    return n.value
+
+
+def gdr_backward_workspace(prob):
+    n = ctypes.c_size_t(0)
+    st = lib().gdr_backward_workspace(ctypes.byref(prob), ctypes.byref(n))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_backward_workspace")
+    return n.value
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _workspace(nbytes, device):
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def gdr_forward(q, k, v, g, beta, h0=None, *, use_qk_l2norm=True, channelwise=False,
+                algo="auto", chunk_size=0, out_dtype=torch.float32, ht=True,
+                stream=None):
+    """Returns (o, ht).  ``ht`` may be True (allocate), None (not wanted) or a
+    tensor to write the final state into (it may be ``h0`` itself)."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype)
+    for t, n in ((g, "g"), (beta, "beta"), (h0, "h0")):
+        _check(t, n, torch.float32)
+    prob = make_problem(B, T, Hk, Hv, Dk, Dv, q.dtype, out_dtype, use_qk_l2norm,
+                        channelwise, algo, chunk_size)
+    o = torch.empty((B, T, Hv, Dv), dtype=out_dtype, device=q.device)
+    if ht is True:
+        ht = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=q.device)
+    _check(ht, "ht", torch.float32)
+    ws = _workspace(gdr_forward_workspace(prob), q.device)
+    st = lib().gdr_forward(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                           _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _ptr(ws),
+                           0 if ws is None else ws.numel(), _stream(stream))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_forward")
+    return o, ht
+
+
+def gdr_backward(q, k, v, g, beta, h0, dout, dht=None, *, use_qk_l2norm=True,
+                 channelwise=False, algo="auto", chunk_size=0,
+                 out_dtype=torch.float32, want_dh0=True, stream=None):
+    """Returns (dq, dk, dv, dg, dbeta, dh0); dh0 is None if not wanted."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _check(t, n, q.dtype)
+    for t, n in ((g, "g"), (beta, "beta"), (h0, "h0"), (dht, "dht")):
+        _check(t, n, torch.float32)
+    prob = make_problem(B, T, Hk, Hv, Dk, Dv, q.dtype, out_dtype, use_qk_l2norm,
+                        channelwise, algo, chunk_size)
+    dev = q.device
+    dq = torch.empty((B, T, Hk, Dk), dtype=out_dtype, device=dev)
+    dk = torch.empty((B, T, Hk, Dk), dtype=out_dtype, device=dev)
+    dv = torch.empty((B, T, Hv, Dv), dtype=out_dtype, device=dev)
+    dg = torch.empty(g.shape, dtype=torch.float32, device=dev)
+    dbeta = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
+    dh0 = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=dev) if want_dh0 else None
+    ws = _workspace(gdr_backward_workspace(prob), dev)
+    st = lib().gdr_backward(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                            _ptr(beta), _ptr(h0), _ptr(dout), _ptr(dht), _ptr(dq),
+                            _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0),
+                            _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_backward")
+    return dq, dk, dv, dg, dbeta, dh0

@@ -1,0 +1,206 @@
+// C ABI of libgdr (declared in include/gdr.h): argument validation,
+// workspace sizing and carving, algorithm choice, kernel launches.
+// Nothing here allocates, frees or synchronises.
+
+#include <gdr.h>
+
+#include <string.h>
+
+#include <string>
+
+#include "gdr_internal.h"
+
+namespace {
+
+thread_local std::string g_last_hip_error;
+
+using gdr::Shape;
+
+constexpr size_t kWsAlign = 256;
+
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+bool misaligned(const void* p, uintptr_t a = 16) {
+  return p != nullptr && (reinterpret_cast<uintptr_t>(p) % a) != 0;
+}
+
+gdr_status check_problem(const gdr_problem* p) {
+  if (!p) return GDR_ERR_NULL_ARG;
+  if (p->B < 0 || p->T < 0 || p->Hk <= 0 || p->Hv <= 0 || p->Dk <= 0 || p->Dv <= 0)
+    return GDR_ERR_BAD_SHAPE;
+  if (p->Hv % p->Hk != 0) return GDR_ERR_BAD_SHAPE;
+  if (p->Dk != p->Dv || (p->Dk != 16 && p->Dk != 128)) return GDR_ERR_UNSUPPORTED;
+  if ((p->io_dtype != GDR_F32 && p->io_dtype != GDR_BF16) ||
+      (p->out_dtype != GDR_F32 && p->out_dtype != GDR_BF16))
+    return GDR_ERR_UNSUPPORTED;
+  if (p->flags & ~static_cast<uint32_t>(GDR_USE_QK_L2NORM | GDR_CHANNELWISE)) return GDR_ERR_UNSUPPORTED;
+  if (p->algo < GDR_ALGO_AUTO || p->algo > GDR_ALGO_CHUNKED) return GDR_ERR_UNSUPPORTED;
+  if (p->chunk_size != 0 && p->chunk_size != 16 && p->chunk_size != 32 && p->chunk_size != 64)
+    return GDR_ERR_UNSUPPORTED;
+  // grid limits: B is a grid dimension, B*T*Hk rows in the epilogue
+  if (p->B > 65535 || p->Hv > 65535) return GDR_ERR_UNSUPPORTED;
+  if (p->B * p->T * p->Hk > 0x7fffffffLL) return GDR_ERR_UNSUPPORTED;
+  return GDR_OK;
+}
+
+Shape shape_of(const gdr_problem* p) {
+  Shape s;
+  s.B = p->B;
+  s.T = p->T;
+  s.Hk = p->Hk;
+  s.Hv = p->Hv;
+  s.D = p->Dk;
+  s.io_bf16 = p->io_dtype == GDR_BF16;
+  s.out_bf16 = p->out_dtype == GDR_BF16;
+  s.l2norm = (p->flags & GDR_USE_QK_L2NORM) != 0;
+  s.channelwise = (p->flags & GDR_CHANNELWISE) != 0;
+  return s;
+}
+
+// The chunked path is not built yet: CHUNKED is rejected, AUTO is sequential.
+gdr_status resolve_algo(const gdr_problem* p, int* algo) {
+  if (p->algo == GDR_ALGO_CHUNKED) return GDR_ERR_UNSUPPORTED;
+  *algo = GDR_ALGO_SEQUENTIAL;
+  return GDR_OK;
+}
+
+// ---- workspace plans: byte offsets of each carved buffer -----------------
+struct BwdPlan {
+  size_t ckpt, scratch, pdq, pdk, pdb, pdg, total;
+};
+
+BwdPlan plan_seq_bwd(const Shape& s) {
+  BwdPlan w{};
+  const size_t ns = static_cast<size_t>(gdr::seq_bwd_slices(s));
+  const size_t rows = static_cast<size_t>(s.B * s.T * s.Hv);
+  size_t off = 0;
+  w.ckpt = off;    off = align_up(off + gdr::seq_bwd_ckpt_floats(s) * 4);
+  w.scratch = off; off = align_up(off + gdr::seq_bwd_scratch_floats(s) * 4);
+  w.pdq = off;     off = align_up(off + ns * rows * s.D * 4);
+  w.pdk = off;     off = align_up(off + ns * rows * s.D * 4);
+  w.pdb = off;     off = align_up(off + ns * rows * 4);
+  w.pdg = off;     off = align_up(off + ns * rows * (s.channelwise ? s.D : 1) * 4);
+  w.total = off;
+  return w;
+}
+
+gdr_status hip_fail(hipError_t e) {
+  g_last_hip_error = hipGetErrorString(e);
+  return GDR_ERR_HIP;
+}
+
+template <typename T> T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+const char* gdr_status_str(gdr_status s) {
+  switch (s) {
+    case GDR_OK: return "ok";
+    case GDR_ERR_NULL_ARG: return "required pointer argument is NULL";
+    case GDR_ERR_BAD_SHAPE: return "invalid shape (negative size or Hv % Hk != 0)";
+    case GDR_ERR_UNSUPPORTED: return "unsupported problem (dims, dtype, flags, algo or chunk size)";
+    case GDR_ERR_BAD_ALIGNMENT: return "pointer not 16-byte aligned (workspace: 256-byte)";
+    case GDR_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the size query returned";
+    case GDR_ERR_HIP: return "HIP error (see gdr_last_hip_error)";
+  }
+  return "unknown gdr_status";
+}
+
+const char* gdr_last_hip_error(void) { return g_last_hip_error.c_str(); }
+
+gdr_status gdr_forward_workspace(const gdr_problem* p, size_t* bytes) {
+  gdr_status st = check_problem(p);
+  if (st != GDR_OK) return st;
+  if (!bytes) return GDR_ERR_NULL_ARG;
+  int algo;
+  if ((st = resolve_algo(p, &algo)) != GDR_OK) return st;
+  *bytes = 0;
+  return GDR_OK;
+}
+
+gdr_status gdr_backward_workspace(const gdr_problem* p, size_t* bytes) {
+  gdr_status st = check_problem(p);
+  if (st != GDR_OK) return st;
+  if (!bytes) return GDR_ERR_NULL_ARG;
+  int algo;
+  if ((st = resolve_algo(p, &algo)) != GDR_OK) return st;
+  const Shape s = shape_of(p);
+  *bytes = (s.B == 0 || s.T == 0) ? 0 : plan_seq_bwd(s).total;
+  return GDR_OK;
+}
+
+gdr_status gdr_forward(const gdr_problem* p, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const float* h0, void* o, float* ht,
+                       void* ws, size_t ws_bytes, void* hip_stream) {
+  gdr_status st = check_problem(p);
+  if (st != GDR_OK) return st;
+  const Shape s = shape_of(p);
+  const bool empty = s.B == 0 || s.T == 0;
+  if (!empty && (!q || !k || !v || !g || !beta || !o)) return GDR_ERR_NULL_ARG;
+  const void* ptrs[] = {q, k, v, g, beta, h0, o, ht};
+  for (const void* ptr : ptrs)
+    if (misaligned(ptr)) return GDR_ERR_BAD_ALIGNMENT;
+  if (misaligned(ws, kWsAlign)) return GDR_ERR_BAD_ALIGNMENT;
+  int algo;
+  if ((st = resolve_algo(p, &algo)) != GDR_OK) return st;
+  (void)ws;
+  (void)ws_bytes;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (s.B == 0) return GDR_OK;
+  const size_t state_bytes = static_cast<size_t>(s.B * s.Hv) * s.D * s.D * sizeof(float);
+  if (s.T == 0) {
+    if (!ht) return GDR_OK;
+    hipError_t e = h0 ? (h0 == ht ? hipSuccess : hipMemcpyAsync(ht, h0, state_bytes, hipMemcpyDeviceToDevice, stream))
+                      : hipMemsetAsync(ht, 0, state_bytes, stream);
+    return e == hipSuccess ? GDR_OK : hip_fail(e);
+  }
+  gdr::SeqFwdArgs a{q, k, v, g, beta, h0, o, ht};
+  hipError_t e = gdr::launch_seq_fwd(s, a, stream);
+  return e == hipSuccess ? GDR_OK : hip_fail(e);
+}
+
+gdr_status gdr_backward(const gdr_problem* p, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const float* h0, const void* dout,
+                        const float* dht, void* dq, void* dk, void* dv, float* dg, float* dbeta,
+                        float* dh0, void* ws, size_t ws_bytes, void* hip_stream) {
+  gdr_status st = check_problem(p);
+  if (st != GDR_OK) return st;
+  const Shape s = shape_of(p);
+  const bool empty = s.B == 0 || s.T == 0;
+  if (!empty && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
+    return GDR_ERR_NULL_ARG;
+  const void* ptrs[] = {q, k, v, g, beta, h0, dout, dht, dq, dk, dv, dg, dbeta, dh0};
+  for (const void* ptr : ptrs)
+    if (misaligned(ptr)) return GDR_ERR_BAD_ALIGNMENT;
+  if (misaligned(ws, kWsAlign)) return GDR_ERR_BAD_ALIGNMENT;
+  int algo;
+  if ((st = resolve_algo(p, &algo)) != GDR_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (s.B == 0) return GDR_OK;
+  const size_t state_bytes = static_cast<size_t>(s.B * s.Hv) * s.D * s.D * sizeof(float);
+  if (s.T == 0) {
+    if (!dh0) return GDR_OK;
+    hipError_t e = dht ? hipMemcpyAsync(dh0, dht, state_bytes, hipMemcpyDeviceToDevice, stream)
+                       : hipMemsetAsync(dh0, 0, state_bytes, stream);
+    return e == hipSuccess ? GDR_OK : hip_fail(e);
+  }
+  const BwdPlan w = plan_seq_bwd(s);
+  if (!ws) return GDR_ERR_NULL_ARG;
+  if (ws_bytes < w.total) return GDR_ERR_WORKSPACE_TOO_SMALL;
+  gdr::SeqBwdArgs a{q, k, v, dout, g, beta, h0, dht, dv, dh0,
+                    at<float>(ws, w.ckpt), at<float>(ws, w.scratch), at<float>(ws, w.pdq),
+                    at<float>(ws, w.pdk), at<float>(ws, w.pdb), at<float>(ws, w.pdg)};
+  hipError_t e = gdr::launch_seq_bwd(s, a, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  gdr::EpiArgs ea{q, k, a.part_dq, a.part_dk, a.part_db, a.part_dg, gdr::seq_bwd_slices(s), dq, dk, dbeta, dg};
+  e = gdr::launch_bwd_epilogue(s, ea, stream);
+  return e == hipSuccess ? GDR_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Device-side helpers shared by the libgdr kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+constexpr float kL2Eps = 1e-6f;  // q/k L2-norm eps (Megatron-LM page, "Why")
+
+typedef uint16_t bf16_t;  // raw bf16 bits
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// ---- typed scalar / 4-vector loads and stores (T = float or bf16_t) ------
+template <typename T> __device__ __forceinline__ float ld1(const T* p);
+template <> __device__ __forceinline__ float ld1<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ld1<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
+
+template <typename T> __device__ __forceinline__ void ld4(const T* p, float (&x)[4]);
+template <> __device__ __forceinline__ void ld4<float>(const float* p, float (&x)[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+template <> __device__ __forceinline__ void ld4<bf16_t>(const bf16_t* p, float (&x)[4]) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  x[0] = __uint_as_float(v.x << 16); x[1] = __uint_as_float(v.x & 0xffff0000u);
+  x[2] = __uint_as_float(v.y << 16); x[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
+template <typename T> __device__ __forceinline__ void st1(T* p, float x);
+template <> __device__ __forceinline__ void st1<float>(float* p, float x) { *p = x; }
+template <> __device__ __forceinline__ void st1<bf16_t>(bf16_t* p, float x) { *p = f32_to_bf16(x); }
+
+template <typename T> __device__ __forceinline__ void st4(T* p, const float (&x)[4]);
+template <> __device__ __forceinline__ void st4<float>(float* p, const float (&x)[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+template <> __device__ __forceinline__ void st4<bf16_t>(bf16_t* p, const float (&x)[4]) {
+  uint2 v;
+  v.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
+  v.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+  *reinterpret_cast<uint2*>(p) = v;
+}
+
+// Sum over the lanes whose ids differ only in the bits of [LO, HI) masks,
+// i.e. xor-butterfly with masks LO, 2*LO, ..., HI/2.  Every lane ends with
+// the same total; the order of additions is fixed (deterministic).
+template <int LO, int HI>
+__device__ __forceinline__ float xsum(float x) {
+#pragma unroll
+  for (int m = LO; m < HI; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+}  // namespace gdr

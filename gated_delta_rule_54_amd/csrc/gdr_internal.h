@@ -1,0 +1,57 @@
+// Host-side interface between the C ABI (gdr_api.hip) and the kernel
+// translation units.  Shapes here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+struct Shape {
+  int64_t B, T;
+  int Hk, Hv, D;      // Dk == Dv == D
+  bool io_bf16, out_bf16, l2norm, channelwise;
+};
+
+// ---- sequential (token-by-token) path ------------------------------------
+struct SeqFwdArgs {
+  const void *q, *k, *v;
+  const float *g, *beta, *h0;
+  void* o;
+  float* ht;
+};
+hipError_t launch_seq_fwd(const Shape& s, const SeqFwdArgs& a, hipStream_t st);
+
+// Checkpoint every kSeqSeg tokens; per-WG replay scratch of kSeqSeg states.
+constexpr int kSeqSeg = 16;
+int seq_bwd_slices(const Shape& s);            // value slices per head
+size_t seq_bwd_ckpt_floats(const Shape& s);    // checkpoint buffer
+size_t seq_bwd_scratch_floats(const Shape& s); // replay buffer
+
+struct SeqBwdArgs {
+  const void *q, *k, *v, *dout;
+  const float *g, *beta, *h0, *dht;
+  void* dv;
+  float* dh0;
+  float* ckpt;       // seq_bwd_ckpt_floats
+  float* scratch;    // seq_bwd_scratch_floats
+  float* part_dq;    // [NS][B][T][Hv][D] partial dq_hat per value slice
+  float* part_dk;    // [NS][B][T][Hv][D]
+  float* part_db;    // [NS][B][T][Hv]
+  float* part_dg;    // [NS][B][T][Hv] or [NS][B][T][Hv][D]
+};
+hipError_t launch_seq_bwd(const Shape& s, const SeqBwdArgs& a, hipStream_t st);
+
+// ---- backward epilogue (shared by both paths) ------------------------------
+// Sums per-slice / per-v-head partials in a fixed order, applies the L2-norm
+// VJP and writes dq, dk (out dtype); sums dbeta / dg partials when given.
+struct EpiArgs {
+  const void *q, *k;
+  const float *part_dq, *part_dk, *part_db, *part_dg;  // part_db/dg may be null
+  int nslices;
+  void *dq, *dk;
+  float *dbeta, *dg;
+};
+hipError_t launch_bwd_epilogue(const Shape& s, const EpiArgs& a, hipStream_t st);
+
+}  // namespace gdr

@@ -1,0 +1,141 @@
+/*
+ * gdr.h - C ABI of libgdr: the gated delta rule (forward and VJP) on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  The pages this library follows all turn on the gated
+ * delta rule ("Adding VJP for gated delta net", ml-explore/mlx pull request
+ * 4565; "Two-pass optimization for channelwise gated delta rule kernel",
+ * pytorch/executorch pull request 21020; "perf(gated_delta_net): fold q/k
+ * L2-norm into the gated_delta_rule kernel", NVIDIA/Megatron-LM pull request
+ * 5396).  Per batch b and value head h, a state S (Dv x Dk) evolves per
+ * token t as
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,
+ * the published gated delta rule (Yang, Kautz & Hatamizadeh, ICLR 2025).
+ *   - alpha_t = exp(g_t).  g is a scalar per (b, t, h), or, with
+ *     GDR_CHANNELWISE, one value per key channel (the ExecuTorch page's
+ *     channelwise kernel): then the decay diag(alpha_t) is applied to the
+ *     state before the prediction, S_{t-1} diag(alpha_t) (I - beta k k^T).
+ *   - With GDR_USE_QK_L2NORM, q_t and k_t are replaced by
+ *     x * (sum x^2 + 1e-6)^(-1/2) over the key dim inside the kernels (the
+ *     Megatron-LM page, "What"/"Why"); without it they are used as given.
+ *   - GQA: q and k have Hk heads; value head h reads k/q head h / (Hv/Hk).
+ *   - No output scale is applied.
+ *
+ * Memory.  The state is stored as H = S^T with layout [B, Hv, Dk, Dv]
+ * (Dv contiguous), always fp32.  All tensors are dense, row-major and
+ * contiguous:
+ *   q, k          [B, T, Hk, Dk]     io_dtype
+ *   v, dout       [B, T, Hv, Dv]     io_dtype
+ *   g             [B, T, Hv] (scalar gate) or [B, T, Hv, Dk] (channelwise), fp32
+ *   beta          [B, T, Hv]         fp32
+ *   h0, ht, dh0, dht  [B, Hv, Dk, Dv] fp32
+ *   o, dv         [B, T, Hv, Dv]     out_dtype
+ *   dq, dk        [B, T, Hk, Dk]     out_dtype
+ *   dg            same shape as g, fp32;  dbeta [B, T, Hv] fp32
+ *
+ * Ownership and threading.  Every tensor pointer, including the workspace,
+ * is a DEVICE pointer owned by the caller.  The library never allocates,
+ * frees or synchronises: calls validate, then enqueue kernels on
+ * `hip_stream` (a hipStream_t; NULL = the default stream) and return.  Calls
+ * on different streams may run concurrently if their buffers are disjoint.
+ *
+ * Errors.  All arguments are checked before anything is launched; on any
+ * error nothing is written and a status other than GDR_OK is returned.  A
+ * failed kernel launch returns GDR_ERR_HIP and the HIP error text is kept in
+ * a thread-local string read by gdr_last_hip_error().  No exception or abort
+ * crosses this boundary.  NaN/Inf inputs propagate and never trap.
+ *
+ * Supported sizes.  Dk == Dv, with Dk in {16, 128}; Hv % Hk == 0; T >= 0
+ * (T == 0: forward copies h0, or zeros, into ht; backward copies dht, or
+ * zeros, into dh0).  Every pointer must be 16-byte aligned, the workspace
+ * 256-byte aligned.  Results are bitwise reproducible from run to run
+ * (fixed reduction orders, no floating-point atomics).
+ */
+#ifndef GDR_H_
+#define GDR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR_ABI_VERSION 1
+
+typedef enum gdr_status {
+  GDR_OK = 0,
+  GDR_ERR_NULL_ARG = 1,            /* a required pointer is NULL            */
+  GDR_ERR_BAD_SHAPE = 2,           /* negative/zero sizes, Hv % Hk != 0     */
+  GDR_ERR_UNSUPPORTED = 3,         /* a valid problem this build cannot run */
+  GDR_ERR_BAD_ALIGNMENT = 4,       /* pointer not 16 B (workspace 256 B)    */
+  GDR_ERR_WORKSPACE_TOO_SMALL = 5, /* ws_bytes below the *_workspace size   */
+  GDR_ERR_HIP = 6                  /* a HIP launch or copy failed           */
+} gdr_status;
+
+typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+
+/* How the time axis is processed.  Both are HIP kernels.
+ *   SEQUENTIAL: one token after another, fp32 state on chip (the decode
+ *     kernel; the MLX page's "sequential" VJP).  Every shape is supported.
+ *   CHUNKED: tokens grouped in chunks of chunk_size; the work inside a chunk
+ *     runs as dense matrix-core products (the MLX page's "chunked" VJP).
+ *     Scalar gate only; bf16 io uses fp16 matrix-core operands with fp32
+ *     accumulation (Dk = 128), fp32 io uses fp32 matrix-core operands.
+ *   AUTO: CHUNKED when supported and T > 64, else SEQUENTIAL. */
+typedef enum gdr_algo {
+  GDR_ALGO_AUTO = 0,
+  GDR_ALGO_SEQUENTIAL = 1,
+  GDR_ALGO_CHUNKED = 2
+} gdr_algo;
+
+enum { GDR_USE_QK_L2NORM = 1u, GDR_CHANNELWISE = 2u };
+
+typedef struct gdr_problem {
+  int64_t B, T;       /* batch, tokens                                      */
+  int32_t Hk, Hv;     /* k/q heads, v heads (Hv % Hk == 0)                  */
+  int32_t Dk, Dv;     /* key and value head dims                            */
+  int32_t io_dtype;   /* gdr_dtype of q, k, v, dout                         */
+  int32_t out_dtype;  /* gdr_dtype of o, dq, dk, dv                         */
+  uint32_t flags;     /* GDR_USE_QK_L2NORM | GDR_CHANNELWISE                */
+  int32_t algo;       /* gdr_algo                                           */
+  int32_t chunk_size; /* CHUNKED only: 16, 32 or 64; 0 means 64             */
+} gdr_problem;
+
+/* Workspace bytes the call needs for problem *p (0 is possible).  Returns
+ * the same validation status gdr_forward/gdr_backward would for the shape
+ * part of the problem; *bytes is written only on GDR_OK. */
+gdr_status gdr_forward_workspace(const gdr_problem* p, size_t* bytes);
+gdr_status gdr_backward_workspace(const gdr_problem* p, size_t* bytes);
+
+/* Forward pass.  h0 may be NULL (zero initial state).  ht may be NULL (final
+ * state not wanted) and may alias h0 exactly (in-place decode: each kernel
+ * reads its whole part of the state before writing it).  o must not alias
+ * any input.  ws may be NULL when the workspace size is 0. */
+gdr_status gdr_forward(const gdr_problem* p, const void* q, const void* k,
+                       const void* v, const float* g, const float* beta,
+                       const float* h0, void* o, float* ht, void* ws,
+                       size_t ws_bytes, void* hip_stream);
+
+/* VJP of gdr_forward for the loss <dout, o> + <dht, ht>.  The backward is
+ * stateless: it takes the forward's raw inputs (q, k unnormalised when the
+ * flag is set) and recomputes what it needs; nothing from a forward call is
+ * kept.  h0 and dht may be NULL (zeros); dh0 may be NULL (not wanted).
+ * dq, dk, dv, dg, dbeta are required and must not alias inputs. */
+gdr_status gdr_backward(const gdr_problem* p, const void* q, const void* k,
+                        const void* v, const float* g, const float* beta,
+                        const float* h0, const void* dout, const float* dht,
+                        void* dq, void* dk, void* dv, float* dg, float* dbeta,
+                        float* dh0, void* ws, size_t ws_bytes,
+                        void* hip_stream);
+
+const char* gdr_status_str(gdr_status s); /* static string, never NULL      */
+const char* gdr_last_hip_error(void);     /* this thread's last HIP error   */
+int gdr_abi_version(void);                /* GDR_ABI_VERSION                */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H_ */

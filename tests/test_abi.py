@@ -1,0 +1,123 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol in
+include/gdr.h, and rejects bad arguments before touching the GPU (every call
+below fails validation, so no HIP call is made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_54_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "gdr.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return set(re.findall(r"\b(gdr_[a-z0-9_]+)\s*\(", txt))
+
+
+def test_every_declared_symbol_is_exported():
+    declared = header_functions()
+    assert declared == set(B.SYMBOLS)
+    lib = B.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    lib = B.lib()
+    assert lib.gdr_abi_version() == 1
+    for s in range(7):
+        assert len(lib.gdr_status_str(s)) > 0
+    assert lib.gdr_status_str(99) == b"unknown gdr_status"
+    assert lib.gdr_last_hip_error() == b""
+
+
+def prob(**kw):
+    base = dict(B=2, T=8, Hk=2, Hv=4, Dk=16, Dv=16, io_dtype=0, out_dtype=0, flags=1,
+                algo=0, chunk_size=0)
+    base.update(kw)
+    return B.GdrProblem(**base)
+
+
+def fwd_ws(p):
+    n = ctypes.c_size_t(12345)
+    return B.lib().gdr_forward_workspace(ctypes.byref(p), ctypes.byref(n)), n.value
+
+
+def bwd_ws(p):
+    n = ctypes.c_size_t(12345)
+    return B.lib().gdr_backward_workspace(ctypes.byref(p), ctypes.byref(n)), n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hv=3), 2), (dict(T=-1), 2), (dict(B=-2), 2), (dict(Hk=0), 2), (dict(Dk=0), 2),
+    (dict(Dk=64, Dv=64), 3), (dict(Dk=16, Dv=128), 3), (dict(io_dtype=2), 3),
+    (dict(out_dtype=-1), 3), (dict(flags=4), 3), (dict(algo=3), 3), (dict(chunk_size=48), 3),
+])
+def test_workspace_query_rejects_bad_problems(kw, status):
+    assert fwd_ws(prob(**kw))[0] == status
+    assert bwd_ws(prob(**kw))[0] == status
+
+
+def test_workspace_query_null_args():
+    assert B.lib().gdr_forward_workspace(None, None) == 1
+    p = prob()
+    assert B.lib().gdr_backward_workspace(ctypes.byref(p), None) == 1
+
+
+def test_workspace_sizes_scale_with_problem():
+    st, n0 = bwd_ws(prob(T=0))
+    assert st == 0 and n0 == 0
+    st, n1 = bwd_ws(prob(T=64, algo=1))
+    st2, n2 = bwd_ws(prob(T=128, algo=1))
+    assert st == 0 and st2 == 0 and 0 < n1 < n2 and n1 % 256 == 0
+
+
+FAKE = 0x10000  # an aligned address that is never dereferenced
+
+
+def call_fwd(p, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, o=FAKE, ht=None,
+             ws=None, nws=0):
+    return B.lib().gdr_forward(ctypes.byref(p), q, k, v, g, beta, h0, o, ht, ws, nws, None)
+
+
+def call_bwd(p, ws=None, nws=0, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, dout=FAKE, dht=None,
+                dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, dbeta=FAKE, dh0=None)
+    args.update(over)
+    return B.lib().gdr_backward(ctypes.byref(p), *args.values(), ws, nws, None)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "o"])
+def test_forward_null_inputs(name):
+    assert call_fwd(prob(), **{name: None}) == 1
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "dout", "dq", "dk", "dv",
+                                  "dg", "dbeta"])
+def test_backward_null_inputs(name):
+    assert call_bwd(prob(), **{name: None}) == 1
+
+
+@pytest.mark.parametrize("name", ["q", "v", "h0", "o", "ht"])
+def test_forward_misaligned(name):
+    assert call_fwd(prob(), **{name: FAKE + 8}) == 4
+
+
+def test_backward_misaligned_and_workspace():
+    assert call_bwd(prob(), dq=FAKE + 4) == 4
+    assert call_bwd(prob(), ws=FAKE + 16, nws=1 << 30) == 4      # workspace needs 256 B
+    st, need = bwd_ws(prob())
+    assert st == 0 and need > 0
+    assert call_bwd(prob()) == 1                                   # missing workspace
+    assert call_bwd(prob(), ws=FAKE, nws=need - 1) == 5            # too small
+
+
+def test_bad_problem_beats_everything():
+    assert call_fwd(prob(Hv=3), q=None) == 2
+    assert call_bwd(prob(Dk=32, Dv=32), dq=None) == 3
+    assert B.lib().gdr_forward(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, 0, None) == 1
