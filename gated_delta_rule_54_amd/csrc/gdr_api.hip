@@ -57,10 +57,22 @@ Shape shape_of(const gdr_problem* p) {
   return s;
 }
 
-// The chunked path is not built yet: CHUNKED is rejected, AUTO is sequential.
-gdr_status resolve_algo(const gdr_problem* p, int* algo) {
-  if (p->algo == GDR_ALGO_CHUNKED) return GDR_ERR_UNSUPPORTED;
-  *algo = GDR_ALGO_SEQUENTIAL;
+// Chunk size actually used (0 means 64).
+int chunk_of(const gdr_problem* p) { return p->chunk_size ? p->chunk_size : 64; }
+
+constexpr bool kChunkedBackward = true;
+
+// SEQUENTIAL or CHUNKED for this call; CHUNKED needs a scalar gate.
+gdr_status resolve_algo(const gdr_problem* p, bool backward, int* algo) {
+  const bool chunk_ok = !(p->flags & GDR_CHANNELWISE) && (!backward || kChunkedBackward);
+  if (p->algo == GDR_ALGO_CHUNKED) {
+    if (!chunk_ok) return GDR_ERR_UNSUPPORTED;
+    *algo = GDR_ALGO_CHUNKED;
+  } else if (p->algo == GDR_ALGO_AUTO) {
+    *algo = (chunk_ok && p->T > 64) ? GDR_ALGO_CHUNKED : GDR_ALGO_SEQUENTIAL;
+  } else {
+    *algo = GDR_ALGO_SEQUENTIAL;
+  }
   return GDR_OK;
 }
 
@@ -80,6 +92,23 @@ BwdPlan plan_seq_bwd(const Shape& s) {
   w.pdk = off;     off = align_up(off + ns * rows * s.D * 4);
   w.pdb = off;     off = align_up(off + ns * rows * 4);
   w.pdg = off;     off = align_up(off + ns * rows * (s.channelwise ? s.D : 1) * 4);
+  w.total = off;
+  return w;
+}
+
+struct ChunkBwdPlan {
+  size_t tmat, hst, dhst, pdq, pdk, total;
+};
+
+ChunkBwdPlan plan_chunk_bwd(const Shape& s, int C) {
+  ChunkBwdPlan w{};
+  const size_t rows = static_cast<size_t>(s.B * s.T * s.Hv);
+  size_t off = 0;
+  w.tmat = off; off = align_up(off + gdr::chunk_tmat_bytes(s, C));
+  w.hst = off;  off = align_up(off + gdr::chunk_state_bytes(s, C));
+  w.dhst = off; off = align_up(off + gdr::chunk_state_bytes(s, C));
+  w.pdq = off;  off = align_up(off + rows * s.D * 4);
+  w.pdk = off;  off = align_up(off + rows * s.D * 4);
   w.total = off;
   return w;
 }
@@ -119,8 +148,9 @@ gdr_status gdr_forward_workspace(const gdr_problem* p, size_t* bytes) {
   if (st != GDR_OK) return st;
   if (!bytes) return GDR_ERR_NULL_ARG;
   int algo;
-  if ((st = resolve_algo(p, &algo)) != GDR_OK) return st;
-  *bytes = 0;
+  if ((st = resolve_algo(p, false, &algo)) != GDR_OK) return st;
+  const Shape s = shape_of(p);
+  *bytes = (algo == GDR_ALGO_CHUNKED && s.B > 0 && s.T > 0) ? align_up(gdr::chunk_tmat_bytes(s, chunk_of(p))) : 0;
   return GDR_OK;
 }
 
@@ -129,9 +159,10 @@ gdr_status gdr_backward_workspace(const gdr_problem* p, size_t* bytes) {
   if (st != GDR_OK) return st;
   if (!bytes) return GDR_ERR_NULL_ARG;
   int algo;
-  if ((st = resolve_algo(p, &algo)) != GDR_OK) return st;
+  if ((st = resolve_algo(p, true, &algo)) != GDR_OK) return st;
   const Shape s = shape_of(p);
-  *bytes = (s.B == 0 || s.T == 0) ? 0 : plan_seq_bwd(s).total;
+  *bytes = (s.B == 0 || s.T == 0) ? 0
+           : algo == GDR_ALGO_CHUNKED ? plan_chunk_bwd(s, chunk_of(p)).total : plan_seq_bwd(s).total;
   return GDR_OK;
 }
 
@@ -148,9 +179,7 @@ gdr_status gdr_forward(const gdr_problem* p, const void* q, const void* k, const
     if (misaligned(ptr)) return GDR_ERR_BAD_ALIGNMENT;
   if (misaligned(ws, kWsAlign)) return GDR_ERR_BAD_ALIGNMENT;
   int algo;
-  if ((st = resolve_algo(p, &algo)) != GDR_OK) return st;
-  (void)ws;
-  (void)ws_bytes;
+  if ((st = resolve_algo(p, false, &algo)) != GDR_OK) return st;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   if (s.B == 0) return GDR_OK;
   const size_t state_bytes = static_cast<size_t>(s.B * s.Hv) * s.D * s.D * sizeof(float);
@@ -158,6 +187,14 @@ gdr_status gdr_forward(const gdr_problem* p, const void* q, const void* k, const
     if (!ht) return GDR_OK;
     hipError_t e = h0 ? (h0 == ht ? hipSuccess : hipMemcpyAsync(ht, h0, state_bytes, hipMemcpyDeviceToDevice, stream))
                       : hipMemsetAsync(ht, 0, state_bytes, stream);
+    return e == hipSuccess ? GDR_OK : hip_fail(e);
+  }
+  if (algo == GDR_ALGO_CHUNKED) {
+    const size_t need = align_up(gdr::chunk_tmat_bytes(s, chunk_of(p)));
+    if (!ws) return GDR_ERR_NULL_ARG;
+    if (ws_bytes < need) return GDR_ERR_WORKSPACE_TOO_SMALL;
+    gdr::ChunkFwdArgs a{q, k, v, g, beta, h0, o, ht, ws};
+    hipError_t e = gdr::launch_chunk_fwd(s, chunk_of(p), a, stream);
     return e == hipSuccess ? GDR_OK : hip_fail(e);
   }
   gdr::SeqFwdArgs a{q, k, v, g, beta, h0, o, ht};
@@ -180,7 +217,7 @@ gdr_status gdr_backward(const gdr_problem* p, const void* q, const void* k, cons
     if (misaligned(ptr)) return GDR_ERR_BAD_ALIGNMENT;
   if (misaligned(ws, kWsAlign)) return GDR_ERR_BAD_ALIGNMENT;
   int algo;
-  if ((st = resolve_algo(p, &algo)) != GDR_OK) return st;
+  if ((st = resolve_algo(p, true, &algo)) != GDR_OK) return st;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   if (s.B == 0) return GDR_OK;
   const size_t state_bytes = static_cast<size_t>(s.B * s.Hv) * s.D * s.D * sizeof(float);
@@ -188,6 +225,19 @@ gdr_status gdr_backward(const gdr_problem* p, const void* q, const void* k, cons
     if (!dh0) return GDR_OK;
     hipError_t e = dht ? hipMemcpyAsync(dh0, dht, state_bytes, hipMemcpyDeviceToDevice, stream)
                        : hipMemsetAsync(dh0, 0, state_bytes, stream);
+    return e == hipSuccess ? GDR_OK : hip_fail(e);
+  }
+  if (algo == GDR_ALGO_CHUNKED) {
+    const int C = chunk_of(p);
+    const ChunkBwdPlan w = plan_chunk_bwd(s, C);
+    if (!ws) return GDR_ERR_NULL_ARG;
+    if (ws_bytes < w.total) return GDR_ERR_WORKSPACE_TOO_SMALL;
+    gdr::ChunkBwdArgs a{q, k, v, dout, g, beta, h0, dht, dv, dh0, at<void>(ws, w.tmat), at<void>(ws, w.hst),
+                        at<void>(ws, w.dhst), at<float>(ws, w.pdq), at<float>(ws, w.pdk), dg, dbeta};
+    hipError_t e = gdr::launch_chunk_bwd(s, C, a, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    gdr::EpiArgs ea{q, k, a.pdq, a.pdk, nullptr, nullptr, 1, dq, dk, nullptr, nullptr};
+    e = gdr::launch_bwd_epilogue(s, ea, stream);
     return e == hipSuccess ? GDR_OK : hip_fail(e);
   }
   const BwdPlan w = plan_seq_bwd(s);

@@ -1,0 +1,91 @@
+"""GPU parity of the chunked (matrix-core) kernels against the fp64 oracle,
+through the C ABI.  Tolerances: 1e-4 for fp32 io, 2e-3 for bf16 io (max
+|x - ref| / max |ref| per tensor, fp32 outputs)."""
+
+import numpy as np
+import pytest
+
+from gated_delta_rule_54_amd.synth import make_inputs
+from tests.test_gpu_sequential import check_fwd
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+def test_tiny_oracle_case_chunked_forward(C):
+    """B=1, T=64, Hk=Hv=2, D=16, fp32, zero h0: one chunk at C=64, several
+    at C=16/32 (fp32 matrix-core operands)."""
+    x = make_inputs(0, 1, 64, 2, 2, 16, 16, io_dtype="f32")
+    check_fwd(x, "f32", h0=False, algo=("chunked", C))
+
+
+@pytest.mark.parametrize("T,C", [(1, 16), (17, 16), (100, 64), (100, 32), (129, 64)])
+@pytest.mark.parametrize("l2", [True, False])
+def test_fp32_d16_ragged(T, C, l2):
+    x = make_inputs(200 + T, 2, T, 1, 4, 16, 16, io_dtype="f32", h0_std=0.5)
+    check_fwd(x, "f32", l2=l2, algo=("chunked", C))
+
+
+@pytest.mark.parametrize("T,C", [(1, 64), (50, 64), (64, 64), (200, 64), (200, 32), (77, 16)])
+def test_bf16_d128_chunked_forward(T, C):
+    """bf16 io, Dk=Dv=128: fp16 matrix-core operands for C >= 32, fp32 for C=16."""
+    x = make_inputs(300 + T + C, 2, T, 2, 4, 128, 128, io_dtype="bf16", h0_std=0.02)
+    check_fwd(x, "bf16", algo=("chunked", C))
+
+
+def test_fp32_d128_chunked_forward():
+    x = make_inputs(77, 1, 150, 2, 4, 128, 128, io_dtype="f32", h0_std=0.02)
+    check_fwd(x, "f32", algo=("chunked", 64))
+
+
+def test_prefill_b4_t4096():
+    """Chunked prefill forward: B=4, T=4096, Hk=16, Hv=32, D=128, bf16,
+    zero h0, C=64.  The GPU runs the whole problem; the oracle checks three
+    sampled (b, k-head) groups (both v-heads each)."""
+    x = make_inputs(2, 4, 4096, 16, 32, 128, 128, io_dtype="bf16", with_do=False)
+    check_fwd(x, "bf16", h0=False, heads=[(0, 0), (2, 7), (3, 15)], algo=("chunked", 64))
+
+
+# ------------------------------------------------------------------ VJP
+
+from tests.test_gpu_sequential import SWEEP, check_bwd  # noqa: E402
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+def test_tiny_oracle_case_chunked_vjp(C):
+    """B=1, T=64, Hk=Hv=2, D=16, fp32, do ~ N(0,1), zero h0."""
+    x = make_inputs(0, 1, 64, 2, 2, 16, 16, io_dtype="f32")
+    check_bwd(x, "f32", h0=False, algo=("chunked", C))
+
+
+@pytest.mark.parametrize("T,C", [(1, 16), (17, 16), (100, 64), (100, 32), (129, 64)])
+@pytest.mark.parametrize("l2", [True, False])
+def test_fp32_d16_ragged_vjp(T, C, l2):
+    """Ragged T, GQA 1:4, nonzero h0 and dht, flag on/off."""
+    x = make_inputs(500 + T, 2, T, 1, 4, 16, 16, io_dtype="f32", h0_std=0.5)
+    dht = np.random.default_rng(T).standard_normal((2, 4, 16, 16)).astype(np.float32)
+    check_bwd(x, "f32", l2=l2, dht=dht, algo=("chunked", C))
+
+
+@pytest.mark.parametrize("T,C", [(1, 64), (50, 64), (64, 64), (200, 64), (200, 32), (77, 16)])
+def test_bf16_d128_chunked_vjp(T, C):
+    x = make_inputs(600 + T + C, 2, T, 2, 4, 128, 128, io_dtype="bf16", h0_std=0.02)
+    dht = (0.1 * np.random.default_rng(T).standard_normal((2, 4, 128, 128))).astype(np.float32)
+    check_bwd(x, "bf16", dht=dht, algo=("chunked", C))
+
+
+def test_fp32_d128_chunked_vjp():
+    x = make_inputs(78, 1, 150, 2, 4, 128, 128, io_dtype="f32", h0_std=0.02)
+    check_bwd(x, "f32", algo=("chunked", 64))
+
+
+@pytest.mark.parametrize("B,T", SWEEP)
+def test_chunked_vjp_sweep(B, T):
+    """The backward sweep of the MLX page's benchmark (B in {1,4,8}, T in
+    {8,64,512,4096}, Hk=16, Hv=32, D=128, bf16, C=64), h0 ~ N(0, 0.02);
+    oracle on every head for short T, on sampled groups for long T."""
+    Hk, Hv, D = 16, 32, 128
+    x = make_inputs(3000 + 10 * B + [8, 64, 512, 4096].index(T), B, T, Hk, Hv, D, D,
+                    io_dtype="bf16", h0_std=0.02)
+    heads = None if T <= 64 else ([(B - 1, Hk - 1)] if T == 4096 else [(0, 0), (B - 1, 5)])
+    check_bwd(x, "bf16", heads=heads, algo=("chunked", 64))

@@ -32,10 +32,17 @@ def group_slice(x, b, kh, grp):
     return out
 
 
+def algo_kw(algo):
+    """'sequential' | 'chunked' | ('chunked', C) -> binding keyword arguments."""
+    if isinstance(algo, tuple):
+        return dict(algo=algo[0], chunk_size=algo[1])
+    return dict(algo=algo)
+
+
 def check_fwd(x, io, l2=True, cw=False, h0=True, heads=None, algo="sequential"):
     t = to_dev(x, io)
     o, ht = gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"] if h0 else None,
-                            use_qk_l2norm=l2, channelwise=cw, algo=algo)
+                            use_qk_l2norm=l2, channelwise=cw, **algo_kw(algo))
     torch.cuda.synchronize()
     o, ht = host(o), host(ht)
     grp = x["v"].shape[2] // x["q"].shape[2]
@@ -47,6 +54,7 @@ def check_fwd(x, io, l2=True, cw=False, h0=True, heads=None, algo="sequential"):
             go, ght = o, ht
         else:
             go, ght = o[b:b + 1, :, kh * grp:(kh + 1) * grp], ht[b:b + 1, kh * grp:(kh + 1) * grp]
+        print(f"  fwd {algo} b={b} kh={kh}: o {relerr(go, ro):.2e} ht {relerr(ght, rht):.2e}")
         assert relerr(go, ro) < TOL[io], ("o", relerr(go, ro))
         assert relerr(ght, rht) < TOL[io], ("ht", relerr(ght, rht))
 
@@ -55,7 +63,7 @@ def check_bwd(x, io, l2=True, cw=False, h0=True, dht=None, heads=None, algo="seq
     t = to_dev(x, io)
     dht_t = None if dht is None else dev(dht)
     grads = gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"] if h0 else None,
-                             t["do"], dht_t, use_qk_l2norm=l2, channelwise=cw, algo=algo)
+                             t["do"], dht_t, use_qk_l2norm=l2, channelwise=cw, **algo_kw(algo))
     torch.cuda.synchronize()
     grads = [host(a) for a in grads]
     grp = x["v"].shape[2] // x["q"].shape[2]
@@ -69,6 +77,7 @@ def check_bwd(x, io, l2=True, cw=False, h0=True, dht=None, heads=None, algo="seq
                 vs = slice(kh * grp, (kh + 1) * grp)
                 a = (a[b:b + 1, :, kh:kh + 1] if name in ("dq", "dk")
                      else a[b:b + 1, vs] if name == "dh0" else a[b:b + 1, :, vs])
+            print(f"  bwd {algo} {name}: {relerr(a, r):.2e}")
             assert relerr(a, r) < TOL[io], (name, relerr(a, r))
 
 
