@@ -1,0 +1,289 @@
+"""Benchmark of the gated delta rule hot path on one MI355X.
+
+One step = chunked forward + VJP (gdr_forward then gdr_backward, C = 64) over
+a batch of B=4 sequences of T=4096 tokens, Hk=16, Hv=32, Dk=Dv=128, bf16
+inputs, the backward sweep shape of the page "Adding VJP for gated delta
+net" (ml-explore/mlx pull request 4565, "Performance").  Inputs are seeded
+synthetic data resident in HBM before timing starts.  The decode path
+(B=8, 256 single-token steps over 32 rotated state buffers) is measured in
+the same run and reported under "decode".
+
+Prints one JSON line.  `value` is fwd+bwd tokens/s; `roofline` is for the
+kernel that takes the most time in the timed region (per-kernel durations
+come from HIP events the library records around each launch);
+`cpu_baseline` is the fp64 oracle timed on a bounded sample on the host.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFS = 2500.0   # MI355X dense fp16/bf16 matrix cores, TFLOP/s
+
+B, T, HK, HV, D, C = 4, 4096, 16, 32, 128, 64
+DEC_B, DEC_STEPS, DEC_BUFFERS = 8, 256, 32
+
+
+def kernel_flops_per_token_head(name, d=D, c=C):
+    """Algorithmic FLOPs each kernel is responsible for, per (token, v-head):
+    every matrix product counted once at 2mnk, products whose result is used
+    only on one triangle of a C x C block counted at half."""
+    return {
+        "chunk_prep": c * d + c * c / 3,
+        "chunk_fwd": 6 * d * d + 3 * c * d,
+        "chunk_states": 4 * d * d + c * d,
+        "chunk_dh": 6 * d * d + 3 * c * d,
+        "chunk_grad": 10 * d * d + 12 * c * d + 2 * c * c / 3,
+    }.get(name)
+
+
+def canonical_flops_per_token_head(d=D, c=C):
+    """Minimal fwd + bwd count: fwd 6d^2 + 5Cd + C^2/3, bwd (with one
+    recompute of the chunk states) 16d^2 + 14Cd + C^2."""
+    return (6 * d * d + 5 * c * d + c * c / 3) + (16 * d * d + 14 * c * d + c * c)
+
+
+def kernel_bytes_per_token_head(name, d=D, c=C, grp=HV // HK):
+    """Algorithmic HBM bytes per (token, v-head) of each kernel (bf16 io, fp16
+    T and chunk states, fp32 partial gradients); k/q rows are shared by the
+    `grp` v-heads of a k-head."""
+    kq = 2 * d * 2 / grp   # k and q rows, bf16
+    vec = d * 2            # one bf16 row of v / o / do
+    gates = 8              # g and beta, fp32
+    tm = 2 * c             # T (fp16 C x C per chunk)
+    st = 2 * d * d / c     # one fp16 d x d state per chunk
+    return {
+        "chunk_prep": kq / 2 + gates + tm,
+        "chunk_fwd": kq + vec + gates + tm + vec,
+        "chunk_states": kq / 2 + vec + gates + tm + st,
+        "chunk_dh": kq + vec + gates + tm + vec + st,
+        "chunk_grad": kq + 2 * vec + gates + tm + 2 * st + 2 * d * 4 + gates,
+        "bwd_epilogue": 2 * d * 4 + (2 * d * 2 + 2 * d * 2) / grp,
+    }.get(name)
+
+
+def src_digest():
+    """Digest of the kernel sources; a stored counter profile is only used
+    while it matches."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_54_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel):
+    """HBM bytes per launch from the committed counter profile of this kernel,
+    or None when there is none or the sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    ent = rec.get("kernels", {}).get(kernel)
+    if not ent or rec.get("src_digest") != src_digest():
+        return None
+    return ent["bytes_per_launch"]
+
+
+def make_device_inputs(torch, seed, b, t, with_do=True):
+    from gated_delta_rule_54_amd.synth import make_inputs
+    x = make_inputs(seed, b, t, HK, HV, D, D, io_dtype="bf16", with_do=with_do)
+    dev = torch.device("cuda")
+    out = {}
+    for n, a in x.items():
+        if a is None:
+            out[n] = None
+            continue
+        tt = torch.from_numpy(a).to(dev)
+        out[n] = tt.to(torch.bfloat16) if n in ("q", "k", "v", "do") else tt
+    return x, out
+
+
+def bench_chunked(torch, gdr, steps, warmup):
+    _, t = make_device_inputs(torch, 2, B, T)
+    kw = dict(algo="chunked", chunk_size=C, out_dtype=torch.bfloat16)
+
+    def step():
+        gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], None, **kw)
+        gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], None, t["do"], **kw)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    gdr.gdr_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    kernels = gdr.gdr_profile_read()
+    gdr.gdr_profile_enable(False)
+    ms = e0.elapsed_time(e1) / steps
+    return ms, wall, kernels
+
+
+def bench_decode(torch, gdr):
+    """B=8 single-token steps, state updated in place, rotating over
+    DEC_BUFFERS independent states so a step's 16 MiB state is not served
+    from the 256 MB last-level cache."""
+    g = torch.Generator(device="cuda").manual_seed(1)
+    sh = lambda *s: torch.randn(*s, device="cuda", generator=g)
+    q = sh(DEC_STEPS, DEC_B, 1, HK, D).bfloat16()
+    k = sh(DEC_STEPS, DEC_B, 1, HK, D).bfloat16()
+    v = sh(DEC_STEPS, DEC_B, 1, HV, D).bfloat16()
+    gg = -torch.nn.functional.softplus(sh(DEC_STEPS, DEC_B, 1, HV))
+    bb = torch.sigmoid(sh(DEC_STEPS, DEC_B, 1, HV))
+    states = [sh(DEC_B, HV, D, D) * 0.02 for _ in range(DEC_BUFFERS)]
+
+    def run(n, buffers):
+        for i in range(n):
+            s = states[i % buffers]
+            gdr.gdr_forward(q[i % DEC_STEPS], k[i % DEC_STEPS], v[i % DEC_STEPS], gg[i % DEC_STEPS],
+                            bb[i % DEC_STEPS], s, ht=s, algo="sequential", out_dtype=torch.bfloat16)
+
+    out = {}
+    for label, buffers in (("rotated", DEC_BUFFERS), ("single_buffer_cache_warm", 1)):
+        run(32, buffers)
+        torch.cuda.synchronize()
+        gdr.gdr_profile_enable(True)
+        w0 = time.perf_counter()
+        run(DEC_STEPS, buffers)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        kt = gdr.gdr_profile_read()
+        gdr.gdr_profile_enable(False)
+        ms, n = kt["seq_fwd"]
+        us = 1000.0 * ms / n
+        state_bytes = 2 * DEC_B * HV * D * D * 4
+        out[label] = {"kernel_us_per_step": round(us, 3), "wall_us_per_step": round(1e6 * wall / DEC_STEPS, 2),
+                      "state_GBps": round(state_bytes / (us * 1e-6) / 1e9, 1),
+                      "frac_hbm_peak": round(state_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    out["state_bytes_per_step"] = 2 * DEC_B * HV * D * D * 4
+    out["config"] = f"B={DEC_B} Hk={HK} Hv={HV} Dk=Dv={D}, {DEC_STEPS} single-token steps, bf16 io, fp32 state"
+    return out
+
+
+def cpu_baseline(sample_groups=2):
+    """The fp64 oracle (forward + VJP) on `sample_groups` (b, k-head) groups
+    of the full-length workload (each group = the 2 v-heads sharing a
+    k-head), scaled to whole-workload tokens/s."""
+    import numpy as np
+    from gated_delta_rule_54_amd.synth import make_inputs
+    from oracle import gdr_oracle as orc
+    from threadpoolctl import threadpool_limits
+    x = make_inputs(2, 1, T, 1, HV // HK, D, D, io_dtype="bf16")
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for _ in range(sample_groups):
+            orc.forward(x["q"], x["k"], x["v"], x["g"], x["beta"])
+            orc.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], None, x["do"])
+        sec = time.perf_counter() - t0
+    heads = sample_groups * (HV // HK)
+    whole = sec * (B * HV) / heads
+    return {"value": round(B * T / whole, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{sample_groups} (b, k-head) group(s) = {heads} v-heads x T={T} fwd+bwd in fp64 "
+                      f"numpy ({sec:.1f} s, one thread); scaled by {B * HV // heads}x to B={B}, Hv={HV}",
+            "cpu_model": _cpu_model(), "host_threads": os.cpu_count()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU mode).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_54_amd as gdr
+    gdr.lib()  # fail loudly if the library was not built
+
+    ms, wall, kernels = bench_chunked(torch, gdr, args.steps, args.warmup)
+    tokens = B * T
+    th = B * T * HV
+    per_kernel = {}
+    for name, (tot, n) in kernels.items():
+        avg_ms = tot / n
+        ent = {"avg_us": round(1000 * avg_ms, 2), "launches_per_step": n / args.steps,
+               "share_of_step": round(tot / args.steps / ms, 4)}
+        f = kernel_flops_per_token_head(name)
+        by = kernel_bytes_per_token_head(name)
+        if f is not None:
+            ent["TFLOPs"] = round(f * th / (avg_ms * 1e-3) / 1e12, 2)
+        if by is not None:
+            ent["GBps"] = round(by * th / (avg_ms * 1e-3) / 1e9, 1)
+        per_kernel[name] = ent
+    dom = max(kernels, key=lambda n: kernels[n][0])
+    avg_s = kernels[dom][0] / kernels[dom][1] * 1e-3
+    f = kernel_flops_per_token_head(dom)
+    if f is not None:
+        ach = f * th / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_F16_PEAK_TFS, 4)}
+    else:
+        ach = kernel_bytes_per_token_head(dom) * th / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = dom
+    roof["traffic"] = stored_traffic(dom)
+    canon = canonical_flops_per_token_head() * th
+    line = {
+        "metric": "fwd+bwd tokens/s at B=4,T=4096,Hv=32,D=128; decode state GB/s vs HBM peak",
+        "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded numpy PCG64; q,k,v,do ~ N(0,1) in bf16, g=-softplus(N(0,1)), beta=sigmoid(N(0,1)))",
+        "config": {"workload": "chunked gated delta rule forward + VJP", "B": B, "T": T, "Hk": HK, "Hv": HV,
+                   "Dk": D, "Dv": D, "chunk": C, "io": "bf16", "matrix_core_operands": "f16",
+                   "accumulate_and_state": "f32", "use_qk_l2norm": True, "gate": "scalar",
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "path": {"canonical_TFLOPs": round(canon / (ms * 1e-3) / 1e12, 2),
+                 "canonical_frac_mfma": round(canon / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFS, 4),
+                 "wall_ms_per_step": round(1000 * wall / args.steps, 3)},
+        "kernels": per_kernel,
+    }
+    if not args.no_decode:
+        line["decode"] = bench_decode(torch, gdr)
+    line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -5,7 +5,7 @@ torch tensors to the C entry points declared in include/gdr.h.
 """
 
 from .binding import (GdrError, gdr_backward, gdr_backward_workspace, gdr_forward,
-                      gdr_forward_workspace, lib)
+                      gdr_forward_workspace, gdr_profile_enable, gdr_profile_read, lib)
 
 __all__ = ["GdrError", "gdr_forward", "gdr_backward", "gdr_forward_workspace",
-           "gdr_backward_workspace", "lib"]
+           "gdr_backward_workspace", "gdr_profile_enable", "gdr_profile_read", "lib"]

@@ -23,8 +23,8 @@ ALGOS = {"auto": GDR_ALGO_AUTO, "sequential": GDR_ALGO_SEQUENTIAL,
 
 # Every symbol include/gdr.h declares.
 SYMBOLS = ("gdr_forward_workspace", "gdr_backward_workspace", "gdr_forward",
-           "gdr_backward", "gdr_status_str", "gdr_last_hip_error",
-           "gdr_abi_version")
+           "gdr_backward", "gdr_profile_enable", "gdr_profile_read",
+           "gdr_status_str", "gdr_last_hip_error", "gdr_abi_version")
 
 
 class GdrProblem(ctypes.Structure):
@@ -34,6 +34,11 @@ class GdrProblem(ctypes.Structure):
                 ("io_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("flags", ctypes.c_uint32), ("algo", ctypes.c_int32),
                 ("chunk_size", ctypes.c_int32)]
+
+
+class GdrKernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("total_ms", ctypes.c_double),
+                ("launches", ctypes.c_int64)]
 
 
 class GdrError(RuntimeError):
@@ -66,6 +71,11 @@ def lib():
         for name in ("gdr_forward_workspace", "gdr_backward_workspace",
                      "gdr_forward", "gdr_backward"):
             getattr(L, name).restype = ctypes.c_int
+        L.gdr_profile_enable.argtypes = [ctypes.c_int]
+        L.gdr_profile_enable.restype = ctypes.c_int
+        L.gdr_profile_read.argtypes = [ctypes.POINTER(GdrKernelTime), ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_int)]
+        L.gdr_profile_read.restype = ctypes.c_int
         L.gdr_status_str.argtypes = [ctypes.c_int]
         L.gdr_status_str.restype = ctypes.c_char_p
         L.gdr_last_hip_error.restype = ctypes.c_char_p
@@ -103,6 +113,24 @@ def gdr_backward_workspace(prob):
     if st != GDR_OK:
         raise GdrError(st, "gdr_backward_workspace")
     return n.value
+
+
+def gdr_profile_enable(on=True):
+    st = lib().gdr_profile_enable(1 if on else 0)
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_profile_enable")
+
+
+def gdr_profile_read():
+    """{kernel name: (total ms, launches)} of the events recorded since the
+    last read; waits for them to complete."""
+    cap = 32
+    buf = (GdrKernelTime * cap)()
+    n = ctypes.c_int(0)
+    st = lib().gdr_profile_read(buf, cap, ctypes.byref(n))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_profile_read")
+    return {buf[i].name.decode(): (buf[i].total_ms, buf[i].launches) for i in range(min(n.value, cap))}
 
 
 def _ptr(t):

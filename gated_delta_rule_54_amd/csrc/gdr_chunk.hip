@@ -883,6 +883,7 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(CArgs a) {
 // Host side.
 template <typename CF, typename TI>
 hipError_t prep(const CArgs& a, hipStream_t st) {
+  ProfScope ps("chunk_prep", st);
   hipLaunchKernelGGL((chunk_prep_kernel<CF, TI>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(64), 0,
                      st, a);
   return hipGetLastError();
@@ -890,6 +891,7 @@ hipError_t prep(const CArgs& a, hipStream_t st) {
 
 template <typename CF, typename TI, typename TO>
 hipError_t dh(const CArgs& a, hipStream_t st) {
+  ProfScope ps("chunk_dh", st);
   hipLaunchKernelGGL((chunk_dh_kernel<CF, TI, TO>), dim3(CF::DK / CF::BV, a.Hv, static_cast<unsigned>(a.B)),
                      dim3(256), 0, st, a);
   return hipGetLastError();
@@ -897,6 +899,7 @@ hipError_t dh(const CArgs& a, hipStream_t st) {
 
 template <typename CF, typename TI>
 hipError_t grad(const CArgs& a, hipStream_t st) {
+  ProfScope ps("chunk_grad", st);
   hipLaunchKernelGGL((chunk_grad_kernel<CF, TI>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(256), 0,
                      st, a);
   return hipGetLastError();
@@ -904,6 +907,7 @@ hipError_t grad(const CArgs& a, hipStream_t st) {
 
 template <typename CF, typename TI, typename TO, bool WO, bool SH>
 hipError_t fwd(const CArgs& a, hipStream_t st) {
+  ProfScope ps(WO ? "chunk_fwd" : "chunk_states", st);
   hipLaunchKernelGGL((chunk_fwd_kernel<CF, TI, TO, WO, SH>), dim3(CF::DK / CF::BV, a.Hv, static_cast<unsigned>(a.B)),
                      dim3(256), 0, st, a);
   return hipGetLastError();

@@ -7,6 +7,17 @@
 
 namespace gdr {
 
+// Brackets one kernel launch with profiling events when gdr_profile_enable
+// is on for this thread (no-op otherwise).
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t st);
+  ~ProfScope();
+ private:
+  hipStream_t stream_;
+  bool active_;
+};
+
 struct Shape {
   int64_t B, T;
   int Hk, Hv, D;      // Dk == Dv == D

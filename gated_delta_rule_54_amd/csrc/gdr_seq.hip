@@ -430,6 +430,7 @@ template <int D, typename TI, typename TO, bool CW>
 hipError_t fwd_go(const Shape& s, const SeqFwdArgs& a, hipStream_t st) {
   constexpr int BV = fwd_bv<D>();
   dim3 grid(D / BV, s.Hv, static_cast<unsigned>(s.B));
+  ProfScope ps("seq_fwd", st);
   hipLaunchKernelGGL((seq_fwd_kernel<D, BV, TI, TO, CW>), grid, dim3(64), 0, st, dims_of(s), a);
   return hipGetLastError();
 }
@@ -439,6 +440,7 @@ hipError_t bwd_go(const Shape& s, const SeqBwdArgs& a, hipStream_t st) {
   constexpr int BV = bwd_bv<D>();
   const int nck = static_cast<int>((s.T + kSeqSeg - 1) / kSeqSeg);
   dim3 grid(D / BV, s.Hv, static_cast<unsigned>(s.B));
+  ProfScope ps("seq_bwd", st);
   hipLaunchKernelGGL((seq_bwd_kernel<D, BV, TI, TO, CW>), grid, dim3(64), 0, st, dims_of(s), a, nck, D / BV);
   return hipGetLastError();
 }
@@ -446,6 +448,7 @@ hipError_t bwd_go(const Shape& s, const SeqBwdArgs& a, hipStream_t st) {
 template <int D, typename TI, typename TO, bool CW>
 hipError_t epi_go(const Shape& s, const EpiArgs& a, hipStream_t st) {
   const int64_t rows = s.B * s.T * s.Hk;
+  ProfScope ps("bwd_epilogue", st);
   hipLaunchKernelGGL((epilogue_kernel<D, TI, TO, CW>), dim3(static_cast<unsigned>(rows)), dim3(64), 0, st,
                      dims_of(s), a);
   return hipGetLastError();

@@ -130,6 +130,22 @@ gdr_status gdr_backward(const gdr_problem* p, const void* q, const void* k,
                         float* dh0, void* ws, size_t ws_bytes,
                         void* hip_stream);
 
+/* Per-kernel timing for benchmarks (not for use under graph capture).
+ * While enabled, every kernel that gdr_forward / gdr_backward launch from the
+ * calling thread is bracketed by a pair of HIP events recorded on the call's
+ * stream (events are created on first use and recycled).  gdr_profile_read
+ * waits for all recorded events, writes up to `cap` per-kernel entries
+ * (static kernel name, summed milliseconds, launch count) to `out`, stores
+ * the number of kernels seen in *n and clears the record.  Disabling drops
+ * any unread record. */
+typedef struct gdr_kernel_time {
+  const char* name;
+  double total_ms;
+  int64_t launches;
+} gdr_kernel_time;
+gdr_status gdr_profile_enable(int on);
+gdr_status gdr_profile_read(gdr_kernel_time* out, int cap, int* n);
+
 const char* gdr_status_str(gdr_status s); /* static string, never NULL      */
 const char* gdr_last_hip_error(void);     /* this thread's last HIP error   */
 int gdr_abi_version(void);                /* GDR_ABI_VERSION                */
