@@ -880,6 +880,557 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(CArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// fp16-operand chains for bf16 io, Dk = Dv = 128, value slices of 64 columns,
+// C in {32, 64}.  Wave w owns the 16-column strip j0 + 16w .. j0 + 16w + 15
+// of every C x 64 and 128 x 64 tile of its workgroup, so a C x 16 product
+// held in MFMA accumulators can be fed straight back as the operand of the
+// next product that contracts over the chunk rows ("chained" operand): the
+// k index of such a product is relabelled so that lane group g supplies rows
+// {4g..4g+3, 16+4g..16+4g+3} of each 32-row block, exactly the rows its
+// accumulators hold; the LDS-side operand is read with the same relabelling
+// (two 8-byte reads per fragment).  The next chunk's inputs are prefetched
+// into registers while the current chunk computes; all loads are
+// branch-free (rows past the sequence end are clamped, then zeroed).
+namespace f16c {
+
+constexpr int DK = 128, BV = 64, LDK = DK + 8;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ f16x8 ld8(const _Float16* p) { return *reinterpret_cast<const f16x8*>(p); }
+
+// A fragment of A[m][k] (row-major, k contiguous) for the relabelled 32-row
+// block kb: elements 0..3 <- k = 32kb + 4g + 0..3, 4..7 <- 32kb + 16 + 4g + 0..3.
+__device__ __forceinline__ f16x8 perm_frag(const _Float16* A, int ld, int m, int kb) {
+  const int g = lane_id() >> 4;
+  const f16x4 lo = *reinterpret_cast<const f16x4*>(A + m * ld + 32 * kb + 4 * g);
+  const f16x4 hi = *reinterpret_cast<const f16x4*>(A + m * ld + 32 * kb + 16 + 4 * g);
+  return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Chained B fragments of a C x 16 strip x[tr][e] (fp32 accumulators).
+template <int NT>
+__device__ __forceinline__ void chain_frags(f16x8 (&bf)[NT / 2], const f32x4 (&x)[NT]) {
+#pragma unroll
+  for (int kb = 0; kb < NT / 2; ++kb)
+    bf[kb] = f16x8{static_cast<_Float16>(x[2 * kb][0]), static_cast<_Float16>(x[2 * kb][1]),
+                   static_cast<_Float16>(x[2 * kb][2]), static_cast<_Float16>(x[2 * kb][3]),
+                   static_cast<_Float16>(x[2 * kb + 1][0]), static_cast<_Float16>(x[2 * kb + 1][1]),
+                   static_cast<_Float16>(x[2 * kb + 1][2]), static_cast<_Float16>(x[2 * kb + 1][3])};
+}
+
+// acc[t] += A[16t : 16t+16, 0:C] * X for t < NO (X chained as bf).
+template <int NO, int NT>
+__device__ __forceinline__ void mma_chain_rows(f32x4 (&acc)[NO], const _Float16* A, int ld, const f16x8 (&bf)[NT / 2]) {
+  const int m = lane_id() & 15;
+#pragma unroll
+  for (int kb = 0; kb < NT / 2; ++kb) {
+    f16x8 af[NO];
+#pragma unroll
+    for (int t = 0; t < NO; ++t) af[t] = perm_frag(A, ld, 16 * t + m, kb);
+#pragma unroll
+    for (int t = 0; t < NO; ++t) acc[t] = F16Op::mma(af[t], bf[kb], acc[t]);
+  }
+}
+
+// acc[t] += A[16t : 16t+16, 0:K] * B where B^T rows n0..n0+15 are read from
+// Bt (k contiguous); K a multiple of 32.  k-outer so the NO accumulators are
+// independent and the B fragment is shared.
+template <int NO, int K>
+__device__ __forceinline__ void mma_rows(f32x4 (&acc)[NO], const _Float16* A, int lda, const _Float16* Bt, int ldb,
+                                         int n0) {
+  const int r = lane_id() & 15, kl = (lane_id() >> 4) * 8;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const f16x8 bfr = ld8(Bt + (n0 + r) * ldb + k0 + kl);
+    f16x8 af[NO];
+#pragma unroll
+    for (int t = 0; t < NO; ++t) af[t] = ld8(A + (16 * t + r) * lda + k0 + kl);
+#pragma unroll
+    for (int t = 0; t < NO; ++t) acc[t] = F16Op::mma(af[t], bfr, acc[t]);
+  }
+}
+
+// One C x C row block: acc[t] = Q[m0:m0+16] . K[16t : 16t+16]^T over DK.
+template <int NT>
+__device__ __forceinline__ void mma_qk_row(f32x4 (&acc)[NT], const _Float16* Qs, const _Float16* Ks, int m0) {
+  const int r = lane_id() & 15, kl = (lane_id() >> 4) * 8;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = zero4();
+#pragma unroll
+  for (int k0 = 0; k0 < DK; k0 += 32) {
+    const f16x8 af = ld8(Qs + (m0 + r) * LDK + k0 + kl);
+    f16x8 bfr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) bfr[t] = ld8(Ks + (16 * t + r) * LDK + k0 + kl);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = F16Op::mma(af, bfr[t], acc[t]);
+  }
+}
+
+// Raw inputs of one chunk held in registers between the prefetch and the
+// LDS staging.  K/Q rows: thread -> (row tid / TPR, EPT elements).
+template <int C, bool WANT_Q>
+struct Pre {
+  static constexpr int TPR = 256 / C, EPT = DK / TPR, NV = EPT / 8;
+  static constexpr int NTU = (C * C / 8 + 255) / 256;   // 16-byte units of T per thread
+  uint4 k[NV], q[WANT_Q ? NV : 1];
+  uint4 t[NTU];
+  float gv, bv;
+  uint32_t v[C / 16][2];  // this lane's strip rows of v (forward) or dO (dh), bf16 pairs
+};
+
+__device__ __forceinline__ uint4 sel4(bool ok, uint4 x) {
+  return ok ? x : uint4{0u, 0u, 0u, 0u};
+}
+
+template <int C, bool WANT_Q>
+__device__ __forceinline__ void prefetch(Pre<C, WANT_Q>& p, const CArgs& a, int64_t b, int c, int kh, int hv,
+                                         int jcol, const void* vsrc) {
+  using P = Pre<C, WANT_Q>;
+  const int tid = threadIdx.x, g = lane_id() >> 4;
+  const int64_t t0 = static_cast<int64_t>(c) * C;
+  const int L = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
+  const int r = tid / P::TPR, part = tid % P::TPR;
+  const int rc = r < L ? r : L - 1;
+  const bf16_t* kb = static_cast<const bf16_t*>(a.k) + ((b * a.T + t0) * a.Hk + kh) * DK;
+  const bf16_t* qb = static_cast<const bf16_t*>(a.q) + ((b * a.T + t0) * a.Hk + kh) * DK;
+  const int off = rc * a.Hk * DK + part * P::EPT;
+#pragma unroll
+  for (int u = 0; u < P::NV; ++u) {
+    p.k[u] = sel4(r < L, *reinterpret_cast<const uint4*>(kb + off + 8 * u));
+    if constexpr (WANT_Q) p.q[u] = sel4(r < L, *reinterpret_cast<const uint4*>(qb + off + 8 * u));
+  }
+  const uint4* tsrc = reinterpret_cast<const uint4*>(static_cast<const _Float16*>(a.tmat) +
+                                                     ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(C * C));
+#pragma unroll
+  for (int u = 0; u < P::NTU; ++u) {
+    const int e = tid + 256 * u;
+    if (P::NTU * 256 == C * C / 8 || e < C * C / 8) p.t[u] = tsrc[e];
+  }
+  if (tid < 64) {
+    const int rr = tid < L ? tid : L - 1;
+    const int64_t row = (b * a.T + t0 + rr) * a.Hv + hv;
+    const float gv = a.g[row], bv = a.beta[row];
+    p.gv = tid < L ? gv : 0.f;
+    p.bv = tid < L ? bv : 0.f;
+  }
+  const bf16_t* vb = static_cast<const bf16_t*>(vsrc) + ((b * a.T + t0) * a.Hv + hv) * DK + jcol;
+#pragma unroll
+  for (int tr = 0; tr < C / 16; ++tr)
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+      const int r0 = 16 * tr + 4 * g + 2 * e2, r1 = r0 + 1;
+      const uint32_t x0 = vb[(r0 < L ? r0 : L - 1) * a.Hv * DK];
+      const uint32_t x1 = vb[(r1 < L ? r1 : L - 1) * a.Hv * DK];
+      p.v[tr][e2] = (r0 < L ? x0 : 0u) | ((r1 < L ? x1 : 0u) << 16);
+    }
+}
+
+__device__ __forceinline__ void unpack_strip(float (&x)[4], const uint32_t (&w)[2]) {
+  x[0] = __uint_as_float(w[0] << 16);
+  x[1] = __uint_as_float(w[0] & 0xffff0000u);
+  x[2] = __uint_as_float(w[1] << 16);
+  x[3] = __uint_as_float(w[1] & 0xffff0000u);
+}
+
+__device__ __forceinline__ void unpack8(const uint4& u, float (&x)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// Normalise the prefetched rows and write them as fp16: row-major
+// dst[r][i] (16-byte stores) and, if TRANS, transposed dstT[i][r].
+template <int C, int NV, bool TRANS>
+__device__ __forceinline__ void stage_rows_pre(_Float16* dst, _Float16* dstT, const uint4 (&raw)[NV], int l2) {
+  constexpr int TPR = 256 / C, EPT = DK / TPR, LDC = C + 8;
+  const int tid = threadIdx.x, r = tid / TPR, part = tid % TPR;
+  float x[NV][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    unpack8(raw[u], x[u]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += x[u][i] * x[u][i];
+  }
+  ss = xsum<1, TPR>(ss);
+  const float rn = l2 ? rsqrtf(ss + kL2Eps) : 1.f;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    f16x8 h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(x[u][i] * rn);
+    *reinterpret_cast<f16x8*>(dst + r * LDK + part * EPT + 8 * u) = h;
+    if constexpr (TRANS) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dstT[(part * EPT + 8 * u + i) * LDC + r] = h[i];
+    }
+  }
+}
+
+// T (row-major from the prep kernel) -> Ts[r][s] or, transposed, Ts[s][r].
+template <int C, int NTU, bool TRANS>
+__device__ __forceinline__ void stage_t_pre(_Float16* Ts, const uint4 (&raw)[NTU]) {
+  constexpr int LDC = C + 8;
+#pragma unroll
+  for (int u = 0; u < NTU; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    if (e < C * C / 8) {
+      const int r = (8 * e) / C, s = (8 * e) % C;
+      if constexpr (!TRANS) {
+        *reinterpret_cast<uint4*>(Ts + r * LDC + s) = raw[u];
+      } else {
+        const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Ts[(s + 2 * i) * LDC + r] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i] & 0xffffu));
+          Ts[(s + 2 * i + 1) * LDC + r] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i] >> 16));
+        }
+      }
+    }
+  }
+}
+
+// Gate scalars from the prefetched g, beta (wave 0; caller barriers):
+// G2 = log2(e) * running sum of g (for exp2 of differences), gam, lam, beta,
+// sc[0] = gam_C.
+template <int C>
+__device__ __forceinline__ void stage_gates_pre(float* G2, float* gam, float* lam, float* bet, float* sc, float gv,
+                                                float bv, int L) {
+  const int lane = threadIdx.x;
+  if (lane >= 64) return;
+  float x = gv;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  const float gc = __shfl(x, L - 1, 64);
+  if (lane < C) {
+    G2[lane] = x * kLog2e;
+    gam[lane] = expf(x);
+    lam[lane] = expf(gc - x);
+    bet[lane] = bv;
+  }
+  if (lane == 0) sc[0] = expf(gc);
+}
+
+// P row block m0: exp(G_r - G_s) q_r.k_s for s <= r, else 0.
+__device__ __forceinline__ float pmask(const float* G2, int r, int s, float qk) {
+  return s <= r ? exp2f(G2[r] - G2[s]) * qk : 0.f;
+}
+
+}  // namespace f16c
+
+// Forward chain, fp16 operands (see f16c).  Per chunk and wave:
+// Y = K H0 and Z = Q H0 (16 MFMA each), a 16-row block of P (16), U = T RHS
+// (8, chained), O += P U (8, chained), H = gam_C H + K^T (lam U) (16, chained).
+template <int C, typename TO, bool WRITE_O, bool STORE_H>
+__global__ __launch_bounds__(256) void chunk_fwd_f16_kernel(CArgs a) {
+  using namespace f16c;
+  constexpr int LDC = C + 8, NT = C / 16, NTK = DK / 16;
+  __shared__ __align__(16) _Float16 Ks[C * LDK];
+  __shared__ __align__(16) _Float16 KsT[DK * LDC];
+  __shared__ __align__(16) _Float16 Qs[WRITE_O ? C * LDK : 8];
+  __shared__ __align__(16) _Float16 Ts[C * LDC];
+  __shared__ __align__(16) _Float16 Ps[WRITE_O ? C * LDC : 8];
+  __shared__ __align__(16) _Float16 Hs[BV * LDK];   // Hs[j][i] = H[i][j]
+  __shared__ float G2[C], gam[C], lam[C], bet[C], sc[1];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int hv = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int kh = hv / (a.Hv / a.Hk);
+  const int j0 = blockIdx.x * BV;
+  const int jw = 16 * w + c16;  // this lane's column in the slice
+  const int64_t hbase = (b * a.Hv + hv) * DK * DK + j0 + jw;
+
+  f32x4 h[NTK];
+#pragma unroll
+  for (int ti = 0; ti < NTK; ++ti) {
+    h[ti] = zero4();
+    if (a.h0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[ti][e] = a.h0[hbase + (16 * ti + 4 * g + e) * DK];
+    }
+  }
+  auto write_hs = [&]() {
+#pragma unroll
+    for (int ti = 0; ti < NTK; ++ti) {
+      const f16x4 v4{static_cast<_Float16>(h[ti][0]), static_cast<_Float16>(h[ti][1]),
+                     static_cast<_Float16>(h[ti][2]), static_cast<_Float16>(h[ti][3])};
+      *reinterpret_cast<f16x4*>(Hs + jw * LDK + 16 * ti + 4 * g) = v4;
+    }
+  };
+  Pre<C, WRITE_O> pre;
+  uint32_t vcur[NT][2];
+  int Lcur = 0;
+  auto stage = [&](int c) {
+    const int64_t t0 = static_cast<int64_t>(c) * C;
+    const int L = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
+    stage_rows_pre<C, Pre<C, WRITE_O>::NV, true>(Ks, KsT, pre.k, a.l2);
+    if constexpr (WRITE_O) stage_rows_pre<C, Pre<C, WRITE_O>::NV, false>(Qs, nullptr, pre.q, a.l2);
+    stage_t_pre<C, Pre<C, WRITE_O>::NTU, false>(Ts, pre.t);
+    stage_gates_pre<C>(G2, gam, lam, bet, sc, pre.gv, pre.bv, L);
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) { vcur[tr][0] = pre.v[tr][0]; vcur[tr][1] = pre.v[tr][1]; }
+    Lcur = L;
+  };
+  prefetch<C, WRITE_O>(pre, a, b, 0, kh, hv, j0 + jw, a.v);
+  stage(0);
+  write_hs();
+  __syncthreads();
+
+  for (int c = 0; c < a.NC; ++c) {
+    const int64_t t0 = static_cast<int64_t>(c) * C;
+    const int L = Lcur;
+    if constexpr (STORE_H) {
+      _Float16* dst = static_cast<_Float16*>(a.hst) + (((b * a.Hv + hv) * a.NC + c) * DK + j0) * static_cast<int64_t>(DK);
+#pragma unroll
+      for (int e = tid; e < BV * DK / 8; e += 256) {
+        const int j = (8 * e) / DK, i = (8 * e) % DK;
+        *reinterpret_cast<uint4*>(dst + j * DK + i) = *reinterpret_cast<const uint4*>(Hs + j * LDK + i);
+      }
+    }
+    if (c + 1 < a.NC) prefetch<C, WRITE_O>(pre, a, b, c + 1, kh, hv, j0 + jw, a.v);
+
+    // Y = K H0 -> RHS;  Z = Q H0 -> O
+    f32x4 y[NT], o[NT];
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) y[tr] = zero4();
+    mma_rows<NT, DK>(y, Ks, LDK, Hs, LDK, 16 * w);
+    if constexpr (WRITE_O) {
+#pragma unroll
+      for (int tr = 0; tr < NT; ++tr) o[tr] = zero4();
+      mma_rows<NT, DK>(o, Qs, LDK, Hs, LDK, 16 * w);
+    }
+    f32x4 rhs[NT];
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) {
+      float vv[4];
+      unpack_strip(vv, vcur[tr]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * tr + 4 * g + e;
+        rhs[tr][e] = bet[r] * (vv[e] - gam[r] * y[tr][e]);
+        if constexpr (WRITE_O) o[tr][e] *= gam[r];
+      }
+    }
+    // P row blocks w, w + 4, ...
+    if constexpr (WRITE_O) {
+#pragma unroll
+      for (int rb = w; rb < NT; rb += 4) {
+        f32x4 p[NT];
+        mma_qk_row<NT>(p, Qs, Ks, 16 * rb);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int s2 = 16 * t + c16;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rb + 4 * g + e;
+            Ps[r * LDC + s2] = static_cast<_Float16>(pmask(G2, r, s2, p[t][e]));
+          }
+        }
+      }
+    }
+    // U = T RHS
+    f16x8 bf[NT / 2];
+    chain_frags<NT>(bf, rhs);
+    f32x4 u[NT];
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) u[tr] = zero4();
+    mma_chain_rows<NT, NT>(u, Ts, LDC, bf);
+    __syncthreads();  // Ps complete
+
+    if constexpr (WRITE_O) {
+      chain_frags<NT>(bf, u);
+      mma_chain_rows<NT, NT>(o, Ps, LDC, bf);
+      TO* ob = static_cast<TO*>(a.o) + ((b * a.T + t0) * a.Hv + hv) * DK + j0 + jw;
+#pragma unroll
+      for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * tr + 4 * g + e;
+          if (r < L) st1<TO>(ob + static_cast<int64_t>(r) * a.Hv * DK, o[tr][e]);
+        }
+    }
+    f32x4 lu[NT];
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lu[tr][e] = lam[16 * tr + 4 * g + e] * u[tr][e];
+    chain_frags<NT>(bf, lu);
+    const float gc = sc[0];
+#pragma unroll
+    for (int ti = 0; ti < NTK; ++ti) h[ti] = h[ti] * gc;
+    mma_chain_rows<NTK, NT>(h, KsT, LDC, bf);
+    __syncthreads();  // all reads of this chunk's LDS are done
+    write_hs();
+    if (c + 1 < a.NC) stage(c + 1);
+    __syncthreads();
+  }
+  if (a.ht) {
+#pragma unroll
+    for (int ti = 0; ti < NTK; ++ti)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a.ht[hbase + (16 * ti + 4 * g + e) * DK] = h[ti][e];
+  }
+}
+
+// Reverse dH chain, fp16 operands.  Per chunk and wave: X = K dH (16 MFMA),
+// a 16-row block of P (16), dU = lam X + P^T dO (8, chained), dRHS = T^T dU
+// (8, chained), dH = gam_C dH + Q^T (gam dO) - K^T (beta gam dRHS) (32,
+// chained).  Stores each chunk's incoming dH for the gradient kernel.
+template <int C, typename TO>
+__global__ __launch_bounds__(256) void chunk_dh_f16_kernel(CArgs a) {
+  using namespace f16c;
+  constexpr int LDC = C + 8, NT = C / 16, NTK = DK / 16;
+  __shared__ __align__(16) _Float16 Ks[C * LDK];
+  __shared__ __align__(16) _Float16 KsT[DK * LDC];
+  __shared__ __align__(16) _Float16 Qs[C * LDK];
+  __shared__ __align__(16) _Float16 QsT[DK * LDC];
+  __shared__ __align__(16) _Float16 TsT[C * LDC];   // TsT[r][s] = T[s][r]
+  __shared__ __align__(16) _Float16 PsT[C * LDC];   // PsT[s][r] = P[r][s]
+  __shared__ __align__(16) _Float16 dHs[BV * LDK];  // dHs[j][i] = dH[i][j]
+  __shared__ float G2[C], gam[C], lam[C], bet[C], sc[1];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int hv = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int kh = hv / (a.Hv / a.Hk);
+  const int j0 = blockIdx.x * BV;
+  const int jw = 16 * w + c16;
+  const int64_t hbase = (b * a.Hv + hv) * DK * DK + j0 + jw;
+
+  f32x4 dh[NTK];
+#pragma unroll
+  for (int ti = 0; ti < NTK; ++ti) {
+    dh[ti] = zero4();
+    if (a.dht) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dh[ti][e] = a.dht[hbase + (16 * ti + 4 * g + e) * DK];
+    }
+  }
+  auto write_dhs = [&]() {
+#pragma unroll
+    for (int ti = 0; ti < NTK; ++ti) {
+      const f16x4 v4{static_cast<_Float16>(dh[ti][0]), static_cast<_Float16>(dh[ti][1]),
+                     static_cast<_Float16>(dh[ti][2]), static_cast<_Float16>(dh[ti][3])};
+      *reinterpret_cast<f16x4*>(dHs + jw * LDK + 16 * ti + 4 * g) = v4;
+    }
+  };
+  Pre<C, true> pre;
+  uint32_t docur[NT][2];
+  int Lcur = 0;
+  auto stage = [&](int c) {
+    const int64_t t0 = static_cast<int64_t>(c) * C;
+    const int L = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
+    stage_rows_pre<C, Pre<C, true>::NV, true>(Ks, KsT, pre.k, a.l2);
+    stage_rows_pre<C, Pre<C, true>::NV, true>(Qs, QsT, pre.q, a.l2);
+    stage_t_pre<C, Pre<C, true>::NTU, true>(TsT, pre.t);
+    stage_gates_pre<C>(G2, gam, lam, bet, sc, pre.gv, pre.bv, L);
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) { docur[tr][0] = pre.v[tr][0]; docur[tr][1] = pre.v[tr][1]; }
+    Lcur = L;
+  };
+  prefetch<C, true>(pre, a, b, a.NC - 1, kh, hv, j0 + jw, a.dout);
+  stage(a.NC - 1);
+  write_dhs();
+  __syncthreads();
+
+  for (int c = a.NC - 1; c >= 0; --c) {
+    const int64_t t0 = static_cast<int64_t>(c) * C;
+    const int L = Lcur;
+    {
+      _Float16* dst = static_cast<_Float16*>(a.dhst) + (((b * a.Hv + hv) * a.NC + c) * DK + j0) * static_cast<int64_t>(DK);
+#pragma unroll
+      for (int e = tid; e < BV * DK / 8; e += 256) {
+        const int j = (8 * e) / DK, i = (8 * e) % DK;
+        *reinterpret_cast<uint4*>(dst + j * DK + i) = *reinterpret_cast<const uint4*>(dHs + j * LDK + i);
+      }
+    }
+    if (c > 0) prefetch<C, true>(pre, a, b, c - 1, kh, hv, j0 + jw, a.dout);
+
+    f32x4 du[NT];
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) du[tr] = zero4();
+    mma_rows<NT, DK>(du, Ks, LDK, dHs, LDK, 16 * w);
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) du[tr][e] *= lam[16 * tr + 4 * g + e];
+#pragma unroll
+    for (int rb = w; rb < NT; rb += 4) {
+      f32x4 p[NT];
+      mma_qk_row<NT>(p, Qs, Ks, 16 * rb);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int s2 = 16 * t + c16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rb + 4 * g + e;
+          PsT[s2 * LDC + r] = static_cast<_Float16>(pmask(G2, r, s2, p[t][e]));
+        }
+      }
+    }
+    f32x4 dof[NT], gdo[NT];
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) {
+      float x[4];
+      unpack_strip(x, docur[tr]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dof[tr][e] = x[e];
+        gdo[tr][e] = gam[16 * tr + 4 * g + e] * x[e];
+      }
+    }
+    __syncthreads();  // PsT complete
+
+    f16x8 bf[NT / 2];
+    chain_frags<NT>(bf, dof);
+    mma_chain_rows<NT, NT>(du, PsT, LDC, bf);
+    chain_frags<NT>(bf, du);
+    f32x4 dr[NT];
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) dr[tr] = zero4();
+    mma_chain_rows<NT, NT>(dr, TsT, LDC, bf);
+    TO* dvb = static_cast<TO*>(a.dv) + ((b * a.T + t0) * a.Hv + hv) * DK + j0 + jw;
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * tr + 4 * g + e;
+        if (r < L) st1<TO>(dvb + static_cast<int64_t>(r) * a.Hv * DK, bet[r] * dr[tr][e]);
+        dr[tr][e] *= -bet[r] * gam[r];
+      }
+    const float gc = sc[0];
+#pragma unroll
+    for (int ti = 0; ti < NTK; ++ti) dh[ti] = dh[ti] * gc;
+    chain_frags<NT>(bf, gdo);
+    mma_chain_rows<NTK, NT>(dh, QsT, LDC, bf);
+    chain_frags<NT>(bf, dr);
+    mma_chain_rows<NTK, NT>(dh, KsT, LDC, bf);
+    __syncthreads();
+    write_dhs();
+    if (c > 0) stage(c - 1);
+    __syncthreads();
+  }
+  if (a.dh0) {
+#pragma unroll
+    for (int ti = 0; ti < NTK; ++ti)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a.dh0[hbase + (16 * ti + 4 * g + e) * DK] = dh[ti][e];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 template <typename CF, typename TI>
 hipError_t prep(const CArgs& a, hipStream_t st) {
@@ -892,8 +1443,13 @@ hipError_t prep(const CArgs& a, hipStream_t st) {
 template <typename CF, typename TI, typename TO>
 hipError_t dh(const CArgs& a, hipStream_t st) {
   ProfScope ps("chunk_dh", st);
-  hipLaunchKernelGGL((chunk_dh_kernel<CF, TI, TO>), dim3(CF::DK / CF::BV, a.Hv, static_cast<unsigned>(a.B)),
-                     dim3(256), 0, st, a);
+  if constexpr (std::is_same_v<typename CF::OP, F16Op>) {
+    hipLaunchKernelGGL((chunk_dh_f16_kernel<CF::C, TO>), dim3(f16c::DK / f16c::BV, a.Hv, static_cast<unsigned>(a.B)),
+                       dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((chunk_dh_kernel<CF, TI, TO>), dim3(CF::DK / CF::BV, a.Hv, static_cast<unsigned>(a.B)),
+                       dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -908,8 +1464,13 @@ hipError_t grad(const CArgs& a, hipStream_t st) {
 template <typename CF, typename TI, typename TO, bool WO, bool SH>
 hipError_t fwd(const CArgs& a, hipStream_t st) {
   ProfScope ps(WO ? "chunk_fwd" : "chunk_states", st);
-  hipLaunchKernelGGL((chunk_fwd_kernel<CF, TI, TO, WO, SH>), dim3(CF::DK / CF::BV, a.Hv, static_cast<unsigned>(a.B)),
-                     dim3(256), 0, st, a);
+  if constexpr (std::is_same_v<typename CF::OP, F16Op>) {
+    hipLaunchKernelGGL((chunk_fwd_f16_kernel<CF::C, TO, WO, SH>), dim3(f16c::DK / f16c::BV, a.Hv, static_cast<unsigned>(a.B)),
+                       dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((chunk_fwd_kernel<CF, TI, TO, WO, SH>), dim3(CF::DK / CF::BV, a.Hv, static_cast<unsigned>(a.B)),
+                       dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 
