@@ -43,7 +43,8 @@ struct CArgs {
   const float *g, *beta, *h0, *dht;
   void* o;
   float* ht;
-  void* tmat;    // [B][Hv][NC][C][C] E
+  void* tmat;    // [B][Hv][NC][C][C] E   T = (I + A)^-1
+  void* pmat;    // [B][Hv][NC][C][C] E   P (masked, gate-scaled q.k)
   void* hst;     // [B][Hv][NC][Dv][Dk] E   chunk-entry states H0 (transposed)
   void* dhst;    // [B][Hv][NC][Dv][Dk] E   gradient at each chunk's end
   void* dv;
@@ -138,8 +139,9 @@ __device__ __forceinline__ void stage_t(typename CF::E* Ts, const typename CF::E
 }
 
 // ---------------------------------------------------------------------------
-// T = (I + A)^-1 for one (b, chunk, v-head); one wave.  Lane c computes
-// column c by forward substitution: x_r = [r == c] - sum_{s<r} A_rs x_s.
+// T = (I + A)^-1 and P for one (b, chunk, v-head); one wave.  Lane c computes
+// column c of T by forward substitution: x_r = [r == c] - sum_{s<r} A_rs x_s.
+// P_rs = exp(G_r - G_s) q_r.k_s for s <= r (0 above the diagonal).
 template <typename CF, typename TI>
 __global__ __launch_bounds__(64) void chunk_prep_kernel(CArgs a) {
   using E = typename CF::E;
@@ -147,6 +149,7 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(CArgs a) {
   constexpr int C = CF::C, DK = CF::DK, LDK = CF::LDK;
   constexpr int LDA = C + 1;
   __shared__ __align__(16) E Ks[C * LDK];
+  __shared__ __align__(16) E Qs[C * LDK];
   __shared__ float A[C * LDA];
   __shared__ float G[C], gam[C], lam[C], bet[C], sc[1];
   const int lane = threadIdx.x;
@@ -155,26 +158,47 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(CArgs a) {
   const int kh = hv / (a.Hv / a.Hk);
   const int64_t t0 = static_cast<int64_t>(c) * C;
   const int L = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
+  const int64_t cbase = (b * a.Hv + hv) * a.NC + c;
 
-  // k rows, one lane per row
-  for (int r = lane; r < C; r += 64) {
-    float ss = 0.f;
-    const TI* p = static_cast<const TI*>(a.k) + ((b * a.T + t0 + r) * a.Hk + kh) * DK;
-    if (r < L)
-      for (int i = 0; i < DK; ++i) { const float x = ld1<TI>(p + i); ss += x * x; }
-    const float rn = a.l2 ? rsqrtf(ss + kL2Eps) : 1.f;
-    for (int i = 0; i < DK; ++i) Ks[r * LDK + i] = to_e<E>(r < L ? ld1<TI>(p + i) * rn : 0.f);
+  // q and k rows, one lane per row, normalised over Dk
+  if (lane < C) {
+    const int rc = lane < L ? lane : L - 1;
+    for (int which = 0; which < 2; ++which) {
+      const TI* p = static_cast<const TI*>(which ? a.q : a.k) + ((b * a.T + t0 + rc) * a.Hk + kh) * DK;
+      E* dst = (which ? Qs : Ks) + lane * LDK;
+      float x[DK];
+#pragma unroll
+      for (int i = 0; i < DK; i += 4) {
+        float t4[4];
+        ld4<TI>(p + i, t4);
+        x[i] = t4[0]; x[i + 1] = t4[1]; x[i + 2] = t4[2]; x[i + 3] = t4[3];
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < DK; ++i) ss += x[i] * x[i];
+      const float rn = lane < L ? (a.l2 ? rsqrtf(ss + kL2Eps) : 1.f) : 0.f;
+#pragma unroll
+      for (int i = 0; i < DK; ++i) dst[i] = to_e<E>(x[i] * rn);
+    }
   }
   stage_gates<C>(G, gam, lam, bet, sc, b, t0, L, hv, a);
   __syncthreads();
-  // A_rs = beta_r exp(G_r - G_s) k_r.k_s for s < r
+  E* pdst = static_cast<E*>(a.pmat) + cbase * static_cast<int64_t>(C * C);
   for (int tr = 0; tr < C / 16; ++tr)
-    for (int tc = 0; tc <= tr; ++tc) {
-      const f32x4 s = mma_tile<OP, false, false>(zero4(), Ks, LDK, 16 * tr, Ks, LDK, 16 * tc, DK);
+    for (int tc = 0; tc < C / 16; ++tc) {
+      if (tc <= tr) {
+        const f32x4 s = mma_tile<OP, false, false>(zero4(), Ks, LDK, 16 * tr, Ks, LDK, 16 * tc, DK);
+        const f32x4 qk = mma_tile<OP, false, false>(zero4(), Qs, LDK, 16 * tr, Ks, LDK, 16 * tc, DK);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = acc_row(16 * tr, i), q = acc_col(16 * tc);
-        A[r * LDA + q] = q < r ? bet[r] * expf(G[r] - G[q]) * s[i] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+          const int r = acc_row(16 * tr, i), q = acc_col(16 * tc);
+          const float e = q <= r ? expf(G[r] - G[q]) : 0.f;
+          A[r * LDA + q] = q < r ? bet[r] * e * s[i] : 0.f;
+          pdst[r * C + q] = to_e<E>(e * qk[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pdst[acc_row(16 * tr, i) * C + acc_col(16 * tc)] = to_e<E>(0.f);
       }
     }
   __syncthreads();
@@ -184,10 +208,10 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(CArgs a) {
     for (int r = 0; r < C; ++r) {
       float acc = r == lane ? 1.f : 0.f;
 #pragma unroll
-      for (int s = 0; s < r; ++s) acc -= A[r * LDA + s] * x[s];
+      for (int s2 = 0; s2 < r; ++s2) acc -= A[r * LDA + s2] * x[s2];
       x[r] = acc;
     }
-    E* dst = static_cast<E*>(a.tmat) + ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(C * C);
+    E* dst = static_cast<E*>(a.tmat) + cbase * static_cast<int64_t>(C * C);
 #pragma unroll
     for (int r = 0; r < C; ++r) dst[r * C + lane] = to_e<E>(x[r]);
   }
@@ -978,7 +1002,7 @@ struct Pre {
   static constexpr int TPR = 256 / C, EPT = DK / TPR, NV = EPT / 8;
   static constexpr int NTU = (C * C / 8 + 255) / 256;   // 16-byte units of T per thread
   uint4 k[NV], q[WANT_Q ? NV : 1];
-  uint4 t[NTU];
+  uint4 t[NTU], pm[NTU];
   float gv, bv;
   uint32_t v[C / 16][2];  // this lane's strip rows of v (forward) or dO (dh), bf16 pairs
 };
@@ -1006,10 +1030,15 @@ __device__ __forceinline__ void prefetch(Pre<C, WANT_Q>& p, const CArgs& a, int6
   }
   const uint4* tsrc = reinterpret_cast<const uint4*>(static_cast<const _Float16*>(a.tmat) +
                                                      ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(C * C));
+  const uint4* psrc = reinterpret_cast<const uint4*>(static_cast<const _Float16*>(a.pmat) +
+                                                     ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(C * C));
 #pragma unroll
   for (int u = 0; u < P::NTU; ++u) {
     const int e = tid + 256 * u;
-    if (P::NTU * 256 == C * C / 8 || e < C * C / 8) p.t[u] = tsrc[e];
+    if (P::NTU * 256 == C * C / 8 || e < C * C / 8) {
+      p.t[u] = tsrc[e];
+      p.pm[u] = psrc[e];
+    }
   }
   if (tid < 64) {
     const int rr = tid < L ? tid : L - 1;
@@ -1048,7 +1077,7 @@ __device__ __forceinline__ void unpack8(const uint4& u, float (&x)[8]) {
 
 // Normalise the prefetched rows and write them as fp16: row-major
 // dst[r][i] (16-byte stores) and, if TRANS, transposed dstT[i][r].
-template <int C, int NV, bool TRANS>
+template <int C, int NV, bool TRANS, bool ROW = true>
 __device__ __forceinline__ void stage_rows_pre(_Float16* dst, _Float16* dstT, const uint4 (&raw)[NV], int l2) {
   constexpr int TPR = 256 / C, EPT = DK / TPR, LDC = C + 8;
   const int tid = threadIdx.x, r = tid / TPR, part = tid % TPR;
@@ -1067,7 +1096,7 @@ __device__ __forceinline__ void stage_rows_pre(_Float16* dst, _Float16* dstT, co
     f16x8 h;
 #pragma unroll
     for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(x[u][i] * rn);
-    *reinterpret_cast<f16x8*>(dst + r * LDK + part * EPT + 8 * u) = h;
+    if constexpr (ROW) *reinterpret_cast<f16x8*>(dst + r * LDK + part * EPT + 8 * u) = h;
     if constexpr (TRANS) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) dstT[(part * EPT + 8 * u + i) * LDC + r] = h[i];
@@ -1178,6 +1207,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_f16_kernel(CArgs a) {
     stage_rows_pre<C, Pre<C, WRITE_O>::NV, true>(Ks, KsT, pre.k, a.l2);
     if constexpr (WRITE_O) stage_rows_pre<C, Pre<C, WRITE_O>::NV, false>(Qs, nullptr, pre.q, a.l2);
     stage_t_pre<C, Pre<C, WRITE_O>::NTU, false>(Ts, pre.t);
+    if constexpr (WRITE_O) stage_t_pre<C, Pre<C, WRITE_O>::NTU, false>(Ps, pre.pm);
     stage_gates_pre<C>(G2, gam, lam, bet, sc, pre.gv, pre.bv, L);
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr) { vcur[tr][0] = pre.v[tr][0]; vcur[tr][1] = pre.v[tr][1]; }
@@ -1191,13 +1221,12 @@ __global__ __launch_bounds__(256) void chunk_fwd_f16_kernel(CArgs a) {
   for (int c = 0; c < a.NC; ++c) {
     const int64_t t0 = static_cast<int64_t>(c) * C;
     const int L = Lcur;
-    if constexpr (STORE_H) {
-      _Float16* dst = static_cast<_Float16*>(a.hst) + (((b * a.Hv + hv) * a.NC + c) * DK + j0) * static_cast<int64_t>(DK);
+    if constexpr (STORE_H) {  // chunk entry state, natural [Dk][Dv] layout
+      _Float16* dst = static_cast<_Float16*>(a.hst) + ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(DK * DK) + j0 + jw;
 #pragma unroll
-      for (int e = tid; e < BV * DK / 8; e += 256) {
-        const int j = (8 * e) / DK, i = (8 * e) % DK;
-        *reinterpret_cast<uint4*>(dst + j * DK + i) = *reinterpret_cast<const uint4*>(Hs + j * LDK + i);
-      }
+      for (int ti = 0; ti < NTK; ++ti)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(16 * ti + 4 * g + e) * DK] = static_cast<_Float16>(h[ti][e]);
     }
     if (c + 1 < a.NC) prefetch<C, WRITE_O>(pre, a, b, c + 1, kh, hv, j0 + jw, a.v);
 
@@ -1223,23 +1252,6 @@ __global__ __launch_bounds__(256) void chunk_fwd_f16_kernel(CArgs a) {
         if constexpr (WRITE_O) o[tr][e] *= gam[r];
       }
     }
-    // P row blocks w, w + 4, ...
-    if constexpr (WRITE_O) {
-#pragma unroll
-      for (int rb = w; rb < NT; rb += 4) {
-        f32x4 p[NT];
-        mma_qk_row<NT>(p, Qs, Ks, 16 * rb);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const int s2 = 16 * t + c16;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * rb + 4 * g + e;
-            Ps[r * LDC + s2] = static_cast<_Float16>(pmask(G2, r, s2, p[t][e]));
-          }
-        }
-      }
-    }
     // U = T RHS
     f16x8 bf[NT / 2];
     chain_frags<NT>(bf, rhs);
@@ -1247,7 +1259,6 @@ __global__ __launch_bounds__(256) void chunk_fwd_f16_kernel(CArgs a) {
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr) u[tr] = zero4();
     mma_chain_rows<NT, NT>(u, Ts, LDC, bf);
-    __syncthreads();  // Ps complete
 
     if constexpr (WRITE_O) {
       chain_frags<NT>(bf, u);
@@ -1294,7 +1305,6 @@ __global__ __launch_bounds__(256) void chunk_dh_f16_kernel(CArgs a) {
   constexpr int LDC = C + 8, NT = C / 16, NTK = DK / 16;
   __shared__ __align__(16) _Float16 Ks[C * LDK];
   __shared__ __align__(16) _Float16 KsT[DK * LDC];
-  __shared__ __align__(16) _Float16 Qs[C * LDK];
   __shared__ __align__(16) _Float16 QsT[DK * LDC];
   __shared__ __align__(16) _Float16 TsT[C * LDC];   // TsT[r][s] = T[s][r]
   __shared__ __align__(16) _Float16 PsT[C * LDC];   // PsT[s][r] = P[r][s]
@@ -1333,8 +1343,9 @@ __global__ __launch_bounds__(256) void chunk_dh_f16_kernel(CArgs a) {
     const int64_t t0 = static_cast<int64_t>(c) * C;
     const int L = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
     stage_rows_pre<C, Pre<C, true>::NV, true>(Ks, KsT, pre.k, a.l2);
-    stage_rows_pre<C, Pre<C, true>::NV, true>(Qs, QsT, pre.q, a.l2);
+    stage_rows_pre<C, Pre<C, true>::NV, true, false>(nullptr, QsT, pre.q, a.l2);
     stage_t_pre<C, Pre<C, true>::NTU, true>(TsT, pre.t);
+    stage_t_pre<C, Pre<C, true>::NTU, true>(PsT, pre.pm);
     stage_gates_pre<C>(G2, gam, lam, bet, sc, pre.gv, pre.bv, L);
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr) { docur[tr][0] = pre.v[tr][0]; docur[tr][1] = pre.v[tr][1]; }
@@ -1348,13 +1359,12 @@ __global__ __launch_bounds__(256) void chunk_dh_f16_kernel(CArgs a) {
   for (int c = a.NC - 1; c >= 0; --c) {
     const int64_t t0 = static_cast<int64_t>(c) * C;
     const int L = Lcur;
-    {
-      _Float16* dst = static_cast<_Float16*>(a.dhst) + (((b * a.Hv + hv) * a.NC + c) * DK + j0) * static_cast<int64_t>(DK);
+    {  // gradient at this chunk's end, natural [Dk][Dv] layout
+      _Float16* dst = static_cast<_Float16*>(a.dhst) + ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(DK * DK) + j0 + jw;
 #pragma unroll
-      for (int e = tid; e < BV * DK / 8; e += 256) {
-        const int j = (8 * e) / DK, i = (8 * e) % DK;
-        *reinterpret_cast<uint4*>(dst + j * DK + i) = *reinterpret_cast<const uint4*>(dHs + j * LDK + i);
-      }
+      for (int ti = 0; ti < NTK; ++ti)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(16 * ti + 4 * g + e) * DK] = static_cast<_Float16>(dh[ti][e]);
     }
     if (c > 0) prefetch<C, true>(pre, a, b, c - 1, kh, hv, j0 + jw, a.dout);
 
@@ -1366,20 +1376,6 @@ __global__ __launch_bounds__(256) void chunk_dh_f16_kernel(CArgs a) {
     for (int tr = 0; tr < NT; ++tr)
 #pragma unroll
       for (int e = 0; e < 4; ++e) du[tr][e] *= lam[16 * tr + 4 * g + e];
-#pragma unroll
-    for (int rb = w; rb < NT; rb += 4) {
-      f32x4 p[NT];
-      mma_qk_row<NT>(p, Qs, Ks, 16 * rb);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int s2 = 16 * t + c16;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * rb + 4 * g + e;
-          PsT[s2 * LDC + r] = static_cast<_Float16>(pmask(G2, r, s2, p[t][e]));
-        }
-      }
-    }
     f32x4 dof[NT], gdo[NT];
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr) {
@@ -1391,8 +1387,6 @@ __global__ __launch_bounds__(256) void chunk_dh_f16_kernel(CArgs a) {
         gdo[tr][e] = gam[16 * tr + 4 * g + e] * x[e];
       }
     }
-    __syncthreads();  // PsT complete
-
     f16x8 bf[NT / 2];
     chain_frags<NT>(bf, dof);
     mma_chain_rows<NT, NT>(du, PsT, LDC, bf);
@@ -1430,6 +1424,350 @@ __global__ __launch_bounds__(256) void chunk_dh_f16_kernel(CArgs a) {
   }
 }
 
+namespace f16c {
+
+// acc[t] += A[16t : 16t+16, 0:K] * B, B^T rows n0..n0+15 read through a
+// row-contiguous view (element (n, k) at Bm[k * ldb + n]); B is shared.
+template <int NO, int K>
+__device__ __forceinline__ void mma_rows_bkmin(f32x4 (&acc)[NO], const _Float16* A, int lda, const _Float16* Bm,
+                                               int ldb, int n0) {
+  const int r = lane_id() & 15, kl = (lane_id() >> 4) * 8;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    f16x8 bfr;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bfr[i] = Bm[(k0 + kl + i) * ldb + n0 + r];
+    f16x8 af[NO];
+#pragma unroll
+    for (int t = 0; t < NO; ++t) af[t] = ld8(A + (16 * t + r) * lda + k0 + kl);
+#pragma unroll
+    for (int t = 0; t < NO; ++t) acc[t] = F16Op::mma(af[t], bfr, acc[t]);
+  }
+}
+
+// acc[t] += A[m0 : m0+16, 0:K] * B[:, nb + 16t : nb + 16t + 16]; B^T rows
+// from Bt (k contiguous); the A fragment is shared.
+template <int NCOL, int K>
+__device__ __forceinline__ void mma_cols(f32x4 (&acc)[NCOL], const _Float16* A, int lda, int m0, const _Float16* Bt,
+                                         int ldb, int nb) {
+  const int r = lane_id() & 15, kl = (lane_id() >> 4) * 8;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const f16x8 af = ld8(A + (m0 + r) * lda + k0 + kl);
+    f16x8 bfr[NCOL];
+#pragma unroll
+    for (int t = 0; t < NCOL; ++t) bfr[t] = ld8(Bt + (nb + 16 * t + r) * ldb + k0 + kl);
+#pragma unroll
+    for (int t = 0; t < NCOL; ++t) acc[t] = F16Op::mma(af, bfr[t], acc[t]);
+  }
+}
+
+// Branch-free load of this lane's strip rows (16tr + 4g + e) of a bf16
+// [B,T,Hv,Dv] tensor at column jcol; rows >= L read as 0.
+template <int NT>
+__device__ __forceinline__ void load_strip(f32x4 (&x)[NT], const bf16_t* base, int64_t rstride, int L) {
+  const int g = lane_id() >> 4;
+#pragma unroll
+  for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * tr + 4 * g + e;
+      const float v = bf16_to_f32(base[(r < L ? r : L - 1) * rstride]);
+      x[tr][e] = r < L ? v : 0.f;
+    }
+}
+
+}  // namespace f16c
+
+// All gradients of one chunk except dv and dH (fp16 operands), given its
+// entry state H0 and the gradient dH at its end, both [Dk][Dv] fp16.  The
+// value dim is walked in two halves of 64 columns; wave w owns the 16-column
+// strip 16w.. of a half, so Y = K H0, X = K dH, U = T RHS, dU = lam X + P^T dO
+// and dRHS = T^T dU chain in registers.  The value-dim reductions
+//   X1 = dRHS H0^T, X2 = dO H0^T, dP = dO U^T   (phase 1)
+//   X3 = U dH^T, dT = dU RHS^T                  (phase 2)
+// read row-contiguous copies written to LDS.  Then the C x C stage
+// (dA = -T^T dT T^T) and dq / dk as in chunk_grad_kernel.
+template <int C>
+__global__ __launch_bounds__(256) void chunk_grad_f16_kernel(CArgs a) {
+  using namespace f16c;
+  constexpr int LDC = C + 8, NT = C / 16, LDJ = 64 + 8;
+  constexpr int WPR = 4 / NT;   // waves per row tile in the reductions
+  constexpr int NCK = 8 / WPR;  // Dk column tiles per wave
+  constexpr int NCQ = NT / WPR; // C column tiles per wave
+  constexpr int POOL_HALF = 2 * DK * LDJ + 3 * C * LDJ;
+  constexpr int POOL_CC = 5 * C * LDC;
+  constexpr int POOL = POOL_HALF > POOL_CC ? POOL_HALF : POOL_CC;
+  __shared__ __align__(16) _Float16 Ks[C * LDK];
+  __shared__ __align__(16) _Float16 KsT[DK * LDC];
+  __shared__ __align__(16) _Float16 QsT[DK * LDC];
+  __shared__ __align__(16) _Float16 Ts[C * LDC];
+  __shared__ __align__(16) _Float16 TsT[C * LDC];
+  __shared__ __align__(16) _Float16 PsT[C * LDC];
+  __shared__ __align__(16) _Float16 pool[POOL];
+  __shared__ float G2[C], gam[C], lam[C], bet[C], sc[1];
+  __shared__ float sG[4][C], sGc[4][C], sB[4][C], red[2][4];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int c = blockIdx.x, hv = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int kh = hv / (a.Hv / a.Hk);
+  const int64_t t0 = static_cast<int64_t>(c) * C;
+  const int L = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
+  const int64_t cbase = (b * a.Hv + hv) * a.NC + c;
+  const int rt = w % NT, cq = w / NT;  // reduction tile ownership
+
+  for (int e = tid; e < 4 * C; e += 256) {
+    sG[e / C][e % C] = 0.f;
+    sGc[e / C][e % C] = 0.f;
+    sB[e / C][e % C] = 0.f;
+  }
+  {
+    Pre<C, true> pre;
+    prefetch<C, true>(pre, a, b, c, kh, hv, 0, a.v);
+    stage_rows_pre<C, Pre<C, true>::NV, true>(Ks, KsT, pre.k, a.l2);
+    stage_rows_pre<C, Pre<C, true>::NV, true, false>(nullptr, QsT, pre.q, a.l2);
+    stage_t_pre<C, Pre<C, true>::NTU, false>(Ts, pre.t);
+    stage_t_pre<C, Pre<C, true>::NTU, true>(TsT, pre.t);
+    stage_t_pre<C, Pre<C, true>::NTU, true>(PsT, pre.pm);
+    stage_gates_pre<C>(G2, gam, lam, bet, sc, pre.gv, pre.bv, L);
+  }
+
+  f32x4 x1[NCK], x2[NCK], x3[NCK], dP[NCQ], dT[NCQ];
+#pragma unroll
+  for (int t = 0; t < NCK; ++t) x1[t] = x2[t] = x3[t] = zero4();
+#pragma unroll
+  for (int t = 0; t < NCQ; ++t) dP[t] = dT[t] = zero4();
+  float hh = 0.f;  // this thread's part of <dH, H0>
+  _Float16* H0T = pool;               // H0T[i][j]  = H0[i][jh + j]
+  _Float16* dHT = H0T + DK * LDJ;     // dHT[i][j]  = dH[i][jh + j]
+  _Float16* X0 = dHT + DK * LDJ;      // [C][LDJ]: dRHS, then dU
+  _Float16* X1b = X0 + C * LDJ;       // [C][LDJ]: dO, then RHS
+  _Float16* X2b = X1b + C * LDJ;      // [C][LDJ]: U
+  const _Float16* hsrc = static_cast<const _Float16*>(a.hst) + cbase * static_cast<int64_t>(DK * DK);
+  const _Float16* dhsrc = static_cast<const _Float16*>(a.dhst) + cbase * static_cast<int64_t>(DK * DK);
+  const int64_t rstride = static_cast<int64_t>(a.Hv) * DK;
+
+  for (int jh = 0; jh < DK; jh += 64) {
+    __syncthreads();  // previous users of the pool (and the staging above) are done
+#pragma unroll
+    for (int u = 0; u < DK * 8 / 256; ++u) {
+      const int e = tid + 256 * u;
+      const int i = e / 8, q8 = e % 8;
+      const uint4 hv4 = *reinterpret_cast<const uint4*>(hsrc + i * DK + jh + 8 * q8);
+      const uint4 dv4 = *reinterpret_cast<const uint4*>(dhsrc + i * DK + jh + 8 * q8);
+      *reinterpret_cast<uint4*>(H0T + i * LDJ + 8 * q8) = hv4;
+      *reinterpret_cast<uint4*>(dHT + i * LDJ + 8 * q8) = dv4;
+      const _Float16* ph = reinterpret_cast<const _Float16*>(&hv4);
+      const _Float16* pd = reinterpret_cast<const _Float16*>(&dv4);
+#pragma unroll
+      for (int k2 = 0; k2 < 8; ++k2) hh += static_cast<float>(ph[k2]) * static_cast<float>(pd[k2]);
+    }
+    const int jcol = jh + 16 * w + c16;
+    f32x4 vv[NT], dov[NT];
+    load_strip<NT>(vv, static_cast<const bf16_t*>(a.v) + ((b * a.T + t0) * a.Hv + hv) * DK + jcol, rstride, L);
+    load_strip<NT>(dov, static_cast<const bf16_t*>(a.dout) + ((b * a.T + t0) * a.Hv + hv) * DK + jcol, rstride, L);
+    __syncthreads();
+
+    f32x4 y[NT], du[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) y[t] = du[t] = zero4();
+    mma_rows_bkmin<NT, DK>(y, Ks, LDK, H0T, LDJ, 16 * w);
+    mma_rows_bkmin<NT, DK>(du, Ks, LDK, dHT, LDJ, 16 * w);
+    f32x4 rhs[NT], vmy[NT];
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * tr + 4 * g + e;
+        vmy[tr][e] = vv[tr][e] - gam[r] * y[tr][e];
+        rhs[tr][e] = bet[r] * vmy[tr][e];
+        du[tr][e] *= lam[r];
+      }
+    f16x8 bf[NT / 2];
+    f32x4 u[NT], dr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) u[t] = dr[t] = zero4();
+    chain_frags<NT>(bf, rhs);
+    mma_chain_rows<NT, NT>(u, Ts, LDC, bf);
+    chain_frags<NT>(bf, dov);
+    mma_chain_rows<NT, NT>(du, PsT, LDC, bf);
+    chain_frags<NT>(bf, du);
+    mma_chain_rows<NT, NT>(dr, TsT, LDC, bf);
+    const int jl = 16 * w + c16;
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * tr + 4 * g + e;
+        const float sb = xsum<1, 16>(dr[tr][e] * vmy[tr][e]);
+        const float sy = xsum<1, 16>(dr[tr][e] * y[tr][e]);
+        if (c16 == 0) {
+          sB[w][r] += sb;
+          sG[w][r] -= bet[r] * gam[r] * sy;
+        }
+        X0[r * LDJ + jl] = static_cast<_Float16>(dr[tr][e]);
+        X1b[r * LDJ + jl] = static_cast<_Float16>(dov[tr][e]);
+        X2b[r * LDJ + jl] = static_cast<_Float16>(u[tr][e]);
+      }
+    __syncthreads();
+    // phase 1: X1 += dRHS H0^T, X2 += dO H0^T, dP += dO U^T
+    mma_cols<NCK, 64>(x1, X0, LDJ, 16 * rt, H0T, LDJ, 16 * cq * NCK);
+    mma_cols<NCK, 64>(x2, X1b, LDJ, 16 * rt, H0T, LDJ, 16 * cq * NCK);
+    mma_cols<NCQ, 64>(dP, X1b, LDJ, 16 * rt, X2b, LDJ, 16 * cq * NCQ);
+    __syncthreads();
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * tr + 4 * g + e;
+        X0[r * LDJ + jl] = static_cast<_Float16>(du[tr][e]);
+        X1b[r * LDJ + jl] = static_cast<_Float16>(rhs[tr][e]);
+      }
+    __syncthreads();
+    // phase 2: X3 += U dH^T, dT += dU RHS^T
+    mma_cols<NCK, 64>(x3, X2b, LDJ, 16 * rt, dHT, LDJ, 16 * cq * NCK);
+    mma_cols<NCQ, 64>(dT, X0, LDJ, 16 * rt, X1b, LDJ, 16 * cq * NCQ);
+  }
+  __syncthreads();
+
+  // ---- C x C stage
+  _Float16* dTT = pool;             // dTT[s'][s] = dT[s][s']
+  _Float16* M1s = dTT + C * LDC;
+  _Float16* dPm = M1s + C * LDC;    // dPm[r][s]
+  _Float16* dPmT = dPm + C * LDC;   // dPmT[s][r]
+  _Float16* dAs = dPmT + C * LDC;   // symmetric dAm + dAm^T
+#pragma unroll
+  for (int cc = 0; cc < NCQ; ++cc) {
+    const int s2 = 16 * (cq * NCQ + cc) + c16;
+    f16x4 t4;
+    float col = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * rt + 4 * g + e;
+      t4[e] = static_cast<_Float16>(dT[cc][e]);
+      const float pv = static_cast<float>(PsT[s2 * LDC + r]);      // P_rs
+      const float m = s2 <= r ? exp2f(G2[r] - G2[s2]) : 0.f;
+      const float dpp = dP[cc][e] * pv;
+      const float rs = xsum<1, 16>(dpp);
+      if (c16 == 0) sG[w][r] += rs;
+      col += dpp;
+      dPm[r * LDC + s2] = static_cast<_Float16>(dP[cc][e] * m);
+    }
+    *reinterpret_cast<f16x4*>(dTT + s2 * LDC + 16 * rt + 4 * g) = t4;
+    f16x4 p4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p4[e] = dPm[(16 * rt + 4 * g + e) * LDC + s2];
+    *reinterpret_cast<f16x4*>(dPmT + s2 * LDC + 16 * rt + 4 * g) = p4;
+    col = xsum<16, 64>(col);
+    if (lane < 16) sGc[w][s2] += col;
+  }
+  __syncthreads();
+  f32x4 m1[NCQ];
+#pragma unroll
+  for (int cc = 0; cc < NCQ; ++cc) m1[cc] = zero4();
+  mma_cols<NCQ, C>(m1, TsT, LDC, 16 * rt, dTT, LDC, 16 * cq * NCQ);
+#pragma unroll
+  for (int cc = 0; cc < NCQ; ++cc)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) M1s[(16 * rt + 4 * g + e) * LDC + 16 * (cq * NCQ + cc) + c16] = static_cast<_Float16>(m1[cc][e]);
+  __syncthreads();
+  f32x4 da[NCQ], kk[NCQ];
+#pragma unroll
+  for (int cc = 0; cc < NCQ; ++cc) da[cc] = kk[cc] = zero4();
+  mma_cols<NCQ, C>(da, M1s, LDC, 16 * rt, Ts, LDC, 16 * cq * NCQ);
+  mma_cols<NCQ, DK>(kk, Ks, LDK, 16 * rt, Ks, LDK, 16 * cq * NCQ);
+#pragma unroll
+  for (int cc = 0; cc < NCQ; ++cc) {
+    const int s2 = 16 * (cq * NCQ + cc) + c16;
+    float col = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * rt + 4 * g + e;
+      const float ex = s2 < r ? exp2f(G2[r] - G2[s2]) : 0.f;
+      const float dav = -da[cc][e] * ex;
+      const float dam = dav * bet[r];
+      const float rb = xsum<1, 16>(dav * kk[cc][e]);
+      const float ag = dam * kk[cc][e];
+      const float rg = xsum<1, 16>(ag);
+      if (c16 == 0) {
+        sB[w][r] += rb;
+        sG[w][r] += rg;
+      }
+      col += ag;
+      if (s2 < r) {
+        dAs[r * LDC + s2] = static_cast<_Float16>(dam);
+        dAs[s2 * LDC + r] = static_cast<_Float16>(dam);
+      } else if (s2 == r) {
+        dAs[r * LDC + r] = static_cast<_Float16>(0.f);
+      }
+    }
+    col = xsum<16, 64>(col);
+    if (lane < 16) sGc[w][s2] += col;
+  }
+  __syncthreads();
+
+  // ---- dq, dk per v-head; X2 / X3 terms of dG
+  f32x4 dq[NCK], dk[NCK];
+#pragma unroll
+  for (int t = 0; t < NCK; ++t) dq[t] = dk[t] = zero4();
+  mma_cols<NCK, C>(dq, dPm, LDC, 16 * rt, KsT, LDC, 16 * cq * NCK);
+  mma_cols<NCK, C>(dk, dPmT, LDC, 16 * rt, QsT, LDC, 16 * cq * NCK);
+  mma_cols<NCK, C>(dk, dAs, LDC, 16 * rt, KsT, LDC, 16 * cq * NCK);
+  float gcx = 0.f;
+  float* pq = a.pdq + ((b * a.T + t0) * a.Hv + hv) * DK;
+  float* pk = a.pdk + ((b * a.T + t0) * a.Hv + hv) * DK;
+#pragma unroll
+  for (int ct = 0; ct < NCK; ++ct) {
+    const int i2 = 16 * (cq * NCK + ct) + c16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * rt + 4 * g + e;
+      const float qn = static_cast<float>(QsT[i2 * LDC + r]);
+      const float kn = static_cast<float>(KsT[i2 * LDC + r]);
+      const float t3 = lam[r] * kn * x3[ct][e];
+      const float rg = xsum<1, 16>(gam[r] * qn * x2[ct][e] - t3);
+      gcx += t3;
+      if (c16 == 0) sG[w][r] += rg;
+      const float dqv = dq[ct][e] + gam[r] * x2[ct][e];
+      const float dkv = dk[ct][e] + lam[r] * x3[ct][e] - bet[r] * gam[r] * x1[ct][e];
+      if (r < L) {
+        pq[static_cast<int64_t>(r) * rstride + i2] = dqv;
+        pk[static_cast<int64_t>(r) * rstride + i2] = dkv;
+      }
+    }
+  }
+  hh = xsum<1, 64>(hh);
+  gcx = xsum<1, 64>(gcx);
+  if (lane == 0) {
+    red[0][w] = hh;
+    red[1][w] = gcx;
+  }
+  __syncthreads();
+  if (w == 0) {
+    const int r = lane;
+    float dG = 0.f, dB = 0.f;
+    if (r < C) {
+      dG = sG[0][r] + sG[1][r] + sG[2][r] + sG[3][r] - (sGc[0][r] + sGc[1][r] + sGc[2][r] + sGc[3][r]);
+      dB = sB[0][r] + sB[1][r] + sB[2][r] + sB[3][r];
+    }
+    if (r == L - 1)
+      dG += sc[0] * (red[0][0] + red[0][1] + red[0][2] + red[0][3]) + (red[1][0] + red[1][1] + red[1][2] + red[1][3]);
+    if (r >= L) dG = 0.f;
+    float x = dG;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float yv = __shfl_down(x, off, 64);
+      if (lane + off < 64) x += yv;
+    }
+    if (r < L) {
+      const int64_t row = (b * a.T + t0 + r) * a.Hv + hv;
+      a.dg[row] = x;
+      a.dbeta[row] = dB;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host side.
 template <typename CF, typename TI>
@@ -1456,8 +1794,13 @@ hipError_t dh(const CArgs& a, hipStream_t st) {
 template <typename CF, typename TI>
 hipError_t grad(const CArgs& a, hipStream_t st) {
   ProfScope ps("chunk_grad", st);
-  hipLaunchKernelGGL((chunk_grad_kernel<CF, TI>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(256), 0,
-                     st, a);
+  if constexpr (std::is_same_v<typename CF::OP, F16Op>) {
+    hipLaunchKernelGGL((chunk_grad_f16_kernel<CF::C>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(256), 0,
+                       st, a);
+  } else {
+    hipLaunchKernelGGL((chunk_grad_kernel<CF, TI>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(256), 0,
+                       st, a);
+  }
   return hipGetLastError();
 }
 
@@ -1529,7 +1872,7 @@ size_t chunk_state_bytes(const Shape& s, int C) {
 hipError_t launch_chunk_fwd(const Shape& s, int C, const ChunkFwdArgs& x, hipStream_t st) {
   CArgs a = base_args(s, C);
   a.q = x.q; a.k = x.k; a.v = x.v; a.g = x.g; a.beta = x.beta; a.h0 = x.h0;
-  a.o = x.o; a.ht = x.ht; a.tmat = x.tmat;
+  a.o = x.o; a.ht = x.ht; a.tmat = x.tmat; a.pmat = x.pmat;
   return with_cfg(s, C, [&](auto cfg, auto ti, auto to) -> hipError_t {
     using CF = decltype(cfg);
     using TI = typename decltype(ti)::type;
@@ -1543,7 +1886,7 @@ hipError_t launch_chunk_fwd(const Shape& s, int C, const ChunkFwdArgs& x, hipStr
 hipError_t launch_chunk_bwd(const Shape& s, int C, const ChunkBwdArgs& x, hipStream_t st) {
   CArgs a = base_args(s, C);
   a.q = x.q; a.k = x.k; a.v = x.v; a.dout = x.dout; a.g = x.g; a.beta = x.beta; a.h0 = x.h0; a.dht = x.dht;
-  a.dv = x.dv; a.dh0 = x.dh0; a.tmat = x.tmat; a.hst = x.hst; a.dhst = x.dhst;
+  a.dv = x.dv; a.dh0 = x.dh0; a.tmat = x.tmat; a.pmat = x.pmat; a.hst = x.hst; a.dhst = x.dhst;
   a.pdq = x.pdq; a.pdk = x.pdk; a.dg = x.dg; a.dbeta = x.dbeta;
   return with_cfg(s, C, [&](auto cfg, auto ti, auto to) -> hipError_t {
     using CF = decltype(cfg);

@@ -78,6 +78,7 @@ struct ChunkFwdArgs {
   void* o;
   float* ht;
   void* tmat;  // chunk_tmat_bytes
+  void* pmat;  // chunk_tmat_bytes (masked, gate-scaled q.k per chunk)
 };
 hipError_t launch_chunk_fwd(const Shape& s, int C, const ChunkFwdArgs& a, hipStream_t st);
 
@@ -90,6 +91,7 @@ struct ChunkBwdArgs {
   void* dv;
   float* dh0;
   void* tmat;        // chunk_tmat_bytes
+  void* pmat;        // chunk_tmat_bytes
   void *hst, *dhst;  // chunk_state_bytes each
   float *pdq, *pdk;  // [B][T][Hv][Dk]
   float *dg, *dbeta;
