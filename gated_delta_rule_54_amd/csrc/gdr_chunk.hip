@@ -147,10 +147,10 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(CArgs a) {
   using E = typename CF::E;
   using OP = typename CF::OP;
   constexpr int C = CF::C, DK = CF::DK, LDK = CF::LDK;
-  constexpr int LDA = C + 1;
+  constexpr int LDA = C + 4;
   __shared__ __align__(16) E Ks[C * LDK];
   __shared__ __align__(16) E Qs[C * LDK];
-  __shared__ float A[C * LDA];
+  __shared__ __align__(16) float A[C * LDA];
   __shared__ float G[C], gam[C], lam[C], bet[C], sc[1];
   const int lane = threadIdx.x;
   const int c = blockIdx.x, hv = blockIdx.y;
@@ -203,13 +203,15 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(CArgs a) {
     }
   __syncthreads();
   if (lane < C) {
+    // four interleaved partial sums per row keep the FMA pipeline busy; the
+    // order of additions is fixed (deterministic)
     float x[C];
 #pragma unroll
     for (int r = 0; r < C; ++r) {
-      float acc = r == lane ? 1.f : 0.f;
+      float acc[4] = {r == lane ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s2 = 0; s2 < r; ++s2) acc -= A[r * LDA + s2] * x[s2];
-      x[r] = acc;
+      for (int s2 = 0; s2 < r; ++s2) acc[s2 & 3] -= A[r * LDA + s2] * x[s2];
+      x[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
     E* dst = static_cast<E*>(a.tmat) + cbase * static_cast<int64_t>(C * C);
 #pragma unroll
@@ -1539,6 +1541,9 @@ __global__ __launch_bounds__(256) void chunk_grad_f16_kernel(CArgs a) {
 #pragma unroll
   for (int t = 0; t < NCQ; ++t) dP[t] = dT[t] = zero4();
   float hh = 0.f;  // this thread's part of <dH, H0>
+  f32x4 psb[NT], psy[NT];  // this lane's column parts of the phase-A row sums
+#pragma unroll
+  for (int t = 0; t < NT; ++t) psb[t] = psy[t] = zero4();
   _Float16* H0T = pool;               // H0T[i][j]  = H0[i][jh + j]
   _Float16* dHT = H0T + DK * LDJ;     // dHT[i][j]  = dH[i][jh + j]
   _Float16* X0 = dHT + DK * LDJ;      // [C][LDJ]: dRHS, then dU
@@ -1600,12 +1605,8 @@ __global__ __launch_bounds__(256) void chunk_grad_f16_kernel(CArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * tr + 4 * g + e;
-        const float sb = xsum<1, 16>(dr[tr][e] * vmy[tr][e]);
-        const float sy = xsum<1, 16>(dr[tr][e] * y[tr][e]);
-        if (c16 == 0) {
-          sB[w][r] += sb;
-          sG[w][r] -= bet[r] * gam[r] * sy;
-        }
+        psb[tr][e] += dr[tr][e] * vmy[tr][e];
+        psy[tr][e] += dr[tr][e] * y[tr][e];
         X0[r * LDJ + jl] = static_cast<_Float16>(dr[tr][e]);
         X1b[r * LDJ + jl] = static_cast<_Float16>(dov[tr][e]);
         X2b[r * LDJ + jl] = static_cast<_Float16>(u[tr][e]);
@@ -1629,6 +1630,19 @@ __global__ __launch_bounds__(256) void chunk_grad_f16_kernel(CArgs a) {
     mma_cols<NCK, 64>(x3, X2b, LDJ, 16 * rt, dHT, LDJ, 16 * cq * NCK);
     mma_cols<NCQ, 64>(dT, X0, LDJ, 16 * rt, X1b, LDJ, 16 * cq * NCQ);
   }
+  // phase-A row sums: dbeta_r += sum_j dRHS (V - gam Y), dG_r -= beta gam sum_j dRHS Y
+#pragma unroll
+  for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * tr + 4 * g + e;
+      const float sb = row16_sum(psb[tr][e]);
+      const float sy = row16_sum(psy[tr][e]);
+      if (c16 == 0) {
+        sB[w][r] += sb;
+        sG[w][r] -= bet[r] * gam[r] * sy;
+      }
+    }
   __syncthreads();
 
   // ---- C x C stage
@@ -1637,6 +1651,7 @@ __global__ __launch_bounds__(256) void chunk_grad_f16_kernel(CArgs a) {
   _Float16* dPm = M1s + C * LDC;    // dPm[r][s]
   _Float16* dPmT = dPm + C * LDC;   // dPmT[s][r]
   _Float16* dAs = dPmT + C * LDC;   // symmetric dAm + dAm^T
+  float rowG[4] = {0.f, 0.f, 0.f, 0.f}, rowB[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's row parts
 #pragma unroll
   for (int cc = 0; cc < NCQ; ++cc) {
     const int s2 = 16 * (cq * NCQ + cc) + c16;
@@ -1649,8 +1664,7 @@ __global__ __launch_bounds__(256) void chunk_grad_f16_kernel(CArgs a) {
       const float pv = static_cast<float>(PsT[s2 * LDC + r]);      // P_rs
       const float m = s2 <= r ? exp2f(G2[r] - G2[s2]) : 0.f;
       const float dpp = dP[cc][e] * pv;
-      const float rs = xsum<1, 16>(dpp);
-      if (c16 == 0) sG[w][r] += rs;
+      rowG[e] += dpp;
       col += dpp;
       dPm[r * LDC + s2] = static_cast<_Float16>(dP[cc][e] * m);
     }
@@ -1687,13 +1701,9 @@ __global__ __launch_bounds__(256) void chunk_grad_f16_kernel(CArgs a) {
       const float ex = s2 < r ? exp2f(G2[r] - G2[s2]) : 0.f;
       const float dav = -da[cc][e] * ex;
       const float dam = dav * bet[r];
-      const float rb = xsum<1, 16>(dav * kk[cc][e]);
       const float ag = dam * kk[cc][e];
-      const float rg = xsum<1, 16>(ag);
-      if (c16 == 0) {
-        sB[w][r] += rb;
-        sG[w][r] += rg;
-      }
+      rowB[e] += dav * kk[cc][e];
+      rowG[e] += ag;
       col += ag;
       if (s2 < r) {
         dAs[r * LDC + s2] = static_cast<_Float16>(dam);
@@ -1726,15 +1736,23 @@ __global__ __launch_bounds__(256) void chunk_grad_f16_kernel(CArgs a) {
       const float qn = static_cast<float>(QsT[i2 * LDC + r]);
       const float kn = static_cast<float>(KsT[i2 * LDC + r]);
       const float t3 = lam[r] * kn * x3[ct][e];
-      const float rg = xsum<1, 16>(gam[r] * qn * x2[ct][e] - t3);
+      rowG[e] += gam[r] * qn * x2[ct][e] - t3;
       gcx += t3;
-      if (c16 == 0) sG[w][r] += rg;
       const float dqv = dq[ct][e] + gam[r] * x2[ct][e];
       const float dkv = dk[ct][e] + lam[r] * x3[ct][e] - bet[r] * gam[r] * x1[ct][e];
       if (r < L) {
         pq[static_cast<int64_t>(r) * rstride + i2] = dqv;
         pk[static_cast<int64_t>(r) * rstride + i2] = dkv;
       }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float rg = row16_sum(rowG[e]);
+    const float rb = row16_sum(rowB[e]);
+    if (c16 == 0) {
+      sG[w][16 * rt + 4 * g + e] += rg;
+      sB[w][16 * rt + 4 * g + e] += rb;
     }
   }
   hh = xsum<1, 64>(hh);
