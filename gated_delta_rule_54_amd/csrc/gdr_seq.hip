@@ -421,6 +421,69 @@ __global__ __launch_bounds__(64) void epilogue_kernel(Dims d, EpiArgs a) {
   }
 }
 
+// Dk = 128 epilogue: four rows (b, t, kh) per 256-thread block, one wave per
+// row, two consecutive elements per lane (8-byte partial loads).
+template <typename TI, typename TO, bool CW>
+__global__ __launch_bounds__(256) void epilogue128_kernel(Dims d, EpiArgs a) {
+  constexpr int D = 128;
+  const int lane = threadIdx.x & 63;
+  const int64_t id = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // (b*T + t)*Hk + kh
+  if (id >= d.B * d.T * d.Hk) return;
+  const int kh = static_cast<int>(id % d.Hk);
+  const int64_t bt = id / d.Hk;
+  const int grp = d.Hv / d.Hk;
+  const int64_t pstride = d.B * d.T * d.Hv;
+  const int i = 2 * lane;
+  for (int which = 0; which < 2; ++which) {
+    const float* part = which == 0 ? a.part_dq : a.part_dk;
+    const void* xin = which == 0 ? a.q : a.k;
+    void* xout = which == 0 ? a.dq : a.dk;
+    float s0 = 0.f, s1 = 0.f;
+    for (int gi = 0; gi < grp; ++gi) {
+      const int64_t row = bt * d.Hv + static_cast<int64_t>(kh) * grp + gi;
+      for (int sl = 0; sl < a.nslices; ++sl) {
+        const float2 pv = *reinterpret_cast<const float2*>(part + (sl * pstride + row) * D + i);
+        s0 += pv.x;
+        s1 += pv.y;
+      }
+    }
+    if (d.l2) {
+      const float x0 = ld1<TI>(static_cast<const TI*>(xin) + id * D + i);
+      const float x1 = ld1<TI>(static_cast<const TI*>(xin) + id * D + i + 1);
+      const float ss = xsum<16, 64>(row16_sum(x0 * x0 + x1 * x1));
+      const float r = rsqrtf(ss + kL2Eps);
+      const float sx = xsum<16, 64>(row16_sum((x0 * s0 + x1 * s1) * r));
+      s0 = r * (s0 - x0 * r * sx);
+      s1 = r * (s1 - x1 * r * sx);
+    }
+    st1<TO>(static_cast<TO*>(xout) + id * D + i, s0);
+    st1<TO>(static_cast<TO*>(xout) + id * D + i + 1, s1);
+  }
+  for (int gi = 0; gi < grp; ++gi) {
+    const int64_t row = bt * d.Hv + static_cast<int64_t>(kh) * grp + gi;
+    if (a.part_db && lane == 0) {
+      float sb = 0.f;
+      for (int sl = 0; sl < a.nslices; ++sl) sb += a.part_db[sl * pstride + row];
+      a.dbeta[row] = sb;
+    }
+    if (a.part_dg) {
+      if constexpr (CW) {
+        float g0 = 0.f, g1 = 0.f;
+        for (int sl = 0; sl < a.nslices; ++sl) {
+          g0 += a.part_dg[(sl * pstride + row) * D + i];
+          g1 += a.part_dg[(sl * pstride + row) * D + i + 1];
+        }
+        a.dg[row * D + i] = g0;
+        a.dg[row * D + i + 1] = g1;
+      } else if (lane == 0) {
+        float sg = 0.f;
+        for (int sl = 0; sl < a.nslices; ++sl) sg += a.part_dg[sl * pstride + row];
+        a.dg[row] = sg;
+      }
+    }
+  }
+}
+
 Dims dims_of(const Shape& s) { return Dims{s.B, s.T, s.Hk, s.Hv, s.l2norm ? 1 : 0}; }
 
 template <int D> constexpr int fwd_bv() { return D == 16 ? 16 : 32; }
@@ -449,6 +512,11 @@ template <int D, typename TI, typename TO, bool CW>
 hipError_t epi_go(const Shape& s, const EpiArgs& a, hipStream_t st) {
   const int64_t rows = s.B * s.T * s.Hk;
   ProfScope ps("bwd_epilogue", st);
+  if constexpr (D == 128) {
+    hipLaunchKernelGGL((epilogue128_kernel<TI, TO, CW>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, st,
+                       dims_of(s), a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((epilogue_kernel<D, TI, TO, CW>), dim3(static_cast<unsigned>(rows)), dim3(64), 0, st,
                      dims_of(s), a);
   return hipGetLastError();
