@@ -96,24 +96,6 @@ BwdPlan plan_seq_bwd(const Shape& s) {
   return w;
 }
 
-struct ChunkBwdPlan {
-  size_t tmat, pmat, hst, dhst, pdq, pdk, total;
-};
-
-ChunkBwdPlan plan_chunk_bwd(const Shape& s, int C) {
-  ChunkBwdPlan w{};
-  const size_t rows = static_cast<size_t>(s.B * s.T * s.Hv);
-  size_t off = 0;
-  w.tmat = off; off = align_up(off + gdr::chunk_tmat_bytes(s, C));
-  w.pmat = off; off = align_up(off + gdr::chunk_tmat_bytes(s, C));
-  w.hst = off;  off = align_up(off + gdr::chunk_state_bytes(s, C));
-  w.dhst = off; off = align_up(off + gdr::chunk_state_bytes(s, C));
-  w.pdq = off;  off = align_up(off + rows * s.D * 4);
-  w.pdk = off;  off = align_up(off + rows * s.D * 4);
-  w.total = off;
-  return w;
-}
-
 gdr_status hip_fail(hipError_t e) {
   g_last_hip_error = hipGetErrorString(e);
   return GDR_ERR_HIP;
@@ -151,7 +133,7 @@ gdr_status gdr_forward_workspace(const gdr_problem* p, size_t* bytes) {
   int algo;
   if ((st = resolve_algo(p, false, &algo)) != GDR_OK) return st;
   const Shape s = shape_of(p);
-  *bytes = (algo == GDR_ALGO_CHUNKED && s.B > 0 && s.T > 0) ? 2 * align_up(gdr::chunk_tmat_bytes(s, chunk_of(p))) : 0;
+  *bytes = (algo == GDR_ALGO_CHUNKED && s.B > 0 && s.T > 0) ? gdr::chunk_fwd_workspace(s, chunk_of(p)) : 0;
   return GDR_OK;
 }
 
@@ -163,7 +145,7 @@ gdr_status gdr_backward_workspace(const gdr_problem* p, size_t* bytes) {
   if ((st = resolve_algo(p, true, &algo)) != GDR_OK) return st;
   const Shape s = shape_of(p);
   *bytes = (s.B == 0 || s.T == 0) ? 0
-           : algo == GDR_ALGO_CHUNKED ? plan_chunk_bwd(s, chunk_of(p)).total : plan_seq_bwd(s).total;
+           : algo == GDR_ALGO_CHUNKED ? gdr::chunk_bwd_workspace(s, chunk_of(p)) : plan_seq_bwd(s).total;
   return GDR_OK;
 }
 
@@ -191,11 +173,10 @@ gdr_status gdr_forward(const gdr_problem* p, const void* q, const void* k, const
     return e == hipSuccess ? GDR_OK : hip_fail(e);
   }
   if (algo == GDR_ALGO_CHUNKED) {
-    const size_t tb = align_up(gdr::chunk_tmat_bytes(s, chunk_of(p)));
     if (!ws) return GDR_ERR_NULL_ARG;
-    if (ws_bytes < 2 * tb) return GDR_ERR_WORKSPACE_TOO_SMALL;
-    gdr::ChunkFwdArgs a{q, k, v, g, beta, h0, o, ht, ws, static_cast<char*>(ws) + tb};
-    hipError_t e = gdr::launch_chunk_fwd(s, chunk_of(p), a, stream);
+    if (ws_bytes < gdr::chunk_fwd_workspace(s, chunk_of(p))) return GDR_ERR_WORKSPACE_TOO_SMALL;
+    gdr::ChunkFwdArgs a{q, k, v, g, beta, h0, o, ht};
+    hipError_t e = gdr::launch_chunk_fwd(s, chunk_of(p), a, ws, stream);
     return e == hipSuccess ? GDR_OK : hip_fail(e);
   }
   gdr::SeqFwdArgs a{q, k, v, g, beta, h0, o, ht};
@@ -230,16 +211,10 @@ gdr_status gdr_backward(const gdr_problem* p, const void* q, const void* k, cons
   }
   if (algo == GDR_ALGO_CHUNKED) {
     const int C = chunk_of(p);
-    const ChunkBwdPlan w = plan_chunk_bwd(s, C);
     if (!ws) return GDR_ERR_NULL_ARG;
-    if (ws_bytes < w.total) return GDR_ERR_WORKSPACE_TOO_SMALL;
-    gdr::ChunkBwdArgs a{q, k, v, dout, g, beta, h0, dht, dv, dh0, at<void>(ws, w.tmat), at<void>(ws, w.pmat),
-                        at<void>(ws, w.hst), at<void>(ws, w.dhst), at<float>(ws, w.pdq), at<float>(ws, w.pdk),
-                        dg, dbeta};
-    hipError_t e = gdr::launch_chunk_bwd(s, C, a, stream);
-    if (e != hipSuccess) return hip_fail(e);
-    gdr::EpiArgs ea{q, k, a.pdq, a.pdk, nullptr, nullptr, 1, dq, dk, nullptr, nullptr};
-    e = gdr::launch_bwd_epilogue(s, ea, stream);
+    if (ws_bytes < gdr::chunk_bwd_workspace(s, C)) return GDR_ERR_WORKSPACE_TOO_SMALL;
+    gdr::ChunkBwdArgs a{q, k, v, dout, g, beta, h0, dht, dq, dk, dv, dg, dbeta, dh0};
+    hipError_t e = gdr::launch_chunk_bwd(s, C, a, ws, stream);
     return e == hipSuccess ? GDR_OK : hip_fail(e);
   }
   const BwdPlan w = plan_seq_bwd(s);

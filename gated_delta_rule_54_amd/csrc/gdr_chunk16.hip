@@ -1,0 +1,1206 @@
+// Chunked gated delta rule for bf16 io at Dk = Dv = 128 on gfx950: fp16
+// matrix-core operands (v_mfma_f32_16x16x32_f16), fp32 accumulation, fp32
+// carried state.  The chunk algebra is the one stated at the top of
+// gdr_chunk.hip (the chunk-parallel form behind the "chunked" VJP of the page
+// "Adding VJP for gated delta net", ml-explore/mlx pull request 4565).
+//
+// Work split:
+//   prep16   per (b, v-head, chunk), parallel.  Normalises the chunk's q / k
+//            rows, forms A and P on the matrix cores, inverts I + A, and
+//            writes the chunk's operands as fp16 "images": byte-exact copies
+//            of the padded LDS tiles the other kernels read.
+//              key image   per (b, k-head, chunk):  Kn [C][136] | KnT [128][C+8]
+//                          | Qn [C][136] (forward) or QnT [128][C+8] (VJP)
+//              chunk image per (b, v-head, chunk):  gam | lam | beta | log2(e) G
+//                          (4 x C fp32) | T | P (forward) or T | T^T | P^T (VJP),
+//                          each C x C tile [C][C+8]
+//            Normalisation, transposition and gate math thus happen once per
+//            chunk instead of once per consumer workgroup.
+//   chain16  per (b, v-head, 64-column value half): the sequential pass over
+//            chunks.  Wave w owns a 16-column strip of the state in MFMA
+//            accumulators.  Each chunk's images are copied into one of two LDS
+//            buffers by buffer_load_dwordx4 ... lds (no registers, no ALU)
+//            while the previous chunk computes; one barrier per chunk.
+//   dh16     the reverse pass carrying dH, same structure.
+//   grad16   per (b, v-head, chunk), parallel: every remaining gradient.
+//
+// Chained operands: a C x 16 (or 128 x 16) strip held in accumulators is fed
+// back as the B operand of the next product that contracts over its rows by
+// relabelling that product's k index, so that lane group g supplies rows
+// {4g..4g+3, 16+4g..16+4g+3} of each 32-row block - exactly the rows its
+// accumulators hold.  The LDS-side A operand is read with the same
+// relabelling (two 8-byte reads per fragment).
+//
+// Global traffic of the chain kernels goes through buffer resources whose
+// extent ends at the chunk's last valid row: loads past it return 0 and
+// stores past it are dropped, so ragged last chunks need no branches.
+
+#include <type_traits>
+
+#include "gdr_device.h"
+#include "gdr_internal.h"
+#include "gdr_mma.h"
+
+namespace gdr {
+namespace {
+
+constexpr int DK = 128;       // key dim == value dim
+constexpr int LDK = DK + 8;   // pitch (halves) of [*][DK] tiles
+constexpr int BV = 64;        // value columns per chain workgroup
+constexpr int NTK = DK / 16;  // 16-row tiles of a state strip
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Byte sizes of the images (all multiples of 16).
+template <int C>
+struct Img {
+  static constexpr int LDC = C + 8;                // pitch (halves) of [*][C] tiles
+  static constexpr uint32_t KN = C * LDK * 2;      // Kn or Qn    [C][LDK]
+  static constexpr uint32_t KT = DK * LDC * 2;     // KnT or QnT  [DK][LDC]
+  static constexpr uint32_t KEY_F = 2 * KN + KT;   // Kn | KnT | Qn
+  static constexpr uint32_t KEY_B = KN + 2 * KT;   // Kn | KnT | QnT
+  static constexpr uint32_t GT = 4 * C * 4;        // gam | lam | beta | G2
+  static constexpr uint32_t TM = C * LDC * 2;      // one C x C tile
+  static constexpr uint32_t CHK_F = GT + 2 * TM;   // gates | T | P
+  static constexpr uint32_t CHK_B = GT + 3 * TM;   // gates | T | T^T | P^T
+};
+
+struct K16 {
+  const bf16_t *q, *k, *v, *dout;
+  const float *g, *beta, *h0, *dht;
+  void* o;
+  float* ht;
+  void* dv;
+  float* dh0;
+  char *kimg, *cimg;       // [B][Hk][NC] key images, [B][Hv][NC] chunk images
+  _Float16 *hst, *dhst;    // [B][Hv][NC][DK][DK]: chunk-entry H, chunk-end dH
+  float *pdq, *pdk;        // [B][T][Hv][DK] per-v-head dq_hat / dk_hat
+  float *dg, *dbeta;       // [B][T][Hv]
+  int64_t B, T;
+  int Hk, Hv, NC, l2;
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(nbytes), 0x00020000);
+}
+
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Whole-workgroup copy of NBYTES from buffer r (byte offset off) into LDS at
+// dst, without registers: 16-byte unit e travels in lane e % 64 of wave
+// (e / 64) % 4 during round e / 256 (buffer_load_dwordx4 ... lds writes the
+// wave's 64 units to consecutive LDS addresses).  Completion is observed by
+// wait_all() followed by a barrier.
+template <int NBYTES>
+__device__ __forceinline__ void dma(rsrc_t r, uint32_t off, char* dst) {
+  static_assert(NBYTES % 16 == 0, "images are made of 16-byte units");
+  constexpr int N16 = NBYTES / 16;
+  const int tid = threadIdx.x, w = tid >> 6;
+#pragma unroll
+  for (int u = 0; u < (N16 + 255) / 256; ++u) {
+    const int e = 256 * u + tid;
+    if (N16 % 256 == 0 || e < N16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void)(dst + 16 * (256 * u + 64 * w)), 16, off + 16 * e, 0, 0,
+                                               0);
+  }
+}
+
+__device__ __forceinline__ f16x8 ld8(const _Float16* p) { return *reinterpret_cast<const f16x8*>(p); }
+
+// A fragment of A[m][k] (k contiguous) for the relabelled 32-column block kb:
+// elements 0..3 <- k = 32kb + 4g + 0..3, 4..7 <- 32kb + 16 + 4g + 0..3.
+__device__ __forceinline__ f16x8 perm_frag(const _Float16* A, int ld, int m, int kb) {
+  const int g = lane_id() >> 4;
+  const f16x4 lo = *reinterpret_cast<const f16x4*>(A + m * ld + 32 * kb + 4 * g);
+  const f16x4 hi = *reinterpret_cast<const f16x4*>(A + m * ld + 32 * kb + 16 + 4 * g);
+  return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Chained B fragments of a strip x[t][e] (rows 16t + 4g + e of this lane).
+template <int NT>
+__device__ __forceinline__ void chain_frags(f16x8 (&bf)[NT / 2], const f32x4 (&x)[NT]) {
+#pragma unroll
+  for (int kb = 0; kb < NT / 2; ++kb)
+    bf[kb] = f16x8{static_cast<_Float16>(x[2 * kb][0]), static_cast<_Float16>(x[2 * kb][1]),
+                   static_cast<_Float16>(x[2 * kb][2]), static_cast<_Float16>(x[2 * kb][3]),
+                   static_cast<_Float16>(x[2 * kb + 1][0]), static_cast<_Float16>(x[2 * kb + 1][1]),
+                   static_cast<_Float16>(x[2 * kb + 1][2]), static_cast<_Float16>(x[2 * kb + 1][3])};
+}
+
+// acc[t] += A[16t : 16t+16, 0 : 16 NT] X for t < NO, X chained as bf.
+template <int NO, int NT>
+__device__ __forceinline__ void mma_chain_rows(f32x4 (&acc)[NO], const _Float16* A, int ld, const f16x8 (&bf)[NT / 2]) {
+  const int m = lane_id() & 15;
+#pragma unroll
+  for (int kb = 0; kb < NT / 2; ++kb) {
+    f16x8 af[NO];
+#pragma unroll
+    for (int t = 0; t < NO; ++t) af[t] = perm_frag(A, ld, 16 * t + m, kb);
+#pragma unroll
+    for (int t = 0; t < NO; ++t) acc[t] = F16Op::mma(af[t], bf[kb], acc[t]);
+  }
+}
+
+// acc[t] += A[16t : 16t+16, 0:K] B, B^T rows n0..n0+15 read through a
+// row-contiguous view (element (n, k) at Bm[k * ldb + n]); B is shared.
+template <int NO, int K>
+__device__ __forceinline__ void mma_rows_bkmin(f32x4 (&acc)[NO], const _Float16* A, int lda, const _Float16* Bm,
+                                               int ldb, int n0) {
+  const int r = lane_id() & 15, kl = (lane_id() >> 4) * 8;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    f16x8 bfr;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bfr[i] = Bm[(k0 + kl + i) * ldb + n0 + r];
+    f16x8 af[NO];
+#pragma unroll
+    for (int t = 0; t < NO; ++t) af[t] = ld8(A + (16 * t + r) * lda + k0 + kl);
+#pragma unroll
+    for (int t = 0; t < NO; ++t) acc[t] = F16Op::mma(af[t], bfr, acc[t]);
+  }
+}
+
+// acc[t] += A[m0 : m0+16, 0:K] B[:, nb + 16t : nb + 16t + 16]; B^T rows from
+// Bt (k contiguous); the A fragment is shared.
+template <int NCOL, int K>
+__device__ __forceinline__ void mma_cols(f32x4 (&acc)[NCOL], const _Float16* A, int lda, int m0, const _Float16* Bt,
+                                         int ldb, int nb) {
+  const int r = lane_id() & 15, kl = (lane_id() >> 4) * 8;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const f16x8 af = ld8(A + (m0 + r) * lda + k0 + kl);
+    f16x8 bfr[NCOL];
+#pragma unroll
+    for (int t = 0; t < NCOL; ++t) bfr[t] = ld8(Bt + (nb + 16 * t + r) * ldb + k0 + kl);
+#pragma unroll
+    for (int t = 0; t < NCOL; ++t) acc[t] = F16Op::mma(af, bfr[t], acc[t]);
+  }
+}
+
+// Branch-free load of this lane's strip rows (16tr + 4g + e) of a bf16
+// [B,T,Hv,Dv] tensor at column jcol; rows >= L read as 0.
+template <int NT>
+__device__ __forceinline__ void load_strip(f32x4 (&x)[NT], const bf16_t* base, int64_t rstride, int L) {
+  const int g = lane_id() >> 4;
+#pragma unroll
+  for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * tr + 4 * g + e;
+      const float v = bf16_to_f32(base[(r < L ? r : L - 1) * rstride]);
+      x[tr][e] = r < L ? v : 0.f;
+    }
+}
+
+// This lane's strip rows 16tr + 4g + e of a bf16 tensor through buffer r
+// (rows rowb bytes apart, voff = byte offset of row 4g at the lane's
+// column), one raw bf16 per word so that nothing waits for the loads until
+// the values are used; rows past the buffer end read 0.
+template <int NT>
+__device__ __forceinline__ void load_strip_buf(uint32_t (&x)[NT][4], rsrc_t r, uint32_t voff, uint32_t rowb) {
+#pragma unroll
+  for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[tr][e] = __builtin_amdgcn_raw_buffer_load_b16(r, voff + (16 * tr + e) * rowb, 0, 0);
+}
+
+__device__ __forceinline__ void unpack_strip(float (&x)[4], const uint32_t (&w)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e] << 16);
+}
+
+// Stores this lane's strip rows (as load_strip_buf) as TO; rows past the
+// buffer end are dropped.
+template <typename TO, int NT>
+__device__ __forceinline__ void store_strip_buf(rsrc_t r, uint32_t voff, uint32_t rowb, const f32x4 (&x)[NT]) {
+#pragma unroll
+  for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t off = voff + (16 * tr + e) * rowb;
+      if constexpr (std::is_same_v<TO, float>) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[tr][e]), r, off, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[tr][e])), r, off, 0,
+                                              0);
+      }
+    }
+}
+
+// Chain workgroup -> (b, v-head, value half).  Workgroups are dealt to the
+// eight XCDs round robin; the remap puts the 2 * Hv / Hk workgroups that read
+// one key image (and the 2 that read one chunk image) on the same XCD, so
+// they share its L2.
+struct ChainPos {
+  int half, hv, kh;
+  int64_t b;
+};
+__device__ __forceinline__ ChainPos chain_pos(const K16& a) {
+  const int nb = gridDim.x, l0 = blockIdx.x;
+  const int lg = (nb % 8 == 0) ? (l0 % 8) * (nb / 8) + l0 / 8 : l0;
+  ChainPos p;
+  p.half = lg & 1;
+  p.hv = (lg >> 1) % a.Hv;
+  p.b = (lg >> 1) / a.Hv;
+  p.kh = p.hv / (a.Hv / a.Hk);
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// prep16: one workgroup (4 waves) per (chunk, v-head, b).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint4 sel4(bool ok, uint4 x) { return ok ? x : uint4{0u, 0u, 0u, 0u}; }
+
+__device__ __forceinline__ void unpack8(const uint4& u, float (&x)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// Rows of q or k (thread -> row tid / TPR, elements part * EPT ..), each
+// scaled by (sum x^2 + eps)^(-1/2) over Dk when l2 is set (the L2 norm the
+// Megatron-LM page folds into the kernel), written as fp16 to dst[r][LDK].
+template <int C, int NV>
+__device__ __forceinline__ void norm_rows(_Float16* dst, const uint4 (&raw)[NV], int l2) {
+  constexpr int TPR = 256 / C, EPT = DK / TPR;
+  const int tid = threadIdx.x, r = tid / TPR, part = tid % TPR;
+  float x[NV][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    unpack8(raw[u], x[u]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += x[u][i] * x[u][i];
+  }
+  ss = xsum<1, TPR>(ss);
+  const float rn = l2 ? rsqrtf(ss + kL2Eps) : 1.f;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    f16x8 h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(x[u][i] * rn);
+    *reinterpret_cast<f16x8*>(dst + r * LDK + part * EPT + 8 * u) = h;
+  }
+}
+
+// Writes an image tile of ROWS rows of UPR 16-byte units (the last unit of a
+// row is its zero pad) to global memory; f(row, unit) gives the 8 values.
+template <int ROWS, int UPR, typename F>
+__device__ __forceinline__ void write_tile(char* dst, F&& f) {
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  for (int e = threadIdx.x; e < ROWS * UPR; e += 256) {
+    const int r = e / UPR, u = e % UPR;
+    d[e] = u == UPR - 1 ? uint4{0u, 0u, 0u, 0u} : __builtin_bit_cast(uint4, f(r, u));
+  }
+}
+
+// T = (I + A)^-1 and P for one chunk and v-head; A (strictly lower) and P
+// from K K^T and Q K^T on the matrix cores.  The inverse is blocked in
+// 16 x 16 tiles: wave w inverts diagonal block w by forward substitution
+// (lane = column), then the blocks below the diagonal follow level by level,
+//     T_ij = -T_ii (sum_{k=j}^{i-1} A_ik T_kj),
+// on fp32 matrix cores; everything is fp32 until the images are written.
+template <int C, bool BWD>
+__global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
+  using IM = Img<C>;
+  constexpr int NT = C / 16, LDA = C + 4, LDC = IM::LDC;
+  constexpr int TPR = 256 / C, EPT = DK / TPR, NV = EPT / 8;
+  __shared__ __align__(16) _Float16 Ks[C * LDK];
+  __shared__ __align__(16) _Float16 Qs[C * LDK];
+  __shared__ __align__(16) float A[C * LDA];
+  __shared__ __align__(16) float Tf[C * LDA];
+  __shared__ __align__(16) _Float16 Pst[C * LDC];
+  __shared__ __align__(16) float gates[4 * C];  // gam | lam | beta | G2
+  float* gam = gates;
+  float* lam = gates + C;
+  float* bet = gates + 2 * C;
+  float* G2 = gates + 3 * C;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int c = blockIdx.x, hv = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int grp = a.Hv / a.Hk, kh = hv / grp;
+  const int64_t t0 = static_cast<int64_t>(c) * C;
+  const int L = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
+  {
+    const int r = tid / TPR, part = tid % TPR;
+    const int rc = r < L ? r : L - 1;
+    const int64_t off = ((b * a.T + t0 + rc) * a.Hk + kh) * DK + part * EPT;
+    uint4 kr[NV], qr[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      kr[u] = sel4(r < L, *reinterpret_cast<const uint4*>(a.k + off + 8 * u));
+      qr[u] = sel4(r < L, *reinterpret_cast<const uint4*>(a.q + off + 8 * u));
+    }
+    float gv = 0.f, bv = 0.f;
+    if (tid < 64) {
+      const int rr = tid < L ? tid : L - 1;
+      const int64_t row = (b * a.T + t0 + rr) * a.Hv + hv;
+      gv = a.g[row];
+      bv = a.beta[row];
+      gv = tid < L ? gv : 0.f;
+      bv = tid < L ? bv : 0.f;
+    }
+    norm_rows<C, NV>(Ks, kr, a.l2);
+    norm_rows<C, NV>(Qs, qr, a.l2);
+    if (tid < 64) {  // running sum G over the chunk (g = 0 past the end)
+      float x = gv;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      const float gc = __shfl(x, L - 1, 64);
+      if (lane < C) {
+        G2[lane] = x * kLog2e;
+        gam[lane] = expf(x);
+        lam[lane] = expf(gc - x);
+        bet[lane] = bv;
+      }
+    }
+  }
+  __syncthreads();
+  // A (fp32) and P (fp16) tiles; tile t = w + 4q of the NT x NT grid
+  for (int t = w; t < NT * NT; t += 4) {
+    const int tr = t / NT, tc = t % NT;
+    f32x4 kk = zero4(), qk = zero4();
+    if (tc <= tr) {
+      kk = mma_tile<F16Op, false, false>(zero4(), Ks, LDK, 16 * tr, Ks, LDK, 16 * tc, DK);
+      qk = mma_tile<F16Op, false, false>(zero4(), Qs, LDK, 16 * tr, Ks, LDK, 16 * tc, DK);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * tr + 4 * g + e, s2 = 16 * tc + c16;
+      const float ex = s2 <= r ? exp2f(G2[r] - G2[s2]) : 0.f;
+      A[r * LDA + s2] = s2 < r ? bet[r] * ex * kk[e] : 0.f;
+      Pst[r * LDC + s2] = static_cast<_Float16>(ex * qk[e]);
+    }
+  }
+  __syncthreads();
+  if (w < NT && lane < 16) {  // diagonal blocks
+    const int o = 16 * w;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc[2] = {r == lane ? 1.f : 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < r; ++s2) acc[s2 & 1] -= A[(o + r) * LDA + o + s2] * x[s2];
+      x[r] = acc[0] + acc[1];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Tf[(o + r) * LDA + o + lane] = x[r];
+  }
+  __syncthreads();
+  for (int d = 1; d < NT; ++d) {  // blocks below the diagonal, one distance at a time
+    const int i = d + w;
+    if (i < NT) {
+      const int j = i - d;
+      f32x4 m = zero4();
+      for (int k = j; k < i; ++k) {
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+          const float av = A[(16 * i + c16) * LDA + 16 * k + k0 + g];
+          const float bv = Tf[(16 * k + k0 + g) * LDA + 16 * j + c16];
+          m = F32Op::mma(av, bv, m);
+        }
+      }
+      // T_ij = -T_ii m; m's accumulators supply B(k = 4g + e, n) directly
+      f32x4 tij = zero4();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tij = F32Op::mma(Tf[(16 * i + c16) * LDA + 16 * i + 4 * g + e], m[e], tij);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Tf[(16 * i + 4 * g + e) * LDA + 16 * j + c16] = -tij[e];
+    }
+    __syncthreads();
+  }
+
+  // ---- chunk image
+  char* cim = a.cimg + ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(BWD ? IM::CHK_B : IM::CHK_F);
+  for (int e = tid; e < C; e += 256)
+    reinterpret_cast<float4*>(cim)[e] = reinterpret_cast<const float4*>(gates)[e];
+  constexpr int UC = C / 8 + 1;  // 16-byte units per [*][LDC] row
+  write_tile<C, UC>(cim + IM::GT, [&](int r, int u) {  // T, zero above the diagonal blocks
+    f16x8 v;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = static_cast<_Float16>((8 * u + q) / 16 <= r / 16 ? Tf[r * LDA + 8 * u + q] : 0.f);
+    return v;
+  });
+  if constexpr (!BWD) {
+    write_tile<C, UC>(cim + IM::GT + IM::TM, [&](int r, int u) { return ld8(Pst + r * LDC + 8 * u); });
+  } else {
+    write_tile<C, UC>(cim + IM::GT + IM::TM, [&](int s, int u) {  // T^T
+      f16x8 v;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = static_cast<_Float16>(s / 16 <= (8 * u + q) / 16 ? Tf[(8 * u + q) * LDA + s] : 0.f);
+      return v;
+    });
+    write_tile<C, UC>(cim + IM::GT + 2 * IM::TM, [&](int s, int u) {  // P^T
+      f16x8 v;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = Pst[(8 * u + q) * LDC + s];
+      return v;
+    });
+  }
+  // ---- key image (one v-head of each k-head group writes it)
+  if (hv % grp != 0) return;
+  char* kim = a.kimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(BWD ? IM::KEY_B : IM::KEY_F);
+  constexpr int UK = DK / 8 + 1;  // 16-byte units per [*][LDK] row
+  write_tile<C, UK>(kim, [&](int r, int u) { return ld8(Ks + r * LDK + 8 * u); });
+  write_tile<DK, UC>(kim + IM::KN, [&](int i, int u) {  // KnT
+    f16x8 v;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = Ks[(8 * u + q) * LDK + i];
+    return v;
+  });
+  if constexpr (!BWD) {
+    write_tile<C, UK>(kim + IM::KN + IM::KT, [&](int r, int u) { return ld8(Qs + r * LDK + 8 * u); });
+  } else {
+    write_tile<DK, UC>(kim + IM::KN + IM::KT, [&](int i, int u) {  // QnT
+      f16x8 v;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = Qs[(8 * u + q) * LDK + i];
+      return v;
+    });
+  }
+}
+
+// ---------------------------------------------------------------------------
+// chain16: forward pass over chunks (WRITE_O: outputs; STORE_H: every
+// chunk's entry state for the VJP).  Per chunk and wave:
+//   Y = Kn H, Z = Qn H          (16 MFMA each, H chained)
+//   U = T (beta (V - gam Y))    (8, chained)
+//   O = gam Z + P U             (8, chained)
+//   H = gam_C H + KnT (lam U)   (16, chained)
+// ---------------------------------------------------------------------------
+template <int C, typename TO, bool WRITE_O, bool STORE_H>
+__global__ __launch_bounds__(256) void chain16_kernel(K16 a) {
+  using IM = Img<C>;
+  constexpr int NT = C / 16, LDC = IM::LDC;
+  constexpr uint32_t CB = WRITE_O ? IM::GT + 2 * IM::TM : IM::GT + IM::TM;  // gates | T | P
+  constexpr uint32_t KB = WRITE_O ? 2 * IM::KN + IM::KT : IM::KN + IM::KT;  // Kn | KnT | Qn
+  constexpr uint32_t KSTR = WRITE_O ? IM::KEY_F : IM::KEY_B;
+  constexpr uint32_t CSTR = WRITE_O ? IM::CHK_F : IM::CHK_B;
+  __shared__ __align__(16) char bufA[CB + KB];
+  __shared__ __align__(16) char bufB[CB + KB];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const ChainPos p = chain_pos(a);
+  const int jcol = p.half * BV + 16 * w + c16;  // this lane's state column
+  const int64_t hbase = (p.b * a.Hv + p.hv) * DK * DK + jcol;
+  const char* kim0 = a.kimg + (p.b * a.Hk + p.kh) * a.NC * static_cast<int64_t>(KSTR);
+  const char* cim0 = a.cimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(CSTR);
+  const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;         // bf16 row pitch of v
+  const uint32_t rowo = static_cast<uint32_t>(a.Hv) * DK * sizeof(TO);  // row pitch of o
+  const uint32_t voffv = 4 * g * rowv + (p.hv * DK + jcol) * 2;
+  const uint32_t voffo = 4 * g * rowo + (p.hv * DK + jcol) * static_cast<uint32_t>(sizeof(TO));
+
+  f32x4 h[NTK];
+#pragma unroll
+  for (int ti = 0; ti < NTK; ++ti) {
+    h[ti] = zero4();
+    if (a.h0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[ti][e] = a.h0[hbase + (16 * ti + 4 * g + e) * DK];
+    }
+  }
+  auto rows_of = [&](int c) { return static_cast<int>(a.T - static_cast<int64_t>(c) * C < C ? a.T - static_cast<int64_t>(c) * C : C); };
+  auto seq_rsrc = [&](const void* base, int esize, int c, uint32_t rowb) {
+    const char* p0 = static_cast<const char*>(base) + (p.b * a.T + static_cast<int64_t>(c) * C) * a.Hv * DK * esize;
+    return make_rsrc(p0, static_cast<uint32_t>(rows_of(c)) * rowb);
+  };
+  auto stage = [&](int c, char* buf) {
+    dma<CB>(make_rsrc(cim0 + c * static_cast<int64_t>(CSTR), CB), 0, buf);
+    dma<KB>(make_rsrc(kim0 + c * static_cast<int64_t>(KSTR), KB), 0, buf + CB);
+  };
+
+  uint32_t vcur[NT][4], vnext[NT][4];
+  f32x4 o[NT];
+  stage(0, bufA);
+  load_strip_buf<NT>(vcur, seq_rsrc(a.v, 2, 0, rowv), voffv, rowv);
+  wait_all();
+  __syncthreads();
+
+  auto step = [&](int c, const char* cur, char* nxt) __attribute__((always_inline)) {
+    if (c + 1 < a.NC) {
+      stage(c + 1, nxt);
+      load_strip_buf<NT>(vnext, seq_rsrc(a.v, 2, c + 1, rowv), voffv, rowv);
+    }
+    if constexpr (WRITE_O) {  // previous chunk's outputs (their stores retire during this chunk)
+      if (c > 0) store_strip_buf<TO, NT>(seq_rsrc(a.o, sizeof(TO), c - 1, rowo), voffo, rowo, o);
+    }
+    if constexpr (STORE_H) {  // chunk entry state, natural [Dk][Dv] layout
+      const rsrc_t hr = make_rsrc(a.hst + ((p.b * a.Hv + p.hv) * a.NC + c) * static_cast<int64_t>(DK * DK), DK * DK * 2);
+#pragma unroll
+      for (int ti = 0; ti < NTK; ++ti)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<_Float16>(h[ti][e])), hr,
+                                                ((16 * ti + 4 * g + e) * DK + jcol) * 2, 0, 0);
+    }
+    const float* gam = reinterpret_cast<const float*>(cur);
+    const float* lam = gam + C;
+    const float* bet = gam + 2 * C;
+    const _Float16* Tm = reinterpret_cast<const _Float16*>(cur + IM::GT);
+    const _Float16* Pm = Tm + C * LDC;
+    const _Float16* Kn = reinterpret_cast<const _Float16*>(cur + CB);
+    const _Float16* KnT = Kn + C * LDK;
+    const _Float16* Qn = KnT + DK * LDC;
+
+    f16x8 hf[NTK / 2];
+    chain_frags<NTK>(hf, h);
+    f32x4 y[NT], u[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) y[t] = u[t] = zero4();
+    mma_chain_rows<NT, NTK>(y, Kn, LDK, hf);
+    if constexpr (WRITE_O) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) o[t] = zero4();
+      mma_chain_rows<NT, NTK>(o, Qn, LDK, hf);
+    }
+    f32x4 rhs[NT];
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) {
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * tr + 4 * g);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
+      float vv[4];
+      unpack_strip(vv, vcur[tr]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rhs[tr][e] = bv[e] * (vv[e] - gv[e] * y[tr][e]);
+        if constexpr (WRITE_O) o[tr][e] *= gv[e];
+      }
+    }
+    f16x8 bf[NT / 2];
+    chain_frags<NT>(bf, rhs);
+    mma_chain_rows<NT, NT>(u, Tm, LDC, bf);
+    if constexpr (WRITE_O) {
+      chain_frags<NT>(bf, u);
+      mma_chain_rows<NT, NT>(o, Pm, LDC, bf);
+    }
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) {
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(lam + 16 * tr + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[tr][e] *= lv[e];
+    }
+    chain_frags<NT>(bf, u);
+    const float gc = gam[rows_of(c) - 1];
+#pragma unroll
+    for (int ti = 0; ti < NTK; ++ti) h[ti] = h[ti] * gc;
+    mma_chain_rows<NTK, NT>(h, KnT, LDC, bf);
+    wait_all();
+    __syncthreads();
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vcur[tr][e] = vnext[tr][e];
+  };
+  for (int c = 0; c < a.NC; c += 2) {
+    step(c, bufA, bufB);
+    if (c + 1 < a.NC) step(c + 1, bufB, bufA);
+  }
+  if constexpr (WRITE_O) store_strip_buf<TO, NT>(seq_rsrc(a.o, sizeof(TO), a.NC - 1, rowo), voffo, rowo, o);
+  if (a.ht) {
+#pragma unroll
+    for (int ti = 0; ti < NTK; ++ti)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a.ht[hbase + (16 * ti + 4 * g + e) * DK] = h[ti][e];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dh16: reverse pass carrying dH.  Per chunk and wave:
+//   dU   = lam (Kn dH) + P^T dO           (16 + 8 MFMA, chained)
+//   dRHS = T^T dU                         (8, chained);  dv = beta dRHS
+//   dH   = gam_C dH + QnT (gam dO) - KnT (beta gam dRHS)   (16 + 16, chained)
+// Every chunk's incoming dH (the gradient at its end) is stored for grad16.
+// ---------------------------------------------------------------------------
+template <int C, typename TO>
+__global__ __launch_bounds__(256) void dh16_kernel(K16 a) {
+  using IM = Img<C>;
+  constexpr int NT = C / 16, LDC = IM::LDC;
+  constexpr uint32_t CB = IM::GT + 2 * IM::TM;  // gates | T^T | P^T
+  constexpr uint32_t KB = IM::KEY_B;            // Kn | KnT | QnT
+  __shared__ __align__(16) char bufA[CB + KB];
+  __shared__ __align__(16) char bufB[CB + KB];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const ChainPos p = chain_pos(a);
+  const int jcol = p.half * BV + 16 * w + c16;
+  const int64_t hbase = (p.b * a.Hv + p.hv) * DK * DK + jcol;
+  const char* kim0 = a.kimg + (p.b * a.Hk + p.kh) * a.NC * static_cast<int64_t>(IM::KEY_B);
+  const char* cim0 = a.cimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::CHK_B);
+  const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
+  const uint32_t rowo = static_cast<uint32_t>(a.Hv) * DK * sizeof(TO);
+  const uint32_t voffv = 4 * g * rowv + (p.hv * DK + jcol) * 2;
+  const uint32_t voffo = 4 * g * rowo + (p.hv * DK + jcol) * static_cast<uint32_t>(sizeof(TO));
+
+  f32x4 dh[NTK];
+#pragma unroll
+  for (int ti = 0; ti < NTK; ++ti) {
+    dh[ti] = zero4();
+    if (a.dht) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dh[ti][e] = a.dht[hbase + (16 * ti + 4 * g + e) * DK];
+    }
+  }
+  auto rows_of = [&](int c) { return static_cast<int>(a.T - static_cast<int64_t>(c) * C < C ? a.T - static_cast<int64_t>(c) * C : C); };
+  auto seq_rsrc = [&](const void* base, int esize, int c, uint32_t rowb) {
+    const char* p0 = static_cast<const char*>(base) + (p.b * a.T + static_cast<int64_t>(c) * C) * a.Hv * DK * esize;
+    return make_rsrc(p0, static_cast<uint32_t>(rows_of(c)) * rowb);
+  };
+  auto stage = [&](int c, char* buf) {
+    const char* cim = cim0 + c * static_cast<int64_t>(IM::CHK_B);
+    dma<IM::GT>(make_rsrc(cim, IM::GT), 0, buf);
+    dma<2 * IM::TM>(make_rsrc(cim + IM::GT + IM::TM, 2 * IM::TM), 0, buf + IM::GT);
+    dma<KB>(make_rsrc(kim0 + c * static_cast<int64_t>(IM::KEY_B), KB), 0, buf + CB);
+  };
+
+  uint32_t dcur[NT][4], dnext[NT][4];
+  f32x4 dvv[NT];
+  stage(a.NC - 1, bufA);
+  load_strip_buf<NT>(dcur, seq_rsrc(a.dout, 2, a.NC - 1, rowv), voffv, rowv);
+  wait_all();
+  __syncthreads();
+
+  auto step = [&](int c, const char* cur, char* nxt) __attribute__((always_inline)) {
+    if (c > 0) {
+      stage(c - 1, nxt);
+      load_strip_buf<NT>(dnext, seq_rsrc(a.dout, 2, c - 1, rowv), voffv, rowv);
+    }
+    if (c + 1 < a.NC) store_strip_buf<TO, NT>(seq_rsrc(a.dv, sizeof(TO), c + 1, rowo), voffo, rowo, dvv);
+    {  // gradient at this chunk's end, natural [Dk][Dv] layout
+      const rsrc_t hr = make_rsrc(a.dhst + ((p.b * a.Hv + p.hv) * a.NC + c) * static_cast<int64_t>(DK * DK), DK * DK * 2);
+#pragma unroll
+      for (int ti = 0; ti < NTK; ++ti)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<_Float16>(dh[ti][e])), hr,
+                                                ((16 * ti + 4 * g + e) * DK + jcol) * 2, 0, 0);
+    }
+    const float* gam = reinterpret_cast<const float*>(cur);
+    const float* lam = gam + C;
+    const float* bet = gam + 2 * C;
+    const _Float16* TmT = reinterpret_cast<const _Float16*>(cur + IM::GT);
+    const _Float16* PmT = TmT + C * LDC;
+    const _Float16* Kn = reinterpret_cast<const _Float16*>(cur + CB);
+    const _Float16* KnT = Kn + C * LDK;
+    const _Float16* QnT = KnT + DK * LDC;
+
+    f16x8 hf[NTK / 2];
+    chain_frags<NTK>(hf, dh);
+    f32x4 du[NT], dr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) du[t] = dr[t] = zero4();
+    mma_chain_rows<NT, NTK>(du, Kn, LDK, hf);
+    f32x4 dof[NT], gdo[NT];
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) {
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(lam + 16 * tr + 4 * g);
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * tr + 4 * g);
+      float x[4];
+      unpack_strip(x, dcur[tr]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        du[tr][e] *= lv[e];
+        dof[tr][e] = x[e];
+        gdo[tr][e] = gv[e] * x[e];
+      }
+    }
+    f16x8 bf[NT / 2];
+    chain_frags<NT>(bf, dof);
+    mma_chain_rows<NT, NT>(du, PmT, LDC, bf);
+    chain_frags<NT>(bf, du);
+    mma_chain_rows<NT, NT>(dr, TmT, LDC, bf);
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) {
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * tr + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dvv[tr][e] = bv[e] * dr[tr][e];
+        dr[tr][e] = -gv[e] * dvv[tr][e];
+      }
+    }
+    const float gc = gam[rows_of(c) - 1];
+#pragma unroll
+    for (int ti = 0; ti < NTK; ++ti) dh[ti] = dh[ti] * gc;
+    chain_frags<NT>(bf, gdo);
+    mma_chain_rows<NTK, NT>(dh, QnT, LDC, bf);
+    chain_frags<NT>(bf, dr);
+    mma_chain_rows<NTK, NT>(dh, KnT, LDC, bf);
+    wait_all();
+    __syncthreads();
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dcur[tr][e] = dnext[tr][e];
+  };
+  // chunks NC-1, NC-2, ... alternate between the two buffers
+  for (int i = 0; i < a.NC; i += 2) {
+    step(a.NC - 1 - i, bufA, bufB);
+    if (i + 1 < a.NC) step(a.NC - 2 - i, bufB, bufA);
+  }
+  store_strip_buf<TO, NT>(seq_rsrc(a.dv, sizeof(TO), 0, rowo), voffo, rowo, dvv);
+  if (a.dh0) {
+#pragma unroll
+    for (int ti = 0; ti < NTK; ++ti)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a.dh0[hbase + (16 * ti + 4 * g + e) * DK] = dh[ti][e];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// grad16: all gradients of one chunk except dv and dH, given its entry state
+// H0 and the gradient dH at its end (both [Dk][Dv] fp16).  The value dim is
+// walked in two halves of 64 columns; wave w owns the 16-column strip 16w..
+// of a half, so Y = K H0, X = K dH, U = T RHS, dU = lam X + P^T dO and
+// dRHS = T^T dU chain in registers.  The value-dim reductions
+//   X1 = dRHS H0^T, X2 = dO H0^T, dP = dO U^T   (phase 1)
+//   X3 = U dH^T, dT = dU RHS^T                  (phase 2)
+// read row-contiguous copies written to LDS.  Then the C x C stage
+// (dA = -T^T dT T^T), dq_hat and dk_hat of this v-head, dbeta and dg.
+// ---------------------------------------------------------------------------
+template <int C>
+__global__ __launch_bounds__(256) void grad16_kernel(K16 a) {
+  using IM = Img<C>;
+  constexpr int LDC = IM::LDC, NT = C / 16, LDJ = 64 + 8;
+  constexpr int WPR = 4 / NT;    // waves per row tile in the reductions
+  constexpr int NCK = 8 / WPR;   // Dk column tiles per wave
+  constexpr int NCQ = NT / WPR;  // C column tiles per wave
+  constexpr int POOL_HALF = 2 * DK * LDJ + 3 * C * LDJ;
+  constexpr int POOL_CC = 5 * C * LDC;
+  constexpr int POOL = POOL_HALF > POOL_CC ? POOL_HALF : POOL_CC;
+  __shared__ __align__(16) char img[IM::CHK_B + IM::KEY_B];
+  __shared__ __align__(16) _Float16 pool[POOL];
+  __shared__ float sG[4][C], sGc[4][C], sB[4][C], red[2][4];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int c = blockIdx.x, hv = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int kh = hv / (a.Hv / a.Hk);
+  const int64_t t0 = static_cast<int64_t>(c) * C;
+  const int L = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
+  const int64_t cbase = (b * a.Hv + hv) * a.NC + c;
+  const int rt = w % NT, cq = w / NT;  // reduction tile ownership
+
+  dma<IM::CHK_B>(make_rsrc(a.cimg + cbase * static_cast<int64_t>(IM::CHK_B), IM::CHK_B), 0, img);
+  dma<IM::KEY_B>(make_rsrc(a.kimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(IM::KEY_B), IM::KEY_B), 0,
+                 img + IM::CHK_B);
+  for (int e = tid; e < 4 * C; e += 256) {
+    sG[e / C][e % C] = 0.f;
+    sGc[e / C][e % C] = 0.f;
+    sB[e / C][e % C] = 0.f;
+  }
+  wait_all();
+  __syncthreads();
+  const float* gam = reinterpret_cast<const float*>(img);
+  const float* lam = gam + C;
+  const float* bet = gam + 2 * C;
+  const float* G2 = gam + 3 * C;
+  const _Float16* Ts = reinterpret_cast<const _Float16*>(img + IM::GT);
+  const _Float16* TsT = Ts + C * LDC;
+  const _Float16* PsT = TsT + C * LDC;
+  const _Float16* Ks = reinterpret_cast<const _Float16*>(img + IM::CHK_B);
+  const _Float16* KsT = Ks + C * LDK;
+  const _Float16* QsT = KsT + DK * LDC;
+  const float gamC = gam[L - 1];
+
+  f32x4 x1[NCK], x2[NCK], x3[NCK], dP[NCQ], dT[NCQ];
+#pragma unroll
+  for (int t = 0; t < NCK; ++t) x1[t] = x2[t] = x3[t] = zero4();
+#pragma unroll
+  for (int t = 0; t < NCQ; ++t) dP[t] = dT[t] = zero4();
+  float hh = 0.f;  // this thread's part of <dH, H0>
+  f32x4 psb[NT], psy[NT];  // this lane's column parts of the phase-A row sums
+#pragma unroll
+  for (int t = 0; t < NT; ++t) psb[t] = psy[t] = zero4();
+  _Float16* H0T = pool;               // H0T[i][j]  = H0[i][jh + j]
+  _Float16* dHT = H0T + DK * LDJ;     // dHT[i][j]  = dH[i][jh + j]
+  _Float16* X0 = dHT + DK * LDJ;      // [C][LDJ]: dRHS, then dU
+  _Float16* X1b = X0 + C * LDJ;       // [C][LDJ]: dO, then RHS
+  _Float16* X2b = X1b + C * LDJ;      // [C][LDJ]: U
+  const _Float16* hsrc = a.hst + cbase * static_cast<int64_t>(DK * DK);
+  const _Float16* dhsrc = a.dhst + cbase * static_cast<int64_t>(DK * DK);
+  const int64_t rstride = static_cast<int64_t>(a.Hv) * DK;
+
+  for (int jh = 0; jh < DK; jh += 64) {
+    __syncthreads();  // previous users of the pool (and the staging above) are done
+#pragma unroll
+    for (int u = 0; u < DK * 8 / 256; ++u) {
+      const int e = tid + 256 * u;
+      const int i = e / 8, q8 = e % 8;
+      const uint4 hv4 = *reinterpret_cast<const uint4*>(hsrc + i * DK + jh + 8 * q8);
+      const uint4 dv4 = *reinterpret_cast<const uint4*>(dhsrc + i * DK + jh + 8 * q8);
+      *reinterpret_cast<uint4*>(H0T + i * LDJ + 8 * q8) = hv4;
+      *reinterpret_cast<uint4*>(dHT + i * LDJ + 8 * q8) = dv4;
+      const _Float16* ph = reinterpret_cast<const _Float16*>(&hv4);
+      const _Float16* pd = reinterpret_cast<const _Float16*>(&dv4);
+#pragma unroll
+      for (int k2 = 0; k2 < 8; ++k2) hh += static_cast<float>(ph[k2]) * static_cast<float>(pd[k2]);
+    }
+    const int jcol = jh + 16 * w + c16;
+    f32x4 vv[NT], dov[NT];
+    load_strip<NT>(vv, static_cast<const bf16_t*>(a.v) + ((b * a.T + t0) * a.Hv + hv) * DK + jcol, rstride, L);
+    load_strip<NT>(dov, static_cast<const bf16_t*>(a.dout) + ((b * a.T + t0) * a.Hv + hv) * DK + jcol, rstride, L);
+    __syncthreads();
+
+    f32x4 y[NT], du[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) y[t] = du[t] = zero4();
+    mma_rows_bkmin<NT, DK>(y, Ks, LDK, H0T, LDJ, 16 * w);
+    mma_rows_bkmin<NT, DK>(du, Ks, LDK, dHT, LDJ, 16 * w);
+    f32x4 rhs[NT], vmy[NT];
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * tr + 4 * g + e;
+        vmy[tr][e] = vv[tr][e] - gam[r] * y[tr][e];
+        rhs[tr][e] = bet[r] * vmy[tr][e];
+        du[tr][e] *= lam[r];
+      }
+    f16x8 bf[NT / 2];
+    f32x4 u[NT], dr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) u[t] = dr[t] = zero4();
+    chain_frags<NT>(bf, rhs);
+    mma_chain_rows<NT, NT>(u, Ts, LDC, bf);
+    chain_frags<NT>(bf, dov);
+    mma_chain_rows<NT, NT>(du, PsT, LDC, bf);
+    chain_frags<NT>(bf, du);
+    mma_chain_rows<NT, NT>(dr, TsT, LDC, bf);
+    const int jl = 16 * w + c16;
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * tr + 4 * g + e;
+        psb[tr][e] += dr[tr][e] * vmy[tr][e];
+        psy[tr][e] += dr[tr][e] * y[tr][e];
+        X0[r * LDJ + jl] = static_cast<_Float16>(dr[tr][e]);
+        X1b[r * LDJ + jl] = static_cast<_Float16>(dov[tr][e]);
+        X2b[r * LDJ + jl] = static_cast<_Float16>(u[tr][e]);
+      }
+    __syncthreads();
+    // phase 1: X1 += dRHS H0^T, X2 += dO H0^T, dP += dO U^T
+    mma_cols<NCK, 64>(x1, X0, LDJ, 16 * rt, H0T, LDJ, 16 * cq * NCK);
+    mma_cols<NCK, 64>(x2, X1b, LDJ, 16 * rt, H0T, LDJ, 16 * cq * NCK);
+    mma_cols<NCQ, 64>(dP, X1b, LDJ, 16 * rt, X2b, LDJ, 16 * cq * NCQ);
+    __syncthreads();
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * tr + 4 * g + e;
+        X0[r * LDJ + jl] = static_cast<_Float16>(du[tr][e]);
+        X1b[r * LDJ + jl] = static_cast<_Float16>(rhs[tr][e]);
+      }
+    __syncthreads();
+    // phase 2: X3 += U dH^T, dT += dU RHS^T
+    mma_cols<NCK, 64>(x3, X2b, LDJ, 16 * rt, dHT, LDJ, 16 * cq * NCK);
+    mma_cols<NCQ, 64>(dT, X0, LDJ, 16 * rt, X1b, LDJ, 16 * cq * NCQ);
+  }
+  // phase-A row sums: dbeta_r += sum_j dRHS (V - gam Y), dG_r -= beta gam sum_j dRHS Y
+#pragma unroll
+  for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * tr + 4 * g + e;
+      const float sb = row16_sum(psb[tr][e]);
+      const float sy = row16_sum(psy[tr][e]);
+      if (c16 == 0) {
+        sB[w][r] += sb;
+        sG[w][r] -= bet[r] * gam[r] * sy;
+      }
+    }
+  __syncthreads();
+
+  // ---- C x C stage
+  _Float16* dTT = pool;             // dTT[s'][s] = dT[s][s']
+  _Float16* M1s = dTT + C * LDC;
+  _Float16* dPm = M1s + C * LDC;    // dPm[r][s]
+  _Float16* dPmT = dPm + C * LDC;   // dPmT[s][r]
+  _Float16* dAs = dPmT + C * LDC;   // symmetric dAm + dAm^T
+  float rowG[4] = {0.f, 0.f, 0.f, 0.f}, rowB[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's row parts
+#pragma unroll
+  for (int cc = 0; cc < NCQ; ++cc) {
+    const int s2 = 16 * (cq * NCQ + cc) + c16;
+    f16x4 t4;
+    float col = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * rt + 4 * g + e;
+      t4[e] = static_cast<_Float16>(dT[cc][e]);
+      const float pv = static_cast<float>(PsT[s2 * LDC + r]);      // P_rs
+      const float m = s2 <= r ? exp2f(G2[r] - G2[s2]) : 0.f;
+      const float dpp = dP[cc][e] * pv;
+      rowG[e] += dpp;
+      col += dpp;
+      dPm[r * LDC + s2] = static_cast<_Float16>(dP[cc][e] * m);
+    }
+    *reinterpret_cast<f16x4*>(dTT + s2 * LDC + 16 * rt + 4 * g) = t4;
+    f16x4 p4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p4[e] = dPm[(16 * rt + 4 * g + e) * LDC + s2];
+    *reinterpret_cast<f16x4*>(dPmT + s2 * LDC + 16 * rt + 4 * g) = p4;
+    col = xsum<16, 64>(col);
+    if (lane < 16) sGc[w][s2] += col;
+  }
+  __syncthreads();
+  f32x4 m1[NCQ];
+#pragma unroll
+  for (int cc = 0; cc < NCQ; ++cc) m1[cc] = zero4();
+  mma_cols<NCQ, C>(m1, TsT, LDC, 16 * rt, dTT, LDC, 16 * cq * NCQ);
+#pragma unroll
+  for (int cc = 0; cc < NCQ; ++cc)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) M1s[(16 * rt + 4 * g + e) * LDC + 16 * (cq * NCQ + cc) + c16] = static_cast<_Float16>(m1[cc][e]);
+  __syncthreads();
+  f32x4 da[NCQ], kk[NCQ];
+#pragma unroll
+  for (int cc = 0; cc < NCQ; ++cc) da[cc] = kk[cc] = zero4();
+  mma_cols<NCQ, C>(da, M1s, LDC, 16 * rt, Ts, LDC, 16 * cq * NCQ);
+  mma_cols<NCQ, DK>(kk, Ks, LDK, 16 * rt, Ks, LDK, 16 * cq * NCQ);
+#pragma unroll
+  for (int cc = 0; cc < NCQ; ++cc) {
+    const int s2 = 16 * (cq * NCQ + cc) + c16;
+    float col = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * rt + 4 * g + e;
+      const float ex = s2 < r ? exp2f(G2[r] - G2[s2]) : 0.f;
+      const float dav = -da[cc][e] * ex;
+      const float dam = dav * bet[r];
+      const float ag = dam * kk[cc][e];
+      rowB[e] += dav * kk[cc][e];
+      rowG[e] += ag;
+      col += ag;
+      if (s2 < r) {
+        dAs[r * LDC + s2] = static_cast<_Float16>(dam);
+        dAs[s2 * LDC + r] = static_cast<_Float16>(dam);
+      } else if (s2 == r) {
+        dAs[r * LDC + r] = static_cast<_Float16>(0.f);
+      }
+    }
+    col = xsum<16, 64>(col);
+    if (lane < 16) sGc[w][s2] += col;
+  }
+  __syncthreads();
+
+  // ---- dq, dk per v-head; X2 / X3 terms of dG
+  f32x4 dq[NCK], dk[NCK];
+#pragma unroll
+  for (int t = 0; t < NCK; ++t) dq[t] = dk[t] = zero4();
+  mma_cols<NCK, C>(dq, dPm, LDC, 16 * rt, KsT, LDC, 16 * cq * NCK);
+  mma_cols<NCK, C>(dk, dPmT, LDC, 16 * rt, QsT, LDC, 16 * cq * NCK);
+  mma_cols<NCK, C>(dk, dAs, LDC, 16 * rt, KsT, LDC, 16 * cq * NCK);
+  float gcx = 0.f;
+  float* pq = a.pdq + ((b * a.T + t0) * a.Hv + hv) * DK;
+  float* pk = a.pdk + ((b * a.T + t0) * a.Hv + hv) * DK;
+#pragma unroll
+  for (int ct = 0; ct < NCK; ++ct) {
+    const int i2 = 16 * (cq * NCK + ct) + c16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * rt + 4 * g + e;
+      const float qn = static_cast<float>(QsT[i2 * LDC + r]);
+      const float kn = static_cast<float>(KsT[i2 * LDC + r]);
+      const float t3 = lam[r] * kn * x3[ct][e];
+      rowG[e] += gam[r] * qn * x2[ct][e] - t3;
+      gcx += t3;
+      const float dqv = dq[ct][e] + gam[r] * x2[ct][e];
+      const float dkv = dk[ct][e] + lam[r] * x3[ct][e] - bet[r] * gam[r] * x1[ct][e];
+      if (r < L) {
+        pq[static_cast<int64_t>(r) * rstride + i2] = dqv;
+        pk[static_cast<int64_t>(r) * rstride + i2] = dkv;
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float rg = row16_sum(rowG[e]);
+    const float rb = row16_sum(rowB[e]);
+    if (c16 == 0) {
+      sG[w][16 * rt + 4 * g + e] += rg;
+      sB[w][16 * rt + 4 * g + e] += rb;
+    }
+  }
+  hh = xsum<1, 64>(hh);
+  gcx = xsum<1, 64>(gcx);
+  if (lane == 0) {
+    red[0][w] = hh;
+    red[1][w] = gcx;
+  }
+  __syncthreads();
+  if (w == 0) {
+    const int r = lane;
+    float dG = 0.f, dB = 0.f;
+    if (r < C) {
+      dG = sG[0][r] + sG[1][r] + sG[2][r] + sG[3][r] - (sGc[0][r] + sGc[1][r] + sGc[2][r] + sGc[3][r]);
+      dB = sB[0][r] + sB[1][r] + sB[2][r] + sB[3][r];
+    }
+    if (r == L - 1)
+      dG += gamC * (red[0][0] + red[0][1] + red[0][2] + red[0][3]) + (red[1][0] + red[1][1] + red[1][2] + red[1][3]);
+    if (r >= L) dG = 0.f;
+    float x = dG;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float yv = __shfl_down(x, off, 64);
+      if (lane + off < 64) x += yv;
+    }
+    if (r < L) {
+      const int64_t row = (b * a.T + t0 + r) * a.Hv + hv;
+      a.dg[row] = x;
+      a.dbeta[row] = dB;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Ws16 {
+  size_t kimg, cimg, hst, dhst, pdq, pdk, total;
+};
+
+template <int C>
+Ws16 plan16(const Shape& s, bool bwd) {
+  using IM = Img<C>;
+  const size_t nc = static_cast<size_t>((s.T + C - 1) / C);
+  const size_t nk = static_cast<size_t>(s.B) * s.Hk * nc, nv = static_cast<size_t>(s.B) * s.Hv * nc;
+  Ws16 w{};
+  size_t off = 0;
+  w.kimg = off; off = up(off + nk * (bwd ? IM::KEY_B : IM::KEY_F));
+  w.cimg = off; off = up(off + nv * (bwd ? IM::CHK_B : IM::CHK_F));
+  if (bwd) {
+    const size_t rows = static_cast<size_t>(s.B * s.T) * s.Hv;
+    w.hst = off;  off = up(off + nv * DK * DK * 2);
+    w.dhst = off; off = up(off + nv * DK * DK * 2);
+    w.pdq = off;  off = up(off + rows * DK * 4);
+    w.pdk = off;  off = up(off + rows * DK * 4);
+  }
+  w.total = off;
+  return w;
+}
+
+Ws16 plan_any(const Shape& s, int C, bool bwd) { return C == 64 ? plan16<64>(s, bwd) : plan16<32>(s, bwd); }
+
+K16 args16(const Shape& s, int C, void* ws, const Ws16& w) {
+  K16 a{};
+  a.B = s.B;
+  a.T = s.T;
+  a.Hk = s.Hk;
+  a.Hv = s.Hv;
+  a.NC = static_cast<int>((s.T + C - 1) / C);
+  a.l2 = s.l2norm ? 1 : 0;
+  char* base = static_cast<char*>(ws);
+  a.kimg = base + w.kimg;
+  a.cimg = base + w.cimg;
+  if (w.hst || w.dhst) {
+    a.hst = reinterpret_cast<_Float16*>(base + w.hst);
+    a.dhst = reinterpret_cast<_Float16*>(base + w.dhst);
+    a.pdq = reinterpret_cast<float*>(base + w.pdq);
+    a.pdk = reinterpret_cast<float*>(base + w.pdk);
+  }
+  return a;
+}
+
+template <int C, bool BWD>
+hipError_t prep16(const K16& a, hipStream_t st) {
+  ProfScope ps("chunk_prep", st);
+  hipLaunchKernelGGL((prep16_kernel<C, BWD>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int C, typename TO, bool WO, bool SH>
+hipError_t chain16(const K16& a, hipStream_t st) {
+  ProfScope ps(WO ? "chunk_fwd" : "chunk_states", st);
+  hipLaunchKernelGGL((chain16_kernel<C, TO, WO, SH>), dim3(static_cast<unsigned>(2 * a.Hv * a.B)), dim3(256), 0, st,
+                     a);
+  return hipGetLastError();
+}
+
+template <int C, typename TO>
+hipError_t dh16(const K16& a, hipStream_t st) {
+  ProfScope ps("chunk_dh", st);
+  hipLaunchKernelGGL((dh16_kernel<C, TO>), dim3(static_cast<unsigned>(2 * a.Hv * a.B)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int C>
+hipError_t grad16(const K16& a, hipStream_t st) {
+  ProfScope ps("chunk_grad", st);
+  hipLaunchKernelGGL((grad16_kernel<C>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int C, typename TO>
+hipError_t fwd_all(const Shape& s, const ChunkFwdArgs& x, void* ws, hipStream_t st) {
+  K16 a = args16(s, C, ws, plan16<C>(s, false));
+  a.q = static_cast<const bf16_t*>(x.q);
+  a.k = static_cast<const bf16_t*>(x.k);
+  a.v = static_cast<const bf16_t*>(x.v);
+  a.g = x.g;
+  a.beta = x.beta;
+  a.h0 = x.h0;
+  a.o = x.o;
+  a.ht = x.ht;
+  hipError_t e = prep16<C, false>(a, st);
+  return e == hipSuccess ? chain16<C, TO, true, false>(a, st) : e;
+}
+
+template <int C, typename TO>
+hipError_t bwd_all(const Shape& s, const ChunkBwdArgs& x, void* ws, hipStream_t st) {
+  K16 a = args16(s, C, ws, plan16<C>(s, true));
+  a.q = static_cast<const bf16_t*>(x.q);
+  a.k = static_cast<const bf16_t*>(x.k);
+  a.v = static_cast<const bf16_t*>(x.v);
+  a.dout = static_cast<const bf16_t*>(x.dout);
+  a.g = x.g;
+  a.beta = x.beta;
+  a.h0 = x.h0;
+  a.dht = x.dht;
+  a.dv = x.dv;
+  a.dh0 = x.dh0;
+  a.dg = x.dg;
+  a.dbeta = x.dbeta;
+  hipError_t e = prep16<C, true>(a, st);
+  if (e == hipSuccess) e = chain16<C, TO, false, true>(a, st);
+  if (e == hipSuccess) e = dh16<C, TO>(a, st);
+  if (e == hipSuccess) e = grad16<C>(a, st);
+  if (e != hipSuccess) return e;
+  EpiArgs ea{x.q, x.k, a.pdq, a.pdk, nullptr, nullptr, 1, x.dq, x.dk, nullptr, nullptr};
+  return launch_bwd_epilogue(s, ea, st);
+}
+
+}  // namespace
+
+size_t chunk16_fwd_workspace(const Shape& s, int C) { return plan_any(s, C, false).total; }
+size_t chunk16_bwd_workspace(const Shape& s, int C) { return plan_any(s, C, true).total; }
+
+hipError_t launch_chunk16_fwd(const Shape& s, int C, const ChunkFwdArgs& x, void* ws, hipStream_t st) {
+  if (C == 64) return s.out_bf16 ? fwd_all<64, bf16_t>(s, x, ws, st) : fwd_all<64, float>(s, x, ws, st);
+  if (C == 32) return s.out_bf16 ? fwd_all<32, bf16_t>(s, x, ws, st) : fwd_all<32, float>(s, x, ws, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk16_bwd(const Shape& s, int C, const ChunkBwdArgs& x, void* ws, hipStream_t st) {
+  if (C == 64) return s.out_bf16 ? bwd_all<64, bf16_t>(s, x, ws, st) : bwd_all<64, float>(s, x, ws, st);
+  if (C == 32) return s.out_bf16 ? bwd_all<32, bf16_t>(s, x, ws, st) : bwd_all<32, float>(s, x, ws, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

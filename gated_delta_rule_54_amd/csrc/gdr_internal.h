@@ -66,36 +66,35 @@ struct EpiArgs {
 hipError_t launch_bwd_epilogue(const Shape& s, const EpiArgs& a, hipStream_t st);
 
 // ---- chunked (matrix-core) path --------------------------------------------
-// fp16 matrix-core operands are used for bf16 io with Dk = 128 and C >= 32;
-// every other supported shape uses fp32 operands.
+// fp16 matrix-core operands are used for bf16 io with Dk = 128 and C >= 32
+// (gdr_chunk16.hip); every other supported shape uses fp32 operands
+// (gdr_chunk.hip).  Each implementation sizes and carves its own workspace.
 bool chunk_uses_f16(const Shape& s, int C);
-size_t chunk_tmat_bytes(const Shape& s, int C);   // T = (I + A)^-1 per chunk
-size_t chunk_state_bytes(const Shape& s, int C);  // one Dk x Dv matrix per chunk
+size_t chunk_fwd_workspace(const Shape& s, int C);
+size_t chunk_bwd_workspace(const Shape& s, int C);
 
 struct ChunkFwdArgs {
   const void *q, *k, *v;
   const float *g, *beta, *h0;
   void* o;
   float* ht;
-  void* tmat;  // chunk_tmat_bytes
-  void* pmat;  // chunk_tmat_bytes (masked, gate-scaled q.k per chunk)
 };
-hipError_t launch_chunk_fwd(const Shape& s, int C, const ChunkFwdArgs& a, hipStream_t st);
+hipError_t launch_chunk_fwd(const Shape& s, int C, const ChunkFwdArgs& a, void* ws, hipStream_t st);
 
-// VJP: recomputes T and every chunk's entry state, runs the reverse dH pass
-// (writes dv, dh0) and the per-chunk gradient pass (writes dg, dbeta and
-// per-v-head dq_hat / dk_hat for the epilogue).
+// VJP: recomputes every chunk's entry state, runs the reverse dH pass
+// (writes dv, dh0), the per-chunk gradient pass (dg, dbeta, per-v-head
+// dq_hat / dk_hat) and the epilogue (dq, dk).
 struct ChunkBwdArgs {
   const void *q, *k, *v, *dout;
   const float *g, *beta, *h0, *dht;
-  void* dv;
-  float* dh0;
-  void* tmat;        // chunk_tmat_bytes
-  void* pmat;        // chunk_tmat_bytes
-  void *hst, *dhst;  // chunk_state_bytes each
-  float *pdq, *pdk;  // [B][T][Hv][Dk]
-  float *dg, *dbeta;
+  void *dq, *dk, *dv;
+  float *dg, *dbeta, *dh0;
 };
-hipError_t launch_chunk_bwd(const Shape& s, int C, const ChunkBwdArgs& a, hipStream_t st);
+hipError_t launch_chunk_bwd(const Shape& s, int C, const ChunkBwdArgs& a, void* ws, hipStream_t st);
+
+size_t chunk16_fwd_workspace(const Shape& s, int C);
+size_t chunk16_bwd_workspace(const Shape& s, int C);
+hipError_t launch_chunk16_fwd(const Shape& s, int C, const ChunkFwdArgs& a, void* ws, hipStream_t st);
+hipError_t launch_chunk16_bwd(const Shape& s, int C, const ChunkBwdArgs& a, void* ws, hipStream_t st);
 
 }  // namespace gdr
