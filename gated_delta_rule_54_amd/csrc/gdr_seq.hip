@@ -421,61 +421,99 @@ __global__ __launch_bounds__(64) void epilogue_kernel(Dims d, EpiArgs a) {
   }
 }
 
-// Dk = 128 epilogue: four rows (b, t, kh) per 256-thread block, one wave per
-// row, two consecutive elements per lane (8-byte partial loads).
+// Dk = 128 epilogue: one 16-lane DPP row per (row (b, t, kh), dq or dk),
+// eight consecutive elements per lane (16-byte input loads, 32-byte partial
+// loads), so a 256-thread block covers 8 rows; the row reductions of the
+// L2-norm VJP are DPP row sums.  dbeta / dg partials (sequential path) are
+// summed by the dq groups.
+template <typename T> __device__ __forceinline__ void ld8f(const T* p, float (&x)[8]);
+template <> __device__ __forceinline__ void ld8f<float>(const float* p, float (&x)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+template <> __device__ __forceinline__ void ld8f<bf16_t>(const bf16_t* p, float (&x)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(w[k] << 16);
+    x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+  }
+}
+template <typename T> __device__ __forceinline__ void st8(T* p, const float (&x)[8]);
+template <> __device__ __forceinline__ void st8<float>(float* p, const float (&x)[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+}
+template <> __device__ __forceinline__ void st8<bf16_t>(bf16_t* p, const float (&x)[8]) {
+  uint4 u;
+  uint32_t* w = reinterpret_cast<uint32_t*>(&u);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = static_cast<uint32_t>(f32_to_bf16(x[2 * k])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * k + 1])) << 16);
+  *reinterpret_cast<uint4*>(p) = u;
+}
+
 template <typename TI, typename TO, bool CW>
 __global__ __launch_bounds__(256) void epilogue128_kernel(Dims d, EpiArgs a) {
   constexpr int D = 128;
-  const int lane = threadIdx.x & 63;
-  const int64_t id = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // (b*T + t)*Hk + kh
-  if (id >= d.B * d.T * d.Hk) return;
+  const int sub = threadIdx.x & 15;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int64_t rows = d.B * d.T * d.Hk;
+  if (item >= 2 * rows) return;  // whole 16-lane groups leave together
+  const int which = static_cast<int>(item & 1);
+  const int64_t id = item >> 1;  // (b*T + t)*Hk + kh
   const int kh = static_cast<int>(id % d.Hk);
   const int64_t bt = id / d.Hk;
   const int grp = d.Hv / d.Hk;
   const int64_t pstride = d.B * d.T * d.Hv;
-  const int i = 2 * lane;
-  for (int which = 0; which < 2; ++which) {
-    const float* part = which == 0 ? a.part_dq : a.part_dk;
-    const void* xin = which == 0 ? a.q : a.k;
-    void* xout = which == 0 ? a.dq : a.dk;
-    float s0 = 0.f, s1 = 0.f;
-    for (int gi = 0; gi < grp; ++gi) {
-      const int64_t row = bt * d.Hv + static_cast<int64_t>(kh) * grp + gi;
-      for (int sl = 0; sl < a.nslices; ++sl) {
-        const float2 pv = *reinterpret_cast<const float2*>(part + (sl * pstride + row) * D + i);
-        s0 += pv.x;
-        s1 += pv.y;
-      }
-    }
-    if (d.l2) {
-      const float x0 = ld1<TI>(static_cast<const TI*>(xin) + id * D + i);
-      const float x1 = ld1<TI>(static_cast<const TI*>(xin) + id * D + i + 1);
-      const float ss = xsum<16, 64>(row16_sum(x0 * x0 + x1 * x1));
-      const float r = rsqrtf(ss + kL2Eps);
-      const float sx = xsum<16, 64>(row16_sum((x0 * s0 + x1 * s1) * r));
-      s0 = r * (s0 - x0 * r * sx);
-      s1 = r * (s1 - x1 * r * sx);
-    }
-    st1<TO>(static_cast<TO*>(xout) + id * D + i, s0);
-    st1<TO>(static_cast<TO*>(xout) + id * D + i + 1, s1);
-  }
+  const int i = 8 * sub;
+  const float* part = which == 0 ? a.part_dq : a.part_dk;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int gi = 0; gi < grp; ++gi) {
     const int64_t row = bt * d.Hv + static_cast<int64_t>(kh) * grp + gi;
-    if (a.part_db && lane == 0) {
+    for (int sl = 0; sl < a.nslices; ++sl) {
+      float pv[8];
+      ld8f<float>(part + (sl * pstride + row) * D + i, pv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] += pv[e];
+    }
+  }
+  if (d.l2) {
+    float x[8];
+    ld8f<TI>(static_cast<const TI*>(which == 0 ? a.q : a.k) + id * D + i, x);
+    float ss = 0.f, sx = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ss += x[e] * x[e];
+      sx += x[e] * s[e];
+    }
+    ss = row16_sum(ss);
+    sx = row16_sum(sx);
+    const float r = rsqrtf(ss + kL2Eps);
+    sx *= r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = r * (s[e] - x[e] * r * sx);
+  }
+  st8<TO>(static_cast<TO*>(which == 0 ? a.dq : a.dk) + id * D + i, s);
+  if (which != 0) return;
+  for (int gi = 0; gi < grp; ++gi) {
+    const int64_t row = bt * d.Hv + static_cast<int64_t>(kh) * grp + gi;
+    if (a.part_db && sub == 0) {
       float sb = 0.f;
       for (int sl = 0; sl < a.nslices; ++sl) sb += a.part_db[sl * pstride + row];
       a.dbeta[row] = sb;
     }
     if (a.part_dg) {
       if constexpr (CW) {
-        float g0 = 0.f, g1 = 0.f;
+        float gsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int sl = 0; sl < a.nslices; ++sl) {
-          g0 += a.part_dg[(sl * pstride + row) * D + i];
-          g1 += a.part_dg[(sl * pstride + row) * D + i + 1];
+          float pv[8];
+          ld8f<float>(a.part_dg + (sl * pstride + row) * D + i, pv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gsum[e] += pv[e];
         }
-        a.dg[row * D + i] = g0;
-        a.dg[row * D + i + 1] = g1;
-      } else if (lane == 0) {
+        st8<float>(a.dg + row * D + i, gsum);
+      } else if (sub == 0) {
         float sg = 0.f;
         for (int sl = 0; sl < a.nslices; ++sl) sg += a.part_dg[sl * pstride + row];
         a.dg[row] = sg;
@@ -513,8 +551,8 @@ hipError_t epi_go(const Shape& s, const EpiArgs& a, hipStream_t st) {
   const int64_t rows = s.B * s.T * s.Hk;
   ProfScope ps("bwd_epilogue", st);
   if constexpr (D == 128) {
-    hipLaunchKernelGGL((epilogue128_kernel<TI, TO, CW>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, st,
-                       dims_of(s), a);
+    hipLaunchKernelGGL((epilogue128_kernel<TI, TO, CW>), dim3(static_cast<unsigned>((2 * rows + 15) / 16)), dim3(256), 0,
+                       st, dims_of(s), a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((epilogue_kernel<D, TI, TO, CW>), dim3(static_cast<unsigned>(rows)), dim3(64), 0, st,
