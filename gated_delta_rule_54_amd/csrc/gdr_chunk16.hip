@@ -91,21 +91,21 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t nbytes) {
 
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Whole-workgroup copy of NBYTES from buffer r (byte offset off) into LDS at
-// dst, without registers: 16-byte unit e travels in lane e % 64 of wave
-// (e / 64) % 4 during round e / 256 (buffer_load_dwordx4 ... lds writes the
-// wave's 64 units to consecutive LDS addresses).  Completion is observed by
-// wait_all() followed by a barrier.
-template <int NBYTES>
+// Whole-workgroup (NTH threads) copy of NBYTES from buffer r (byte offset
+// off) into LDS at dst, without registers: 16-byte unit e travels in lane
+// e % 64 of wave (e / 64) % (NTH / 64) during round e / NTH
+// (buffer_load_dwordx4 ... lds writes the wave's 64 units to consecutive LDS
+// addresses).  Completion is observed by wait_all() followed by a barrier.
+template <int NBYTES, int NTH = 256>
 __device__ __forceinline__ void dma(rsrc_t r, uint32_t off, char* dst) {
   static_assert(NBYTES % 16 == 0, "images are made of 16-byte units");
   constexpr int N16 = NBYTES / 16;
   const int tid = threadIdx.x, w = tid >> 6;
 #pragma unroll
-  for (int u = 0; u < (N16 + 255) / 256; ++u) {
-    const int e = 256 * u + tid;
-    if (N16 % 256 == 0 || e < N16)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void)(dst + 16 * (256 * u + 64 * w)), 16, off + 16 * e, 0, 0,
+  for (int u = 0; u < (N16 + NTH - 1) / NTH; ++u) {
+    const int e = NTH * u + tid;
+    if (N16 % NTH == 0 || e < N16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void)(dst + 16 * (NTH * u + 64 * w)), 16, off + 16 * e, 0, 0,
                                                0);
   }
 }
@@ -761,28 +761,51 @@ __global__ __launch_bounds__(256) void dh16_kernel(K16 a) {
 
 // ---------------------------------------------------------------------------
 // grad16: all gradients of one chunk except dv and dH, given its entry state
-// H0 and the gradient dH at its end (both [Dk][Dv] fp16).  The value dim is
-// walked in two halves of 64 columns; wave w owns the 16-column strip 16w..
-// of a half, so Y = K H0, X = K dH, U = T RHS, dU = lam X + P^T dO and
-// dRHS = T^T dU chain in registers.  The value-dim reductions
-//   X1 = dRHS H0^T, X2 = dO H0^T, dP = dO U^T   (phase 1)
-//   X3 = U dH^T, dT = dU RHS^T                  (phase 2)
-// read row-contiguous copies written to LDS.  Then the C x C stage
-// (dA = -T^T dT T^T), dq_hat and dk_hat of this v-head, dbeta and dg.
+// H0 and the gradient dH at its end (both [Dk][Dv] fp16).  Eight waves.
+//   Phase A  wave w owns the 16-column value strip jw = 16w .. 16w+15 and
+//            chains in registers Y = K H0, X = K dH, U = T RHS,
+//            dU = lam X + P^T dO, dRHS = T^T dU; it writes dRHS, dO and U
+//            (then dU, RHS) as row-major [C][Dv] copies to LDS.
+//   Phase 1  X1 = dRHS H0^T, X2 = dO H0^T (wave w: Dk tile w, all rows),
+//            dP = dO U^T (C x C tiles dealt to the waves).
+//   Phase 2  X3 = U dH^T, dT = dU RHS^T.
+//   Then the C x C stage (dA = -T^T dT T^T), dq_hat / dk_hat of this v-head
+//   (wave w: Dk tile w), dbeta and dg.  H0 / dH are read straight from
+//   global memory: as chained strips for phase A and as row fragments for
+//   phases 1 and 2.
 // ---------------------------------------------------------------------------
+template <int NO, int K>
+__device__ __forceinline__ void mma_rows(f32x4 (&acc)[NO], const _Float16* A, int lda, const _Float16* Bt, int ldb,
+                                         int n0) {
+  const int r = lane_id() & 15, kl = (lane_id() >> 4) * 8;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const f16x8 bfr = ld8(Bt + (n0 + r) * ldb + k0 + kl);
+    f16x8 af[NO];
+#pragma unroll
+    for (int t = 0; t < NO; ++t) af[t] = ld8(A + (16 * t + r) * lda + k0 + kl);
+#pragma unroll
+    for (int t = 0; t < NO; ++t) acc[t] = F16Op::mma(af[t], bfr, acc[t]);
+  }
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ _Float16 h_of(uint32_t u) { return __builtin_bit_cast(_Float16, static_cast<uint16_t>(u)); }
+
 template <int C>
-__global__ __launch_bounds__(256) void grad16_kernel(K16 a) {
+__global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   using IM = Img<C>;
-  constexpr int LDC = IM::LDC, NT = C / 16, LDJ = 64 + 8;
-  constexpr int WPR = 4 / NT;    // waves per row tile in the reductions
-  constexpr int NCK = 8 / WPR;   // Dk column tiles per wave
-  constexpr int NCQ = NT / WPR;  // C column tiles per wave
-  constexpr int POOL_HALF = 2 * DK * LDJ + 3 * C * LDJ;
-  constexpr int POOL_CC = 5 * C * LDC;
-  constexpr int POOL = POOL_HALF > POOL_CC ? POOL_HALF : POOL_CC;
+  constexpr int NW = 8;
+  constexpr int LDC = IM::LDC, NT = C / 16, LDX = DK + 8;
+  constexpr int NQ = NT * NT;                    // C x C tiles
+  constexpr int DPW = NQ >= NW ? NQ / NW : 1;    // C x C tiles per wave, all in one row tile
+  constexpr int XB = 3 * C * LDX;
+  static_assert(5 * C * LDC <= XB, "C x C stage buffers alias the strip buffers");
   __shared__ __align__(16) char img[IM::CHK_B + IM::KEY_B];
-  __shared__ __align__(16) _Float16 pool[POOL];
-  __shared__ float sG[4][C], sGc[4][C], sB[4][C], red[2][4];
+  __shared__ __align__(16) _Float16 xb[XB];
+  __shared__ float sG[NW][C], sGc[NW][C], sB[NW][C], red[2][NW];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int c = blockIdx.x, hv = blockIdx.y;
@@ -791,12 +814,41 @@ __global__ __launch_bounds__(256) void grad16_kernel(K16 a) {
   const int64_t t0 = static_cast<int64_t>(c) * C;
   const int L = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
   const int64_t cbase = (b * a.Hv + hv) * a.NC + c;
-  const int rt = w % NT, cq = w / NT;  // reduction tile ownership
+  const int jw = 16 * w + c16;         // phase A value column
+  const int i2 = 16 * w + c16;         // phase 1/2 and dq/dk key row
+  const bool qact = w * DPW < NQ;      // this wave owns C x C tiles
+  const int qr = (w * DPW) / NT, qc0 = (w * DPW) % NT;
 
-  dma<IM::CHK_B>(make_rsrc(a.cimg + cbase * static_cast<int64_t>(IM::CHK_B), IM::CHK_B), 0, img);
-  dma<IM::KEY_B>(make_rsrc(a.kimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(IM::KEY_B), IM::KEY_B), 0,
-                 img + IM::CHK_B);
-  for (int e = tid; e < 4 * C; e += 256) {
+  dma<IM::CHK_B, 512>(make_rsrc(a.cimg + cbase * static_cast<int64_t>(IM::CHK_B), IM::CHK_B), 0, img);
+  dma<IM::KEY_B, 512>(make_rsrc(a.kimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(IM::KEY_B), IM::KEY_B),
+                      0, img + IM::CHK_B);
+  // H0 / dH: chained strips (rows 16ti + 4g + e, column jw) and row fragments
+  // (row i2, columns 32ks + 8g ..) straight from global memory
+  const rsrc_t hr = make_rsrc(a.hst + cbase * static_cast<int64_t>(DK * DK), DK * DK * 2);
+  const rsrc_t dhr = make_rsrc(a.dhst + cbase * static_cast<int64_t>(DK * DK), DK * DK * 2);
+  uint32_t h0u[NTK][4], dhu[NTK][4];
+#pragma unroll
+  for (int ti = 0; ti < NTK; ++ti)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t off = ((16 * ti + 4 * g + e) * DK + jw) * 2;
+      h0u[ti][e] = __builtin_amdgcn_raw_buffer_load_b16(hr, off, 0, 0);
+      dhu[ti][e] = __builtin_amdgcn_raw_buffer_load_b16(dhr, off, 0, 0);
+    }
+  u32x4 h0r[DK / 32], dhrw[DK / 32];
+#pragma unroll
+  for (int ks = 0; ks < DK / 32; ++ks) {
+    const uint32_t off = (i2 * DK + 32 * ks + 8 * g) * 2;
+    h0r[ks] = __builtin_amdgcn_raw_buffer_load_b128(hr, off, 0, 0);
+    dhrw[ks] = __builtin_amdgcn_raw_buffer_load_b128(dhr, off, 0, 0);
+  }
+  const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
+  const uint32_t voffv = 4 * g * rowv + (hv * DK + jw) * 2;
+  const int64_t seq0 = (b * a.T + t0) * a.Hv * DK;
+  uint32_t vraw[NT][4], draw[NT][4];
+  load_strip_buf<NT>(vraw, make_rsrc(a.v + seq0, static_cast<uint32_t>(L) * rowv), voffv, rowv);
+  load_strip_buf<NT>(draw, make_rsrc(a.dout + seq0, static_cast<uint32_t>(L) * rowv), voffv, rowv);
+  for (int e = tid; e < NW * C; e += 512) {
     sG[e / C][e % C] = 0.f;
     sGc[e / C][e % C] = 0.f;
     sB[e / C][e % C] = 0.f;
@@ -814,103 +866,69 @@ __global__ __launch_bounds__(256) void grad16_kernel(K16 a) {
   const _Float16* KsT = Ks + C * LDK;
   const _Float16* QsT = KsT + DK * LDC;
   const float gamC = gam[L - 1];
+  _Float16* X0 = xb;             // dRHS, then dU
+  _Float16* X1b = xb + C * LDX;  // dO, then RHS
+  _Float16* X2b = X1b + C * LDX; // U
 
-  f32x4 x1[NCK], x2[NCK], x3[NCK], dP[NCQ], dT[NCQ];
+  // ---- phase A
+  f16x8 h0f[NTK / 2], dhf[NTK / 2];
+  float hh = 0.f;  // this lane's part of <dH, H0>
 #pragma unroll
-  for (int t = 0; t < NCK; ++t) x1[t] = x2[t] = x3[t] = zero4();
+  for (int kb = 0; kb < NTK / 2; ++kb) {
 #pragma unroll
-  for (int t = 0; t < NCQ; ++t) dP[t] = dT[t] = zero4();
-  float hh = 0.f;  // this thread's part of <dH, H0>
-  f32x4 psb[NT], psy[NT];  // this lane's column parts of the phase-A row sums
-#pragma unroll
-  for (int t = 0; t < NT; ++t) psb[t] = psy[t] = zero4();
-  _Float16* H0T = pool;               // H0T[i][j]  = H0[i][jh + j]
-  _Float16* dHT = H0T + DK * LDJ;     // dHT[i][j]  = dH[i][jh + j]
-  _Float16* X0 = dHT + DK * LDJ;      // [C][LDJ]: dRHS, then dU
-  _Float16* X1b = X0 + C * LDJ;       // [C][LDJ]: dO, then RHS
-  _Float16* X2b = X1b + C * LDJ;      // [C][LDJ]: U
-  const _Float16* hsrc = a.hst + cbase * static_cast<int64_t>(DK * DK);
-  const _Float16* dhsrc = a.dhst + cbase * static_cast<int64_t>(DK * DK);
-  const int64_t rstride = static_cast<int64_t>(a.Hv) * DK;
-
-  for (int jh = 0; jh < DK; jh += 64) {
-    __syncthreads();  // previous users of the pool (and the staging above) are done
-#pragma unroll
-    for (int u = 0; u < DK * 8 / 256; ++u) {
-      const int e = tid + 256 * u;
-      const int i = e / 8, q8 = e % 8;
-      const uint4 hv4 = *reinterpret_cast<const uint4*>(hsrc + i * DK + jh + 8 * q8);
-      const uint4 dv4 = *reinterpret_cast<const uint4*>(dhsrc + i * DK + jh + 8 * q8);
-      *reinterpret_cast<uint4*>(H0T + i * LDJ + 8 * q8) = hv4;
-      *reinterpret_cast<uint4*>(dHT + i * LDJ + 8 * q8) = dv4;
-      const _Float16* ph = reinterpret_cast<const _Float16*>(&hv4);
-      const _Float16* pd = reinterpret_cast<const _Float16*>(&dv4);
-#pragma unroll
-      for (int k2 = 0; k2 < 8; ++k2) hh += static_cast<float>(ph[k2]) * static_cast<float>(pd[k2]);
+    for (int e = 0; e < 4; ++e) {
+      h0f[kb][e] = h_of(h0u[2 * kb][e]);
+      h0f[kb][4 + e] = h_of(h0u[2 * kb + 1][e]);
+      dhf[kb][e] = h_of(dhu[2 * kb][e]);
+      dhf[kb][4 + e] = h_of(dhu[2 * kb + 1][e]);
     }
-    const int jcol = jh + 16 * w + c16;
-    f32x4 vv[NT], dov[NT];
-    load_strip<NT>(vv, static_cast<const bf16_t*>(a.v) + ((b * a.T + t0) * a.Hv + hv) * DK + jcol, rstride, L);
-    load_strip<NT>(dov, static_cast<const bf16_t*>(a.dout) + ((b * a.T + t0) * a.Hv + hv) * DK + jcol, rstride, L);
-    __syncthreads();
-
-    f32x4 y[NT], du[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) y[t] = du[t] = zero4();
-    mma_rows_bkmin<NT, DK>(y, Ks, LDK, H0T, LDJ, 16 * w);
-    mma_rows_bkmin<NT, DK>(du, Ks, LDK, dHT, LDJ, 16 * w);
-    f32x4 rhs[NT], vmy[NT];
-#pragma unroll
-    for (int tr = 0; tr < NT; ++tr)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * tr + 4 * g + e;
-        vmy[tr][e] = vv[tr][e] - gam[r] * y[tr][e];
-        rhs[tr][e] = bet[r] * vmy[tr][e];
-        du[tr][e] *= lam[r];
-      }
-    f16x8 bf[NT / 2];
-    f32x4 u[NT], dr[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) u[t] = dr[t] = zero4();
-    chain_frags<NT>(bf, rhs);
-    mma_chain_rows<NT, NT>(u, Ts, LDC, bf);
-    chain_frags<NT>(bf, dov);
-    mma_chain_rows<NT, NT>(du, PsT, LDC, bf);
-    chain_frags<NT>(bf, du);
-    mma_chain_rows<NT, NT>(dr, TsT, LDC, bf);
-    const int jl = 16 * w + c16;
-#pragma unroll
-    for (int tr = 0; tr < NT; ++tr)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * tr + 4 * g + e;
-        psb[tr][e] += dr[tr][e] * vmy[tr][e];
-        psy[tr][e] += dr[tr][e] * y[tr][e];
-        X0[r * LDJ + jl] = static_cast<_Float16>(dr[tr][e]);
-        X1b[r * LDJ + jl] = static_cast<_Float16>(dov[tr][e]);
-        X2b[r * LDJ + jl] = static_cast<_Float16>(u[tr][e]);
-      }
-    __syncthreads();
-    // phase 1: X1 += dRHS H0^T, X2 += dO H0^T, dP += dO U^T
-    mma_cols<NCK, 64>(x1, X0, LDJ, 16 * rt, H0T, LDJ, 16 * cq * NCK);
-    mma_cols<NCK, 64>(x2, X1b, LDJ, 16 * rt, H0T, LDJ, 16 * cq * NCK);
-    mma_cols<NCQ, 64>(dP, X1b, LDJ, 16 * rt, X2b, LDJ, 16 * cq * NCQ);
-    __syncthreads();
-#pragma unroll
-    for (int tr = 0; tr < NT; ++tr)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * tr + 4 * g + e;
-        X0[r * LDJ + jl] = static_cast<_Float16>(du[tr][e]);
-        X1b[r * LDJ + jl] = static_cast<_Float16>(rhs[tr][e]);
-      }
-    __syncthreads();
-    // phase 2: X3 += U dH^T, dT += dU RHS^T
-    mma_cols<NCK, 64>(x3, X2b, LDJ, 16 * rt, dHT, LDJ, 16 * cq * NCK);
-    mma_cols<NCQ, 64>(dT, X0, LDJ, 16 * rt, X1b, LDJ, 16 * cq * NCQ);
+    for (int p2 = 0; p2 < 4; ++p2)
+      hh = __builtin_amdgcn_fdot2(f16x2{h0f[kb][2 * p2], h0f[kb][2 * p2 + 1]},
+                                  f16x2{dhf[kb][2 * p2], dhf[kb][2 * p2 + 1]}, hh, false);
   }
-  // phase-A row sums: dbeta_r += sum_j dRHS (V - gam Y), dG_r -= beta gam sum_j dRHS Y
+  f32x4 y[NT], du[NT], u[NT], dr[NT], rhs[NT], dov[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) y[t] = du[t] = u[t] = dr[t] = zero4();
+  mma_chain_rows<NT, NTK>(y, Ks, LDK, h0f);
+  mma_chain_rows<NT, NTK>(du, Ks, LDK, dhf);
+  f32x4 psb[NT], psy[NT];
+#pragma unroll
+  for (int tr = 0; tr < NT; ++tr) {
+    const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * tr + 4 * g);
+    const f32x4 lv = *reinterpret_cast<const f32x4*>(lam + 16 * tr + 4 * g);
+    const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
+    float vv[4], dd[4];
+    unpack_strip(vv, vraw[tr]);
+    unpack_strip(dd, draw[tr]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float vmy = vv[e] - gv[e] * y[tr][e];
+      psb[tr][e] = vmy;  // completed below once dRHS is known
+      rhs[tr][e] = bv[e] * vmy;
+      du[tr][e] *= lv[e];
+      dov[tr][e] = dd[e];
+    }
+  }
+  f16x8 bf[NT / 2];
+  chain_frags<NT>(bf, rhs);
+  mma_chain_rows<NT, NT>(u, Ts, LDC, bf);
+  chain_frags<NT>(bf, dov);
+  mma_chain_rows<NT, NT>(du, PsT, LDC, bf);
+  chain_frags<NT>(bf, du);
+  mma_chain_rows<NT, NT>(dr, TsT, LDC, bf);
+#pragma unroll
+  for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * tr + 4 * g + e;
+      psb[tr][e] *= dr[tr][e];
+      psy[tr][e] = dr[tr][e] * y[tr][e];
+      X0[r * LDX + jw] = static_cast<_Float16>(dr[tr][e]);
+      X1b[r * LDX + jw] = static_cast<_Float16>(dov[tr][e]);
+      X2b[r * LDX + jw] = static_cast<_Float16>(u[tr][e]);
+    }
+  // dbeta_r += sum_j dRHS (V - gam Y);  dG_r -= beta gam sum_j dRHS Y
 #pragma unroll
   for (int tr = 0; tr < NT; ++tr)
 #pragma unroll
@@ -925,116 +943,182 @@ __global__ __launch_bounds__(256) void grad16_kernel(K16 a) {
     }
   __syncthreads();
 
-  // ---- C x C stage
-  _Float16* dTT = pool;             // dTT[s'][s] = dT[s][s']
-  _Float16* M1s = dTT + C * LDC;
-  _Float16* dPm = M1s + C * LDC;    // dPm[r][s]
-  _Float16* dPmT = dPm + C * LDC;   // dPmT[s][r]
-  _Float16* dAs = dPmT + C * LDC;   // symmetric dAm + dAm^T
-  float rowG[4] = {0.f, 0.f, 0.f, 0.f}, rowB[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's row parts
+  // ---- phase 1: X1 = dRHS H0^T, X2 = dO H0^T, dP = dO U^T
+  f32x4 x1[NT], x2[NT], x3[NT], dP[DPW], dT[DPW];
 #pragma unroll
-  for (int cc = 0; cc < NCQ; ++cc) {
-    const int s2 = 16 * (cq * NCQ + cc) + c16;
-    f16x4 t4;
-    float col = 0.f;
+  for (int t = 0; t < NT; ++t) x1[t] = x2[t] = x3[t] = zero4();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * rt + 4 * g + e;
-      t4[e] = static_cast<_Float16>(dT[cc][e]);
-      const float pv = static_cast<float>(PsT[s2 * LDC + r]);      // P_rs
-      const float m = s2 <= r ? exp2f(G2[r] - G2[s2]) : 0.f;
-      const float dpp = dP[cc][e] * pv;
-      rowG[e] += dpp;
-      col += dpp;
-      dPm[r * LDC + s2] = static_cast<_Float16>(dP[cc][e] * m);
+  for (int t = 0; t < DPW; ++t) dP[t] = dT[t] = zero4();
+#pragma unroll
+  for (int ks = 0; ks < DK / 32; ++ks) {
+    const f16x8 bfr = __builtin_bit_cast(f16x8, h0r[ks]);
+    f16x8 a1[NT], a2[NT];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      a1[rt] = ld8(X0 + (16 * rt + c16) * LDX + 32 * ks + 8 * g);
+      a2[rt] = ld8(X1b + (16 * rt + c16) * LDX + 32 * ks + 8 * g);
     }
-    *reinterpret_cast<f16x4*>(dTT + s2 * LDC + 16 * rt + 4 * g) = t4;
-    f16x4 p4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) p4[e] = dPm[(16 * rt + 4 * g + e) * LDC + s2];
-    *reinterpret_cast<f16x4*>(dPmT + s2 * LDC + 16 * rt + 4 * g) = p4;
-    col = xsum<16, 64>(col);
-    if (lane < 16) sGc[w][s2] += col;
+    for (int rt = 0; rt < NT; ++rt) {
+      x1[rt] = F16Op::mma(a1[rt], bfr, x1[rt]);
+      x2[rt] = F16Op::mma(a2[rt], bfr, x2[rt]);
+    }
+  }
+  if (qact) {
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      const f16x8 af = ld8(X1b + (16 * qr + c16) * LDX + 32 * ks + 8 * g);
+#pragma unroll
+      for (int t = 0; t < DPW; ++t)
+        dP[t] = F16Op::mma(af, ld8(X2b + (16 * (qc0 + t) + c16) * LDX + 32 * ks + 8 * g), dP[t]);
+    }
   }
   __syncthreads();
-  f32x4 m1[NCQ];
 #pragma unroll
-  for (int cc = 0; cc < NCQ; ++cc) m1[cc] = zero4();
-  mma_cols<NCQ, C>(m1, TsT, LDC, 16 * rt, dTT, LDC, 16 * cq * NCQ);
-#pragma unroll
-  for (int cc = 0; cc < NCQ; ++cc)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) M1s[(16 * rt + 4 * g + e) * LDC + 16 * (cq * NCQ + cc) + c16] = static_cast<_Float16>(m1[cc][e]);
-  __syncthreads();
-  f32x4 da[NCQ], kk[NCQ];
-#pragma unroll
-  for (int cc = 0; cc < NCQ; ++cc) da[cc] = kk[cc] = zero4();
-  mma_cols<NCQ, C>(da, M1s, LDC, 16 * rt, Ts, LDC, 16 * cq * NCQ);
-  mma_cols<NCQ, DK>(kk, Ks, LDK, 16 * rt, Ks, LDK, 16 * cq * NCQ);
-#pragma unroll
-  for (int cc = 0; cc < NCQ; ++cc) {
-    const int s2 = 16 * (cq * NCQ + cc) + c16;
-    float col = 0.f;
+  for (int tr = 0; tr < NT; ++tr)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 16 * rt + 4 * g + e;
-      const float ex = s2 < r ? exp2f(G2[r] - G2[s2]) : 0.f;
-      const float dav = -da[cc][e] * ex;
-      const float dam = dav * bet[r];
-      const float ag = dam * kk[cc][e];
-      rowB[e] += dav * kk[cc][e];
-      rowG[e] += ag;
-      col += ag;
-      if (s2 < r) {
-        dAs[r * LDC + s2] = static_cast<_Float16>(dam);
-        dAs[s2 * LDC + r] = static_cast<_Float16>(dam);
-      } else if (s2 == r) {
-        dAs[r * LDC + r] = static_cast<_Float16>(0.f);
-      }
+      const int r = 16 * tr + 4 * g + e;
+      X0[r * LDX + jw] = static_cast<_Float16>(du[tr][e]);
+      X1b[r * LDX + jw] = static_cast<_Float16>(rhs[tr][e]);
     }
-    col = xsum<16, 64>(col);
-    if (lane < 16) sGc[w][s2] += col;
+  __syncthreads();
+  // ---- phase 2: X3 = U dH^T, dT = dU RHS^T
+#pragma unroll
+  for (int ks = 0; ks < DK / 32; ++ks) {
+    const f16x8 bfr = __builtin_bit_cast(f16x8, dhrw[ks]);
+    f16x8 a3[NT];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) a3[rt] = ld8(X2b + (16 * rt + c16) * LDX + 32 * ks + 8 * g);
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) x3[rt] = F16Op::mma(a3[rt], bfr, x3[rt]);
+  }
+  if (qact) {
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      const f16x8 af = ld8(X0 + (16 * qr + c16) * LDX + 32 * ks + 8 * g);
+#pragma unroll
+      for (int t = 0; t < DPW; ++t)
+        dT[t] = F16Op::mma(af, ld8(X1b + (16 * (qc0 + t) + c16) * LDX + 32 * ks + 8 * g), dT[t]);
+    }
   }
   __syncthreads();
 
-  // ---- dq, dk per v-head; X2 / X3 terms of dG
-  f32x4 dq[NCK], dk[NCK];
+  // ---- C x C stage on the tiles (qr, qc0 + t)
+  _Float16* dTT = xb;              // dTT[s'][s] = dT[s][s']
+  _Float16* M1s = dTT + C * LDC;
+  _Float16* dPm = M1s + C * LDC;   // dPm[r][s]
+  _Float16* dPmT = dPm + C * LDC;  // dPmT[s][r]
+  _Float16* dAs = dPmT + C * LDC;  // symmetric dAm + dAm^T
+  float rgc[4] = {0.f, 0.f, 0.f, 0.f}, rbc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (qact) {
 #pragma unroll
-  for (int t = 0; t < NCK; ++t) dq[t] = dk[t] = zero4();
-  mma_cols<NCK, C>(dq, dPm, LDC, 16 * rt, KsT, LDC, 16 * cq * NCK);
-  mma_cols<NCK, C>(dk, dPmT, LDC, 16 * rt, QsT, LDC, 16 * cq * NCK);
-  mma_cols<NCK, C>(dk, dAs, LDC, 16 * rt, KsT, LDC, 16 * cq * NCK);
+    for (int t = 0; t < DPW; ++t) {
+      const int s2 = 16 * (qc0 + t) + c16;
+      f16x4 t4, p4;
+      float col = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * qr + 4 * g + e;
+        t4[e] = static_cast<_Float16>(dT[t][e]);
+        const float pv = static_cast<float>(PsT[s2 * LDC + r]);  // P_rs
+        const float m = s2 <= r ? __builtin_amdgcn_exp2f(G2[r] - G2[s2]) : 0.f;
+        const float dpp = dP[t][e] * pv;
+        rgc[e] += dpp;
+        col += dpp;
+        p4[e] = static_cast<_Float16>(dP[t][e] * m);
+        dPm[r * LDC + s2] = p4[e];
+      }
+      *reinterpret_cast<f16x4*>(dTT + s2 * LDC + 16 * qr + 4 * g) = t4;
+      *reinterpret_cast<f16x4*>(dPmT + s2 * LDC + 16 * qr + 4 * g) = p4;
+      col = xsum<16, 64>(col);
+      if (lane < 16) sGc[w][s2] += col;
+    }
+  }
+  __syncthreads();
+  if (qact) {
+    f32x4 m1[DPW];
+#pragma unroll
+    for (int t = 0; t < DPW; ++t) m1[t] = zero4();
+    mma_cols<DPW, C>(m1, TsT, LDC, 16 * qr, dTT, LDC, 16 * qc0);
+#pragma unroll
+    for (int t = 0; t < DPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        M1s[(16 * qr + 4 * g + e) * LDC + 16 * (qc0 + t) + c16] = static_cast<_Float16>(m1[t][e]);
+  }
+  __syncthreads();
+  if (qact) {
+    f32x4 da[DPW], kk[DPW];
+#pragma unroll
+    for (int t = 0; t < DPW; ++t) da[t] = kk[t] = zero4();
+    mma_cols<DPW, C>(da, M1s, LDC, 16 * qr, Ts, LDC, 16 * qc0);
+    mma_cols<DPW, DK>(kk, Ks, LDK, 16 * qr, Ks, LDK, 16 * qc0);
+#pragma unroll
+    for (int t = 0; t < DPW; ++t) {
+      const int s2 = 16 * (qc0 + t) + c16;
+      float col = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * qr + 4 * g + e;
+        const float ex = s2 < r ? __builtin_amdgcn_exp2f(G2[r] - G2[s2]) : 0.f;
+        const float dav = -da[t][e] * ex;
+        const float dam = dav * bet[r];
+        const float ag = dam * kk[t][e];
+        rbc[e] += dav * kk[t][e];
+        rgc[e] += ag;
+        col += ag;
+        if (s2 < r) {
+          dAs[r * LDC + s2] = static_cast<_Float16>(dam);
+          dAs[s2 * LDC + r] = static_cast<_Float16>(dam);
+        } else if (s2 == r) {
+          dAs[r * LDC + r] = static_cast<_Float16>(0.f);
+        }
+      }
+      col = xsum<16, 64>(col);
+      if (lane < 16) sGc[w][s2] += col;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float rg = row16_sum(rgc[e]);
+      const float rb = row16_sum(rbc[e]);
+      if (c16 == 0) {
+        sG[w][16 * qr + 4 * g + e] += rg;
+        sB[w][16 * qr + 4 * g + e] += rb;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- dq_hat, dk_hat on Dk tile w; X2 / X3 terms of dG
+  f32x4 dq[NT], dk[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) dq[t] = dk[t] = zero4();
+  mma_rows<NT, C>(dq, dPm, LDC, KsT, LDC, 16 * w);
+  mma_rows<NT, C>(dk, dPmT, LDC, QsT, LDC, 16 * w);
+  mma_rows<NT, C>(dk, dAs, LDC, KsT, LDC, 16 * w);
+  const uint32_t rowp = static_cast<uint32_t>(a.Hv) * DK * 4;
+  const rsrc_t pqr = make_rsrc(a.pdq + (b * a.T + t0) * a.Hv * DK, static_cast<uint32_t>(L) * rowp);
+  const rsrc_t pkr = make_rsrc(a.pdk + (b * a.T + t0) * a.Hv * DK, static_cast<uint32_t>(L) * rowp);
+  const uint32_t voffp = 4 * g * rowp + (hv * DK + i2) * 4;
   float gcx = 0.f;
-  float* pq = a.pdq + ((b * a.T + t0) * a.Hv + hv) * DK;
-  float* pk = a.pdk + ((b * a.T + t0) * a.Hv + hv) * DK;
 #pragma unroll
-  for (int ct = 0; ct < NCK; ++ct) {
-    const int i2 = 16 * (cq * NCK + ct) + c16;
+  for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * rt + 4 * g + e;
       const float qn = static_cast<float>(QsT[i2 * LDC + r]);
       const float kn = static_cast<float>(KsT[i2 * LDC + r]);
-      const float t3 = lam[r] * kn * x3[ct][e];
-      rowG[e] += gam[r] * qn * x2[ct][e] - t3;
+      const float t3 = lam[r] * kn * x3[rt][e];
       gcx += t3;
-      const float dqv = dq[ct][e] + gam[r] * x2[ct][e];
-      const float dkv = dk[ct][e] + lam[r] * x3[ct][e] - bet[r] * gam[r] * x1[ct][e];
-      if (r < L) {
-        pq[static_cast<int64_t>(r) * rstride + i2] = dqv;
-        pk[static_cast<int64_t>(r) * rstride + i2] = dkv;
-      }
+      const float rg = row16_sum(gam[r] * qn * x2[rt][e] - t3);
+      if (c16 == 0) sG[w][r] += rg;
+      const float dqv = dq[rt][e] + gam[r] * x2[rt][e];
+      const float dkv = dk[rt][e] + lam[r] * x3[rt][e] - bet[r] * gam[r] * x1[rt][e];
+      const uint32_t off = voffp + (16 * rt + e) * rowp;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dqv), pqr, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dkv), pkr, off, 0, 0);
     }
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float rg = row16_sum(rowG[e]);
-    const float rb = row16_sum(rowB[e]);
-    if (c16 == 0) {
-      sG[w][16 * rt + 4 * g + e] += rg;
-      sB[w][16 * rt + 4 * g + e] += rb;
-    }
-  }
   hh = xsum<1, 64>(hh);
   gcx = xsum<1, 64>(gcx);
   if (lane == 0) {
@@ -1046,13 +1130,23 @@ __global__ __launch_bounds__(256) void grad16_kernel(K16 a) {
     const int r = lane;
     float dG = 0.f, dB = 0.f;
     if (r < C) {
-      dG = sG[0][r] + sG[1][r] + sG[2][r] + sG[3][r] - (sGc[0][r] + sGc[1][r] + sGc[2][r] + sGc[3][r]);
-      dB = sB[0][r] + sB[1][r] + sB[2][r] + sB[3][r];
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) {
+        dG += sG[w2][r] - sGc[w2][r];
+        dB += sB[w2][r];
+      }
     }
-    if (r == L - 1)
-      dG += gamC * (red[0][0] + red[0][1] + red[0][2] + red[0][3]) + (red[1][0] + red[1][1] + red[1][2] + red[1][3]);
+    if (r == L - 1) {
+      float hs = 0.f, xs = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) {
+        hs += red[0][w2];
+        xs += red[1][w2];
+      }
+      dG += gamC * hs + xs;
+    }
     if (r >= L) dG = 0.f;
-    float x = dG;
+    float x = dG;  // dg_t = sum_{r >= t} dG_r
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float yv = __shfl_down(x, off, 64);
@@ -1143,7 +1237,7 @@ hipError_t dh16(const K16& a, hipStream_t st) {
 template <int C>
 hipError_t grad16(const K16& a, hipStream_t st) {
   ProfScope ps("chunk_grad", st);
-  hipLaunchKernelGGL((grad16_kernel<C>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((grad16_kernel<C>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
