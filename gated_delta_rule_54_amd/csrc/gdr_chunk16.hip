@@ -84,6 +84,8 @@ struct K16 {
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+// Wave index as a scalar (wave-uniform by construction).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(nbytes), 0x00020000);
@@ -100,13 +102,12 @@ template <int NBYTES, int NTH = 256>
 __device__ __forceinline__ void dma(rsrc_t r, uint32_t off, char* dst) {
   static_assert(NBYTES % 16 == 0, "images are made of 16-byte units");
   constexpr int N16 = NBYTES / 16;
-  const int tid = threadIdx.x, w = tid >> 6;
+  const int tid = threadIdx.x, w = wave_id();
 #pragma unroll
   for (int u = 0; u < (N16 + NTH - 1) / NTH; ++u) {
-    const int e = NTH * u + tid;
-    if (N16 % NTH == 0 || e < N16)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void)(dst + 16 * (NTH * u + 64 * w)), 16, off + 16 * e, 0, 0,
-                                               0);
+    if (N16 % NTH == 0 || NTH * u + tid < N16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void)(dst + 16 * (NTH * u + 64 * w)), 16, off + 16 * tid,
+                                               16 * NTH * u, 0, 0);
   }
 }
 
@@ -807,7 +808,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   __shared__ __align__(16) _Float16 xb[XB];
   __shared__ float sG[NW][C], sGc[NW][C], sB[NW][C], red[2][NW];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int c = blockIdx.x, hv = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int kh = hv / (a.Hv / a.Hk);
