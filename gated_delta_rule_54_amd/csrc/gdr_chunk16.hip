@@ -77,10 +77,12 @@ struct K16 {
   float* dh0;
   char *kimg, *cimg;       // [B][Hk][NC] key images, [B][Hv][NC] chunk images
   _Float16 *hst, *dhst;    // [B][Hv][NC][DK][DK]: chunk-entry H, chunk-end dH
-  float *pdq, *pdk;        // [B][T][Hv][DK] per-v-head dq_hat / dk_hat
+  float *pdq, *pdk;        // [B][T][Hk][DK] running sums of dq_hat / dk_hat over a group's v-heads
+  void *dq, *dk;           // [B][T][Hk][DK] out dtype
   float *dg, *dbeta;       // [B][T][Hv]
   int64_t B, T;
   int Hk, Hv, NC, l2;
+  int gi;                  // v-head within its k-head group (gradient launches)
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -762,7 +764,13 @@ __global__ __launch_bounds__(256) void dh16_kernel(K16 a) {
 
 // ---------------------------------------------------------------------------
 // grad16: all gradients of one chunk except dv and dH, given its entry state
-// H0 and the gradient dH at its end (both [Dk][Dv] fp16).  Eight waves.
+// H0 and the gradient dH at its end (both [Dk][Dv] fp16).  Eight waves.  One
+// launch per v-head of a k-head group (v-head gi of every group), in order:
+// dq_hat / dk_hat of the group are summed in fp32 in a running buffer
+// (FIRST stores, MID adds), and the launch of the group's last v-head adds
+// its share, applies the L2-norm VJP and writes dq, dk (LAST; ONLY when the
+// group has one v-head).  The sum order is fixed, so results are
+// reproducible.
 //   Phase A  wave w owns the 16-column value strip jw = 16w .. 16w+15 and
 //            chains in registers Y = K H0, X = K dH, U = T RHS,
 //            dU = lam X + P^T dO, dRHS = T^T dU; it writes dRHS, dO and U
@@ -795,7 +803,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ _Float16 h_of(uint32_t u) { return __builtin_bit_cast(_Float16, static_cast<uint16_t>(u)); }
 
-template <int C>
+enum GradMode { kFirst = 0, kMid = 1, kLast = 2, kOnly = 3 };
+
+template <int C, typename TO, int MODE>
 __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   using IM = Img<C>;
   constexpr int NW = 8;
@@ -807,11 +817,13 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   __shared__ __align__(16) char img[IM::CHK_B + IM::KEY_B];
   __shared__ __align__(16) _Float16 xb[XB];
   __shared__ float sG[NW][C], sGc[NW][C], sB[NW][C], red[2][NW];
+  __shared__ float sN[4][NW][C];  // L2-norm VJP row partials: |q|^2, q.dq_hat, |k|^2, k.dk_hat
+  __shared__ __align__(16) float sDot[4][C];
 
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-  const int c = blockIdx.x, hv = blockIdx.y;
+  const int c = blockIdx.x, kh = blockIdx.y;
   const int64_t b = blockIdx.z;
-  const int kh = hv / (a.Hv / a.Hk);
+  const int hv = kh * (a.Hv / a.Hk) + a.gi;
   const int64_t t0 = static_cast<int64_t>(c) * C;
   const int L = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
   const int64_t cbase = (b * a.Hv + hv) * a.NC + c;
@@ -1098,10 +1110,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   mma_rows<NT, C>(dq, dPm, LDC, KsT, LDC, 16 * w);
   mma_rows<NT, C>(dk, dPmT, LDC, QsT, LDC, 16 * w);
   mma_rows<NT, C>(dk, dAs, LDC, KsT, LDC, 16 * w);
-  const uint32_t rowp = static_cast<uint32_t>(a.Hv) * DK * 4;
-  const rsrc_t pqr = make_rsrc(a.pdq + (b * a.T + t0) * a.Hv * DK, static_cast<uint32_t>(L) * rowp);
-  const rsrc_t pkr = make_rsrc(a.pdk + (b * a.T + t0) * a.Hv * DK, static_cast<uint32_t>(L) * rowp);
-  const uint32_t voffp = 4 * g * rowp + (hv * DK + i2) * 4;
+  float dqv[NT][4], dkv[NT][4];
   float gcx = 0.f;
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt)
@@ -1114,12 +1123,37 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       gcx += t3;
       const float rg = row16_sum(gam[r] * qn * x2[rt][e] - t3);
       if (c16 == 0) sG[w][r] += rg;
-      const float dqv = dq[rt][e] + gam[r] * x2[rt][e];
-      const float dkv = dk[rt][e] + lam[r] * x3[rt][e] - bet[r] * gam[r] * x1[rt][e];
-      const uint32_t off = voffp + (16 * rt + e) * rowp;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dqv), pqr, off, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dkv), pkr, off, 0, 0);
+      dqv[rt][e] = dq[rt][e] + gam[r] * x2[rt][e];
+      dkv[rt][e] = dk[rt][e] + lam[r] * x3[rt][e] - bet[r] * gam[r] * x1[rt][e];
     }
+  // ---- group sums of dq_hat / dk_hat (rows 16rt + 4g + e, column i2)
+  {
+    const uint32_t rowp = static_cast<uint32_t>(a.Hk) * DK * 4;
+    const int64_t seqp = (b * a.T + t0) * a.Hk * DK;
+    const rsrc_t pqr = make_rsrc(a.pdq + seqp, static_cast<uint32_t>(L) * rowp);
+    const rsrc_t pkr = make_rsrc(a.pdk + seqp, static_cast<uint32_t>(L) * rowp);
+    const uint32_t voffp = 4 * g * rowp + (kh * DK + i2) * 4;
+    if constexpr (MODE == kMid || MODE == kLast) {
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t off = voffp + (16 * rt + e) * rowp;
+          dqv[rt][e] += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pqr, off, 0, 0));
+          dkv[rt][e] += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pkr, off, 0, 0));
+        }
+    }
+    if constexpr (MODE == kFirst || MODE == kMid) {
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t off = voffp + (16 * rt + e) * rowp;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dqv[rt][e]), pqr, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dkv[rt][e]), pkr, off, 0, 0);
+        }
+    }
+  }
   hh = xsum<1, 64>(hh);
   gcx = xsum<1, 64>(gcx);
   if (lane == 0) {
@@ -1159,6 +1193,77 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       a.dbeta[row] = dB;
     }
   }
+  if constexpr (MODE == kLast || MODE == kOnly) {
+    // L2-norm VJP of the group's sums: dx = r (dx_hat - r^2 x (x . dx_hat)),
+    // r = (|x|^2 + eps)^(-1/2), from the raw q / k rows (the Megatron-LM page's
+    // fold of the norm into the kernel, differentiated)
+    if (a.l2) {
+      const uint32_t rowk = static_cast<uint32_t>(a.Hk) * DK * 2;
+      const int64_t seqk = (b * a.T + t0) * a.Hk * DK;
+      const uint32_t voffk = 4 * g * rowk + (kh * DK + i2) * 2;
+      uint32_t qraw[NT][4], kraw[NT][4];
+      load_strip_buf<NT>(qraw, make_rsrc(a.q + seqk, static_cast<uint32_t>(L) * rowk), voffk, rowk);
+      load_strip_buf<NT>(kraw, make_rsrc(a.k + seqk, static_cast<uint32_t>(L) * rowk), voffk, rowk);
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        float xq[4], xk[4];
+        unpack_strip(xq, qraw[rt]);
+        unpack_strip(xk, kraw[rt]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float s0 = row16_sum(xq[e] * xq[e]);
+          const float s1 = row16_sum(xq[e] * dqv[rt][e]);
+          const float s2 = row16_sum(xk[e] * xk[e]);
+          const float s3 = row16_sum(xk[e] * dkv[rt][e]);
+          if (c16 == 0) {
+            const int r = 16 * rt + 4 * g + e;
+            sN[0][w][r] = s0;
+            sN[1][w][r] = s1;
+            sN[2][w][r] = s2;
+            sN[3][w][r] = s3;
+          }
+        }
+      }
+      __syncthreads();
+      if (tid < 4 * C) {
+        const int m = tid / C, r = tid % C;
+        float sum = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) sum += sN[m][w2][r];
+        sDot[m][r] = sum;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        float xq[4], xk[4];
+        unpack_strip(xq, qraw[rt]);
+        unpack_strip(xk, kraw[rt]);
+        const f32x4 qq = *reinterpret_cast<const f32x4*>(&sDot[0][16 * rt + 4 * g]);
+        const f32x4 qd = *reinterpret_cast<const f32x4*>(&sDot[1][16 * rt + 4 * g]);
+        const f32x4 kk2 = *reinterpret_cast<const f32x4*>(&sDot[2][16 * rt + 4 * g]);
+        const f32x4 kd = *reinterpret_cast<const f32x4*>(&sDot[3][16 * rt + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float rq = rsqrtf(qq[e] + kL2Eps), rk = rsqrtf(kk2[e] + kL2Eps);
+          dqv[rt][e] = rq * (dqv[rt][e] - rq * rq * xq[e] * qd[e]);
+          dkv[rt][e] = rk * (dkv[rt][e] - rk * rk * xk[e] * kd[e]);
+        }
+      }
+    }
+    const uint32_t rowo = static_cast<uint32_t>(a.Hk) * DK * sizeof(TO);
+    const int64_t seqo = (b * a.T + t0) * a.Hk * DK * static_cast<int64_t>(sizeof(TO));
+    const uint32_t voffo = 4 * g * rowo + (kh * DK + i2) * static_cast<uint32_t>(sizeof(TO));
+    f32x4 oq[NT], ok[NT];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        oq[rt][e] = dqv[rt][e];
+        ok[rt][e] = dkv[rt][e];
+      }
+    store_strip_buf<TO, NT>(make_rsrc(static_cast<char*>(a.dq) + seqo, static_cast<uint32_t>(L) * rowo), voffo, rowo, oq);
+    store_strip_buf<TO, NT>(make_rsrc(static_cast<char*>(a.dk) + seqo, static_cast<uint32_t>(L) * rowo), voffo, rowo, ok);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1168,7 +1273,7 @@ constexpr size_t kAlign = 256;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Ws16 {
-  size_t kimg, cimg, hst, dhst, pdq, pdk, total;
+  size_t kimg, cimg, hst, dhst, pdq, pdk, total;  // pdq / pdk: group running sums (Hv > Hk)
 };
 
 template <int C>
@@ -1181,11 +1286,13 @@ Ws16 plan16(const Shape& s, bool bwd) {
   w.kimg = off; off = up(off + nk * (bwd ? IM::KEY_B : IM::KEY_F));
   w.cimg = off; off = up(off + nv * (bwd ? IM::CHK_B : IM::CHK_F));
   if (bwd) {
-    const size_t rows = static_cast<size_t>(s.B * s.T) * s.Hv;
+    const size_t rows = static_cast<size_t>(s.B * s.T) * s.Hk;
     w.hst = off;  off = up(off + nv * DK * DK * 2);
     w.dhst = off; off = up(off + nv * DK * DK * 2);
-    w.pdq = off;  off = up(off + rows * DK * 4);
-    w.pdk = off;  off = up(off + rows * DK * 4);
+    if (s.Hv > s.Hk) {
+      w.pdq = off;  off = up(off + rows * DK * 4);
+      w.pdk = off;  off = up(off + rows * DK * 4);
+    }
   }
   w.total = off;
   return w;
@@ -1207,8 +1314,10 @@ K16 args16(const Shape& s, int C, void* ws, const Ws16& w) {
   if (w.hst || w.dhst) {
     a.hst = reinterpret_cast<_Float16*>(base + w.hst);
     a.dhst = reinterpret_cast<_Float16*>(base + w.dhst);
-    a.pdq = reinterpret_cast<float*>(base + w.pdq);
-    a.pdk = reinterpret_cast<float*>(base + w.pdk);
+    if (s.Hv > s.Hk) {
+      a.pdq = reinterpret_cast<float*>(base + w.pdq);
+      a.pdk = reinterpret_cast<float*>(base + w.pdk);
+    }
   }
   return a;
 }
@@ -1235,11 +1344,25 @@ hipError_t dh16(const K16& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int C>
-hipError_t grad16(const K16& a, hipStream_t st) {
-  ProfScope ps("chunk_grad", st);
-  hipLaunchKernelGGL((grad16_kernel<C>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(512), 0, st, a);
-  return hipGetLastError();
+template <int C, typename TO>
+hipError_t grad16(K16 a, hipStream_t st) {
+  const int grp = a.Hv / a.Hk;
+  for (int gi = 0; gi < grp; ++gi) {
+    a.gi = gi;
+    const dim3 grid(a.NC, a.Hk, static_cast<unsigned>(a.B));
+    ProfScope ps("chunk_grad", st);
+    if (grp == 1)
+      hipLaunchKernelGGL((grad16_kernel<C, TO, kOnly>), grid, dim3(512), 0, st, a);
+    else if (gi == 0)
+      hipLaunchKernelGGL((grad16_kernel<C, TO, kFirst>), grid, dim3(512), 0, st, a);
+    else if (gi + 1 < grp)
+      hipLaunchKernelGGL((grad16_kernel<C, TO, kMid>), grid, dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((grad16_kernel<C, TO, kLast>), grid, dim3(512), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int C, typename TO>
@@ -1272,13 +1395,13 @@ hipError_t bwd_all(const Shape& s, const ChunkBwdArgs& x, void* ws, hipStream_t 
   a.dh0 = x.dh0;
   a.dg = x.dg;
   a.dbeta = x.dbeta;
+  a.dq = x.dq;
+  a.dk = x.dk;
   hipError_t e = prep16<C, true>(a, st);
   if (e == hipSuccess) e = chain16<C, TO, false, true>(a, st);
   if (e == hipSuccess) e = dh16<C, TO>(a, st);
-  if (e == hipSuccess) e = grad16<C>(a, st);
-  if (e != hipSuccess) return e;
-  EpiArgs ea{x.q, x.k, a.pdq, a.pdk, nullptr, nullptr, 1, x.dq, x.dk, nullptr, nullptr};
-  return launch_bwd_epilogue(s, ea, st);
+  if (e == hipSuccess) e = grad16<C, TO>(a, st);
+  return e;
 }
 
 }  // namespace

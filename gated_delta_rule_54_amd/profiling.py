@@ -1,0 +1,179 @@
+"""Per-kernel HBM traffic of a bench.py run, from rocprofv3 counter databases.
+
+Two profiled runs of the same command,
+
+    rocprofv3 --pmc FETCH_SIZE -d DIR_F -o f -- python3 bench.py --steps 1 --warmup 1 \\
+        --no-decode --no-cpu-baseline --copy-calibration-mib 256
+    rocprofv3 --pmc WRITE_SIZE -d DIR_W -o w -- python3 bench.py ... (same flags)
+
+give, per dispatch, the KiB the L2 read from and wrote to memory.  The last
+kernels of that command are a plain elementwise copy of a known size
+(``--copy-calibration-mib``), which moves exactly that many bytes each way;
+the ratio of its counters to its size is the calibration factor the kernel
+figures are divided by.  Then
+
+    python -m gated_delta_rule_54_amd.profiling traffic DIR_F/f_results.db DIR_W/w_results.db \\
+        --copy-mib 256 --json profiles/traffic.json --md profiles/<name>.md
+
+writes the per-launch bytes of each library kernel (keyed by the names the
+library's own event timing uses) together with a digest of the kernel
+sources; bench.py reports the dominant kernel's figure only while that
+digest matches.
+
+    python -m gated_delta_rule_54_amd.profiling trace KT_results.db --md profiles/<name>.md
+
+summarises a ``rocprofv3 --kernel-trace --stats`` database (per-kernel calls,
+total and average duration).
+"""
+
+import argparse
+import collections
+import hashlib
+import json
+import os
+import re
+import sqlite3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+# demangled kernel name pattern -> library timing name
+KERNELS = [
+    (r"prep16_kernel", "chunk_prep"),
+    (r"chain16_kernel<\d+, [^,]+, true, false>", "chunk_fwd"),
+    (r"chain16_kernel<\d+, [^,]+, false, true>", "chunk_states"),
+    (r"dh16_kernel", "chunk_dh"),
+    (r"grad16_kernel", "chunk_grad"),
+    (r"epilogue128_kernel", "bwd_epilogue"),
+    (r"seq_fwd_kernel", "seq_fwd"),
+]
+COPY_PATTERN = r"neg_kernel"
+
+
+def src_digest():
+    """Digest of the kernel sources (same definition as bench.py's)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(_HERE, "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def per_dispatch(db, counter):
+    """{dispatch_id: (kernel name, summed counter value)} for one counter."""
+    con = sqlite3.connect(db)
+    rows = con.execute("select dispatch_id, name, counter_value from pmc_events where counter_name = ?",
+                       (counter,)).fetchall()
+    out = {}
+    for did, name, v in rows:
+        n, s = out.get(did, (name, 0.0))
+        out[did] = (n, s + float(v))
+    return out
+
+
+def label(name):
+    if re.search(COPY_PATTERN, name):
+        return "copy"
+    for pat, lab in KERNELS:
+        if re.search(pat, name):
+            return lab
+    return None
+
+
+def per_kernel(db, counter):
+    """{label: mean KiB per launch} over the dispatches of each kernel."""
+    acc = collections.defaultdict(list)
+    for name, v in per_dispatch(db, counter).values():
+        lab = label(name)
+        if lab is not None:
+            acc[lab].append(v)
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def traffic(args):
+    fetch = per_kernel(args.fetch_db, "FETCH_SIZE")
+    write = per_kernel(args.write_db, "WRITE_SIZE")
+    if "copy" not in fetch or "copy" not in write:
+        raise SystemExit("the calibration copy kernel was not found in the databases")
+    size_kib = args.copy_mib * 1024.0
+    f_scale = fetch["copy"][0] / size_kib
+    w_scale = write["copy"][0] / size_kib
+    kernels = {}
+    for lab in sorted(set(fetch) | set(write)):
+        if lab == "copy" or lab not in fetch or lab not in write:
+            continue
+        fb = fetch[lab][0] * 1024.0 / f_scale
+        wb = write[lab][0] * 1024.0 / w_scale
+        kernels[lab] = {"fetch_bytes_per_launch": int(fb), "write_bytes_per_launch": int(wb),
+                        "bytes_per_launch": int(fb + wb), "launches": fetch[lab][1]}
+    rec = {"src_digest": src_digest(),
+           "calibration": {"copy_mib": args.copy_mib, "fetch_factor": round(f_scale, 4),
+                           "write_factor": round(w_scale, 4)},
+           "kernels": kernels}
+    with open(args.json, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    if args.md:
+        lines = ["# HBM traffic per kernel launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", ""]
+        if args.command:
+            lines += ["Commands (from the repository root on one MI355X, library built):", "", "```", args.command,
+                      "```", ""]
+        lines += [f"Calibration: a {args.copy_mib:g} MiB elementwise copy read {f_scale:.4f}x and wrote "
+                  f"{w_scale:.4f}x its size by these counters; the figures below are divided by those "
+                  "factors.", "",
+                  "| kernel | launches | fetch MB/launch | write MB/launch | total MB/launch |",
+                  "|---|---:|---:|---:|---:|"]
+        for lab, k in kernels.items():
+            lines.append(f"| {lab} | {k['launches']} | {k['fetch_bytes_per_launch'] / 1e6:.1f} | "
+                         f"{k['write_bytes_per_launch'] / 1e6:.1f} | {k['bytes_per_launch'] / 1e6:.1f} |")
+        lines += ["", f"Kernel sources digest: `{rec['src_digest']}`", ""]
+        with open(args.md, "w") as fh:
+            fh.write("\n".join(lines))
+    print(json.dumps(rec))
+
+
+def trace(args):
+    con = sqlite3.connect(args.db)
+    rows = con.execute("select name, total_calls, total_duration, average, percentage from top_kernels "
+                       "order by total_duration desc").fetchall()  # durations in microseconds
+    lines = ["# Kernel trace (rocprofv3 --kernel-trace --stats)", ""]
+    if args.command:
+        lines += ["Command (from the repository root on one MI355X, library built):", "", "```", args.command, "```",
+                  ""]
+    lines += ["| kernel | library name | calls | total us | avg us | % of GPU time |", "|---|---|---:|---:|---:|---:|"]
+    for name, calls, tot, avg, pct in rows[:args.top]:
+        short = re.sub(r"gdr::\(anonymous namespace\)::", "", name)
+        short = re.sub(r"\(gdr::[^)]*\)$", "", short)
+        if len(short) > 90:
+            short = short[:87] + "..."
+        lines.append(f"| `{short}` | {label(name) or ''} | {calls} | {tot:.1f} | {avg:.2f} | "
+                     f"{pct:.1f} |")
+    lines += ["", f"Kernel sources digest: `{src_digest()}`", ""]
+    text = "\n".join(lines)
+    if args.md:
+        with open(args.md, "w") as fh:
+            fh.write(text)
+    print(text)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_db")
+    t.add_argument("write_db")
+    t.add_argument("--copy-mib", type=float, required=True)
+    t.add_argument("--json", required=True)
+    t.add_argument("--md", default=None)
+    t.add_argument("--command", default="")
+    k = sub.add_parser("trace")
+    k.add_argument("db")
+    k.add_argument("--md", default=None)
+    k.add_argument("--command", default="")
+    k.add_argument("--top", type=int, default=16)
+    args = ap.parse_args()
+    traffic(args) if args.cmd == "traffic" else trace(args)
+
+
+if __name__ == "__main__":
+    main()
