@@ -146,7 +146,10 @@ def bench_chunked(torch, gdr, steps, warmup):
 def bench_decode(torch, gdr):
     """B=8 single-token steps, state updated in place, rotating over
     DEC_BUFFERS independent states so a step's 16 MiB state is not served
-    from the 256 MB last-level cache."""
+    from the 256 MB last-level cache.  Per step: the kernel time from the
+    library's events around each launch (which include the launch's own
+    dispatch), the host wall time, and the time per step of a HIP graph of
+    all steps replayed once."""
     g = torch.Generator(device="cuda").manual_seed(1)
     sh = lambda *s: torch.randn(*s, device="cuda", generator=g)
     q = sh(DEC_STEPS, DEC_B, 1, HK, D).bfloat16()
@@ -176,9 +179,26 @@ def bench_decode(torch, gdr):
         ms, n = kt["seq_fwd"]
         us = 1000.0 * ms / n
         state_bytes = 2 * DEC_B * HV * D * D * 4
+        # the same steps captured once into a HIP graph and replayed: no host
+        # launch gaps and no per-kernel events
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run(DEC_STEPS, buffers)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        gus = 1000.0 * e0.elapsed_time(e1) / DEC_STEPS
+        del graph
         out[label] = {"kernel_us_per_step": round(us, 3), "wall_us_per_step": round(1e6 * wall / DEC_STEPS, 2),
+                      "graph_us_per_step": round(gus, 3),
                       "state_GBps": round(state_bytes / (us * 1e-6) / 1e9, 1),
-                      "frac_hbm_peak": round(state_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                      "frac_hbm_peak": round(state_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "graph_state_GBps": round(state_bytes / (gus * 1e-6) / 1e9, 1),
+                      "graph_frac_hbm_peak": round(state_bytes / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     out["state_bytes_per_step"] = 2 * DEC_B * HV * D * D * 4
     out["config"] = f"B={DEC_B} Hk={HK} Hv={HV} Dk=Dv={D}, {DEC_STEPS} single-token steps, bf16 io, fp32 state"
     return out

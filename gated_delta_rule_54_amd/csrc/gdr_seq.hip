@@ -30,6 +30,8 @@
 namespace gdr {
 namespace {
 
+typedef float f32x4n __attribute__((ext_vector_type(4)));  // native vector for non-temporal access
+
 template <int D, int BV>
 struct Lay {
   static constexpr int NCG = BV / 4;    // 4-column groups per slice
@@ -161,8 +163,12 @@ __global__ __launch_bounds__(64) void seq_fwd_kernel(Dims d, SeqFwdArgs a) {
   float h[L::RPL][4];
 #pragma unroll
   for (int m = 0; m < L::RPL; ++m) {
-    if (a.h0) ld4<float>(a.h0 + hbase + m * D, h[m]);
-    else h[m][0] = h[m][1] = h[m][2] = h[m][3] = 0.f;
+    if (a.h0) {  // streamed once: non-temporal
+      const f32x4n t4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4n*>(a.h0 + hbase + m * D));
+      h[m][0] = t4[0]; h[m][1] = t4[1]; h[m][2] = t4[2]; h[m][3] = t4[3];
+    } else {
+      h[m][0] = h[m][1] = h[m][2] = h[m][3] = 0.f;
+    }
   }
   Tok<L::RPL, CW> cur, nxt;
   load_tok<D, L, TI, CW, true, false>(cur, d, a.q, a.k, a.v, nullptr, a.g, a.beta, b, 0, kh, hv, i0, j0);
@@ -176,7 +182,8 @@ __global__ __launch_bounds__(64) void seq_fwd_kernel(Dims d, SeqFwdArgs a) {
   }
   if (a.ht) {
 #pragma unroll
-    for (int m = 0; m < L::RPL; ++m) st4<float>(a.ht + hbase + m * D, h[m]);
+    for (int m = 0; m < L::RPL; ++m)
+      __builtin_nontemporal_store(f32x4n{h[m][0], h[m][1], h[m][2], h[m][3]}, reinterpret_cast<f32x4n*>(a.ht + hbase + m * D));
   }
 }
 
