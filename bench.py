@@ -52,12 +52,11 @@ def canonical_flops_per_token_head(d=D, c=C):
 
 def image_bytes(d=D, c=C):
     """Byte sizes of the per-chunk operand images the prep kernel writes (fp16
-    tiles padded by 8 halves per row, fp32 gate vectors): key image per
-    (b, k-head, chunk) and chunk image per (b, v-head, chunk), forward (F)
-    and VJP (B) layouts."""
-    kn, kt, tm, gt = c * (d + 8) * 2, d * (c + 8) * 2, c * (c + 8) * 2, 4 * c * 4
-    return {"KEY_F": 2 * kn + kt, "KEY_B": kn + 2 * kt,
-            "CHK_F": gt + 2 * tm, "CHK_B": gt + 3 * tm, "KN": kn, "KT": kt, "TM": tm, "GT": gt}
+    tiles padded by 8 halves per row, fp32 gate vectors): key image (Kn | Qn)
+    per (b, k-head, chunk) and chunk image (gates | T | P) per (b, v-head,
+    chunk); forward and VJP read the same format."""
+    kn, tm, gt = c * (d + 8) * 2, c * (c + 8) * 2, 4 * c * 4
+    return {"KEY": 2 * kn, "CHK": gt + 2 * tm, "KN": kn, "TM": tm, "GT": gt}
 
 
 def kernel_bytes_per_token_head(name, d=D, c=C, grp=HV // HK):
@@ -74,14 +73,13 @@ def kernel_bytes_per_token_head(name, d=D, c=C, grp=HV // HK):
     vec = d * 2              # one bf16 row of v / o / do
     gates = 8                # g and beta, fp32
     st = 2 * d * d / c       # one fp16 d x d state per chunk
-    prep_f = kq + gates + im["KEY_F"] / (c * grp) + im["CHK_F"] / c
-    prep_b = kq + gates + im["KEY_B"] / (c * grp) + im["CHK_B"] / c
+    prep = kq + gates + im["KEY"] / (c * grp) + im["CHK"] / c
     return {
-        "chunk_prep": prep_f + prep_b,
-        "chunk_fwd": im["KEY_F"] / (c * grp) + im["CHK_F"] / c + 2 * vec,
-        "chunk_states": (im["KN"] + im["KT"]) / (c * grp) + (im["GT"] + im["TM"]) / c + vec + st,
-        "chunk_dh": im["KEY_B"] / (c * grp) + (im["GT"] + 2 * im["TM"]) / c + 2 * vec + st,
-        "chunk_grad": (im["KEY_B"] + im["CHK_B"]) / c + 2 * st + 2 * vec + gates
+        "chunk_prep": 2 * prep,
+        "chunk_fwd": im["KEY"] / (c * grp) + im["CHK"] / c + 2 * vec,
+        "chunk_states": im["KN"] / (c * grp) + (im["GT"] + im["TM"]) / c + vec + st,
+        "chunk_dh": im["KEY"] / (c * grp) + im["CHK"] / c + 2 * vec + st,
+        "chunk_grad": (im["KEY"] + im["CHK"]) / c + 2 * st + 2 * vec + gates
                       + (2 * (grp - 1) * 2 * d * 4 + 2 * d * 2 + 2 * d * 2) / grp,
         "bwd_epilogue": 2 * d * 4 + (2 * d * 2 + 2 * d * 2) / grp,
     }.get(name)

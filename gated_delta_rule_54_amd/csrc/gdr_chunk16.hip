@@ -9,13 +9,14 @@
 //            rows, forms A and P on the matrix cores, inverts I + A, and
 //            writes the chunk's operands as fp16 "images": byte-exact copies
 //            of the padded LDS tiles the other kernels read.
-//              key image   per (b, k-head, chunk):  Kn [C][136] | KnT [128][C+8]
-//                          | Qn [C][136] (forward) or QnT [128][C+8] (VJP)
+//              key image   per (b, k-head, chunk):  Kn [C][136] | Qn [C][136]
 //              chunk image per (b, v-head, chunk):  gam | lam | beta | log2(e) G
-//                          (4 x C fp32) | T | P (forward) or T | T^T | P^T (VJP),
-//                          each C x C tile [C][C+8]
-//            Normalisation, transposition and gate math thus happen once per
-//            chunk instead of once per consumer workgroup.
+//                          (4 x C fp32) | T | P, each C x C tile [C][C+8]
+//            Normalisation and gate math thus happen once per chunk instead
+//            of once per consumer workgroup.  Products that need a tile
+//            transposed (Kn^T, Qn^T, T^T, P^T) read it from the row-major
+//            copy with ds_read_b64_tr_b16, so the images hold each tile once
+//            and forward and VJP share one image format.
 //   chain16  per (b, v-head, 64-column value half): the sequential pass over
 //            chunks.  Wave w owns a 16-column strip of the state in MFMA
 //            accumulators.  Each chunk's images are copied into one of two LDS
@@ -59,13 +60,10 @@ template <int C>
 struct Img {
   static constexpr int LDC = C + 8;                // pitch (halves) of [*][C] tiles
   static constexpr uint32_t KN = C * LDK * 2;      // Kn or Qn    [C][LDK]
-  static constexpr uint32_t KT = DK * LDC * 2;     // KnT or QnT  [DK][LDC]
-  static constexpr uint32_t KEY_F = 2 * KN + KT;   // Kn | KnT | Qn
-  static constexpr uint32_t KEY_B = KN + 2 * KT;   // Kn | KnT | QnT
+  static constexpr uint32_t KEY = 2 * KN;          // Kn | Qn
   static constexpr uint32_t GT = 4 * C * 4;        // gam | lam | beta | G2
   static constexpr uint32_t TM = C * LDC * 2;      // one C x C tile
-  static constexpr uint32_t CHK_F = GT + 2 * TM;   // gates | T | P
-  static constexpr uint32_t CHK_B = GT + 3 * TM;   // gates | T | T^T | P^T
+  static constexpr uint32_t CHK = GT + 2 * TM;     // gates | T | P
 };
 
 struct K16 {
@@ -124,6 +122,37 @@ __device__ __forceinline__ f16x8 perm_frag(const _Float16* A, int ld, int m, int
   return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Transposed reads.  ds_read_b64_tr_b16 treats each 16-lane group as one
+// unit: lane p of the group names 4 consecutive halves (its row of a 16 x 4
+// block D[p][0..3]) and receives D[p/4 + 4i][p%4], i = 0..3.  Pointing lane p
+// at row k0 + p/4, columns n0 + 4(p%4) .. +3 of a row-major M[k][n] thus
+// hands lane p the column n0 + p of rows k0 .. k0+3: a k-run of M^T.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ f16x4 tr4(const _Float16* M, int ld, int k0, int n0) {
+  const int p = lane_id() & 15;
+  const _Float16* src = M + (k0 + (p >> 2)) * ld + n0 + 4 * (p & 3);
+  return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src));
+}
+
+// perm_frag of A = M^T (A[m][k] = M[k][m], M row-major) for rows m0 + (lane & 15).
+__device__ __forceinline__ f16x8 perm_frag_t(const _Float16* M, int ld, int m0, int kb) {
+  const int g = lane_id() >> 4;
+  const f16x4 lo = tr4(M, ld, 32 * kb + 4 * g, m0);
+  const f16x4 hi = tr4(M, ld, 32 * kb + 16 + 4 * g, m0);
+  return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Plain-order fragment (k = k0 + 8g .. k0 + 8g + 7) of column n0 + (lane & 15)
+// of a row-major M[k][n]: the A fragment of M^T, or the B fragment of M.
+__device__ __forceinline__ f16x8 frag_t(const _Float16* M, int ld, int k0, int n0) {
+  const int g = lane_id() >> 4;
+  const f16x4 lo = tr4(M, ld, k0 + 8 * g, n0);
+  const f16x4 hi = tr4(M, ld, k0 + 8 * g + 4, n0);
+  return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 // Chained B fragments of a strip x[t][e] (rows 16t + 4g + e of this lane).
 template <int NT>
 __device__ __forceinline__ void chain_frags(f16x8 (&bf)[NT / 2], const f32x4 (&x)[NT]) {
@@ -149,22 +178,17 @@ __device__ __forceinline__ void mma_chain_rows(f32x4 (&acc)[NO], const _Float16*
   }
 }
 
-// acc[t] += A[16t : 16t+16, 0:K] B, B^T rows n0..n0+15 read through a
-// row-contiguous view (element (n, k) at Bm[k * ldb + n]); B is shared.
-template <int NO, int K>
-__device__ __forceinline__ void mma_rows_bkmin(f32x4 (&acc)[NO], const _Float16* A, int lda, const _Float16* Bm,
-                                               int ldb, int n0) {
-  const int r = lane_id() & 15, kl = (lane_id() >> 4) * 8;
+// mma_chain_rows with A = M^T, M row-major [16 NT][ld].
+template <int NO, int NT>
+__device__ __forceinline__ void mma_chain_rows_t(f32x4 (&acc)[NO], const _Float16* M, int ld,
+                                                 const f16x8 (&bf)[NT / 2]) {
 #pragma unroll
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    f16x8 bfr;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) bfr[i] = Bm[(k0 + kl + i) * ldb + n0 + r];
+  for (int kb = 0; kb < NT / 2; ++kb) {
     f16x8 af[NO];
 #pragma unroll
-    for (int t = 0; t < NO; ++t) af[t] = ld8(A + (16 * t + r) * lda + k0 + kl);
+    for (int t = 0; t < NO; ++t) af[t] = perm_frag_t(M, ld, 16 * t, kb);
 #pragma unroll
-    for (int t = 0; t < NO; ++t) acc[t] = F16Op::mma(af[t], bfr, acc[t]);
+    for (int t = 0; t < NO; ++t) acc[t] = F16Op::mma(af[t], bf[kb], acc[t]);
   }
 }
 
@@ -177,6 +201,22 @@ __device__ __forceinline__ void mma_cols(f32x4 (&acc)[NCOL], const _Float16* A, 
 #pragma unroll
   for (int k0 = 0; k0 < K; k0 += 32) {
     const f16x8 af = ld8(A + (m0 + r) * lda + k0 + kl);
+    f16x8 bfr[NCOL];
+#pragma unroll
+    for (int t = 0; t < NCOL; ++t) bfr[t] = ld8(Bt + (nb + 16 * t + r) * ldb + k0 + kl);
+#pragma unroll
+    for (int t = 0; t < NCOL; ++t) acc[t] = F16Op::mma(af, bfr[t], acc[t]);
+  }
+}
+
+// mma_cols with A = M^T (A[m][k] = M[k][m], M row-major).
+template <int NCOL, int K>
+__device__ __forceinline__ void mma_cols_t(f32x4 (&acc)[NCOL], const _Float16* M, int ldm, int m0, const _Float16* Bt,
+                                           int ldb, int nb) {
+  const int r = lane_id() & 15, kl = (lane_id() >> 4) * 8;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const f16x8 af = frag_t(M, ldm, k0, m0);
     f16x8 bfr[NCOL];
 #pragma unroll
     for (int t = 0; t < NCOL; ++t) bfr[t] = ld8(Bt + (nb + 16 * t + r) * ldb + k0 + kl);
@@ -312,7 +352,7 @@ __device__ __forceinline__ void write_tile(char* dst, F&& f) {
 // (lane = column), then the blocks below the diagonal follow level by level,
 //     T_ij = -T_ii (sum_{k=j}^{i-1} A_ik T_kj),
 // on fp32 matrix cores; everything is fp32 until the images are written.
-template <int C, bool BWD>
+template <int C>
 __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
   using IM = Img<C>;
   constexpr int NT = C / 16, LDA = C + 4, LDC = IM::LDC;
@@ -427,7 +467,7 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
   }
 
   // ---- chunk image
-  char* cim = a.cimg + ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(BWD ? IM::CHK_B : IM::CHK_F);
+  char* cim = a.cimg + ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(IM::CHK);
   for (int e = tid; e < C; e += 256)
     reinterpret_cast<float4*>(cim)[e] = reinterpret_cast<const float4*>(gates)[e];
   constexpr int UC = C / 8 + 1;  // 16-byte units per [*][LDC] row
@@ -437,43 +477,13 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
     for (int q = 0; q < 8; ++q) v[q] = static_cast<_Float16>((8 * u + q) / 16 <= r / 16 ? Tf[r * LDA + 8 * u + q] : 0.f);
     return v;
   });
-  if constexpr (!BWD) {
-    write_tile<C, UC>(cim + IM::GT + IM::TM, [&](int r, int u) { return ld8(Pst + r * LDC + 8 * u); });
-  } else {
-    write_tile<C, UC>(cim + IM::GT + IM::TM, [&](int s, int u) {  // T^T
-      f16x8 v;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = static_cast<_Float16>(s / 16 <= (8 * u + q) / 16 ? Tf[(8 * u + q) * LDA + s] : 0.f);
-      return v;
-    });
-    write_tile<C, UC>(cim + IM::GT + 2 * IM::TM, [&](int s, int u) {  // P^T
-      f16x8 v;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = Pst[(8 * u + q) * LDC + s];
-      return v;
-    });
-  }
+  write_tile<C, UC>(cim + IM::GT + IM::TM, [&](int r, int u) { return ld8(Pst + r * LDC + 8 * u); });
   // ---- key image (one v-head of each k-head group writes it)
   if (hv % grp != 0) return;
-  char* kim = a.kimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(BWD ? IM::KEY_B : IM::KEY_F);
+  char* kim = a.kimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(IM::KEY);
   constexpr int UK = DK / 8 + 1;  // 16-byte units per [*][LDK] row
   write_tile<C, UK>(kim, [&](int r, int u) { return ld8(Ks + r * LDK + 8 * u); });
-  write_tile<DK, UC>(kim + IM::KN, [&](int i, int u) {  // KnT
-    f16x8 v;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = Ks[(8 * u + q) * LDK + i];
-    return v;
-  });
-  if constexpr (!BWD) {
-    write_tile<C, UK>(kim + IM::KN + IM::KT, [&](int r, int u) { return ld8(Qs + r * LDK + 8 * u); });
-  } else {
-    write_tile<DK, UC>(kim + IM::KN + IM::KT, [&](int i, int u) {  // QnT
-      f16x8 v;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = Qs[(8 * u + q) * LDK + i];
-      return v;
-    });
-  }
+  write_tile<C, UK>(kim + IM::KN, [&](int r, int u) { return ld8(Qs + r * LDK + 8 * u); });
 }
 
 // ---------------------------------------------------------------------------
@@ -482,16 +492,16 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
 //   Y = Kn H, Z = Qn H          (16 MFMA each, H chained)
 //   U = T (beta (V - gam Y))    (8, chained)
 //   O = gam Z + P U             (8, chained)
-//   H = gam_C H + KnT (lam U)   (16, chained)
+//   H = gam_C H + Kn^T (lam U)  (16, chained)
 // ---------------------------------------------------------------------------
 template <int C, typename TO, bool WRITE_O, bool STORE_H>
 __global__ __launch_bounds__(256) void chain16_kernel(K16 a) {
   using IM = Img<C>;
   constexpr int NT = C / 16, LDC = IM::LDC;
-  constexpr uint32_t CB = WRITE_O ? IM::GT + 2 * IM::TM : IM::GT + IM::TM;  // gates | T | P
-  constexpr uint32_t KB = WRITE_O ? 2 * IM::KN + IM::KT : IM::KN + IM::KT;  // Kn | KnT | Qn
-  constexpr uint32_t KSTR = WRITE_O ? IM::KEY_F : IM::KEY_B;
-  constexpr uint32_t CSTR = WRITE_O ? IM::CHK_F : IM::CHK_B;
+  constexpr uint32_t CB = WRITE_O ? IM::CHK : IM::GT + IM::TM;  // gates | T (| P)
+  constexpr uint32_t KB = WRITE_O ? IM::KEY : IM::KN;           // Kn (| Qn)
+  constexpr uint32_t KSTR = IM::KEY;
+  constexpr uint32_t CSTR = IM::CHK;
   __shared__ __align__(16) char bufA[CB + KB];
   __shared__ __align__(16) char bufB[CB + KB];
 
@@ -555,8 +565,7 @@ __global__ __launch_bounds__(256) void chain16_kernel(K16 a) {
     const _Float16* Tm = reinterpret_cast<const _Float16*>(cur + IM::GT);
     const _Float16* Pm = Tm + C * LDC;
     const _Float16* Kn = reinterpret_cast<const _Float16*>(cur + CB);
-    const _Float16* KnT = Kn + C * LDK;
-    const _Float16* Qn = KnT + DK * LDC;
+    const _Float16* Qn = Kn + C * LDK;
 
     f16x8 hf[NTK / 2];
     chain_frags<NTK>(hf, h);
@@ -599,7 +608,7 @@ __global__ __launch_bounds__(256) void chain16_kernel(K16 a) {
     const float gc = gam[rows_of(c) - 1];
 #pragma unroll
     for (int ti = 0; ti < NTK; ++ti) h[ti] = h[ti] * gc;
-    mma_chain_rows<NTK, NT>(h, KnT, LDC, bf);
+    mma_chain_rows_t<NTK, NT>(h, Kn, LDK, bf);
     wait_all();
     __syncthreads();
 #pragma unroll
@@ -624,15 +633,15 @@ __global__ __launch_bounds__(256) void chain16_kernel(K16 a) {
 // dh16: reverse pass carrying dH.  Per chunk and wave:
 //   dU   = lam (Kn dH) + P^T dO           (16 + 8 MFMA, chained)
 //   dRHS = T^T dU                         (8, chained);  dv = beta dRHS
-//   dH   = gam_C dH + QnT (gam dO) - KnT (beta gam dRHS)   (16 + 16, chained)
+//   dH   = gam_C dH + Qn^T (gam dO) - Kn^T (beta gam dRHS)   (16 + 16, chained)
 // Every chunk's incoming dH (the gradient at its end) is stored for grad16.
 // ---------------------------------------------------------------------------
 template <int C, typename TO>
 __global__ __launch_bounds__(256) void dh16_kernel(K16 a) {
   using IM = Img<C>;
   constexpr int NT = C / 16, LDC = IM::LDC;
-  constexpr uint32_t CB = IM::GT + 2 * IM::TM;  // gates | T^T | P^T
-  constexpr uint32_t KB = IM::KEY_B;            // Kn | KnT | QnT
+  constexpr uint32_t CB = IM::CHK;  // gates | T | P
+  constexpr uint32_t KB = IM::KEY;  // Kn | Qn
   __shared__ __align__(16) char bufA[CB + KB];
   __shared__ __align__(16) char bufB[CB + KB];
 
@@ -640,8 +649,8 @@ __global__ __launch_bounds__(256) void dh16_kernel(K16 a) {
   const ChainPos p = chain_pos(a);
   const int jcol = p.half * BV + 16 * w + c16;
   const int64_t hbase = (p.b * a.Hv + p.hv) * DK * DK + jcol;
-  const char* kim0 = a.kimg + (p.b * a.Hk + p.kh) * a.NC * static_cast<int64_t>(IM::KEY_B);
-  const char* cim0 = a.cimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::CHK_B);
+  const char* kim0 = a.kimg + (p.b * a.Hk + p.kh) * a.NC * static_cast<int64_t>(IM::KEY);
+  const char* cim0 = a.cimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::CHK);
   const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
   const uint32_t rowo = static_cast<uint32_t>(a.Hv) * DK * sizeof(TO);
   const uint32_t voffv = 4 * g * rowv + (p.hv * DK + jcol) * 2;
@@ -662,10 +671,8 @@ __global__ __launch_bounds__(256) void dh16_kernel(K16 a) {
     return make_rsrc(p0, static_cast<uint32_t>(rows_of(c)) * rowb);
   };
   auto stage = [&](int c, char* buf) {
-    const char* cim = cim0 + c * static_cast<int64_t>(IM::CHK_B);
-    dma<IM::GT>(make_rsrc(cim, IM::GT), 0, buf);
-    dma<2 * IM::TM>(make_rsrc(cim + IM::GT + IM::TM, 2 * IM::TM), 0, buf + IM::GT);
-    dma<KB>(make_rsrc(kim0 + c * static_cast<int64_t>(IM::KEY_B), KB), 0, buf + CB);
+    dma<CB>(make_rsrc(cim0 + c * static_cast<int64_t>(IM::CHK), CB), 0, buf);
+    dma<KB>(make_rsrc(kim0 + c * static_cast<int64_t>(IM::KEY), KB), 0, buf + CB);
   };
 
   uint32_t dcur[NT][4], dnext[NT][4];
@@ -693,11 +700,10 @@ __global__ __launch_bounds__(256) void dh16_kernel(K16 a) {
     const float* gam = reinterpret_cast<const float*>(cur);
     const float* lam = gam + C;
     const float* bet = gam + 2 * C;
-    const _Float16* TmT = reinterpret_cast<const _Float16*>(cur + IM::GT);
-    const _Float16* PmT = TmT + C * LDC;
+    const _Float16* Tm = reinterpret_cast<const _Float16*>(cur + IM::GT);
+    const _Float16* Pm = Tm + C * LDC;
     const _Float16* Kn = reinterpret_cast<const _Float16*>(cur + CB);
-    const _Float16* KnT = Kn + C * LDK;
-    const _Float16* QnT = KnT + DK * LDC;
+    const _Float16* Qn = Kn + C * LDK;
 
     f16x8 hf[NTK / 2];
     chain_frags<NTK>(hf, dh);
@@ -721,9 +727,9 @@ __global__ __launch_bounds__(256) void dh16_kernel(K16 a) {
     }
     f16x8 bf[NT / 2];
     chain_frags<NT>(bf, dof);
-    mma_chain_rows<NT, NT>(du, PmT, LDC, bf);
+    mma_chain_rows_t<NT, NT>(du, Pm, LDC, bf);
     chain_frags<NT>(bf, du);
-    mma_chain_rows<NT, NT>(dr, TmT, LDC, bf);
+    mma_chain_rows_t<NT, NT>(dr, Tm, LDC, bf);
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr) {
       const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
@@ -738,9 +744,9 @@ __global__ __launch_bounds__(256) void dh16_kernel(K16 a) {
 #pragma unroll
     for (int ti = 0; ti < NTK; ++ti) dh[ti] = dh[ti] * gc;
     chain_frags<NT>(bf, gdo);
-    mma_chain_rows<NTK, NT>(dh, QnT, LDC, bf);
+    mma_chain_rows_t<NTK, NT>(dh, Qn, LDK, bf);
     chain_frags<NT>(bf, dr);
-    mma_chain_rows<NTK, NT>(dh, KnT, LDC, bf);
+    mma_chain_rows_t<NTK, NT>(dh, Kn, LDK, bf);
     wait_all();
     __syncthreads();
 #pragma unroll
@@ -783,13 +789,15 @@ __global__ __launch_bounds__(256) void dh16_kernel(K16 a) {
 //   global memory: as chained strips for phase A and as row fragments for
 //   phases 1 and 2.
 // ---------------------------------------------------------------------------
+// acc[t] += A[16t : 16t+16, 0:K] Bm[0:K, n0 : n0+16], Bm row-major; the B
+// fragment is shared.
 template <int NO, int K>
-__device__ __forceinline__ void mma_rows(f32x4 (&acc)[NO], const _Float16* A, int lda, const _Float16* Bt, int ldb,
+__device__ __forceinline__ void mma_rows(f32x4 (&acc)[NO], const _Float16* A, int lda, const _Float16* Bm, int ldb,
                                          int n0) {
   const int r = lane_id() & 15, kl = (lane_id() >> 4) * 8;
 #pragma unroll
   for (int k0 = 0; k0 < K; k0 += 32) {
-    const f16x8 bfr = ld8(Bt + (n0 + r) * ldb + k0 + kl);
+    const f16x8 bfr = frag_t(Bm, ldb, k0, n0);
     f16x8 af[NO];
 #pragma unroll
     for (int t = 0; t < NO; ++t) af[t] = ld8(A + (16 * t + r) * lda + k0 + kl);
@@ -814,7 +822,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   constexpr int DPW = NQ >= NW ? NQ / NW : 1;    // C x C tiles per wave, all in one row tile
   constexpr int XB = 3 * C * LDX;
   static_assert(5 * C * LDC <= XB, "C x C stage buffers alias the strip buffers");
-  __shared__ __align__(16) char img[IM::CHK_B + IM::KEY_B];
+  __shared__ __align__(16) char img[IM::CHK + IM::KEY];
   __shared__ __align__(16) _Float16 xb[XB];
   __shared__ float sG[NW][C], sGc[NW][C], sB[NW][C], red[2][NW];
   __shared__ float sN[4][NW][C];  // L2-norm VJP row partials: |q|^2, q.dq_hat, |k|^2, k.dk_hat
@@ -832,9 +840,9 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   const bool qact = w * DPW < NQ;      // this wave owns C x C tiles
   const int qr = (w * DPW) / NT, qc0 = (w * DPW) % NT;
 
-  dma<IM::CHK_B, 512>(make_rsrc(a.cimg + cbase * static_cast<int64_t>(IM::CHK_B), IM::CHK_B), 0, img);
-  dma<IM::KEY_B, 512>(make_rsrc(a.kimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(IM::KEY_B), IM::KEY_B),
-                      0, img + IM::CHK_B);
+  dma<IM::CHK, 512>(make_rsrc(a.cimg + cbase * static_cast<int64_t>(IM::CHK), IM::CHK), 0, img);
+  dma<IM::KEY, 512>(make_rsrc(a.kimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(IM::KEY), IM::KEY), 0,
+                    img + IM::CHK);
   // H0 / dH: chained strips (rows 16ti + 4g + e, column jw) and row fragments
   // (row i2, columns 32ks + 8g ..) straight from global memory
   const rsrc_t hr = make_rsrc(a.hst + cbase * static_cast<int64_t>(DK * DK), DK * DK * 2);
@@ -873,11 +881,9 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   const float* bet = gam + 2 * C;
   const float* G2 = gam + 3 * C;
   const _Float16* Ts = reinterpret_cast<const _Float16*>(img + IM::GT);
-  const _Float16* TsT = Ts + C * LDC;
-  const _Float16* PsT = TsT + C * LDC;
-  const _Float16* Ks = reinterpret_cast<const _Float16*>(img + IM::CHK_B);
-  const _Float16* KsT = Ks + C * LDK;
-  const _Float16* QsT = KsT + DK * LDC;
+  const _Float16* Ps = Ts + C * LDC;
+  const _Float16* Ks = reinterpret_cast<const _Float16*>(img + IM::CHK);
+  const _Float16* Qs = Ks + C * LDK;
   const float gamC = gam[L - 1];
   _Float16* X0 = xb;             // dRHS, then dU
   _Float16* X1b = xb + C * LDX;  // dO, then RHS
@@ -927,9 +933,9 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   chain_frags<NT>(bf, rhs);
   mma_chain_rows<NT, NT>(u, Ts, LDC, bf);
   chain_frags<NT>(bf, dov);
-  mma_chain_rows<NT, NT>(du, PsT, LDC, bf);
+  mma_chain_rows_t<NT, NT>(du, Ps, LDC, bf);
   chain_frags<NT>(bf, du);
-  mma_chain_rows<NT, NT>(dr, TsT, LDC, bf);
+  mma_chain_rows_t<NT, NT>(dr, Ts, LDC, bf);
 #pragma unroll
   for (int tr = 0; tr < NT; ++tr)
 #pragma unroll
@@ -1034,7 +1040,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * qr + 4 * g + e;
         t4[e] = static_cast<_Float16>(dT[t][e]);
-        const float pv = static_cast<float>(PsT[s2 * LDC + r]);  // P_rs
+        const float pv = static_cast<float>(Ps[r * LDC + s2]);  // P_rs
         const float m = s2 <= r ? __builtin_amdgcn_exp2f(G2[r] - G2[s2]) : 0.f;
         const float dpp = dP[t][e] * pv;
         rgc[e] += dpp;
@@ -1053,7 +1059,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     f32x4 m1[DPW];
 #pragma unroll
     for (int t = 0; t < DPW; ++t) m1[t] = zero4();
-    mma_cols<DPW, C>(m1, TsT, LDC, 16 * qr, dTT, LDC, 16 * qc0);
+    mma_cols_t<DPW, C>(m1, Ts, LDC, 16 * qr, dTT, LDC, 16 * qc0);
 #pragma unroll
     for (int t = 0; t < DPW; ++t)
 #pragma unroll
@@ -1107,9 +1113,9 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   f32x4 dq[NT], dk[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) dq[t] = dk[t] = zero4();
-  mma_rows<NT, C>(dq, dPm, LDC, KsT, LDC, 16 * w);
-  mma_rows<NT, C>(dk, dPmT, LDC, QsT, LDC, 16 * w);
-  mma_rows<NT, C>(dk, dAs, LDC, KsT, LDC, 16 * w);
+  mma_rows<NT, C>(dq, dPm, LDC, Ks, LDK, 16 * w);
+  mma_rows<NT, C>(dk, dPmT, LDC, Qs, LDK, 16 * w);
+  mma_rows<NT, C>(dk, dAs, LDC, Ks, LDK, 16 * w);
   float dqv[NT][4], dkv[NT][4];
   float gcx = 0.f;
 #pragma unroll
@@ -1117,8 +1123,8 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * rt + 4 * g + e;
-      const float qn = static_cast<float>(QsT[i2 * LDC + r]);
-      const float kn = static_cast<float>(KsT[i2 * LDC + r]);
+      const float qn = static_cast<float>(Qs[r * LDK + i2]);
+      const float kn = static_cast<float>(Ks[r * LDK + i2]);
       const float t3 = lam[r] * kn * x3[rt][e];
       gcx += t3;
       const float rg = row16_sum(gam[r] * qn * x2[rt][e] - t3);
@@ -1283,8 +1289,8 @@ Ws16 plan16(const Shape& s, bool bwd) {
   const size_t nk = static_cast<size_t>(s.B) * s.Hk * nc, nv = static_cast<size_t>(s.B) * s.Hv * nc;
   Ws16 w{};
   size_t off = 0;
-  w.kimg = off; off = up(off + nk * (bwd ? IM::KEY_B : IM::KEY_F));
-  w.cimg = off; off = up(off + nv * (bwd ? IM::CHK_B : IM::CHK_F));
+  w.kimg = off; off = up(off + nk * IM::KEY);
+  w.cimg = off; off = up(off + nv * IM::CHK);
   if (bwd) {
     const size_t rows = static_cast<size_t>(s.B * s.T) * s.Hk;
     w.hst = off;  off = up(off + nv * DK * DK * 2);
@@ -1322,10 +1328,10 @@ K16 args16(const Shape& s, int C, void* ws, const Ws16& w) {
   return a;
 }
 
-template <int C, bool BWD>
+template <int C>
 hipError_t prep16(const K16& a, hipStream_t st) {
   ProfScope ps("chunk_prep", st);
-  hipLaunchKernelGGL((prep16_kernel<C, BWD>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prep16_kernel<C>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1376,7 +1382,7 @@ hipError_t fwd_all(const Shape& s, const ChunkFwdArgs& x, void* ws, hipStream_t 
   a.h0 = x.h0;
   a.o = x.o;
   a.ht = x.ht;
-  hipError_t e = prep16<C, false>(a, st);
+  hipError_t e = prep16<C>(a, st);
   return e == hipSuccess ? chain16<C, TO, true, false>(a, st) : e;
 }
 
@@ -1397,7 +1403,7 @@ hipError_t bwd_all(const Shape& s, const ChunkBwdArgs& x, void* ws, hipStream_t 
   a.dbeta = x.dbeta;
   a.dq = x.dq;
   a.dk = x.dk;
-  hipError_t e = prep16<C, true>(a, st);
+  hipError_t e = prep16<C>(a, st);
   if (e == hipSuccess) e = chain16<C, TO, false, true>(a, st);
   if (e == hipSuccess) e = dh16<C, TO>(a, st);
   if (e == hipSuccess) e = grad16<C, TO>(a, st);
