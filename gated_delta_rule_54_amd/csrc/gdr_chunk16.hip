@@ -52,6 +52,7 @@ constexpr int NTK = DK / 16;  // 16-row tiles of a state strip
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -93,16 +94,16 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t nbytes) {
 
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Whole-workgroup (NTH threads) copy of NBYTES from buffer r (byte offset
-// off) into LDS at dst, without registers: 16-byte unit e travels in lane
-// e % 64 of wave (e / 64) % (NTH / 64) during round e / NTH
-// (buffer_load_dwordx4 ... lds writes the wave's 64 units to consecutive LDS
-// addresses).  Completion is observed by wait_all() followed by a barrier.
-template <int NBYTES, int NTH = 256>
-__device__ __forceinline__ void dma(rsrc_t r, uint32_t off, char* dst) {
+// Copy by NTH threads (thread tid of the group, in its wave wq) of NBYTES
+// from buffer r (byte offset off) into LDS at dst, without registers:
+// 16-byte unit e travels in lane e % 64 of wave (e / 64) % (NTH / 64) during
+// round e / NTH (buffer_load_dwordx4 ... lds writes the wave's 64 units to
+// consecutive LDS addresses).  Completion is observed by wait_all() followed
+// by a barrier.
+template <int NBYTES, int NTH>
+__device__ __forceinline__ void dma(rsrc_t r, uint32_t off, char* dst, int tid, int w) {
   static_assert(NBYTES % 16 == 0, "images are made of 16-byte units");
   constexpr int N16 = NBYTES / 16;
-  const int tid = threadIdx.x, w = wave_id();
 #pragma unroll
   for (int u = 0; u < (N16 + NTH - 1) / NTH; ++u) {
     if (N16 % NTH == 0 || NTH * u + tid < N16)
@@ -487,35 +488,167 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
 }
 
 // ---------------------------------------------------------------------------
+// Chain kernels: four compute waves and one producer wave per workgroup.
+// The compute waves own the state in MFMA accumulators and touch only LDS;
+// the producer wave issues all bulk global traffic of the chunk loop: it
+// copies the next chunk's images and the rows of v / dO for this value half
+// (C x 64 bf16) into LDS by buffer_load ... lds, and stores the previous
+// chunk's o / dv from an LDS tile [C][LDO] (written from the accumulators)
+// as 16-byte rows.  One barrier per chunk; a wave stalled on memory issue
+// never holds up the matrix cores.  Chunk states (H for the VJP, dH) leave
+// the compute waves as four 16-byte stores per lane in chained-fragment
+// order (see frag_off).
+// ---------------------------------------------------------------------------
+constexpr int NCW = 4;  // compute waves of a chain workgroup; wave NCW is the producer
+
+// Workgroup barrier that orders LDS accesses only (global stores in flight
+// stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Chunk states (H entering a chunk, dH at a chunk's end; fp16) are stored
+// per (b, v-head, chunk) as [8][NTK / 2][64][8] halves: entry (wg, kb, lane,
+// i) is row 32kb + 16(i / 4) + 4(lane / 16) + i % 4, column 16wg + lane % 16
+// of the state, i.e. the chained fragment kb of that lane's 16-column strip.
+// Byte offset of this lane's fragment kb of column group wg:
+__device__ __forceinline__ uint32_t frag_off(int wg, int kb) {
+  return static_cast<uint32_t>(((wg * (NTK / 2) + kb) * 64 + lane_id()) * 16);
+}
+
+// Copy by one wave of rows 0 .. ROWS-1 (RB bytes each, rows rowb bytes apart
+// from byte col0 of buffer r) into LDS at dst as a packed [ROWS][RB] tile;
+// rows >= L repeat row L - 1 (finite values that the chunk algebra multiplies
+// by zero).
+template <int ROWS, int RB>
+__device__ __forceinline__ void dma_rows(rsrc_t r, uint32_t rowb, uint32_t col0, int L, char* dst) {
+  constexpr int UPR = RB / 16, N16 = ROWS * UPR;
+  static_assert(N16 % 64 == 0, "whole wave rounds");
+  const int lane = lane_id();
+#pragma unroll
+  for (int u = 0; u < N16 / 64; ++u) {
+    const int e = 64 * u + lane;
+    const int row = e / UPR, cu = e % UPR;
+    const int rr = row < L ? row : L - 1;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void)(dst + 1024 * u), 16, rr * rowb + col0 + 16 * cu, 0, 0, 0);
+  }
+}
+
+// Rows r0 .. r0+3 of column c0 + (lane & 15) of a packed bf16 [*][ld] tile, as fp32.
+__device__ __forceinline__ void tile_col4_bf16(float (&x)[4], const uint16_t* M, int ld, int r0, int c0) {
+  const int n = c0 + (lane_id() & 15);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(static_cast<uint32_t>(M[(r0 + e) * ld + n]) << 16);
+}
+
+// Output tile of one chunk and value half: [C][LDO] elements of TO.
+template <typename TO>
+struct OutTile {
+  static constexpr int LDO = std::is_same_v<TO, float> ? BV + 4 : BV + 8;
+  static constexpr int UPR = BV * static_cast<int>(sizeof(TO)) / 16;  // 16-byte units per row
+  template <int C>
+  static constexpr uint32_t bytes() { return C * LDO * sizeof(TO); }
+};
+
+// This lane's strip rows 16tr + 4g + e of column col into the output tile.
+template <typename TO, int NT>
+__device__ __forceinline__ void put_strip(char* os, int col, const f32x4 (&x)[NT]) {
+  constexpr int LDO = OutTile<TO>::LDO;
+  const int g = lane_id() >> 4;
+#pragma unroll
+  for (int tr = 0; tr < NT; ++tr)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = (16 * tr + 4 * g + e) * LDO + col;
+      if constexpr (std::is_same_v<TO, float>)
+        reinterpret_cast<float*>(os)[i] = x[tr][e];
+      else
+        reinterpret_cast<uint16_t*>(os)[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x[tr][e]));
+    }
+}
+
+// One wave stores the output tile's rows to buffer r (rows rowb bytes apart
+// from byte col0); rows past the buffer end are dropped.
+template <typename TO, int C>
+__device__ __forceinline__ void flush_tile(const char* os, rsrc_t r, uint32_t rowb, uint32_t col0) {
+  constexpr int LDO = OutTile<TO>::LDO, UPR = OutTile<TO>::UPR, N16 = C * UPR;
+  static_assert(N16 % 64 == 0, "whole wave rounds");
+  const int lane = lane_id();
+#pragma unroll
+  for (int u = 0; u < N16 / 64; ++u) {
+    const int e = 64 * u + lane, row = e / UPR, cu = e % UPR;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(os + row * LDO * sizeof(TO) + 16 * cu);
+    __builtin_amdgcn_raw_buffer_store_b128(val, r, row * rowb + col0 + 16 * cu, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // chain16: forward pass over chunks (WRITE_O: outputs; STORE_H: every
-// chunk's entry state for the VJP).  Per chunk and wave:
+// chunk's entry state for the VJP).  Per chunk and compute wave:
 //   Y = Kn H, Z = Qn H          (16 MFMA each, H chained)
 //   U = T (beta (V - gam Y))    (8, chained)
 //   O = gam Z + P U             (8, chained)
 //   H = gam_C H + Kn^T (lam U)  (16, chained)
 // ---------------------------------------------------------------------------
 template <int C, typename TO, bool WRITE_O, bool STORE_H>
-__global__ __launch_bounds__(256) void chain16_kernel(K16 a) {
+__global__ __launch_bounds__(64 * (NCW + 1)) void chain16_kernel(K16 a) {
   using IM = Img<C>;
   constexpr int NT = C / 16, LDC = IM::LDC;
   constexpr uint32_t CB = WRITE_O ? IM::CHK : IM::GT + IM::TM;  // gates | T (| P)
   constexpr uint32_t KB = WRITE_O ? IM::KEY : IM::KN;           // Kn (| Qn)
-  constexpr uint32_t KSTR = IM::KEY;
-  constexpr uint32_t CSTR = IM::CHK;
-  __shared__ __align__(16) char bufA[CB + KB];
-  __shared__ __align__(16) char bufB[CB + KB];
+  constexpr uint32_t VB = C * BV * 2;                           // v tile [C][BV] bf16
+  constexpr uint32_t OB = WRITE_O ? OutTile<TO>::template bytes<C>() : 16;
+  __shared__ __align__(16) char bufA[CB + KB + VB];
+  __shared__ __align__(16) char bufB[CB + KB + VB];
+  __shared__ __align__(16) char osA[OB];
+  __shared__ __align__(16) char osB[OB];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int w = wave_id(), lane = lane_id(), g = lane >> 4, c16 = lane & 15;
   const ChainPos p = chain_pos(a);
-  const int jcol = p.half * BV + 16 * w + c16;  // this lane's state column
-  const int64_t hbase = (p.b * a.Hv + p.hv) * DK * DK + jcol;
-  const char* kim0 = a.kimg + (p.b * a.Hk + p.kh) * a.NC * static_cast<int64_t>(KSTR);
-  const char* cim0 = a.cimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(CSTR);
+  auto rows_of = [&](int c) { return static_cast<int>(a.T - static_cast<int64_t>(c) * C < C ? a.T - static_cast<int64_t>(c) * C : C); };
+  auto seq_rsrc = [&](const void* base, int esize, int c, uint32_t rowb) {
+    const char* p0 = static_cast<const char*>(base) + (p.b * a.T + static_cast<int64_t>(c) * C) * a.Hv * DK * esize;
+    return make_rsrc(p0, static_cast<uint32_t>(rows_of(c)) * rowb);
+  };
   const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;         // bf16 row pitch of v
   const uint32_t rowo = static_cast<uint32_t>(a.Hv) * DK * sizeof(TO);  // row pitch of o
-  const uint32_t voffv = 4 * g * rowv + (p.hv * DK + jcol) * 2;
-  const uint32_t voffo = 4 * g * rowo + (p.hv * DK + jcol) * static_cast<uint32_t>(sizeof(TO));
 
+  if (w == NCW) {  // ---- producer wave
+    const char* kim0 = a.kimg + (p.b * a.Hk + p.kh) * a.NC * static_cast<int64_t>(IM::KEY);
+    const char* cim0 = a.cimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::CHK);
+    const uint32_t colv = (p.hv * DK + p.half * BV) * 2;
+    const uint32_t colo = (p.hv * DK + p.half * BV) * static_cast<uint32_t>(sizeof(TO));
+    auto stage = [&](int c, char* buf) {
+      dma<CB, 64>(make_rsrc(cim0 + c * static_cast<int64_t>(IM::CHK), CB), 0, buf, lane, 0);
+      dma<KB, 64>(make_rsrc(kim0 + c * static_cast<int64_t>(IM::KEY), KB), 0, buf + CB, lane, 0);
+      dma_rows<C, BV * 2>(seq_rsrc(a.v, 2, c, rowv), rowv, colv, rows_of(c), buf + CB + KB);
+    };
+    auto pstep = [&](int c, char* nxt, const char* os_prev) __attribute__((always_inline)) {
+      if (c + 1 < a.NC) stage(c + 1, nxt);
+      if constexpr (WRITE_O) {
+        if (c > 0) flush_tile<TO, C>(os_prev, seq_rsrc(a.o, sizeof(TO), c - 1, rowo), rowo, colo);
+      }
+      wait_all();
+      lds_barrier();
+    };
+    stage(0, bufA);
+    wait_all();
+    lds_barrier();
+    for (int c = 0; c < a.NC; c += 2) {
+      pstep(c, bufB, osB);
+      if (c + 1 < a.NC) pstep(c + 1, bufA, osA);
+    }
+    if constexpr (WRITE_O)
+      flush_tile<TO, C>(((a.NC - 1) & 1) ? osB : osA, seq_rsrc(a.o, sizeof(TO), a.NC - 1, rowo), rowo, colo);
+    return;
+  }
+
+  // ---- compute waves
+  const int jcol = p.half * BV + 16 * w + c16;  // this lane's state column
+  const int wg = p.half * NCW + w;              // column group of the chunk-state layout
+  const int64_t hbase = (p.b * a.Hv + p.hv) * DK * DK + jcol;
   f32x4 h[NTK];
 #pragma unroll
   for (int ti = 0; ti < NTK; ++ti) {
@@ -525,40 +658,9 @@ __global__ __launch_bounds__(256) void chain16_kernel(K16 a) {
       for (int e = 0; e < 4; ++e) h[ti][e] = a.h0[hbase + (16 * ti + 4 * g + e) * DK];
     }
   }
-  auto rows_of = [&](int c) { return static_cast<int>(a.T - static_cast<int64_t>(c) * C < C ? a.T - static_cast<int64_t>(c) * C : C); };
-  auto seq_rsrc = [&](const void* base, int esize, int c, uint32_t rowb) {
-    const char* p0 = static_cast<const char*>(base) + (p.b * a.T + static_cast<int64_t>(c) * C) * a.Hv * DK * esize;
-    return make_rsrc(p0, static_cast<uint32_t>(rows_of(c)) * rowb);
-  };
-  auto stage = [&](int c, char* buf) {
-    dma<CB>(make_rsrc(cim0 + c * static_cast<int64_t>(CSTR), CB), 0, buf);
-    dma<KB>(make_rsrc(kim0 + c * static_cast<int64_t>(KSTR), KB), 0, buf + CB);
-  };
+  lds_barrier();
 
-  uint32_t vcur[NT][4], vnext[NT][4];
-  f32x4 o[NT];
-  stage(0, bufA);
-  load_strip_buf<NT>(vcur, seq_rsrc(a.v, 2, 0, rowv), voffv, rowv);
-  wait_all();
-  __syncthreads();
-
-  auto step = [&](int c, const char* cur, char* nxt) __attribute__((always_inline)) {
-    if (c + 1 < a.NC) {
-      stage(c + 1, nxt);
-      load_strip_buf<NT>(vnext, seq_rsrc(a.v, 2, c + 1, rowv), voffv, rowv);
-    }
-    if constexpr (WRITE_O) {  // previous chunk's outputs (their stores retire during this chunk)
-      if (c > 0) store_strip_buf<TO, NT>(seq_rsrc(a.o, sizeof(TO), c - 1, rowo), voffo, rowo, o);
-    }
-    if constexpr (STORE_H) {  // chunk entry state, natural [Dk][Dv] layout
-      const rsrc_t hr = make_rsrc(a.hst + ((p.b * a.Hv + p.hv) * a.NC + c) * static_cast<int64_t>(DK * DK), DK * DK * 2);
-#pragma unroll
-      for (int ti = 0; ti < NTK; ++ti)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<_Float16>(h[ti][e])), hr,
-                                                ((16 * ti + 4 * g + e) * DK + jcol) * 2, 0, 0);
-    }
+  auto step = [&](int c, const char* cur, char* os) __attribute__((always_inline)) {
     const float* gam = reinterpret_cast<const float*>(cur);
     const float* lam = gam + C;
     const float* bet = gam + 2 * C;
@@ -566,10 +668,11 @@ __global__ __launch_bounds__(256) void chain16_kernel(K16 a) {
     const _Float16* Pm = Tm + C * LDC;
     const _Float16* Kn = reinterpret_cast<const _Float16*>(cur + CB);
     const _Float16* Qn = Kn + C * LDK;
+    const uint16_t* Vs = reinterpret_cast<const uint16_t*>(cur + CB + KB);
 
     f16x8 hf[NTK / 2];
     chain_frags<NTK>(hf, h);
-    f32x4 y[NT], u[NT];
+    f32x4 y[NT], u[NT], o[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) y[t] = u[t] = zero4();
     mma_chain_rows<NT, NTK>(y, Kn, LDK, hf);
@@ -578,13 +681,19 @@ __global__ __launch_bounds__(256) void chain16_kernel(K16 a) {
       for (int t = 0; t < NT; ++t) o[t] = zero4();
       mma_chain_rows<NT, NTK>(o, Qn, LDK, hf);
     }
+    if constexpr (STORE_H) {  // entry state of chunk c
+      const rsrc_t hr = make_rsrc(a.hst + ((p.b * a.Hv + p.hv) * a.NC + c) * static_cast<int64_t>(DK * DK), DK * DK * 2);
+#pragma unroll
+      for (int kb = 0; kb < NTK / 2; ++kb)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hf[kb]), hr, frag_off(wg, kb), 0, 0);
+    }
     f32x4 rhs[NT];
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr) {
       const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * tr + 4 * g);
       const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
       float vv[4];
-      unpack_strip(vv, vcur[tr]);
+      tile_col4_bf16(vv, Vs, BV, 16 * tr + 4 * g, 16 * w);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         rhs[tr][e] = bv[e] * (vv[e] - gv[e] * y[tr][e]);
@@ -609,18 +718,13 @@ __global__ __launch_bounds__(256) void chain16_kernel(K16 a) {
 #pragma unroll
     for (int ti = 0; ti < NTK; ++ti) h[ti] = h[ti] * gc;
     mma_chain_rows_t<NTK, NT>(h, Kn, LDK, bf);
-    wait_all();
-    __syncthreads();
-#pragma unroll
-    for (int tr = 0; tr < NT; ++tr)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vcur[tr][e] = vnext[tr][e];
+    if constexpr (WRITE_O) put_strip<TO, NT>(os, 16 * w + c16, o);
+    lds_barrier();
   };
   for (int c = 0; c < a.NC; c += 2) {
-    step(c, bufA, bufB);
-    if (c + 1 < a.NC) step(c + 1, bufB, bufA);
+    step(c, bufA, osA);
+    if (c + 1 < a.NC) step(c + 1, bufB, osB);
   }
-  if constexpr (WRITE_O) store_strip_buf<TO, NT>(seq_rsrc(a.o, sizeof(TO), a.NC - 1, rowo), voffo, rowo, o);
   if (a.ht) {
 #pragma unroll
     for (int ti = 0; ti < NTK; ++ti)
@@ -630,32 +734,66 @@ __global__ __launch_bounds__(256) void chain16_kernel(K16 a) {
 }
 
 // ---------------------------------------------------------------------------
-// dh16: reverse pass carrying dH.  Per chunk and wave:
+// dh16: reverse pass carrying dH.  Per chunk and compute wave:
 //   dU   = lam (Kn dH) + P^T dO           (16 + 8 MFMA, chained)
 //   dRHS = T^T dU                         (8, chained);  dv = beta dRHS
 //   dH   = gam_C dH + Qn^T (gam dO) - Kn^T (beta gam dRHS)   (16 + 16, chained)
 // Every chunk's incoming dH (the gradient at its end) is stored for grad16.
 // ---------------------------------------------------------------------------
 template <int C, typename TO>
-__global__ __launch_bounds__(256) void dh16_kernel(K16 a) {
+__global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
   using IM = Img<C>;
   constexpr int NT = C / 16, LDC = IM::LDC;
   constexpr uint32_t CB = IM::CHK;  // gates | T | P
   constexpr uint32_t KB = IM::KEY;  // Kn | Qn
-  __shared__ __align__(16) char bufA[CB + KB];
-  __shared__ __align__(16) char bufB[CB + KB];
+  constexpr uint32_t VB = C * BV * 2;
+  constexpr uint32_t OB = OutTile<TO>::template bytes<C>();
+  __shared__ __align__(16) char bufA[CB + KB + VB];
+  __shared__ __align__(16) char bufB[CB + KB + VB];
+  __shared__ __align__(16) char osA[OB];
+  __shared__ __align__(16) char osB[OB];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int w = wave_id(), lane = lane_id(), g = lane >> 4, c16 = lane & 15;
   const ChainPos p = chain_pos(a);
-  const int jcol = p.half * BV + 16 * w + c16;
-  const int64_t hbase = (p.b * a.Hv + p.hv) * DK * DK + jcol;
-  const char* kim0 = a.kimg + (p.b * a.Hk + p.kh) * a.NC * static_cast<int64_t>(IM::KEY);
-  const char* cim0 = a.cimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::CHK);
+  auto rows_of = [&](int c) { return static_cast<int>(a.T - static_cast<int64_t>(c) * C < C ? a.T - static_cast<int64_t>(c) * C : C); };
+  auto seq_rsrc = [&](const void* base, int esize, int c, uint32_t rowb) {
+    const char* p0 = static_cast<const char*>(base) + (p.b * a.T + static_cast<int64_t>(c) * C) * a.Hv * DK * esize;
+    return make_rsrc(p0, static_cast<uint32_t>(rows_of(c)) * rowb);
+  };
   const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
   const uint32_t rowo = static_cast<uint32_t>(a.Hv) * DK * sizeof(TO);
-  const uint32_t voffv = 4 * g * rowv + (p.hv * DK + jcol) * 2;
-  const uint32_t voffo = 4 * g * rowo + (p.hv * DK + jcol) * static_cast<uint32_t>(sizeof(TO));
 
+  if (w == NCW) {  // ---- producer wave: chunks NC-1, NC-2, ...
+    const char* kim0 = a.kimg + (p.b * a.Hk + p.kh) * a.NC * static_cast<int64_t>(IM::KEY);
+    const char* cim0 = a.cimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::CHK);
+    const uint32_t colv = (p.hv * DK + p.half * BV) * 2;
+    const uint32_t colo = (p.hv * DK + p.half * BV) * static_cast<uint32_t>(sizeof(TO));
+    auto stage = [&](int c, char* buf) {
+      dma<CB, 64>(make_rsrc(cim0 + c * static_cast<int64_t>(IM::CHK), CB), 0, buf, lane, 0);
+      dma<KB, 64>(make_rsrc(kim0 + c * static_cast<int64_t>(IM::KEY), KB), 0, buf + CB, lane, 0);
+      dma_rows<C, BV * 2>(seq_rsrc(a.dout, 2, c, rowv), rowv, colv, rows_of(c), buf + CB + KB);
+    };
+    auto pstep = [&](int c, char* nxt, const char* os_prev) __attribute__((always_inline)) {
+      if (c > 0) stage(c - 1, nxt);
+      if (c + 1 < a.NC) flush_tile<TO, C>(os_prev, seq_rsrc(a.dv, sizeof(TO), c + 1, rowo), rowo, colo);
+      wait_all();
+      lds_barrier();
+    };
+    stage(a.NC - 1, bufA);
+    wait_all();
+    lds_barrier();
+    for (int i = 0; i < a.NC; i += 2) {
+      pstep(a.NC - 1 - i, bufB, osB);
+      if (i + 1 < a.NC) pstep(a.NC - 2 - i, bufA, osA);
+    }
+    flush_tile<TO, C>(((a.NC - 1) & 1) ? osB : osA, seq_rsrc(a.dv, sizeof(TO), 0, rowo), rowo, colo);
+    return;
+  }
+
+  // ---- compute waves
+  const int jcol = p.half * BV + 16 * w + c16;
+  const int wg = p.half * NCW + w;
+  const int64_t hbase = (p.b * a.Hv + p.hv) * DK * DK + jcol;
   f32x4 dh[NTK];
 #pragma unroll
   for (int ti = 0; ti < NTK; ++ti) {
@@ -665,38 +803,9 @@ __global__ __launch_bounds__(256) void dh16_kernel(K16 a) {
       for (int e = 0; e < 4; ++e) dh[ti][e] = a.dht[hbase + (16 * ti + 4 * g + e) * DK];
     }
   }
-  auto rows_of = [&](int c) { return static_cast<int>(a.T - static_cast<int64_t>(c) * C < C ? a.T - static_cast<int64_t>(c) * C : C); };
-  auto seq_rsrc = [&](const void* base, int esize, int c, uint32_t rowb) {
-    const char* p0 = static_cast<const char*>(base) + (p.b * a.T + static_cast<int64_t>(c) * C) * a.Hv * DK * esize;
-    return make_rsrc(p0, static_cast<uint32_t>(rows_of(c)) * rowb);
-  };
-  auto stage = [&](int c, char* buf) {
-    dma<CB>(make_rsrc(cim0 + c * static_cast<int64_t>(IM::CHK), CB), 0, buf);
-    dma<KB>(make_rsrc(kim0 + c * static_cast<int64_t>(IM::KEY), KB), 0, buf + CB);
-  };
+  lds_barrier();
 
-  uint32_t dcur[NT][4], dnext[NT][4];
-  f32x4 dvv[NT];
-  stage(a.NC - 1, bufA);
-  load_strip_buf<NT>(dcur, seq_rsrc(a.dout, 2, a.NC - 1, rowv), voffv, rowv);
-  wait_all();
-  __syncthreads();
-
-  auto step = [&](int c, const char* cur, char* nxt) __attribute__((always_inline)) {
-    if (c > 0) {
-      stage(c - 1, nxt);
-      load_strip_buf<NT>(dnext, seq_rsrc(a.dout, 2, c - 1, rowv), voffv, rowv);
-    }
-    if (c + 1 < a.NC) store_strip_buf<TO, NT>(seq_rsrc(a.dv, sizeof(TO), c + 1, rowo), voffo, rowo, dvv);
-    {  // gradient at this chunk's end, natural [Dk][Dv] layout
-      const rsrc_t hr = make_rsrc(a.dhst + ((p.b * a.Hv + p.hv) * a.NC + c) * static_cast<int64_t>(DK * DK), DK * DK * 2);
-#pragma unroll
-      for (int ti = 0; ti < NTK; ++ti)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<_Float16>(dh[ti][e])), hr,
-                                                ((16 * ti + 4 * g + e) * DK + jcol) * 2, 0, 0);
-    }
+  auto step = [&](int c, const char* cur, char* os) __attribute__((always_inline)) {
     const float* gam = reinterpret_cast<const float*>(cur);
     const float* lam = gam + C;
     const float* bet = gam + 2 * C;
@@ -704,20 +813,27 @@ __global__ __launch_bounds__(256) void dh16_kernel(K16 a) {
     const _Float16* Pm = Tm + C * LDC;
     const _Float16* Kn = reinterpret_cast<const _Float16*>(cur + CB);
     const _Float16* Qn = Kn + C * LDK;
+    const uint16_t* Ds = reinterpret_cast<const uint16_t*>(cur + CB + KB);
 
     f16x8 hf[NTK / 2];
     chain_frags<NTK>(hf, dh);
-    f32x4 du[NT], dr[NT];
+    f32x4 du[NT], dr[NT], dvv[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) du[t] = dr[t] = zero4();
     mma_chain_rows<NT, NTK>(du, Kn, LDK, hf);
+    {  // gradient at this chunk's end
+      const rsrc_t hr = make_rsrc(a.dhst + ((p.b * a.Hv + p.hv) * a.NC + c) * static_cast<int64_t>(DK * DK), DK * DK * 2);
+#pragma unroll
+      for (int kb = 0; kb < NTK / 2; ++kb)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hf[kb]), hr, frag_off(wg, kb), 0, 0);
+    }
     f32x4 dof[NT], gdo[NT];
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr) {
       const f32x4 lv = *reinterpret_cast<const f32x4*>(lam + 16 * tr + 4 * g);
       const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * tr + 4 * g);
       float x[4];
-      unpack_strip(x, dcur[tr]);
+      tile_col4_bf16(x, Ds, BV, 16 * tr + 4 * g, 16 * w);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         du[tr][e] *= lv[e];
@@ -740,6 +856,7 @@ __global__ __launch_bounds__(256) void dh16_kernel(K16 a) {
         dr[tr][e] = -gv[e] * dvv[tr][e];
       }
     }
+    put_strip<TO, NT>(os, 16 * w + c16, dvv);
     const float gc = gam[rows_of(c) - 1];
 #pragma unroll
     for (int ti = 0; ti < NTK; ++ti) dh[ti] = dh[ti] * gc;
@@ -747,19 +864,13 @@ __global__ __launch_bounds__(256) void dh16_kernel(K16 a) {
     mma_chain_rows_t<NTK, NT>(dh, Qn, LDK, bf);
     chain_frags<NT>(bf, dr);
     mma_chain_rows_t<NTK, NT>(dh, Kn, LDK, bf);
-    wait_all();
-    __syncthreads();
-#pragma unroll
-    for (int tr = 0; tr < NT; ++tr)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dcur[tr][e] = dnext[tr][e];
+    lds_barrier();
   };
   // chunks NC-1, NC-2, ... alternate between the two buffers
   for (int i = 0; i < a.NC; i += 2) {
-    step(a.NC - 1 - i, bufA, bufB);
-    if (i + 1 < a.NC) step(a.NC - 2 - i, bufB, bufA);
+    step(a.NC - 1 - i, bufA, osA);
+    if (i + 1 < a.NC) step(a.NC - 2 - i, bufB, osB);
   }
-  store_strip_buf<TO, NT>(seq_rsrc(a.dv, sizeof(TO), 0, rowo), voffo, rowo, dvv);
   if (a.dh0) {
 #pragma unroll
     for (int ti = 0; ti < NTK; ++ti)
@@ -807,9 +918,7 @@ __device__ __forceinline__ void mma_rows(f32x4 (&acc)[NO], const _Float16* A, in
 }
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ _Float16 h_of(uint32_t u) { return __builtin_bit_cast(_Float16, static_cast<uint16_t>(u)); }
 
 enum GradMode { kFirst = 0, kMid = 1, kLast = 2, kOnly = 3 };
 
@@ -827,6 +936,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   __shared__ float sG[NW][C], sGc[NW][C], sB[NW][C], red[2][NW];
   __shared__ float sN[4][NW][C];  // L2-norm VJP row partials: |q|^2, q.dq_hat, |k|^2, k.dk_hat
   __shared__ __align__(16) float sDot[4][C];
+  __shared__ __align__(16) _Float16 Hs[DK * LDK];  // H0, then dH, as Hs[j][i]
 
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int c = blockIdx.x, kh = blockIdx.y;
@@ -840,29 +950,28 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   const bool qact = w * DPW < NQ;      // this wave owns C x C tiles
   const int qr = (w * DPW) / NT, qc0 = (w * DPW) % NT;
 
-  dma<IM::CHK, 512>(make_rsrc(a.cimg + cbase * static_cast<int64_t>(IM::CHK), IM::CHK), 0, img);
+  dma<IM::CHK, 512>(make_rsrc(a.cimg + cbase * static_cast<int64_t>(IM::CHK), IM::CHK), 0, img, tid, w);
   dma<IM::KEY, 512>(make_rsrc(a.kimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(IM::KEY), IM::KEY), 0,
-                    img + IM::CHK);
-  // H0 / dH: chained strips (rows 16ti + 4g + e, column jw) and row fragments
-  // (row i2, columns 32ks + 8g ..) straight from global memory
+                    img + IM::CHK, tid, w);
+  // H0 / dH: this lane's chained strips (rows 16ti + 4g + e, column jw), as
+  // stored by the chain kernels; the row fragments of phases 1 / 2 come from
+  // the transposed copy Hs written from these strips
   const rsrc_t hr = make_rsrc(a.hst + cbase * static_cast<int64_t>(DK * DK), DK * DK * 2);
   const rsrc_t dhr = make_rsrc(a.dhst + cbase * static_cast<int64_t>(DK * DK), DK * DK * 2);
-  uint32_t h0u[NTK][4], dhu[NTK][4];
+  f16x8 h0f[NTK / 2], dhf[NTK / 2];
 #pragma unroll
-  for (int ti = 0; ti < NTK; ++ti)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t off = ((16 * ti + 4 * g + e) * DK + jw) * 2;
-      h0u[ti][e] = __builtin_amdgcn_raw_buffer_load_b16(hr, off, 0, 0);
-      dhu[ti][e] = __builtin_amdgcn_raw_buffer_load_b16(dhr, off, 0, 0);
-    }
-  u32x4 h0r[DK / 32], dhrw[DK / 32];
-#pragma unroll
-  for (int ks = 0; ks < DK / 32; ++ks) {
-    const uint32_t off = (i2 * DK + 32 * ks + 8 * g) * 2;
-    h0r[ks] = __builtin_amdgcn_raw_buffer_load_b128(hr, off, 0, 0);
-    dhrw[ks] = __builtin_amdgcn_raw_buffer_load_b128(dhr, off, 0, 0);
+  for (int kb = 0; kb < NTK / 2; ++kb) {
+    h0f[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(hr, frag_off(w, kb), 0, 0));
+    dhf[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(dhr, frag_off(w, kb), 0, 0));
   }
+  // Hs[j][i] <- strips (rows i of column j = jw)
+  auto put_state = [&](const f16x8 (&f)[NTK / 2]) {
+#pragma unroll
+    for (int kb = 0; kb < NTK / 2; ++kb) {
+      *reinterpret_cast<f16x4*>(Hs + jw * LDK + 32 * kb + 4 * g) = f16x4{f[kb][0], f[kb][1], f[kb][2], f[kb][3]};
+      *reinterpret_cast<f16x4*>(Hs + jw * LDK + 32 * kb + 16 + 4 * g) = f16x4{f[kb][4], f[kb][5], f[kb][6], f[kb][7]};
+    }
+  };
   const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
   const uint32_t voffv = 4 * g * rowv + (hv * DK + jw) * 2;
   const int64_t seq0 = (b * a.T + t0) * a.Hv * DK;
@@ -890,17 +999,10 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   _Float16* X2b = X1b + C * LDX; // U
 
   // ---- phase A
-  f16x8 h0f[NTK / 2], dhf[NTK / 2];
+  put_state(h0f);
   float hh = 0.f;  // this lane's part of <dH, H0>
 #pragma unroll
   for (int kb = 0; kb < NTK / 2; ++kb) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      h0f[kb][e] = h_of(h0u[2 * kb][e]);
-      h0f[kb][4 + e] = h_of(h0u[2 * kb + 1][e]);
-      dhf[kb][e] = h_of(dhu[2 * kb][e]);
-      dhf[kb][4 + e] = h_of(dhu[2 * kb + 1][e]);
-    }
 #pragma unroll
     for (int p2 = 0; p2 < 4; ++p2)
       hh = __builtin_amdgcn_fdot2(f16x2{h0f[kb][2 * p2], h0f[kb][2 * p2 + 1]},
@@ -970,7 +1072,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   for (int t = 0; t < DPW; ++t) dP[t] = dT[t] = zero4();
 #pragma unroll
   for (int ks = 0; ks < DK / 32; ++ks) {
-    const f16x8 bfr = __builtin_bit_cast(f16x8, h0r[ks]);
+    const f16x8 bfr = frag_t(Hs, LDK, 32 * ks, 16 * w);  // H0[i2][32ks + 8g ..]
     f16x8 a1[NT], a2[NT];
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
@@ -1001,11 +1103,12 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       X0[r * LDX + jw] = static_cast<_Float16>(du[tr][e]);
       X1b[r * LDX + jw] = static_cast<_Float16>(rhs[tr][e]);
     }
+  put_state(dhf);
   __syncthreads();
   // ---- phase 2: X3 = U dH^T, dT = dU RHS^T
 #pragma unroll
   for (int ks = 0; ks < DK / 32; ++ks) {
-    const f16x8 bfr = __builtin_bit_cast(f16x8, dhrw[ks]);
+    const f16x8 bfr = frag_t(Hs, LDK, 32 * ks, 16 * w);  // dH[i2][32ks + 8g ..]
     f16x8 a3[NT];
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) a3[rt] = ld8(X2b + (16 * rt + c16) * LDX + 32 * ks + 8 * g);
@@ -1338,15 +1441,15 @@ hipError_t prep16(const K16& a, hipStream_t st) {
 template <int C, typename TO, bool WO, bool SH>
 hipError_t chain16(const K16& a, hipStream_t st) {
   ProfScope ps(WO ? "chunk_fwd" : "chunk_states", st);
-  hipLaunchKernelGGL((chain16_kernel<C, TO, WO, SH>), dim3(static_cast<unsigned>(2 * a.Hv * a.B)), dim3(256), 0, st,
-                     a);
+  hipLaunchKernelGGL((chain16_kernel<C, TO, WO, SH>), dim3(static_cast<unsigned>(2 * a.Hv * a.B)), dim3(64 * (NCW + 1)),
+                     0, st, a);
   return hipGetLastError();
 }
 
 template <int C, typename TO>
 hipError_t dh16(const K16& a, hipStream_t st) {
   ProfScope ps("chunk_dh", st);
-  hipLaunchKernelGGL((dh16_kernel<C, TO>), dim3(static_cast<unsigned>(2 * a.Hv * a.B)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((dh16_kernel<C, TO>), dim3(static_cast<unsigned>(2 * a.Hv * a.B)), dim3(64 * (NCW + 1)), 0, st, a);
   return hipGetLastError();
 }
 
