@@ -154,6 +154,18 @@ __device__ __forceinline__ f16x8 frag_t(const _Float16* M, int ld, int k0, int n
   return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Four bf16 values carried as the 16-bit halves of a transpose-read result,
+// widened to fp32.  The halves are taken from the two 32-bit words: a
+// bit_cast of a single vector element would read the vector's first element.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void bf16x4_to_f32(float (&x)[4], f16x4 h) {
+  const u32x2 u = __builtin_bit_cast(u32x2, h);
+  x[0] = __uint_as_float(u[0] << 16);
+  x[1] = __uint_as_float(u[0] & 0xffff0000u);
+  x[2] = __uint_as_float(u[1] << 16);
+  x[3] = __uint_as_float(u[1] & 0xffff0000u);
+}
+
 // Chained B fragments of a strip x[t][e] (rows 16t + 4g + e of this lane).
 template <int NT>
 __device__ __forceinline__ void chain_frags(f16x8 (&bf)[NT / 2], const f32x4 (&x)[NT]) {
@@ -518,21 +530,21 @@ __device__ __forceinline__ uint32_t frag_off(int wg, int kb) {
   return static_cast<uint32_t>(((wg * (NTK / 2) + kb) * 64 + lane_id()) * 16);
 }
 
-// Copy by one wave of rows 0 .. ROWS-1 (RB bytes each, rows rowb bytes apart
-// from byte col0 of buffer r) into LDS at dst as a packed [ROWS][RB] tile;
-// rows >= L repeat row L - 1 (finite values that the chunk algebra multiplies
-// by zero).
-template <int ROWS, int RB>
-__device__ __forceinline__ void dma_rows(rsrc_t r, uint32_t rowb, uint32_t col0, int L, char* dst) {
+// Copy by NTH threads (as dma) of rows 0 .. ROWS-1 (RB bytes each, rows rowb
+// bytes apart from byte col0 of buffer r) into LDS at dst as a packed
+// [ROWS][RB] tile; rows >= L repeat row L - 1 (finite values that the chunk
+// algebra multiplies by zero).
+template <int ROWS, int RB, int NTH>
+__device__ __forceinline__ void dma_rows(rsrc_t r, uint32_t rowb, uint32_t col0, int L, char* dst, int tid, int w) {
   constexpr int UPR = RB / 16, N16 = ROWS * UPR;
-  static_assert(N16 % 64 == 0, "whole wave rounds");
-  const int lane = lane_id();
+  static_assert(N16 % NTH == 0, "whole rounds");
 #pragma unroll
-  for (int u = 0; u < N16 / 64; ++u) {
-    const int e = 64 * u + lane;
+  for (int u = 0; u < N16 / NTH; ++u) {
+    const int e = NTH * u + tid;
     const int row = e / UPR, cu = e % UPR;
     const int rr = row < L ? row : L - 1;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void)(dst + 1024 * u), 16, rr * rowb + col0 + 16 * cu, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void)(dst + 16 * (NTH * u + 64 * w)), 16,
+                                             rr * rowb + col0 + 16 * cu, 0, 0, 0);
   }
 }
 
@@ -623,7 +635,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void chain16_kernel(K16 a) {
     auto stage = [&](int c, char* buf) {
       dma<CB, 64>(make_rsrc(cim0 + c * static_cast<int64_t>(IM::CHK), CB), 0, buf, lane, 0);
       dma<KB, 64>(make_rsrc(kim0 + c * static_cast<int64_t>(IM::KEY), KB), 0, buf + CB, lane, 0);
-      dma_rows<C, BV * 2>(seq_rsrc(a.v, 2, c, rowv), rowv, colv, rows_of(c), buf + CB + KB);
+      dma_rows<C, BV * 2, 64>(seq_rsrc(a.v, 2, c, rowv), rowv, colv, rows_of(c), buf + CB + KB, lane, 0);
     };
     auto pstep = [&](int c, char* nxt, const char* os_prev) __attribute__((always_inline)) {
       if (c + 1 < a.NC) stage(c + 1, nxt);
@@ -771,7 +783,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
     auto stage = [&](int c, char* buf) {
       dma<CB, 64>(make_rsrc(cim0 + c * static_cast<int64_t>(IM::CHK), CB), 0, buf, lane, 0);
       dma<KB, 64>(make_rsrc(kim0 + c * static_cast<int64_t>(IM::KEY), KB), 0, buf + CB, lane, 0);
-      dma_rows<C, BV * 2>(seq_rsrc(a.dout, 2, c, rowv), rowv, colv, rows_of(c), buf + CB + KB);
+      dma_rows<C, BV * 2, 64>(seq_rsrc(a.dout, 2, c, rowv), rowv, colv, rows_of(c), buf + CB + KB, lane, 0);
     };
     auto pstep = [&](int c, char* nxt, const char* os_prev) __attribute__((always_inline)) {
       if (c > 0) stage(c - 1, nxt);
@@ -926,17 +938,24 @@ template <int C, typename TO, int MODE>
 __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   using IM = Img<C>;
   constexpr int NW = 8;
-  constexpr int LDC = IM::LDC, NT = C / 16, LDX = DK + 8;
+  constexpr int LDC = IM::LDC, NT = C / 16;
+  constexpr int LDR = C + 8;                     // pitch of the transposed strip tiles X[j][r]
+  constexpr int XT = DK * LDR;                   // halves per strip tile
+  constexpr int XB = 3 * XT;
+  constexpr int LDQ = DK + 8;                    // pitch of the dq / dk output tiles
   constexpr int NQ = NT * NT;                    // C x C tiles
   constexpr int DPW = NQ >= NW ? NQ / NW : 1;    // C x C tiles per wave, all in one row tile
-  constexpr int XB = 3 * C * LDX;
   static_assert(5 * C * LDC <= XB, "C x C stage buffers alias the strip buffers");
+  static_assert(2 * C * DK <= XB, "raw v / dO tiles fit the strip buffers");
+  static_assert(2 * C * DK <= DK * LDK, "raw q / k tiles fit the state tile");
+  static_assert(2 * C * LDQ * 2 + 4 * NW * C * 4 <= XB * 2, "dq / dk tiles and norm partials fit the strip buffers");
   __shared__ __align__(16) char img[IM::CHK + IM::KEY];
   __shared__ __align__(16) _Float16 xb[XB];
+  __shared__ __align__(16) _Float16 Hs[DK * LDK];  // H0, then dH, as Hs[j][i]; then raw q / k rows
   __shared__ float sG[NW][C], sGc[NW][C], sB[NW][C], red[2][NW];
-  __shared__ float sN[4][NW][C];  // L2-norm VJP row partials: |q|^2, q.dq_hat, |k|^2, k.dk_hat
   __shared__ __align__(16) float sDot[4][C];
-  __shared__ __align__(16) _Float16 Hs[DK * LDK];  // H0, then dH, as Hs[j][i]
+  // L2-norm VJP row partials |q|^2, q.dq_hat, |k|^2, k.dk_hat, after the dq / dk output tiles
+  float (*sN)[NW][C] = reinterpret_cast<float (*)[NW][C]>(xb + 2 * C * LDQ);
 
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int c = blockIdx.x, kh = blockIdx.y;
@@ -972,12 +991,13 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       *reinterpret_cast<f16x4*>(Hs + jw * LDK + 32 * kb + 16 + 4 * g) = f16x4{f[kb][4], f[kb][5], f[kb][6], f[kb][7]};
     }
   };
+  // raw v / dO rows of the chunk, packed [C][DK] bf16, in the strip buffers
   const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
-  const uint32_t voffv = 4 * g * rowv + (hv * DK + jw) * 2;
   const int64_t seq0 = (b * a.T + t0) * a.Hv * DK;
-  uint32_t vraw[NT][4], draw[NT][4];
-  load_strip_buf<NT>(vraw, make_rsrc(a.v + seq0, static_cast<uint32_t>(L) * rowv), voffv, rowv);
-  load_strip_buf<NT>(draw, make_rsrc(a.dout + seq0, static_cast<uint32_t>(L) * rowv), voffv, rowv);
+  dma_rows<C, DK * 2, 512>(make_rsrc(a.v + seq0, static_cast<uint32_t>(L) * rowv), rowv, hv * DK * 2, L,
+                           reinterpret_cast<char*>(xb), tid, w);
+  dma_rows<C, DK * 2, 512>(make_rsrc(a.dout + seq0, static_cast<uint32_t>(L) * rowv), rowv, hv * DK * 2, L,
+                           reinterpret_cast<char*>(xb + C * DK), tid, w);
   for (int e = tid; e < NW * C; e += 512) {
     sG[e / C][e % C] = 0.f;
     sGc[e / C][e % C] = 0.f;
@@ -994,9 +1014,18 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   const _Float16* Ks = reinterpret_cast<const _Float16*>(img + IM::CHK);
   const _Float16* Qs = Ks + C * LDK;
   const float gamC = gam[L - 1];
-  _Float16* X0 = xb;             // dRHS, then dU
-  _Float16* X1b = xb + C * LDX;  // dO, then RHS
-  _Float16* X2b = X1b + C * LDX; // U
+  // strip tiles, transposed (X[j][r]): dRHS then dU | dO then RHS | U
+  _Float16* X0 = xb;
+  _Float16* X1b = xb + XT;
+  _Float16* X2b = xb + 2 * XT;
+  // this lane's strip rows 16tr + 4g .. +3 of column jw into X[jw][.]
+  auto put_strip_t = [&](_Float16* X, const f32x4 (&x)[NT]) {
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr)
+      *reinterpret_cast<f16x4*>(X + jw * LDR + 16 * tr + 4 * g) =
+          f16x4{static_cast<_Float16>(x[tr][0]), static_cast<_Float16>(x[tr][1]), static_cast<_Float16>(x[tr][2]),
+                static_cast<_Float16>(x[tr][3])};
+  };
 
   // ---- phase A
   put_state(h0f);
@@ -1009,10 +1038,17 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
                                   f16x2{dhf[kb][2 * p2], dhf[kb][2 * p2 + 1]}, hh, false);
   }
   f32x4 y[NT], du[NT], u[NT], dr[NT], rhs[NT], dov[NT];
+  f16x4 vraw[NT], draw[NT];
+#pragma unroll
+  for (int tr = 0; tr < NT; ++tr) {
+    vraw[tr] = tr4(xb, DK, 16 * tr + 4 * g, 16 * w);
+    draw[tr] = tr4(xb + C * DK, DK, 16 * tr + 4 * g, 16 * w);
+  }
 #pragma unroll
   for (int t = 0; t < NT; ++t) y[t] = du[t] = u[t] = dr[t] = zero4();
   mma_chain_rows<NT, NTK>(y, Ks, LDK, h0f);
   mma_chain_rows<NT, NTK>(du, Ks, LDK, dhf);
+  lds_barrier();  // every wave holds its v / dO strips: the strip tiles may be overwritten
   f32x4 psb[NT], psy[NT];
 #pragma unroll
   for (int tr = 0; tr < NT; ++tr) {
@@ -1020,8 +1056,8 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     const f32x4 lv = *reinterpret_cast<const f32x4*>(lam + 16 * tr + 4 * g);
     const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
     float vv[4], dd[4];
-    unpack_strip(vv, vraw[tr]);
-    unpack_strip(dd, draw[tr]);
+    bf16x4_to_f32(vv, vraw[tr]);
+    bf16x4_to_f32(dd, draw[tr]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float vmy = vv[e] - gv[e] * y[tr][e];
@@ -1042,13 +1078,12 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   for (int tr = 0; tr < NT; ++tr)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 16 * tr + 4 * g + e;
       psb[tr][e] *= dr[tr][e];
       psy[tr][e] = dr[tr][e] * y[tr][e];
-      X0[r * LDX + jw] = static_cast<_Float16>(dr[tr][e]);
-      X1b[r * LDX + jw] = static_cast<_Float16>(dov[tr][e]);
-      X2b[r * LDX + jw] = static_cast<_Float16>(u[tr][e]);
     }
+  put_strip_t(X0, dr);
+  put_strip_t(X1b, dov);
+  put_strip_t(X2b, u);
   // dbeta_r += sum_j dRHS (V - gam Y);  dG_r -= beta gam sum_j dRHS Y
 #pragma unroll
   for (int tr = 0; tr < NT; ++tr)
@@ -1076,8 +1111,8 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     f16x8 a1[NT], a2[NT];
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
-      a1[rt] = ld8(X0 + (16 * rt + c16) * LDX + 32 * ks + 8 * g);
-      a2[rt] = ld8(X1b + (16 * rt + c16) * LDX + 32 * ks + 8 * g);
+      a1[rt] = frag_t(X0, LDR, 32 * ks, 16 * rt);
+      a2[rt] = frag_t(X1b, LDR, 32 * ks, 16 * rt);
     }
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
@@ -1088,21 +1123,14 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   if (qact) {
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
-      const f16x8 af = ld8(X1b + (16 * qr + c16) * LDX + 32 * ks + 8 * g);
+      const f16x8 af = frag_t(X1b, LDR, 32 * ks, 16 * qr);
 #pragma unroll
-      for (int t = 0; t < DPW; ++t)
-        dP[t] = F16Op::mma(af, ld8(X2b + (16 * (qc0 + t) + c16) * LDX + 32 * ks + 8 * g), dP[t]);
+      for (int t = 0; t < DPW; ++t) dP[t] = F16Op::mma(af, frag_t(X2b, LDR, 32 * ks, 16 * (qc0 + t)), dP[t]);
     }
   }
   __syncthreads();
-#pragma unroll
-  for (int tr = 0; tr < NT; ++tr)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * tr + 4 * g + e;
-      X0[r * LDX + jw] = static_cast<_Float16>(du[tr][e]);
-      X1b[r * LDX + jw] = static_cast<_Float16>(rhs[tr][e]);
-    }
+  put_strip_t(X0, du);
+  put_strip_t(X1b, rhs);
   put_state(dhf);
   __syncthreads();
   // ---- phase 2: X3 = U dH^T, dT = dU RHS^T
@@ -1111,20 +1139,53 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     const f16x8 bfr = frag_t(Hs, LDK, 32 * ks, 16 * w);  // dH[i2][32ks + 8g ..]
     f16x8 a3[NT];
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt) a3[rt] = ld8(X2b + (16 * rt + c16) * LDX + 32 * ks + 8 * g);
+    for (int rt = 0; rt < NT; ++rt) a3[rt] = frag_t(X2b, LDR, 32 * ks, 16 * rt);
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) x3[rt] = F16Op::mma(a3[rt], bfr, x3[rt]);
   }
   if (qact) {
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
-      const f16x8 af = ld8(X0 + (16 * qr + c16) * LDX + 32 * ks + 8 * g);
+      const f16x8 af = frag_t(X0, LDR, 32 * ks, 16 * qr);
 #pragma unroll
-      for (int t = 0; t < DPW; ++t)
-        dT[t] = F16Op::mma(af, ld8(X1b + (16 * (qc0 + t) + c16) * LDX + 32 * ks + 8 * g), dT[t]);
+      for (int t = 0; t < DPW; ++t) dT[t] = F16Op::mma(af, frag_t(X1b, LDR, 32 * ks, 16 * (qc0 + t)), dT[t]);
     }
   }
   __syncthreads();
+
+  // Loads used after the products, issued now: the group's running sums of
+  // dq_hat / dk_hat (earlier v-heads; stored per (b, chunk, k-head) in this
+  // kernel's own lane order, 16 bytes per lane and row tile) and, for the
+  // norm VJP, the raw q / k rows of the chunk (rows >= L repeat row L - 1).
+  const int64_t ptile = ((b * a.NC + c) * a.Hk + kh) * static_cast<int64_t>(C * DK);
+  const rsrc_t pqr = make_rsrc(a.pdq + ptile, C * DK * 4);
+  const rsrc_t pkr = make_rsrc(a.pdk + ptile, C * DK * 4);
+  auto poff = [&](int rt) { return static_cast<uint32_t>(((w * NT + rt) * 64 + lane) * 16); };
+  u32x4 pq[NT], pk[NT];
+  if constexpr (MODE == kMid || MODE == kLast) {
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      pq[rt] = __builtin_amdgcn_raw_buffer_load_b128(pqr, poff(rt), 0, 0);
+      pk[rt] = __builtin_amdgcn_raw_buffer_load_b128(pkr, poff(rt), 0, 0);
+    }
+  }
+  constexpr int QKU = C * DK * 2 / 16 / 512;  // 16-byte units of one raw tile per thread
+  u32x4 qraw[QKU], kraw[QKU];
+  const uint32_t rowk = static_cast<uint32_t>(a.Hk) * DK * 2;
+  if constexpr (MODE == kLast || MODE == kOnly) {
+    if (a.l2) {
+      const int64_t seqk = (b * a.T + t0) * a.Hk * DK;
+      const rsrc_t qr_ = make_rsrc(a.q + seqk, static_cast<uint32_t>(L) * rowk);
+      const rsrc_t kr_ = make_rsrc(a.k + seqk, static_cast<uint32_t>(L) * rowk);
+#pragma unroll
+      for (int u2 = 0; u2 < QKU; ++u2) {
+        const int e = 512 * u2 + tid, row = e / 16, cu = e % 16;
+        const uint32_t off = (row < L ? row : L - 1) * rowk + kh * DK * 2 + 16 * cu;
+        qraw[u2] = __builtin_amdgcn_raw_buffer_load_b128(qr_, off, 0, 0);
+        kraw[u2] = __builtin_amdgcn_raw_buffer_load_b128(kr_, off, 0, 0);
+      }
+    }
+  }
 
   // ---- C x C stage on the tiles (qr, qc0 + t)
   _Float16* dTT = xb;              // dTT[s'][s] = dT[s][s']
@@ -1236,31 +1297,24 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       dkv[rt][e] = dk[rt][e] + lam[r] * x3[rt][e] - bet[r] * gam[r] * x1[rt][e];
     }
   // ---- group sums of dq_hat / dk_hat (rows 16rt + 4g + e, column i2)
-  {
-    const uint32_t rowp = static_cast<uint32_t>(a.Hk) * DK * 4;
-    const int64_t seqp = (b * a.T + t0) * a.Hk * DK;
-    const rsrc_t pqr = make_rsrc(a.pdq + seqp, static_cast<uint32_t>(L) * rowp);
-    const rsrc_t pkr = make_rsrc(a.pdk + seqp, static_cast<uint32_t>(L) * rowp);
-    const uint32_t voffp = 4 * g * rowp + (kh * DK + i2) * 4;
-    if constexpr (MODE == kMid || MODE == kLast) {
+  if constexpr (MODE == kMid || MODE == kLast) {
 #pragma unroll
-      for (int rt = 0; rt < NT; ++rt)
+    for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t off = voffp + (16 * rt + e) * rowp;
-          dqv[rt][e] += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pqr, off, 0, 0));
-          dkv[rt][e] += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pkr, off, 0, 0));
-        }
-    }
-    if constexpr (MODE == kFirst || MODE == kMid) {
+      for (int e = 0; e < 4; ++e) {
+        dqv[rt][e] += __uint_as_float(pq[rt][e]);
+        dkv[rt][e] += __uint_as_float(pk[rt][e]);
+      }
+  }
+  if constexpr (MODE == kFirst || MODE == kMid) {
 #pragma unroll
-      for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t off = voffp + (16 * rt + e) * rowp;
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dqv[rt][e]), pqr, off, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dkv[rt][e]), pkr, off, 0, 0);
-        }
+    for (int rt = 0; rt < NT; ++rt) {
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(dqv[rt][0]), __float_as_uint(dqv[rt][1]),
+                                                   __float_as_uint(dqv[rt][2]), __float_as_uint(dqv[rt][3])},
+                                             pqr, poff(rt), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(dkv[rt][0]), __float_as_uint(dkv[rt][1]),
+                                                   __float_as_uint(dkv[rt][2]), __float_as_uint(dkv[rt][3])},
+                                             pkr, poff(rt), 0, 0);
     }
   }
   hh = xsum<1, 64>(hh);
@@ -1268,6 +1322,15 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   if (lane == 0) {
     red[0][w] = hh;
     red[1][w] = gcx;
+  }
+  if constexpr (MODE == kLast || MODE == kOnly) {  // raw q / k rows into the state tile, packed [C][DK]
+    if (a.l2) {
+#pragma unroll
+      for (int u2 = 0; u2 < QKU; ++u2) {
+        *reinterpret_cast<u32x4*>(Hs + (512 * u2 + tid) * 8) = qraw[u2];
+        *reinterpret_cast<u32x4*>(Hs + C * DK + (512 * u2 + tid) * 8) = kraw[u2];
+      }
+    }
   }
   __syncthreads();
   if (w == 0) {
@@ -1307,23 +1370,20 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     // r = (|x|^2 + eps)^(-1/2), from the raw q / k rows (the Megatron-LM page's
     // fold of the norm into the kernel, differentiated)
     if (a.l2) {
-      const uint32_t rowk = static_cast<uint32_t>(a.Hk) * DK * 2;
-      const int64_t seqk = (b * a.T + t0) * a.Hk * DK;
-      const uint32_t voffk = 4 * g * rowk + (kh * DK + i2) * 2;
-      uint32_t qraw[NT][4], kraw[NT][4];
-      load_strip_buf<NT>(qraw, make_rsrc(a.q + seqk, static_cast<uint32_t>(L) * rowk), voffk, rowk);
-      load_strip_buf<NT>(kraw, make_rsrc(a.k + seqk, static_cast<uint32_t>(L) * rowk), voffk, rowk);
+      float xq[NT][4], xk[NT][4];  // raw q / k at this lane's rows 16rt + 4g + e, column i2
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) {
-        float xq[4], xk[4];
-        unpack_strip(xq, qraw[rt]);
-        unpack_strip(xk, kraw[rt]);
+        bf16x4_to_f32(xq[rt], tr4(Hs, DK, 16 * rt + 4 * g, 16 * w));
+        bf16x4_to_f32(xk[rt], tr4(Hs + C * DK, DK, 16 * rt + 4 * g, 16 * w));
+      }
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float s0 = row16_sum(xq[e] * xq[e]);
-          const float s1 = row16_sum(xq[e] * dqv[rt][e]);
-          const float s2 = row16_sum(xk[e] * xk[e]);
-          const float s3 = row16_sum(xk[e] * dkv[rt][e]);
+          const float s0 = row16_sum(xq[rt][e] * xq[rt][e]);
+          const float s1 = row16_sum(xq[rt][e] * dqv[rt][e]);
+          const float s2 = row16_sum(xk[rt][e] * xk[rt][e]);
+          const float s3 = row16_sum(xk[rt][e] * dkv[rt][e]);
           if (c16 == 0) {
             const int r = 16 * rt + 4 * g + e;
             sN[0][w][r] = s0;
@@ -1344,9 +1404,6 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       __syncthreads();
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) {
-        float xq[4], xk[4];
-        unpack_strip(xq, qraw[rt]);
-        unpack_strip(xk, kraw[rt]);
         const f32x4 qq = *reinterpret_cast<const f32x4*>(&sDot[0][16 * rt + 4 * g]);
         const f32x4 qd = *reinterpret_cast<const f32x4*>(&sDot[1][16 * rt + 4 * g]);
         const f32x4 kk2 = *reinterpret_cast<const f32x4*>(&sDot[2][16 * rt + 4 * g]);
@@ -1354,14 +1411,15 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float rq = rsqrtf(qq[e] + kL2Eps), rk = rsqrtf(kk2[e] + kL2Eps);
-          dqv[rt][e] = rq * (dqv[rt][e] - rq * rq * xq[e] * qd[e]);
-          dkv[rt][e] = rk * (dkv[rt][e] - rk * rk * xk[e] * kd[e]);
+          dqv[rt][e] = rq * (dqv[rt][e] - rq * rq * xq[rt][e] * qd[e]);
+          dkv[rt][e] = rk * (dkv[rt][e] - rk * rk * xk[rt][e] * kd[e]);
         }
       }
     }
     const uint32_t rowo = static_cast<uint32_t>(a.Hk) * DK * sizeof(TO);
     const int64_t seqo = (b * a.T + t0) * a.Hk * DK * static_cast<int64_t>(sizeof(TO));
-    const uint32_t voffo = 4 * g * rowo + (kh * DK + i2) * static_cast<uint32_t>(sizeof(TO));
+    const rsrc_t oqr = make_rsrc(static_cast<char*>(a.dq) + seqo, static_cast<uint32_t>(L) * rowo);
+    const rsrc_t okr = make_rsrc(static_cast<char*>(a.dk) + seqo, static_cast<uint32_t>(L) * rowo);
     f32x4 oq[NT], ok[NT];
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt)
@@ -1370,8 +1428,30 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
         oq[rt][e] = dqv[rt][e];
         ok[rt][e] = dkv[rt][e];
       }
-    store_strip_buf<TO, NT>(make_rsrc(static_cast<char*>(a.dq) + seqo, static_cast<uint32_t>(L) * rowo), voffo, rowo, oq);
-    store_strip_buf<TO, NT>(make_rsrc(static_cast<char*>(a.dk) + seqo, static_cast<uint32_t>(L) * rowo), voffo, rowo, ok);
+    if constexpr (std::is_same_v<TO, float>) {
+      const uint32_t voffo = 4 * g * rowo + (kh * DK + i2) * 4;
+      store_strip_buf<TO, NT>(oqr, voffo, rowo, oq);
+      store_strip_buf<TO, NT>(okr, voffo, rowo, ok);
+    } else {  // through [C][LDQ] tiles in the strip buffers, stored as 16-byte rows
+      uint16_t* Oq = reinterpret_cast<uint16_t*>(xb);
+      uint16_t* Ok = Oq + C * LDQ;
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rt + 4 * g + e;
+          Oq[r * LDQ + i2] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(oq[rt][e]));
+          Ok[r * LDQ + i2] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(ok[rt][e]));
+        }
+      lds_barrier();
+#pragma unroll
+      for (int u2 = 0; u2 < C * DK * 2 / 16 / 512; ++u2) {
+        const int e = 512 * u2 + tid, row = e / 16, cu = e % 16;
+        const uint32_t off = row * rowo + kh * DK * 2 + 16 * cu;
+        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(Oq + row * LDQ + 8 * cu), oqr, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(Ok + row * LDQ + 8 * cu), okr, off, 0, 0);
+      }
+    }
   }
 }
 
@@ -1395,7 +1475,7 @@ Ws16 plan16(const Shape& s, bool bwd) {
   w.kimg = off; off = up(off + nk * IM::KEY);
   w.cimg = off; off = up(off + nv * IM::CHK);
   if (bwd) {
-    const size_t rows = static_cast<size_t>(s.B * s.T) * s.Hk;
+    const size_t rows = static_cast<size_t>(s.B) * nc * C * s.Hk;  // running-sum tiles per (b, chunk, k-head)
     w.hst = off;  off = up(off + nv * DK * DK * 2);
     w.dhst = off; off = up(off + nv * DK * DK * 2);
     if (s.Hv > s.Hk) {
