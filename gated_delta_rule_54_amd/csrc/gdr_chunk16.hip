@@ -370,11 +370,22 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
   using IM = Img<C>;
   constexpr int NT = C / 16, LDA = C + 4, LDC = IM::LDC;
   constexpr int TPR = 256 / C, EPT = DK / TPR, NV = EPT / 8;
+  static_assert(C * LDC <= C * LDK, "the fp16 T tile reuses the Qn buffer");
   __shared__ __align__(16) _Float16 Ks[C * LDK];
-  __shared__ __align__(16) _Float16 Qs[C * LDK];
+  __shared__ __align__(16) _Float16 Qs[C * LDK];  // Qn, then the fp16 T tile [C][LDC]
   __shared__ __align__(16) float A[C * LDA];
   __shared__ __align__(16) float Tf[C * LDA];
   __shared__ __align__(16) _Float16 Pst[C * LDC];
+  _Float16* Tst = Qs;
+  // zeroes the 16-byte units of a [C][LDC] fp16 tile that lie above its
+  // 16 x 16 diagonal blocks (no other thread writes them)
+  auto zero_upper = [&](_Float16* M) {
+    constexpr int UR = LDC / 8;
+    for (int e = threadIdx.x; e < C * UR; e += 256) {
+      const int r = e / UR, u = e % UR;
+      if (u < C / 8 && u / 2 > r / 16) reinterpret_cast<uint4*>(M)[e] = uint4{0u, 0u, 0u, 0u};
+    }
+  };
   __shared__ __align__(16) float gates[4 * C];  // gam | lam | beta | G2
   float* gam = gates;
   float* lam = gates + C;
@@ -424,14 +435,27 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
       }
     }
   }
+  zero_upper(Pst);  // P above its diagonal blocks
   __syncthreads();
-  // A (fp32) and P (fp16) tiles; tile t = w + 4q of the NT x NT grid
-  for (int t = w; t < NT * NT; t += 4) {
-    const int tr = t / NT, tc = t % NT;
+  // A (fp32) and P (fp16) on the NT(NT+1)/2 tiles on or below the diagonal,
+  // dealt to the waves; each tile's fragments are read before its products
+  constexpr int NL = NT * (NT + 1) / 2, KS = DK / 32;
+  for (int t = w; t < NL; t += 4) {
+    int tr = 0;
+    while ((tr + 1) * (tr + 2) / 2 <= t) ++tr;
+    const int tc = t - tr * (tr + 1) / 2;
+    f16x8 ka[KS], qa[KS], kb[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      ka[ks] = ld8(Ks + (16 * tr + c16) * LDK + 32 * ks + 8 * g);
+      qa[ks] = ld8(Qs + (16 * tr + c16) * LDK + 32 * ks + 8 * g);
+      kb[ks] = ld8(Ks + (16 * tc + c16) * LDK + 32 * ks + 8 * g);
+    }
     f32x4 kk = zero4(), qk = zero4();
-    if (tc <= tr) {
-      kk = mma_tile<F16Op, false, false>(zero4(), Ks, LDK, 16 * tr, Ks, LDK, 16 * tc, DK);
-      qk = mma_tile<F16Op, false, false>(zero4(), Qs, LDK, 16 * tr, Ks, LDK, 16 * tc, DK);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kk = F16Op::mma(ka[ks], kb[ks], kk);
+      qk = F16Op::mma(qa[ks], kb[ks], qk);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -441,7 +465,15 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
       Pst[r * LDC + s2] = static_cast<_Float16>(ex * qk[e]);
     }
   }
+  // ---- key image (one v-head of each k-head group writes it), while Kn / Qn are intact
+  constexpr int UK = DK / 8 + 1;  // 16-byte units per [*][LDK] row
+  if (hv % grp == 0) {
+    char* kim = a.kimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(IM::KEY);
+    write_tile<C, UK>(kim, [&](int r, int u) { return ld8(Ks + r * LDK + 8 * u); });
+    write_tile<C, UK>(kim + IM::KN, [&](int r, int u) { return ld8(Qs + r * LDK + 8 * u); });
+  }
   __syncthreads();
+  zero_upper(Tst);  // T above its diagonal blocks
   if (w < NT && lane < 16) {  // diagonal blocks
     const int o = 16 * w;
     float x[16];
@@ -453,7 +485,10 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
       x[r] = acc[0] + acc[1];
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) Tf[(o + r) * LDA + o + lane] = x[r];
+    for (int r = 0; r < 16; ++r) {
+      Tf[(o + r) * LDA + o + lane] = x[r];
+      Tst[(o + r) * LDC + o + lane] = static_cast<_Float16>(x[r]);
+    }
   }
   __syncthreads();
   for (int d = 1; d < NT; ++d) {  // blocks below the diagonal, one distance at a time
@@ -474,7 +509,10 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) tij = F32Op::mma(Tf[(16 * i + c16) * LDA + 16 * i + 4 * g + e], m[e], tij);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Tf[(16 * i + 4 * g + e) * LDA + 16 * j + c16] = -tij[e];
+      for (int e = 0; e < 4; ++e) {
+        Tf[(16 * i + 4 * g + e) * LDA + 16 * j + c16] = -tij[e];
+        Tst[(16 * i + 4 * g + e) * LDC + 16 * j + c16] = static_cast<_Float16>(-tij[e]);
+      }
     }
     __syncthreads();
   }
@@ -484,19 +522,8 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
   for (int e = tid; e < C; e += 256)
     reinterpret_cast<float4*>(cim)[e] = reinterpret_cast<const float4*>(gates)[e];
   constexpr int UC = C / 8 + 1;  // 16-byte units per [*][LDC] row
-  write_tile<C, UC>(cim + IM::GT, [&](int r, int u) {  // T, zero above the diagonal blocks
-    f16x8 v;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = static_cast<_Float16>((8 * u + q) / 16 <= r / 16 ? Tf[r * LDA + 8 * u + q] : 0.f);
-    return v;
-  });
+  write_tile<C, UC>(cim + IM::GT, [&](int r, int u) { return ld8(Tst + r * LDC + 8 * u); });
   write_tile<C, UC>(cim + IM::GT + IM::TM, [&](int r, int u) { return ld8(Pst + r * LDC + 8 * u); });
-  // ---- key image (one v-head of each k-head group writes it)
-  if (hv % grp != 0) return;
-  char* kim = a.kimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(IM::KEY);
-  constexpr int UK = DK / 8 + 1;  // 16-byte units per [*][LDK] row
-  write_tile<C, UK>(kim, [&](int r, int u) { return ld8(Ks + r * LDK + 8 * u); });
-  write_tile<C, UK>(kim + IM::KN, [&](int r, int u) { return ld8(Qs + r * LDK + 8 * u); });
 }
 
 // ---------------------------------------------------------------------------
