@@ -191,6 +191,24 @@ __device__ __forceinline__ void mma_chain_rows(f32x4 (&acc)[NO], const _Float16*
   }
 }
 
+// mma_chain_rows for two chained operands sharing A: acc1 += A X1, acc2 += A X2.
+template <int NO, int NT>
+__device__ __forceinline__ void mma_chain_rows2(f32x4 (&acc1)[NO], f32x4 (&acc2)[NO], const _Float16* A, int ld,
+                                                const f16x8 (&bf1)[NT / 2], const f16x8 (&bf2)[NT / 2]) {
+  const int m = lane_id() & 15;
+#pragma unroll
+  for (int kb = 0; kb < NT / 2; ++kb) {
+    f16x8 af[NO];
+#pragma unroll
+    for (int t = 0; t < NO; ++t) af[t] = perm_frag(A, ld, 16 * t + m, kb);
+#pragma unroll
+    for (int t = 0; t < NO; ++t) {
+      acc1[t] = F16Op::mma(af[t], bf1[kb], acc1[t]);
+      acc2[t] = F16Op::mma(af[t], bf2[kb], acc2[t]);
+    }
+  }
+}
+
 // mma_chain_rows with A = M^T, M row-major [16 NT][ld].
 template <int NO, int NT>
 __device__ __forceinline__ void mma_chain_rows_t(f32x4 (&acc)[NO], const _Float16* M, int ld,
@@ -979,7 +997,9 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   __shared__ __align__(16) char img[IM::CHK + IM::KEY];
   __shared__ __align__(16) _Float16 xb[XB];
   __shared__ __align__(16) _Float16 Hs[DK * LDK];  // H0, then dH, as Hs[j][i]; then raw q / k rows
-  __shared__ float sG[NW][C], sGc[NW][C], sB[NW][C], red[2][NW];
+  __shared__ __align__(16) float sG[NW][C];
+  __shared__ __align__(16) float sB[NW][C];
+  __shared__ float sGc[NW][C], red[2][NW];
   __shared__ __align__(16) float sDot[4][C];
   // L2-norm VJP row partials |q|^2, q.dq_hat, |k|^2, k.dk_hat, after the dq / dk output tiles
   float (*sN)[NW][C] = reinterpret_cast<float (*)[NW][C]>(xb + 2 * C * LDQ);
@@ -1025,11 +1045,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
                            reinterpret_cast<char*>(xb), tid, w);
   dma_rows<C, DK * 2, 512>(make_rsrc(a.dout + seq0, static_cast<uint32_t>(L) * rowv), rowv, hv * DK * 2, L,
                            reinterpret_cast<char*>(xb + C * DK), tid, w);
-  for (int e = tid; e < NW * C; e += 512) {
-    sG[e / C][e % C] = 0.f;
-    sGc[e / C][e % C] = 0.f;
-    sB[e / C][e % C] = 0.f;
-  }
+  for (int e = tid; e < NW * C; e += 512) sGc[e / C][e % C] = 0.f;
   wait_all();
   __syncthreads();
   const float* gam = reinterpret_cast<const float*>(img);
@@ -1073,8 +1089,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) y[t] = du[t] = u[t] = dr[t] = zero4();
-  mma_chain_rows<NT, NTK>(y, Ks, LDK, h0f);
-  mma_chain_rows<NT, NTK>(du, Ks, LDK, dhf);
+  mma_chain_rows2<NT, NTK>(y, du, Ks, LDK, h0f, dhf);
   lds_barrier();  // every wave holds its v / dO strips: the strip tiles may be overwritten
   f32x4 psb[NT], psy[NT];
 #pragma unroll
@@ -1111,19 +1126,24 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   put_strip_t(X0, dr);
   put_strip_t(X1b, dov);
   put_strip_t(X2b, u);
-  // dbeta_r += sum_j dRHS (V - gam Y);  dG_r -= beta gam sum_j dRHS Y
+  // This wave's shares of dbeta_r and dG_r (rows 16tr + 4g + e, summed over
+  // its 16 value columns) start the per-wave row sums sB / sG:
+  // dbeta_r = sum_j dRHS (V - gam Y);  dG_r = -beta gam sum_j dRHS Y + ...
 #pragma unroll
-  for (int tr = 0; tr < NT; ++tr)
+  for (int tr = 0; tr < NT; ++tr) {
+    const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * tr + 4 * g);
+    const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
+    f32x4 rb, rg;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 16 * tr + 4 * g + e;
-      const float sb = row16_sum(psb[tr][e]);
-      const float sy = row16_sum(psy[tr][e]);
-      if (c16 == 0) {
-        sB[w][r] += sb;
-        sG[w][r] -= bet[r] * gam[r] * sy;
-      }
+      rb[e] = row16_sum(psb[tr][e]);
+      rg[e] = -bv[e] * gv[e] * row16_sum(psy[tr][e]);
     }
+    if (c16 == 0) {
+      *reinterpret_cast<f32x4*>(&sB[w][16 * tr + 4 * g]) = rb;
+      *reinterpret_cast<f32x4*>(&sG[w][16 * tr + 4 * g]) = rg;
+    }
+  }
   __syncthreads();
 
   // ---- phase 1: X1 = dRHS H0^T, X2 = dO H0^T, dP = dO U^T
@@ -1288,14 +1308,17 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       col = xsum<16, 64>(col);
       if (lane < 16) sGc[w][s2] += col;
     }
+    f32x4 rg, rb;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float rg = row16_sum(rgc[e]);
-      const float rb = row16_sum(rbc[e]);
-      if (c16 == 0) {
-        sG[w][16 * qr + 4 * g + e] += rg;
-        sB[w][16 * qr + 4 * g + e] += rb;
-      }
+      rg[e] = row16_sum(rgc[e]);
+      rb[e] = row16_sum(rbc[e]);
+    }
+    if (c16 == 0) {
+      f32x4* pg = reinterpret_cast<f32x4*>(&sG[w][16 * qr + 4 * g]);
+      f32x4* pb = reinterpret_cast<f32x4*>(&sB[w][16 * qr + 4 * g]);
+      *pg = *pg + rg;
+      *pb = *pb + rb;
     }
   }
   __syncthreads();
@@ -1310,19 +1333,28 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   float dqv[NT][4], dkv[NT][4];
   float gcx = 0.f;
 #pragma unroll
-  for (int rt = 0; rt < NT; ++rt)
+  for (int rt = 0; rt < NT; ++rt) {
+    const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * rt + 4 * g);
+    const f32x4 lv = *reinterpret_cast<const f32x4*>(lam + 16 * rt + 4 * g);
+    const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * rt + 4 * g);
+    f32x4 rgx;
+    const f16x4 qn4 = tr4(Qs, LDK, 16 * rt + 4 * g, 16 * w);  // Qn[16rt + 4g + e][i2]
+    const f16x4 kn4 = tr4(Ks, LDK, 16 * rt + 4 * g, 16 * w);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 16 * rt + 4 * g + e;
-      const float qn = static_cast<float>(Qs[r * LDK + i2]);
-      const float kn = static_cast<float>(Ks[r * LDK + i2]);
-      const float t3 = lam[r] * kn * x3[rt][e];
+      const float qn = static_cast<float>(qn4[e]);
+      const float kn = static_cast<float>(kn4[e]);
+      const float t3 = lv[e] * kn * x3[rt][e];
       gcx += t3;
-      const float rg = row16_sum(gam[r] * qn * x2[rt][e] - t3);
-      if (c16 == 0) sG[w][r] += rg;
-      dqv[rt][e] = dq[rt][e] + gam[r] * x2[rt][e];
-      dkv[rt][e] = dk[rt][e] + lam[r] * x3[rt][e] - bet[r] * gam[r] * x1[rt][e];
+      rgx[e] = row16_sum(gv[e] * qn * x2[rt][e] - t3);
+      dqv[rt][e] = dq[rt][e] + gv[e] * x2[rt][e];
+      dkv[rt][e] = dk[rt][e] + lv[e] * x3[rt][e] - bv[e] * gv[e] * x1[rt][e];
     }
+    if (c16 == 0) {
+      f32x4* pg = reinterpret_cast<f32x4*>(&sG[w][16 * rt + 4 * g]);
+      *pg = *pg + rgx;
+    }
+  }
   // ---- group sums of dq_hat / dk_hat (rows 16rt + 4g + e, column i2)
   if constexpr (MODE == kMid || MODE == kLast) {
 #pragma unroll
