@@ -44,6 +44,12 @@ Readings where the pages are silent (each also listed in the design doc):
   * GQA: v-head hv reads k/q head hv // (Hv // Hk).
   * No output scale; beta is not clamped.
   * g = log(alpha) is passed in; alpha = exp(g).
+  * Fused gate activation (the fold-the-caller's-prep-into-the-kernel idea of
+    [MEG] applied to the gates; a reading, the pages name no activation):
+    with fused_gates the g and beta arguments are pre-activations a, b and
+    the recurrence uses g = -softplus(a) = -log(1 + e^a) (so alpha =
+    1 / (1 + e^a) <= 1) and beta = sigmoid(b); the VJP then returns the
+    gradients with respect to a and b.
 
 Array shapes (all functions): q, k [B,T,Hk,Dk]; v [B,T,Hv,Dv];
 g [B,T,Hv] (scalar gate) or [B,T,Hv,Dk] (channelwise); beta [B,T,Hv];
@@ -57,6 +63,25 @@ L2_EPS = 1e-6
 
 def _f64(x):
     return np.array(x, dtype=np.float64, copy=True)
+
+
+def _sigmoid(x):
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def gate_activation(a, b):
+    """Fused gates: g = -softplus(a) = -(max(a, 0) + log1p(e^-|a|)) and
+    beta = sigmoid(b), in float64."""
+    a, b = _f64(a), _f64(b)
+    return -(np.maximum(a, 0.0) + np.log1p(np.exp(-np.abs(a)))), _sigmoid(b)
+
+
+def gate_activation_vjp(a, b, dg, dbeta):
+    """Chain rule through gate_activation: d/da = -sigmoid(a) dg,
+    d/db = beta (1 - beta) dbeta."""
+    sb = _sigmoid(_f64(b))
+    return -_sigmoid(_f64(a)) * dg, sb * (1.0 - sb) * dbeta
 
 
 def l2norm(x, eps=L2_EPS):
@@ -95,12 +120,15 @@ def _decay(g, t, channelwise):
     return a[..., :, None] if channelwise else a[..., None, None]
 
 
-def forward(q, k, v, g, beta, h0=None, use_qk_l2norm=True, channelwise=False):
+def forward(q, k, v, g, beta, h0=None, use_qk_l2norm=True, channelwise=False, fused_gates=False):
     """Token-by-token recurrence, returns (o [B,T,Hv,Dv], ht [B,Hv,Dk,Dv]).
 
     One step per token exactly as written in the module docstring: decay the
-    state, predict, form the delta, rank-one update, read out.
+    state, predict, form the delta, rank-one update, read out.  With
+    fused_gates, g and beta are the pre-activations of gate_activation.
     """
+    if fused_gates:
+        g, beta = gate_activation(g, beta)
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     qh, kh = _prepare(q, k, use_qk_l2norm, Hv)
@@ -118,7 +146,7 @@ def forward(q, k, v, g, beta, h0=None, use_qk_l2norm=True, channelwise=False):
 
 
 def backward(q, k, v, g, beta, h0, do, dht=None, use_qk_l2norm=True,
-             channelwise=False):
+             channelwise=False, fused_gates=False):
     """Hand-derived VJP of ``forward``; returns dq, dk, dv, dg, dbeta, dh0.
 
     The forward is replayed once and every state H_0..H_T is kept (plain and
@@ -132,7 +160,12 @@ def backward(q, k, v, g, beta, h0, do, dht=None, use_qk_l2norm=True,
         dg   = <dD, D>  (per row of D when channelwise),  dH = diag(alpha) dD
     After t = 0, dh0 = dH.  q/k gradients are summed over the v-heads that
     share a k-head (in v-head order) and then passed through ``l2norm_vjp``.
+    With fused_gates, g and beta are pre-activations and dg, dbeta are
+    returned with respect to them (``gate_activation_vjp``).
     """
+    if fused_gates:
+        a_pre, b_pre = g, beta
+        g, beta = gate_activation(a_pre, b_pre)
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     grp = Hv // Hk
@@ -182,6 +215,8 @@ def backward(q, k, v, g, beta, h0, do, dht=None, use_qk_l2norm=True,
         dk = l2norm_vjp(k, dk_hat)
     else:
         dq, dk = dq_hat, dk_hat
+    if fused_gates:
+        dg, dbeta = gate_activation_vjp(a_pre, b_pre, dg, dbeta)
     return dq, dk, dv, dg, dbeta, dH
 
 

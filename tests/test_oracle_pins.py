@@ -361,3 +361,80 @@ def test_p5_split_sequence_forward_and_backward(cw):
     for i in range(5):
         assert relerr(np.concatenate([ga[i], gb[i]], 1), full[i]) < 1e-12
     assert relerr(ga[5], full[5]) < 1e-12
+
+
+# --------------------------------------------------------- fused gate activation
+
+def test_p16_gate_activation_closed_forms():
+    """Fused gates at a = b = 0: g = -softplus(0) = -log 2 (alpha = 1/2) and
+    beta = sigmoid(0) = 1/2; far out, softplus(a) -> a and sigmoid -> 0 / 1,
+    with no overflow."""
+    g, b = orc.gate_activation(np.array([0.0, 800.0, -800.0]), np.array([0.0, 800.0, -800.0]))
+    assert np.allclose(g, [-np.log(2.0), -800.0, 0.0], rtol=0, atol=1e-15)
+    assert np.allclose(b, [0.5, 1.0, 0.0], rtol=0, atol=1e-15)
+    assert np.all(np.isfinite(g)) and np.all(np.isfinite(b))
+
+
+def test_p16_saturated_gates_write_the_value():
+    """Pre-activations a -> -inf (alpha -> 1) and b -> +inf (beta -> 1) turn
+    the fused-gate recurrence into the plain full write of pin P1:
+    S_t k_t = v_t for unit keys."""
+    B, T, H, D = 2, 6, 3, 8
+    k = unit_rows(rand(B, T, H, D))
+    v = rand(B, T, H, D)
+    o, _ = orc.forward(k, k, v, np.full((B, T, H), -80.0), np.full((B, T, H), 80.0),
+                       h0=rand(B, H, D, D), use_qk_l2norm=False, fused_gates=True)
+    assert relerr(o, v) < 1e-12
+
+
+def _loss_fg(q, k, v, a, b, h0, do, dht, flag, cw):
+    o, ht = orc.forward(q, k, v, a, b, h0, use_qk_l2norm=flag, channelwise=cw, fused_gates=True)
+    return np.sum(o * do) + np.sum(ht * dht)
+
+
+@pytest.mark.parametrize("flag,cw", [(True, False), (True, True), (False, False)])
+def test_p16_fused_gate_finite_differences(flag, cw):
+    """Central differences of <do, o> + <dht, ht> in the pre-activations a, b
+    (and the other inputs) against the fused-gate VJP."""
+    rng = np.random.default_rng(41 + 2 * flag + cw)
+    B, T, Hk, Hv, D = 1, 5, 1, 2, 4
+    r = lambda *s: rng.standard_normal(s)
+    q, k, v = r(B, T, Hk, D), r(B, T, Hk, D), r(B, T, Hv, D)
+    a = r(B, T, Hv, D) if cw else r(B, T, Hv)
+    b = r(B, T, Hv)
+    h0, do, dht = r(B, Hv, D, D), r(B, T, Hv, D), r(B, Hv, D, D)
+    grads = orc.backward(q, k, v, a, b, h0, do, dht, use_qk_l2norm=flag, channelwise=cw, fused_gates=True)
+    args = [q, k, v, a, b, h0]
+    for ai in range(6):
+        x = args[ai]
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += 1e-6
+            xm[idx] -= 1e-6
+            ap, am = list(args), list(args)
+            ap[ai], am[ai] = xp, xm
+            fd[idx] = (_loss_fg(*ap, do, dht, flag, cw) - _loss_fg(*am, do, dht, flag, cw)) / 2e-6
+        assert relerr(grads[ai], fd) < 1e-6, ("grad", ai)
+
+
+def test_p16_fused_gates_autograd_of_the_textbook_form():
+    """torch autograd through -softplus / sigmoid followed by the textbook
+    recurrence gives the fused-gate oracle's outputs and gradients."""
+    B, T, Hk, Hv, D = 1, 7, 1, 2, 5
+    q, k, v = rand(B, T, Hk, D), rand(B, T, Hk, D), rand(B, T, Hv, D)
+    a, b = rand(B, T, Hv), rand(B, T, Hv)
+    h0, do, dht = rand(B, Hv, D, D), rand(B, T, Hv, D), rand(B, Hv, D, D)
+    tens = [torch.tensor(x, requires_grad=True) for x in (q, k, v, a, b, h0)]
+    g_t = -torch.nn.functional.softplus(tens[3])
+    beta_t = torch.sigmoid(tens[4])
+    o_t, ht_t = _torch_forward(tens[0], tens[1], tens[2], g_t, beta_t, tens[5], True, False, Hv)
+    ((o_t * torch.tensor(do)).sum() + (ht_t * torch.tensor(dht)).sum()).backward()
+    o, ht = orc.forward(q, k, v, a, b, h0, fused_gates=True)
+    assert relerr(o, o_t.detach().numpy()) < 1e-12
+    assert relerr(ht, ht_t.detach().numpy()) < 1e-12
+    grads = orc.backward(q, k, v, a, b, h0, do, dht, fused_gates=True)
+    for gi, tt in enumerate(tens):
+        assert relerr(grads[gi], tt.grad.numpy()) < 1e-11, gi
