@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libgdr.so")
 GDR_OK = 0
 GDR_F32, GDR_BF16 = 0, 1
 GDR_ALGO_AUTO, GDR_ALGO_SEQUENTIAL, GDR_ALGO_CHUNKED = 0, 1, 2
-GDR_USE_QK_L2NORM, GDR_CHANNELWISE = 1, 2
+GDR_USE_QK_L2NORM, GDR_CHANNELWISE, GDR_FUSED_GATES = 1, 2, 4
 ALGOS = {"auto": GDR_ALGO_AUTO, "sequential": GDR_ALGO_SEQUENTIAL,
          "chunked": GDR_ALGO_CHUNKED}
 
@@ -93,8 +93,9 @@ def _dt(t):
 
 
 def make_problem(B, T, Hk, Hv, Dk, Dv, io_dtype, out_dtype, use_qk_l2norm=True,
-                 channelwise=False, algo="auto", chunk_size=0):
-    flags = (GDR_USE_QK_L2NORM if use_qk_l2norm else 0) | (GDR_CHANNELWISE if channelwise else 0)
+                 channelwise=False, algo="auto", chunk_size=0, fused_gates=False):
+    flags = ((GDR_USE_QK_L2NORM if use_qk_l2norm else 0) | (GDR_CHANNELWISE if channelwise else 0)
+             | (GDR_FUSED_GATES if fused_gates else 0))
     return GdrProblem(B, T, Hk, Hv, Dk, Dv, _dt(io_dtype), _dt(out_dtype), flags,
                       ALGOS[algo], chunk_size)
 
@@ -159,9 +160,10 @@ def _workspace(nbytes, device):
 
 def gdr_forward(q, k, v, g, beta, h0=None, *, use_qk_l2norm=True, channelwise=False,
                 algo="auto", chunk_size=0, out_dtype=torch.float32, ht=True,
-                stream=None):
+                stream=None, fused_gates=False):
     """Returns (o, ht).  ``ht`` may be True (allocate), None (not wanted) or a
-    tensor to write the final state into (it may be ``h0`` itself)."""
+    tensor to write the final state into (it may be ``h0`` itself).  With
+    ``fused_gates`` g and beta are pre-activations (GDR_FUSED_GATES)."""
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -169,7 +171,7 @@ def gdr_forward(q, k, v, g, beta, h0=None, *, use_qk_l2norm=True, channelwise=Fa
     for t, n in ((g, "g"), (beta, "beta"), (h0, "h0")):
         _check(t, n, torch.float32)
     prob = make_problem(B, T, Hk, Hv, Dk, Dv, q.dtype, out_dtype, use_qk_l2norm,
-                        channelwise, algo, chunk_size)
+                        channelwise, algo, chunk_size, fused_gates)
     o = torch.empty((B, T, Hv, Dv), dtype=out_dtype, device=q.device)
     if ht is True:
         ht = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=q.device)
@@ -185,8 +187,10 @@ def gdr_forward(q, k, v, g, beta, h0=None, *, use_qk_l2norm=True, channelwise=Fa
 
 def gdr_backward(q, k, v, g, beta, h0, dout, dht=None, *, use_qk_l2norm=True,
                  channelwise=False, algo="auto", chunk_size=0,
-                 out_dtype=torch.float32, want_dh0=True, stream=None):
-    """Returns (dq, dk, dv, dg, dbeta, dh0); dh0 is None if not wanted."""
+                 out_dtype=torch.float32, want_dh0=True, stream=None, fused_gates=False):
+    """Returns (dq, dk, dv, dg, dbeta, dh0); dh0 is None if not wanted.  With
+    ``fused_gates`` g and beta are pre-activations and dg, dbeta are the
+    gradients with respect to them."""
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
@@ -194,7 +198,7 @@ def gdr_backward(q, k, v, g, beta, h0, dout, dht=None, *, use_qk_l2norm=True,
     for t, n in ((g, "g"), (beta, "beta"), (h0, "h0"), (dht, "dht")):
         _check(t, n, torch.float32)
     prob = make_problem(B, T, Hk, Hv, Dk, Dv, q.dtype, out_dtype, use_qk_l2norm,
-                        channelwise, algo, chunk_size)
+                        channelwise, algo, chunk_size, fused_gates)
     dev = q.device
     dq = torch.empty((B, T, Hk, Dk), dtype=out_dtype, device=dev)
     dk = torch.empty((B, T, Hk, Dk), dtype=out_dtype, device=dev)

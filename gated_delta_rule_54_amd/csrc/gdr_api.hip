@@ -33,7 +33,8 @@ gdr_status check_problem(const gdr_problem* p) {
   if ((p->io_dtype != GDR_F32 && p->io_dtype != GDR_BF16) ||
       (p->out_dtype != GDR_F32 && p->out_dtype != GDR_BF16))
     return GDR_ERR_UNSUPPORTED;
-  if (p->flags & ~static_cast<uint32_t>(GDR_USE_QK_L2NORM | GDR_CHANNELWISE)) return GDR_ERR_UNSUPPORTED;
+  if (p->flags & ~static_cast<uint32_t>(GDR_USE_QK_L2NORM | GDR_CHANNELWISE | GDR_FUSED_GATES))
+    return GDR_ERR_UNSUPPORTED;
   if (p->algo < GDR_ALGO_AUTO || p->algo > GDR_ALGO_CHUNKED) return GDR_ERR_UNSUPPORTED;
   if (p->chunk_size != 0 && p->chunk_size != 16 && p->chunk_size != 32 && p->chunk_size != 64)
     return GDR_ERR_UNSUPPORTED;
@@ -54,6 +55,7 @@ Shape shape_of(const gdr_problem* p) {
   s.out_bf16 = p->out_dtype == GDR_BF16;
   s.l2norm = (p->flags & GDR_USE_QK_L2NORM) != 0;
   s.channelwise = (p->flags & GDR_CHANNELWISE) != 0;
+  s.fused_gates = (p->flags & GDR_FUSED_GATES) != 0;
   return s;
 }
 
@@ -225,7 +227,7 @@ gdr_status gdr_backward(const gdr_problem* p, const void* q, const void* k, cons
                     at<float>(ws, w.pdk), at<float>(ws, w.pdb), at<float>(ws, w.pdg)};
   hipError_t e = gdr::launch_seq_bwd(s, a, stream);
   if (e != hipSuccess) return hip_fail(e);
-  gdr::EpiArgs ea{q, k, a.part_dq, a.part_dk, a.part_db, a.part_dg, gdr::seq_bwd_slices(s), dq, dk, dbeta, dg};
+  gdr::EpiArgs ea{q, k, a.part_dq, a.part_dk, a.part_db, a.part_dg, gdr::seq_bwd_slices(s), dq, dk, dbeta, dg, g, beta};
   e = gdr::launch_bwd_epilogue(s, ea, stream);
   return e == hipSuccess ? GDR_OK : hip_fail(e);
 }

@@ -53,6 +53,7 @@ struct CArgs {
   float *dg, *dbeta;  // [B][T][Hv]
   int64_t B, T;
   int Hk, Hv, NC, l2;
+  int fg;  // fused gate activation: g, beta hold pre-activations
 };
 
 template <typename OP_, int C_, int DK_, int BV_, int BVG_>
@@ -114,8 +115,11 @@ __device__ __forceinline__ void stage_gates(float* G, float* gam, float* lam, fl
   const int lane = threadIdx.x;
   if (lane >= 64) return;
   const int64_t row = (b * a.T + t0 + lane) * a.Hv + hv;
-  float x = lane < L ? a.g[row] : 0.f;
-  const float bt = lane < L ? a.beta[row] : 0.f;
+  float x = 0.f, bt = 0.f;
+  if (lane < L) {
+    x = a.fg ? fg_log_alpha(a.g[row]) : a.g[row];
+    bt = a.fg ? fg_beta(a.beta[row]) : a.beta[row];
+  }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const float y = __shfl_up(x, off, 64);
@@ -899,8 +903,8 @@ __global__ __launch_bounds__(256) void chunk_grad_kernel(CArgs a) {
     }
     if (r < L) {
       const int64_t row = (b * a.T + t0 + r) * a.Hv + hv;
-      a.dg[row] = x;
-      a.dbeta[row] = dB;
+      a.dg[row] = a.fg ? x * fg_dlog_alpha(a.g[row]) : x;
+      a.dbeta[row] = a.fg ? dB * fg_dbeta(a.beta[row]) : dB;
     }
   }
 }
@@ -945,6 +949,7 @@ CArgs base_args(const Shape& s, int C) {
   a.Hv = s.Hv;
   a.NC = static_cast<int>((s.T + C - 1) / C);
   a.l2 = s.l2norm ? 1 : 0;
+  a.fg = s.fused_gates ? 1 : 0;
   return a;
 }
 

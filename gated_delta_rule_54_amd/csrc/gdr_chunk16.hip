@@ -81,6 +81,7 @@ struct K16 {
   float *dg, *dbeta;       // [B][T][Hv]
   int64_t B, T;
   int Hk, Hv, NC, l2;
+  int fg;                  // fused gate activation: g, beta hold pre-activations
   int gi;                  // v-head within its k-head group (gradient launches)
 };
 
@@ -430,8 +431,8 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
     if (tid < 64) {
       const int rr = tid < L ? tid : L - 1;
       const int64_t row = (b * a.T + t0 + rr) * a.Hv + hv;
-      gv = a.g[row];
-      bv = a.beta[row];
+      gv = a.fg ? fg_log_alpha(a.g[row]) : a.g[row];
+      bv = a.fg ? fg_beta(a.beta[row]) : a.beta[row];
       gv = tid < L ? gv : 0.f;
       bv = tid < L ? bv : 0.f;
     }
@@ -1420,8 +1421,8 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     }
     if (r < L) {
       const int64_t row = (b * a.T + t0 + r) * a.Hv + hv;
-      a.dg[row] = x;
-      a.dbeta[row] = dB;
+      a.dg[row] = a.fg ? x * fg_dlog_alpha(a.g[row]) : x;
+      a.dbeta[row] = a.fg ? dB * fg_dbeta(a.beta[row]) : dB;
     }
   }
   if constexpr (MODE == kLast || MODE == kOnly) {
@@ -1556,6 +1557,7 @@ K16 args16(const Shape& s, int C, void* ws, const Ws16& w) {
   a.Hv = s.Hv;
   a.NC = static_cast<int>((s.T + C - 1) / C);
   a.l2 = s.l2norm ? 1 : 0;
+  a.fg = s.fused_gates ? 1 : 0;
   char* base = static_cast<char*>(ws);
   a.kimg = base + w.kimg;
   a.cimg = base + w.cimg;

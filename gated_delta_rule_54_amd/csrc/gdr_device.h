@@ -53,6 +53,19 @@ template <> __device__ __forceinline__ void st4<bf16_t>(bf16_t* p, const float (
   *reinterpret_cast<uint2*>(p) = v;
 }
 
+// Fused gate activation: g = -softplus(a) = -(max(a, 0) + log1p(e^-|a|)),
+// alpha = exp(g) = 1 / (1 + e^a), beta = sigmoid(b); and the factors that
+// take dL/dg and dL/dbeta to dL/da = -sigmoid(a) dL/dg and
+// dL/db = beta (1 - beta) dL/dbeta.
+__device__ __forceinline__ float fg_log_alpha(float a) { return -(fmaxf(a, 0.f) + log1pf(expf(-fabsf(a)))); }
+__device__ __forceinline__ float fg_alpha(float a) { return 1.f / (1.f + expf(a)); }
+__device__ __forceinline__ float fg_beta(float b) { return 1.f / (1.f + expf(-b)); }
+__device__ __forceinline__ float fg_dlog_alpha(float a) { return -1.f / (1.f + expf(-a)); }
+__device__ __forceinline__ float fg_dbeta(float b) {
+  const float s = fg_beta(b);
+  return s * (1.f - s);
+}
+
 // Sum over the lanes whose ids differ only in the bits of [LO, HI) masks,
 // i.e. xor-butterfly with masks LO, 2*LO, ..., HI/2.  Every lane ends with
 // the same total; the order of additions is fixed (deterministic).

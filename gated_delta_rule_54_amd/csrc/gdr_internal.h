@@ -21,7 +21,7 @@ class ProfScope {
 struct Shape {
   int64_t B, T;
   int Hk, Hv, D;      // Dk == Dv == D
-  bool io_bf16, out_bf16, l2norm, channelwise;
+  bool io_bf16, out_bf16, l2norm, channelwise, fused_gates;
 };
 
 // ---- sequential (token-by-token) path ------------------------------------
@@ -62,6 +62,7 @@ struct EpiArgs {
   int nslices;
   void *dq, *dk;
   float *dbeta, *dg;
+  const float *g, *beta;  // gate inputs (pre-activations with fused gates)
 };
 hipError_t launch_bwd_epilogue(const Shape& s, const EpiArgs& a, hipStream_t st);
 

@@ -44,6 +44,7 @@ struct Dims {
   int64_t B, T;
   int Hk, Hv;
   int l2;
+  int fg;  // fused gate activation: g, beta hold pre-activations
 };
 
 template <int N, typename T>
@@ -84,11 +85,11 @@ __device__ __forceinline__ void load_tok(Tok<L::RPL, CW>& x, const Dims& d,
   if constexpr (CW) {
     ld_rows<RPL, float>(g + grow * D + i0, x.a);
 #pragma unroll
-    for (int m = 0; m < RPL; ++m) x.a[m] = expf(x.a[m]);
+    for (int m = 0; m < RPL; ++m) x.a[m] = d.fg ? fg_alpha(x.a[m]) : expf(x.a[m]);
   } else {
-    x.a[0] = expf(g[grow]);
+    x.a[0] = d.fg ? fg_alpha(g[grow]) : expf(g[grow]);
   }
-  x.beta = beta[grow];
+  x.beta = d.fg ? fg_beta(beta[grow]) : beta[grow];
 }
 
 template <int RPL, bool CW>
@@ -410,19 +411,19 @@ __global__ __launch_bounds__(64) void epilogue_kernel(Dims d, EpiArgs a) {
     if (a.part_db && lane == 0) {
       float s = 0.f;
       for (int sl = 0; sl < a.nslices; ++sl) s += a.part_db[sl * pstride + row];
-      a.dbeta[row] = s;
+      a.dbeta[row] = d.fg ? s * fg_dbeta(a.beta[row]) : s;
     }
     if (a.part_dg) {
       if constexpr (CW) {
         for (int i = lane; i < D; i += 64) {
           float s = 0.f;
           for (int sl = 0; sl < a.nslices; ++sl) s += a.part_dg[(sl * pstride + row) * D + i];
-          a.dg[row * D + i] = s;
+          a.dg[row * D + i] = d.fg ? s * fg_dlog_alpha(a.g[row * D + i]) : s;
         }
       } else if (lane == 0) {
         float s = 0.f;
         for (int sl = 0; sl < a.nslices; ++sl) s += a.part_dg[sl * pstride + row];
-        a.dg[row] = s;
+        a.dg[row] = d.fg ? s * fg_dlog_alpha(a.g[row]) : s;
       }
     }
   }
@@ -508,7 +509,7 @@ __global__ __launch_bounds__(256) void epilogue128_kernel(Dims d, EpiArgs a) {
     if (a.part_db && sub == 0) {
       float sb = 0.f;
       for (int sl = 0; sl < a.nslices; ++sl) sb += a.part_db[sl * pstride + row];
-      a.dbeta[row] = sb;
+      a.dbeta[row] = d.fg ? sb * fg_dbeta(a.beta[row]) : sb;
     }
     if (a.part_dg) {
       if constexpr (CW) {
@@ -519,17 +520,21 @@ __global__ __launch_bounds__(256) void epilogue128_kernel(Dims d, EpiArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) gsum[e] += pv[e];
         }
+        if (d.fg) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gsum[e] *= fg_dlog_alpha(a.g[row * D + i + e]);
+        }
         st8<float>(a.dg + row * D + i, gsum);
       } else if (sub == 0) {
         float sg = 0.f;
         for (int sl = 0; sl < a.nslices; ++sl) sg += a.part_dg[sl * pstride + row];
-        a.dg[row] = sg;
+        a.dg[row] = d.fg ? sg * fg_dlog_alpha(a.g[row]) : sg;
       }
     }
   }
 }
 
-Dims dims_of(const Shape& s) { return Dims{s.B, s.T, s.Hk, s.Hv, s.l2norm ? 1 : 0}; }
+Dims dims_of(const Shape& s) { return Dims{s.B, s.T, s.Hk, s.Hv, s.l2norm ? 1 : 0, s.fused_gates ? 1 : 0}; }
 
 template <int D> constexpr int fwd_bv() { return D == 16 ? 16 : 32; }
 template <int D> constexpr int bwd_bv() { return D == 16 ? 16 : 32; }

@@ -26,11 +26,13 @@ def round_bf16(x):
 
 
 def make_inputs(seed, B, T, Hk, Hv, Dk, Dv, io_dtype="bf16",
-                channelwise=False, h0_std=None, with_do=True):
+                channelwise=False, h0_std=None, with_do=True, gate_preact=False):
     """Return a dict of float32 numpy arrays (bf16-exact where io is bf16).
 
     Keys: q, k [B,T,Hk,Dk]; v [B,T,Hv,Dv]; g [B,T,Hv] or [B,T,Hv,Dk];
     beta [B,T,Hv]; h0 [B,Hv,Dk,Dv] or None; do [B,T,Hv,Dv] or None.
+    With gate_preact, g and beta are the N(0, 1) draws themselves (the
+    pre-activations of the fused-gate flag), from the same stream.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     rnd = lambda shape: rng.standard_normal(shape, dtype=np.float32)
@@ -43,8 +45,11 @@ def make_inputs(seed, B, T, Hk, Hv, Dk, Dv, io_dtype="bf16",
     if h0_std is not None:
         h0 = (rnd((B, Hv, Dk, Dv)) * np.float32(h0_std)).astype(np.float32)
     do = rnd((B, T, Hv, Dv)) if with_do else None
-    g = (-np.logaddexp(0.0, a.astype(np.float64))).astype(np.float32)
-    beta = (1.0 / (1.0 + np.exp(-b.astype(np.float64)))).astype(np.float32)
+    if gate_preact:
+        g, beta = a, b
+    else:
+        g = (-np.logaddexp(0.0, a.astype(np.float64))).astype(np.float32)
+        beta = (1.0 / (1.0 + np.exp(-b.astype(np.float64)))).astype(np.float32)
     if io_dtype == "bf16":
         q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
         if do is not None:

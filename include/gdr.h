@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 1
+#define GDR_ABI_VERSION 2
 
 typedef enum gdr_status {
   GDR_OK = 0,
@@ -90,7 +90,14 @@ typedef enum gdr_algo {
   GDR_ALGO_CHUNKED = 2
 } gdr_algo;
 
-enum { GDR_USE_QK_L2NORM = 1u, GDR_CHANNELWISE = 2u };
+/* GDR_FUSED_GATES: g and beta carry pre-activations a and b; the kernels
+ * use g = -softplus(a) = -log(1 + e^a) (so alpha = 1 / (1 + e^a)) and
+ * beta = sigmoid(b), and gdr_backward returns dg = dL/da and dbeta = dL/db.
+ * This folds the caller's gate preparation into the kernels, in the spirit
+ * of the Megatron-LM page's L2-norm fold ("What"/"Why"); the activations are
+ * this library's choice (the pages name none).  Works with every algorithm
+ * and with GDR_CHANNELWISE (then a has g's per-channel shape). */
+enum { GDR_USE_QK_L2NORM = 1u, GDR_CHANNELWISE = 2u, GDR_FUSED_GATES = 4u };
 
 typedef struct gdr_problem {
   int64_t B, T;       /* batch, tokens                                      */
@@ -98,7 +105,7 @@ typedef struct gdr_problem {
   int32_t Dk, Dv;     /* key and value head dims                            */
   int32_t io_dtype;   /* gdr_dtype of q, k, v, dout                         */
   int32_t out_dtype;  /* gdr_dtype of o, dq, dk, dv                         */
-  uint32_t flags;     /* GDR_USE_QK_L2NORM | GDR_CHANNELWISE                */
+  uint32_t flags;     /* GDR_USE_QK_L2NORM | GDR_CHANNELWISE | GDR_FUSED_GATES */
   int32_t algo;       /* gdr_algo                                           */
   int32_t chunk_size; /* CHUNKED only: 16, 32 or 64; 0 means 64             */
 } gdr_problem;

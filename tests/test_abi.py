@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     lib = B.lib()
-    assert lib.gdr_abi_version() == 1
+    assert lib.gdr_abi_version() == 2
     for s in range(7):
         assert len(lib.gdr_status_str(s)) > 0
     assert lib.gdr_status_str(99) == b"unknown gdr_status"
@@ -56,7 +56,7 @@ def bwd_ws(p):
 @pytest.mark.parametrize("kw,status", [
     (dict(Hv=3), 2), (dict(T=-1), 2), (dict(B=-2), 2), (dict(Hk=0), 2), (dict(Dk=0), 2),
     (dict(Dk=64, Dv=64), 3), (dict(Dk=16, Dv=128), 3), (dict(io_dtype=2), 3),
-    (dict(out_dtype=-1), 3), (dict(flags=4), 3), (dict(algo=3), 3), (dict(chunk_size=48), 3),
+    (dict(out_dtype=-1), 3), (dict(flags=8), 3), (dict(algo=3), 3), (dict(chunk_size=48), 3),
 ])
 def test_workspace_query_rejects_bad_problems(kw, status):
     assert fwd_ws(prob(**kw))[0] == status

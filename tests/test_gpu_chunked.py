@@ -89,3 +89,15 @@ def test_chunked_vjp_sweep(B, T):
                     io_dtype="bf16", h0_std=0.02)
     heads = None if T <= 64 else ([(B - 1, Hk - 1)] if T == 4096 else [(0, 0), (B - 1, 5)])
     check_bwd(x, "bf16", heads=heads, algo=("chunked", 64))
+
+
+@pytest.mark.parametrize("io,D,T,C", [("f32", 16, 70, 32), ("bf16", 128, 150, 64), ("bf16", 128, 77, 32)])
+def test_fused_gates_chunked(io, D, T, C):
+    """GDR_FUSED_GATES on the chunked path (fp32 operands at D=16, fp16
+    operands at D=128; ragged last chunk; GQA 2:4): pre-activation gates,
+    forward and VJP against the fused-gate oracle."""
+    x = make_inputs(1200 + T + C, 2, T, 2, 4, D, D, io_dtype=io, h0_std=0.02 if D == 128 else 0.5,
+                    gate_preact=True)
+    dht = (0.1 * np.random.default_rng(T).standard_normal((2, 4, D, D))).astype(np.float32)
+    check_fwd(x, io, algo=("chunked", C), fg=True)
+    check_bwd(x, io, dht=dht, algo=("chunked", C), fg=True)

@@ -39,17 +39,17 @@ def algo_kw(algo):
     return dict(algo=algo)
 
 
-def check_fwd(x, io, l2=True, cw=False, h0=True, heads=None, algo="sequential"):
+def check_fwd(x, io, l2=True, cw=False, h0=True, heads=None, algo="sequential", fg=False):
     t = to_dev(x, io)
     o, ht = gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"] if h0 else None,
-                            use_qk_l2norm=l2, channelwise=cw, **algo_kw(algo))
+                            use_qk_l2norm=l2, channelwise=cw, fused_gates=fg, **algo_kw(algo))
     torch.cuda.synchronize()
     o, ht = host(o), host(ht)
     grp = x["v"].shape[2] // x["q"].shape[2]
     for (b, kh) in heads or [(None, None)]:
         xs = x if b is None else group_slice(x, b, kh, grp)
         ro, rht = orc.forward(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"],
-                              xs["h0"] if h0 else None, use_qk_l2norm=l2, channelwise=cw)
+                              xs["h0"] if h0 else None, use_qk_l2norm=l2, channelwise=cw, fused_gates=fg)
         if b is None:
             go, ght = o, ht
         else:
@@ -59,11 +59,12 @@ def check_fwd(x, io, l2=True, cw=False, h0=True, heads=None, algo="sequential"):
         assert relerr(ght, rht) < TOL[io], ("ht", relerr(ght, rht))
 
 
-def check_bwd(x, io, l2=True, cw=False, h0=True, dht=None, heads=None, algo="sequential"):
+def check_bwd(x, io, l2=True, cw=False, h0=True, dht=None, heads=None, algo="sequential", fg=False):
     t = to_dev(x, io)
     dht_t = None if dht is None else dev(dht)
     grads = gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"] if h0 else None,
-                             t["do"], dht_t, use_qk_l2norm=l2, channelwise=cw, **algo_kw(algo))
+                             t["do"], dht_t, use_qk_l2norm=l2, channelwise=cw, fused_gates=fg,
+                             **algo_kw(algo))
     torch.cuda.synchronize()
     grads = [host(a) for a in grads]
     grp = x["v"].shape[2] // x["q"].shape[2]
@@ -71,7 +72,7 @@ def check_bwd(x, io, l2=True, cw=False, h0=True, dht=None, heads=None, algo="seq
         xs = x if b is None else group_slice(x, b, kh, grp)
         dh = dht if (dht is None or b is None) else dht[b:b + 1, kh * grp:(kh + 1) * grp]
         ref = orc.backward(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], xs["h0"] if h0 else None,
-                           xs["do"], dh, use_qk_l2norm=l2, channelwise=cw)
+                           xs["do"], dh, use_qk_l2norm=l2, channelwise=cw, fused_gates=fg)
         for name, a, r in zip(GRAD_NAMES, grads, ref):
             if b is not None:
                 vs = slice(kh * grp, (kh + 1) * grp)
@@ -194,3 +195,30 @@ def test_sequential_vjp_sweep(B, T):
                     io_dtype="bf16", h0_std=0.02)
     heads = None if T <= 64 else ([(B - 1, Hk - 1)] if T == 4096 else [(0, 0), (B - 1, 5)])
     check_bwd(x, "bf16", heads=heads)
+
+
+# ------------------------------------------------------- fused gate activation
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("T,cw", [(1, False), (33, False), (17, True)])
+def test_fused_gates_sequential_fp32(T, cw):
+    """GDR_FUSED_GATES on the sequential kernels (fp32, D=16, GQA 1:4):
+    g, beta are pre-activations; forward and VJP (d/da, d/db) against the
+    fused-gate oracle."""
+    x = make_inputs(900 + T, 2, T, 1, 4, 16, 16, io_dtype="f32", channelwise=cw, h0_std=0.5,
+                    gate_preact=True)
+    dht = np.random.default_rng(T).standard_normal((2, 4, 16, 16)).astype(np.float32)
+    check_fwd(x, "f32", cw=cw, fg=True)
+    check_bwd(x, "f32", cw=cw, dht=dht, fg=True)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("cw", [False, True])
+def test_fused_gates_decode_bf16_d128(cw):
+    """Fused gates on the decode kernel at D=128 (bf16 io), single token and
+    a short prefill, plus the sequential VJP."""
+    for T in (1, 24):
+        x = make_inputs(950 + T + 7 * cw, 2, T, 2, 4, 128, 128, io_dtype="bf16", channelwise=cw,
+                        h0_std=0.02, gate_preact=True)
+        check_fwd(x, "bf16", cw=cw, fg=True)
+    check_bwd(x, "bf16", cw=cw, fg=True)
