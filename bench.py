@@ -100,9 +100,9 @@ def stored_traffic(kernel):
     return ent["bytes_per_launch"]
 
 
-def make_device_inputs(torch, seed, b, t, with_do=True):
+def make_device_inputs(torch, seed, b, t, with_do=True, gate_preact=False):
     from gated_delta_rule_54_amd.synth import make_inputs
-    x = make_inputs(seed, b, t, HK, HV, D, D, io_dtype="bf16", with_do=with_do)
+    x = make_inputs(seed, b, t, HK, HV, D, D, io_dtype="bf16", with_do=with_do, gate_preact=gate_preact)
     dev = torch.device("cuda")
     out = {}
     for n, a in x.items():
@@ -114,9 +114,12 @@ def make_device_inputs(torch, seed, b, t, with_do=True):
     return x, out
 
 
-def bench_chunked(torch, gdr, steps, warmup):
-    _, t = make_device_inputs(torch, 2, B, T)
-    kw = dict(algo="chunked", chunk_size=C, out_dtype=torch.bfloat16)
+def bench_chunked(torch, gdr, steps, warmup, fused_gates=False):
+    """One step = chunked forward + VJP of the whole workload.  With
+    fused_gates the gates are passed as pre-activations (same draws) and
+    activated inside the kernels."""
+    _, t = make_device_inputs(torch, 2, B, T, gate_preact=fused_gates)
+    kw = dict(algo="chunked", chunk_size=C, out_dtype=torch.bfloat16, fused_gates=fused_gates)
 
     def step():
         gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], None, **kw)
@@ -320,6 +323,9 @@ def main():
                  "wall_ms_per_step": round(1000 * wall / args.steps, 3)},
         "kernels": per_kernel,
     }
+    fms, _, _ = bench_chunked(torch, gdr, args.steps, args.warmup, fused_gates=True)
+    line["variants"] = {"fused_gates": {"ms_per_step": round(fms, 4), "tokens_per_s": round(tokens / (fms * 1e-3), 1),
+                                        "note": "same step with g, beta passed as pre-activations"}}
     if not args.no_decode:
         line["decode"] = bench_decode(torch, gdr)
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()
