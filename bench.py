@@ -205,6 +205,54 @@ def bench_decode(torch, gdr):
     return out
 
 
+def bench_channelwise(torch, gdr, reps=20):
+    """Channelwise-gate prefill forward (per-channel g of shape [B, T, Hv, Dk])
+    at B=1, Hk=16, Hv=32, D=128, bf16 io, zero h0, for T in {128, 512, 2048}:
+    the chunked path (C=64) against the sequential one; time per call from
+    events around `reps` back-to-back calls, plus the chunked kernels' own
+    times."""
+    from gated_delta_rule_54_amd.synth import make_inputs
+    dev = torch.device("cuda")
+    out = {}
+    for t_len in (128, 512, 2048):
+        x = make_inputs(7000 + t_len, 1, t_len, HK, HV, D, D, io_dtype="bf16", channelwise=True, with_do=False)
+        t = {n: (None if a is None else torch.from_numpy(a).to(dev)) for n, a in x.items()}
+        for n in ("q", "k", "v"):
+            t[n] = t[n].to(torch.bfloat16)
+        ent = {}
+        for algo in ("sequential", "chunked"):
+            kw = dict(algo=algo, channelwise=True, out_dtype=torch.bfloat16)
+            if algo == "chunked":
+                kw["chunk_size"] = C
+
+            def call():
+                gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], None, **kw)
+
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            us = 1000.0 * e0.elapsed_time(e1) / reps
+            ent[f"{algo}_us"] = round(us, 2)
+            if algo == "chunked":  # a separate pass with the library's per-kernel events
+                gdr.gdr_profile_enable(True)
+                for _ in range(reps):
+                    call()
+                kt = gdr.gdr_profile_read()
+                gdr.gdr_profile_enable(False)
+                ent["chunked_kernels_us"] = {k: round(1000.0 * v[0] / v[1], 2) for k, v in kt.items()}
+        ent["speedup"] = round(ent["sequential_us"] / ent["chunked_us"], 2)
+        ent["chunked_tokens_per_s"] = round(t_len / (ent["chunked_us"] * 1e-6), 1)
+        out[f"T={t_len}"] = ent
+    out["config"] = f"B=1 Hk={HK} Hv={HV} Dk=Dv={D}, channelwise gate, bf16 io, zero h0, chunk {C}"
+    return out
+
+
 def cpu_baseline(min_seconds=10.0, max_groups=32):
     """The fp64 oracle (forward + VJP) on (b, k-head) groups of the
     full-length workload (each group = the 2 v-heads sharing a k-head), run
@@ -326,6 +374,7 @@ def main():
     fms, _, _ = bench_chunked(torch, gdr, args.steps, args.warmup, fused_gates=True)
     line["variants"] = {"fused_gates": {"ms_per_step": round(fms, 4), "tokens_per_s": round(tokens / (fms * 1e-3), 1),
                                         "note": "same step with g, beta passed as pre-activations"}}
+    line["variants"]["channelwise_prefill"] = bench_channelwise(torch, gdr)
     if not args.no_decode:
         line["decode"] = bench_decode(torch, gdr)
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()

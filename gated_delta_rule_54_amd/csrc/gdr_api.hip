@@ -66,7 +66,11 @@ constexpr bool kChunkedBackward = true;
 
 // SEQUENTIAL or CHUNKED for this call; CHUNKED needs a scalar gate.
 gdr_status resolve_algo(const gdr_problem* p, bool backward, int* algo) {
-  const bool chunk_ok = !(p->flags & GDR_CHANNELWISE) && (!backward || kChunkedBackward);
+  // channelwise gates: chunked forward on the fp16 matrix-core path only
+  // (bf16 io, Dk = 128, C >= 32); their VJP runs sequentially
+  const bool chunk_ok = (p->flags & GDR_CHANNELWISE)
+                            ? !backward && gdr::chunk_uses_f16(shape_of(p), chunk_of(p))
+                            : !backward || kChunkedBackward;
   if (p->algo == GDR_ALGO_CHUNKED) {
     if (!chunk_ok) return GDR_ERR_UNSUPPORTED;
     *algo = GDR_ALGO_CHUNKED;

@@ -1516,6 +1516,418 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
 }
 
 // ---------------------------------------------------------------------------
+// Channelwise gates (the per-key-channel decay of the page "Two-pass
+// optimization for channelwise gated delta rule kernel") on the chunked
+// path, forward only.  With G_r the per-channel running sum of g over the
+// chunk, the chunk algebra of the scalar gate holds with each key and query
+// row scaled per channel:
+//   Y = (K o e^G) H0,  RHS = beta (V - Y),  U = T RHS,
+//   O = (Q o e^G) H0 + P U,  H_C = diag(e^{G_C}) H0 + (K o e^{G_C - G})^T U,
+//   A_rs = beta_r sum_i k_ri k_si e^{G_ri - G_si}  (s < r),
+//   P_rs = sum_i q_ri k_si e^{G_ri - G_si}          (s <= r).
+// Blocks of A / P below the 16-row diagonal blocks run on the matrix cores
+// with both factors taken relative to the first row b of the row block
+// (k_r e^{G_r - G_b} and k_s e^{G_b - G_s}, each <= 1 because g <= 0); the
+// diagonal blocks are summed exactly in fp32 with one exponential per pair
+// and channel, so no gate value can overflow a factor.
+// ---------------------------------------------------------------------------
+template <int C>
+struct ImgCW {
+  static constexpr int LDC = C + 8;
+  static constexpr uint32_t KN = C * LDK * 2;       // one [C][LDK] fp16 tile
+  static constexpr uint32_t KEY = 3 * KN;           // K o e^G | Q o e^G | K o e^{G_C - G}
+  static constexpr uint32_t GT = (C + DK) * 4;      // beta [C] | e^{G_C} [DK]
+  static constexpr uint32_t TM = C * LDC * 2;
+  static constexpr uint32_t CHK = GT + 2 * TM;      // gates | T | P
+};
+
+// T = (I + A)^-1 of one chunk (A strictly lower, fp32 [C][LDA]) into Tf
+// (fp32) and Tst (fp16 [C][LDC], whose blocks above the diagonal blocks the
+// caller has zeroed): wave w inverts diagonal block w by substitution, the
+// blocks below follow one distance at a time on fp32 matrix cores.  Called by
+// all 256 threads; ends with a barrier.
+template <int C, int LDA, int LDC>
+__device__ __forceinline__ void unit_lower_inverse(const float* A, float* Tf, _Float16* Tst) {
+  constexpr int NT = C / 16;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  if (w < NT && lane < 16) {
+    const int o = 16 * w;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc[2] = {r == lane ? 1.f : 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < r; ++s2) acc[s2 & 1] -= A[(o + r) * LDA + o + s2] * x[s2];
+      x[r] = acc[0] + acc[1];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      Tf[(o + r) * LDA + o + lane] = x[r];
+      Tst[(o + r) * LDC + o + lane] = static_cast<_Float16>(x[r]);
+    }
+  }
+  __syncthreads();
+  for (int d = 1; d < NT; ++d) {
+    const int i = d + w;
+    if (i < NT) {
+      const int j = i - d;
+      f32x4 m = zero4();
+      for (int k = j; k < i; ++k) {
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+          const float av = A[(16 * i + c16) * LDA + 16 * k + k0 + g];
+          const float bv = Tf[(16 * k + k0 + g) * LDA + 16 * j + c16];
+          m = F32Op::mma(av, bv, m);
+        }
+      }
+      f32x4 tij = zero4();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tij = F32Op::mma(Tf[(16 * i + c16) * LDA + 16 * i + 4 * g + e], m[e], tij);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Tf[(16 * i + 4 * g + e) * LDA + 16 * j + c16] = -tij[e];
+        Tst[(16 * i + 4 * g + e) * LDC + 16 * j + c16] = static_cast<_Float16>(-tij[e]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Eight consecutive fp32 values at p (16-byte aligned).
+__device__ __forceinline__ void ld8f(float (&x)[8], const float* p) {
+  const float4 a0 = *reinterpret_cast<const float4*>(p), a1 = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
+  x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
+}
+
+// Rows of the 16-row diagonal blocks that 16-lane group grp of a cwprep
+// workgroup sums: C = 64: block grp & 3, local rows {w, 7-w, 8+w, 15-w} of
+// wave w = grp / 4 (every group of a wave runs the same loop bounds; 34
+// pairs each); C = 32: block grp & 1, local rows {w, 15-w} or {7-w, 8+w}.
+template <int C>
+__device__ __forceinline__ int diag_row(int grp, int j) {
+  const int w = grp >> 2;
+  if constexpr (C == 64) {
+    const int rl = j == 0 ? w : j == 1 ? 7 - w : j == 2 ? 8 + w : 15 - w;
+    return 16 * (grp & 3) + rl;
+  } else {
+    const int sel = (grp >> 1) & 1;
+    const int rl = sel == 0 ? (j == 0 ? w : 15 - w) : (j == 0 ? 7 - w : 8 + w);
+    return 16 * (grp & 1) + rl;
+  }
+}
+
+template <int C>
+__global__ __launch_bounds__(256) void cwprep16_kernel(K16 a) {
+  using IM = ImgCW<C>;
+  constexpr int NT = C / 16, LDA = C + 4, LDC = IM::LDC, LDG = DK + 4;
+  constexpr int TPR = 256 / C, EPT = DK / TPR, NV = EPT / 8;
+  static_assert(C == 64 || C == 32, "chunk of 32 or 64 rows");
+  __shared__ __align__(16) _Float16 Ks[C * LDK];
+  __shared__ __align__(16) _Float16 Qs[C * LDK];
+  __shared__ __align__(16) float G2[C * LDG];      // log2(e) * G[r][i]
+  __shared__ __align__(16) float A[C * LDA];
+  __shared__ __align__(16) float Tf[C * LDA];
+  __shared__ __align__(16) _Float16 Pst[C * LDC];
+  __shared__ __align__(16) _Float16 Tst[C * LDC];
+  __shared__ __align__(16) _Float16 Lk[16 * LDK];
+  __shared__ __align__(16) _Float16 Lq[16 * LDK];
+  __shared__ __align__(16) _Float16 Rt[(C - 16) * LDK];
+  __shared__ float bet[C];
+  __shared__ float half_sum[DK];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int c = blockIdx.x, hv = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int kh = hv / (a.Hv / a.Hk);
+  const int64_t t0 = static_cast<int64_t>(c) * C;
+  const int L = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
+  // gates: thread -> channel tid % DK, rows of half tid / DK, running sum in
+  // registers (g = 0 past the end)
+  constexpr int RH = C / 2;
+  const int gi = tid & (DK - 1), gh = tid >> 7;
+  float gr[RH];
+  {
+    const float* gp = a.g + ((b * a.T + t0 + gh * RH) * a.Hv + hv) * DK + gi;
+    const int64_t rs = static_cast<int64_t>(a.Hv) * DK;
+#pragma unroll
+    for (int j = 0; j < RH; ++j) gr[j] = gh * RH + j < L ? gp[j * rs] : 0.f;
+  }
+  {  // q / k rows (normalised, fp16) and beta
+    const int r = tid / TPR, part = tid % TPR;
+    const int rc = r < L ? r : L - 1;
+    const int64_t off = ((b * a.T + t0 + rc) * a.Hk + kh) * DK + part * EPT;
+    uint4 kr[NV], qr[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      kr[u] = sel4(r < L, *reinterpret_cast<const uint4*>(a.k + off + 8 * u));
+      qr[u] = sel4(r < L, *reinterpret_cast<const uint4*>(a.q + off + 8 * u));
+    }
+    norm_rows<C, NV>(Ks, kr, a.l2);
+    norm_rows<C, NV>(Qs, qr, a.l2);
+    if (tid < C) {
+      float bv = 0.f;
+      if (tid < L) {
+        bv = a.beta[(b * a.T + t0 + tid) * a.Hv + hv];
+        if (a.fg) bv = fg_beta(bv);
+      }
+      bet[tid] = bv;
+    }
+    for (int e = tid; e < C * LDC / 8; e += 256) reinterpret_cast<uint4*>(Pst)[e] = uint4{0u, 0u, 0u, 0u};
+    for (int e = tid; e < C * LDC / 8; e += 256) reinterpret_cast<uint4*>(Tst)[e] = uint4{0u, 0u, 0u, 0u};
+  }
+  float run = 0.f;
+#pragma unroll
+  for (int j = 0; j < RH; ++j) {
+    run += a.fg && gh * RH + j < L ? fg_log_alpha(gr[j]) : gr[j];
+    gr[j] = run;
+  }
+  if (gh == 0) {
+    half_sum[gi] = run;
+#pragma unroll
+    for (int j = 0; j < RH; ++j) G2[j * LDG + gi] = gr[j] * kLog2e;
+  }
+  __syncthreads();
+  if (gh == 1) {
+    const float base = half_sum[gi];
+#pragma unroll
+    for (int j = 0; j < RH; ++j) G2[(RH + j) * LDG + gi] = (gr[j] + base) * kLog2e;
+  }
+  __syncthreads();
+
+  // diagonal blocks, exactly in fp32: a 16-lane group per row set, eight
+  // channels per lane, one exponential per pair and channel, DPP row sums
+  {
+    const int grp = tid >> 4, i0 = 8 * c16;
+#pragma unroll 1
+    for (int j = 0; j < NT; ++j) {
+      const int rr = diag_row<C>(grp, j), s0 = rr & ~15;
+      float gr8[8], kr8[8], qr8[8];
+      ld8f(gr8, G2 + rr * LDG + i0);
+      {
+        const f16x8 kv = ld8(Ks + rr * LDK + i0), qv = ld8(Qs + rr * LDK + i0);
+#pragma unroll
+        for (int q2 = 0; q2 < 8; ++q2) {
+          kr8[q2] = static_cast<float>(kv[q2]);
+          qr8[q2] = static_cast<float>(qv[q2]);
+        }
+      }
+      for (int ss = s0; ss <= rr; ++ss) {
+        float gs8[8];
+        ld8f(gs8, G2 + ss * LDG + i0);
+        const f16x8 ks = ld8(Ks + ss * LDK + i0);
+        float kk = 0.f, qk = 0.f;
+#pragma unroll
+        for (int q2 = 0; q2 < 8; ++q2) {
+          const float x = static_cast<float>(ks[q2]) * __builtin_amdgcn_exp2f(gr8[q2] - gs8[q2]);
+          kk += kr8[q2] * x;
+          qk += qr8[q2] * x;
+        }
+        kk = row16_sum(kk);
+        qk = row16_sum(qk);
+        if (c16 == 0) {
+          A[rr * LDA + ss] = ss < rr ? bet[rr] * kk : 0.f;
+          Pst[rr * LDC + ss] = static_cast<_Float16>(qk);
+        }
+      }
+    }
+  }
+  // blocks below the diagonal, one row block R at a time, on the matrix cores
+  for (int R = 1; R < NT; ++R) {
+    const int bref = 16 * R;
+    for (int e = tid; e < (16 + bref) * (DK / 8); e += 256) {
+      const int row = e / (DK / 8), i0 = 8 * (e % (DK / 8));
+      float gb[8], gx[8];
+      ld8f(gb, G2 + bref * LDG + i0);
+      if (row < 16) {  // row block R of k and q, scaled by e^{G_r - G_b} <= 1
+        ld8f(gx, G2 + (bref + row) * LDG + i0);
+        const f16x8 kv = ld8(Ks + (bref + row) * LDK + i0), qv = ld8(Qs + (bref + row) * LDK + i0);
+        f16x8 ko, qo;
+#pragma unroll
+        for (int q2 = 0; q2 < 8; ++q2) {
+          const float f = __builtin_amdgcn_exp2f(gx[q2] - gb[q2]);
+          ko[q2] = static_cast<_Float16>(static_cast<float>(kv[q2]) * f);
+          qo[q2] = static_cast<_Float16>(static_cast<float>(qv[q2]) * f);
+        }
+        *reinterpret_cast<f16x8*>(Lk + row * LDK + i0) = ko;
+        *reinterpret_cast<f16x8*>(Lq + row * LDK + i0) = qo;
+      } else {  // rows s < b of k, scaled by e^{G_b - G_s} <= 1
+        const int s2 = row - 16;
+        ld8f(gx, G2 + s2 * LDG + i0);
+        const f16x8 kv = ld8(Ks + s2 * LDK + i0);
+        f16x8 ko;
+#pragma unroll
+        for (int q2 = 0; q2 < 8; ++q2)
+          ko[q2] = static_cast<_Float16>(static_cast<float>(kv[q2]) * __builtin_amdgcn_exp2f(gb[q2] - gx[q2]));
+        *reinterpret_cast<f16x8*>(Rt + s2 * LDK + i0) = ko;
+      }
+    }
+    __syncthreads();
+    if (w < R) {  // tile (R, S = w)
+      const f32x4 kk = mma_tile<F16Op, false, false>(zero4(), Lk, LDK, 0, Rt, LDK, 16 * w, DK);
+      const f32x4 qk = mma_tile<F16Op, false, false>(zero4(), Lq, LDK, 0, Rt, LDK, 16 * w, DK);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = bref + 4 * g + e, ss = 16 * w + c16;
+        A[rr * LDA + ss] = bet[rr] * kk[e];
+        Pst[rr * LDC + ss] = static_cast<_Float16>(qk[e]);
+      }
+    }
+    __syncthreads();
+  }
+  unit_lower_inverse<C, LDA, LDC>(A, Tf, Tst);
+
+  // ---- images of this (b, v-head, chunk)
+  char* cim = a.cimg + ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(IM::CHK);
+  float* cg = reinterpret_cast<float*>(cim);
+  for (int e = tid; e < C + DK; e += 256)
+    cg[e] = e < C ? bet[e] : __builtin_amdgcn_exp2f(G2[(C - 1) * LDG + e - C]);
+  constexpr int UC = LDC / 8;
+  write_tile<C, UC>(cim + IM::GT, [&](int r, int u) { return ld8(Tst + r * LDC + 8 * u); });
+  write_tile<C, UC>(cim + IM::GT + IM::TM, [&](int r, int u) { return ld8(Pst + r * LDC + 8 * u); });
+  char* kim = a.kimg + ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(IM::KEY);
+  constexpr int UK = LDK / 8;
+  // row r, unit u of X o e^G (to_end false) or X o e^{G_C - G} (to_end true)
+  auto scaled = [&](const _Float16* X, int r, int u, bool to_end) {
+    float gx[8];
+    ld8f(gx, G2 + r * LDG + 8 * u);
+    if (to_end) {
+      float ge[8];
+      ld8f(ge, G2 + (C - 1) * LDG + 8 * u);
+#pragma unroll
+      for (int q2 = 0; q2 < 8; ++q2) gx[q2] = ge[q2] - gx[q2];
+    }
+    const f16x8 xv = ld8(X + r * LDK + 8 * u);
+    f16x8 v;
+#pragma unroll
+    for (int q2 = 0; q2 < 8; ++q2)
+      v[q2] = static_cast<_Float16>(static_cast<float>(xv[q2]) * __builtin_amdgcn_exp2f(gx[q2]));
+    return v;
+  };
+  write_tile<C, UK>(kim, [&](int r, int u) { return scaled(Ks, r, u, false); });
+  write_tile<C, UK>(kim + IM::KN, [&](int r, int u) { return scaled(Qs, r, u, false); });
+  write_tile<C, UK>(kim + 2 * IM::KN, [&](int r, int u) { return scaled(Ks, r, u, true); });
+}
+
+// Channelwise forward chain: as chain16 with outputs, using the scaled key
+// rows of the channelwise images and decaying H's rows by e^{G_C}:
+//   Y = Kg H, Z = Qg H, U = T (beta (V - Y)), O = Z + P U,
+//   H = diag(e^{G_C}) H + Kl^T U.
+// The chunk's o leaves the compute waves as 2-byte stores (their LDS share
+// holds the three key tiles).
+template <int C, typename TO>
+__global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
+  using IM = ImgCW<C>;
+  constexpr int NT = C / 16, LDC = IM::LDC;
+  constexpr uint32_t CB = IM::CHK, KB = IM::KEY, VB = C * BV * 2;
+  __shared__ __align__(16) char bufA[CB + KB + VB];
+  __shared__ __align__(16) char bufB[CB + KB + VB];
+
+  const int w = wave_id(), lane = lane_id(), g = lane >> 4, c16 = lane & 15;
+  const ChainPos p = chain_pos(a);
+  auto rows_of = [&](int c) { return static_cast<int>(a.T - static_cast<int64_t>(c) * C < C ? a.T - static_cast<int64_t>(c) * C : C); };
+  auto seq_rsrc = [&](const void* base, int esize, int c, uint32_t rowb) {
+    const char* p0 = static_cast<const char*>(base) + (p.b * a.T + static_cast<int64_t>(c) * C) * a.Hv * DK * esize;
+    return make_rsrc(p0, static_cast<uint32_t>(rows_of(c)) * rowb);
+  };
+  const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
+  const uint32_t rowo = static_cast<uint32_t>(a.Hv) * DK * sizeof(TO);
+
+  if (w == NCW) {  // ---- producer wave
+    const char* kim0 = a.kimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::KEY);
+    const char* cim0 = a.cimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::CHK);
+    const uint32_t colv = (p.hv * DK + p.half * BV) * 2;
+    auto stage = [&](int c, char* buf) {
+      dma<CB, 64>(make_rsrc(cim0 + c * static_cast<int64_t>(IM::CHK), CB), 0, buf, lane, 0);
+      dma<KB, 64>(make_rsrc(kim0 + c * static_cast<int64_t>(IM::KEY), KB), 0, buf + CB, lane, 0);
+      dma_rows<C, BV * 2, 64>(seq_rsrc(a.v, 2, c, rowv), rowv, colv, rows_of(c), buf + CB + KB, lane, 0);
+    };
+    stage(0, bufA);
+    wait_all();
+    lds_barrier();
+    for (int c = 0; c < a.NC; c += 2) {
+      if (c + 1 < a.NC) stage(c + 1, bufB);
+      wait_all();
+      lds_barrier();
+      if (c + 1 < a.NC) {
+        if (c + 2 < a.NC) stage(c + 2, bufA);
+        wait_all();
+        lds_barrier();
+      }
+    }
+    return;
+  }
+
+  // ---- compute waves
+  const int jcol = p.half * BV + 16 * w + c16;
+  const int64_t hbase = (p.b * a.Hv + p.hv) * DK * DK + jcol;
+  const uint32_t voffo = 4 * g * rowo + (p.hv * DK + jcol) * static_cast<uint32_t>(sizeof(TO));
+  f32x4 h[NTK];
+#pragma unroll
+  for (int ti = 0; ti < NTK; ++ti) {
+    h[ti] = zero4();
+    if (a.h0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[ti][e] = a.h0[hbase + (16 * ti + 4 * g + e) * DK];
+    }
+  }
+  lds_barrier();
+  f32x4 o[NT];
+  auto step = [&](int c, const char* cur) __attribute__((always_inline)) {
+    if (c > 0) store_strip_buf<TO, NT>(seq_rsrc(a.o, sizeof(TO), c - 1, rowo), voffo, rowo, o);
+    const float* bet = reinterpret_cast<const float*>(cur);
+    const float* gC = bet + C;
+    const _Float16* Tm = reinterpret_cast<const _Float16*>(cur + IM::GT);
+    const _Float16* Pm = Tm + C * LDC;
+    const _Float16* Kg = reinterpret_cast<const _Float16*>(cur + CB);
+    const _Float16* Qg = Kg + C * LDK;
+    const _Float16* Kl = Qg + C * LDK;
+    const uint16_t* Vs = reinterpret_cast<const uint16_t*>(cur + CB + KB);
+
+    f16x8 hf[NTK / 2];
+    chain_frags<NTK>(hf, h);
+    f32x4 y[NT], u[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) y[t] = u[t] = o[t] = zero4();
+    mma_chain_rows<NT, NTK>(y, Kg, LDK, hf);
+    mma_chain_rows<NT, NTK>(o, Qg, LDK, hf);
+    f32x4 rhs[NT];
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) {
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
+      float vv[4];
+      tile_col4_bf16(vv, Vs, BV, 16 * tr + 4 * g, 16 * w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rhs[tr][e] = bv[e] * (vv[e] - y[tr][e]);
+    }
+    f16x8 bf[NT / 2];
+    chain_frags<NT>(bf, rhs);
+    mma_chain_rows<NT, NT>(u, Tm, LDC, bf);
+    chain_frags<NT>(bf, u);
+    mma_chain_rows<NT, NT>(o, Pm, LDC, bf);
+#pragma unroll
+    for (int ti = 0; ti < NTK; ++ti) {
+      const f32x4 dec = *reinterpret_cast<const f32x4*>(gC + 16 * ti + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[ti][e] *= dec[e];
+    }
+    mma_chain_rows_t<NTK, NT>(h, Kl, LDK, bf);
+    lds_barrier();
+  };
+  for (int c = 0; c < a.NC; c += 2) {
+    step(c, bufA);
+    if (c + 1 < a.NC) step(c + 1, bufB);
+  }
+  store_strip_buf<TO, NT>(seq_rsrc(a.o, sizeof(TO), a.NC - 1, rowo), voffo, rowo, o);
+  if (a.ht) {
+#pragma unroll
+    for (int ti = 0; ti < NTK; ++ti)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a.ht[hbase + (16 * ti + 4 * g + e) * DK] = h[ti][e];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 constexpr size_t kAlign = 256;
@@ -1654,12 +2066,56 @@ hipError_t bwd_all(const Shape& s, const ChunkBwdArgs& x, void* ws, hipStream_t 
   return e;
 }
 
+// Channelwise forward: per-v-head key and chunk images, prep then chain.
+template <int C>
+Ws16 plan_cw(const Shape& s) {
+  using IM = ImgCW<C>;
+  const size_t nv = static_cast<size_t>(s.B) * s.Hv * static_cast<size_t>((s.T + C - 1) / C);
+  Ws16 w{};
+  size_t off = 0;
+  w.kimg = off; off = up(off + nv * IM::KEY);
+  w.cimg = off; off = up(off + nv * IM::CHK);
+  w.total = off;
+  return w;
+}
+
+template <int C, typename TO>
+hipError_t fwd_cw(const Shape& s, const ChunkFwdArgs& x, void* ws, hipStream_t st) {
+  K16 a = args16(s, C, ws, plan_cw<C>(s));
+  a.q = static_cast<const bf16_t*>(x.q);
+  a.k = static_cast<const bf16_t*>(x.k);
+  a.v = static_cast<const bf16_t*>(x.v);
+  a.g = x.g;
+  a.beta = x.beta;
+  a.h0 = x.h0;
+  a.o = x.o;
+  a.ht = x.ht;
+  {
+    ProfScope ps("chunk_prep_cw", st);
+    hipLaunchKernelGGL((cwprep16_kernel<C>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(256), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  ProfScope ps("chunk_fwd_cw", st);
+  hipLaunchKernelGGL((cwchain16_kernel<C, TO>), dim3(static_cast<unsigned>(2 * a.Hv * a.B)), dim3(64 * (NCW + 1)), 0,
+                     st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-size_t chunk16_fwd_workspace(const Shape& s, int C) { return plan_any(s, C, false).total; }
+size_t chunk16_fwd_workspace(const Shape& s, int C) {
+  if (s.channelwise) return C == 64 ? plan_cw<64>(s).total : plan_cw<32>(s).total;
+  return plan_any(s, C, false).total;
+}
 size_t chunk16_bwd_workspace(const Shape& s, int C) { return plan_any(s, C, true).total; }
 
 hipError_t launch_chunk16_fwd(const Shape& s, int C, const ChunkFwdArgs& x, void* ws, hipStream_t st) {
+  if (s.channelwise) {
+    if (C == 64) return s.out_bf16 ? fwd_cw<64, bf16_t>(s, x, ws, st) : fwd_cw<64, float>(s, x, ws, st);
+    if (C == 32) return s.out_bf16 ? fwd_cw<32, bf16_t>(s, x, ws, st) : fwd_cw<32, float>(s, x, ws, st);
+    return hipErrorInvalidValue;
+  }
   if (C == 64) return s.out_bf16 ? fwd_all<64, bf16_t>(s, x, ws, st) : fwd_all<64, float>(s, x, ws, st);
   if (C == 32) return s.out_bf16 ? fwd_all<32, bf16_t>(s, x, ws, st) : fwd_all<32, float>(s, x, ws, st);
   return hipErrorInvalidValue;

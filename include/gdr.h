@@ -109,6 +109,10 @@ typedef struct gdr_problem {
   int32_t algo;       /* gdr_algo                                           */
   int32_t chunk_size; /* CHUNKED only: 16, 32 or 64; 0 means 64             */
 } gdr_problem;
+/* With GDR_CHANNELWISE, GDR_ALGO_CHUNKED is supported for the forward pass
+ * with bf16 io, Dk = Dv = 128 and chunk_size 32 or 64 (else
+ * GDR_ERR_UNSUPPORTED); the backward pass is sequential only.  AUTO picks
+ * the chunked forward there when T > 64. */
 
 /* Workspace bytes the call needs for problem *p (0 is possible).  Returns
  * the same validation status gdr_forward/gdr_backward would for the shape

@@ -121,3 +121,21 @@ def test_bad_problem_beats_everything():
     assert call_fwd(prob(Hv=3), q=None) == 2
     assert call_bwd(prob(Dk=32, Dv=32), dq=None) == 3
     assert B.lib().gdr_forward(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, 0, None) == 1
+
+
+def test_channelwise_chunked_forward_support():
+    """Channelwise gates: chunked forward only with bf16 io, D = 128 and
+    C in {32, 64}; the chunked backward is refused; AUTO falls back to the
+    sequential kernels (no workspace) where the chunked forward is absent."""
+    cw = dict(flags=3, io_dtype=1, Dk=128, Dv=128, T=256)
+    for C in (0, 32, 64):
+        st, n = fwd_ws(prob(algo=2, chunk_size=C, **cw))
+        assert st == 0 and n > 0
+    assert fwd_ws(prob(algo=2, chunk_size=16, **cw))[0] == 3
+    assert fwd_ws(prob(algo=2, flags=3, T=256))[0] == 3          # fp32 io, D = 16
+    assert bwd_ws(prob(algo=2, **cw))[0] == 3
+    st, n = fwd_ws(prob(algo=0, **cw))
+    assert st == 0 and n > 0                                      # AUTO -> chunked
+    assert fwd_ws(prob(algo=0, **dict(cw, T=64))) == (0, 0)       # short: sequential
+    assert fwd_ws(prob(algo=0, flags=3, T=256)) == (0, 0)         # fp32: sequential
+    assert bwd_ws(prob(algo=0, **cw))[0] == 0                     # AUTO VJP: sequential

@@ -5,7 +5,7 @@ through the C ABI.  Tolerances: 1e-4 for fp32 io, 2e-3 for bf16 io (max
 import numpy as np
 import pytest
 
-from gated_delta_rule_54_amd.synth import make_inputs
+from gated_delta_rule_54_amd.synth import make_inputs, round_bf16
 from tests.test_gpu_sequential import check_fwd
 
 pytestmark = pytest.mark.gpu
@@ -101,3 +101,36 @@ def test_fused_gates_chunked(io, D, T, C):
     dht = (0.1 * np.random.default_rng(T).standard_normal((2, 4, D, D))).astype(np.float32)
     check_fwd(x, io, algo=("chunked", C), fg=True)
     check_bwd(x, io, dht=dht, algo=("chunked", C), fg=True)
+
+
+# ------------------------------------------------- channelwise chunked forward
+
+@pytest.mark.parametrize("T,C", [(1, 64), (50, 64), (64, 64), (200, 64), (200, 32), (97, 32)])
+@pytest.mark.parametrize("l2", [True, False])
+def test_channelwise_chunked_forward(T, C, l2):
+    """Per-channel gate on the chunked forward (bf16 io, D=128, fp16 operands):
+    ragged last chunk, GQA 2:4, nonzero h0, flag on/off.  With the flag off
+    the rows of q and k are unit vectors already (rounded to bf16), as raw
+    N(0, 1) keys of norm ~11 make the recurrence itself diverge."""
+    x = make_inputs(1400 + T + C + l2, 2, T, 2, 4, 128, 128, io_dtype="bf16", channelwise=True,
+                    h0_std=0.02, with_do=False)
+    if not l2:
+        for n in ("q", "k"):
+            u = x[n] / np.linalg.norm(x[n].astype(np.float64), axis=-1, keepdims=True)
+            x[n] = round_bf16(u.astype(np.float32))
+    check_fwd(x, "bf16", l2=l2, cw=True, algo=("chunked", C))
+
+
+def test_channelwise_chunked_forward_fused_gates():
+    x = make_inputs(1500, 2, 150, 2, 4, 128, 128, io_dtype="bf16", channelwise=True,
+                    h0_std=0.02, with_do=False, gate_preact=True)
+    check_fwd(x, "bf16", cw=True, algo=("chunked", 64), fg=True)
+
+
+@pytest.mark.parametrize("T", [128, 512, 2048])
+def test_channelwise_chunked_prefill(T):
+    """Channelwise prefill B=1, Hk=16, Hv=32, D=128, bf16, zero h0, C=64:
+    the GPU runs every head; the oracle checks two sampled k-head groups."""
+    x = make_inputs(1600 + T, 1, T, 16, 32, 128, 128, io_dtype="bf16", channelwise=True,
+                    with_do=False)
+    check_fwd(x, "bf16", cw=True, h0=False, heads=[(0, 0), (0, 11)], algo=("chunked", 64))
