@@ -344,9 +344,9 @@ __device__ __forceinline__ void unpack8(const uint4& u, float (&x)[8]) {
 // Rows of q or k (thread -> row tid / TPR, elements part * EPT ..), each
 // scaled by (sum x^2 + eps)^(-1/2) over Dk when l2 is set (the L2 norm the
 // Megatron-LM page folds into the kernel), written as fp16 to dst[r][LDK].
-template <int C, int NV>
+template <int C, int NV, int NTH = 256>
 __device__ __forceinline__ void norm_rows(_Float16* dst, const uint4 (&raw)[NV], int l2) {
-  constexpr int TPR = 256 / C, EPT = DK / TPR;
+  constexpr int TPR = NTH / C, EPT = DK / TPR;
   const int tid = threadIdx.x, r = tid / TPR, part = tid % TPR;
   float x[NV][8];
   float ss = 0.f;
@@ -369,10 +369,10 @@ __device__ __forceinline__ void norm_rows(_Float16* dst, const uint4 (&raw)[NV],
 
 // Writes an image tile of ROWS rows of UPR 16-byte units (the last unit of a
 // row is its zero pad) to global memory; f(row, unit) gives the 8 values.
-template <int ROWS, int UPR, typename F>
+template <int ROWS, int UPR, int NTH = 256, typename F>
 __device__ __forceinline__ void write_tile(char* dst, F&& f) {
   uint4* d = reinterpret_cast<uint4*>(dst);
-  for (int e = threadIdx.x; e < ROWS * UPR; e += 256) {
+  for (int e = threadIdx.x; e < ROWS * UPR; e += NTH) {
     const int r = e / UPR, u = e % UPR;
     d[e] = u == UPR - 1 ? uint4{0u, 0u, 0u, 0u} : __builtin_bit_cast(uint4, f(r, u));
   }
@@ -1545,7 +1545,7 @@ struct ImgCW {
 // (fp32) and Tst (fp16 [C][LDC], whose blocks above the diagonal blocks the
 // caller has zeroed): wave w inverts diagonal block w by substitution, the
 // blocks below follow one distance at a time on fp32 matrix cores.  Called by
-// all 256 threads; ends with a barrier.
+// every thread of the workgroup (4 waves or more); ends with a barrier.
 template <int C, int LDA, int LDC>
 __device__ __forceinline__ void unit_lower_inverse(const float* A, float* Tf, _Float16* Tst) {
   constexpr int NT = C / 16;
@@ -1600,28 +1600,25 @@ __device__ __forceinline__ void ld8f(float (&x)[8], const float* p) {
   x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
 }
 
-// Rows of the 16-row diagonal blocks that 16-lane group grp of a cwprep
-// workgroup sums: C = 64: block grp & 3, local rows {w, 7-w, 8+w, 15-w} of
-// wave w = grp / 4 (every group of a wave runs the same loop bounds; 34
-// pairs each); C = 32: block grp & 1, local rows {w, 15-w} or {7-w, 8+w}.
+// Rows of the 16-row diagonal blocks that 16-lane group grp (0..31) of a
+// cwprep workgroup sums: C = 64: block grp & 3, local rows {w, 15 - w} of
+// wave w = grp / 4 (17 pairs per group; all groups of a wave run the same
+// loop bounds); C = 32: block grp & 1, local row w or 15 - w.
 template <int C>
 __device__ __forceinline__ int diag_row(int grp, int j) {
   const int w = grp >> 2;
   if constexpr (C == 64) {
-    const int rl = j == 0 ? w : j == 1 ? 7 - w : j == 2 ? 8 + w : 15 - w;
-    return 16 * (grp & 3) + rl;
+    return 16 * (grp & 3) + (j == 0 ? w : 15 - w);
   } else {
-    const int sel = (grp >> 1) & 1;
-    const int rl = sel == 0 ? (j == 0 ? w : 15 - w) : (j == 0 ? 7 - w : 8 + w);
-    return 16 * (grp & 1) + rl;
+    return 16 * (grp & 1) + (((grp >> 1) & 1) == 0 ? w : 15 - w);
   }
 }
 
 template <int C>
-__global__ __launch_bounds__(256) void cwprep16_kernel(K16 a) {
+__global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
   using IM = ImgCW<C>;
-  constexpr int NT = C / 16, LDA = C + 4, LDC = IM::LDC, LDG = DK + 4;
-  constexpr int TPR = 256 / C, EPT = DK / TPR, NV = EPT / 8;
+  constexpr int NTH = 512, NT = C / 16, LDA = C + 4, LDC = IM::LDC, LDG = DK + 4;
+  constexpr int TPR = NTH / C, EPT = DK / TPR, NV = EPT / 8;
   static_assert(C == 64 || C == 32, "chunk of 32 or 64 rows");
   __shared__ __align__(16) _Float16 Ks[C * LDK];
   __shared__ __align__(16) _Float16 Qs[C * LDK];
@@ -1630,11 +1627,8 @@ __global__ __launch_bounds__(256) void cwprep16_kernel(K16 a) {
   __shared__ __align__(16) float Tf[C * LDA];
   __shared__ __align__(16) _Float16 Pst[C * LDC];
   __shared__ __align__(16) _Float16 Tst[C * LDC];
-  __shared__ __align__(16) _Float16 Lk[16 * LDK];
-  __shared__ __align__(16) _Float16 Lq[16 * LDK];
-  __shared__ __align__(16) _Float16 Rt[(C - 16) * LDK];
   __shared__ float bet[C];
-  __shared__ float half_sum[DK];
+  __shared__ float part_sum[4 * DK];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int c = blockIdx.x, hv = blockIdx.y;
@@ -1642,16 +1636,16 @@ __global__ __launch_bounds__(256) void cwprep16_kernel(K16 a) {
   const int kh = hv / (a.Hv / a.Hk);
   const int64_t t0 = static_cast<int64_t>(c) * C;
   const int L = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
-  // gates: thread -> channel tid % DK, rows of half tid / DK, running sum in
-  // registers (g = 0 past the end)
-  constexpr int RH = C / 2;
-  const int gi = tid & (DK - 1), gh = tid >> 7;
-  float gr[RH];
+  // gates: thread -> channel tid % DK, rows of quarter tid / DK, running sum
+  // in registers (g = 0 past the end)
+  constexpr int RQ = C / 4;
+  const int gi = tid & (DK - 1), gq = tid >> 7;
+  float gr[RQ];
   {
-    const float* gp = a.g + ((b * a.T + t0 + gh * RH) * a.Hv + hv) * DK + gi;
+    const float* gp = a.g + ((b * a.T + t0 + gq * RQ) * a.Hv + hv) * DK + gi;
     const int64_t rs = static_cast<int64_t>(a.Hv) * DK;
 #pragma unroll
-    for (int j = 0; j < RH; ++j) gr[j] = gh * RH + j < L ? gp[j * rs] : 0.f;
+    for (int j = 0; j < RQ; ++j) gr[j] = gq * RQ + j < L ? gp[j * rs] : 0.f;
   }
   {  // q / k rows (normalised, fp16) and beta
     const int r = tid / TPR, part = tid % TPR;
@@ -1663,8 +1657,8 @@ __global__ __launch_bounds__(256) void cwprep16_kernel(K16 a) {
       kr[u] = sel4(r < L, *reinterpret_cast<const uint4*>(a.k + off + 8 * u));
       qr[u] = sel4(r < L, *reinterpret_cast<const uint4*>(a.q + off + 8 * u));
     }
-    norm_rows<C, NV>(Ks, kr, a.l2);
-    norm_rows<C, NV>(Qs, qr, a.l2);
+    norm_rows<C, NV, NTH>(Ks, kr, a.l2);
+    norm_rows<C, NV, NTH>(Qs, qr, a.l2);
     if (tid < C) {
       float bv = 0.f;
       if (tid < L) {
@@ -1673,34 +1667,68 @@ __global__ __launch_bounds__(256) void cwprep16_kernel(K16 a) {
       }
       bet[tid] = bv;
     }
-    for (int e = tid; e < C * LDC / 8; e += 256) reinterpret_cast<uint4*>(Pst)[e] = uint4{0u, 0u, 0u, 0u};
-    for (int e = tid; e < C * LDC / 8; e += 256) reinterpret_cast<uint4*>(Tst)[e] = uint4{0u, 0u, 0u, 0u};
+    for (int e = tid; e < C * LDC / 8; e += NTH) reinterpret_cast<uint4*>(Pst)[e] = uint4{0u, 0u, 0u, 0u};
+    for (int e = tid; e < C * LDC / 8; e += NTH) reinterpret_cast<uint4*>(Tst)[e] = uint4{0u, 0u, 0u, 0u};
   }
-  float run = 0.f;
+  float run = 0.f, tv = 0.f;
 #pragma unroll
-  for (int j = 0; j < RH; ++j) {
-    run += a.fg && gh * RH + j < L ? fg_log_alpha(gr[j]) : gr[j];
+  for (int j = 0; j < RQ; ++j) {
+    const float gj = a.fg && gq * RQ + j < L ? fg_log_alpha(gr[j]) : gr[j];
+    run += gj;
+    tv += fabsf(gj);
     gr[j] = run;
   }
-  if (gh == 0) {
-    half_sum[gi] = run;
+  part_sum[gq * DK + gi] = run;
+  // the factored diagonal blocks need every factor e^{+-(G_r - G_o)} of a
+  // block inside the fp32 range: a total |g| over a block of at most
+  // kSpan (log2 units) bounds them by 2^kSpan; else the exact sums
+  constexpr float kSpan = 96.f;
+  const bool exact = __syncthreads_or(tv * kLog2e > kSpan * RQ / 16);
+  {
+    float base = 0.f;
+    for (int q2 = 0; q2 < gq; ++q2) base += part_sum[q2 * DK + gi];
 #pragma unroll
-    for (int j = 0; j < RH; ++j) G2[j * LDG + gi] = gr[j] * kLog2e;
-  }
-  __syncthreads();
-  if (gh == 1) {
-    const float base = half_sum[gi];
-#pragma unroll
-    for (int j = 0; j < RH; ++j) G2[(RH + j) * LDG + gi] = (gr[j] + base) * kLog2e;
+    for (int j = 0; j < RQ; ++j) G2[(gq * RQ + j) * LDG + gi] = (gr[j] + base) * kLog2e;
   }
   __syncthreads();
 
-  // diagonal blocks, exactly in fp32: a 16-lane group per row set, eight
-  // channels per lane, one exponential per pair and channel, DPP row sums
-  {
+  // ---- A (fp32) and P (fp16) on and below the 16 x 16 diagonal blocks.
+  // Diagonal block o (rows o .. o+15), factored about its first row:
+  //   e^{G_r - G_s} = e^{G_r - G_o} e^{G_o - G_s},
+  // on fp32 matrix cores, wave w taking block w % 4 and channel half w / 4
+  // (the lane's 16 channels are a relabelling of the contraction index,
+  // the same for both operands).
+  f32x4 dkk = zero4(), dqk = zero4();
+  if (!exact) {
+    if ((w & 3) < NT) {
+      const int o = 16 * (w & 3), h = w >> 2, row = o + c16;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i0 = 32 * g + 16 * h + 8 * u;
+        float gx[8], go[8];
+        ld8f(gx, G2 + row * LDG + i0);
+        ld8f(go, G2 + o * LDG + i0);
+        const f16x8 kv = ld8(Ks + row * LDK + i0), qv = ld8(Qs + row * LDK + i0);
+#pragma unroll
+        for (int q2 = 0; q2 < 8; ++q2) {
+          const float x = gx[q2] - go[q2];
+          const float fa = __builtin_amdgcn_exp2f(x), fb = __builtin_amdgcn_exp2f(-x);
+          const float kf = static_cast<float>(kv[q2]);
+          dkk = F32Op::mma(kf * fa, kf * fb, dkk);
+          dqk = F32Op::mma(static_cast<float>(qv[q2]) * fa, kf * fb, dqk);
+        }
+      }
+      if (h == 1) {  // the second channel half hands its sums to the first
+        float4* part = reinterpret_cast<float4*>(Tf + ((w & 3) * 64 + lane) * 8);
+        part[0] = make_float4(dkk[0], dkk[1], dkk[2], dkk[3]);
+        part[1] = make_float4(dqk[0], dqk[1], dqk[2], dqk[3]);
+      }
+    }
+  } else {  // exact: a 16-lane group per row, eight channels per lane, one
+            // exponential per pair and channel, four pairs in flight, DPP row sums
     const int grp = tid >> 4, i0 = 8 * c16;
 #pragma unroll 1
-    for (int j = 0; j < NT; ++j) {
+    for (int j = 0; j < C / 32; ++j) {
       const int rr = diag_row<C>(grp, j), s0 = rr & ~15;
       float gr8[8], kr8[8], qr8[8];
       ld8f(gr8, G2 + rr * LDG + i0);
@@ -1712,79 +1740,103 @@ __global__ __launch_bounds__(256) void cwprep16_kernel(K16 a) {
           qr8[q2] = static_cast<float>(qv[q2]);
         }
       }
-      for (int ss = s0; ss <= rr; ++ss) {
-        float gs8[8];
-        ld8f(gs8, G2 + ss * LDG + i0);
-        const f16x8 ks = ld8(Ks + ss * LDK + i0);
-        float kk = 0.f, qk = 0.f;
+#pragma unroll 1
+      for (int sb = s0; sb <= rr; sb += 4) {
+        float kk[4], qk[4];
 #pragma unroll
-        for (int q2 = 0; q2 < 8; ++q2) {
-          const float x = static_cast<float>(ks[q2]) * __builtin_amdgcn_exp2f(gr8[q2] - gs8[q2]);
-          kk += kr8[q2] * x;
-          qk += qr8[q2] * x;
+        for (int u = 0; u < 4; ++u) {
+          const int ss = sb + u <= rr ? sb + u : rr;
+          float gs8[8];
+          ld8f(gs8, G2 + ss * LDG + i0);
+          const f16x8 ks = ld8(Ks + ss * LDK + i0);
+          kk[u] = qk[u] = 0.f;
+#pragma unroll
+          for (int q2 = 0; q2 < 8; ++q2) {
+            const float x = static_cast<float>(ks[q2]) * __builtin_amdgcn_exp2f(gr8[q2] - gs8[q2]);
+            kk[u] += kr8[q2] * x;
+            qk[u] += qr8[q2] * x;
+          }
         }
-        kk = row16_sum(kk);
-        qk = row16_sum(qk);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          kk[u] = row16_sum(kk[u]);
+          qk[u] = row16_sum(qk[u]);
+        }
         if (c16 == 0) {
-          A[rr * LDA + ss] = ss < rr ? bet[rr] * kk : 0.f;
-          Pst[rr * LDC + ss] = static_cast<_Float16>(qk);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int ss = sb + u;
+            if (ss <= rr) {
+              A[rr * LDA + ss] = ss < rr ? bet[rr] * kk[u] : 0.f;
+              Pst[rr * LDC + ss] = static_cast<_Float16>(qk[u]);
+            }
+          }
         }
       }
     }
   }
-  // blocks below the diagonal, one row block R at a time, on the matrix cores
-  for (int R = 1; R < NT; ++R) {
-    const int bref = 16 * R;
-    for (int e = tid; e < (16 + bref) * (DK / 8); e += 256) {
-      const int row = e / (DK / 8), i0 = 8 * (e % (DK / 8));
-      float gb[8], gx[8];
+  // Tiles (R, S), S < R, below the diagonal blocks, about the first row
+  // b = 16R of row block R (both factors <= 1 for g <= 0):
+  //   (k_r e^{G_r - G_b}) . (k_s e^{G_b - G_s}), fp16 matrix cores, one tile
+  // (both products) per wave, operands built in registers.
+  for (int t = w; t < NT * (NT - 1) / 2; t += 8) {
+    int R = 1;
+    while (R * (R + 1) / 2 <= t) ++R;
+    const int S = t - R * (R - 1) / 2, bref = 16 * R, r = bref + c16, sr = 16 * S + c16;
+    f32x4 kk = zero4(), qk = zero4();
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      const int i0 = 32 * ks + 8 * g;
+      float gb[8], gx[8], gs[8];
       ld8f(gb, G2 + bref * LDG + i0);
-      if (row < 16) {  // row block R of k and q, scaled by e^{G_r - G_b} <= 1
-        ld8f(gx, G2 + (bref + row) * LDG + i0);
-        const f16x8 kv = ld8(Ks + (bref + row) * LDK + i0), qv = ld8(Qs + (bref + row) * LDK + i0);
-        f16x8 ko, qo;
+      ld8f(gx, G2 + r * LDG + i0);
+      ld8f(gs, G2 + sr * LDG + i0);
+      const f16x8 kv = ld8(Ks + r * LDK + i0), qv = ld8(Qs + r * LDK + i0), sv = ld8(Ks + sr * LDK + i0);
+      f16x8 ak, aq, bs;
 #pragma unroll
-        for (int q2 = 0; q2 < 8; ++q2) {
-          const float f = __builtin_amdgcn_exp2f(gx[q2] - gb[q2]);
-          ko[q2] = static_cast<_Float16>(static_cast<float>(kv[q2]) * f);
-          qo[q2] = static_cast<_Float16>(static_cast<float>(qv[q2]) * f);
-        }
-        *reinterpret_cast<f16x8*>(Lk + row * LDK + i0) = ko;
-        *reinterpret_cast<f16x8*>(Lq + row * LDK + i0) = qo;
-      } else {  // rows s < b of k, scaled by e^{G_b - G_s} <= 1
-        const int s2 = row - 16;
-        ld8f(gx, G2 + s2 * LDG + i0);
-        const f16x8 kv = ld8(Ks + s2 * LDK + i0);
-        f16x8 ko;
-#pragma unroll
-        for (int q2 = 0; q2 < 8; ++q2)
-          ko[q2] = static_cast<_Float16>(static_cast<float>(kv[q2]) * __builtin_amdgcn_exp2f(gb[q2] - gx[q2]));
-        *reinterpret_cast<f16x8*>(Rt + s2 * LDK + i0) = ko;
+      for (int q2 = 0; q2 < 8; ++q2) {
+        const float fr = __builtin_amdgcn_exp2f(gx[q2] - gb[q2]);
+        const float fs = __builtin_amdgcn_exp2f(gb[q2] - gs[q2]);
+        ak[q2] = static_cast<_Float16>(static_cast<float>(kv[q2]) * fr);
+        aq[q2] = static_cast<_Float16>(static_cast<float>(qv[q2]) * fr);
+        bs[q2] = static_cast<_Float16>(static_cast<float>(sv[q2]) * fs);
       }
+      kk = F16Op::mma(ak, bs, kk);
+      qk = F16Op::mma(aq, bs, qk);
     }
-    __syncthreads();
-    if (w < R) {  // tile (R, S = w)
-      const f32x4 kk = mma_tile<F16Op, false, false>(zero4(), Lk, LDK, 0, Rt, LDK, 16 * w, DK);
-      const f32x4 qk = mma_tile<F16Op, false, false>(zero4(), Lq, LDK, 0, Rt, LDK, 16 * w, DK);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rr = bref + 4 * g + e, ss = 16 * w + c16;
-        A[rr * LDA + ss] = bet[rr] * kk[e];
-        Pst[rr * LDC + ss] = static_cast<_Float16>(qk[e]);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int rr = bref + 4 * g + e, ss = 16 * S + c16;
+      A[rr * LDA + ss] = bet[rr] * kk[e];
+      Pst[rr * LDC + ss] = static_cast<_Float16>(qk[e]);
     }
-    __syncthreads();
   }
+  __syncthreads();
+  if (!exact && w < 4 && w < NT) {  // diagonal blocks: both halves, lower triangle
+    const float4* part = reinterpret_cast<const float4*>(Tf + (w * 64 + lane) * 8);
+    const float4 pk = part[0], pq = part[1];
+    dkk[0] += pk.x; dkk[1] += pk.y; dkk[2] += pk.z; dkk[3] += pk.w;
+    dqk[0] += pq.x; dqk[1] += pq.y; dqk[2] += pq.z; dqk[3] += pq.w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rr = 16 * w + 4 * g + e, ss = 16 * w + c16;
+      if (ss <= rr) {
+        A[rr * LDA + ss] = ss < rr ? bet[rr] * dkk[e] : 0.f;
+        Pst[rr * LDC + ss] = static_cast<_Float16>(dqk[e]);
+      }
+    }
+  }
+  __syncthreads();
   unit_lower_inverse<C, LDA, LDC>(A, Tf, Tst);
 
   // ---- images of this (b, v-head, chunk)
   char* cim = a.cimg + ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(IM::CHK);
   float* cg = reinterpret_cast<float*>(cim);
-  for (int e = tid; e < C + DK; e += 256)
+  for (int e = tid; e < C + DK; e += NTH)
     cg[e] = e < C ? bet[e] : __builtin_amdgcn_exp2f(G2[(C - 1) * LDG + e - C]);
   constexpr int UC = LDC / 8;
-  write_tile<C, UC>(cim + IM::GT, [&](int r, int u) { return ld8(Tst + r * LDC + 8 * u); });
-  write_tile<C, UC>(cim + IM::GT + IM::TM, [&](int r, int u) { return ld8(Pst + r * LDC + 8 * u); });
+  write_tile<C, UC, NTH>(cim + IM::GT, [&](int r, int u) { return ld8(Tst + r * LDC + 8 * u); });
+  write_tile<C, UC, NTH>(cim + IM::GT + IM::TM, [&](int r, int u) { return ld8(Pst + r * LDC + 8 * u); });
   char* kim = a.kimg + ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(IM::KEY);
   constexpr int UK = LDK / 8;
   // row r, unit u of X o e^G (to_end false) or X o e^{G_C - G} (to_end true)
@@ -1804,9 +1856,9 @@ __global__ __launch_bounds__(256) void cwprep16_kernel(K16 a) {
       v[q2] = static_cast<_Float16>(static_cast<float>(xv[q2]) * __builtin_amdgcn_exp2f(gx[q2]));
     return v;
   };
-  write_tile<C, UK>(kim, [&](int r, int u) { return scaled(Ks, r, u, false); });
-  write_tile<C, UK>(kim + IM::KN, [&](int r, int u) { return scaled(Qs, r, u, false); });
-  write_tile<C, UK>(kim + 2 * IM::KN, [&](int r, int u) { return scaled(Ks, r, u, true); });
+  write_tile<C, UK, NTH>(kim, [&](int r, int u) { return scaled(Ks, r, u, false); });
+  write_tile<C, UK, NTH>(kim + IM::KN, [&](int r, int u) { return scaled(Qs, r, u, false); });
+  write_tile<C, UK, NTH>(kim + 2 * IM::KN, [&](int r, int u) { return scaled(Ks, r, u, true); });
 }
 
 // Channelwise forward chain: as chain16 with outputs, using the scaled key
@@ -2092,7 +2144,7 @@ hipError_t fwd_cw(const Shape& s, const ChunkFwdArgs& x, void* ws, hipStream_t s
   a.ht = x.ht;
   {
     ProfScope ps("chunk_prep_cw", st);
-    hipLaunchKernelGGL((cwprep16_kernel<C>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((cwprep16_kernel<C>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(512), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -134,3 +134,25 @@ def test_channelwise_chunked_prefill(T):
     x = make_inputs(1600 + T, 1, T, 16, 32, 128, 128, io_dtype="bf16", channelwise=True,
                     with_do=False)
     check_fwd(x, "bf16", cw=True, h0=False, heads=[(0, 0), (0, 11)], algo=("chunked", 64))
+
+
+@pytest.mark.parametrize("scale,C", [(4.0, 64), (4.0, 32), (30.0, 64), (30.0, 32)])
+def test_channelwise_chunked_strong_decay(scale, C):
+    """Per-channel gates g = -scale * U(0.9, 1.0): at scale 4 a 16-row block
+    decays by up to e^-64 per channel (diagonal blocks still factored, the
+    factors near 2^92); at scale 30 the diagonal blocks take the exact
+    per-pair sums."""
+    x = make_inputs(1700 + int(scale) + C, 2, 150, 2, 4, 128, 128, io_dtype="bf16",
+                    channelwise=True, h0_std=0.02, with_do=False)
+    u = np.random.default_rng(C).uniform(0.9, 1.0, x["g"].shape)
+    x["g"] = (-scale * u).astype(np.float32)
+    check_fwd(x, "bf16", cw=True, algo=("chunked", C))
+
+
+def test_channelwise_chunked_mixed_decay():
+    """Strong decay (g = -30) on a few channels of the second chunk only:
+    that chunk takes the exact diagonal sums, the others the factored ones."""
+    x = make_inputs(1750, 2, 200, 2, 4, 128, 128, io_dtype="bf16", channelwise=True,
+                    h0_std=0.02, with_do=False)
+    x["g"][:, 64:128, :, 5:9] = -30.0
+    check_fwd(x, "bf16", cw=True, algo=("chunked", 64))
