@@ -30,24 +30,29 @@ B, T, HK, HV, D, C = 4, 4096, 16, 32, 128, 64
 DEC_B, DEC_STEPS, DEC_BUFFERS = 8, 256, 32
 
 
-def kernel_flops_per_token_head(name, d=D, c=C):
+def kernel_flops_per_token_head(name, d=D, c=C, saved=True):
     """Algorithmic FLOPs each kernel does in one step, per (token, v-head),
     summed over its launches in the step: every matrix product counted once
     at 2mnk, products whose result is used only on one triangle of a C x C
-    block counted at half.  chunk_prep runs twice per step."""
+    block counted at half.  chunk_prep runs once per step when the forward
+    saves its chunks for the VJP (saved), else twice."""
     return {
-        "chunk_prep": 2 * (c * d + c * c / 3),
+        "chunk_prep": (1 if saved else 2) * (c * d + c * c / 3),
         "chunk_fwd": 6 * d * d + 3 * c * d,
+        "chunk_fwd_save": 6 * d * d + 3 * c * d,
         "chunk_states": 4 * d * d + c * d,
         "chunk_dh": 6 * d * d + 3 * c * d,
         "chunk_grad": 10 * d * d + 12 * c * d + 2 * c * c / 3,
     }.get(name)
 
 
-def canonical_flops_per_token_head(d=D, c=C):
+def canonical_flops_per_token_head(d=D, c=C, saved=True):
     """Minimal fwd + bwd count: fwd 6d^2 + 5Cd + C^2/3, bwd (with one
-    recompute of the chunk states) 16d^2 + 14Cd + C^2."""
-    return (6 * d * d + 5 * c * d + c * c / 3) + (16 * d * d + 14 * c * d + c * c)
+    recompute of the chunk states) 16d^2 + 14Cd + C^2; when the forward saves
+    its chunk states and operands for the VJP (saved) the recompute, one state
+    pass 4d^2 + Cd and one prep Cd + C^2/3, is not part of the step."""
+    full = (6 * d * d + 5 * c * d + c * c / 3) + (16 * d * d + 14 * c * d + c * c)
+    return full - (4 * d * d + c * d + c * d + c * c / 3) if saved else full
 
 
 def image_bytes(d=D, c=C):
@@ -59,12 +64,14 @@ def image_bytes(d=D, c=C):
     return {"KEY": 2 * kn, "CHK": gt + 2 * tm, "KN": kn, "TM": tm, "GT": gt}
 
 
-def kernel_bytes_per_token_head(name, d=D, c=C, grp=HV // HK):
+def kernel_bytes_per_token_head(name, d=D, c=C, grp=HV // HK, saved=True):
     """Algorithmic HBM bytes each kernel moves in one step, per (token,
     v-head), summed over its launches: what it must read and write once, with
     k/q rows and key images shared by the `grp` v-heads of a k-head (bf16 io
     and outputs, fp16 images and chunk states, fp32 gates).  chunk_prep runs
-    once for the forward and once for the VJP; chunk_grad runs once per
+    once for the forward and, unless the forward saved its chunks for the
+    VJP (saved; then chunk_fwd_save also stores every chunk's entry state),
+    once more for the VJP; chunk_grad runs once per
     v-head of a group, carrying an fp32 running sum of dq_hat / dk_hat per
     k-head between launches (written grp - 1 times, read grp - 1 times), the
     last launch reading the raw q / k rows and writing dq, dk."""
@@ -75,8 +82,9 @@ def kernel_bytes_per_token_head(name, d=D, c=C, grp=HV // HK):
     st = 2 * d * d / c       # one fp16 d x d state per chunk
     prep = kq + gates + im["KEY"] / (c * grp) + im["CHK"] / c
     return {
-        "chunk_prep": 2 * prep,
+        "chunk_prep": (1 if saved else 2) * prep,
         "chunk_fwd": im["KEY"] / (c * grp) + im["CHK"] / c + 2 * vec,
+        "chunk_fwd_save": im["KEY"] / (c * grp) + im["CHK"] / c + 2 * vec + st,
         "chunk_states": im["KN"] / (c * grp) + (im["GT"] + im["TM"]) / c + vec + st,
         "chunk_dh": im["KEY"] / (c * grp) + im["CHK"] / c + 2 * vec + st,
         "chunk_grad": (im["KEY"] + im["CHK"]) / c + 2 * st + 2 * vec + gates
@@ -114,16 +122,23 @@ def make_device_inputs(torch, seed, b, t, with_do=True, gate_preact=False):
     return x, out
 
 
-def bench_chunked(torch, gdr, steps, warmup, fused_gates=False):
-    """One step = chunked forward + VJP of the whole workload.  With
-    fused_gates the gates are passed as pre-activations (same draws) and
-    activated inside the kernels."""
+def bench_chunked(torch, gdr, steps, warmup, fused_gates=False, saved=True):
+    """One step = chunked forward + VJP of the whole workload.  With saved
+    the forward keeps its chunk images and chunk entry states for the VJP
+    (GDR_SAVE_CHUNKS), else the VJP recomputes them.  With fused_gates the
+    gates are passed as pre-activations (same draws) and activated inside
+    the kernels."""
     _, t = make_device_inputs(torch, 2, B, T, gate_preact=fused_gates)
     kw = dict(algo="chunked", chunk_size=C, out_dtype=torch.bfloat16, fused_gates=fused_gates)
 
     def step():
-        gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], None, **kw)
-        gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], None, t["do"], **kw)
+        if saved:
+            _, _, sv = gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], None,
+                                       save_for_backward=True, **kw)
+            gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], None, t["do"], saved=sv, **kw)
+        else:
+            gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], None, **kw)
+            gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], None, t["do"], **kw)
 
     for _ in range(warmup):
         step()
@@ -364,6 +379,7 @@ def main():
         "config": {"workload": "chunked gated delta rule forward + VJP", "B": B, "T": T, "Hk": HK, "Hv": HV,
                    "Dk": D, "Dv": D, "chunk": C, "io": "bf16", "matrix_core_operands": "f16",
                    "accumulate_and_state": "f32", "use_qk_l2norm": True, "gate": "scalar",
+                   "vjp_inputs": "forward saves chunk images and chunk states (GDR_SAVE_CHUNKS)",
                    "parallelism": "single GPU"},
         "roofline": roof,
         "path": {"canonical_TFLOPs": round(canon / (ms * 1e-3) / 1e12, 2),
@@ -372,8 +388,14 @@ def main():
         "kernels": per_kernel,
     }
     fms, _, _ = bench_chunked(torch, gdr, args.steps, args.warmup, fused_gates=True)
-    line["variants"] = {"fused_gates": {"ms_per_step": round(fms, 4), "tokens_per_s": round(tokens / (fms * 1e-3), 1),
-                                        "note": "same step with g, beta passed as pre-activations"}}
+    sms, _, skern = bench_chunked(torch, gdr, args.steps, args.warmup, saved=False)
+    line["variants"] = {
+        "fused_gates": {"ms_per_step": round(fms, 4), "tokens_per_s": round(tokens / (fms * 1e-3), 1),
+                        "note": "same step with g, beta passed as pre-activations"},
+        "stateless_vjp": {"ms_per_step": round(sms, 4), "tokens_per_s": round(tokens / (sms * 1e-3), 1),
+                          "kernels_avg_us": {k: round(1000 * v[0] / v[1], 2) for k, v in skern.items()},
+                          "note": "same step without GDR_SAVE_CHUNKS: the VJP recomputes the chunk "
+                                  "images and chunk states"}}
     line["variants"]["channelwise_prefill"] = bench_channelwise(torch, gdr)
     if not args.no_decode:
         line["decode"] = bench_decode(torch, gdr)

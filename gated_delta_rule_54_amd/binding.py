@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libgdr.so")
 GDR_OK = 0
 GDR_F32, GDR_BF16 = 0, 1
 GDR_ALGO_AUTO, GDR_ALGO_SEQUENTIAL, GDR_ALGO_CHUNKED = 0, 1, 2
-GDR_USE_QK_L2NORM, GDR_CHANNELWISE, GDR_FUSED_GATES = 1, 2, 4
+GDR_USE_QK_L2NORM, GDR_CHANNELWISE, GDR_FUSED_GATES, GDR_SAVE_CHUNKS = 1, 2, 4, 8
 ALGOS = {"auto": GDR_ALGO_AUTO, "sequential": GDR_ALGO_SEQUENTIAL,
          "chunked": GDR_ALGO_CHUNKED}
 
@@ -93,9 +93,9 @@ def _dt(t):
 
 
 def make_problem(B, T, Hk, Hv, Dk, Dv, io_dtype, out_dtype, use_qk_l2norm=True,
-                 channelwise=False, algo="auto", chunk_size=0, fused_gates=False):
+                 channelwise=False, algo="auto", chunk_size=0, fused_gates=False, save_chunks=False):
     flags = ((GDR_USE_QK_L2NORM if use_qk_l2norm else 0) | (GDR_CHANNELWISE if channelwise else 0)
-             | (GDR_FUSED_GATES if fused_gates else 0))
+             | (GDR_FUSED_GATES if fused_gates else 0) | (GDR_SAVE_CHUNKS if save_chunks else 0))
     return GdrProblem(B, T, Hk, Hv, Dk, Dv, _dt(io_dtype), _dt(out_dtype), flags,
                       ALGOS[algo], chunk_size)
 
@@ -158,12 +158,28 @@ def _workspace(nbytes, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
+class SavedChunks:
+    """The workspace a ``gdr_forward(..., save_for_backward=True)`` call left
+    its chunk images and chunk entry states in (GDR_SAVE_CHUNKS), for the
+    ``gdr_backward`` of the same problem and inputs."""
+
+    def __init__(self, ws, key):
+        self.ws, self.key = ws, key
+
+
+def _save_key(prob):
+    return (prob.B, prob.T, prob.Hk, prob.Hv, prob.Dk, prob.Dv, prob.io_dtype,
+            prob.flags & ~GDR_SAVE_CHUNKS, prob.algo, prob.chunk_size)
+
+
 def gdr_forward(q, k, v, g, beta, h0=None, *, use_qk_l2norm=True, channelwise=False,
                 algo="auto", chunk_size=0, out_dtype=torch.float32, ht=True,
-                stream=None, fused_gates=False):
-    """Returns (o, ht).  ``ht`` may be True (allocate), None (not wanted) or a
-    tensor to write the final state into (it may be ``h0`` itself).  With
-    ``fused_gates`` g and beta are pre-activations (GDR_FUSED_GATES)."""
+                stream=None, fused_gates=False, save_for_backward=False):
+    """Returns (o, ht), or (o, ht, saved) with ``save_for_backward`` (pass
+    ``saved`` to ``gdr_backward``).  ``ht`` may be True (allocate), None (not
+    wanted) or a tensor to write the final state into (it may be ``h0``
+    itself).  With ``fused_gates`` g and beta are pre-activations
+    (GDR_FUSED_GATES)."""
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -171,7 +187,7 @@ def gdr_forward(q, k, v, g, beta, h0=None, *, use_qk_l2norm=True, channelwise=Fa
     for t, n in ((g, "g"), (beta, "beta"), (h0, "h0")):
         _check(t, n, torch.float32)
     prob = make_problem(B, T, Hk, Hv, Dk, Dv, q.dtype, out_dtype, use_qk_l2norm,
-                        channelwise, algo, chunk_size, fused_gates)
+                        channelwise, algo, chunk_size, fused_gates, save_for_backward)
     o = torch.empty((B, T, Hv, Dv), dtype=out_dtype, device=q.device)
     if ht is True:
         ht = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=q.device)
@@ -182,15 +198,19 @@ def gdr_forward(q, k, v, g, beta, h0=None, *, use_qk_l2norm=True, channelwise=Fa
                            0 if ws is None else ws.numel(), _stream(stream))
     if st != GDR_OK:
         raise GdrError(st, "gdr_forward")
+    if save_for_backward:
+        return o, ht, SavedChunks(ws, _save_key(prob))
     return o, ht
 
 
 def gdr_backward(q, k, v, g, beta, h0, dout, dht=None, *, use_qk_l2norm=True,
                  channelwise=False, algo="auto", chunk_size=0,
-                 out_dtype=torch.float32, want_dh0=True, stream=None, fused_gates=False):
+                 out_dtype=torch.float32, want_dh0=True, stream=None, fused_gates=False,
+                 saved=None):
     """Returns (dq, dk, dv, dg, dbeta, dh0); dh0 is None if not wanted.  With
     ``fused_gates`` g and beta are pre-activations and dg, dbeta are the
-    gradients with respect to them."""
+    gradients with respect to them.  ``saved`` is what the forward of the
+    same problem and inputs returned with ``save_for_backward``."""
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
@@ -198,7 +218,9 @@ def gdr_backward(q, k, v, g, beta, h0, dout, dht=None, *, use_qk_l2norm=True,
     for t, n in ((g, "g"), (beta, "beta"), (h0, "h0"), (dht, "dht")):
         _check(t, n, torch.float32)
     prob = make_problem(B, T, Hk, Hv, Dk, Dv, q.dtype, out_dtype, use_qk_l2norm,
-                        channelwise, algo, chunk_size, fused_gates)
+                        channelwise, algo, chunk_size, fused_gates, saved is not None)
+    if saved is not None and saved.key != _save_key(prob):
+        raise ValueError("saved chunks belong to a different problem")
     dev = q.device
     dq = torch.empty((B, T, Hk, Dk), dtype=out_dtype, device=dev)
     dk = torch.empty((B, T, Hk, Dk), dtype=out_dtype, device=dev)
@@ -206,7 +228,11 @@ def gdr_backward(q, k, v, g, beta, h0, dout, dht=None, *, use_qk_l2norm=True,
     dg = torch.empty(g.shape, dtype=torch.float32, device=dev)
     dbeta = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
     dh0 = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=dev) if want_dh0 else None
-    ws = _workspace(gdr_backward_workspace(prob), dev)
+    nws = gdr_backward_workspace(prob)
+    if saved is not None and saved.ws is not None and saved.ws.numel() >= nws:
+        ws = saved.ws  # the forward's images and chunk states
+    else:
+        ws = _workspace(nws, dev)
     st = lib().gdr_backward(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                             _ptr(beta), _ptr(h0), _ptr(dout), _ptr(dht), _ptr(dq),
                             _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0),

@@ -33,7 +33,7 @@ gdr_status check_problem(const gdr_problem* p) {
   if ((p->io_dtype != GDR_F32 && p->io_dtype != GDR_BF16) ||
       (p->out_dtype != GDR_F32 && p->out_dtype != GDR_BF16))
     return GDR_ERR_UNSUPPORTED;
-  if (p->flags & ~static_cast<uint32_t>(GDR_USE_QK_L2NORM | GDR_CHANNELWISE | GDR_FUSED_GATES))
+  if (p->flags & ~static_cast<uint32_t>(GDR_USE_QK_L2NORM | GDR_CHANNELWISE | GDR_FUSED_GATES | GDR_SAVE_CHUNKS))
     return GDR_ERR_UNSUPPORTED;
   if (p->algo < GDR_ALGO_AUTO || p->algo > GDR_ALGO_CHUNKED) return GDR_ERR_UNSUPPORTED;
   if (p->chunk_size != 0 && p->chunk_size != 16 && p->chunk_size != 32 && p->chunk_size != 64)
@@ -56,6 +56,7 @@ Shape shape_of(const gdr_problem* p) {
   s.l2norm = (p->flags & GDR_USE_QK_L2NORM) != 0;
   s.channelwise = (p->flags & GDR_CHANNELWISE) != 0;
   s.fused_gates = (p->flags & GDR_FUSED_GATES) != 0;
+  s.save_chunks = (p->flags & GDR_SAVE_CHUNKS) != 0 && !s.channelwise;
   return s;
 }
 

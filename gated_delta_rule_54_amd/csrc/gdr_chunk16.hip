@@ -2045,7 +2045,7 @@ hipError_t prep16(const K16& a, hipStream_t st) {
 
 template <int C, typename TO, bool WO, bool SH>
 hipError_t chain16(const K16& a, hipStream_t st) {
-  ProfScope ps(WO ? "chunk_fwd" : "chunk_states", st);
+  ProfScope ps(WO ? (SH ? "chunk_fwd_save" : "chunk_fwd") : "chunk_states", st);
   hipLaunchKernelGGL((chain16_kernel<C, TO, WO, SH>), dim3(static_cast<unsigned>(2 * a.Hv * a.B)), dim3(64 * (NCW + 1)),
                      0, st, a);
   return hipGetLastError();
@@ -2081,7 +2081,7 @@ hipError_t grad16(K16 a, hipStream_t st) {
 
 template <int C, typename TO>
 hipError_t fwd_all(const Shape& s, const ChunkFwdArgs& x, void* ws, hipStream_t st) {
-  K16 a = args16(s, C, ws, plan16<C>(s, false));
+  K16 a = args16(s, C, ws, plan16<C>(s, s.save_chunks));
   a.q = static_cast<const bf16_t*>(x.q);
   a.k = static_cast<const bf16_t*>(x.k);
   a.v = static_cast<const bf16_t*>(x.v);
@@ -2091,7 +2091,8 @@ hipError_t fwd_all(const Shape& s, const ChunkFwdArgs& x, void* ws, hipStream_t 
   a.o = x.o;
   a.ht = x.ht;
   hipError_t e = prep16<C>(a, st);
-  return e == hipSuccess ? chain16<C, TO, true, false>(a, st) : e;
+  if (e != hipSuccess) return e;
+  return s.save_chunks ? chain16<C, TO, true, true>(a, st) : chain16<C, TO, true, false>(a, st);
 }
 
 template <int C, typename TO>
@@ -2111,8 +2112,11 @@ hipError_t bwd_all(const Shape& s, const ChunkBwdArgs& x, void* ws, hipStream_t 
   a.dbeta = x.dbeta;
   a.dq = x.dq;
   a.dk = x.dk;
-  hipError_t e = prep16<C>(a, st);
-  if (e == hipSuccess) e = chain16<C, TO, false, true>(a, st);
+  hipError_t e = hipSuccess;
+  if (!s.save_chunks) {  // else the forward left the images and chunk states in ws
+    e = prep16<C>(a, st);
+    if (e == hipSuccess) e = chain16<C, TO, false, true>(a, st);
+  }
   if (e == hipSuccess) e = dh16<C, TO>(a, st);
   if (e == hipSuccess) e = grad16<C, TO>(a, st);
   return e;
@@ -2158,7 +2162,7 @@ hipError_t fwd_cw(const Shape& s, const ChunkFwdArgs& x, void* ws, hipStream_t s
 
 size_t chunk16_fwd_workspace(const Shape& s, int C) {
   if (s.channelwise) return C == 64 ? plan_cw<64>(s).total : plan_cw<32>(s).total;
-  return plan_any(s, C, false).total;
+  return plan_any(s, C, s.save_chunks).total;
 }
 size_t chunk16_bwd_workspace(const Shape& s, int C) { return plan_any(s, C, true).total; }
 

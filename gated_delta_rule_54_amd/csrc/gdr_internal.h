@@ -22,6 +22,7 @@ struct Shape {
   int64_t B, T;
   int Hk, Hv, D;      // Dk == Dv == D
   bool io_bf16, out_bf16, l2norm, channelwise, fused_gates;
+  bool save_chunks;  // fp16 chunked path: forward keeps images and chunk states, backward reuses them
 };
 
 // ---- sequential (token-by-token) path ------------------------------------

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 2
+#define GDR_ABI_VERSION 3
 
 typedef enum gdr_status {
   GDR_OK = 0,
@@ -97,7 +97,18 @@ typedef enum gdr_algo {
  * of the Megatron-LM page's L2-norm fold ("What"/"Why"); the activations are
  * this library's choice (the pages name none).  Works with every algorithm
  * and with GDR_CHANNELWISE (then a has g's per-channel shape). */
-enum { GDR_USE_QK_L2NORM = 1u, GDR_CHANNELWISE = 2u, GDR_FUSED_GATES = 4u };
+/* GDR_SAVE_CHUNKS: keep the forward's per-chunk work for the VJP (what a
+ * training step's autograd saves), on the chunked algorithm with bf16 io,
+ * Dk = Dv = 128, chunk_size 32 or 64 and a scalar gate; elsewhere the flag
+ * changes nothing.  gdr_forward then needs gdr_backward_workspace(p) bytes
+ * of workspace (gdr_forward_workspace reports that size) and leaves the
+ * chunk images (normalised q/k, gates, T = (I + A)^-1, P) and every
+ * chunk's entry state there; gdr_backward with the same problem, the same
+ * inputs and that workspace, untouched in between, reads them instead of
+ * recomputing them (it skips the prep and the chunk-state pass).  The
+ * library cannot check that contract: a workspace not written by such a
+ * forward gives wrong gradients (never an out-of-bounds access). */
+enum { GDR_USE_QK_L2NORM = 1u, GDR_CHANNELWISE = 2u, GDR_FUSED_GATES = 4u, GDR_SAVE_CHUNKS = 8u };
 
 typedef struct gdr_problem {
   int64_t B, T;       /* batch, tokens                                      */
@@ -105,7 +116,8 @@ typedef struct gdr_problem {
   int32_t Dk, Dv;     /* key and value head dims                            */
   int32_t io_dtype;   /* gdr_dtype of q, k, v, dout                         */
   int32_t out_dtype;  /* gdr_dtype of o, dq, dk, dv                         */
-  uint32_t flags;     /* GDR_USE_QK_L2NORM | GDR_CHANNELWISE | GDR_FUSED_GATES */
+  uint32_t flags;     /* GDR_USE_QK_L2NORM | GDR_CHANNELWISE | GDR_FUSED_GATES
+                         | GDR_SAVE_CHUNKS                                    */
   int32_t algo;       /* gdr_algo                                           */
   int32_t chunk_size; /* CHUNKED only: 16, 32 or 64; 0 means 64             */
 } gdr_problem;

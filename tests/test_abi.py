@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     lib = B.lib()
-    assert lib.gdr_abi_version() == 2
+    assert lib.gdr_abi_version() == 3
     for s in range(7):
         assert len(lib.gdr_status_str(s)) > 0
     assert lib.gdr_status_str(99) == b"unknown gdr_status"
@@ -56,7 +56,7 @@ def bwd_ws(p):
 @pytest.mark.parametrize("kw,status", [
     (dict(Hv=3), 2), (dict(T=-1), 2), (dict(B=-2), 2), (dict(Hk=0), 2), (dict(Dk=0), 2),
     (dict(Dk=64, Dv=64), 3), (dict(Dk=16, Dv=128), 3), (dict(io_dtype=2), 3),
-    (dict(out_dtype=-1), 3), (dict(flags=8), 3), (dict(algo=3), 3), (dict(chunk_size=48), 3),
+    (dict(out_dtype=-1), 3), (dict(flags=16), 3), (dict(algo=3), 3), (dict(chunk_size=48), 3),
 ])
 def test_workspace_query_rejects_bad_problems(kw, status):
     assert fwd_ws(prob(**kw))[0] == status
@@ -139,3 +139,21 @@ def test_channelwise_chunked_forward_support():
     assert fwd_ws(prob(algo=0, **dict(cw, T=64))) == (0, 0)       # short: sequential
     assert fwd_ws(prob(algo=0, flags=3, T=256)) == (0, 0)         # fp32: sequential
     assert bwd_ws(prob(algo=0, **cw))[0] == 0                     # AUTO VJP: sequential
+
+
+def test_save_chunks_workspace():
+    """GDR_SAVE_CHUNKS: on the fp16 chunked path the forward asks for the
+    backward's workspace (it leaves images and chunk states there); where the
+    flag changes nothing the sizes are those without it."""
+    base = dict(io_dtype=1, Dk=128, Dv=128, T=256, algo=2)
+    for C in (32, 64):
+        st, nf = fwd_ws(prob(flags=1 | 8, chunk_size=C, **base))
+        st2, nb = bwd_ws(prob(flags=1 | 8, chunk_size=C, **base))
+        assert st == 0 and st2 == 0 and nf == nb
+        assert bwd_ws(prob(flags=1, chunk_size=C, **base)) == (0, nb)
+        assert fwd_ws(prob(flags=1, chunk_size=C, **base))[1] < nf
+    assert fwd_ws(prob(flags=1 | 8, **dict(base, algo=1))) == (0, 0)            # sequential
+    for f in (1, 1 | 8):                                                         # fp32 io, D = 16
+        assert fwd_ws(prob(flags=f, algo=2, T=256)) == fwd_ws(prob(flags=1, algo=2, T=256))
+    cw = dict(base, chunk_size=64)
+    assert fwd_ws(prob(flags=3 | 8, **cw)) == fwd_ws(prob(flags=3, **cw))       # channelwise

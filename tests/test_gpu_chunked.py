@@ -156,3 +156,34 @@ def test_channelwise_chunked_mixed_decay():
                     h0_std=0.02, with_do=False)
     x["g"][:, 64:128, :, 5:9] = -30.0
     check_fwd(x, "bf16", cw=True, algo=("chunked", 64))
+
+
+# ------------------------------------------------ forward saves for the VJP
+
+@pytest.mark.parametrize("T,C", [(200, 64), (97, 32), (64, 64)])
+def test_saved_chunks_match_stateless(T, C):
+    """GDR_SAVE_CHUNKS: the forward that keeps its images and chunk states
+    gives the same o / ht, and the VJP that reads them the same gradients,
+    bit for bit, as the stateless calls (GQA 2:4, h0 and dht nonzero);
+    the stateless results are checked against the oracle."""
+    import torch
+    import gated_delta_rule_54_amd as gdr
+    from tests._util import host
+    x = make_inputs(1800 + T + C, 2, T, 2, 4, 128, 128, io_dtype="bf16", h0_std=0.02)
+    dht = (0.1 * np.random.default_rng(T).standard_normal((2, 4, 128, 128))).astype(np.float32)
+    check_fwd(x, "bf16", algo=("chunked", C))
+    check_bwd(x, "bf16", dht=dht, algo=("chunked", C))
+    from tests.test_gpu_sequential import to_dev
+    from tests._util import dev
+    t = to_dev(x, "bf16")
+    kw = dict(algo="chunked", chunk_size=C)
+    o0, ht0 = gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], **kw)
+    o1, ht1, saved = gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"],
+                                     save_for_backward=True, **kw)
+    g0 = gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], t["do"], dev(dht), **kw)
+    g1 = gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], t["do"], dev(dht),
+                          saved=saved, **kw)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(o0), host(o1)) and np.array_equal(host(ht0), host(ht1))
+    for a0, a1 in zip(g0, g1):
+        assert np.array_equal(host(a0), host(a1))
