@@ -23,7 +23,8 @@ ALGOS = {"auto": GDR_ALGO_AUTO, "sequential": GDR_ALGO_SEQUENTIAL,
 
 # Every symbol include/gdr.h declares.
 SYMBOLS = ("gdr_forward_workspace", "gdr_backward_workspace", "gdr_forward",
-           "gdr_backward", "gdr_profile_enable", "gdr_profile_read",
+           "gdr_backward", "gdr_forward_varlen", "gdr_backward_varlen",
+           "gdr_profile_enable", "gdr_profile_read",
            "gdr_status_str", "gdr_last_hip_error", "gdr_abi_version")
 
 
@@ -68,8 +69,11 @@ def lib():
         L.gdr_forward.argtypes = [P, vp, vp, vp, fp, fp, fp, vp, fp, vp, sz, vp]
         L.gdr_backward.argtypes = [P, vp, vp, vp, fp, fp, fp, vp, fp,
                                    vp, vp, vp, fp, fp, fp, vp, sz, vp]
+        L.gdr_forward_varlen.argtypes = [P, vp, vp, vp, vp, fp, fp, fp, vp, fp, vp, sz, vp]
+        L.gdr_backward_varlen.argtypes = [P, vp, vp, vp, vp, fp, fp, fp, vp, fp,
+                                          vp, vp, vp, fp, fp, fp, vp, sz, vp]
         for name in ("gdr_forward_workspace", "gdr_backward_workspace",
-                     "gdr_forward", "gdr_backward"):
+                     "gdr_forward", "gdr_backward", "gdr_forward_varlen", "gdr_backward_varlen"):
             getattr(L, name).restype = ctypes.c_int
         L.gdr_profile_enable.argtypes = [ctypes.c_int]
         L.gdr_profile_enable.restype = ctypes.c_int
@@ -172,30 +176,52 @@ def _save_key(prob):
             prob.flags & ~GDR_SAVE_CHUNKS, prob.algo, prob.chunk_size)
 
 
+def _ragged_dims(q, cu_seqlens, max_seqlen):
+    """(number of sequences, length bound) of a ragged batch."""
+    if q.shape[0] != 1:
+        raise ValueError("a ragged batch holds its sequences in one row: q must be [1, rows, Hk, Dk]")
+    if cu_seqlens.dtype != torch.int64 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+        raise TypeError("cu_seqlens must be a 1-d int64 device tensor")
+    n = cu_seqlens.numel() - 1
+    if max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if n > 0 else 0
+    return n, max_seqlen
+
+
 def gdr_forward(q, k, v, g, beta, h0=None, *, use_qk_l2norm=True, channelwise=False,
                 algo="auto", chunk_size=0, out_dtype=torch.float32, ht=True,
-                stream=None, fused_gates=False, save_for_backward=False):
+                stream=None, fused_gates=False, save_for_backward=False,
+                cu_seqlens=None, max_seqlen=None):
     """Returns (o, ht), or (o, ht, saved) with ``save_for_backward`` (pass
     ``saved`` to ``gdr_backward``).  ``ht`` may be True (allocate), None (not
     wanted) or a tensor to write the final state into (it may be ``h0``
     itself).  With ``fused_gates`` g and beta are pre-activations
-    (GDR_FUSED_GATES)."""
+    (GDR_FUSED_GATES).  ``cu_seqlens`` (int64 device tensor [N + 1]) makes
+    the batch ragged (gdr_forward_varlen): q, k, v, g, beta hold the N
+    sequences end to end in their token axis with a leading 1, h0 / ht are
+    [N, Hv, Dk, Dv]; ``max_seqlen`` bounds the lengths (read from the
+    offsets when not given)."""
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, q.dtype)
     for t, n in ((g, "g"), (beta, "beta"), (h0, "h0")):
         _check(t, n, torch.float32)
+    o = torch.empty((B, T, Hv, Dv), dtype=out_dtype, device=q.device)
+    if cu_seqlens is not None:  # ragged batch: q [1, rows, Hk, Dk], one state per sequence
+        B, T = _ragged_dims(q, cu_seqlens, max_seqlen)
     prob = make_problem(B, T, Hk, Hv, Dk, Dv, q.dtype, out_dtype, use_qk_l2norm,
                         channelwise, algo, chunk_size, fused_gates, save_for_backward)
-    o = torch.empty((B, T, Hv, Dv), dtype=out_dtype, device=q.device)
     if ht is True:
         ht = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=q.device)
     _check(ht, "ht", torch.float32)
     ws = _workspace(gdr_forward_workspace(prob), q.device)
-    st = lib().gdr_forward(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                           _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht), _ptr(ws),
-                           0 if ws is None else ws.numel(), _stream(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht),
+            _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    if cu_seqlens is not None:
+        st = lib().gdr_forward_varlen(ctypes.byref(prob), _ptr(cu_seqlens), *args)
+    else:
+        st = lib().gdr_forward(ctypes.byref(prob), *args)
     if st != GDR_OK:
         raise GdrError(st, "gdr_forward")
     if save_for_backward:
@@ -206,37 +232,44 @@ def gdr_forward(q, k, v, g, beta, h0=None, *, use_qk_l2norm=True, channelwise=Fa
 def gdr_backward(q, k, v, g, beta, h0, dout, dht=None, *, use_qk_l2norm=True,
                  channelwise=False, algo="auto", chunk_size=0,
                  out_dtype=torch.float32, want_dh0=True, stream=None, fused_gates=False,
-                 saved=None):
+                 saved=None, cu_seqlens=None, max_seqlen=None):
     """Returns (dq, dk, dv, dg, dbeta, dh0); dh0 is None if not wanted.  With
     ``fused_gates`` g and beta are pre-activations and dg, dbeta are the
     gradients with respect to them.  ``saved`` is what the forward of the
-    same problem and inputs returned with ``save_for_backward``."""
+    same problem and inputs returned with ``save_for_backward``.
+    ``cu_seqlens`` / ``max_seqlen`` as for ``gdr_forward``
+    (gdr_backward_varlen)."""
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _check(t, n, q.dtype)
     for t, n in ((g, "g"), (beta, "beta"), (h0, "h0"), (dht, "dht")):
         _check(t, n, torch.float32)
-    prob = make_problem(B, T, Hk, Hv, Dk, Dv, q.dtype, out_dtype, use_qk_l2norm,
-                        channelwise, algo, chunk_size, fused_gates, saved is not None)
-    if saved is not None and saved.key != _save_key(prob):
-        raise ValueError("saved chunks belong to a different problem")
     dev = q.device
     dq = torch.empty((B, T, Hk, Dk), dtype=out_dtype, device=dev)
     dk = torch.empty((B, T, Hk, Dk), dtype=out_dtype, device=dev)
     dv = torch.empty((B, T, Hv, Dv), dtype=out_dtype, device=dev)
     dg = torch.empty(g.shape, dtype=torch.float32, device=dev)
     dbeta = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
+    if cu_seqlens is not None:
+        B, T = _ragged_dims(q, cu_seqlens, max_seqlen)
+    prob = make_problem(B, T, Hk, Hv, Dk, Dv, q.dtype, out_dtype, use_qk_l2norm,
+                        channelwise, algo, chunk_size, fused_gates, saved is not None)
+    if saved is not None and saved.key != _save_key(prob):
+        raise ValueError("saved chunks belong to a different problem")
     dh0 = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=dev) if want_dh0 else None
     nws = gdr_backward_workspace(prob)
     if saved is not None and saved.ws is not None and saved.ws.numel() >= nws:
         ws = saved.ws  # the forward's images and chunk states
     else:
         ws = _workspace(nws, dev)
-    st = lib().gdr_backward(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                            _ptr(beta), _ptr(h0), _ptr(dout), _ptr(dht), _ptr(dq),
-                            _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0),
-                            _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(dout), _ptr(dht),
+            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0),
+            _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    if cu_seqlens is not None:
+        st = lib().gdr_backward_varlen(ctypes.byref(prob), _ptr(cu_seqlens), *args)
+    else:
+        st = lib().gdr_backward(ctypes.byref(prob), *args)
     if st != GDR_OK:
         raise GdrError(st, "gdr_backward")
     return dq, dk, dv, dg, dbeta, dh0

@@ -66,18 +66,23 @@ int chunk_of(const gdr_problem* p) { return p->chunk_size ? p->chunk_size : 64; 
 constexpr bool kChunkedBackward = true;
 
 // SEQUENTIAL or CHUNKED for this call; CHUNKED needs a scalar gate.
-gdr_status resolve_algo(const gdr_problem* p, bool backward, int* algo) {
+gdr_status resolve_algo(const gdr_problem* p, bool backward, int* algo, bool ragged = false) {
   // channelwise gates: chunked forward on the fp16 matrix-core path only
-  // (bf16 io, Dk = 128, C >= 32); their VJP runs sequentially
-  const bool chunk_ok = (p->flags & GDR_CHANNELWISE)
-                            ? !backward && gdr::chunk_uses_f16(shape_of(p), chunk_of(p))
-                            : !backward || kChunkedBackward;
+  // (bf16 io, Dk = 128, C >= 32); their VJP runs sequentially.  Ragged
+  // batches: the chunked kernels on that path, and the sequential forward.
+  const bool f16 = gdr::chunk_uses_f16(shape_of(p), chunk_of(p));
+  const bool chunk_ok = (p->flags & GDR_CHANNELWISE) ? !backward && f16
+                                                     : (!backward || kChunkedBackward) && (!ragged || f16);
+  const bool seq_ok = !(ragged && backward);
   if (p->algo == GDR_ALGO_CHUNKED) {
     if (!chunk_ok) return GDR_ERR_UNSUPPORTED;
     *algo = GDR_ALGO_CHUNKED;
   } else if (p->algo == GDR_ALGO_AUTO) {
-    *algo = (chunk_ok && p->T > 64) ? GDR_ALGO_CHUNKED : GDR_ALGO_SEQUENTIAL;
+    if (chunk_ok && (p->T > 64 || !seq_ok)) *algo = GDR_ALGO_CHUNKED;
+    else if (seq_ok) *algo = GDR_ALGO_SEQUENTIAL;
+    else return GDR_ERR_UNSUPPORTED;
   } else {
+    if (!seq_ok) return GDR_ERR_UNSUPPORTED;
     *algo = GDR_ALGO_SEQUENTIAL;
   }
   return GDR_OK;
@@ -156,20 +161,24 @@ gdr_status gdr_backward_workspace(const gdr_problem* p, size_t* bytes) {
   return GDR_OK;
 }
 
-gdr_status gdr_forward(const gdr_problem* p, const void* q, const void* k, const void* v,
-                       const float* g, const float* beta, const float* h0, void* o, float* ht,
-                       void* ws, size_t ws_bytes, void* hip_stream) {
+namespace {
+
+// gdr_forward / gdr_forward_varlen (cu: ragged-batch row offsets or null).
+gdr_status forward_impl(const gdr_problem* p, const int64_t* cu, bool ragged, const void* q, const void* k,
+                        const void* v, const float* g, const float* beta, const float* h0, void* o, float* ht,
+                        void* ws, size_t ws_bytes, void* hip_stream) {
   gdr_status st = check_problem(p);
   if (st != GDR_OK) return st;
   const Shape s = shape_of(p);
   const bool empty = s.B == 0 || s.T == 0;
   if (!empty && (!q || !k || !v || !g || !beta || !o)) return GDR_ERR_NULL_ARG;
+  if (ragged && !empty && !cu) return GDR_ERR_NULL_ARG;
   const void* ptrs[] = {q, k, v, g, beta, h0, o, ht};
   for (const void* ptr : ptrs)
     if (misaligned(ptr)) return GDR_ERR_BAD_ALIGNMENT;
-  if (misaligned(ws, kWsAlign)) return GDR_ERR_BAD_ALIGNMENT;
+  if (misaligned(ws, kWsAlign) || misaligned(cu, 8)) return GDR_ERR_BAD_ALIGNMENT;
   int algo;
-  if ((st = resolve_algo(p, false, &algo)) != GDR_OK) return st;
+  if ((st = resolve_algo(p, false, &algo, ragged)) != GDR_OK) return st;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   if (s.B == 0) return GDR_OK;
   const size_t state_bytes = static_cast<size_t>(s.B * s.Hv) * s.D * s.D * sizeof(float);
@@ -182,31 +191,33 @@ gdr_status gdr_forward(const gdr_problem* p, const void* q, const void* k, const
   if (algo == GDR_ALGO_CHUNKED) {
     if (!ws) return GDR_ERR_NULL_ARG;
     if (ws_bytes < gdr::chunk_fwd_workspace(s, chunk_of(p))) return GDR_ERR_WORKSPACE_TOO_SMALL;
-    gdr::ChunkFwdArgs a{q, k, v, g, beta, h0, o, ht};
+    gdr::ChunkFwdArgs a{q, k, v, g, beta, h0, o, ht, cu};
     hipError_t e = gdr::launch_chunk_fwd(s, chunk_of(p), a, ws, stream);
     return e == hipSuccess ? GDR_OK : hip_fail(e);
   }
-  gdr::SeqFwdArgs a{q, k, v, g, beta, h0, o, ht};
+  gdr::SeqFwdArgs a{q, k, v, g, beta, h0, o, ht, cu};
   hipError_t e = gdr::launch_seq_fwd(s, a, stream);
   return e == hipSuccess ? GDR_OK : hip_fail(e);
 }
 
-gdr_status gdr_backward(const gdr_problem* p, const void* q, const void* k, const void* v,
-                        const float* g, const float* beta, const float* h0, const void* dout,
-                        const float* dht, void* dq, void* dk, void* dv, float* dg, float* dbeta,
-                        float* dh0, void* ws, size_t ws_bytes, void* hip_stream) {
+// gdr_backward / gdr_backward_varlen.
+gdr_status backward_impl(const gdr_problem* p, const int64_t* cu, bool ragged, const void* q, const void* k,
+                         const void* v, const float* g, const float* beta, const float* h0, const void* dout,
+                         const float* dht, void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
+                         void* ws, size_t ws_bytes, void* hip_stream) {
   gdr_status st = check_problem(p);
   if (st != GDR_OK) return st;
   const Shape s = shape_of(p);
   const bool empty = s.B == 0 || s.T == 0;
   if (!empty && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
     return GDR_ERR_NULL_ARG;
+  if (ragged && !empty && !cu) return GDR_ERR_NULL_ARG;
   const void* ptrs[] = {q, k, v, g, beta, h0, dout, dht, dq, dk, dv, dg, dbeta, dh0};
   for (const void* ptr : ptrs)
     if (misaligned(ptr)) return GDR_ERR_BAD_ALIGNMENT;
-  if (misaligned(ws, kWsAlign)) return GDR_ERR_BAD_ALIGNMENT;
+  if (misaligned(ws, kWsAlign) || misaligned(cu, 8)) return GDR_ERR_BAD_ALIGNMENT;
   int algo;
-  if ((st = resolve_algo(p, true, &algo)) != GDR_OK) return st;
+  if ((st = resolve_algo(p, true, &algo, ragged)) != GDR_OK) return st;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   if (s.B == 0) return GDR_OK;
   const size_t state_bytes = static_cast<size_t>(s.B * s.Hv) * s.D * s.D * sizeof(float);
@@ -220,7 +231,7 @@ gdr_status gdr_backward(const gdr_problem* p, const void* q, const void* k, cons
     const int C = chunk_of(p);
     if (!ws) return GDR_ERR_NULL_ARG;
     if (ws_bytes < gdr::chunk_bwd_workspace(s, C)) return GDR_ERR_WORKSPACE_TOO_SMALL;
-    gdr::ChunkBwdArgs a{q, k, v, dout, g, beta, h0, dht, dq, dk, dv, dg, dbeta, dh0};
+    gdr::ChunkBwdArgs a{q, k, v, dout, g, beta, h0, dht, dq, dk, dv, dg, dbeta, dh0, cu};
     hipError_t e = gdr::launch_chunk_bwd(s, C, a, ws, stream);
     return e == hipSuccess ? GDR_OK : hip_fail(e);
   }
@@ -235,6 +246,36 @@ gdr_status gdr_backward(const gdr_problem* p, const void* q, const void* k, cons
   gdr::EpiArgs ea{q, k, a.part_dq, a.part_dk, a.part_db, a.part_dg, gdr::seq_bwd_slices(s), dq, dk, dbeta, dg, g, beta};
   e = gdr::launch_bwd_epilogue(s, ea, stream);
   return e == hipSuccess ? GDR_OK : hip_fail(e);
+}
+
+}  // namespace
+
+gdr_status gdr_forward(const gdr_problem* p, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const float* h0, void* o, float* ht,
+                       void* ws, size_t ws_bytes, void* hip_stream) {
+  return forward_impl(p, nullptr, false, q, k, v, g, beta, h0, o, ht, ws, ws_bytes, hip_stream);
+}
+
+gdr_status gdr_forward_varlen(const gdr_problem* p, const int64_t* cu_seqlens, const void* q, const void* k,
+                              const void* v, const float* g, const float* beta, const float* h0, void* o,
+                              float* ht, void* ws, size_t ws_bytes, void* hip_stream) {
+  return forward_impl(p, cu_seqlens, true, q, k, v, g, beta, h0, o, ht, ws, ws_bytes, hip_stream);
+}
+
+gdr_status gdr_backward(const gdr_problem* p, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const float* h0, const void* dout,
+                        const float* dht, void* dq, void* dk, void* dv, float* dg, float* dbeta,
+                        float* dh0, void* ws, size_t ws_bytes, void* hip_stream) {
+  return backward_impl(p, nullptr, false, q, k, v, g, beta, h0, dout, dht, dq, dk, dv, dg, dbeta, dh0, ws,
+                       ws_bytes, hip_stream);
+}
+
+gdr_status gdr_backward_varlen(const gdr_problem* p, const int64_t* cu_seqlens, const void* q, const void* k,
+                               const void* v, const float* g, const float* beta, const float* h0,
+                               const void* dout, const float* dht, void* dq, void* dk, void* dv, float* dg,
+                               float* dbeta, float* dh0, void* ws, size_t ws_bytes, void* hip_stream) {
+  return backward_impl(p, cu_seqlens, true, q, k, v, g, beta, h0, dout, dht, dq, dk, dv, dg, dbeta, dh0, ws,
+                       ws_bytes, hip_stream);
 }
 
 }  // extern "C"

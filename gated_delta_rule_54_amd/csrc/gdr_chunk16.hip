@@ -83,7 +83,21 @@ struct K16 {
   int Hk, Hv, NC, l2;
   int fg;                  // fused gate activation: g, beta hold pre-activations
   int gi;                  // v-head within its k-head group (gradient launches)
+  const int64_t* cu;       // ragged batch: sequence b is rows cu[b] .. cu[b+1) (null: rows b*T .. b*T+T)
 };
+
+// Sequence b of the batch: its first token row and its length.  A ragged
+// batch gives row offsets cu[0..B] (each length clamped to [0, T]: the
+// workspace holds ceil(T / C) chunks per sequence); otherwise sequence b is
+// rows b * T .. b * T + T - 1.
+struct SeqSpan {
+  int64_t t0, len;
+};
+__device__ __forceinline__ SeqSpan seq_span(const K16& a, int64_t b) {
+  if (!a.cu) return SeqSpan{b * a.T, a.T};
+  const int64_t s0 = a.cu[b], n = a.cu[b + 1] - s0;
+  return SeqSpan{s0, n < 0 ? 0 : (n > a.T ? a.T : n)};
+}
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // Wave index as a scalar (wave-uniform by construction).
@@ -416,11 +430,13 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
   const int64_t b = blockIdx.z;
   const int grp = a.Hv / a.Hk, kh = hv / grp;
   const int64_t t0 = static_cast<int64_t>(c) * C;
-  const int L = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
+  const SeqSpan sp = seq_span(a, b);
+  if (t0 >= sp.len) return;  // past the end of a shorter sequence of a ragged batch
+  const int L = static_cast<int>(sp.len - t0 < C ? sp.len - t0 : C);
   {
     const int r = tid / TPR, part = tid % TPR;
     const int rc = r < L ? r : L - 1;
-    const int64_t off = ((b * a.T + t0 + rc) * a.Hk + kh) * DK + part * EPT;
+    const int64_t off = ((sp.t0 + t0 + rc) * a.Hk + kh) * DK + part * EPT;
     uint4 kr[NV], qr[NV];
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
@@ -430,7 +446,7 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
     float gv = 0.f, bv = 0.f;
     if (tid < 64) {
       const int rr = tid < L ? tid : L - 1;
-      const int64_t row = (b * a.T + t0 + rr) * a.Hv + hv;
+      const int64_t row = (sp.t0 + t0 + rr) * a.Hv + hv;
       gv = a.fg ? fg_log_alpha(a.g[row]) : a.g[row];
       bv = a.fg ? fg_beta(a.beta[row]) : a.beta[row];
       gv = tid < L ? gv : 0.f;
@@ -665,9 +681,18 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void chain16_kernel(K16 a) {
 
   const int w = wave_id(), lane = lane_id(), g = lane >> 4, c16 = lane & 15;
   const ChainPos p = chain_pos(a);
-  auto rows_of = [&](int c) { return static_cast<int>(a.T - static_cast<int64_t>(c) * C < C ? a.T - static_cast<int64_t>(c) * C : C); };
+  const SeqSpan sp = seq_span(a, p.b);
+  const int nc = static_cast<int>((sp.len + C - 1) / C);
+  if (nc == 0) {  // empty sequence of a ragged batch: the state passes through
+    if (w < NCW && a.ht) {
+      const int64_t base = (p.b * a.Hv + p.hv) * DK * DK + p.half * BV + 16 * w + c16;
+      for (int i = 0; i < DK; ++i) a.ht[base + i * DK] = a.h0 ? a.h0[base + i * DK] : 0.f;
+    }
+    return;
+  }
+  auto rows_of = [&](int c) { return static_cast<int>(sp.len - static_cast<int64_t>(c) * C < C ? sp.len - static_cast<int64_t>(c) * C : C); };
   auto seq_rsrc = [&](const void* base, int esize, int c, uint32_t rowb) {
-    const char* p0 = static_cast<const char*>(base) + (p.b * a.T + static_cast<int64_t>(c) * C) * a.Hv * DK * esize;
+    const char* p0 = static_cast<const char*>(base) + (sp.t0 + static_cast<int64_t>(c) * C) * a.Hv * DK * esize;
     return make_rsrc(p0, static_cast<uint32_t>(rows_of(c)) * rowb);
   };
   const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;         // bf16 row pitch of v
@@ -684,7 +709,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void chain16_kernel(K16 a) {
       dma_rows<C, BV * 2, 64>(seq_rsrc(a.v, 2, c, rowv), rowv, colv, rows_of(c), buf + CB + KB, lane, 0);
     };
     auto pstep = [&](int c, char* nxt, const char* os_prev) __attribute__((always_inline)) {
-      if (c + 1 < a.NC) stage(c + 1, nxt);
+      if (c + 1 < nc) stage(c + 1, nxt);
       if constexpr (WRITE_O) {
         if (c > 0) flush_tile<TO, C>(os_prev, seq_rsrc(a.o, sizeof(TO), c - 1, rowo), rowo, colo);
       }
@@ -694,12 +719,12 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void chain16_kernel(K16 a) {
     stage(0, bufA);
     wait_all();
     lds_barrier();
-    for (int c = 0; c < a.NC; c += 2) {
+    for (int c = 0; c < nc; c += 2) {
       pstep(c, bufB, osB);
-      if (c + 1 < a.NC) pstep(c + 1, bufA, osA);
+      if (c + 1 < nc) pstep(c + 1, bufA, osA);
     }
     if constexpr (WRITE_O)
-      flush_tile<TO, C>(((a.NC - 1) & 1) ? osB : osA, seq_rsrc(a.o, sizeof(TO), a.NC - 1, rowo), rowo, colo);
+      flush_tile<TO, C>(((nc - 1) & 1) ? osB : osA, seq_rsrc(a.o, sizeof(TO), nc - 1, rowo), rowo, colo);
     return;
   }
 
@@ -779,9 +804,9 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void chain16_kernel(K16 a) {
     if constexpr (WRITE_O) put_strip<TO, NT>(os, 16 * w + c16, o);
     lds_barrier();
   };
-  for (int c = 0; c < a.NC; c += 2) {
+  for (int c = 0; c < nc; c += 2) {
     step(c, bufA, osA);
-    if (c + 1 < a.NC) step(c + 1, bufB, osB);
+    if (c + 1 < nc) step(c + 1, bufB, osB);
   }
   if (a.ht) {
 #pragma unroll
@@ -813,9 +838,18 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
 
   const int w = wave_id(), lane = lane_id(), g = lane >> 4, c16 = lane & 15;
   const ChainPos p = chain_pos(a);
-  auto rows_of = [&](int c) { return static_cast<int>(a.T - static_cast<int64_t>(c) * C < C ? a.T - static_cast<int64_t>(c) * C : C); };
+  const SeqSpan sp = seq_span(a, p.b);
+  const int nc = static_cast<int>((sp.len + C - 1) / C);
+  if (nc == 0) {  // empty sequence of a ragged batch: the state passes through
+    if (w < NCW && a.dh0) {
+      const int64_t base = (p.b * a.Hv + p.hv) * DK * DK + p.half * BV + 16 * w + c16;
+      for (int i = 0; i < DK; ++i) a.dh0[base + i * DK] = a.dht ? a.dht[base + i * DK] : 0.f;
+    }
+    return;
+  }
+  auto rows_of = [&](int c) { return static_cast<int>(sp.len - static_cast<int64_t>(c) * C < C ? sp.len - static_cast<int64_t>(c) * C : C); };
   auto seq_rsrc = [&](const void* base, int esize, int c, uint32_t rowb) {
-    const char* p0 = static_cast<const char*>(base) + (p.b * a.T + static_cast<int64_t>(c) * C) * a.Hv * DK * esize;
+    const char* p0 = static_cast<const char*>(base) + (sp.t0 + static_cast<int64_t>(c) * C) * a.Hv * DK * esize;
     return make_rsrc(p0, static_cast<uint32_t>(rows_of(c)) * rowb);
   };
   const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
@@ -833,18 +867,18 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
     };
     auto pstep = [&](int c, char* nxt, const char* os_prev) __attribute__((always_inline)) {
       if (c > 0) stage(c - 1, nxt);
-      if (c + 1 < a.NC) flush_tile<TO, C>(os_prev, seq_rsrc(a.dv, sizeof(TO), c + 1, rowo), rowo, colo);
+      if (c + 1 < nc) flush_tile<TO, C>(os_prev, seq_rsrc(a.dv, sizeof(TO), c + 1, rowo), rowo, colo);
       wait_all();
       lds_barrier();
     };
-    stage(a.NC - 1, bufA);
+    stage(nc - 1, bufA);
     wait_all();
     lds_barrier();
-    for (int i = 0; i < a.NC; i += 2) {
-      pstep(a.NC - 1 - i, bufB, osB);
-      if (i + 1 < a.NC) pstep(a.NC - 2 - i, bufA, osA);
+    for (int i = 0; i < nc; i += 2) {
+      pstep(nc - 1 - i, bufB, osB);
+      if (i + 1 < nc) pstep(nc - 2 - i, bufA, osA);
     }
-    flush_tile<TO, C>(((a.NC - 1) & 1) ? osB : osA, seq_rsrc(a.dv, sizeof(TO), 0, rowo), rowo, colo);
+    flush_tile<TO, C>(((nc - 1) & 1) ? osB : osA, seq_rsrc(a.dv, sizeof(TO), 0, rowo), rowo, colo);
     return;
   }
 
@@ -925,9 +959,9 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
     lds_barrier();
   };
   // chunks NC-1, NC-2, ... alternate between the two buffers
-  for (int i = 0; i < a.NC; i += 2) {
-    step(a.NC - 1 - i, bufA, osA);
-    if (i + 1 < a.NC) step(a.NC - 2 - i, bufB, osB);
+  for (int i = 0; i < nc; i += 2) {
+    step(nc - 1 - i, bufA, osA);
+    if (i + 1 < nc) step(nc - 2 - i, bufB, osB);
   }
   if (a.dh0) {
 #pragma unroll
@@ -1010,7 +1044,9 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   const int64_t b = blockIdx.z;
   const int hv = kh * (a.Hv / a.Hk) + a.gi;
   const int64_t t0 = static_cast<int64_t>(c) * C;
-  const int L = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
+  const SeqSpan sp = seq_span(a, b);
+  if (t0 >= sp.len) return;  // past the end of a shorter sequence of a ragged batch
+  const int L = static_cast<int>(sp.len - t0 < C ? sp.len - t0 : C);
   const int64_t cbase = (b * a.Hv + hv) * a.NC + c;
   const int jw = 16 * w + c16;         // phase A value column
   const int i2 = 16 * w + c16;         // phase 1/2 and dq/dk key row
@@ -1041,7 +1077,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   };
   // raw v / dO rows of the chunk, packed [C][DK] bf16, in the strip buffers
   const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
-  const int64_t seq0 = (b * a.T + t0) * a.Hv * DK;
+  const int64_t seq0 = (sp.t0 + t0) * a.Hv * DK;
   dma_rows<C, DK * 2, 512>(make_rsrc(a.v + seq0, static_cast<uint32_t>(L) * rowv), rowv, hv * DK * 2, L,
                            reinterpret_cast<char*>(xb), tid, w);
   dma_rows<C, DK * 2, 512>(make_rsrc(a.dout + seq0, static_cast<uint32_t>(L) * rowv), rowv, hv * DK * 2, L,
@@ -1222,7 +1258,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   const uint32_t rowk = static_cast<uint32_t>(a.Hk) * DK * 2;
   if constexpr (MODE == kLast || MODE == kOnly) {
     if (a.l2) {
-      const int64_t seqk = (b * a.T + t0) * a.Hk * DK;
+      const int64_t seqk = (sp.t0 + t0) * a.Hk * DK;
       const rsrc_t qr_ = make_rsrc(a.q + seqk, static_cast<uint32_t>(L) * rowk);
       const rsrc_t kr_ = make_rsrc(a.k + seqk, static_cast<uint32_t>(L) * rowk);
 #pragma unroll
@@ -1420,7 +1456,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       if (lane + off < 64) x += yv;
     }
     if (r < L) {
-      const int64_t row = (b * a.T + t0 + r) * a.Hv + hv;
+      const int64_t row = (sp.t0 + t0 + r) * a.Hv + hv;
       a.dg[row] = a.fg ? x * fg_dlog_alpha(a.g[row]) : x;
       a.dbeta[row] = a.fg ? dB * fg_dbeta(a.beta[row]) : dB;
     }
@@ -1477,7 +1513,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       }
     }
     const uint32_t rowo = static_cast<uint32_t>(a.Hk) * DK * sizeof(TO);
-    const int64_t seqo = (b * a.T + t0) * a.Hk * DK * static_cast<int64_t>(sizeof(TO));
+    const int64_t seqo = (sp.t0 + t0) * a.Hk * DK * static_cast<int64_t>(sizeof(TO));
     const rsrc_t oqr = make_rsrc(static_cast<char*>(a.dq) + seqo, static_cast<uint32_t>(L) * rowo);
     const rsrc_t okr = make_rsrc(static_cast<char*>(a.dk) + seqo, static_cast<uint32_t>(L) * rowo);
     f32x4 oq[NT], ok[NT];
@@ -1635,14 +1671,16 @@ __global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
   const int64_t b = blockIdx.z;
   const int kh = hv / (a.Hv / a.Hk);
   const int64_t t0 = static_cast<int64_t>(c) * C;
-  const int L = static_cast<int>(a.T - t0 < C ? a.T - t0 : C);
+  const SeqSpan sp = seq_span(a, b);
+  if (t0 >= sp.len) return;  // past the end of a shorter sequence of a ragged batch
+  const int L = static_cast<int>(sp.len - t0 < C ? sp.len - t0 : C);
   // gates: thread -> channel tid % DK, rows of quarter tid / DK, running sum
   // in registers (g = 0 past the end)
   constexpr int RQ = C / 4;
   const int gi = tid & (DK - 1), gq = tid >> 7;
   float gr[RQ];
   {
-    const float* gp = a.g + ((b * a.T + t0 + gq * RQ) * a.Hv + hv) * DK + gi;
+    const float* gp = a.g + ((sp.t0 + t0 + gq * RQ) * a.Hv + hv) * DK + gi;
     const int64_t rs = static_cast<int64_t>(a.Hv) * DK;
 #pragma unroll
     for (int j = 0; j < RQ; ++j) gr[j] = gq * RQ + j < L ? gp[j * rs] : 0.f;
@@ -1650,7 +1688,7 @@ __global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
   {  // q / k rows (normalised, fp16) and beta
     const int r = tid / TPR, part = tid % TPR;
     const int rc = r < L ? r : L - 1;
-    const int64_t off = ((b * a.T + t0 + rc) * a.Hk + kh) * DK + part * EPT;
+    const int64_t off = ((sp.t0 + t0 + rc) * a.Hk + kh) * DK + part * EPT;
     uint4 kr[NV], qr[NV];
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
@@ -1662,7 +1700,7 @@ __global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
     if (tid < C) {
       float bv = 0.f;
       if (tid < L) {
-        bv = a.beta[(b * a.T + t0 + tid) * a.Hv + hv];
+        bv = a.beta[(sp.t0 + t0 + tid) * a.Hv + hv];
         if (a.fg) bv = fg_beta(bv);
       }
       bet[tid] = bv;
@@ -1877,9 +1915,18 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
 
   const int w = wave_id(), lane = lane_id(), g = lane >> 4, c16 = lane & 15;
   const ChainPos p = chain_pos(a);
-  auto rows_of = [&](int c) { return static_cast<int>(a.T - static_cast<int64_t>(c) * C < C ? a.T - static_cast<int64_t>(c) * C : C); };
+  const SeqSpan sp = seq_span(a, p.b);
+  const int nc = static_cast<int>((sp.len + C - 1) / C);
+  if (nc == 0) {  // empty sequence of a ragged batch: the state passes through
+    if (w < NCW && a.ht) {
+      const int64_t base = (p.b * a.Hv + p.hv) * DK * DK + p.half * BV + 16 * w + c16;
+      for (int i = 0; i < DK; ++i) a.ht[base + i * DK] = a.h0 ? a.h0[base + i * DK] : 0.f;
+    }
+    return;
+  }
+  auto rows_of = [&](int c) { return static_cast<int>(sp.len - static_cast<int64_t>(c) * C < C ? sp.len - static_cast<int64_t>(c) * C : C); };
   auto seq_rsrc = [&](const void* base, int esize, int c, uint32_t rowb) {
-    const char* p0 = static_cast<const char*>(base) + (p.b * a.T + static_cast<int64_t>(c) * C) * a.Hv * DK * esize;
+    const char* p0 = static_cast<const char*>(base) + (sp.t0 + static_cast<int64_t>(c) * C) * a.Hv * DK * esize;
     return make_rsrc(p0, static_cast<uint32_t>(rows_of(c)) * rowb);
   };
   const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
@@ -1897,12 +1944,12 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
     stage(0, bufA);
     wait_all();
     lds_barrier();
-    for (int c = 0; c < a.NC; c += 2) {
-      if (c + 1 < a.NC) stage(c + 1, bufB);
+    for (int c = 0; c < nc; c += 2) {
+      if (c + 1 < nc) stage(c + 1, bufB);
       wait_all();
       lds_barrier();
-      if (c + 1 < a.NC) {
-        if (c + 2 < a.NC) stage(c + 2, bufA);
+      if (c + 1 < nc) {
+        if (c + 2 < nc) stage(c + 2, bufA);
         wait_all();
         lds_barrier();
       }
@@ -1966,11 +2013,11 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
     mma_chain_rows_t<NTK, NT>(h, Kl, LDK, bf);
     lds_barrier();
   };
-  for (int c = 0; c < a.NC; c += 2) {
+  for (int c = 0; c < nc; c += 2) {
     step(c, bufA);
-    if (c + 1 < a.NC) step(c + 1, bufB);
+    if (c + 1 < nc) step(c + 1, bufB);
   }
-  store_strip_buf<TO, NT>(seq_rsrc(a.o, sizeof(TO), a.NC - 1, rowo), voffo, rowo, o);
+  store_strip_buf<TO, NT>(seq_rsrc(a.o, sizeof(TO), nc - 1, rowo), voffo, rowo, o);
   if (a.ht) {
 #pragma unroll
     for (int ti = 0; ti < NTK; ++ti)
@@ -2082,6 +2129,7 @@ hipError_t grad16(K16 a, hipStream_t st) {
 template <int C, typename TO>
 hipError_t fwd_all(const Shape& s, const ChunkFwdArgs& x, void* ws, hipStream_t st) {
   K16 a = args16(s, C, ws, plan16<C>(s, s.save_chunks));
+  a.cu = x.cu;
   a.q = static_cast<const bf16_t*>(x.q);
   a.k = static_cast<const bf16_t*>(x.k);
   a.v = static_cast<const bf16_t*>(x.v);
@@ -2098,6 +2146,7 @@ hipError_t fwd_all(const Shape& s, const ChunkFwdArgs& x, void* ws, hipStream_t 
 template <int C, typename TO>
 hipError_t bwd_all(const Shape& s, const ChunkBwdArgs& x, void* ws, hipStream_t st) {
   K16 a = args16(s, C, ws, plan16<C>(s, true));
+  a.cu = x.cu;
   a.q = static_cast<const bf16_t*>(x.q);
   a.k = static_cast<const bf16_t*>(x.k);
   a.v = static_cast<const bf16_t*>(x.v);
@@ -2138,6 +2187,7 @@ Ws16 plan_cw(const Shape& s) {
 template <int C, typename TO>
 hipError_t fwd_cw(const Shape& s, const ChunkFwdArgs& x, void* ws, hipStream_t st) {
   K16 a = args16(s, C, ws, plan_cw<C>(s));
+  a.cu = x.cu;
   a.q = static_cast<const bf16_t*>(x.q);
   a.k = static_cast<const bf16_t*>(x.k);
   a.v = static_cast<const bf16_t*>(x.v);

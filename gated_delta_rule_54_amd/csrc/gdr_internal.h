@@ -31,6 +31,7 @@ struct SeqFwdArgs {
   const float *g, *beta, *h0;
   void* o;
   float* ht;
+  const int64_t* cu;  // ragged batch row offsets [B + 1], or null
 };
 hipError_t launch_seq_fwd(const Shape& s, const SeqFwdArgs& a, hipStream_t st);
 
@@ -80,6 +81,7 @@ struct ChunkFwdArgs {
   const float *g, *beta, *h0;
   void* o;
   float* ht;
+  const int64_t* cu;  // ragged batch row offsets [B + 1] (fp16 path only), or null
 };
 hipError_t launch_chunk_fwd(const Shape& s, int C, const ChunkFwdArgs& a, void* ws, hipStream_t st);
 
@@ -91,6 +93,7 @@ struct ChunkBwdArgs {
   const float *g, *beta, *h0, *dht;
   void *dq, *dk, *dv;
   float *dg, *dbeta, *dh0;
+  const int64_t* cu;  // ragged batch row offsets [B + 1] (fp16 path only), or null
 };
 hipError_t launch_chunk_bwd(const Shape& s, int C, const ChunkBwdArgs& a, void* ws, hipStream_t st);
 

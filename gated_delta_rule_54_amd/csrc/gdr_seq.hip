@@ -72,12 +72,12 @@ template <int D, typename L, typename TI, bool CW, bool WANT_Q, bool WANT_DO>
 __device__ __forceinline__ void load_tok(Tok<L::RPL, CW>& x, const Dims& d,
                                          const void* q, const void* k, const void* v,
                                          const void* dout, const float* g,
-                                         const float* beta, int64_t b, int64_t t,
+                                         const float* beta, int64_t row,
                                          int kh, int hv, int i0, int j0) {
   constexpr int RPL = L::RPL;
-  const int64_t krow = ((b * d.T + t) * d.Hk + kh) * D + i0;
-  const int64_t vrow = ((b * d.T + t) * d.Hv + hv) * D + j0;
-  const int64_t grow = (b * d.T + t) * d.Hv + hv;
+  const int64_t krow = (row * d.Hk + kh) * D + i0;
+  const int64_t vrow = (row * d.Hv + hv) * D + j0;
+  const int64_t grow = row * d.Hv + hv;
   ld_rows<RPL, TI>(static_cast<const TI*>(k) + krow, x.k);
   if constexpr (WANT_Q) ld_rows<RPL, TI>(static_cast<const TI*>(q) + krow, x.q);
   ld4<TI>(static_cast<const TI*>(v) + vrow, x.v);
@@ -171,14 +171,22 @@ __global__ __launch_bounds__(64) void seq_fwd_kernel(Dims d, SeqFwdArgs a) {
       h[m][0] = h[m][1] = h[m][2] = h[m][3] = 0.f;
     }
   }
+  // sequence b: rows tb .. tb + len - 1 (a ragged batch gives offsets cu[0..B],
+  // lengths clamped to [0, T])
+  int64_t tb = b * d.T, len = d.T;
+  if (a.cu) {
+    tb = a.cu[b];
+    len = a.cu[b + 1] - tb;
+    len = len < 0 ? 0 : (len > d.T ? d.T : len);
+  }
   Tok<L::RPL, CW> cur, nxt;
-  load_tok<D, L, TI, CW, true, false>(cur, d, a.q, a.k, a.v, nullptr, a.g, a.beta, b, 0, kh, hv, i0, j0);
-  for (int64_t t = 0; t < d.T; ++t) {
-    if (t + 1 < d.T)  // prefetch the next token while this one computes
-      load_tok<D, L, TI, CW, true, false>(nxt, d, a.q, a.k, a.v, nullptr, a.g, a.beta, b, t + 1, kh, hv, i0, j0);
+  if (len > 0) load_tok<D, L, TI, CW, true, false>(cur, d, a.q, a.k, a.v, nullptr, a.g, a.beta, tb, kh, hv, i0, j0);
+  for (int64_t t = 0; t < len; ++t) {
+    if (t + 1 < len)  // prefetch the next token while this one computes
+      load_tok<D, L, TI, CW, true, false>(nxt, d, a.q, a.k, a.v, nullptr, a.g, a.beta, tb + t + 1, kh, hv, i0, j0);
     float u[4], o[4];
     fwd_step<L, CW, true>(h, cur, d.l2, u, o);
-    if (rg == 0) st4<TO>(static_cast<TO*>(a.o) + ((b * d.T + t) * d.Hv + hv) * D + j0, o);
+    if (rg == 0) st4<TO>(static_cast<TO*>(a.o) + ((tb + t) * d.Hv + hv) * D + j0, o);
     cur = nxt;
   }
   if (a.ht) {
@@ -236,7 +244,7 @@ __global__ __launch_bounds__(64) void seq_bwd_kernel(Dims d, SeqBwdArgs a, int n
       for (int m = 0; m < RPL; ++m) st4<float>(lane_ptr(ck, t / kSeqSeg, m), h[m]);
     }
     Tok<RPL, CW> x;
-    load_tok<D, L, TI, CW, false, false>(x, d, a.q, a.k, a.v, nullptr, a.g, a.beta, b, t, kh, hv, i0, j0);
+    load_tok<D, L, TI, CW, false, false>(x, d, a.q, a.k, a.v, nullptr, a.g, a.beta, b * d.T + t, kh, hv, i0, j0);
     float u[4], o[4];
     fwd_step<L, CW, false>(h, x, d.l2, u, o);
   }
@@ -257,14 +265,15 @@ __global__ __launch_bounds__(64) void seq_bwd_kernel(Dims d, SeqBwdArgs a, int n
 #pragma unroll
       for (int m = 0; m < RPL; ++m) st4<float>(lane_ptr(sc, tau, m), h[m]);
       Tok<RPL, CW> x;
-      load_tok<D, L, TI, CW, false, false>(x, d, a.q, a.k, a.v, nullptr, a.g, a.beta, b, t0 + tau, kh, hv, i0, j0);
+      load_tok<D, L, TI, CW, false, false>(x, d, a.q, a.k, a.v, nullptr, a.g, a.beta, b * d.T + t0 + tau, kh, hv,
+                                           i0, j0);
       float u[4], o[4];
       fwd_step<L, CW, false>(h, x, d.l2, u, o);
     }
     for (int tau = len - 1; tau >= 0; --tau) {
       const int64_t t = t0 + tau;
       Tok<RPL, CW> x;
-      load_tok<D, L, TI, CW, true, true>(x, d, a.q, a.k, a.v, a.dout, a.g, a.beta, b, t, kh, hv, i0, j0);
+      load_tok<D, L, TI, CW, true, true>(x, d, a.q, a.k, a.v, a.dout, a.g, a.beta, b * d.T + t, kh, hv, i0, j0);
       float Dm[RPL][4];
 #pragma unroll
       for (int m = 0; m < RPL; ++m) {

@@ -141,10 +141,10 @@ gdr_status gdr_forward(const gdr_problem* p, const void* q, const void* k,
                        const float* h0, void* o, float* ht, void* ws,
                        size_t ws_bytes, void* hip_stream);
 
-/* VJP of gdr_forward for the loss <dout, o> + <dht, ht>.  The backward is
- * stateless: it takes the forward's raw inputs (q, k unnormalised when the
- * flag is set) and recomputes what it needs; nothing from a forward call is
- * kept.  h0 and dht may be NULL (zeros); dh0 may be NULL (not wanted).
+/* VJP of gdr_forward for the loss <dout, o> + <dht, ht>.  Without
+ * GDR_SAVE_CHUNKS the backward is stateless: it takes the forward's raw
+ * inputs (q, k unnormalised when the flag is set) and recomputes what it
+ * needs.  h0 and dht may be NULL (zeros); dh0 may be NULL (not wanted).
  * dq, dk, dv, dg, dbeta are required and must not alias inputs. */
 gdr_status gdr_backward(const gdr_problem* p, const void* q, const void* k,
                         const void* v, const float* g, const float* beta,
@@ -152,6 +152,41 @@ gdr_status gdr_backward(const gdr_problem* p, const void* q, const void* k,
                         void* dq, void* dk, void* dv, float* dg, float* dbeta,
                         float* dh0, void* ws, size_t ws_bytes,
                         void* hip_stream);
+
+/* Ragged (packed) batches: p->B sequences of different lengths laid end to
+ * end along the token axis, for prefill of a batch of prompts.  cu_seqlens
+ * (device memory, int64, B + 1 entries, 8-byte aligned) holds the row
+ * offsets: sequence b is token rows cu_seqlens[b] .. cu_seqlens[b+1] - 1 of
+ * q, k [rows, Hk, Dk], v, o, dout, dv [rows, Hv, Dv], g [rows, Hv] or
+ * [rows, Hv, Dk], beta [rows, Hv], dq, dk, dg, dbeta likewise; h0, ht, dht,
+ * dh0 stay [B, Hv, Dk, Dv], one state per sequence.  p->T is an upper bound
+ * on every length: workspace sizes (gdr_forward_workspace /
+ * gdr_backward_workspace of the same p) hold ceil(T / C) chunks per
+ * sequence.  The library reads the offsets only on the device, so it cannot
+ * check them: it clamps each length to [0, T] (tokens past T are neither
+ * read nor written) and reads and writes only the rows the offsets name,
+ * which must lie inside the caller's buffers.  A sequence of length 0
+ * passes its state through (ht = h0, dh0 = dht).  Each sequence gives
+ * exactly what a separate call on it would (this is not a feature of the
+ * pages: an interface variant for batches of unequal prompts).
+ * Supported: the forward with GDR_ALGO_SEQUENTIAL (every shape) or
+ * GDR_ALGO_CHUNKED (bf16 io, Dk = Dv = 128, chunk_size 32 or 64, scalar or
+ * channelwise gate); the backward with GDR_ALGO_CHUNKED on that path and a
+ * scalar gate (GDR_SAVE_CHUNKS included).  Other combinations return
+ * GDR_ERR_UNSUPPORTED; AUTO picks the chunked kernels where they are
+ * supported (the forward only when T > 64). */
+gdr_status gdr_forward_varlen(const gdr_problem* p, const int64_t* cu_seqlens,
+                              const void* q, const void* k, const void* v,
+                              const float* g, const float* beta,
+                              const float* h0, void* o, float* ht, void* ws,
+                              size_t ws_bytes, void* hip_stream);
+gdr_status gdr_backward_varlen(const gdr_problem* p, const int64_t* cu_seqlens,
+                               const void* q, const void* k, const void* v,
+                               const float* g, const float* beta,
+                               const float* h0, const void* dout,
+                               const float* dht, void* dq, void* dk, void* dv,
+                               float* dg, float* dbeta, float* dh0, void* ws,
+                               size_t ws_bytes, void* hip_stream);
 
 /* Per-kernel timing for benchmarks (not for use under graph capture).
  * While enabled, every kernel that gdr_forward / gdr_backward launch from the

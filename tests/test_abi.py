@@ -157,3 +157,28 @@ def test_save_chunks_workspace():
         assert fwd_ws(prob(flags=f, algo=2, T=256)) == fwd_ws(prob(flags=1, algo=2, T=256))
     cw = dict(base, chunk_size=64)
     assert fwd_ws(prob(flags=3 | 8, **cw)) == fwd_ws(prob(flags=3, **cw))       # channelwise
+
+
+def call_fwd_varlen(p, cu, ws=None, nws=0):
+    return B.lib().gdr_forward_varlen(ctypes.byref(p), cu, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                                      ws, nws, None)
+
+
+def call_bwd_varlen(p, cu, ws=None, nws=0):
+    return B.lib().gdr_backward_varlen(ctypes.byref(p), cu, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                                       FAKE, FAKE, FAKE, FAKE, FAKE, None, ws, nws, None)
+
+
+def test_varlen_validation():
+    """Ragged batches: offsets required and 8-byte aligned; the sequential
+    VJP and the fp32 chunked path refuse them (all before any launch)."""
+    bf = dict(io_dtype=1, Dk=128, Dv=128, T=256)
+    assert call_fwd_varlen(prob(**bf), None) == 1
+    assert call_bwd_varlen(prob(**bf), None) == 1
+    assert call_fwd_varlen(prob(**bf), FAKE + 4) == 4
+    assert call_bwd_varlen(prob(algo=1, **bf), FAKE) == 3           # sequential VJP
+    assert call_bwd_varlen(prob(algo=2, T=256), FAKE) == 3          # fp32 io, D = 16 chunked
+    assert call_bwd_varlen(prob(algo=0, T=256), FAKE) == 3          # AUTO finds no kernel
+    assert call_bwd_varlen(prob(algo=2, flags=3, **bf), FAKE) == 3  # channelwise VJP
+    assert call_fwd_varlen(prob(algo=2, T=256), FAKE) == 3          # fp32 chunked forward
+    assert call_bwd_varlen(prob(algo=2, **bf), FAKE) == 1           # chunked: workspace missing
