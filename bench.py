@@ -20,6 +20,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -268,6 +270,74 @@ def bench_channelwise(torch, gdr, reps=20):
     return out
 
 
+def ragged_lengths(seed=11, total=B * T, lo=128, hi=2048):
+    """A prefill batch of prompts of unequal length: lengths uniform in
+    [lo, hi] (seeded) until their sum reaches `total` tokens (the last one
+    trimmed)."""
+    rng = np.random.default_rng(seed)
+    out, s = [], 0
+    while s < total:
+        n = int(min(rng.integers(lo, hi + 1), total - s))
+        out.append(n)
+        s += n
+    return out
+
+
+def bench_ragged(torch, gdr, reps=10):
+    """Fwd + VJP (forward saving its chunks) of a ragged batch with the same
+    16,384 tokens as the headline workload (Hk=16, Hv=32, D=128, bf16,
+    C=64, zero h0), against the same sequences zero-padded to the longest
+    one as a uniform batch (gdr_forward / gdr_backward)."""
+    from gated_delta_rule_54_amd.synth import make_inputs
+    lens = ragged_lengths()
+    n, rows, tmax = len(lens), sum(lens), max(lens)
+    x = make_inputs(8, 1, rows, HK, HV, D, D, io_dtype="bf16")
+    dev = torch.device("cuda")
+    t = {k: (None if a is None else torch.from_numpy(a).to(dev)) for k, a in x.items()}
+    for k in ("q", "k", "v", "do"):
+        t[k] = t[k].to(torch.bfloat16)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int64, device=dev)
+    kw = dict(algo="chunked", chunk_size=C, out_dtype=torch.bfloat16)
+
+    def ragged():
+        _, _, sv = gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], None, save_for_backward=True,
+                                   cu_seqlens=cu, max_seqlen=tmax, **kw)
+        gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], None, t["do"], saved=sv, cu_seqlens=cu,
+                         max_seqlen=tmax, **kw)
+
+    pad = {}
+    for k, a in t.items():
+        if a is None:
+            continue
+        z = torch.zeros((n, tmax) + tuple(a.shape[2:]), dtype=a.dtype, device=dev)
+        for i in range(n):
+            z[i, :lens[i]] = a[0, int(cu[i]):int(cu[i + 1])]
+        pad[k] = z
+
+    def padded():
+        _, _, sv = gdr.gdr_forward(pad["q"], pad["k"], pad["v"], pad["g"], pad["beta"], None,
+                                   save_for_backward=True, **kw)
+        gdr.gdr_backward(pad["q"], pad["k"], pad["v"], pad["g"], pad["beta"], None, pad["do"], saved=sv, **kw)
+
+    out = {}
+    for name, fn in (("ragged", ragged), ("padded", padded)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(rows / (ms * 1e-3), 1)}
+    out["config"] = (f"{n} sequences, lengths U[128, 2048] (seed 11), {rows} tokens, longest {tmax}; "
+                     f"Hk={HK} Hv={HV} D={D} bf16, C={C}, fwd saving chunks + VJP; padded = the same "
+                     f"sequences zero-padded to {tmax} as a uniform batch")
+    return out
+
+
 def cpu_baseline(min_seconds=10.0, max_groups=32):
     """The fp64 oracle (forward + VJP) on (b, k-head) groups of the
     full-length workload (each group = the 2 v-heads sharing a k-head), run
@@ -397,6 +467,7 @@ def main():
                           "note": "same step without GDR_SAVE_CHUNKS: the VJP recomputes the chunk "
                                   "images and chunk states"}}
     line["variants"]["channelwise_prefill"] = bench_channelwise(torch, gdr)
+    line["variants"]["ragged_prefill"] = bench_ragged(torch, gdr)
     if not args.no_decode:
         line["decode"] = bench_decode(torch, gdr)
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()
