@@ -375,6 +375,23 @@ def _cpu_model():
     return None
 
 
+def variants(torch, gdr, args, tokens):
+    """The other measured legs: the same step with fused gates and with the
+    stateless VJP, the channelwise prefill and the ragged prefill."""
+    fms, _, _ = bench_chunked(torch, gdr, args.steps, args.warmup, fused_gates=True)
+    sms, _, skern = bench_chunked(torch, gdr, args.steps, args.warmup, saved=False)
+    return {
+        "fused_gates": {"ms_per_step": round(fms, 4), "tokens_per_s": round(tokens / (fms * 1e-3), 1),
+                        "note": "same step with g, beta passed as pre-activations"},
+        "stateless_vjp": {"ms_per_step": round(sms, 4), "tokens_per_s": round(tokens / (sms * 1e-3), 1),
+                          "kernels_avg_us": {k: round(1000 * v[0] / v[1], 2) for k, v in skern.items()},
+                          "note": "same step without GDR_SAVE_CHUNKS: the VJP recomputes the chunk "
+                                  "images and chunk states"},
+        "channelwise_prefill": bench_channelwise(torch, gdr),
+        "ragged_prefill": bench_ragged(torch, gdr),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -382,6 +399,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="time only the headline step (no fused-gate, stateless, channelwise or ragged legs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy this many MiB once with a plain elementwise kernel "
                          "(reference for HBM byte counters)")
@@ -431,6 +450,12 @@ def main():
     roof["bytes_per_launch"] = None if by is None else int(by * th)
     roof["flops_per_launch"] = None if f is None else int(f * th)
     roof["kernel"] = dom
+    grids = {"chunk_prep": ((T // C, HV, B), 256), "chunk_fwd_save": ((2 * HV * B, 1, 1), 320),
+             "chunk_fwd": ((2 * HV * B, 1, 1), 320), "chunk_states": ((2 * HV * B, 1, 1), 320),
+             "chunk_dh": ((2 * HV * B, 1, 1), 320), "chunk_grad": ((T // C, HK, B), 512)}
+    if dom in grids:  # to find the same launches in a rocprofv3 kernel trace
+        (gx, gy, gz), th_ = grids[dom]
+        roof["launch"] = f"{gx} x {gy} x {gz} workgroups x {th_} threads"
     roof["traffic"] = stored_traffic(dom)
     canon = canonical_flops_per_token_head() * th
     line = {
@@ -457,17 +482,10 @@ def main():
                  "wall_ms_per_step": round(1000 * wall / args.steps, 3)},
         "kernels": per_kernel,
     }
-    fms, _, _ = bench_chunked(torch, gdr, args.steps, args.warmup, fused_gates=True)
-    sms, _, skern = bench_chunked(torch, gdr, args.steps, args.warmup, saved=False)
-    line["variants"] = {
-        "fused_gates": {"ms_per_step": round(fms, 4), "tokens_per_s": round(tokens / (fms * 1e-3), 1),
-                        "note": "same step with g, beta passed as pre-activations"},
-        "stateless_vjp": {"ms_per_step": round(sms, 4), "tokens_per_s": round(tokens / (sms * 1e-3), 1),
-                          "kernels_avg_us": {k: round(1000 * v[0] / v[1], 2) for k, v in skern.items()},
-                          "note": "same step without GDR_SAVE_CHUNKS: the VJP recomputes the chunk "
-                                  "images and chunk states"}}
-    line["variants"]["channelwise_prefill"] = bench_channelwise(torch, gdr)
-    line["variants"]["ragged_prefill"] = bench_ragged(torch, gdr)
+    if args.no_variants:
+        line["variants"] = None
+    else:
+        line["variants"] = variants(torch, gdr, args, tokens)
     if not args.no_decode:
         line["decode"] = bench_decode(torch, gdr)
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()

@@ -38,8 +38,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 # demangled kernel name pattern -> library timing name
 KERNELS = [
+    (r"cwprep16_kernel", "chunk_prep_cw"),
+    (r"cwchain16_kernel", "chunk_fwd_cw"),
     (r"prep16_kernel", "chunk_prep"),
     (r"chain16_kernel<\d+, [^,]+, true, false>", "chunk_fwd"),
+    (r"chain16_kernel<\d+, [^,]+, true, true>", "chunk_fwd_save"),
     (r"chain16_kernel<\d+, [^,]+, false, true>", "chunk_states"),
     (r"dh16_kernel", "chunk_dh"),
     (r"grad16_kernel", "chunk_grad"),
@@ -148,6 +151,21 @@ def trace(args):
             short = short[:87] + "..."
         lines.append(f"| `{short}` | {label(name) or ''} | {calls} | {tot:.1f} | {avg:.2f} | "
                      f"{pct:.1f} |")
+    # the same launches split by grid (workgroups), so a workload's launches
+    # can be told apart from other shapes of the same kernel in the command
+    acc = collections.defaultdict(lambda: [0, 0.0])
+    for name, gx, gy, gz, wx, n, tot in con.execute(
+            "select name, grid_x / workgroup_x, grid_y, grid_z, workgroup_x, count(*), sum(duration) "
+            "from kernels group by name, grid_x, grid_y, grid_z, workgroup_x"):
+        lab = label(name)
+        if lab is not None:
+            a = acc[(lab, int(gx), gy, gz, wx)]
+            a[0] += n
+            a[1] += tot
+    lines += ["", "Library kernels by launch grid (all template instances of a kernel together):", "",
+              "| library name | grid (workgroups) | threads | calls | avg us |", "|---|---|---:|---:|---:|"]
+    for (lab, gx, gy, gz, wx), (n, tot) in sorted(acc.items(), key=lambda kv: (kv[0][0], -kv[1][0])):
+        lines.append(f"| {lab} | {gx} x {gy} x {gz} | {wx} | {n} | {tot / n / 1000.0:.2f} |")
     lines += ["", f"Kernel sources digest: `{src_digest()}`", ""]
     text = "\n".join(lines)
     if args.md:
