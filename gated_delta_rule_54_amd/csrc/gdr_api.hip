@@ -69,11 +69,11 @@ constexpr bool kChunkedBackward = true;
 gdr_status resolve_algo(const gdr_problem* p, bool backward, int* algo, bool ragged = false) {
   // channelwise gates: chunked forward on the fp16 matrix-core path only
   // (bf16 io, Dk = 128, C >= 32); their VJP runs sequentially.  Ragged
-  // batches: the chunked kernels on that path, and the sequential forward.
+  // batches: the chunked kernels on that path, and the sequential ones.
   const bool f16 = gdr::chunk_uses_f16(shape_of(p), chunk_of(p));
   const bool chunk_ok = (p->flags & GDR_CHANNELWISE) ? !backward && f16
                                                      : (!backward || kChunkedBackward) && (!ragged || f16);
-  const bool seq_ok = !(ragged && backward);
+  const bool seq_ok = true;
   if (p->algo == GDR_ALGO_CHUNKED) {
     if (!chunk_ok) return GDR_ERR_UNSUPPORTED;
     *algo = GDR_ALGO_CHUNKED;
@@ -240,10 +240,11 @@ gdr_status backward_impl(const gdr_problem* p, const int64_t* cu, bool ragged, c
   if (ws_bytes < w.total) return GDR_ERR_WORKSPACE_TOO_SMALL;
   gdr::SeqBwdArgs a{q, k, v, dout, g, beta, h0, dht, dv, dh0,
                     at<float>(ws, w.ckpt), at<float>(ws, w.scratch), at<float>(ws, w.pdq),
-                    at<float>(ws, w.pdk), at<float>(ws, w.pdb), at<float>(ws, w.pdg)};
+                    at<float>(ws, w.pdk), at<float>(ws, w.pdb), at<float>(ws, w.pdg), cu};
   hipError_t e = gdr::launch_seq_bwd(s, a, stream);
   if (e != hipSuccess) return hip_fail(e);
-  gdr::EpiArgs ea{q, k, a.part_dq, a.part_dk, a.part_db, a.part_dg, gdr::seq_bwd_slices(s), dq, dk, dbeta, dg, g, beta};
+  gdr::EpiArgs ea{q, k, a.part_dq, a.part_dk, a.part_db, a.part_dg, gdr::seq_bwd_slices(s), dq, dk, dbeta, dg, g, beta,
+                  cu};
   e = gdr::launch_bwd_epilogue(s, ea, stream);
   return e == hipSuccess ? GDR_OK : hip_fail(e);
 }

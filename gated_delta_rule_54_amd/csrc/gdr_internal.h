@@ -52,6 +52,7 @@ struct SeqBwdArgs {
   float* part_dk;    // [NS][B][T][Hv][D]
   float* part_db;    // [NS][B][T][Hv]
   float* part_dg;    // [NS][B][T][Hv] or [NS][B][T][Hv][D]
+  const int64_t* cu; // ragged batch row offsets [B + 1], or null (partials stay [B][T])
 };
 hipError_t launch_seq_bwd(const Shape& s, const SeqBwdArgs& a, hipStream_t st);
 
@@ -65,6 +66,7 @@ struct EpiArgs {
   void *dq, *dk;
   float *dbeta, *dg;
   const float *g, *beta;  // gate inputs (pre-activations with fused gates)
+  const int64_t* cu;      // ragged batch row offsets [B + 1], or null
 };
 hipError_t launch_bwd_epilogue(const Shape& s, const EpiArgs& a, hipStream_t st);
 

@@ -231,6 +231,15 @@ __global__ __launch_bounds__(64) void seq_bwd_kernel(Dims d, SeqBwdArgs a, int n
     return base + ((idx * RPL + m) * 64 + lane) * 4;
   };
 
+  // sequence b: token rows tb .. tb + len - 1 (ragged: offsets cu, lengths
+  // clamped to [0, T]); partial sums stay indexed by (b, t) as for B x T
+  int64_t tb = b * d.T, slen = d.T;
+  if (a.cu) {
+    tb = a.cu[b];
+    slen = a.cu[b + 1] - tb;
+    slen = slen < 0 ? 0 : (slen > d.T ? d.T : slen);
+  }
+  const int nckb = static_cast<int>((slen + kSeqSeg - 1) / kSeqSeg);
   float h[RPL][4];
 #pragma unroll
   for (int m = 0; m < RPL; ++m) {
@@ -238,13 +247,13 @@ __global__ __launch_bounds__(64) void seq_bwd_kernel(Dims d, SeqBwdArgs a, int n
     else h[m][0] = h[m][1] = h[m][2] = h[m][3] = 0.f;
   }
   // phase 1: checkpoints
-  for (int64_t t = 0; t < d.T; ++t) {
+  for (int64_t t = 0; t < slen; ++t) {
     if (t % kSeqSeg == 0) {
 #pragma unroll
       for (int m = 0; m < RPL; ++m) st4<float>(lane_ptr(ck, t / kSeqSeg, m), h[m]);
     }
     Tok<RPL, CW> x;
-    load_tok<D, L, TI, CW, false, false>(x, d, a.q, a.k, a.v, nullptr, a.g, a.beta, b * d.T + t, kh, hv, i0, j0);
+    load_tok<D, L, TI, CW, false, false>(x, d, a.q, a.k, a.v, nullptr, a.g, a.beta, tb + t, kh, hv, i0, j0);
     float u[4], o[4];
     fwd_step<L, CW, false>(h, x, d.l2, u, o);
   }
@@ -256,24 +265,24 @@ __global__ __launch_bounds__(64) void seq_bwd_kernel(Dims d, SeqBwdArgs a, int n
     if (a.dht) ld4<float>(a.dht + hbase + m * D, dH[m]);
     else dH[m][0] = dH[m][1] = dH[m][2] = dH[m][3] = 0.f;
   }
-  for (int c = nck - 1; c >= 0; --c) {
+  for (int c = nckb - 1; c >= 0; --c) {
     const int64_t t0 = static_cast<int64_t>(c) * kSeqSeg;
-    const int len = static_cast<int>(d.T - t0 < kSeqSeg ? d.T - t0 : kSeqSeg);
+    const int len = static_cast<int>(slen - t0 < kSeqSeg ? slen - t0 : kSeqSeg);
 #pragma unroll
     for (int m = 0; m < RPL; ++m) ld4<float>(lane_ptr(ck, c, m), h[m]);
     for (int tau = 0; tau < len; ++tau) {
 #pragma unroll
       for (int m = 0; m < RPL; ++m) st4<float>(lane_ptr(sc, tau, m), h[m]);
       Tok<RPL, CW> x;
-      load_tok<D, L, TI, CW, false, false>(x, d, a.q, a.k, a.v, nullptr, a.g, a.beta, b * d.T + t0 + tau, kh, hv,
-                                           i0, j0);
+      load_tok<D, L, TI, CW, false, false>(x, d, a.q, a.k, a.v, nullptr, a.g, a.beta, tb + t0 + tau, kh, hv, i0,
+                                           j0);
       float u[4], o[4];
       fwd_step<L, CW, false>(h, x, d.l2, u, o);
     }
     for (int tau = len - 1; tau >= 0; --tau) {
       const int64_t t = t0 + tau;
       Tok<RPL, CW> x;
-      load_tok<D, L, TI, CW, true, true>(x, d, a.q, a.k, a.v, a.dout, a.g, a.beta, b * d.T + t, kh, hv, i0, j0);
+      load_tok<D, L, TI, CW, true, true>(x, d, a.q, a.k, a.v, a.dout, a.g, a.beta, tb + t, kh, hv, i0, j0);
       float Dm[RPL][4];
 #pragma unroll
       for (int m = 0; m < RPL; ++m) {
@@ -336,8 +345,8 @@ __global__ __launch_bounds__(64) void seq_bwd_kernel(Dims d, SeqBwdArgs a, int n
       dbs = xsum<1, L::NCG>(dbs);
       if constexpr (!CW) dgs = xsum<1, 64>(dgs);
 
-      const int64_t row = (b * d.T + t) * d.Hv + hv;        // (b, t, hv)
-      const int64_t prow = static_cast<int64_t>(slice) * d.B * d.T * d.Hv + row;
+      const int64_t row = (tb + t) * d.Hv + hv;                    // token row, v-head
+      const int64_t prow = (static_cast<int64_t>(slice) * d.B * d.T + b * d.T + t) * d.Hv + hv;  // (slice, b, t, hv)
       if (cg == 0) {
         float* pq = a.part_dq + prow * D + i0;
         float* pk = a.part_dk + prow * D + i0;
@@ -375,9 +384,16 @@ template <int D, typename TI, typename TO, bool CW>
 __global__ __launch_bounds__(64) void epilogue_kernel(Dims d, EpiArgs a) {
   constexpr int EPT = (D + 63) / 64;
   const int lane = threadIdx.x;
-  const int64_t id = blockIdx.x;          // (b*T + t)*Hk + kh
-  const int kh = static_cast<int>(id % d.Hk);
-  const int64_t bt = id / d.Hk;
+  const int64_t pid = blockIdx.x;         // (b*T + t)*Hk + kh
+  const int kh = static_cast<int>(pid % d.Hk);
+  const int64_t bt = pid / d.Hk;
+  int64_t io = bt;                        // token row (ragged: cu[b] + t)
+  if (a.cu) {
+    const int64_t b = bt / d.T, t = bt % d.T, s0 = a.cu[b];
+    if (t >= a.cu[b + 1] - s0) return;   // past the end of sequence b
+    io = s0 + t;
+  }
+  const int64_t id = io * d.Hk + kh;
   const int grp = d.Hv / d.Hk;
   const int64_t pstride = d.B * d.T * d.Hv;  // rows per slice
   for (int which = 0; which < 2; ++which) {
@@ -416,23 +432,24 @@ __global__ __launch_bounds__(64) void epilogue_kernel(Dims d, EpiArgs a) {
   }
   // dbeta, dg for the group's v-heads
   for (int gi = 0; gi < grp; ++gi) {
-    const int64_t row = bt * d.Hv + static_cast<int64_t>(kh) * grp + gi;
+    const int64_t row = bt * d.Hv + static_cast<int64_t>(kh) * grp + gi;  // partials
+    const int64_t orow = io * d.Hv + static_cast<int64_t>(kh) * grp + gi;  // outputs, gates
     if (a.part_db && lane == 0) {
       float s = 0.f;
       for (int sl = 0; sl < a.nslices; ++sl) s += a.part_db[sl * pstride + row];
-      a.dbeta[row] = d.fg ? s * fg_dbeta(a.beta[row]) : s;
+      a.dbeta[orow] = d.fg ? s * fg_dbeta(a.beta[orow]) : s;
     }
     if (a.part_dg) {
       if constexpr (CW) {
         for (int i = lane; i < D; i += 64) {
           float s = 0.f;
           for (int sl = 0; sl < a.nslices; ++sl) s += a.part_dg[(sl * pstride + row) * D + i];
-          a.dg[row * D + i] = d.fg ? s * fg_dlog_alpha(a.g[row * D + i]) : s;
+          a.dg[orow * D + i] = d.fg ? s * fg_dlog_alpha(a.g[orow * D + i]) : s;
         }
       } else if (lane == 0) {
         float s = 0.f;
         for (int sl = 0; sl < a.nslices; ++sl) s += a.part_dg[sl * pstride + row];
-        a.dg[row] = d.fg ? s * fg_dlog_alpha(a.g[row]) : s;
+        a.dg[orow] = d.fg ? s * fg_dlog_alpha(a.g[orow]) : s;
       }
     }
   }
@@ -478,9 +495,16 @@ __global__ __launch_bounds__(256) void epilogue128_kernel(Dims d, EpiArgs a) {
   const int64_t rows = d.B * d.T * d.Hk;
   if (item >= 2 * rows) return;  // whole 16-lane groups leave together
   const int which = static_cast<int>(item & 1);
-  const int64_t id = item >> 1;  // (b*T + t)*Hk + kh
-  const int kh = static_cast<int>(id % d.Hk);
-  const int64_t bt = id / d.Hk;
+  const int64_t pid = item >> 1;  // (b*T + t)*Hk + kh
+  const int kh = static_cast<int>(pid % d.Hk);
+  const int64_t bt = pid / d.Hk;
+  int64_t io = bt;                // token row (ragged: cu[b] + t)
+  if (a.cu) {
+    const int64_t b = bt / d.T, t = bt % d.T, s0 = a.cu[b];
+    if (t >= a.cu[b + 1] - s0) return;  // past the end of sequence b (the whole 16-lane group)
+    io = s0 + t;
+  }
+  const int64_t id = io * d.Hk + kh;
   const int grp = d.Hv / d.Hk;
   const int64_t pstride = d.B * d.T * d.Hv;
   const int i = 8 * sub;
@@ -514,11 +538,12 @@ __global__ __launch_bounds__(256) void epilogue128_kernel(Dims d, EpiArgs a) {
   st8<TO>(static_cast<TO*>(which == 0 ? a.dq : a.dk) + id * D + i, s);
   if (which != 0) return;
   for (int gi = 0; gi < grp; ++gi) {
-    const int64_t row = bt * d.Hv + static_cast<int64_t>(kh) * grp + gi;
+    const int64_t row = bt * d.Hv + static_cast<int64_t>(kh) * grp + gi;  // partials
+    const int64_t orow = io * d.Hv + static_cast<int64_t>(kh) * grp + gi;  // outputs, gates
     if (a.part_db && sub == 0) {
       float sb = 0.f;
       for (int sl = 0; sl < a.nslices; ++sl) sb += a.part_db[sl * pstride + row];
-      a.dbeta[row] = d.fg ? sb * fg_dbeta(a.beta[row]) : sb;
+      a.dbeta[orow] = d.fg ? sb * fg_dbeta(a.beta[orow]) : sb;
     }
     if (a.part_dg) {
       if constexpr (CW) {
@@ -531,13 +556,13 @@ __global__ __launch_bounds__(256) void epilogue128_kernel(Dims d, EpiArgs a) {
         }
         if (d.fg) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) gsum[e] *= fg_dlog_alpha(a.g[row * D + i + e]);
+          for (int e = 0; e < 8; ++e) gsum[e] *= fg_dlog_alpha(a.g[orow * D + i + e]);
         }
-        st8<float>(a.dg + row * D + i, gsum);
+        st8<float>(a.dg + orow * D + i, gsum);
       } else if (sub == 0) {
         float sg = 0.f;
         for (int sl = 0; sl < a.nslices; ++sl) sg += a.part_dg[sl * pstride + row];
-        a.dg[row] = d.fg ? sg * fg_dlog_alpha(a.g[row]) : sg;
+        a.dg[orow] = d.fg ? sg * fg_dlog_alpha(a.g[orow]) : sg;
       }
     }
   }

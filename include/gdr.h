@@ -169,12 +169,12 @@ gdr_status gdr_backward(const gdr_problem* p, const void* q, const void* k,
  * passes its state through (ht = h0, dh0 = dht).  Each sequence gives
  * exactly what a separate call on it would (this is not a feature of the
  * pages: an interface variant for batches of unequal prompts).
- * Supported: the forward with GDR_ALGO_SEQUENTIAL (every shape) or
- * GDR_ALGO_CHUNKED (bf16 io, Dk = Dv = 128, chunk_size 32 or 64, scalar or
- * channelwise gate); the backward with GDR_ALGO_CHUNKED on that path and a
- * scalar gate (GDR_SAVE_CHUNKS included).  Other combinations return
- * GDR_ERR_UNSUPPORTED; AUTO picks the chunked kernels where they are
- * supported (the forward only when T > 64). */
+ * Supported: GDR_ALGO_SEQUENTIAL (every shape, both passes) and
+ * GDR_ALGO_CHUNKED on its fp16 path (bf16 io, Dk = Dv = 128, chunk_size 32
+ * or 64; the forward with a scalar or channelwise gate, the backward with a
+ * scalar gate, GDR_SAVE_CHUNKS included).  The fp32 chunked path (fp32 io
+ * or Dk = 16) returns GDR_ERR_UNSUPPORTED; AUTO picks as for gdr_forward /
+ * gdr_backward. */
 gdr_status gdr_forward_varlen(const gdr_problem* p, const int64_t* cu_seqlens,
                               const void* q, const void* k, const void* v,
                               const float* g, const float* beta,

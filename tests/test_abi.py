@@ -170,15 +170,15 @@ def call_bwd_varlen(p, cu, ws=None, nws=0):
 
 
 def test_varlen_validation():
-    """Ragged batches: offsets required and 8-byte aligned; the sequential
-    VJP and the fp32 chunked path refuse them (all before any launch)."""
+    """Ragged batches: offsets required and 8-byte aligned; the fp32 chunked
+    path refuses them (all before any launch)."""
     bf = dict(io_dtype=1, Dk=128, Dv=128, T=256)
     assert call_fwd_varlen(prob(**bf), None) == 1
     assert call_bwd_varlen(prob(**bf), None) == 1
     assert call_fwd_varlen(prob(**bf), FAKE + 4) == 4
-    assert call_bwd_varlen(prob(algo=1, **bf), FAKE) == 3           # sequential VJP
     assert call_bwd_varlen(prob(algo=2, T=256), FAKE) == 3          # fp32 io, D = 16 chunked
-    assert call_bwd_varlen(prob(algo=0, T=256), FAKE) == 3          # AUTO finds no kernel
-    assert call_bwd_varlen(prob(algo=2, flags=3, **bf), FAKE) == 3  # channelwise VJP
+    assert call_bwd_varlen(prob(algo=2, flags=3, **bf), FAKE) == 3  # channelwise chunked VJP
     assert call_fwd_varlen(prob(algo=2, T=256), FAKE) == 3          # fp32 chunked forward
     assert call_bwd_varlen(prob(algo=2, **bf), FAKE) == 1           # chunked: workspace missing
+    assert call_bwd_varlen(prob(algo=1, **bf), FAKE) == 1           # sequential: workspace missing
+    assert call_bwd_varlen(prob(algo=0, T=256), FAKE) == 1          # AUTO -> sequential

@@ -120,3 +120,11 @@ def test_ragged_equal_lengths_match_uniform_batch():
     assert np.array_equal(host(h0), host(h1))
     for a, b_ in zip(g0, g1):
         assert np.array_equal(host(a).reshape(host(b_).shape), host(b_))
+
+
+@pytest.mark.parametrize("io,D,cw", [("f32", 16, False), ("f32", 16, True), ("bf16", 128, False),
+                                     ("bf16", 128, True)])
+def test_ragged_sequential_vjp(io, D, cw):
+    """The sequential VJP (and its epilogue) on a ragged batch: lengths 0,
+    20, 1, 37 (segments of 16 tokens, ragged), both gate modes."""
+    run_and_check([0, 20, 1, 37], io, "sequential", cw=cw, seed=23 + D + cw, D=D)
