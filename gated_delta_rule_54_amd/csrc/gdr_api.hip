@@ -67,11 +67,11 @@ constexpr bool kChunkedBackward = true;
 
 // SEQUENTIAL or CHUNKED for this call; CHUNKED needs a scalar gate.
 gdr_status resolve_algo(const gdr_problem* p, bool backward, int* algo, bool ragged = false) {
-  // channelwise gates: chunked forward on the fp16 matrix-core path only
-  // (bf16 io, Dk = 128, C >= 32); their VJP runs sequentially.  Ragged
-  // batches: the chunked kernels on that path, and the sequential ones.
+  // channelwise gates: chunked kernels on the fp16 matrix-core path only
+  // (bf16 io, Dk = 128, C >= 32).  Ragged batches: the chunked kernels on
+  // that path, and the sequential ones.
   const bool f16 = gdr::chunk_uses_f16(shape_of(p), chunk_of(p));
-  const bool chunk_ok = (p->flags & GDR_CHANNELWISE) ? !backward && f16
+  const bool chunk_ok = (p->flags & GDR_CHANNELWISE) ? f16
                                                      : (!backward || kChunkedBackward) && (!ragged || f16);
   const bool seq_ok = true;
   if (p->algo == GDR_ALGO_CHUNKED) {

@@ -1899,13 +1899,14 @@ __global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
   write_tile<C, UK, NTH>(kim + 2 * IM::KN, [&](int r, int u) { return scaled(Ks, r, u, true); });
 }
 
-// Channelwise forward chain: as chain16 with outputs, using the scaled key
-// rows of the channelwise images and decaying H's rows by e^{G_C}:
+// Channelwise forward chain: as chain16, using the scaled key rows of the
+// channelwise images and decaying H's rows by e^{G_C}:
 //   Y = Kg H, Z = Qg H, U = T (beta (V - Y)), O = Z + P U,
 //   H = diag(e^{G_C}) H + Kl^T U.
 // The chunk's o leaves the compute waves as 2-byte stores (their LDS share
-// holds the three key tiles).
-template <int C, typename TO>
+// holds the three key tiles).  STORE_H: every chunk's entry state is stored
+// for the VJP (fp16, chained-fragment order); WRITE_O false: no outputs.
+template <int C, typename TO, bool WRITE_O, bool STORE_H>
 __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
   using IM = ImgCW<C>;
   constexpr int NT = C / 16, LDC = IM::LDC;
@@ -1959,6 +1960,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
 
   // ---- compute waves
   const int jcol = p.half * BV + 16 * w + c16;
+  const int wg = p.half * NCW + w;  // column group of the chunk-state layout
   const int64_t hbase = (p.b * a.Hv + p.hv) * DK * DK + jcol;
   const uint32_t voffo = 4 * g * rowo + (p.hv * DK + jcol) * static_cast<uint32_t>(sizeof(TO));
   f32x4 h[NTK];
@@ -1973,7 +1975,9 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
   lds_barrier();
   f32x4 o[NT];
   auto step = [&](int c, const char* cur) __attribute__((always_inline)) {
-    if (c > 0) store_strip_buf<TO, NT>(seq_rsrc(a.o, sizeof(TO), c - 1, rowo), voffo, rowo, o);
+    if constexpr (WRITE_O) {
+      if (c > 0) store_strip_buf<TO, NT>(seq_rsrc(a.o, sizeof(TO), c - 1, rowo), voffo, rowo, o);
+    }
     const float* bet = reinterpret_cast<const float*>(cur);
     const float* gC = bet + C;
     const _Float16* Tm = reinterpret_cast<const _Float16*>(cur + IM::GT);
@@ -1985,11 +1989,17 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
 
     f16x8 hf[NTK / 2];
     chain_frags<NTK>(hf, h);
+    if constexpr (STORE_H) {  // entry state of chunk c
+      const rsrc_t hr = make_rsrc(a.hst + ((p.b * a.Hv + p.hv) * a.NC + c) * static_cast<int64_t>(DK * DK), DK * DK * 2);
+#pragma unroll
+      for (int kb = 0; kb < NTK / 2; ++kb)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hf[kb]), hr, frag_off(wg, kb), 0, 0);
+    }
     f32x4 y[NT], u[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) y[t] = u[t] = o[t] = zero4();
     mma_chain_rows<NT, NTK>(y, Kg, LDK, hf);
-    mma_chain_rows<NT, NTK>(o, Qg, LDK, hf);
+    if constexpr (WRITE_O) mma_chain_rows<NT, NTK>(o, Qg, LDK, hf);
     f32x4 rhs[NT];
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr) {
@@ -2003,7 +2013,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
     chain_frags<NT>(bf, rhs);
     mma_chain_rows<NT, NT>(u, Tm, LDC, bf);
     chain_frags<NT>(bf, u);
-    mma_chain_rows<NT, NT>(o, Pm, LDC, bf);
+    if constexpr (WRITE_O) mma_chain_rows<NT, NT>(o, Pm, LDC, bf);
 #pragma unroll
     for (int ti = 0; ti < NTK; ++ti) {
       const f32x4 dec = *reinterpret_cast<const f32x4*>(gC + 16 * ti + 4 * g);
@@ -2017,12 +2027,146 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
     step(c, bufA);
     if (c + 1 < nc) step(c + 1, bufB);
   }
-  store_strip_buf<TO, NT>(seq_rsrc(a.o, sizeof(TO), nc - 1, rowo), voffo, rowo, o);
+  if constexpr (WRITE_O) store_strip_buf<TO, NT>(seq_rsrc(a.o, sizeof(TO), nc - 1, rowo), voffo, rowo, o);
   if (a.ht) {
 #pragma unroll
     for (int ti = 0; ti < NTK; ++ti)
 #pragma unroll
       for (int e = 0; e < 4; ++e) a.ht[hbase + (16 * ti + 4 * g + e) * DK] = h[ti][e];
+  }
+}
+
+// Channelwise reverse chain: carries dH backwards over the chunks with the
+// channelwise images and stores every chunk's end gradient for the per-chunk
+// VJP; writes dh0.  Per chunk and compute wave:
+//   dU = Kl dH + P^T dO,  dRHS = T^T dU,
+//   dH = diag(e^{G_C}) dH + Qg^T dO - Kg^T (beta dRHS).
+// (dv and the other gradients come from the per-chunk VJP.)
+template <int C>
+__global__ __launch_bounds__(64 * (NCW + 1)) void cwdh16_kernel(K16 a) {
+  using IM = ImgCW<C>;
+  constexpr int NT = C / 16, LDC = IM::LDC;
+  constexpr uint32_t CB = IM::CHK, KB = IM::KEY, VB = C * BV * 2;
+  __shared__ __align__(16) char bufA[CB + KB + VB];
+  __shared__ __align__(16) char bufB[CB + KB + VB];
+
+  const int w = wave_id(), lane = lane_id(), g = lane >> 4, c16 = lane & 15;
+  const ChainPos p = chain_pos(a);
+  const SeqSpan sp = seq_span(a, p.b);
+  const int nc = static_cast<int>((sp.len + C - 1) / C);
+  if (nc == 0) {  // empty sequence of a ragged batch: the gradient passes through
+    if (w < NCW && a.dh0) {
+      const int64_t base = (p.b * a.Hv + p.hv) * DK * DK + p.half * BV + 16 * w + c16;
+      for (int i = 0; i < DK; ++i) a.dh0[base + i * DK] = a.dht ? a.dht[base + i * DK] : 0.f;
+    }
+    return;
+  }
+  auto rows_of = [&](int c) { return static_cast<int>(sp.len - static_cast<int64_t>(c) * C < C ? sp.len - static_cast<int64_t>(c) * C : C); };
+  const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
+
+  if (w == NCW) {  // ---- producer wave: chunks nc-1, nc-2, ...
+    const char* kim0 = a.kimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::KEY);
+    const char* cim0 = a.cimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::CHK);
+    const uint32_t colv = (p.hv * DK + p.half * BV) * 2;
+    auto stage = [&](int c, char* buf) {
+      const char* p0 = reinterpret_cast<const char*>(a.dout) + (sp.t0 + static_cast<int64_t>(c) * C) * rowv;
+      dma<CB, 64>(make_rsrc(cim0 + c * static_cast<int64_t>(IM::CHK), CB), 0, buf, lane, 0);
+      dma<KB, 64>(make_rsrc(kim0 + c * static_cast<int64_t>(IM::KEY), KB), 0, buf + CB, lane, 0);
+      dma_rows<C, BV * 2, 64>(make_rsrc(p0, static_cast<uint32_t>(rows_of(c)) * rowv), rowv, colv, rows_of(c),
+                              buf + CB + KB, lane, 0);
+    };
+    stage(nc - 1, bufA);
+    wait_all();
+    lds_barrier();
+    for (int i = 0; i < nc; i += 2) {
+      if (nc - 2 - i >= 0) stage(nc - 2 - i, bufB);
+      wait_all();
+      lds_barrier();
+      if (i + 1 < nc) {
+        if (nc - 3 - i >= 0) stage(nc - 3 - i, bufA);
+        wait_all();
+        lds_barrier();
+      }
+    }
+    return;
+  }
+
+  // ---- compute waves
+  const int jcol = p.half * BV + 16 * w + c16;
+  const int wg = p.half * NCW + w;
+  const int64_t hbase = (p.b * a.Hv + p.hv) * DK * DK + jcol;
+  f32x4 dh[NTK];
+#pragma unroll
+  for (int ti = 0; ti < NTK; ++ti) {
+    dh[ti] = zero4();
+    if (a.dht) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dh[ti][e] = a.dht[hbase + (16 * ti + 4 * g + e) * DK];
+    }
+  }
+  lds_barrier();
+
+  auto step = [&](int c, const char* cur) __attribute__((always_inline)) {
+    const float* bet = reinterpret_cast<const float*>(cur);
+    const float* gC = bet + C;
+    const _Float16* Tm = reinterpret_cast<const _Float16*>(cur + IM::GT);
+    const _Float16* Pm = Tm + C * LDC;
+    const _Float16* Kg = reinterpret_cast<const _Float16*>(cur + CB);
+    const _Float16* Qg = Kg + C * LDK;
+    const _Float16* Kl = Qg + C * LDK;
+    const uint16_t* Ds = reinterpret_cast<const uint16_t*>(cur + CB + KB);
+
+    f16x8 hf[NTK / 2];
+    chain_frags<NTK>(hf, dh);
+    {  // gradient at this chunk's end
+      const rsrc_t hr = make_rsrc(a.dhst + ((p.b * a.Hv + p.hv) * a.NC + c) * static_cast<int64_t>(DK * DK), DK * DK * 2);
+#pragma unroll
+      for (int kb = 0; kb < NTK / 2; ++kb)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hf[kb]), hr, frag_off(wg, kb), 0, 0);
+    }
+    f32x4 du[NT], dr[NT], dof[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) du[t] = dr[t] = zero4();
+    mma_chain_rows<NT, NTK>(du, Kl, LDK, hf);
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) {
+      float x[4];
+      tile_col4_bf16(x, Ds, BV, 16 * tr + 4 * g, 16 * w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dof[tr][e] = x[e];
+    }
+    f16x8 bf[NT / 2], bo[NT / 2];
+    chain_frags<NT>(bo, dof);
+    mma_chain_rows_t<NT, NT>(du, Pm, LDC, bo);
+    chain_frags<NT>(bf, du);
+    mma_chain_rows_t<NT, NT>(dr, Tm, LDC, bf);
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) {
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dr[tr][e] = -bv[e] * dr[tr][e];
+    }
+#pragma unroll
+    for (int ti = 0; ti < NTK; ++ti) {
+      const f32x4 dec = *reinterpret_cast<const f32x4*>(gC + 16 * ti + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dh[ti][e] *= dec[e];
+    }
+    mma_chain_rows_t<NTK, NT>(dh, Qg, LDK, bo);
+    chain_frags<NT>(bf, dr);
+    mma_chain_rows_t<NTK, NT>(dh, Kg, LDK, bf);
+    lds_barrier();
+  };
+  // chunks nc-1, nc-2, ... alternate between the two buffers
+  for (int i = 0; i < nc; i += 2) {
+    step(nc - 1 - i, bufA);
+    if (i + 1 < nc) step(nc - 2 - i, bufB);
+  }
+  if (a.dh0) {
+#pragma unroll
+    for (int ti = 0; ti < NTK; ++ti)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a.dh0[hbase + (16 * ti + 4 * g + e) * DK] = dh[ti][e];
   }
 }
 
@@ -2203,9 +2347,88 @@ hipError_t fwd_cw(const Shape& s, const ChunkFwdArgs& x, void* ws, hipStream_t s
     if (e != hipSuccess) return e;
   }
   ProfScope ps("chunk_fwd_cw", st);
-  hipLaunchKernelGGL((cwchain16_kernel<C, TO>), dim3(static_cast<unsigned>(2 * a.Hv * a.B)), dim3(64 * (NCW + 1)), 0,
-                     st, a);
+  hipLaunchKernelGGL((cwchain16_kernel<C, TO, true, false>), dim3(static_cast<unsigned>(2 * a.Hv * a.B)),
+                     dim3(64 * (NCW + 1)), 0, st, a);
   return hipGetLastError();
+}
+
+// Channelwise VJP: the chunk images, every chunk's entry state (forward
+// chain), every chunk's end gradient and dh0 (reverse chain), then the
+// sequential VJP inside every chunk from those two states, all chunks in
+// parallel (partial sums per value slice), and the epilogue (slice and
+// group sums, L2-norm VJP, dq / dk / dbeta / dg).
+struct WsCW {
+  size_t kimg, cimg, hst, dhst, pdq, pdk, pdb, pdg, ckpt, scratch, total;
+};
+
+template <int C>
+WsCW plan_cw_bwd(const Shape& s) {
+  using IM = ImgCW<C>;
+  const size_t nv = static_cast<size_t>(s.B) * s.Hv * static_cast<size_t>((s.T + C - 1) / C);
+  const size_t ns = static_cast<size_t>(seq_bwd_slices(s)), rows = static_cast<size_t>(s.B * s.T * s.Hv);
+  WsCW w{};
+  size_t off = 0;
+  w.kimg = off;    off = up(off + nv * IM::KEY);
+  w.cimg = off;    off = up(off + nv * IM::CHK);
+  w.hst = off;     off = up(off + nv * DK * DK * 2);
+  w.dhst = off;    off = up(off + nv * DK * DK * 2);
+  w.pdq = off;     off = up(off + ns * rows * DK * 4);
+  w.pdk = off;     off = up(off + ns * rows * DK * 4);
+  w.pdb = off;     off = up(off + ns * rows * 4);
+  w.pdg = off;     off = up(off + ns * rows * DK * 4);
+  w.ckpt = off;    off = up(off + seq_bwd_chunk_ckpt_floats(s, C) * 4);
+  w.scratch = off; off = up(off + seq_bwd_chunk_scratch_floats(s, C) * 4);
+  w.total = off;
+  return w;
+}
+
+template <int C>
+hipError_t bwd_cw(const Shape& s, const ChunkBwdArgs& x, void* ws, hipStream_t st) {
+  const WsCW w = plan_cw_bwd<C>(s);
+  Ws16 w16{};
+  w16.kimg = w.kimg;
+  w16.cimg = w.cimg;
+  w16.hst = w.hst;
+  w16.dhst = w.dhst;
+  K16 a = args16(s, C, ws, w16);
+  a.cu = x.cu;
+  a.q = static_cast<const bf16_t*>(x.q);
+  a.k = static_cast<const bf16_t*>(x.k);
+  a.v = static_cast<const bf16_t*>(x.v);
+  a.dout = static_cast<const bf16_t*>(x.dout);
+  a.g = x.g;
+  a.beta = x.beta;
+  a.h0 = x.h0;
+  a.dht = x.dht;
+  a.dh0 = x.dh0;
+  const dim3 chains(static_cast<unsigned>(2 * a.Hv * a.B));
+  {
+    ProfScope ps("chunk_prep_cw", st);
+    hipLaunchKernelGGL((cwprep16_kernel<C>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(512), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    ProfScope ps("chunk_states_cw", st);
+    hipLaunchKernelGGL((cwchain16_kernel<C, bf16_t, false, true>), chains, dim3(64 * (NCW + 1)), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    ProfScope ps("chunk_dh_cw", st);
+    hipLaunchKernelGGL((cwdh16_kernel<C>), chains, dim3(64 * (NCW + 1)), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  char* base = static_cast<char*>(ws);
+  auto fp = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
+  SeqBwdArgs sa{x.q, x.k, x.v, x.dout, x.g, x.beta, x.h0, x.dht, x.dv, nullptr, fp(w.ckpt), fp(w.scratch),
+                fp(w.pdq), fp(w.pdk), fp(w.pdb), fp(w.pdg), x.cu, a.hst, a.dhst, C, a.NC};
+  hipError_t e = launch_seq_bwd_chunks(s, sa, st);
+  if (e != hipSuccess) return e;
+  EpiArgs ea{x.q, x.k, sa.part_dq, sa.part_dk, sa.part_db, sa.part_dg, seq_bwd_slices(s), x.dq, x.dk, x.dbeta,
+             x.dg, x.g, x.beta, x.cu};
+  return launch_bwd_epilogue(s, ea, st);
 }
 
 }  // namespace
@@ -2214,7 +2437,10 @@ size_t chunk16_fwd_workspace(const Shape& s, int C) {
   if (s.channelwise) return C == 64 ? plan_cw<64>(s).total : plan_cw<32>(s).total;
   return plan_any(s, C, s.save_chunks).total;
 }
-size_t chunk16_bwd_workspace(const Shape& s, int C) { return plan_any(s, C, true).total; }
+size_t chunk16_bwd_workspace(const Shape& s, int C) {
+  if (s.channelwise) return C == 64 ? plan_cw_bwd<64>(s).total : plan_cw_bwd<32>(s).total;
+  return plan_any(s, C, true).total;
+}
 
 hipError_t launch_chunk16_fwd(const Shape& s, int C, const ChunkFwdArgs& x, void* ws, hipStream_t st) {
   if (s.channelwise) {
@@ -2228,6 +2454,11 @@ hipError_t launch_chunk16_fwd(const Shape& s, int C, const ChunkFwdArgs& x, void
 }
 
 hipError_t launch_chunk16_bwd(const Shape& s, int C, const ChunkBwdArgs& x, void* ws, hipStream_t st) {
+  if (s.channelwise) {
+    if (C == 64) return bwd_cw<64>(s, x, ws, st);
+    if (C == 32) return bwd_cw<32>(s, x, ws, st);
+    return hipErrorInvalidValue;
+  }
   if (C == 64) return s.out_bf16 ? bwd_all<64, bf16_t>(s, x, ws, st) : bwd_all<64, float>(s, x, ws, st);
   if (C == 32) return s.out_bf16 ? bwd_all<32, bf16_t>(s, x, ws, st) : bwd_all<32, float>(s, x, ws, st);
   return hipErrorInvalidValue;

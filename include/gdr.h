@@ -121,10 +121,11 @@ typedef struct gdr_problem {
   int32_t algo;       /* gdr_algo                                           */
   int32_t chunk_size; /* CHUNKED only: 16, 32 or 64; 0 means 64             */
 } gdr_problem;
-/* With GDR_CHANNELWISE, GDR_ALGO_CHUNKED is supported for the forward pass
- * with bf16 io, Dk = Dv = 128 and chunk_size 32 or 64 (else
- * GDR_ERR_UNSUPPORTED); the backward pass is sequential only.  AUTO picks
- * the chunked forward there when T > 64. */
+/* With GDR_CHANNELWISE, GDR_ALGO_CHUNKED is supported with bf16 io,
+ * Dk = Dv = 128 and chunk_size 32 or 64 (else GDR_ERR_UNSUPPORTED); its VJP
+ * runs the sequential VJP inside every chunk, all chunks in parallel, from
+ * chunk states the chunk chains store.  AUTO picks the chunked kernels there
+ * when T > 64. */
 
 /* Workspace bytes the call needs for problem *p (0 is possible).  Returns
  * the same validation status gdr_forward/gdr_backward would for the shape
@@ -171,10 +172,9 @@ gdr_status gdr_backward(const gdr_problem* p, const void* q, const void* k,
  * pages: an interface variant for batches of unequal prompts).
  * Supported: GDR_ALGO_SEQUENTIAL (every shape, both passes) and
  * GDR_ALGO_CHUNKED on its fp16 path (bf16 io, Dk = Dv = 128, chunk_size 32
- * or 64; the forward with a scalar or channelwise gate, the backward with a
- * scalar gate, GDR_SAVE_CHUNKS included).  The fp32 chunked path (fp32 io
- * or Dk = 16) returns GDR_ERR_UNSUPPORTED; AUTO picks as for gdr_forward /
- * gdr_backward. */
+ * or 64; scalar or channelwise gate; GDR_SAVE_CHUNKS with a scalar gate).
+ * The fp32 chunked path (fp32 io or Dk = 16) returns GDR_ERR_UNSUPPORTED;
+ * AUTO picks as for gdr_forward / gdr_backward. */
 gdr_status gdr_forward_varlen(const gdr_problem* p, const int64_t* cu_seqlens,
                               const void* q, const void* k, const void* v,
                               const float* g, const float* beta,

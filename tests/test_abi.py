@@ -123,22 +123,25 @@ def test_bad_problem_beats_everything():
     assert B.lib().gdr_forward(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, 0, None) == 1
 
 
-def test_channelwise_chunked_forward_support():
-    """Channelwise gates: chunked forward only with bf16 io, D = 128 and
-    C in {32, 64}; the chunked backward is refused; AUTO falls back to the
-    sequential kernels (no workspace) where the chunked forward is absent."""
+def test_channelwise_chunked_support():
+    """Channelwise gates: chunked forward and VJP only with bf16 io, D = 128
+    and C in {32, 64}; AUTO falls back to the sequential kernels (forward:
+    no workspace) where the chunked ones are absent."""
     cw = dict(flags=3, io_dtype=1, Dk=128, Dv=128, T=256)
     for C in (0, 32, 64):
         st, n = fwd_ws(prob(algo=2, chunk_size=C, **cw))
         assert st == 0 and n > 0
+        st, n2 = bwd_ws(prob(algo=2, chunk_size=C, **cw))
+        assert st == 0 and n2 > n
     assert fwd_ws(prob(algo=2, chunk_size=16, **cw))[0] == 3
+    assert bwd_ws(prob(algo=2, chunk_size=16, **cw))[0] == 3
     assert fwd_ws(prob(algo=2, flags=3, T=256))[0] == 3          # fp32 io, D = 16
-    assert bwd_ws(prob(algo=2, **cw))[0] == 3
+    assert bwd_ws(prob(algo=2, flags=3, T=256))[0] == 3
     st, n = fwd_ws(prob(algo=0, **cw))
     assert st == 0 and n > 0                                      # AUTO -> chunked
+    assert bwd_ws(prob(algo=0, **cw)) == bwd_ws(prob(algo=2, **cw))
     assert fwd_ws(prob(algo=0, **dict(cw, T=64))) == (0, 0)       # short: sequential
     assert fwd_ws(prob(algo=0, flags=3, T=256)) == (0, 0)         # fp32: sequential
-    assert bwd_ws(prob(algo=0, **cw))[0] == 0                     # AUTO VJP: sequential
 
 
 def test_save_chunks_workspace():
@@ -177,7 +180,7 @@ def test_varlen_validation():
     assert call_bwd_varlen(prob(**bf), None) == 1
     assert call_fwd_varlen(prob(**bf), FAKE + 4) == 4
     assert call_bwd_varlen(prob(algo=2, T=256), FAKE) == 3          # fp32 io, D = 16 chunked
-    assert call_bwd_varlen(prob(algo=2, flags=3, **bf), FAKE) == 3  # channelwise chunked VJP
+    assert call_bwd_varlen(prob(algo=2, flags=3, **bf), FAKE) == 1  # channelwise chunked VJP: no workspace
     assert call_fwd_varlen(prob(algo=2, T=256), FAKE) == 3          # fp32 chunked forward
     assert call_bwd_varlen(prob(algo=2, **bf), FAKE) == 1           # chunked: workspace missing
     assert call_bwd_varlen(prob(algo=1, **bf), FAKE) == 1           # sequential: workspace missing

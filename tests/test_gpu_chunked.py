@@ -187,3 +187,31 @@ def test_saved_chunks_match_stateless(T, C):
     assert np.array_equal(host(o0), host(o1)) and np.array_equal(host(ht0), host(ht1))
     for a0, a1 in zip(g0, g1):
         assert np.array_equal(host(a0), host(a1))
+
+
+# ------------------------------------------------ channelwise chunked VJP
+
+@pytest.mark.parametrize("T,C", [(1, 64), (50, 64), (64, 64), (200, 64), (97, 32), (130, 32)])
+def test_channelwise_chunked_vjp(T, C):
+    """Channelwise gates on the chunked VJP (chunk states from the chains,
+    the sequential VJP inside every chunk): ragged last chunk, GQA 2:4, h0
+    and dht nonzero, bf16 io, D=128."""
+    x = make_inputs(1900 + T + C, 2, T, 2, 4, 128, 128, io_dtype="bf16", channelwise=True, h0_std=0.02)
+    dht = (0.1 * np.random.default_rng(T + C).standard_normal((2, 4, 128, 128))).astype(np.float32)
+    check_bwd(x, "bf16", cw=True, dht=dht, algo=("chunked", C))
+
+
+def test_channelwise_chunked_vjp_fused_gates_and_strong_decay():
+    x = make_inputs(1950, 2, 150, 2, 4, 128, 128, io_dtype="bf16", channelwise=True, h0_std=0.02,
+                    gate_preact=True)
+    check_bwd(x, "bf16", cw=True, algo=("chunked", 64), fg=True)
+    y = make_inputs(1951, 2, 150, 2, 4, 128, 128, io_dtype="bf16", channelwise=True, h0_std=0.02)
+    y["g"][:, 64:128, :, 5:9] = -30.0   # the exact diagonal sums in the second chunk
+    check_bwd(y, "bf16", cw=True, algo=("chunked", 64))
+
+
+def test_channelwise_chunked_vjp_prefill_t2048():
+    """B=1, Hk=16, Hv=32, T=2048 (the channelwise prefill shape), sampled
+    k-head groups against the oracle."""
+    x = make_inputs(1960, 1, 2048, 16, 32, 128, 128, io_dtype="bf16", channelwise=True)
+    check_bwd(x, "bf16", cw=True, h0=False, heads=[(0, 3)], algo=("chunked", 64))

@@ -128,3 +128,7 @@ def test_ragged_sequential_vjp(io, D, cw):
     """The sequential VJP (and its epilogue) on a ragged batch: lengths 0,
     20, 1, 37 (segments of 16 tokens, ragged), both gate modes."""
     run_and_check([0, 20, 1, 37], io, "sequential", cw=cw, seed=23 + D + cw, D=D)
+
+
+def test_ragged_channelwise_chunked_vjp():
+    run_and_check([0, 90, 1, 150], "bf16", "chunked", 64, cw=True, seed=29)
