@@ -227,7 +227,7 @@ def bench_channelwise(torch, gdr, reps=20):
     at B=1, Hk=16, Hv=32, D=128, bf16 io, zero h0, for T in {128, 512, 2048}:
     the chunked path (C=64) against the sequential one; time per call from
     events around `reps` back-to-back calls, plus the chunked kernels' own
-    times."""
+    times; then the VJP of the same call, chunked against sequential."""
     from gated_delta_rule_54_amd.synth import make_inputs
     dev = torch.device("cuda")
     out = {}
@@ -265,6 +265,28 @@ def bench_channelwise(torch, gdr, reps=20):
                 ent["chunked_kernels_us"] = {k: round(1000.0 * v[0] / v[1], 2) for k, v in kt.items()}
         ent["speedup"] = round(ent["sequential_us"] / ent["chunked_us"], 2)
         ent["chunked_tokens_per_s"] = round(t_len / (ent["chunked_us"] * 1e-6), 1)
+        # the VJP of the same call (do ~ N(0, 1)), chunked against sequential
+        do = torch.randn(t["v"].shape, device=dev, generator=torch.Generator(device=dev).manual_seed(t_len))
+        do = do.to(torch.bfloat16)
+        for algo in ("sequential", "chunked"):
+            kw = dict(algo=algo, channelwise=True, out_dtype=torch.bfloat16)
+            if algo == "chunked":
+                kw["chunk_size"] = C
+
+            def vjp():
+                gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], None, do, **kw)
+
+            vjp()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = max(2, reps // 4)
+            e0.record()
+            for _ in range(n):
+                vjp()
+            e1.record()
+            torch.cuda.synchronize()
+            ent[f"vjp_{algo}_us"] = round(1000.0 * e0.elapsed_time(e1) / n, 2)
+        ent["vjp_speedup"] = round(ent["vjp_sequential_us"] / ent["vjp_chunked_us"], 2)
         out[f"T={t_len}"] = ent
     out["config"] = f"B=1 Hk={HK} Hv={HV} Dk=Dv={D}, channelwise gate, bf16 io, zero h0, chunk {C}"
     return out
