@@ -196,6 +196,109 @@ __global__ __launch_bounds__(64) void seq_fwd_kernel(Dims d, SeqFwdArgs a) {
   }
 }
 
+// Decode step (T = 1, Dk = Dv = 128): NW waves per 128 x 32 state slice,
+// wave w owning rows (128/NW)w .. (128/NW)(w+1) - 1 (128/(8 NW) rows x 4
+// columns per lane), so each wave issues 1/NW of the state loads and stores
+// of seq_fwd_kernel; the sums over Dk (|k|^2, |q|^2, k.q, p, r) add the
+// waves' parts through LDS.
+template <typename TI, typename TO, bool CW, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_kernel(Dims d, SeqFwdArgs a) {
+  constexpr int D = 128, BV = 32, NCG = 8, RPL = D / NW / 8, NV = 11;
+  __shared__ float part[NW][NCG][NV + 1];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int cg = lane % NCG, rg = lane / NCG;
+  const int hv = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int kh = hv / (d.Hv / d.Hk);
+  const int j0 = blockIdx.x * BV + cg * 4;
+  const int i0 = (D / NW) * w + rg * RPL;
+  const int64_t hbase = ((b * d.Hv + hv) * D + i0) * D + j0;
+  int64_t tb = b * d.T, len = d.T;  // ragged batch: rows cu[b] .., length 0 or 1
+  if (a.cu) {
+    tb = a.cu[b];
+    len = a.cu[b + 1] - tb;
+    len = len < 0 ? 0 : (len > d.T ? d.T : len);
+  }
+  float h[RPL][4];
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) {
+    if (a.h0) {  // streamed once: non-temporal
+      const f32x4n t4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4n*>(a.h0 + hbase + m * D));
+      h[m][0] = t4[0]; h[m][1] = t4[1]; h[m][2] = t4[2]; h[m][3] = t4[3];
+    } else {
+      h[m][0] = h[m][1] = h[m][2] = h[m][3] = 0.f;
+    }
+  }
+  if (len > 0) {  // the same for every thread of the block
+    const int64_t krow = (tb * d.Hk + kh) * D + i0;
+    const int64_t vrow = (tb * d.Hv + hv) * D + j0;
+    const int64_t grow = tb * d.Hv + hv;
+    float k[RPL], q[RPL], v[4], al[CW ? RPL : 1];
+    ld_rows<RPL, TI>(static_cast<const TI*>(a.k) + krow, k);
+    ld_rows<RPL, TI>(static_cast<const TI*>(a.q) + krow, q);
+    ld4<TI>(static_cast<const TI*>(a.v) + vrow, v);
+    if constexpr (CW) {
+      ld_rows<RPL, float>(a.g + grow * D + i0, al);
+#pragma unroll
+      for (int m = 0; m < RPL; ++m) al[m] = d.fg ? fg_alpha(al[m]) : expf(al[m]);
+    } else {
+      al[0] = d.fg ? fg_alpha(a.g[grow]) : expf(a.g[grow]);
+    }
+    const float beta = d.fg ? fg_beta(a.beta[grow]) : a.beta[grow];
+    // this wave's halves of the sums over Dk
+    float x[NV] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // |k|^2 |q|^2 k.q p[4] r[4]
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+      x[0] += k[m] * k[m];
+      x[1] += q[m] * q[m];
+      x[2] += k[m] * q[m];
+      const float am = CW ? al[CW ? m : 0] : al[0];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float dme = am * h[m][e];
+        h[m][e] = dme;
+        x[3 + e] += dme * k[m];
+        x[7 + e] += dme * q[m];
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NV; ++n) x[n] = xsum<NCG, 64>(x[n]);
+    if (rg == 0) {
+#pragma unroll
+      for (int n = 0; n < NV; ++n) part[w][cg][n] = x[n];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {  // all waves' parts in one order (every wave gets the same sums)
+      float t = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) t += part[w2][cg][n];
+      x[n] = t;
+    }
+    const float rk = d.l2 ? rsqrtf(x[0] + kL2Eps) : 1.f;
+    const float rq = d.l2 ? rsqrtf(x[1] + kL2Eps) : 1.f;
+    const float kq = x[2] * rk * rq;
+    float u[4], o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      u[e] = beta * (v[e] - x[3 + e] * rk);
+      o[e] = x[7 + e] * rq + kq * u[e];
+    }
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+      const float km = k[m] * rk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[m][e] += km * u[e];
+    }
+    if (w == 0 && rg == 0) st4<TO>(static_cast<TO*>(a.o) + vrow, o);
+  }
+  if (a.ht) {
+#pragma unroll
+    for (int m = 0; m < RPL; ++m)
+      __builtin_nontemporal_store(f32x4n{h[m][0], h[m][1], h[m][2], h[m][3]}, reinterpret_cast<f32x4n*>(a.ht + hbase + m * D));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Sequential VJP.  Phase 1 replays the forward and stores the state before
 // every kSeqSeg-th token (lane-private layout).  Phase 2 walks the segments
@@ -615,6 +718,7 @@ __global__ __launch_bounds__(256) void epilogue128_kernel(Dims d, EpiArgs a) {
 Dims dims_of(const Shape& s) { return Dims{s.B, s.T, s.Hk, s.Hv, s.l2norm ? 1 : 0, s.fused_gates ? 1 : 0}; }
 
 template <int D> constexpr int fwd_bv() { return D == 16 ? 16 : 32; }
+constexpr int kDecWaves = 2;  // waves per decode slice (1, 4 and 8 measured slower at B=8, Hv=32)
 template <int D> constexpr int bwd_bv() { return D == 16 ? 16 : 32; }
 
 template <int D, typename TI, typename TO, bool CW>
@@ -622,6 +726,12 @@ hipError_t fwd_go(const Shape& s, const SeqFwdArgs& a, hipStream_t st) {
   constexpr int BV = fwd_bv<D>();
   dim3 grid(D / BV, s.Hv, static_cast<unsigned>(s.B));
   ProfScope ps("seq_fwd", st);
+  if constexpr (D == 128) {
+    if (s.T == 1) {  // decode step
+      hipLaunchKernelGGL((decode_kernel<TI, TO, CW, kDecWaves>), grid, dim3(64 * kDecWaves), 0, st, dims_of(s), a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((seq_fwd_kernel<D, BV, TI, TO, CW>), grid, dim3(64), 0, st, dims_of(s), a);
   return hipGetLastError();
 }

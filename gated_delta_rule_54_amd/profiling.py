@@ -48,6 +48,7 @@ KERNELS = [
     (r"grad16_kernel", "chunk_grad"),
     (r"epilogue128_kernel", "bwd_epilogue"),
     (r"seq_fwd_kernel", "seq_fwd"),
+    (r"decode_kernel", "seq_fwd"),
 ]
 COPY_PATTERN = r"neg_kernel"
 
