@@ -399,10 +399,11 @@ __device__ __forceinline__ void write_tile(char* dst, F&& f) {
 //     T_ij = -T_ii (sum_{k=j}^{i-1} A_ik T_kj),
 // on fp32 matrix cores; everything is fp32 until the images are written.
 template <int C>
-__global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
+__global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
   using IM = Img<C>;
+  constexpr int NTH = 512, NW = NTH / 64;
   constexpr int NT = C / 16, LDA = C + 4, LDC = IM::LDC;
-  constexpr int TPR = 256 / C, EPT = DK / TPR, NV = EPT / 8;
+  constexpr int TPR = NTH / C, EPT = DK / TPR, NV = EPT / 8;
   static_assert(C * LDC <= C * LDK, "the fp16 T tile reuses the Qn buffer");
   __shared__ __align__(16) _Float16 Ks[C * LDK];
   __shared__ __align__(16) _Float16 Qs[C * LDK];  // Qn, then the fp16 T tile [C][LDC]
@@ -414,7 +415,7 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
   // 16 x 16 diagonal blocks (no other thread writes them)
   auto zero_upper = [&](_Float16* M) {
     constexpr int UR = LDC / 8;
-    for (int e = threadIdx.x; e < C * UR; e += 256) {
+    for (int e = threadIdx.x; e < C * UR; e += NTH) {
       const int r = e / UR, u = e % UR;
       if (u < C / 8 && u / 2 > r / 16) reinterpret_cast<uint4*>(M)[e] = uint4{0u, 0u, 0u, 0u};
     }
@@ -452,8 +453,8 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
       gv = tid < L ? gv : 0.f;
       bv = tid < L ? bv : 0.f;
     }
-    norm_rows<C, NV>(Ks, kr, a.l2);
-    norm_rows<C, NV>(Qs, qr, a.l2);
+    norm_rows<C, NV, NTH>(Ks, kr, a.l2);
+    norm_rows<C, NV, NTH>(Qs, qr, a.l2);
     if (tid < 64) {  // running sum G over the chunk (g = 0 past the end)
       float x = gv;
 #pragma unroll
@@ -475,7 +476,7 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
   // A (fp32) and P (fp16) on the NT(NT+1)/2 tiles on or below the diagonal,
   // dealt to the waves; each tile's fragments are read before its products
   constexpr int NL = NT * (NT + 1) / 2, KS = DK / 32;
-  for (int t = w; t < NL; t += 4) {
+  for (int t = w; t < NL; t += NW) {
     int tr = 0;
     while ((tr + 1) * (tr + 2) / 2 <= t) ++tr;
     const int tc = t - tr * (tr + 1) / 2;
@@ -495,7 +496,7 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * tr + 4 * g + e, s2 = 16 * tc + c16;
-      const float ex = s2 <= r ? exp2f(G2[r] - G2[s2]) : 0.f;
+      const float ex = s2 <= r ? __builtin_amdgcn_exp2f(G2[r] - G2[s2]) : 0.f;
       A[r * LDA + s2] = s2 < r ? bet[r] * ex * kk[e] : 0.f;
       Pst[r * LDC + s2] = static_cast<_Float16>(ex * qk[e]);
     }
@@ -504,8 +505,8 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
   constexpr int UK = DK / 8 + 1;  // 16-byte units per [*][LDK] row
   if (hv % grp == 0) {
     char* kim = a.kimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(IM::KEY);
-    write_tile<C, UK>(kim, [&](int r, int u) { return ld8(Ks + r * LDK + 8 * u); });
-    write_tile<C, UK>(kim + IM::KN, [&](int r, int u) { return ld8(Qs + r * LDK + 8 * u); });
+    write_tile<C, UK, NTH>(kim, [&](int r, int u) { return ld8(Ks + r * LDK + 8 * u); });
+    write_tile<C, UK, NTH>(kim + IM::KN, [&](int r, int u) { return ld8(Qs + r * LDK + 8 * u); });
   }
   __syncthreads();
   zero_upper(Tst);  // T above its diagonal blocks
@@ -554,11 +555,11 @@ __global__ __launch_bounds__(256) void prep16_kernel(K16 a) {
 
   // ---- chunk image
   char* cim = a.cimg + ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(IM::CHK);
-  for (int e = tid; e < C; e += 256)
+  for (int e = tid; e < C; e += NTH)
     reinterpret_cast<float4*>(cim)[e] = reinterpret_cast<const float4*>(gates)[e];
   constexpr int UC = C / 8 + 1;  // 16-byte units per [*][LDC] row
-  write_tile<C, UC>(cim + IM::GT, [&](int r, int u) { return ld8(Tst + r * LDC + 8 * u); });
-  write_tile<C, UC>(cim + IM::GT + IM::TM, [&](int r, int u) { return ld8(Pst + r * LDC + 8 * u); });
+  write_tile<C, UC, NTH>(cim + IM::GT, [&](int r, int u) { return ld8(Tst + r * LDC + 8 * u); });
+  write_tile<C, UC, NTH>(cim + IM::GT + IM::TM, [&](int r, int u) { return ld8(Pst + r * LDC + 8 * u); });
 }
 
 // ---------------------------------------------------------------------------
@@ -2230,7 +2231,7 @@ K16 args16(const Shape& s, int C, void* ws, const Ws16& w) {
 template <int C>
 hipError_t prep16(const K16& a, hipStream_t st) {
   ProfScope ps("chunk_prep", st);
-  hipLaunchKernelGGL((prep16_kernel<C>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prep16_kernel<C>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
