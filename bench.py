@@ -161,7 +161,7 @@ def bench_chunked(torch, gdr, steps, warmup, fused_gates=False, saved=True):
     return ms, wall, kernels
 
 
-def bench_decode(torch, gdr):
+def bench_decode(torch, gdr, graph=True):
     """B=8 single-token steps, state updated in place, rotating over
     DEC_BUFFERS independent states so a step's 16 MiB state is not served
     from the 256 MB last-level cache.  Per step: the kernel time from the
@@ -197,26 +197,28 @@ def bench_decode(torch, gdr):
         ms, n = kt["seq_fwd"]
         us = 1000.0 * ms / n
         state_bytes = 2 * DEC_B * HV * D * D * 4
+        out[label] = {"kernel_us_per_step": round(us, 3), "wall_us_per_step": round(1e6 * wall / DEC_STEPS, 2),
+                      "state_GBps": round(state_bytes / (us * 1e-6) / 1e9, 1),
+                      "frac_hbm_peak": round(state_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        if not graph:
+            continue
         # the same steps captured once into a HIP graph and replayed: no host
         # launch gaps and no per-kernel events
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
+        graph_ = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph_):
             run(DEC_STEPS, buffers)
-        graph.replay()
+        graph_.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        graph.replay()
+        graph_.replay()
         e1.record()
         torch.cuda.synchronize()
         gus = 1000.0 * e0.elapsed_time(e1) / DEC_STEPS
-        del graph
-        out[label] = {"kernel_us_per_step": round(us, 3), "wall_us_per_step": round(1e6 * wall / DEC_STEPS, 2),
-                      "graph_us_per_step": round(gus, 3),
-                      "state_GBps": round(state_bytes / (us * 1e-6) / 1e9, 1),
-                      "frac_hbm_peak": round(state_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                      "graph_state_GBps": round(state_bytes / (gus * 1e-6) / 1e9, 1),
-                      "graph_frac_hbm_peak": round(state_bytes / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del graph_
+        out[label].update({"graph_us_per_step": round(gus, 3),
+                           "graph_state_GBps": round(state_bytes / (gus * 1e-6) / 1e9, 1),
+                           "graph_frac_hbm_peak": round(state_bytes / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
     out["state_bytes_per_step"] = 2 * DEC_B * HV * D * D * 4
     out["config"] = f"B={DEC_B} Hk={HK} Hv={HV} Dk=Dv={D}, {DEC_STEPS} single-token steps, bf16 io, fp32 state"
     return out
@@ -423,6 +425,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="time only the headline step (no fused-gate, stateless, channelwise or ragged legs)")
+    ap.add_argument("--only-decode", action="store_true",
+                    help="run only the decode leg (for counter runs of the decode kernel)")
+    ap.add_argument("--no-graph", action="store_true", help="decode leg without the replayed HIP graph")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy this many MiB once with a plain elementwise kernel "
                          "(reference for HBM byte counters)")
@@ -436,6 +441,10 @@ def main():
     import gated_delta_rule_54_amd as gdr
     gdr.lib()  # fail loudly if the library was not built
 
+    if args.only_decode:
+        print(json.dumps({"decode": bench_decode(torch, gdr, graph=not args.no_graph)}), flush=True)
+        copy_calibration(torch, args.copy_calibration_mib)
+        return
     ms, wall, kernels = bench_chunked(torch, gdr, args.steps, args.warmup)
     tokens = B * T
     th = B * T * HV
@@ -472,7 +481,7 @@ def main():
     roof["bytes_per_launch"] = None if by is None else int(by * th)
     roof["flops_per_launch"] = None if f is None else int(f * th)
     roof["kernel"] = dom
-    grids = {"chunk_prep": ((T // C, HV, B), 256), "chunk_fwd_save": ((2 * HV * B, 1, 1), 320),
+    grids = {"chunk_prep": ((T // C, HV, B), 512), "chunk_fwd_save": ((2 * HV * B, 1, 1), 320),
              "chunk_fwd": ((2 * HV * B, 1, 1), 320), "chunk_states": ((2 * HV * B, 1, 1), 320),
              "chunk_dh": ((2 * HV * B, 1, 1), 320), "chunk_grad": ((T // C, HK, B), 512)}
     if dom in grids:  # to find the same launches in a rocprofv3 kernel trace
@@ -509,16 +518,22 @@ def main():
     else:
         line["variants"] = variants(torch, gdr, args, tokens)
     if not args.no_decode:
-        line["decode"] = bench_decode(torch, gdr)
+        line["decode"] = bench_decode(torch, gdr, graph=not args.no_graph)
     line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()
     print(json.dumps(line), flush=True)
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
+    copy_calibration(torch, args.copy_calibration_mib)
+
+
+def copy_calibration(torch, mib):
+    """One plain elementwise copy of `mib` MiB (reference for HBM byte counters)."""
+    if not mib:
+        return
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

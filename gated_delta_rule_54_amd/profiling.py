@@ -39,7 +39,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # demangled kernel name pattern -> library timing name
 KERNELS = [
     (r"cwprep16_kernel", "chunk_prep_cw"),
-    (r"cwchain16_kernel", "chunk_fwd_cw"),
+    (r"cwchain16_kernel<\d+, [^,]+, true, false>", "chunk_fwd_cw"),
+    (r"cwchain16_kernel<\d+, [^,]+, false, true>", "chunk_states_cw"),
+    (r"cwdh16_kernel", "chunk_dh_cw"),
     (r"prep16_kernel", "chunk_prep"),
     (r"chain16_kernel<\d+, [^,]+, true, false>", "chunk_fwd"),
     (r"chain16_kernel<\d+, [^,]+, true, true>", "chunk_fwd_save"),
@@ -47,8 +49,10 @@ KERNELS = [
     (r"dh16_kernel", "chunk_dh"),
     (r"grad16_kernel", "chunk_grad"),
     (r"epilogue128_kernel", "bwd_epilogue"),
+    (r"seq_bwd_kernel<[^>]*, true>", "seq_bwd_chunks"),
+    (r"seq_bwd_kernel", "seq_bwd"),
     (r"seq_fwd_kernel", "seq_fwd"),
-    (r"decode_kernel", "seq_fwd"),
+    (r"decode_kernel", "decode"),
 ]
 COPY_PATTERN = r"neg_kernel"
 
@@ -85,13 +89,15 @@ def label(name):
 
 
 def per_kernel(db, counter):
-    """{label: mean KiB per launch} over the dispatches of each kernel."""
+    """{label: (mean KiB per launch, launches)} over the dispatches of each
+    kernel; for the calibration copy, its largest dispatch (the command may
+    run small elementwise kernels of the same name for its inputs)."""
     acc = collections.defaultdict(list)
     for name, v in per_dispatch(db, counter).values():
         lab = label(name)
         if lab is not None:
             acc[lab].append(v)
-    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+    return {k: ((max(v), 1) if k == "copy" else (sum(v) / len(v), len(v))) for k, v in acc.items()}
 
 
 def traffic(args):
