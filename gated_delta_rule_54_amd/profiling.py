@@ -23,7 +23,13 @@ digest matches.
     python -m gated_delta_rule_54_amd.profiling trace KT_results.db --md profiles/<name>.md
 
 summarises a ``rocprofv3 --kernel-trace --stats`` database (per-kernel calls,
-total and average duration).
+total and average duration), and
+
+    rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_F32 \
+        SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE -d DIR_M -o m -- python3 bench.py ...
+    python -m gated_delta_rule_54_amd.profiling mfma DIR_M/m_results.db --md profiles/<name>.md
+
+the matrix-core busy fraction and executed matrix-core FLOPs per launch.
 """
 
 import argparse
@@ -142,6 +148,53 @@ def traffic(args):
     print(json.dumps(rec))
 
 
+def mfma(args):
+    """Matrix-core use per kernel launch from one counter run with
+    SQ_INSTS_VALU_MFMA_MOPS_F16, SQ_INSTS_VALU_MFMA_MOPS_F32 (units of 512
+    FLOPs, summed over shader engines), SQ_VALU_MFMA_BUSY_CYCLES (summed over
+    SIMDs) and GRBM_GUI_ACTIVE (GPU busy cycles, the same on every XCD: the
+    largest is taken).  Busy fraction = MFMA busy cycles / (GPU busy cycles x
+    SIMDs), the definition of rocprofv3's derived MfmaUtil counter."""
+    con = sqlite3.connect(args.db)
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    names, durs = {}, {}
+    for did, name, cn, cv, dur in con.execute(
+            "select dispatch_id, name, counter_name, counter_value, duration from pmc_events"):
+        per[did][cn].append(float(cv))
+        names[did], durs[did] = name, float(dur)
+    acc = collections.defaultdict(list)
+    for did, x in per.items():
+        lab = label(names[did])
+        if lab is None or lab == "copy" or not x.get("GRBM_GUI_ACTIVE"):
+            continue
+        gui = max(x["GRBM_GUI_ACTIVE"])
+        busy = sum(x.get("SQ_VALU_MFMA_BUSY_CYCLES", [0.0]))
+        f16 = 512.0 * sum(x.get("SQ_INSTS_VALU_MFMA_MOPS_F16", [0.0]))
+        f32 = 512.0 * sum(x.get("SQ_INSTS_VALU_MFMA_MOPS_F32", [0.0]))
+        acc[lab].append((busy / (gui * args.simds), f16, f32, durs[did]))
+    lines = ["# Matrix-core use per kernel launch (rocprofv3 counters)", ""]
+    if args.command:
+        lines += ["Command (from the repository root on one MI355X, library built):", "", "```", args.command, "```",
+                  ""]
+    lines += [f"Busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {args.simds} SIMDs).  FLOPs = executed "
+              "matrix-core FLOPs (MOPS counters x 512), including the zero padding of partial tiles.  "
+              "Rate = FLOPs / counter-run duration (the counter run serialises launches).", "",
+              "| kernel | launches | MFMA busy | fp16 GFLOP/launch | fp32 GFLOP/launch | duration us | "
+              "fp16+fp32 TFLOP/s |", "|---|---:|---:|---:|---:|---:|---:|"]
+    for lab in sorted(acc):
+        v = acc[lab]
+        n = len(v)
+        busy, f16, f32, dur = (sum(e[i] for e in v) / n for i in range(4))
+        lines.append(f"| {lab} | {n} | {100 * busy:.1f}% | {f16 / 1e9:.2f} | {f32 / 1e9:.2f} | "
+                     f"{dur / 1000.0:.1f} | {(f16 + f32) / dur / 1e3:.1f} |")
+    lines += ["", f"Kernel sources digest: `{src_digest()}`", ""]
+    text = "\n".join(lines)
+    if args.md:
+        with open(args.md, "w") as fh:
+            fh.write(text)
+    print(text)
+
+
 def trace(args):
     con = sqlite3.connect(args.db)
     rows = con.execute("select name, total_calls, total_duration, average, percentage from top_kernels "
@@ -196,8 +249,13 @@ def main():
     k.add_argument("--md", default=None)
     k.add_argument("--command", default="")
     k.add_argument("--top", type=int, default=16)
+    m = sub.add_parser("mfma")
+    m.add_argument("db")
+    m.add_argument("--md", default=None)
+    m.add_argument("--command", default="")
+    m.add_argument("--simds", type=int, default=1024, help="SIMDs on the GPU (MI355X: 256 CUs x 4)")
     args = ap.parse_args()
-    traffic(args) if args.cmd == "traffic" else trace(args)
+    {"traffic": traffic, "trace": trace, "mfma": mfma}[args.cmd](args)
 
 
 if __name__ == "__main__":
