@@ -294,6 +294,103 @@ def bench_channelwise(torch, gdr, reps=20):
     return out
 
 
+def bench_vjp_sweep(torch, gdr):
+    """The backward sweep of the page "Adding VJP for gated delta net"
+    (ml-explore/mlx pull request 4565, "Performance"): B in {1, 4, 8} x T in
+    {8, 64, 512, 4096}, Hk=16, Hv=32, D=128, bf16 io, zero h0, do ~ N(0, 1).
+    The stateless VJP (gdr_backward alone, which recomputes what it needs),
+    chunked (C=64) against sequential; time per call from events around
+    back-to-back calls.  Inputs drawn on the device with the same
+    distributions as the other legs."""
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    bmax, tmax = 8, 4096
+    rn = lambda *s: torch.randn(*s, device="cuda", generator=gen)
+    full = {"q": rn(bmax, tmax, HK, D).bfloat16(), "k": rn(bmax, tmax, HK, D).bfloat16(),
+            "v": rn(bmax, tmax, HV, D).bfloat16(), "do": rn(bmax, tmax, HV, D).bfloat16(),
+            "g": -torch.nn.functional.softplus(rn(bmax, tmax, HV)), "beta": torch.sigmoid(rn(bmax, tmax, HV))}
+    out = {}
+    for b in (1, 4, 8):
+        for t_len in (8, 64, 512, 4096):
+            t = {n: a[:b, :t_len].contiguous() for n, a in full.items()}
+            ent = {}
+            for algo in ("sequential", "chunked"):
+                kw = dict(algo=algo, out_dtype=torch.bfloat16)
+                if algo == "chunked":
+                    kw["chunk_size"] = C
+
+                def vjp():
+                    gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], None, t["do"], **kw)
+
+                vjp()
+                torch.cuda.synchronize()
+                reps = 2 if (algo == "sequential" and t_len >= 512) else 10
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    vjp()
+                e1.record()
+                torch.cuda.synchronize()
+                ent[f"{algo}_us"] = round(1000.0 * e0.elapsed_time(e1) / reps, 2)
+            ent["chunked_tokens_per_s"] = round(b * t_len / (ent["chunked_us"] * 1e-6), 1)
+            ent["speedup"] = round(ent["sequential_us"] / ent["chunked_us"], 2)
+            out[f"B={b},T={t_len}"] = ent
+            del t
+    out["config"] = (f"Hk={HK} Hv={HV} Dk=Dv={D}, bf16 io, scalar gate, zero h0, chunk {C}; "
+                     "stateless VJP, sequential against chunked")
+    return out
+
+
+def bench_channelwise_decode(torch, gdr, t_prefill=2048, steps=128):
+    """Channelwise gate: a B=1 prefill of t_prefill tokens (chunked), then
+    `steps` single-token steps carrying the state in place (Hk=16, Hv=32,
+    D=128, bf16 io).  The 2 MiB state stays in the last-level cache between
+    steps, so the per-step figure is cache-warm."""
+    from gated_delta_rule_54_amd.synth import make_inputs
+    dev = torch.device("cuda")
+    x = make_inputs(9000 + t_prefill, 1, t_prefill + steps, HK, HV, D, D, io_dtype="bf16", channelwise=True,
+                    with_do=False)
+    t = {n: (None if a is None else torch.from_numpy(a).to(dev)) for n, a in x.items()}
+    for n in ("q", "k", "v"):
+        t[n] = t[n].to(torch.bfloat16)
+    sl = lambda a, i, j: a[:, i:j].contiguous()
+    _, state = gdr.gdr_forward(sl(t["q"], 0, t_prefill), sl(t["k"], 0, t_prefill), sl(t["v"], 0, t_prefill),
+                               sl(t["g"], 0, t_prefill), sl(t["beta"], 0, t_prefill), None, algo="chunked",
+                               chunk_size=C, channelwise=True, out_dtype=torch.bfloat16)
+    toks = [{n: sl(t[n], t_prefill + i, t_prefill + i + 1) for n in ("q", "k", "v", "g", "beta")}
+            for i in range(steps)]
+
+    def run():
+        for z in toks:
+            gdr.gdr_forward(z["q"], z["k"], z["v"], z["g"], z["beta"], state, ht=state, algo="sequential",
+                            channelwise=True, out_dtype=torch.bfloat16)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run()
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * e0.elapsed_time(e1) / steps
+    graph = torch.cuda.CUDAGraph()  # the same steps as one replayed HIP graph (no host launch gaps)
+    with torch.cuda.graph(graph):
+        run()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    gus = 1000.0 * e0.elapsed_time(e1) / steps
+    del graph
+    state_bytes = 2 * HV * D * D * 4
+    return {"us_per_step": round(us, 3), "graph_us_per_step": round(gus, 3),
+            "graph_state_GBps_cache_warm": round(state_bytes / (gus * 1e-6) / 1e9, 1),
+            "config": f"B=1 Hk={HK} Hv={HV} Dk=Dv={D}, channelwise gate, chunked prefill of {t_prefill} tokens "
+                      f"then {steps} single-token steps in place (events around back-to-back calls, and one "
+                      "replayed HIP graph of the steps)"}
+
+
 def ragged_lengths(seed=11, total=B * T, lo=128, hi=2048):
     """A prefill batch of prompts of unequal length: lengths uniform in
     [lo, hi] (seeded) until their sum reaches `total` tokens (the last one
@@ -401,7 +498,8 @@ def _cpu_model():
 
 def variants(torch, gdr, args, tokens):
     """The other measured legs: the same step with fused gates and with the
-    stateless VJP, the channelwise prefill and the ragged prefill."""
+    stateless VJP, the channelwise prefill and decode, the ragged prefill and
+    the backward sweep."""
     fms, _, _ = bench_chunked(torch, gdr, args.steps, args.warmup, fused_gates=True)
     sms, _, skern = bench_chunked(torch, gdr, args.steps, args.warmup, saved=False)
     return {
@@ -412,7 +510,9 @@ def variants(torch, gdr, args, tokens):
                           "note": "same step without GDR_SAVE_CHUNKS: the VJP recomputes the chunk "
                                   "images and chunk states"},
         "channelwise_prefill": bench_channelwise(torch, gdr),
+        "channelwise_decode": bench_channelwise_decode(torch, gdr),
         "ragged_prefill": bench_ragged(torch, gdr),
+        "vjp_sweep": bench_vjp_sweep(torch, gdr),
     }
 
 
