@@ -362,6 +362,11 @@ __global__ __launch_bounds__(64) void seq_bwd_kernel(Dims d, SeqBwdArgs a, int n
   auto lane_ptr = [&](float* base, int64_t idx, int m) {  // lane-private float4 slot
     return base + ((idx * RPL + m) * 64 + lane) * 4;
   };
+  // chunk mode keeps the replayed states in fp16 (the chunk's entry state is
+  // already fp16): a lane-private 4-half slot in the same per-wave region
+  auto lane_ptr16 = [&](float* base, int64_t idx, int m) {
+    return reinterpret_cast<_Float16*>(base) + ((idx * RPL + m) * 64 + lane) * 4;
+  };
 
   // sequence b: token rows tb .. tb + len - 1 (ragged: offsets cu, lengths
   // clamped to [0, T]); partial sums stay indexed by (b, t) as for B x T
@@ -419,7 +424,14 @@ __global__ __launch_bounds__(64) void seq_bwd_kernel(Dims d, SeqBwdArgs a, int n
     for (int m = 0; m < RPL; ++m) ld4<float>(lane_ptr(ck, c, m), h[m]);
     for (int tau = 0; tau < len; ++tau) {
 #pragma unroll
-      for (int m = 0; m < RPL; ++m) st4<float>(lane_ptr(sc, tau, m), h[m]);
+      for (int m = 0; m < RPL; ++m) {
+        if constexpr (CHK)
+          *reinterpret_cast<h16x4*>(lane_ptr16(sc, tau, m)) =
+              h16x4{static_cast<_Float16>(h[m][0]), static_cast<_Float16>(h[m][1]), static_cast<_Float16>(h[m][2]),
+                    static_cast<_Float16>(h[m][3])};
+        else
+          st4<float>(lane_ptr(sc, tau, m), h[m]);
+      }
       Tok<RPL, CW> x;
       load_tok<D, L, TI, CW, false, false>(x, d, a.q, a.k, a.v, nullptr, a.g, a.beta, tb + t0 + tau, kh, hv, i0,
                                            j0);
@@ -434,7 +446,13 @@ __global__ __launch_bounds__(64) void seq_bwd_kernel(Dims d, SeqBwdArgs a, int n
 #pragma unroll
       for (int m = 0; m < RPL; ++m) {
         float hp[4];
-        ld4<float>(lane_ptr(sc, tau, m), hp);
+        if constexpr (CHK) {
+          const h16x4 v = *reinterpret_cast<const h16x4*>(lane_ptr16(sc, tau, m));
+          hp[0] = static_cast<float>(v[0]); hp[1] = static_cast<float>(v[1]);
+          hp[2] = static_cast<float>(v[2]); hp[3] = static_cast<float>(v[3]);
+        } else {
+          ld4<float>(lane_ptr(sc, tau, m), hp);
+        }
         const float am = alpha_of(x, m);
 #pragma unroll
         for (int e = 0; e < 4; ++e) Dm[m][e] = am * hp[e];
