@@ -405,12 +405,16 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
   constexpr int NT = C / 16, LDA = C + 4, LDC = IM::LDC;
   constexpr int TPR = NTH / C, EPT = DK / TPR, NV = EPT / 8;
   static_assert(C * LDC <= C * LDK, "the fp16 T tile reuses the Qn buffer");
+  static_assert(C * LDA * 4 <= C * LDK * 2, "the fp32 T tile reuses the Kn buffer");
+  // 53 KB in all, so three workgroups share a CU: Kn, then the fp32 T, then
+  // the fp16 P tile [C][LDC] (P waits in registers until then); Qn, then the
+  // fp16 T tile [C][LDC]
   __shared__ __align__(16) _Float16 Ks[C * LDK];
-  __shared__ __align__(16) _Float16 Qs[C * LDK];  // Qn, then the fp16 T tile [C][LDC]
+  __shared__ __align__(16) _Float16 Qs[C * LDK];
   __shared__ __align__(16) float A[C * LDA];
-  __shared__ __align__(16) float Tf[C * LDA];
-  __shared__ __align__(16) _Float16 Pst[C * LDC];
+  float* Tf = reinterpret_cast<float*>(Ks);
   _Float16* Tst = Qs;
+  _Float16* Pst = Ks;
   // zeroes the 16-byte units of a [C][LDC] fp16 tile that lie above its
   // 16 x 16 diagonal blocks (no other thread writes them)
   auto zero_upper = [&](_Float16* M) {
@@ -471,15 +475,24 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
       }
     }
   }
-  zero_upper(Pst);  // P above its diagonal blocks
   __syncthreads();
-  // A (fp32) and P (fp16) on the NT(NT+1)/2 tiles on or below the diagonal,
-  // dealt to the waves; each tile's fragments are read before its products
+  // A (fp32, to LDS) and P (fp16, kept in registers) on the NT(NT+1)/2 tiles
+  // on or below the diagonal, at most two per wave; each tile's fragments
+  // are read before its products
   constexpr int NL = NT * (NT + 1) / 2, KS = DK / 32;
-  for (int t = w; t < NL; t += NW) {
-    int tr = 0;
+  static_assert(NL <= 2 * NW, "two lower tiles per wave at most");
+  auto tile_rc = [](int t, int& tr, int& tc) {
+    tr = 0;
     while ((tr + 1) * (tr + 2) / 2 <= t) ++tr;
-    const int tc = t - tr * (tr + 1) / 2;
+    tc = t - tr * (tr + 1) / 2;
+  };
+  f16x4 preg[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int t = w + it * NW;
+    if (t >= NL) continue;
+    int tr, tc;
+    tile_rc(t, tr, tc);
     f16x8 ka[KS], qa[KS], kb[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -498,7 +511,7 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
       const int r = 16 * tr + 4 * g + e, s2 = 16 * tc + c16;
       const float ex = s2 <= r ? __builtin_amdgcn_exp2f(G2[r] - G2[s2]) : 0.f;
       A[r * LDA + s2] = s2 < r ? bet[r] * ex * kk[e] : 0.f;
-      Pst[r * LDC + s2] = static_cast<_Float16>(ex * qk[e]);
+      preg[it][e] = static_cast<_Float16>(ex * qk[e]);
     }
   }
   // ---- key image (one v-head of each k-head group writes it), while Kn / Qn are intact
@@ -552,6 +565,18 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
     }
     __syncthreads();
   }
+  // P from registers into the Kn / fp32 T space, zero above its diagonal blocks
+  zero_upper(Pst);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int t = w + it * NW;
+    if (t >= NL) continue;
+    int tr, tc;
+    tile_rc(t, tr, tc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Pst[(16 * tr + 4 * g + e) * LDC + 16 * tc + c16] = preg[it][e];
+  }
+  __syncthreads();
 
   // ---- chunk image
   char* cim = a.cimg + ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(IM::CHK);
