@@ -404,17 +404,18 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
   constexpr int NTH = 512, NW = NTH / 64;
   constexpr int NT = C / 16, LDA = C + 4, LDC = IM::LDC;
   constexpr int TPR = NTH / C, EPT = DK / TPR, NV = EPT / 8;
-  static_assert(C * LDC <= C * LDK, "the fp16 T tile reuses the Qn buffer");
-  static_assert(C * LDA * 4 <= C * LDK * 2, "the fp32 T tile reuses the Kn buffer");
-  // 53 KB in all, so three workgroups share a CU: Kn, then the fp32 T, then
-  // the fp16 P tile [C][LDC] (P waits in registers until then); Qn, then the
-  // fp16 T tile [C][LDC]
+  static_assert(C * LDC <= C * LDK, "an fp16 [C][LDC] tile fits a key tile's space");
+  static_assert(C * LDA * 4 <= C * LDK * 2, "an fp32 [C][LDA] tile fits a key tile's space");
+  // 35 KB in all, so four workgroups share a CU.  Two key-tile spaces:
+  // Kn, then A (fp32), then the fp16 T tile [C][LDC]; Qn, then the fp32 T,
+  // then the fp16 P tile [C][LDC].  A and P wait in registers until the
+  // spaces are free.
   __shared__ __align__(16) _Float16 Ks[C * LDK];
   __shared__ __align__(16) _Float16 Qs[C * LDK];
-  __shared__ __align__(16) float A[C * LDA];
-  float* Tf = reinterpret_cast<float*>(Ks);
-  _Float16* Tst = Qs;
-  _Float16* Pst = Ks;
+  float* A = reinterpret_cast<float*>(Ks);
+  float* Tf = reinterpret_cast<float*>(Qs);
+  _Float16* Tst = Ks;
+  _Float16* Pst = Qs;
   // zeroes the 16-byte units of a [C][LDC] fp16 tile that lie above its
   // 16 x 16 diagonal blocks (no other thread writes them)
   auto zero_upper = [&](_Float16* M) {
@@ -476,9 +477,9 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
     }
   }
   __syncthreads();
-  // A (fp32, to LDS) and P (fp16, kept in registers) on the NT(NT+1)/2 tiles
-  // on or below the diagonal, at most two per wave; each tile's fragments
-  // are read before its products
+  // A (fp32) and P (fp16), kept in registers, on the NT(NT+1)/2 tiles on or
+  // below the diagonal, at most two per wave; each tile's fragments are read
+  // before its products
   constexpr int NL = NT * (NT + 1) / 2, KS = DK / 32;
   static_assert(NL <= 2 * NW, "two lower tiles per wave at most");
   auto tile_rc = [](int t, int& tr, int& tc) {
@@ -487,6 +488,7 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
     tc = t - tr * (tr + 1) / 2;
   };
   f16x4 preg[2];
+  f32x4 areg[2];
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int t = w + it * NW;
@@ -510,7 +512,7 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * tr + 4 * g + e, s2 = 16 * tc + c16;
       const float ex = s2 <= r ? __builtin_amdgcn_exp2f(G2[r] - G2[s2]) : 0.f;
-      A[r * LDA + s2] = s2 < r ? bet[r] * ex * kk[e] : 0.f;
+      areg[it][e] = s2 < r ? bet[r] * ex * kk[e] : 0.f;
       preg[it][e] = static_cast<_Float16>(ex * qk[e]);
     }
   }
@@ -522,8 +524,18 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
     write_tile<C, UK, NTH>(kim + IM::KN, [&](int r, int u) { return ld8(Qs + r * LDK + 8 * u); });
   }
   __syncthreads();
-  zero_upper(Tst);  // T above its diagonal blocks
-  if (w < NT && lane < 16) {  // diagonal blocks
+  // A from registers into the Kn space (only its lower tiles are read)
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int t = w + it * NW;
+    if (t >= NL) continue;
+    int tr, tc;
+    tile_rc(t, tr, tc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) A[(16 * tr + 4 * g + e) * LDA + 16 * tc + c16] = areg[it][e];
+  }
+  __syncthreads();
+  if (w < NT && lane < 16) {  // diagonal blocks (entries above the diagonal come out 0)
     const int o = 16 * w;
     float x[16];
 #pragma unroll
@@ -534,10 +546,7 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
       x[r] = acc[0] + acc[1];
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      Tf[(o + r) * LDA + o + lane] = x[r];
-      Tst[(o + r) * LDC + o + lane] = static_cast<_Float16>(x[r]);
-    }
+    for (int r = 0; r < 16; ++r) Tf[(o + r) * LDA + o + lane] = x[r];
   }
   __syncthreads();
   for (int d = 1; d < NT; ++d) {  // blocks below the diagonal, one distance at a time
@@ -558,14 +567,18 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) tij = F32Op::mma(Tf[(16 * i + c16) * LDA + 16 * i + 4 * g + e], m[e], tij);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Tf[(16 * i + 4 * g + e) * LDA + 16 * j + c16] = -tij[e];
-        Tst[(16 * i + 4 * g + e) * LDC + 16 * j + c16] = static_cast<_Float16>(-tij[e]);
-      }
+      for (int e = 0; e < 4; ++e) Tf[(16 * i + 4 * g + e) * LDA + 16 * j + c16] = -tij[e];
     }
     __syncthreads();
   }
-  // P from registers into the Kn / fp32 T space, zero above its diagonal blocks
+  // fp16 T into the A space (A is no longer read), zero above its diagonal blocks
+  zero_upper(Tst);
+  for (int e = tid; e < C * C; e += NTH) {
+    const int r = e / C, s2 = e % C;
+    if (s2 / 16 <= r / 16) Tst[r * LDC + s2] = static_cast<_Float16>(Tf[r * LDA + s2]);
+  }
+  __syncthreads();
+  // P from registers into the fp32 T space, zero above its diagonal blocks
   zero_upper(Pst);
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
