@@ -1051,7 +1051,7 @@ __device__ __forceinline__ void mma_rows(f32x4 (&acc)[NO], const _Float16* A, in
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 
-enum GradMode { kFirst = 0, kMid = 1, kLast = 2, kOnly = 3 };
+enum GradMode { kFirst = 0, kMid = 1, kLast = 2, kOnly = 3, kSplit = 4 };
 
 template <int C, typename TO, int MODE>
 __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
@@ -1079,9 +1079,12 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   float (*sN)[NW][C] = reinterpret_cast<float (*)[NW][C]>(xb + 2 * C * LDQ);
 
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-  const int c = blockIdx.x, kh = blockIdx.y;
+  // kSplit: one launch for all v-heads (blockIdx.y = v-head), each storing
+  // its own dq_hat / dk_hat rows for the epilogue kernel
+  const int c = blockIdx.x;
+  const int hv = MODE == kSplit ? static_cast<int>(blockIdx.y) : static_cast<int>(blockIdx.y) * (a.Hv / a.Hk) + a.gi;
+  const int kh = MODE == kSplit ? hv / (a.Hv / a.Hk) : static_cast<int>(blockIdx.y);
   const int64_t b = blockIdx.z;
-  const int hv = kh * (a.Hv / a.Hk) + a.gi;
   const int64_t t0 = static_cast<int64_t>(c) * C;
   const SeqSpan sp = seq_span(a, b);
   if (t0 >= sp.len) return;  // past the end of a shorter sequence of a ragged batch
@@ -1439,6 +1442,20 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       for (int e = 0; e < 4; ++e) {
         dqv[rt][e] += __uint_as_float(pq[rt][e]);
         dkv[rt][e] += __uint_as_float(pk[rt][e]);
+      }
+  }
+  if constexpr (MODE == kSplit) {  // rows (b * T + t) * Hv + hv of [B * T * Hv][DK]; rows >= L dropped
+    const uint32_t rowp = static_cast<uint32_t>(a.Hv) * DK * 4;
+    const int64_t prow = (b * a.T + t0) * a.Hv + hv;
+    const rsrc_t sq = make_rsrc(a.pdq + prow * DK, static_cast<uint32_t>(L) * rowp);
+    const rsrc_t sk = make_rsrc(a.pdk + prow * DK, static_cast<uint32_t>(L) * rowp);
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t off = (16 * rt + 4 * g + e) * rowp + i2 * 4;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dqv[rt][e]), sq, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dkv[rt][e]), sk, off, 0, 0);
       }
   }
   if constexpr (MODE == kFirst || MODE == kMid) {
@@ -2219,6 +2236,17 @@ struct Ws16 {
   size_t kimg, cimg, hst, dhst, pdq, pdk, total;  // pdq / pdk: group running sums (Hv > Hk)
 };
 
+// The v-heads of a k-head group run their gradient work as consecutive
+// launches (a running sum of dq_hat / dk_hat, the L2-norm VJP in the last)
+// when one launch fills the GPU; with fewer (chunk, k-head, b) workgroups
+// than CUs they run as one launch over every v-head, and the epilogue kernel
+// sums the group and applies the norm VJP.
+constexpr int kCUs = 256;
+bool grad_split(const Shape& s, int C) {
+  const int64_t nc = (s.T + C - 1) / C;
+  return s.Hv > s.Hk && nc * s.Hk * s.B < kCUs;
+}
+
 template <int C>
 Ws16 plan16(const Shape& s, bool bwd) {
   using IM = Img<C>;
@@ -2229,7 +2257,9 @@ Ws16 plan16(const Shape& s, bool bwd) {
   w.kimg = off; off = up(off + nk * IM::KEY);
   w.cimg = off; off = up(off + nv * IM::CHK);
   if (bwd) {
-    const size_t rows = static_cast<size_t>(s.B) * nc * C * s.Hk;  // running-sum tiles per (b, chunk, k-head)
+    // running-sum tiles per (b, chunk, k-head), or with a split gradient
+    // launch the rows of every v-head ([B * T * Hv][DK] <= B * nc * C * Hv rows)
+    const size_t rows = static_cast<size_t>(s.B) * nc * C * (grad_split(s, C) ? s.Hv : s.Hk);
     w.hst = off;  off = up(off + nv * DK * DK * 2);
     w.dhst = off; off = up(off + nv * DK * DK * 2);
     if (s.Hv > s.Hk) {
@@ -2289,8 +2319,19 @@ hipError_t dh16(const K16& a, hipStream_t st) {
 }
 
 template <int C, typename TO>
-hipError_t grad16(K16 a, hipStream_t st) {
+hipError_t grad16(const Shape& s, K16 a, hipStream_t st) {
   const int grp = a.Hv / a.Hk;
+  if (grad_split(s, C)) {
+    {
+      ProfScope ps("chunk_grad", st);
+      hipLaunchKernelGGL((grad16_kernel<C, TO, kSplit>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(512), 0, st,
+                         a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    EpiArgs ea{a.q, a.k, a.pdq, a.pdk, nullptr, nullptr, 1, a.dq, a.dk, a.dbeta, a.dg, a.g, a.beta, a.cu};
+    return launch_bwd_epilogue(s, ea, st);
+  }
   for (int gi = 0; gi < grp; ++gi) {
     a.gi = gi;
     const dim3 grid(a.NC, a.Hk, static_cast<unsigned>(a.B));
@@ -2350,7 +2391,7 @@ hipError_t bwd_all(const Shape& s, const ChunkBwdArgs& x, void* ws, hipStream_t 
     if (e == hipSuccess) e = chain16<C, TO, false, true>(a, st);
   }
   if (e == hipSuccess) e = dh16<C, TO>(a, st);
-  if (e == hipSuccess) e = grad16<C, TO>(a, st);
+  if (e == hipSuccess) e = grad16<C, TO>(s, a, st);
   return e;
 }
 
