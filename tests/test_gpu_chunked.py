@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from gated_delta_rule_54_amd.synth import make_inputs, round_bf16
-from tests.test_gpu_sequential import check_fwd
+from tests.test_gpu_sequential import check_bwd, check_fwd
 
 pytestmark = pytest.mark.gpu
 
@@ -89,6 +89,27 @@ def test_chunked_vjp_sweep(B, T):
                     io_dtype="bf16", h0_std=0.02)
     heads = None if T <= 64 else ([(B - 1, Hk - 1)] if T == 4096 else [(0, 0), (B - 1, 5)])
     check_bwd(x, "bf16", heads=heads, algo=("chunked", 64))
+
+
+@pytest.mark.parametrize("B,T,Hk,Hv,C", [(2, 500, 16, 64, 64), (1, 1000, 16, 48, 32)])
+def test_chunked_vjp_group_launches(B, T, Hk, Hv, C):
+    """The gradient work of a k-head group as consecutive launches (the
+    (chunk, k-head, b) grid fills the GPU): GQA 1:4 and 1:3, so the launches
+    in the middle add to the group's running sum, ragged last chunk, h0 and
+    dht nonzero; sampled groups against the oracle."""
+    x = make_inputs(3100 + T + Hv, B, T, Hk, Hv, 128, 128, io_dtype="bf16", h0_std=0.02)
+    dht = (0.1 * np.random.default_rng(T + Hv).standard_normal((B, Hv, 128, 128))).astype(np.float32)
+    check_bwd(x, "bf16", dht=dht, heads=[(0, 0), (B - 1, Hk - 1)], algo=("chunked", C))
+
+
+@pytest.mark.parametrize("Hk,Hv", [(2, 8), (1, 3)])
+def test_chunked_vjp_split_group(Hk, Hv):
+    """The gradient work of every v-head in one launch with the epilogue
+    summing each group (grid smaller than the GPU): GQA 1:4 and 1:3, ragged
+    last chunk, h0 and dht nonzero; every head against the oracle."""
+    x = make_inputs(3200 + Hv, 2, 130, Hk, Hv, 128, 128, io_dtype="bf16", h0_std=0.02)
+    dht = (0.1 * np.random.default_rng(Hv).standard_normal((2, Hv, 128, 128))).astype(np.float32)
+    check_bwd(x, "bf16", dht=dht, algo=("chunked", 64))
 
 
 @pytest.mark.parametrize("io,D,T,C", [("f32", 16, 70, 32), ("bf16", 128, 150, 64), ("bf16", 128, 77, 32)])
