@@ -356,8 +356,10 @@ __device__ __forceinline__ void unpack8(const uint4& u, float (&x)[8]) {
 }
 
 // Rows of q or k (thread -> row tid / TPR, elements part * EPT ..), each
-// scaled by (sum x^2 + eps)^(-1/2) over Dk when l2 is set (the L2 norm the
-// Megatron-LM page folds into the kernel), written as fp16 to dst[r][LDK].
+// scaled by r = (sum x^2 + eps)^(-1/2) over Dk when l2 is set (the L2 norm
+// the Megatron-LM page folds into the kernel), written as fp16 to
+// dst[r][LDK]; the row's pad (halves DK .. DK+7) holds r as fp32 bits, then
+// zeros (r = 1 when l2 is not set).
 template <int C, int NV, int NTH = 256>
 __device__ __forceinline__ void norm_rows(_Float16* dst, const uint4 (&raw)[NV], int l2) {
   constexpr int TPR = NTH / C, EPT = DK / TPR;
@@ -379,16 +381,18 @@ __device__ __forceinline__ void norm_rows(_Float16* dst, const uint4 (&raw)[NV],
     for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(x[u][i] * rn);
     *reinterpret_cast<f16x8*>(dst + r * LDK + part * EPT + 8 * u) = h;
   }
+  if (part == 0) *reinterpret_cast<uint4*>(dst + r * LDK + DK) = uint4{__float_as_uint(rn), 0u, 0u, 0u};
 }
 
 // Writes an image tile of ROWS rows of UPR 16-byte units (the last unit of a
-// row is its zero pad) to global memory; f(row, unit) gives the 8 values.
-template <int ROWS, int UPR, int NTH = 256, typename F>
+// row is its pad: zeros, or f's values with KEEP_PAD) to global memory;
+// f(row, unit) gives the 8 values.
+template <int ROWS, int UPR, int NTH = 256, bool KEEP_PAD = false, typename F>
 __device__ __forceinline__ void write_tile(char* dst, F&& f) {
   uint4* d = reinterpret_cast<uint4*>(dst);
   for (int e = threadIdx.x; e < ROWS * UPR; e += NTH) {
     const int r = e / UPR, u = e % UPR;
-    d[e] = u == UPR - 1 ? uint4{0u, 0u, 0u, 0u} : __builtin_bit_cast(uint4, f(r, u));
+    d[e] = (u == UPR - 1 && !KEEP_PAD) ? uint4{0u, 0u, 0u, 0u} : __builtin_bit_cast(uint4, f(r, u));
   }
 }
 
@@ -516,12 +520,13 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
       preg[it][e] = static_cast<_Float16>(ex * qk[e]);
     }
   }
-  // ---- key image (one v-head of each k-head group writes it), while Kn / Qn are intact
+  // ---- key image (one v-head of each k-head group writes it), while Kn / Qn
+  // are intact; each row's pad keeps its norm factor r for the L2-norm VJP
   constexpr int UK = DK / 8 + 1;  // 16-byte units per [*][LDK] row
   if (hv % grp == 0) {
     char* kim = a.kimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(IM::KEY);
-    write_tile<C, UK, NTH>(kim, [&](int r, int u) { return ld8(Ks + r * LDK + 8 * u); });
-    write_tile<C, UK, NTH>(kim + IM::KN, [&](int r, int u) { return ld8(Qs + r * LDK + 8 * u); });
+    write_tile<C, UK, NTH, true>(kim, [&](int r, int u) { return ld8(Ks + r * LDK + 8 * u); });
+    write_tile<C, UK, NTH, true>(kim + IM::KN, [&](int r, int u) { return ld8(Qs + r * LDK + 8 * u); });
   }
   __syncthreads();
   // A from registers into the Kn space (only its lower tiles are read)
@@ -1066,16 +1071,15 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   constexpr int DPW = NQ >= NW ? NQ / NW : 1;    // C x C tiles per wave, all in one row tile
   static_assert(5 * C * LDC <= XB, "C x C stage buffers alias the strip buffers");
   static_assert(2 * C * DK <= XB, "raw v / dO tiles fit the strip buffers");
-  static_assert(2 * C * DK <= DK * LDK, "raw q / k tiles fit the state tile");
   static_assert(2 * C * LDQ * 2 + 4 * NW * C * 4 <= XB * 2, "dq / dk tiles and norm partials fit the strip buffers");
   __shared__ __align__(16) char img[IM::CHK + IM::KEY];
   __shared__ __align__(16) _Float16 xb[XB];
-  __shared__ __align__(16) _Float16 Hs[DK * LDK];  // H0, then dH, as Hs[j][i]; then raw q / k rows
+  __shared__ __align__(16) _Float16 Hs[DK * LDK];  // H0, then dH, as Hs[j][i]
   __shared__ __align__(16) float sG[NW][C];
   __shared__ __align__(16) float sB[NW][C];
   __shared__ float sGc[NW][C], red[2][NW];
-  __shared__ __align__(16) float sDot[4][C];
-  // L2-norm VJP row partials |q|^2, q.dq_hat, |k|^2, k.dk_hat, after the dq / dk output tiles
+  __shared__ __align__(16) float sDot[2][C];
+  // L2-norm VJP row partials q_hat . dq_hat, k_hat . dk_hat, after the dq / dk output tiles
   float (*sN)[NW][C] = reinterpret_cast<float (*)[NW][C]>(xb + 2 * C * LDQ);
 
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
@@ -1281,8 +1285,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
 
   // Loads used after the products, issued now: the group's running sums of
   // dq_hat / dk_hat (earlier v-heads; stored per (b, chunk, k-head) in this
-  // kernel's own lane order, 16 bytes per lane and row tile) and, for the
-  // norm VJP, the raw q / k rows of the chunk (rows >= L repeat row L - 1).
+  // kernel's own lane order, 16 bytes per lane and row tile).
   const int64_t ptile = ((b * a.NC + c) * a.Hk + kh) * static_cast<int64_t>(C * DK);
   const rsrc_t pqr = make_rsrc(a.pdq + ptile, C * DK * 4);
   const rsrc_t pkr = make_rsrc(a.pdk + ptile, C * DK * 4);
@@ -1293,23 +1296,6 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     for (int rt = 0; rt < NT; ++rt) {
       pq[rt] = __builtin_amdgcn_raw_buffer_load_b128(pqr, poff(rt), 0, 0);
       pk[rt] = __builtin_amdgcn_raw_buffer_load_b128(pkr, poff(rt), 0, 0);
-    }
-  }
-  constexpr int QKU = C * DK * 2 / 16 / 512;  // 16-byte units of one raw tile per thread
-  u32x4 qraw[QKU], kraw[QKU];
-  const uint32_t rowk = static_cast<uint32_t>(a.Hk) * DK * 2;
-  if constexpr (MODE == kLast || MODE == kOnly) {
-    if (a.l2) {
-      const int64_t seqk = (sp.t0 + t0) * a.Hk * DK;
-      const rsrc_t qr_ = make_rsrc(a.q + seqk, static_cast<uint32_t>(L) * rowk);
-      const rsrc_t kr_ = make_rsrc(a.k + seqk, static_cast<uint32_t>(L) * rowk);
-#pragma unroll
-      for (int u2 = 0; u2 < QKU; ++u2) {
-        const int e = 512 * u2 + tid, row = e / 16, cu = e % 16;
-        const uint32_t off = (row < L ? row : L - 1) * rowk + kh * DK * 2 + 16 * cu;
-        qraw[u2] = __builtin_amdgcn_raw_buffer_load_b128(qr_, off, 0, 0);
-        kraw[u2] = __builtin_amdgcn_raw_buffer_load_b128(kr_, off, 0, 0);
-      }
     }
   }
 
@@ -1475,15 +1461,6 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     red[0][w] = hh;
     red[1][w] = gcx;
   }
-  if constexpr (MODE == kLast || MODE == kOnly) {  // raw q / k rows into the state tile, packed [C][DK]
-    if (a.l2) {
-#pragma unroll
-      for (int u2 = 0; u2 < QKU; ++u2) {
-        *reinterpret_cast<u32x4*>(Hs + (512 * u2 + tid) * 8) = qraw[u2];
-        *reinterpret_cast<u32x4*>(Hs + C * DK + (512 * u2 + tid) * 8) = kraw[u2];
-      }
-    }
-  }
   __syncthreads();
   if (w == 0) {
     const int r = lane;
@@ -1518,35 +1495,37 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     }
   }
   if constexpr (MODE == kLast || MODE == kOnly) {
-    // L2-norm VJP of the group's sums: dx = r (dx_hat - r^2 x (x . dx_hat)),
-    // r = (|x|^2 + eps)^(-1/2), from the raw q / k rows (the Megatron-LM page's
-    // fold of the norm into the kernel, differentiated)
+    // L2-norm VJP of the group's sums: with x_hat = r x and
+    // r = (|x|^2 + eps)^(-1/2), dx = r (dx_hat - x_hat (x_hat . dx_hat)) (the
+    // Megatron-LM page's fold of the norm into the kernel, differentiated);
+    // x_hat from the key image, r from its rows' pads
     if (a.l2) {
-      float xq[NT][4], xk[NT][4];  // raw q / k at this lane's rows 16rt + 4g + e, column i2
+      float xq[NT][4], xk[NT][4];  // q_hat / k_hat at this lane's rows 16rt + 4g + e, column i2
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) {
-        bf16x4_to_f32(xq[rt], tr4(Hs, DK, 16 * rt + 4 * g, 16 * w));
-        bf16x4_to_f32(xk[rt], tr4(Hs + C * DK, DK, 16 * rt + 4 * g, 16 * w));
+        const f16x4 q4 = tr4(Qs, LDK, 16 * rt + 4 * g, 16 * w);
+        const f16x4 k4 = tr4(Ks, LDK, 16 * rt + 4 * g, 16 * w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xq[rt][e] = static_cast<float>(q4[e]);
+          xk[rt][e] = static_cast<float>(k4[e]);
+        }
       }
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float s0 = row16_sum(xq[rt][e] * xq[rt][e]);
           const float s1 = row16_sum(xq[rt][e] * dqv[rt][e]);
-          const float s2 = row16_sum(xk[rt][e] * xk[rt][e]);
           const float s3 = row16_sum(xk[rt][e] * dkv[rt][e]);
           if (c16 == 0) {
             const int r = 16 * rt + 4 * g + e;
-            sN[0][w][r] = s0;
-            sN[1][w][r] = s1;
-            sN[2][w][r] = s2;
-            sN[3][w][r] = s3;
+            sN[0][w][r] = s1;
+            sN[1][w][r] = s3;
           }
         }
       }
       __syncthreads();
-      if (tid < 4 * C) {
+      if (tid < 2 * C) {
         const int m = tid / C, r = tid % C;
         float sum = 0.f;
 #pragma unroll
@@ -1556,15 +1535,15 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       __syncthreads();
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) {
-        const f32x4 qq = *reinterpret_cast<const f32x4*>(&sDot[0][16 * rt + 4 * g]);
-        const f32x4 qd = *reinterpret_cast<const f32x4*>(&sDot[1][16 * rt + 4 * g]);
-        const f32x4 kk2 = *reinterpret_cast<const f32x4*>(&sDot[2][16 * rt + 4 * g]);
-        const f32x4 kd = *reinterpret_cast<const f32x4*>(&sDot[3][16 * rt + 4 * g]);
+        const f32x4 qd = *reinterpret_cast<const f32x4*>(&sDot[0][16 * rt + 4 * g]);
+        const f32x4 kd = *reinterpret_cast<const f32x4*>(&sDot[1][16 * rt + 4 * g]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float rq = rsqrtf(qq[e] + kL2Eps), rk = rsqrtf(kk2[e] + kL2Eps);
-          dqv[rt][e] = rq * (dqv[rt][e] - rq * rq * xq[rt][e] * qd[e]);
-          dkv[rt][e] = rk * (dkv[rt][e] - rk * rk * xk[rt][e] * kd[e]);
+          const int r = 16 * rt + 4 * g + e;
+          const float rq = *reinterpret_cast<const float*>(Qs + r * LDK + DK);
+          const float rk = *reinterpret_cast<const float*>(Ks + r * LDK + DK);
+          dqv[rt][e] = rq * (dqv[rt][e] - xq[rt][e] * qd[e]);
+          dkv[rt][e] = rk * (dkv[rt][e] - xk[rt][e] * kd[e]);
         }
       }
     }
