@@ -394,11 +394,13 @@ __global__ __launch_bounds__(64) void seq_bwd_kernel(Dims d, SeqBwdArgs a, int n
       else h[m][0] = h[m][1] = h[m][2] = h[m][3] = 0.f;
     }
   }
-  // phase 1: checkpoints
+  // phase 1: checkpoints at the start of every segment (the tokens of the
+  // last segment need no forward pass here: phase 2 replays them)
   for (int64_t t = t_beg; t < t_end; ++t) {
     if ((t - t_beg) % kSeqSeg == 0) {
 #pragma unroll
       for (int m = 0; m < RPL; ++m) st4<float>(lane_ptr(ck, (t - t_beg) / kSeqSeg, m), h[m]);
+      if ((t - t_beg) / kSeqSeg == nckb - 1) break;
     }
     Tok<RPL, CW> x;
     load_tok<D, L, TI, CW, false, false>(x, d, a.q, a.k, a.v, nullptr, a.g, a.beta, tb + t, kh, hv, i0, j0);
