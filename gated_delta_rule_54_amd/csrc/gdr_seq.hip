@@ -739,6 +739,8 @@ Dims dims_of(const Shape& s) { return Dims{s.B, s.T, s.Hk, s.Hv, s.l2norm ? 1 : 
 
 template <int D> constexpr int fwd_bv() { return D == 16 ? 16 : 32; }
 constexpr int kDecWaves = 2;  // waves per decode slice (1, 4 and 8 measured slower at B=8, Hv=32)
+// with fewer slices than CUs (B=1, Hv=32: 3.45 vs 3.66 us per step with 2 waves, 3.82 with 8)
+constexpr int kDecSmallGrid = 256, kDecWavesSmall = 4;
 template <int D> constexpr int bwd_bv() { return D == 16 ? 16 : 32; }
 
 template <int D, typename TI, typename TO, bool CW>
@@ -748,6 +750,11 @@ hipError_t fwd_go(const Shape& s, const SeqFwdArgs& a, hipStream_t st) {
   ProfScope ps("seq_fwd", st);
   if constexpr (D == 128) {
     if (s.T == 1) {  // decode step
+      if (s.B * s.Hv * (D / BV) < kDecSmallGrid) {  // fewer slices than CUs: shorter waves
+        hipLaunchKernelGGL((decode_kernel<TI, TO, CW, kDecWavesSmall>), grid, dim3(64 * kDecWavesSmall), 0, st,
+                           dims_of(s), a);
+        return hipGetLastError();
+      }
       hipLaunchKernelGGL((decode_kernel<TI, TO, CW, kDecWaves>), grid, dim3(64 * kDecWaves), 0, st, dims_of(s), a);
       return hipGetLastError();
     }
