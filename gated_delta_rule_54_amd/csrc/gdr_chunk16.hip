@@ -1691,13 +1691,20 @@ __global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
   constexpr int NTH = 512, NT = C / 16, LDA = C + 4, LDC = IM::LDC, LDG = DK + 4;
   constexpr int TPR = NTH / C, EPT = DK / TPR, NV = EPT / 8;
   static_assert(C == 64 || C == 32, "chunk of 32 or 64 rows");
-  __shared__ __align__(16) _Float16 Ks[C * LDK];
-  __shared__ __align__(16) _Float16 Qs[C * LDK];
-  __shared__ __align__(16) float G2[C * LDG];      // log2(e) * G[r][i]
-  __shared__ __align__(16) float A[C * LDA];
-  __shared__ __align__(16) float Tf[C * LDA];
-  __shared__ __align__(16) _Float16 Pst[C * LDC];
-  __shared__ __align__(16) _Float16 Tst[C * LDC];
+  // 79 KB of LDS, so two workgroups share a CU: one space holds Kn, Qn and
+  // the running gate sums G2 until the images are written, then A, the fp32
+  // and fp16 T and the fp16 P tiles (A and P wait in registers meanwhile)
+  constexpr int KSZ = C * LDK * 2, GSZ = C * LDG * 4, ASZ = C * LDA * 4, CSZ = C * LDC * 2;
+  static_assert(2 * ASZ + 2 * CSZ <= 2 * KSZ + GSZ, "A, T and P fit the Kn / Qn / G2 space");
+  __shared__ __align__(16) char U[2 * KSZ + GSZ];
+  _Float16* Ks = reinterpret_cast<_Float16*>(U);
+  _Float16* Qs = reinterpret_cast<_Float16*>(U + KSZ);
+  float* G2 = reinterpret_cast<float*>(U + 2 * KSZ);  // log2(e) * G[r][i]
+  float* A = reinterpret_cast<float*>(U);
+  float* Tf = reinterpret_cast<float*>(U + ASZ);
+  _Float16* Tst = reinterpret_cast<_Float16*>(U + 2 * ASZ);
+  _Float16* Pst = reinterpret_cast<_Float16*>(U + 2 * ASZ + CSZ);
+  __shared__ __align__(16) float dpart[4 * 64 * 8];  // factored diagonal blocks: second channel half's sums
   __shared__ float bet[C];
   __shared__ float part_sum[4 * DK];
 
@@ -1740,8 +1747,6 @@ __global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
       }
       bet[tid] = bv;
     }
-    for (int e = tid; e < C * LDC / 8; e += NTH) reinterpret_cast<uint4*>(Pst)[e] = uint4{0u, 0u, 0u, 0u};
-    for (int e = tid; e < C * LDC / 8; e += NTH) reinterpret_cast<uint4*>(Tst)[e] = uint4{0u, 0u, 0u, 0u};
   }
   float run = 0.f, tv = 0.f;
 #pragma unroll
@@ -1765,13 +1770,14 @@ __global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
   }
   __syncthreads();
 
-  // ---- A (fp32) and P (fp16) on and below the 16 x 16 diagonal blocks.
+  // ---- A and P on and below the 16 x 16 diagonal blocks, into registers.
   // Diagonal block o (rows o .. o+15), factored about its first row:
   //   e^{G_r - G_s} = e^{G_r - G_o} e^{G_o - G_s},
   // on fp32 matrix cores, wave w taking block w % 4 and channel half w / 4
   // (the lane's 16 channels are a relabelling of the contraction index,
   // the same for both operands).
   f32x4 dkk = zero4(), dqk = zero4();
+  float ea[C / 32], ep[C / 32];  // exact diagonal sums: row diag_row(tid / 16, j), column block start + c16
   if (!exact) {
     if ((w & 3) < NT) {
       const int o = 16 * (w & 3), h = w >> 2, row = o + c16;
@@ -1792,16 +1798,18 @@ __global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
         }
       }
       if (h == 1) {  // the second channel half hands its sums to the first
-        float4* part = reinterpret_cast<float4*>(Tf + ((w & 3) * 64 + lane) * 8);
-        part[0] = make_float4(dkk[0], dkk[1], dkk[2], dkk[3]);
-        part[1] = make_float4(dqk[0], dqk[1], dqk[2], dqk[3]);
+        float4* pp = reinterpret_cast<float4*>(dpart + ((w & 3) * 64 + lane) * 8);
+        pp[0] = make_float4(dkk[0], dkk[1], dkk[2], dkk[3]);
+        pp[1] = make_float4(dqk[0], dqk[1], dqk[2], dqk[3]);
       }
     }
   } else {  // exact: a 16-lane group per row, eight channels per lane, one
-            // exponential per pair and channel, four pairs in flight, DPP row sums
+            // exponential per pair and channel, four pairs in flight, DPP row
+            // sums; lane c16 keeps the entry of column (row block start) + c16
     const int grp = tid >> 4, i0 = 8 * c16;
-#pragma unroll 1
+#pragma unroll
     for (int j = 0; j < C / 32; ++j) {
+      ea[j] = ep[j] = 0.f;
       const int rr = diag_row<C>(grp, j), s0 = rr & ~15;
       float gr8[8], kr8[8], qr8[8];
       ld8f(gr8, G2 + rr * LDG + i0);
@@ -1834,15 +1842,10 @@ __global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
         for (int u = 0; u < 4; ++u) {
           kk[u] = row16_sum(kk[u]);
           qk[u] = row16_sum(qk[u]);
-        }
-        if (c16 == 0) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int ss = sb + u;
-            if (ss <= rr) {
-              A[rr * LDA + ss] = ss < rr ? bet[rr] * kk[u] : 0.f;
-              Pst[rr * LDC + ss] = static_cast<_Float16>(qk[u]);
-            }
+          const int ss = sb + u;
+          if (ss <= rr && ss - s0 == c16) {
+            ea[j] = ss < rr ? bet[rr] * kk[u] : 0.f;
+            ep[j] = qk[u];
           }
         }
       }
@@ -1852,11 +1855,14 @@ __global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
   // b = 16R of row block R (both factors <= 1 for g <= 0):
   //   (k_r e^{G_r - G_b}) . (k_s e^{G_b - G_s}), fp16 matrix cores, one tile
   // (both products) per wave, operands built in registers.
-  for (int t = w; t < NT * (NT - 1) / 2; t += 8) {
-    int R = 1;
-    while (R * (R + 1) / 2 <= t) ++R;
-    const int S = t - R * (R - 1) / 2, bref = 16 * R, r = bref + c16, sr = 16 * S + c16;
-    f32x4 kk = zero4(), qk = zero4();
+  constexpr int NOFF = NT * (NT - 1) / 2;
+  static_assert(NOFF <= 8, "one lower tile per wave");
+  f32x4 okk = zero4(), oqk = zero4();
+  int oR = 1, oS = 0;
+  if (w < NOFF) {
+    while (oR * (oR + 1) / 2 <= w) ++oR;
+    oS = w - oR * (oR - 1) / 2;
+    const int bref = 16 * oR, r = bref + c16, sr = 16 * oS + c16;
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
       const int i0 = 32 * ks + 8 * g;
@@ -1874,42 +1880,17 @@ __global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
         aq[q2] = static_cast<_Float16>(static_cast<float>(qv[q2]) * fr);
         bs[q2] = static_cast<_Float16>(static_cast<float>(sv[q2]) * fs);
       }
-      kk = F16Op::mma(ak, bs, kk);
-      qk = F16Op::mma(aq, bs, qk);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rr = bref + 4 * g + e, ss = 16 * S + c16;
-      A[rr * LDA + ss] = bet[rr] * kk[e];
-      Pst[rr * LDC + ss] = static_cast<_Float16>(qk[e]);
+      okk = F16Op::mma(ak, bs, okk);
+      oqk = F16Op::mma(aq, bs, oqk);
     }
   }
-  __syncthreads();
-  if (!exact && w < 4 && w < NT) {  // diagonal blocks: both halves, lower triangle
-    const float4* part = reinterpret_cast<const float4*>(Tf + (w * 64 + lane) * 8);
-    const float4 pk = part[0], pq = part[1];
-    dkk[0] += pk.x; dkk[1] += pk.y; dkk[2] += pk.z; dkk[3] += pk.w;
-    dqk[0] += pq.x; dqk[1] += pq.y; dqk[2] += pq.z; dqk[3] += pq.w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rr = 16 * w + 4 * g + e, ss = 16 * w + c16;
-      if (ss <= rr) {
-        A[rr * LDA + ss] = ss < rr ? bet[rr] * dkk[e] : 0.f;
-        Pst[rr * LDC + ss] = static_cast<_Float16>(dqk[e]);
-      }
-    }
-  }
-  __syncthreads();
-  unit_lower_inverse<C, LDA, LDC>(A, Tf, Tst);
 
-  // ---- images of this (b, v-head, chunk)
+  // ---- images of this (b, v-head, chunk) that need Kn, Qn, G2: the gates
+  // (beta, e^{G_C}) and the three scaled key tiles
   char* cim = a.cimg + ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(IM::CHK);
   float* cg = reinterpret_cast<float*>(cim);
   for (int e = tid; e < C + DK; e += NTH)
     cg[e] = e < C ? bet[e] : __builtin_amdgcn_exp2f(G2[(C - 1) * LDG + e - C]);
-  constexpr int UC = LDC / 8;
-  write_tile<C, UC, NTH>(cim + IM::GT, [&](int r, int u) { return ld8(Tst + r * LDC + 8 * u); });
-  write_tile<C, UC, NTH>(cim + IM::GT + IM::TM, [&](int r, int u) { return ld8(Pst + r * LDC + 8 * u); });
   char* kim = a.kimg + ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(IM::KEY);
   constexpr int UK = LDK / 8;
   // row r, unit u of X o e^G (to_end false) or X o e^{G_C - G} (to_end true)
@@ -1932,6 +1913,52 @@ __global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
   write_tile<C, UK, NTH>(kim, [&](int r, int u) { return scaled(Ks, r, u, false); });
   write_tile<C, UK, NTH>(kim + IM::KN, [&](int r, int u) { return scaled(Qs, r, u, false); });
   write_tile<C, UK, NTH>(kim + 2 * IM::KN, [&](int r, int u) { return scaled(Ks, r, u, true); });
+  __syncthreads();  // Kn, Qn and G2 are no longer read: their space takes A, T and P
+
+  for (int e = tid; e < 2 * CSZ / 16; e += NTH)  // fp16 T and P tiles start at zero
+    reinterpret_cast<uint4*>(Tst)[e] = uint4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  if (w < NOFF) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rr = 16 * oR + 4 * g + e, ss = 16 * oS + c16;
+      A[rr * LDA + ss] = bet[rr] * okk[e];
+      Pst[rr * LDC + ss] = static_cast<_Float16>(oqk[e]);
+    }
+  }
+  if (!exact) {
+    if (w < 4 && w < NT) {  // diagonal blocks: both halves, lower triangle
+      const float4* pp = reinterpret_cast<const float4*>(dpart + (w * 64 + lane) * 8);
+      const float4 pk = pp[0], pq = pp[1];
+      dkk[0] += pk.x; dkk[1] += pk.y; dkk[2] += pk.z; dkk[3] += pk.w;
+      dqk[0] += pq.x; dqk[1] += pq.y; dqk[2] += pq.z; dqk[3] += pq.w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = 16 * w + 4 * g + e, ss = 16 * w + c16;
+        if (ss <= rr) {
+          A[rr * LDA + ss] = ss < rr ? bet[rr] * dkk[e] : 0.f;
+          Pst[rr * LDC + ss] = static_cast<_Float16>(dqk[e]);
+        }
+      }
+    }
+  } else {
+    const int grp = tid >> 4;
+#pragma unroll
+    for (int j = 0; j < C / 32; ++j) {
+      const int rr = diag_row<C>(grp, j), ss = (rr & ~15) + c16;
+      if (ss <= rr) {
+        A[rr * LDA + ss] = ea[j];
+        Pst[rr * LDC + ss] = static_cast<_Float16>(ep[j]);
+      }
+    }
+  }
+  __syncthreads();
+  unit_lower_inverse<C, LDA, LDC>(A, Tf, Tst);
+
+  // ---- T and P images
+  constexpr int UC = LDC / 8;
+  write_tile<C, UC, NTH>(cim + IM::GT, [&](int r, int u) { return ld8(Tst + r * LDC + 8 * u); });
+  write_tile<C, UC, NTH>(cim + IM::GT + IM::TM, [&](int r, int u) { return ld8(Pst + r * LDC + 8 * u); });
 }
 
 // Channelwise forward chain: as chain16, using the scaled key rows of the
