@@ -76,7 +76,8 @@ def kernel_bytes_per_token_head(name, d=D, c=C, grp=HV // HK, saved=True):
     once more for the VJP; chunk_grad runs once per
     v-head of a group, carrying an fp32 running sum of dq_hat / dk_hat per
     k-head between launches (written grp - 1 times, read grp - 1 times), the
-    last launch reading the raw q / k rows and writing dq, dk."""
+    last launch writing dq, dk (its L2-norm VJP takes q_hat, k_hat and the
+    norm factors from the key image it reads anyway)."""
     im = image_bytes(d, c)
     kq = 2 * d * 2 / grp     # k and q rows, bf16
     vec = d * 2              # one bf16 row of v / o / do
@@ -90,7 +91,7 @@ def kernel_bytes_per_token_head(name, d=D, c=C, grp=HV // HK, saved=True):
         "chunk_states": im["KN"] / (c * grp) + (im["GT"] + im["TM"]) / c + vec + st,
         "chunk_dh": im["KEY"] / (c * grp) + im["CHK"] / c + 2 * vec + st,
         "chunk_grad": (im["KEY"] + im["CHK"]) / c + 2 * st + 2 * vec + gates
-                      + (2 * (grp - 1) * 2 * d * 4 + 2 * d * 2 + 2 * d * 2) / grp,
+                      + (2 * (grp - 1) * 2 * d * 4 + 2 * d * 2) / grp,
         "bwd_epilogue": 2 * d * 4 + (2 * d * 2 + 2 * d * 2) / grp,
     }.get(name)
 
