@@ -334,10 +334,21 @@ def bench_vjp_sweep(torch, gdr):
                 ent[f"{algo}_us"] = round(1000.0 * e0.elapsed_time(e1) / reps, 2)
             ent["chunked_tokens_per_s"] = round(b * t_len / (ent["chunked_us"] * 1e-6), 1)
             ent["speedup"] = round(ent["sequential_us"] / ent["chunked_us"], 2)
+            # the chunked VJP against both roofs: the canonical VJP count
+            # (16d^2 + 14Cd + C^2 per token-head, one recompute of the chunk
+            # states included) and the algorithmic bytes of its kernels
+            th = b * t_len * HV
+            sec = ent["chunked_us"] * 1e-6
+            ent["chunked_TFLOPs"] = round((16 * D * D + 14 * C * D + C * C) * th / sec / 1e12, 2)
+            ent["chunked_frac_mfma"] = round(ent["chunked_TFLOPs"] / MFMA_F16_PEAK_TFS, 4)
+            vjp_bytes = sum(kernel_bytes_per_token_head(k) for k in ("chunk_prep", "chunk_states", "chunk_dh",
+                                                                      "chunk_grad"))
+            ent["chunked_frac_hbm"] = round(vjp_bytes * th / sec / 1e9 / HBM_PEAK_GBS, 4)
             out[f"B={b},T={t_len}"] = ent
             del t
     out["config"] = (f"Hk={HK} Hv={HV} Dk=Dv={D}, bf16 io, scalar gate, zero h0, chunk {C}; "
-                     "stateless VJP, sequential against chunked")
+                     "stateless VJP, sequential against chunked; chunked_frac_* against the fp16 MFMA and "
+                     "HBM peaks")
     return out
 
 
