@@ -129,6 +129,13 @@ __device__ __forceinline__ void dma(rsrc_t r, uint32_t off, char* dst, int tid, 
 
 __device__ __forceinline__ f16x8 ld8(const _Float16* p) { return *reinterpret_cast<const f16x8*>(p); }
 
+// Eight consecutive fp32 values at p (16-byte aligned).
+__device__ __forceinline__ void ld8f(float (&x)[8], const float* p) {
+  const float4 a0 = *reinterpret_cast<const float4*>(p), a1 = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
+  x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
+}
+
 // A fragment of A[m][k] (k contiguous) for the relabelled 32-column block kb:
 // elements 0..3 <- k = 32kb + 4g + 0..3, 4..7 <- 32kb + 16 + 4g + 0..3.
 __device__ __forceinline__ f16x8 perm_frag(const _Float16* A, int ld, int m, int kb) {
@@ -411,15 +418,14 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
   static_assert(C * LDC <= C * LDK, "an fp16 [C][LDC] tile fits a key tile's space");
   static_assert(C * LDA * 4 <= C * LDK * 2, "an fp32 [C][LDA] tile fits a key tile's space");
   // 35 KB in all, so four workgroups share a CU.  Two key-tile spaces:
-  // Kn, then A (fp32), then the fp16 T tile [C][LDC]; Qn, then the fp32 T,
-  // then the fp16 P tile [C][LDC].  A and P wait in registers until the
-  // spaces are free.
+  // Kn, then A (fp32), then the fp16 P tile [C][LDC]; Qn, then the fp32 T
+  // (its image is converted to fp16 as it is written).  A and P wait in
+  // registers until the spaces are free.
   __shared__ __align__(16) _Float16 Ks[C * LDK];
   __shared__ __align__(16) _Float16 Qs[C * LDK];
   float* A = reinterpret_cast<float*>(Ks);
   float* Tf = reinterpret_cast<float*>(Qs);
-  _Float16* Tst = Ks;
-  _Float16* Pst = Qs;
+  _Float16* Pst = Ks;
   // zeroes the 16-byte units of a [C][LDC] fp16 tile that lie above its
   // 16 x 16 diagonal blocks (no other thread writes them)
   auto zero_upper = [&](_Float16* M) {
@@ -576,14 +582,8 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
     }
     __syncthreads();
   }
-  // fp16 T into the A space (A is no longer read), zero above its diagonal blocks
-  zero_upper(Tst);
-  for (int e = tid; e < C * C; e += NTH) {
-    const int r = e / C, s2 = e % C;
-    if (s2 / 16 <= r / 16) Tst[r * LDC + s2] = static_cast<_Float16>(Tf[r * LDA + s2]);
-  }
-  __syncthreads();
-  // P from registers into the fp32 T space, zero above its diagonal blocks
+  // P from registers into the A space (A is no longer read), zero above its
+  // diagonal blocks
   zero_upper(Pst);
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
@@ -601,7 +601,20 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
   for (int e = tid; e < C; e += NTH)
     reinterpret_cast<float4*>(cim)[e] = reinterpret_cast<const float4*>(gates)[e];
   constexpr int UC = C / 8 + 1;  // 16-byte units per [*][LDC] row
-  write_tile<C, UC, NTH>(cim + IM::GT, [&](int r, int u) { return ld8(Tst + r * LDC + 8 * u); });
+  // T from the fp32 tile, zero above its diagonal blocks (never written there)
+  write_tile<C, UC, NTH>(cim + IM::GT, [&](int r, int u) {
+    f16x8 v;
+    if (u / 2 > r / 16) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = static_cast<_Float16>(0.f);
+    } else {
+      float x[8];
+      ld8f(x, Tf + r * LDA + 8 * u);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = static_cast<_Float16>(x[q]);
+    }
+    return v;
+  });
   write_tile<C, UC, NTH>(cim + IM::GT + IM::TM, [&](int r, int u) { return ld8(Pst + r * LDC + 8 * u); });
 }
 
@@ -1672,12 +1685,6 @@ __device__ __forceinline__ void unit_lower_inverse(const float* A, float* Tf, _F
   }
 }
 
-// Eight consecutive fp32 values at p (16-byte aligned).
-__device__ __forceinline__ void ld8f(float (&x)[8], const float* p) {
-  const float4 a0 = *reinterpret_cast<const float4*>(p), a1 = *reinterpret_cast<const float4*>(p + 4);
-  x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
-  x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
-}
 
 // Rows of the 16-row diagonal blocks that 16-lane group grp (0..31) of a
 // cwprep workgroup sums: C = 64: block grp & 3, local rows {w, 15 - w} of
