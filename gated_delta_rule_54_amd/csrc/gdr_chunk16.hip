@@ -667,11 +667,12 @@ __device__ __forceinline__ void dma_rows(rsrc_t r, uint32_t rowb, uint32_t col0,
   }
 }
 
-// Rows r0 .. r0+3 of column c0 + (lane & 15) of a packed bf16 [*][ld] tile, as fp32.
+// Rows r0 .. r0+3 of column c0 + (lane & 15) of a packed bf16 [*][ld] tile,
+// as fp32, by one transpose read (tr4's lane addressing; the bits are moved,
+// not converted).  r0 is the same for the lanes of a 16-lane group, and the
+// calling wave has no LDS copies in flight.
 __device__ __forceinline__ void tile_col4_bf16(float (&x)[4], const uint16_t* M, int ld, int r0, int c0) {
-  const int n = c0 + (lane_id() & 15);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(static_cast<uint32_t>(M[(r0 + e) * ld + n]) << 16);
+  bf16x4_to_f32(x, tr4(reinterpret_cast<const _Float16*>(M), ld, r0, c0));
 }
 
 // Output tile of one chunk and value half: [C][LDO] elements of TO.
