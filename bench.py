@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFS = 2500.0   # MI355X dense fp16/bf16 matrix cores, TFLOP/s
+VALU_F32_PEAK_TFS = 157.3    # MI355X fp32 vector ALUs, TFLOP/s
 
 B, T, HK, HV, D, C = 4, 4096, 16, 32, 128, 64
 DEC_B, DEC_STEPS, DEC_BUFFERS = 8, 256, 32
@@ -344,11 +345,15 @@ def bench_vjp_sweep(torch, gdr):
             vjp_bytes = sum(kernel_bytes_per_token_head(k) for k in ("chunk_prep", "chunk_states", "chunk_dh",
                                                                       "chunk_grad"))
             ent["chunked_frac_hbm"] = round(vjp_bytes * th / sec / 1e9 / HBM_PEAK_GBS, 4)
+            # the sequential VJP on the fp32 vector ALUs: about 22 d^2 FLOPs per
+            # token-head (forward replay, reverse step, checkpoint pass)
+            ent["sequential_TFLOPs"] = round(22 * D * D * th / (ent["sequential_us"] * 1e-6) / 1e12, 3)
+            ent["sequential_frac_valu"] = round(ent["sequential_TFLOPs"] / VALU_F32_PEAK_TFS, 4)
             out[f"B={b},T={t_len}"] = ent
             del t
     out["config"] = (f"Hk={HK} Hv={HV} Dk=Dv={D}, bf16 io, scalar gate, zero h0, chunk {C}; "
                      "stateless VJP, sequential against chunked; chunked_frac_* against the fp16 MFMA and "
-                     "HBM peaks")
+                     "HBM peaks, sequential_frac_valu against the fp32 vector-ALU peak")
     return out
 
 
