@@ -112,6 +112,66 @@ def test_chunked_vjp_split_group(Hk, Hv):
     check_bwd(x, "bf16", dht=dht, algo=("chunked", 64))
 
 
+BF16_OUT = ("o", "dq", "dk", "dv")  # rounded to bf16 by out_dtype; ht, dg, dbeta, dh0 stay fp32
+
+
+def check_bf16_out(x, heads, C, save, dht=None):
+    """Chunked forward + VJP with bf16 outputs (the benchmark's launch
+    configuration), optionally through GDR_SAVE_CHUNKS, against the oracle on
+    the (b, k-head) groups in heads; bf16-rounded outputs get 2^-8 more."""
+    import torch
+    import gated_delta_rule_54_amd as gdr
+    from oracle import gdr_oracle as orc
+    from tests._util import dev, host, relerr
+    from tests.test_gpu_sequential import group_slice, to_dev
+    t = to_dev(x, "bf16")
+    kw = dict(algo="chunked", chunk_size=C, out_dtype=torch.bfloat16)
+    res = gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], save_for_backward=save, **kw)
+    grads = gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], t["do"], dev(dht),
+                             saved=res[2] if save else None, **kw)
+    torch.cuda.synchronize()
+    assert res[0].dtype == torch.bfloat16 and grads[0].dtype == torch.bfloat16
+    o, ht = host(res[0]), host(res[1])
+    grads = [host(a) for a in grads]
+    grp = x["v"].shape[2] // x["q"].shape[2]
+    for (b, kh) in heads:
+        xs = group_slice(x, b, kh, grp)
+        vs = slice(kh * grp, (kh + 1) * grp)
+        dh = None if dht is None else dht[b:b + 1, vs]
+        ro, rht = orc.forward(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], xs["h0"])
+        ref = orc.backward(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], xs["h0"], xs["do"], dh)
+        got = {"o": o[b:b + 1, :, vs], "ht": ht[b:b + 1, vs]}
+        exp = {"o": ro, "ht": rht}
+        for name, a, r in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), grads, ref):
+            got[name] = (a[b:b + 1, :, kh:kh + 1] if name in ("dq", "dk")
+                         else a[b:b + 1, vs] if name == "dh0" else a[b:b + 1, :, vs])
+            exp[name] = r
+        for name in got:
+            e = relerr(got[name], exp[name])
+            print(f"  b={b} kh={kh} {name}: {e:.2e}")
+            assert e < 2e-3 + (2 ** -8 if name in BF16_OUT else 0.0), (name, e)
+
+
+@pytest.mark.parametrize("save", [False, True])
+def test_bf16_outputs_small(save):
+    """bf16 o / dq / dk / dv on a small GQA 2:4 problem with a ragged last
+    chunk (grid smaller than the GPU: one gradient launch plus the epilogue),
+    h0 and dht nonzero."""
+    x = make_inputs(3300 + save, 2, 150, 2, 4, 128, 128, io_dtype="bf16", h0_std=0.02)
+    dht = (0.1 * np.random.default_rng(33).standard_normal((2, 4, 128, 128))).astype(np.float32)
+    check_bf16_out(x, [(0, 0), (0, 1), (1, 0), (1, 1)], 64, save, dht)
+
+
+def test_bf16_outputs_benchmark_shape():
+    """The benchmark's step: B=4, T=4096, Hk=16, Hv=32, D=128, C=64, bf16 io
+    and outputs, the forward saving its chunks for the VJP (gradient work as
+    consecutive launches, the last one writing bf16 dq / dk through LDS);
+    two sampled (b, k-head) groups against the oracle."""
+    x = make_inputs(3400, 4, 4096, 16, 32, 128, 128, io_dtype="bf16")  # zero h0, as benchmarked
+    assert x["h0"] is None
+    check_bf16_out(x, [(0, 0), (3, 15)], 64, True)
+
+
 @pytest.mark.parametrize("io,D,T,C", [("f32", 16, 70, 32), ("bf16", 128, 150, 64), ("bf16", 128, 77, 32)])
 def test_fused_gates_chunked(io, D, T, C):
     """GDR_FUSED_GATES on the chunked path (fp32 operands at D=16, fp16
