@@ -88,6 +88,41 @@ def test_ragged_chunked_vjp_group_launches():
     run_and_check([0, 1, 130, 200], "bf16", "chunked", 64, seed=7, Hk=32, Hv=64)
 
 
+def test_ragged_bf16_outputs_benchmark_heads():
+    """The ragged prefill leg's launch configuration: Hk=16, Hv=32, D=128,
+    C=64, bf16 io and outputs, the forward saving its chunks for the VJP, on
+    sequences of 1 to 1,911 tokens; sampled (sequence, k-head) groups against
+    the oracle run on that sequence alone (bf16-rounded o / dq / dk / dv get
+    2^-8 more)."""
+    lengths, Hk, Hv, D = [128, 1911, 1, 700, 1300], 16, 32, 128
+    seqs, packed, cu = ragged_inputs(lengths, Hk, Hv, D, "bf16", seed=41, dht=False)
+    t = to_dev(packed, "bf16")
+    cud = torch.from_numpy(cu).cuda()
+    kw = dict(algo="chunked", chunk_size=64, cu_seqlens=cud, out_dtype=torch.bfloat16)
+    o, ht, saved = gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], save_for_backward=True, **kw)
+    grads = gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], t["do"], None, saved=saved, **kw)
+    torch.cuda.synchronize()
+    o, ht = host(o), host(ht)
+    grads = [host(a) for a in grads]
+    grp = Hv // Hk
+    for i, kh in ((1, 3), (2, 0), (4, 15)):
+        x, r0, r1, vs = seqs[i], cu[i], cu[i + 1], slice(kh * grp, (kh + 1) * grp)
+        xs = {n: x[n][:, :, kh:kh + 1] if n in ("q", "k") else x[n][:, :, vs] for n in ("q", "k", "v", "g", "beta", "do")}
+        xs["h0"] = x["h0"][:, vs]
+        ro, rht = orc.forward(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], xs["h0"])
+        ref = orc.backward(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], xs["h0"], xs["do"], None)
+        got = {"o": o[:, r0:r1, vs], "ht": ht[i:i + 1, vs]}
+        exp = {"o": ro, "ht": rht}
+        for name, a, r in zip(GRAD_NAMES + ("dh0",), grads, ref):
+            got[name] = (a[i:i + 1, vs] if name == "dh0" else a[:, r0:r1, kh:kh + 1] if name in ("dq", "dk")
+                         else a[:, r0:r1, vs])
+            exp[name] = r
+        for name in got:
+            e = relerr(got[name], exp[name])
+            print(f"  seq {i} kh {kh} {name}: {e:.2e}")
+            assert e < TOL["bf16"] + (2 ** -8 if name in ("o", "dq", "dk", "dv") else 0.0), (i, name, e)
+
+
 def test_ragged_length_bound_above_every_length():
     """max_seqlen larger than every length (more workspace chunks than any
     sequence uses)."""
