@@ -115,7 +115,7 @@ def test_chunked_vjp_split_group(Hk, Hv):
 BF16_OUT = ("o", "dq", "dk", "dv")  # rounded to bf16 by out_dtype; ht, dg, dbeta, dh0 stay fp32
 
 
-def check_bf16_out(x, heads, C, save, dht=None, cw=False):
+def check_bf16_out(x, heads, C, save, dht=None, cw=False, fg=False):
     """Chunked forward + VJP with bf16 outputs (the benchmark's launch
     configuration), optionally through GDR_SAVE_CHUNKS, against the oracle on
     the (b, k-head) groups in heads; bf16-rounded outputs get 2^-8 more."""
@@ -125,7 +125,7 @@ def check_bf16_out(x, heads, C, save, dht=None, cw=False):
     from tests._util import dev, host, relerr
     from tests.test_gpu_sequential import group_slice, to_dev
     t = to_dev(x, "bf16")
-    kw = dict(algo="chunked", chunk_size=C, out_dtype=torch.bfloat16, channelwise=cw)
+    kw = dict(algo="chunked", chunk_size=C, out_dtype=torch.bfloat16, channelwise=cw, fused_gates=fg)
     res = gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], save_for_backward=save, **kw)
     grads = gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], t["do"], dev(dht),
                              saved=res[2] if save else None, **kw)
@@ -138,8 +138,10 @@ def check_bf16_out(x, heads, C, save, dht=None, cw=False):
         xs = group_slice(x, b, kh, grp)
         vs = slice(kh * grp, (kh + 1) * grp)
         dh = None if dht is None else dht[b:b + 1, vs]
-        ro, rht = orc.forward(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], xs["h0"], channelwise=cw)
-        ref = orc.backward(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], xs["h0"], xs["do"], dh, channelwise=cw)
+        ro, rht = orc.forward(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], xs["h0"], channelwise=cw,
+                              fused_gates=fg)
+        ref = orc.backward(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], xs["h0"], xs["do"], dh, channelwise=cw,
+                           fused_gates=fg)
         got = {"o": o[b:b + 1, :, vs], "ht": ht[b:b + 1, vs]}
         exp = {"o": ro, "ht": rht}
         for name, a, r in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), grads, ref):
@@ -170,6 +172,13 @@ def test_bf16_outputs_benchmark_shape():
     x = make_inputs(3400, 4, 4096, 16, 32, 128, 128, io_dtype="bf16")  # zero h0, as benchmarked
     assert x["h0"] is None
     check_bf16_out(x, [(0, 0), (3, 15)], 64, True)
+
+
+def test_bf16_outputs_fused_gates_benchmark_shape():
+    """The fused-gate leg of the benchmark: B=4, T=4096, g and beta passed as
+    pre-activations, bf16 outputs, saved chunks; one sampled group."""
+    x = make_inputs(3450, 4, 4096, 16, 32, 128, 128, io_dtype="bf16", gate_preact=True)
+    check_bf16_out(x, [(2, 9)], 64, True, fg=True)
 
 
 def test_bf16_outputs_channelwise_prefill_shape():
