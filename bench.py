@@ -199,9 +199,9 @@ def bench_decode(torch, gdr, graph=True):
         ms, n = kt["seq_fwd"]
         us = 1000.0 * ms / n
         state_bytes = 2 * DEC_B * HV * D * D * 4
-        out[label] = {"kernel_us_per_step": round(us, 3), "wall_us_per_step": round(1e6 * wall / DEC_STEPS, 2),
-                      "state_GBps": round(state_bytes / (us * 1e-6) / 1e9, 1),
-                      "frac_hbm_peak": round(state_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        out[label] = {"launch_event_us_per_step": round(us, 3), "wall_us_per_step": round(1e6 * wall / DEC_STEPS, 2),
+                      "launch_event_state_GBps": round(state_bytes / (us * 1e-6) / 1e9, 1),
+                      "launch_event_frac_hbm_peak": round(state_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         if not graph:
             continue
         # the same steps captured once into a HIP graph and replayed: no host
@@ -222,6 +222,9 @@ def bench_decode(torch, gdr, graph=True):
                            "graph_state_GBps": round(state_bytes / (gus * 1e-6) / 1e9, 1),
                            "graph_frac_hbm_peak": round(state_bytes / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
     out["state_bytes_per_step"] = 2 * DEC_B * HV * D * D * 4
+    out["note"] = ("launch_event_*: library HIP events around each launch, which include its dispatch; graph_*: "
+                   "one replayed HIP graph of all steps, the closest to the kernel's own duration "
+                   "(rocprofv3 kernel trace in profiles/)")
     out["config"] = f"B={DEC_B} Hk={HK} Hv={HV} Dk=Dv={D}, {DEC_STEPS} single-token steps, bf16 io, fp32 state"
     return out
 
