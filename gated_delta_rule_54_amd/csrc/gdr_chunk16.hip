@@ -1908,27 +1908,36 @@ __global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
   for (int e = tid; e < C + DK; e += NTH)
     cg[e] = e < C ? bet[e] : __builtin_amdgcn_exp2f(G2[(C - 1) * LDG + e - C]);
   char* kim = a.kimg + ((b * a.Hv + hv) * a.NC + c) * static_cast<int64_t>(IM::KEY);
-  constexpr int UK = LDK / 8;
-  // row r, unit u of X o e^G (to_end false) or X o e^{G_C - G} (to_end true)
-  auto scaled = [&](const _Float16* X, int r, int u, bool to_end) {
-    float gx[8];
-    ld8f(gx, G2 + r * LDG + 8 * u);
-    if (to_end) {
-      float ge[8];
+  constexpr int UK = LDK / 8;  // 16-byte units per [*][LDK] row, the last one the zero pad
+  // The three scaled key tiles in one pass: unit u of row r of K o e^G,
+  // Q o e^G and K o e^{G_C - G} share the row's reads of G and K.
+  {
+    uint4* dkg = reinterpret_cast<uint4*>(kim);
+    uint4* dqg = reinterpret_cast<uint4*>(kim + IM::KN);
+    uint4* dkl = reinterpret_cast<uint4*>(kim + 2 * IM::KN);
+    for (int e = tid; e < C * UK; e += NTH) {
+      const int r = e / UK, u = e % UK;
+      if (u == UK - 1) {
+        dkg[e] = dqg[e] = dkl[e] = uint4{0u, 0u, 0u, 0u};
+        continue;
+      }
+      float gx[8], ge[8];
+      ld8f(gx, G2 + r * LDG + 8 * u);
       ld8f(ge, G2 + (C - 1) * LDG + 8 * u);
+      const f16x8 kv = ld8(Ks + r * LDK + 8 * u), qv = ld8(Qs + r * LDK + 8 * u);
+      f16x8 okg, oqg, okl;
 #pragma unroll
-      for (int q2 = 0; q2 < 8; ++q2) gx[q2] = ge[q2] - gx[q2];
+      for (int q2 = 0; q2 < 8; ++q2) {
+        const float f = __builtin_amdgcn_exp2f(gx[q2]), fl = __builtin_amdgcn_exp2f(ge[q2] - gx[q2]);
+        okg[q2] = static_cast<_Float16>(static_cast<float>(kv[q2]) * f);
+        oqg[q2] = static_cast<_Float16>(static_cast<float>(qv[q2]) * f);
+        okl[q2] = static_cast<_Float16>(static_cast<float>(kv[q2]) * fl);
+      }
+      dkg[e] = __builtin_bit_cast(uint4, okg);
+      dqg[e] = __builtin_bit_cast(uint4, oqg);
+      dkl[e] = __builtin_bit_cast(uint4, okl);
     }
-    const f16x8 xv = ld8(X + r * LDK + 8 * u);
-    f16x8 v;
-#pragma unroll
-    for (int q2 = 0; q2 < 8; ++q2)
-      v[q2] = static_cast<_Float16>(static_cast<float>(xv[q2]) * __builtin_amdgcn_exp2f(gx[q2]));
-    return v;
-  };
-  write_tile<C, UK, NTH>(kim, [&](int r, int u) { return scaled(Ks, r, u, false); });
-  write_tile<C, UK, NTH>(kim + IM::KN, [&](int r, int u) { return scaled(Qs, r, u, false); });
-  write_tile<C, UK, NTH>(kim + 2 * IM::KN, [&](int r, int u) { return scaled(Ks, r, u, true); });
+  }
   __syncthreads();  // Kn, Qn and G2 are no longer read: their space takes A, T and P
 
   for (int e = tid; e < 2 * CSZ / 16; e += NTH)  // fp16 T and P tiles start at zero
