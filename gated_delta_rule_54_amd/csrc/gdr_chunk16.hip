@@ -76,7 +76,8 @@ struct K16 {
   float* dh0;
   char *kimg, *cimg;       // [B][Hk][NC] key images, [B][Hv][NC] chunk images
   _Float16 *hst, *dhst;    // [B][Hv][NC][DK][DK]: chunk-entry H, chunk-end dH
-  float *pdq, *pdk;        // [B][T][Hk][DK] running sums of dq_hat / dk_hat over a group's v-heads
+  float *pdq, *pdk;        // dq_hat / dk_hat over a group's v-heads: running-sum tiles per (b, chunk, k-head)
+                           // in the gradient kernel's lane order, or, split launch, rows [B][T][Hv][DK]
   void *dq, *dk;           // [B][T][Hk][DK] out dtype
   float *dg, *dbeta;       // [B][T][Hv]
   int64_t B, T;
@@ -1046,9 +1047,10 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
 //            dP = dO U^T (C x C tiles dealt to the waves).
 //   Phase 2  X3 = U dH^T, dT = dU RHS^T.
 //   Then the C x C stage (dA = -T^T dT T^T), dq_hat / dk_hat of this v-head
-//   (wave w: Dk tile w), dbeta and dg.  H0 / dH are read straight from
-//   global memory: as chained strips for phase A and as row fragments for
-//   phases 1 and 2.
+//   (wave w: Dk tile w), dbeta and dg.  H0 / dH come from global memory
+//   once, as the chained strips the chain kernels store (phase A operands);
+//   phases 1 and 2 take their row fragments from a transposed LDS copy Hs
+//   written from those strips (H0 first, then dH).
 // ---------------------------------------------------------------------------
 // acc[t] += A[16t : 16t+16, 0:K] Bm[0:K, n0 : n0+16], Bm row-major; the B
 // fragment is shared.

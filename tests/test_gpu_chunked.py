@@ -313,3 +313,42 @@ def test_channelwise_chunked_vjp_prefill_t2048():
     k-head groups against the oracle."""
     x = make_inputs(1960, 1, 2048, 16, 32, 128, 128, io_dtype="bf16", channelwise=True)
     check_bwd(x, "bf16", cw=True, h0=False, heads=[(0, 3)], algo=("chunked", 64))
+
+
+# ------------------------------------------------ long sequence
+
+def test_long_sequence_saved_chunks():
+    """One sequence of 65,535 tokens (1,024 chunks of 64, the last one 63
+    rows): the chunk grids' longest axis and a workspace of a thousand chunk
+    states per head.  GQA 2:4, D=128, bf16 io, fp32 outputs, h0 and dht
+    nonzero, the forward saving its chunks for the VJP; k-head group 1
+    (v-heads 2, 3) against the oracle over the whole sequence."""
+    import torch
+    import gated_delta_rule_54_amd as gdr
+    from oracle import gdr_oracle as orc
+    from tests._util import dev, host, relerr
+    from tests.test_gpu_sequential import group_slice, to_dev
+    T = 65535
+    x = make_inputs(6553, 1, T, 2, 4, 128, 128, io_dtype="bf16", h0_std=0.02)
+    dht = (0.1 * np.random.default_rng(6553).standard_normal((1, 4, 128, 128))).astype(np.float32)
+    t = to_dev(x, "bf16")
+    kw = dict(algo="chunked", chunk_size=64)
+    o, ht, saved = gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], save_for_backward=True, **kw)
+    grads = gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], t["do"], dev(dht), saved=saved,
+                             **kw)
+    torch.cuda.synchronize()
+    o, ht = host(o), host(ht)
+    grads = [host(a) for a in grads]
+    del t, saved
+    xs, vs = group_slice(x, 0, 1, 2), slice(2, 4)
+    ro, rht = orc.forward(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], xs["h0"])
+    ref = orc.backward(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], xs["h0"], xs["do"], dht[:, vs])
+    got = {"o": o[:, :, vs], "ht": ht[:, vs]}
+    exp = {"o": ro, "ht": rht}
+    for name, a, r in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), grads, ref):
+        got[name] = a[:, :, 1:2] if name in ("dq", "dk") else a[:, vs] if name == "dh0" else a[:, :, vs]
+        exp[name] = r
+    for name in got:
+        e = relerr(got[name], exp[name])
+        print(f"  T={T} kh=1 {name}: {e:.2e}")
+        assert e < 2e-3, (name, e)
