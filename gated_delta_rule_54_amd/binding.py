@@ -177,15 +177,46 @@ def _save_key(prob):
 
 
 def _ragged_dims(q, cu_seqlens, max_seqlen):
-    """(number of sequences, length bound) of a ragged batch."""
+    """(number of sequences, length bound) of a ragged batch.  Without
+    ``max_seqlen`` the offsets are read back once and checked (start at or
+    after row 0, non-decreasing, end at or before the last row); with it the
+    caller vouches for them and nothing waits on the device."""
     if q.shape[0] != 1:
         raise ValueError("a ragged batch holds its sequences in one row: q must be [1, rows, Hk, Dk]")
     if cu_seqlens.dtype != torch.int64 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
         raise TypeError("cu_seqlens must be a 1-d int64 device tensor")
+    if cu_seqlens.device != q.device:
+        raise ValueError("cu_seqlens must be on the device of q")
     n = cu_seqlens.numel() - 1
+    if n < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
     if max_seqlen is None:
-        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if n > 0 else 0
+        cu = cu_seqlens.cpu()
+        lens = cu[1:] - cu[:-1]
+        if int(cu[0]) < 0 or int(cu[-1]) > q.shape[1] or (n > 0 and int(lens.min()) < 0):
+            raise ValueError(f"cu_seqlens must rise from >= 0 to <= {q.shape[1]} rows")
+        max_seqlen = int(lens.max()) if n > 0 else 0
+    elif max_seqlen < 0:
+        raise ValueError("max_seqlen must be >= 0")
     return n, max_seqlen
+
+
+def _check_shapes(B, T, Hk, Hv, Dk, Dv, N, channelwise, tensors):
+    """Every operand's shape against the problem the call describes (the
+    library takes pointers and sizes only, so this is the last place a
+    mismatch can be caught), and every operand on one device.  B, T are the
+    tensor dims (1, rows for a ragged batch); N is the number of states."""
+    want = {"q": (B, T, Hk, Dk), "k": (B, T, Hk, Dk), "v": (B, T, Hv, Dv), "dout": (B, T, Hv, Dv),
+            "g": (B, T, Hv, Dk) if channelwise else (B, T, Hv), "beta": (B, T, Hv),
+            "h0": (N, Hv, Dk, Dv), "ht": (N, Hv, Dk, Dv), "dht": (N, Hv, Dk, Dv)}
+    dev = tensors["q"].device
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if tuple(t.shape) != want[name]:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want[name]}")
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, q on {dev}")
 
 
 def gdr_forward(q, k, v, g, beta, h0=None, *, use_qk_l2norm=True, channelwise=False,
@@ -208,8 +239,11 @@ def gdr_forward(q, k, v, g, beta, h0=None, *, use_qk_l2norm=True, channelwise=Fa
     for t, n in ((g, "g"), (beta, "beta"), (h0, "h0")):
         _check(t, n, torch.float32)
     o = torch.empty((B, T, Hv, Dv), dtype=out_dtype, device=q.device)
+    B0, T0 = B, T
     if cu_seqlens is not None:  # ragged batch: q [1, rows, Hk, Dk], one state per sequence
         B, T = _ragged_dims(q, cu_seqlens, max_seqlen)
+    _check_shapes(B0, T0, Hk, Hv, Dk, Dv, B, channelwise,
+                  dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0, ht=ht if ht is not True and ht is not None else None))
     prob = make_problem(B, T, Hk, Hv, Dk, Dv, q.dtype, out_dtype, use_qk_l2norm,
                         channelwise, algo, chunk_size, fused_gates, save_for_backward)
     if ht is True:
@@ -251,16 +285,21 @@ def gdr_backward(q, k, v, g, beta, h0, dout, dht=None, *, use_qk_l2norm=True,
     dv = torch.empty((B, T, Hv, Dv), dtype=out_dtype, device=dev)
     dg = torch.empty(g.shape, dtype=torch.float32, device=dev)
     dbeta = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
+    B0, T0 = B, T
     if cu_seqlens is not None:
         B, T = _ragged_dims(q, cu_seqlens, max_seqlen)
+    _check_shapes(B0, T0, Hk, Hv, Dk, Dv, B, channelwise,
+                  dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0, dout=dout, dht=dht))
     prob = make_problem(B, T, Hk, Hv, Dk, Dv, q.dtype, out_dtype, use_qk_l2norm,
                         channelwise, algo, chunk_size, fused_gates, saved is not None)
     if saved is not None and saved.key != _save_key(prob):
         raise ValueError("saved chunks belong to a different problem")
     dh0 = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=dev) if want_dh0 else None
     nws = gdr_backward_workspace(prob)
-    if saved is not None and saved.ws is not None and saved.ws.numel() >= nws:
-        ws = saved.ws  # the forward's images and chunk states
+    if saved is not None:  # the forward's images and chunk states
+        if nws > 0 and (saved.ws is None or saved.ws.numel() < nws):
+            raise ValueError("saved chunks hold a workspace smaller than the backward needs")
+        ws = saved.ws
     else:
         ws = _workspace(nws, dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(dout), _ptr(dht),

@@ -185,3 +185,30 @@ def test_varlen_validation():
     assert call_bwd_varlen(prob(algo=2, **bf), FAKE) == 1           # chunked: workspace missing
     assert call_bwd_varlen(prob(algo=1, **bf), FAKE) == 1           # sequential: workspace missing
     assert call_bwd_varlen(prob(algo=0, T=256), FAKE) == 1          # AUTO -> sequential
+
+
+def test_binding_shape_checks():
+    """The binding compares every operand's shape with the problem before it
+    calls the library (which takes pointers and sizes only): a wrong head
+    count, token count, gate shape or state shape raises ValueError."""
+    import torch
+    Bb, T, Hk, Hv, D = 2, 5, 2, 4, 16
+    ok = dict(q=torch.zeros(Bb, T, Hk, D), k=torch.zeros(Bb, T, Hk, D), v=torch.zeros(Bb, T, Hv, D),
+              g=torch.zeros(Bb, T, Hv), beta=torch.zeros(Bb, T, Hv), h0=torch.zeros(Bb, Hv, D, D),
+              dout=torch.zeros(Bb, T, Hv, D), dht=None)
+    B._check_shapes(Bb, T, Hk, Hv, D, D, Bb, False, ok)
+    B._check_shapes(Bb, T, Hk, Hv, D, D, Bb, True, dict(ok, g=torch.zeros(Bb, T, Hv, D)))
+    bad = [("k", torch.zeros(Bb, T, Hv, D)), ("v", torch.zeros(Bb, T - 1, Hv, D)),
+           ("g", torch.zeros(Bb, T, Hv, D)), ("beta", torch.zeros(Bb, T, Hk)),
+           ("h0", torch.zeros(Bb, Hk, D, D)), ("dout", torch.zeros(Bb, T, Hv, 2 * D)),
+           ("dht", torch.zeros(1, Hv, D, D))]
+    for name, t in bad:
+        with pytest.raises(ValueError, match=name):
+            B._check_shapes(Bb, T, Hk, Hv, D, D, Bb, False, dict(ok, **{name: t}))
+    # ragged: tensors [1, rows, ...], N states
+    rag = dict(ok, q=torch.zeros(1, 9, Hk, D), k=torch.zeros(1, 9, Hk, D), v=torch.zeros(1, 9, Hv, D),
+               g=torch.zeros(1, 9, Hv), beta=torch.zeros(1, 9, Hv), dout=torch.zeros(1, 9, Hv, D),
+               h0=torch.zeros(3, Hv, D, D))
+    B._check_shapes(1, 9, Hk, Hv, D, D, 3, False, rag)
+    with pytest.raises(ValueError, match="h0"):
+        B._check_shapes(1, 9, Hk, Hv, D, D, 2, False, rag)

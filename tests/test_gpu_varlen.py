@@ -174,3 +174,26 @@ def test_ragged_sequential_vjp(io, D, cw):
 
 def test_ragged_channelwise_chunked_vjp():
     run_and_check([0, 90, 1, 150], "bf16", "chunked", 64, cw=True, seed=29)
+
+
+def test_ragged_offsets_and_shapes_checked_before_launch():
+    """Offsets past the packed rows, before row 0 or falling, and operands
+    whose shape disagrees with the problem, raise ValueError in the binding
+    before anything is launched (offsets are read back when max_seqlen is not
+    given)."""
+    seqs, packed, cu = ragged_inputs([10, 20], 2, 4, 128, "bf16", dht=False)
+    t = to_dev(packed, "bf16")
+    args = (t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"])
+    for bad in ([0, 10, 31], [0, 20, 10], [-1, 10, 30]):
+        with pytest.raises(ValueError, match="cu_seqlens"):
+            gdr.gdr_forward(*args, algo="chunked", chunk_size=64,
+                            cu_seqlens=torch.tensor(bad, dtype=torch.int64, device="cuda"))
+    cud = torch.from_numpy(cu).cuda()
+    with pytest.raises(ValueError, match="h0"):
+        gdr.gdr_forward(*args[:5], t["h0"][:1].contiguous(), algo="chunked", chunk_size=64, cu_seqlens=cud)
+    with pytest.raises(ValueError, match="v"):
+        gdr.gdr_forward(t["q"], t["k"], t["v"][:, :29].contiguous(), *args[3:], algo="chunked", chunk_size=64,
+                        cu_seqlens=cud)
+    with pytest.raises(ValueError, match="dout"):
+        gdr.gdr_backward(*args, t["do"][..., :64].contiguous(), None, algo="chunked", chunk_size=64, cu_seqlens=cud)
+    torch.cuda.synchronize()
