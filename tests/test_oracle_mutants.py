@@ -54,6 +54,9 @@ MUTANTS = {
     "chunk carry ignores in-chunk decay":
         ("        Kt = np.exp(last[:, :, None, :] - Gc) * Kc              # exp(G_L - G_s) k_s\n",
          "        Kt = Kc\n"),
+    "channelwise decay on the value axis":
+        ("    return a[..., :, None] if channelwise else a[..., None, None]\n",
+         "    return a[..., None, :] if channelwise else a[..., None, None]\n"),
 }
 
 
@@ -156,8 +159,34 @@ def check_gqa_block_map(orc):
     return relerr(o2[:, :, :2], o1[:, :, :2]) < 1e-14
 
 
+def check_hand_examples(orc):
+    """The 2x2 examples worked by hand in tests/golden/hand_worked_2x2.yaml."""
+    import yaml
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_worked_2x2.yaml")
+    with open(path) as fh:
+        cases = yaml.safe_load(fh)
+    for c in cases.values():
+        cw = c["channelwise"]
+        a = lambda key: np.asarray(c[key], dtype=np.float64)
+        T = len(c["q"])
+        q, k, v = (a(n).reshape(1, T, 1, 2) for n in ("q", "k", "v"))
+        g = np.log(a("alpha")).reshape((1, T, 1, 2) if cw else (1, T, 1))
+        beta = a("beta").reshape(1, T, 1)
+        h0 = None if c["h0"] is None else a("h0").reshape(1, 1, 2, 2)
+        o, ht = orc.forward(q, k, v, g, beta, h0, use_qk_l2norm=False, channelwise=cw)
+        if np.max(np.abs(o.reshape(T, 2) - a("o"))) > 1e-12 or np.max(np.abs(ht.reshape(2, 2) - a("ht"))) > 1e-12:
+            return False
+        if "dout" in c:
+            got = orc.backward(q, k, v, g, beta, h0, a("dout").reshape(1, T, 1, 2), None, use_qk_l2norm=False,
+                               channelwise=cw)
+            for key, x in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), got):
+                if np.max(np.abs(np.asarray(x).reshape(a(key).shape) - a(key))) > 1e-12:
+                    return False
+    return True
+
+
 CHECKS = [check_fd, check_closed_forms, check_chunked, check_caller_norm,
-          check_gqa_block_map]
+          check_gqa_block_map, check_hand_examples]
 
 
 def test_unmutated_oracle_passes_every_check():

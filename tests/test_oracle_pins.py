@@ -438,3 +438,35 @@ def test_p16_fused_gates_autograd_of_the_textbook_form():
     grads = orc.backward(q, k, v, a, b, h0, do, dht, fused_gates=True)
     for gi, tt in enumerate(tens):
         assert relerr(grads[gi], tt.grad.numpy()) < 1e-11, gi
+
+
+def test_p17_hand_worked_examples():
+    """Two examples worked by hand on 2x2 states (tests/golden/
+    hand_worked_2x2.yaml, derivations in the file): a two-token scalar-gate
+    forward, and a one-token channelwise forward with its full VJP, which
+    fixes the key-channel side of the per-channel decay ([ET] summary) and
+    every gradient's sign and index."""
+    import os
+    import yaml
+    path = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_2x2.yaml")
+    with open(path) as fh:
+        cases = yaml.safe_load(fh)
+    assert set(cases) == {"scalar_two_tokens", "channelwise_one_token_with_vjp"}
+    for name, c in cases.items():
+        cw = c["channelwise"]
+        a = lambda key: np.asarray(c[key], dtype=np.float64)
+        T = len(c["q"])
+        q, k, v = (a(n).reshape(1, T, 1, 2) for n in ("q", "k", "v"))
+        g = np.log(a("alpha")).reshape((1, T, 1, 2) if cw else (1, T, 1))
+        beta = a("beta").reshape(1, T, 1)
+        h0 = None if c["h0"] is None else a("h0").reshape(1, 1, 2, 2)
+        o, ht = orc.forward(q, k, v, g, beta, h0, use_qk_l2norm=False, channelwise=cw)
+        np.testing.assert_allclose(o.reshape(T, 2), a("o"), rtol=0, atol=1e-12, err_msg=name)
+        np.testing.assert_allclose(ht.reshape(2, 2), a("ht"), rtol=0, atol=1e-12, err_msg=name)
+        if "dout" not in c:
+            continue
+        do = a("dout").reshape(1, T, 1, 2)
+        got = orc.backward(q, k, v, g, beta, h0, do, None, use_qk_l2norm=False, channelwise=cw)
+        for key, x in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), got):
+            np.testing.assert_allclose(np.asarray(x).reshape(a(key).shape), a(key), rtol=0, atol=1e-12,
+                                       err_msg=f"{name} {key}")
