@@ -228,23 +228,32 @@ def test_fused_gates_decode_bf16_d128(cw):
     check_bwd(x, "bf16", cw=cw, fg=True)
 
 
-@pytest.mark.parametrize("algo", ["sequential", ("chunked", 16)])
-def test_hand_worked_examples(algo):
+@pytest.mark.parametrize("io,D,algo", [("f32", 16, "sequential"), ("f32", 16, ("chunked", 16)),
+                                       ("bf16", 128, "sequential"), ("bf16", 128, ("chunked", 64))])
+def test_hand_worked_examples(io, D, algo):
     """The 2x2 examples worked by hand (tests/golden/hand_worked_2x2.yaml),
-    zero-padded to Dk = Dv = 16 (the padding stays zero through the
-    recurrence and every gradient), fp32, no L2 norm: the HIP path against the
-    hand-derived values directly.  The channelwise case runs on the
-    sequential path only (the fp32 chunked path has a scalar gate)."""
+    zero-padded to Dk = Dv = D (the padding stays zero through the
+    recurrence and every gradient), no L2 norm: the HIP path against the
+    hand-derived values directly.  The channelwise case is skipped on the
+    fp32 chunked path (scalar gate only); with bf16 io only cases whose
+    inputs bf16 holds exactly run (the channelwise one, through the fp16
+    matrix-core kernels when chunked), at 5e-3."""
     import os
     import yaml
+    from gated_delta_rule_54_amd.synth import round_bf16
     with open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked_2x2.yaml")) as fh:
         cases = yaml.safe_load(fh)
-    D = 16
+    tol = 1e-5 if io == "f32" else 5e-3
+    ran = 0
     for name, c in cases.items():
         cw = c["channelwise"]
-        if cw and algo != "sequential":
+        if cw and io == "f32" and algo != "sequential":
             continue
         a = lambda key: np.asarray(c[key], dtype=np.float32)
+        if io == "bf16" and any(not np.array_equal(round_bf16(a(n)), a(n)) for n in ("q", "k", "v", "dout")
+                                if n in c):
+            continue
+        ran += 1
         T = len(c["q"])
 
         def pad_rows(x, lead):
@@ -257,23 +266,25 @@ def test_hand_worked_examples(algo):
         h0 = np.zeros((1, 1, D, D), np.float32)
         if c["h0"] is not None:
             h0[0, 0, :2, :2] = a("h0")
-        t = {n: dev(x) for n, x in dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0).items()}
+        t = {n: dev(x, io_dtype(io) if n in ("q", "k", "v") else torch.float32)
+             for n, x in dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0).items()}
         kw = dict(use_qk_l2norm=False, channelwise=cw, **algo_kw(algo))
         o, ht = gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], **kw)
         want_o = pad_rows(a("o"), (1, T, 1))
         want_ht = np.zeros((1, 1, D, D), np.float32)
         want_ht[0, 0, :2, :2] = a("ht")
         torch.cuda.synchronize()
-        assert np.max(np.abs(host(o) - want_o)) < 1e-5, (name, "o")
-        assert np.max(np.abs(host(ht) - want_ht)) < 1e-5, (name, "ht")
+        assert np.max(np.abs(host(o) - want_o)) < tol, (name, "o")
+        assert np.max(np.abs(host(ht) - want_ht)) < tol, (name, "ht")
         if "dout" not in c:
             continue
         grads = gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"],
-                                 dev(pad_rows(a("dout"), (1, T, 1))), None, **kw)
+                                 dev(pad_rows(a("dout"), (1, T, 1)), io_dtype(io)), None, **kw)
         torch.cuda.synchronize()
         want = {"dq": pad_rows(a("dq"), (1, T, 1)), "dk": pad_rows(a("dk"), (1, T, 1)),
                 "dv": pad_rows(a("dv"), (1, T, 1)), "dg": pad_rows(a("dg"), (1, T, 1)),
                 "dbeta": a("dbeta").reshape(1, T, 1), "dh0": np.zeros((1, 1, D, D), np.float32)}
         want["dh0"][0, 0, :2, :2] = a("dh0")
         for key, x in zip(GRAD_NAMES, grads):
-            assert np.max(np.abs(host(x) - want[key])) < 1e-5, (name, key, host(x).ravel()[:4])
+            assert np.max(np.abs(host(x) - want[key])) < tol, (name, key, host(x).ravel()[:4])
+    assert ran > 0
