@@ -33,29 +33,55 @@ B, T, HK, HV, D, C = 4, 4096, 16, 32, 128, 64
 DEC_B, DEC_STEPS, DEC_BUFFERS = 8, 256, 32
 
 
-def kernel_flops_per_token_head(name, d=D, c=C, saved=True):
-    """Algorithmic FLOPs each kernel does in one step, per (token, v-head),
-    summed over its launches in the step: every matrix product counted once
-    at 2mnk, products whose result is used only on one triangle of a C x C
-    block counted at half.  chunk_prep runs once per step when the forward
-    saves its chunks for the VJP (saved), else twice."""
+# ---- algorithmic counts of the method (per (token, v-head)) ---------------
+# FLOPs: every matrix product once at 2mnk, products used on one triangle of
+# a C x C block at half.  Canonical step count (forward + VJP with one
+# recompute of the chunk states and chunk operands, as a stateless VJP
+# needs): F_fwd = 6d^2 + 5Cd + C^2/3, F_bwd = 16d^2 + 14Cd + C^2.
+# Bytes: the method's own tensors (q, k, v, g, beta, o; dout, dq, dk, dv,
+# dg, dbeta; bf16 rows, fp32 gates), each moved once, q/k rows shared by the
+# grp v-heads of a k-head; intermediates a design chooses to materialise are
+# never counted.  Per step that is 24,832 B/token for the forward and
+# 41,472 B/token for the VJP at Hk=16, Hv=32, d=128, plus ht / dh0.
+
+
+def canonical_flops_per_token_head(d=D, c=C):
+    """F_fwd + F_bwd per (token, v-head)."""
+    return (6 * d * d + 5 * c * d + c * c / 3) + (16 * d * d + 14 * c * d + c * c)
+
+
+def algorithmic_bytes_per_token(d=D, hk=HK, hv=HV):
+    """Minimum HBM bytes of one forward + VJP step per token (without the
+    B * Hv * d^2 * 4 bytes of ht and of dh0)."""
+    row_k, row_v, gates = hk * d * 2, hv * d * 2, hv * 4
+    fwd = 2 * row_k + row_v + 2 * gates + row_v                       # q, k, v, g, beta -> o
+    bwd = 2 * row_k + 2 * row_v + 2 * gates + 2 * row_k + row_v + 2 * gates  # q,k,v,do,g,beta -> dq,dk,dv,dg,dbeta
+    return fwd + bwd
+
+
+def kernel_share_per_token_head(name, d=D, c=C, grp=HV // HK):
+    """(FLOPs, bytes) of the method that a kernel carries, per (token,
+    v-head), summed over its launches in one step.  The canonical FLOPs are
+    split by the step of the chunk algebra each kernel performs: prep forms
+    A, P (2Cd) and T = (I + A)^-1 (C^2/3); a forward chain the inter-chunk
+    products (6d^2 + 3Cd); the reverse chain dU, dRHS and the dH update
+    (6d^2 + 3Cd); the gradient kernel the rest of F_bwd less the recompute
+    (6d^2 + 8Cd + 2C^2/3).  Bytes are the method's tensors the kernel must
+    read or write (q/k rows counted once per k-head group)."""
+    kq = 2 * d * 2 / grp     # q and k rows (bf16), shared by the group
+    row = d * 2              # one bf16 row of v / o / dout / dv
+    gates = 8                # g and beta (fp32)
+    prep_f = 2 * c * d + c * c / 3
+    chain_f = 6 * d * d + 3 * c * d
+    grad_f = 6 * d * d + 8 * c * d + 2 * c * c / 3
     return {
-        "chunk_prep": (1 if saved else 2) * (c * d + c * c / 3),
-        "chunk_fwd": 6 * d * d + 3 * c * d,
-        "chunk_fwd_save": 6 * d * d + 3 * c * d,
-        "chunk_states": 4 * d * d + c * d,
-        "chunk_dh": 6 * d * d + 3 * c * d,
-        "chunk_grad": 10 * d * d + 12 * c * d + 2 * c * c / 3,
+        "chunk_prep": (prep_f, kq + gates),
+        "chunk_fwd": (chain_f, 2 * row),
+        "chunk_fwd_save": (chain_f, 2 * row),
+        "chunk_states": (4 * d * d + c * d, row),
+        "chunk_dh": (chain_f, 2 * row),
+        "chunk_grad": (grad_f, kq + 2 * row + gates + kq + gates),
     }.get(name)
-
-
-def canonical_flops_per_token_head(d=D, c=C, saved=True):
-    """Minimal fwd + bwd count: fwd 6d^2 + 5Cd + C^2/3, bwd (with one
-    recompute of the chunk states) 16d^2 + 14Cd + C^2; when the forward saves
-    its chunk states and operands for the VJP (saved) the recompute, one state
-    pass 4d^2 + Cd and one prep Cd + C^2/3, is not part of the step."""
-    full = (6 * d * d + 5 * c * d + c * c / 3) + (16 * d * d + 14 * c * d + c * c)
-    return full - (4 * d * d + c * d + c * d + c * c / 3) if saved else full
 
 
 def image_bytes(d=D, c=C):
@@ -67,18 +93,17 @@ def image_bytes(d=D, c=C):
     return {"KEY": 2 * kn, "CHK": gt + 2 * tm, "KN": kn, "TM": tm, "GT": gt}
 
 
-def kernel_bytes_per_token_head(name, d=D, c=C, grp=HV // HK, saved=True):
-    """Algorithmic HBM bytes each kernel moves in one step, per (token,
-    v-head), summed over its launches: what it must read and write once, with
-    k/q rows and key images shared by the `grp` v-heads of a k-head (bf16 io
-    and outputs, fp16 images and chunk states, fp32 gates).  chunk_prep runs
-    once for the forward and, unless the forward saved its chunks for the
-    VJP (saved; then chunk_fwd_save also stores every chunk's entry state),
-    once more for the VJP; chunk_grad runs once per
-    v-head of a group, carrying an fp32 running sum of dq_hat / dk_hat per
-    k-head between launches (written grp - 1 times, read grp - 1 times), the
-    last launch writing dq, dk (its L2-norm VJP takes q_hat, k_hat and the
-    norm factors from the key image it reads anyway)."""
+def design_bytes_per_token_head(name, d=D, c=C, grp=HV // HK, saved=True):
+    """HBM bytes each kernel of this design moves in one step, per (token,
+    v-head), summed over its launches: what the kernel reads and writes once,
+    including the intermediates the design materialises (operand images,
+    fp16 chunk states, chunk-end gradients); k/q rows and key images shared
+    by the `grp` v-heads of a k-head.  This is the design's own traffic, not
+    the method's minimum (kernel_share_per_token_head).  chunk_prep runs once
+    for the forward and, unless the forward saved its chunks for the VJP,
+    once more for the VJP; chunk_grad covers a whole k-head group per
+    workgroup (the key image once, both v-heads' chunk images, states, v and
+    dout rows; dq, dk written once)."""
     im = image_bytes(d, c)
     kq = 2 * d * 2 / grp     # k and q rows, bf16
     vec = d * 2              # one bf16 row of v / o / do
@@ -91,9 +116,7 @@ def kernel_bytes_per_token_head(name, d=D, c=C, grp=HV // HK, saved=True):
         "chunk_fwd_save": im["KEY"] / (c * grp) + im["CHK"] / c + 2 * vec + st,
         "chunk_states": im["KN"] / (c * grp) + (im["GT"] + im["TM"]) / c + vec + st,
         "chunk_dh": im["KEY"] / (c * grp) + im["CHK"] / c + 2 * vec + st,
-        "chunk_grad": (im["KEY"] + im["CHK"]) / c + 2 * st + 2 * vec + gates
-                      + (2 * (grp - 1) * 2 * d * 4 + 2 * d * 2) / grp,
-        "bwd_epilogue": 2 * d * 4 + (2 * d * 2 + 2 * d * 2) / grp,
+        "chunk_grad": im["KEY"] / (c * grp) + im["CHK"] / c + 2 * st + 2 * vec + gates + 2 * d * 2 / grp,
     }.get(name)
 
 
@@ -302,7 +325,8 @@ def bench_channelwise(torch, gdr, reps=20):
 def bench_vjp_sweep(torch, gdr):
     """The backward sweep of the page "Adding VJP for gated delta net"
     (ml-explore/mlx pull request 4565, "Performance"): B in {1, 4, 8} x T in
-    {8, 64, 512, 4096}, Hk=16, Hv=32, D=128, bf16 io, zero h0, do ~ N(0, 1).
+    {8, 64, 512, 4096}, Hk=16, Hv=32, D=128, bf16 io, h0 ~ N(0, 0.02),
+    do ~ N(0, 1).
     The stateless VJP (gdr_backward alone, which recomputes what it needs),
     chunked (C=64) against sequential; time per call from events around
     back-to-back calls.  Inputs drawn on the device with the same
@@ -312,11 +336,12 @@ def bench_vjp_sweep(torch, gdr):
     rn = lambda *s: torch.randn(*s, device="cuda", generator=gen)
     full = {"q": rn(bmax, tmax, HK, D).bfloat16(), "k": rn(bmax, tmax, HK, D).bfloat16(),
             "v": rn(bmax, tmax, HV, D).bfloat16(), "do": rn(bmax, tmax, HV, D).bfloat16(),
-            "g": -torch.nn.functional.softplus(rn(bmax, tmax, HV)), "beta": torch.sigmoid(rn(bmax, tmax, HV))}
+            "g": -torch.nn.functional.softplus(rn(bmax, tmax, HV)), "beta": torch.sigmoid(rn(bmax, tmax, HV)),
+            "h0": rn(bmax, HV, D, D) * 0.02}
     out = {}
     for b in (1, 4, 8):
         for t_len in (8, 64, 512, 4096):
-            t = {n: a[:b, :t_len].contiguous() for n, a in full.items()}
+            t = {n: (a[:b] if n == "h0" else a[:b, :t_len]).contiguous() for n, a in full.items()}
             ent = {}
             for algo in ("sequential", "chunked"):
                 kw = dict(algo=algo, out_dtype=torch.bfloat16)
@@ -324,7 +349,7 @@ def bench_vjp_sweep(torch, gdr):
                     kw["chunk_size"] = C
 
                 def vjp():
-                    gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], None, t["do"], **kw)
+                    gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], t["do"], **kw)
 
                 vjp()
                 torch.cuda.synchronize()
@@ -343,18 +368,21 @@ def bench_vjp_sweep(torch, gdr):
             # states included) and the algorithmic bytes of its kernels
             th = b * t_len * HV
             sec = ent["chunked_us"] * 1e-6
-            ent["chunked_TFLOPs"] = round((16 * D * D + 14 * C * D + C * C) * th / sec / 1e12, 2)
+            cc = min(C, t_len)
+            ent["chunked_TFLOPs"] = round((16 * D * D + 14 * cc * D + cc * cc) * th / sec / 1e12, 2)
             ent["chunked_frac_mfma"] = round(ent["chunked_TFLOPs"] / MFMA_F16_PEAK_TFS, 4)
-            vjp_bytes = sum(kernel_bytes_per_token_head(k) for k in ("chunk_prep", "chunk_states", "chunk_dh",
-                                                                      "chunk_grad"))
-            ent["chunked_frac_hbm"] = round(vjp_bytes * th / sec / 1e9 / HBM_PEAK_GBS, 4)
+            # the VJP's minimum I/O: q, k, v, dout, g, beta in; dq, dk, dv,
+            # dg, dbeta out (41,472 B per token here), plus h0 and dh0
+            vjp_bytes = (4 * HK * D * 2 + 2 * HV * D * 2 + 4 * HV * 4 + HV * D * 2) * b * t_len \
+                + 2 * b * HV * D * D * 4
+            ent["chunked_frac_hbm"] = round(vjp_bytes / sec / 1e9 / HBM_PEAK_GBS, 4)
             # the sequential VJP on the fp32 vector ALUs: about 22 d^2 FLOPs per
             # token-head (forward replay, reverse step, checkpoint pass)
             ent["sequential_TFLOPs"] = round(22 * D * D * th / (ent["sequential_us"] * 1e-6) / 1e12, 3)
             ent["sequential_frac_valu"] = round(ent["sequential_TFLOPs"] / VALU_F32_PEAK_TFS, 4)
             out[f"B={b},T={t_len}"] = ent
             del t
-    out["config"] = (f"Hk={HK} Hv={HV} Dk=Dv={D}, bf16 io, scalar gate, zero h0, chunk {C}; "
+    out["config"] = (f"Hk={HK} Hv={HV} Dk=Dv={D}, bf16 io, scalar gate, h0 ~ N(0, 0.02), chunk {C}; "
                      "stateless VJP, sequential against chunked; chunked_frac_* against the fp16 MFMA and "
                      "HBM peaks, sequential_frac_valu against the fp32 vector-ALU peak")
     return out
@@ -479,30 +507,78 @@ def bench_ragged(torch, gdr, reps=10):
     return out
 
 
-def cpu_baseline(min_seconds=10.0, max_groups=32):
-    """The fp64 oracle (forward + VJP) on (b, k-head) groups of the
-    full-length workload (each group = the 2 v-heads sharing a k-head), run
-    until at least `min_seconds` of CPU work, scaled to whole-workload
-    tokens/s."""
-    import numpy as np
-    from gated_delta_rule_54_amd.synth import make_inputs
-    from oracle import gdr_oracle as orc
+_GROUP_INPUTS = None  # the workload's host inputs, shared with forked workers
+
+
+def _oracle_group(i):
+    """fp64 oracle forward + VJP of (b, k-head) group i of the workload (its
+    Hv/Hk v-heads over the full length) on one thread; returns seconds."""
     from threadpoolctl import threadpool_limits
-    x = make_inputs(2, 1, T, 1, HV // HK, D, D, io_dtype="bf16")
+    from oracle import gdr_oracle as orc
+    x, grp = _GROUP_INPUTS, HV // HK
+    b, kh = divmod(i, HK)
+    sl = lambda a, h0, h1: np.ascontiguousarray(a[b:b + 1, :, h0:h1])
+    q, k = sl(x["q"], kh, kh + 1), sl(x["k"], kh, kh + 1)
+    v, do = sl(x["v"], grp * kh, grp * kh + grp), sl(x["do"], grp * kh, grp * kh + grp)
+    g, beta = sl(x["g"], grp * kh, grp * kh + grp), sl(x["beta"], grp * kh, grp * kh + grp)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        sample_groups = 0
-        while sample_groups < max_groups and (sample_groups == 0 or time.perf_counter() - t0 < min_seconds):
-            orc.forward(x["q"], x["k"], x["v"], x["g"], x["beta"])
-            orc.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], None, x["do"])
-            sample_groups += 1
-        sec = time.perf_counter() - t0
-    heads = sample_groups * (HV // HK)
-    whole = sec * (B * HV) / heads
-    return {"value": round(B * T / whole, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{sample_groups} (b, k-head) group(s) = {heads} v-heads x T={T} fwd+bwd in fp64 "
-                      f"numpy ({sec:.1f} s, one thread); scaled by {B * HV // heads}x to B={B}, Hv={HV}",
-            "cpu_model": _cpu_model(), "host_threads": os.cpu_count()}
+        orc.forward(q, k, v, g, beta)
+        orc.backward(q, k, v, g, beta, None, do)
+        return time.perf_counter() - t0
+
+
+def host_cpu_share():
+    """Worker processes for the oracle: the CPUs this process may run on,
+    at most 16 (the host share that goes with one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline():
+    """The fp64 oracle (forward + VJP, numpy, one BLAS thread per process)
+    timed on the host: a sample of the headline workload's (b, k-head)
+    groups (each = the Hv/Hk v-heads of one k-head over all T tokens), one
+    group per worker process, all workers at once; whole-workload tokens/s
+    from the sample's wall time.  Also the oracle's single-thread seconds on
+    the tiny case (B=1, T=64, Hk=Hv=2, D=16, fp32, fwd + VJP) and on the
+    decode case (B=8, Hk=16, Hv=32, D=128, 256 tokens, forward).  Must run
+    before anything touches the GPU: the pool is forked."""
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_limits
+    from gated_delta_rule_54_amd.synth import make_inputs
+    from oracle import gdr_oracle as orc
+    global _GROUP_INPUTS
+    _GROUP_INPUTS = make_inputs(2, B, T, HK, HV, D, D, io_dtype="bf16")
+    cores = host_cpu_share()
+    n_groups = B * HK
+    sample = min(n_groups, cores)
+    with mp.get_context("fork").Pool(cores) as pool:
+        w0 = time.perf_counter()
+        secs = pool.map(_oracle_group, range(sample), chunksize=1)
+        wall = time.perf_counter() - w0
+    _GROUP_INPUTS = None
+    whole = wall * n_groups / sample  # the sample is one round of the pool
+    single = {}
+    with threadpool_limits(limits=1):
+        x = make_inputs(0, 1, 64, 2, 2, 16, 16, io_dtype="f32")
+        t0 = time.perf_counter()
+        orc.forward(x["q"], x["k"], x["v"], x["g"], x["beta"])
+        orc.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], None, x["do"])
+        single["tiny_fwd_vjp_B1_T64_D16_s"] = round(time.perf_counter() - t0, 4)
+        x = make_inputs(1, 8, 256, HK, HV, D, D, io_dtype="bf16", h0_std=0.02, with_do=False)
+        t0 = time.perf_counter()
+        orc.forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+        single["decode_B8_256_steps_fwd_s"] = round(time.perf_counter() - t0, 3)
+    return {"value": round(B * T / whole, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{sample} of the {n_groups} (b, k-head) groups of B={B}, T={T}, Hk={HK}, Hv={HV}, D={D} "
+                      f"(each {HV // HK} v-heads x {T} tokens, fwd + VJP in fp64 numpy), one per worker process, "
+                      f"all at once: {wall:.1f} s wall, {sum(secs):.1f} CPU-s; whole workload = wall x "
+                      f"{n_groups}/{sample}",
+            "cpu_model": _cpu_model(), "host_threads": os.cpu_count(), "single_thread": single}
 
 
 def _cpu_model():
@@ -536,6 +612,46 @@ def variants(torch, gdr, args, tokens):
     }
 
 
+def calibration(torch, gdr):
+    """Measured ceilings of this GPU (include/gdr_calib.h): a streaming copy
+    of 16 MiB (served partly by the last-level cache) and of 512 MiB (beyond
+    it: HBM), read + write bytes per second from the library's events around
+    each launch; and a loop of independent fp16 16x16x32 matrix-core products
+    on register operands (enough waves to fill every SIMD)."""
+    out = {}
+    for mib, reps in ((16, 50), (512, 10)):
+        n = mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            gdr.gdr_calib_copy(src, dst)
+        torch.cuda.synchronize()
+        gdr.gdr_profile_enable(True)
+        for _ in range(reps):
+            gdr.gdr_calib_copy(src, dst)
+        ms, cnt = gdr.gdr_profile_read()["calib_copy"]
+        gdr.gdr_profile_enable(False)
+        us = 1000.0 * ms / cnt
+        out[f"copy_{mib}MiB"] = {"us": round(us, 2), "GBps": round(2 * n / (us * 1e-6) / 1e9, 1),
+                                 "frac_hbm_peak": round(2 * n / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del src, dst
+    wgs, iters = 4096, 4096
+    buf = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    gdr.gdr_calib_mfma(buf, wgs, 64)
+    torch.cuda.synchronize()
+    gdr.gdr_profile_enable(True)
+    flops = gdr.gdr_calib_mfma(buf, wgs, iters)
+    ms, _ = gdr.gdr_profile_read()["calib_mfma"]
+    gdr.gdr_profile_enable(False)
+    tfs = flops / (ms * 1e-3) / 1e12
+    out["mfma_f16_16x16x32"] = {"us": round(1000 * ms, 1), "TFLOPs": round(tfs, 1),
+                                "frac_mfma_peak": round(tfs / MFMA_F16_PEAK_TFS, 4),
+                                "launch": f"{wgs} workgroups x 256 threads, {iters} rounds of 8 products"}
+    out["note"] = ("library events around each launch; the rocprofv3 kernel trace of the same kernels is in "
+                   "profiles/")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -543,10 +659,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-calibration", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="time only the headline step (no fused-gate, stateless, channelwise or ragged legs)")
     ap.add_argument("--only-decode", action="store_true",
                     help="run only the decode leg (for counter runs of the decode kernel)")
+    ap.add_argument("--only-calibration", action="store_true",
+                    help="run only the calibration leg (copy and matrix-core ceilings)")
     ap.add_argument("--no-graph", action="store_true", help="decode leg without the replayed HIP graph")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy this many MiB once with a plain elementwise kernel "
@@ -557,6 +676,11 @@ def main():
               "(the path has no multi-GPU mode).", file=sys.stderr)
         sys.exit(2)
 
+    # the oracle's worker pool is forked before anything touches the GPU
+    cpu = None
+    if not (args.no_cpu_baseline or args.only_decode or args.only_calibration):
+        cpu = cpu_baseline()
+
     import torch
     import gated_delta_rule_54_amd as gdr
     gdr.lib()  # fail loudly if the library was not built
@@ -564,6 +688,9 @@ def main():
     if args.only_decode:
         print(json.dumps({"decode": bench_decode(torch, gdr, graph=not args.no_graph)}), flush=True)
         copy_calibration(torch, args.copy_calibration_mib)
+        return
+    if args.only_calibration:
+        print(json.dumps({"calibration": calibration(torch, gdr)}), flush=True)
         return
     ms, wall, kernels = bench_chunked(torch, gdr, args.steps, args.warmup)
     tokens = B * T
@@ -573,34 +700,33 @@ def main():
         avg_ms = tot / n
         ent = {"avg_us": round(1000 * avg_ms, 2), "launches_per_step": n / args.steps,
                "share_of_step": round(tot / args.steps / ms, 4)}
-        per_step = n / args.steps
-        f = kernel_flops_per_token_head(name)
-        by = kernel_bytes_per_token_head(name)
-        if f is not None:
-            ent["TFLOPs"] = round(f * th / per_step / (avg_ms * 1e-3) / 1e12, 2)
-        if by is not None:
-            ent["GBps"] = round(by * th / per_step / (avg_ms * 1e-3) / 1e9, 1)
+        units = th / (n / args.steps)  # (token, v-head) units one launch processes
+        share = kernel_share_per_token_head(name)
+        if share is not None:
+            ent["alg_TFLOPs"] = round(share[0] * units / (avg_ms * 1e-3) / 1e12, 2)
+            ent["alg_GBps"] = round(share[1] * units / (avg_ms * 1e-3) / 1e9, 1)
+        db = design_bytes_per_token_head(name)
+        if db is not None:
+            ent["design_GBps"] = round(db * units / (avg_ms * 1e-3) / 1e9, 1)
         per_kernel[name] = ent
+    # roofline of the kernel with the largest share of the step, on the
+    # method's algorithmic FLOPs and bytes that kernel carries
     dom = max(kernels, key=lambda n: kernels[n][0])
     avg_s = kernels[dom][0] / kernels[dom][1] * 1e-3
-    dom_per_step = kernels[dom][1] / args.steps
-    f = kernel_flops_per_token_head(dom)
-    by = kernel_bytes_per_token_head(dom)
-    f = None if f is None else f / dom_per_step        # per launch
-    by = None if by is None else by / dom_per_step
-    cands = []
-    if f is not None:
-        ach = f * th / avg_s / 1e12
-        cands.append({"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
-                      "frac": round(ach / MFMA_F16_PEAK_TFS, 4)})
-    if by is not None:
-        ach = by * th / avg_s / 1e9
-        cands.append({"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                      "frac": round(ach / HBM_PEAK_GBS, 4)})
+    units = th / (kernels[dom][1] / args.steps)
+    fl, by = kernel_share_per_token_head(dom)
+    f_launch, b_launch = fl * units, by * units
+    cands = [{"bound": "mfma", "achieved": round(f_launch / avg_s / 1e12, 2), "peak": MFMA_F16_PEAK_TFS,
+              "unit": "TFLOP/s", "frac": round(f_launch / avg_s / 1e12 / MFMA_F16_PEAK_TFS, 4)},
+             {"bound": "hbm", "achieved": round(b_launch / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+              "unit": "GB/s", "frac": round(b_launch / avg_s / 1e9 / HBM_PEAK_GBS, 4)}]
     roof = max(cands, key=lambda r: r["frac"])  # the roof the kernel is closest to
-    roof["bytes_per_launch"] = None if by is None else int(by * th)
-    roof["flops_per_launch"] = None if f is None else int(f * th)
     roof["kernel"] = dom
+    roof["avg_us"] = round(avg_s * 1e6, 2)
+    roof["units_per_launch"] = int(units)
+    roof["alg_flops_per_launch"] = int(f_launch)
+    roof["alg_bytes_per_launch"] = int(b_launch)
+    roof["other_roof"] = [c for c in cands if c is not roof][0]
     grids = {"chunk_prep": ((T // C, HV, B), 512), "chunk_fwd_save": ((2 * HV * B, 1, 1), 320),
              "chunk_fwd": ((2 * HV * B, 1, 1), 320), "chunk_states": ((2 * HV * B, 1, 1), 320),
              "chunk_dh": ((2 * HV * B, 1, 1), 320), "chunk_grad": ((T // C, HK, B), 512)}
@@ -608,10 +734,14 @@ def main():
         (gx, gy, gz), th_ = grids[dom]
         roof["launch"] = f"{gx} x {gy} x {gz} workgroups x {th_} threads"
     roof["traffic"] = stored_traffic(dom)
+    roof["traffic_over_algorithmic"] = (None if roof["traffic"] is None
+                                        else round(roof["traffic"] / b_launch, 3))
     canon = canonical_flops_per_token_head() * th
+    alg_bytes = algorithmic_bytes_per_token() * tokens + 2 * B * HV * D * D * 4  # + ht, dh0
+    sec = ms * 1e-3
     line = {
         "metric": "fwd+bwd tokens/s at B=4,T=4096,Hv=32,D=128; decode state GB/s vs HBM peak",
-        "value": round(tokens / (ms * 1e-3), 1),
+        "value": round(tokens / sec, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -628,8 +758,14 @@ def main():
                    "vjp_inputs": "forward saves chunk images and chunk states (GDR_SAVE_CHUNKS)",
                    "parallelism": "single GPU"},
         "roofline": roof,
-        "path": {"canonical_TFLOPs": round(canon / (ms * 1e-3) / 1e12, 2),
-                 "canonical_frac_mfma": round(canon / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFS, 4),
+        "path": {"canonical_flops_per_step": int(canon),
+                 "canonical_TFLOPs": round(canon / sec / 1e12, 2),
+                 "canonical_frac_mfma": round(canon / sec / 1e12 / MFMA_F16_PEAK_TFS, 4),
+                 "alg_bytes_per_step": int(alg_bytes),
+                 "alg_GBps": round(alg_bytes / sec / 1e9, 1),
+                 "alg_frac_hbm": round(alg_bytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+                 "combined_roofline_frac": round(max(canon / (MFMA_F16_PEAK_TFS * 1e12),
+                                                     alg_bytes / (HBM_PEAK_GBS * 1e9)) / sec, 4),
                  "wall_ms_per_step": round(1000 * wall / args.steps, 3)},
         "kernels": per_kernel,
     }
@@ -639,7 +775,9 @@ def main():
         line["variants"] = variants(torch, gdr, args, tokens)
     if not args.no_decode:
         line["decode"] = bench_decode(torch, gdr, graph=not args.no_graph)
-    line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()
+    if not args.no_calibration:
+        line["calibration"] = calibration(torch, gdr)
+    line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
     copy_calibration(torch, args.copy_calibration_mib)
 

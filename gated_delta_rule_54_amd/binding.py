@@ -22,10 +22,12 @@ ALGOS = {"auto": GDR_ALGO_AUTO, "sequential": GDR_ALGO_SEQUENTIAL,
          "chunked": GDR_ALGO_CHUNKED}
 
 # Every symbol include/gdr.h declares.
-SYMBOLS = ("gdr_forward_workspace", "gdr_backward_workspace", "gdr_forward",
+SYMBOLS = ("gdr_keeps_chunks", "gdr_forward_workspace", "gdr_backward_workspace", "gdr_forward",
            "gdr_backward", "gdr_forward_varlen", "gdr_backward_varlen",
            "gdr_profile_enable", "gdr_profile_read",
            "gdr_status_str", "gdr_last_hip_error", "gdr_abi_version")
+# Every symbol include/gdr_calib.h declares (device ceilings for the benchmark).
+CALIB_SYMBOLS = ("gdr_calib_copy", "gdr_calib_mfma")
 
 
 class GdrProblem(ctypes.Structure):
@@ -64,6 +66,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P = ctypes.POINTER(GdrProblem)
         vp, fp, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t
+        L.gdr_keeps_chunks.argtypes = [P, ctypes.POINTER(ctypes.c_int)]
         L.gdr_forward_workspace.argtypes = [P, ctypes.POINTER(sz)]
         L.gdr_backward_workspace.argtypes = [P, ctypes.POINTER(sz)]
         L.gdr_forward.argtypes = [P, vp, vp, vp, fp, fp, fp, vp, fp, vp, sz, vp]
@@ -72,7 +75,10 @@ def lib():
         L.gdr_forward_varlen.argtypes = [P, vp, vp, vp, vp, fp, fp, fp, vp, fp, vp, sz, vp]
         L.gdr_backward_varlen.argtypes = [P, vp, vp, vp, vp, fp, fp, fp, vp, fp,
                                           vp, vp, vp, fp, fp, fp, vp, sz, vp]
-        for name in ("gdr_forward_workspace", "gdr_backward_workspace",
+        L.gdr_calib_copy.argtypes = [vp, vp, sz, vp]
+        L.gdr_calib_mfma.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(ctypes.c_double), vp]
+        for name in ("gdr_keeps_chunks", "gdr_calib_copy", "gdr_calib_mfma",
+                     "gdr_forward_workspace", "gdr_backward_workspace",
                      "gdr_forward", "gdr_backward", "gdr_forward_varlen", "gdr_backward_varlen"):
             getattr(L, name).restype = ctypes.c_int
         L.gdr_profile_enable.argtypes = [ctypes.c_int]
@@ -102,6 +108,40 @@ def make_problem(B, T, Hk, Hv, Dk, Dv, io_dtype, out_dtype, use_qk_l2norm=True,
              | (GDR_FUSED_GATES if fused_gates else 0) | (GDR_SAVE_CHUNKS if save_chunks else 0))
     return GdrProblem(B, T, Hk, Hv, Dk, Dv, _dt(io_dtype), _dt(out_dtype), flags,
                       ALGOS[algo], chunk_size)
+
+
+def gdr_keeps_chunks(prob):
+    """Whether GDR_SAVE_CHUNKS takes effect for this problem."""
+    n = ctypes.c_int(0)
+    st = lib().gdr_keeps_chunks(ctypes.byref(prob), ctypes.byref(n))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_keeps_chunks")
+    return bool(n.value)
+
+
+def gdr_calib_copy(src, dst, stream=None):
+    """dst <- src with the library's streaming copy kernel (same byte size)."""
+    _check(src, "src")
+    _check(dst, "dst")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same byte size")
+    st = lib().gdr_calib_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_calib_copy")
+
+
+def gdr_calib_mfma(out, workgroups, iters, stream=None):
+    """The matrix-core loop of gdr_calib_mfma into out (float32, at least
+    workgroups * 256 elements); returns the FLOPs the launch executes."""
+    _check(out, "out", torch.float32)
+    if out.numel() < workgroups * 256:
+        raise ValueError("out holds fewer than workgroups * 256 floats")
+    fl = ctypes.c_double(0.0)
+    st = lib().gdr_calib_mfma(_ptr(out), workgroups, iters, ctypes.byref(fl), _stream(stream))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_calib_mfma")
+    return fl.value
 
 
 def gdr_forward_workspace(prob):
@@ -163,12 +203,15 @@ def _workspace(nbytes, device):
 
 
 class SavedChunks:
-    """The workspace a ``gdr_forward(..., save_for_backward=True)`` call left
-    its chunk images and chunk entry states in (GDR_SAVE_CHUNKS), for the
-    ``gdr_backward`` of the same problem and inputs."""
+    """What a ``gdr_forward(..., save_for_backward=True)`` call leaves for the
+    ``gdr_backward`` of the same problem and inputs: the workspace holding its
+    chunk images and chunk entry states (GDR_SAVE_CHUNKS), or, where the
+    library does not keep chunks for the problem (``kept`` False: the
+    sequential algorithm, fp32 io, Dk = 16, the channelwise gate), nothing,
+    and the backward then recomputes."""
 
-    def __init__(self, ws, key):
-        self.ws, self.key = ws, key
+    def __init__(self, ws, key, kept=True):
+        self.ws, self.key, self.kept = ws, key, kept
 
 
 def _save_key(prob):
@@ -246,6 +289,9 @@ def gdr_forward(q, k, v, g, beta, h0=None, *, use_qk_l2norm=True, channelwise=Fa
                   dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0, ht=ht if ht is not True and ht is not None else None))
     prob = make_problem(B, T, Hk, Hv, Dk, Dv, q.dtype, out_dtype, use_qk_l2norm,
                         channelwise, algo, chunk_size, fused_gates, save_for_backward)
+    keep = save_for_backward and gdr_keeps_chunks(prob)
+    if save_for_backward and not keep:  # the library ignores the flag here: call without it
+        prob.flags &= ~GDR_SAVE_CHUNKS
     if ht is True:
         ht = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=q.device)
     _check(ht, "ht", torch.float32)
@@ -259,7 +305,7 @@ def gdr_forward(q, k, v, g, beta, h0=None, *, use_qk_l2norm=True, channelwise=Fa
     if st != GDR_OK:
         raise GdrError(st, "gdr_forward")
     if save_for_backward:
-        return o, ht, SavedChunks(ws, _save_key(prob))
+        return o, ht, SavedChunks(ws if keep else None, _save_key(prob), keep)
     return o, ht
 
 
@@ -294,6 +340,9 @@ def gdr_backward(q, k, v, g, beta, h0, dout, dht=None, *, use_qk_l2norm=True,
                         channelwise, algo, chunk_size, fused_gates, saved is not None)
     if saved is not None and saved.key != _save_key(prob):
         raise ValueError("saved chunks belong to a different problem")
+    if saved is not None and not saved.kept:  # nothing was kept: the stateless VJP
+        prob.flags &= ~GDR_SAVE_CHUNKS
+        saved = None
     dh0 = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=dev) if want_dh0 else None
     nws = gdr_backward_workspace(prob)
     if saved is not None:  # the forward's images and chunk states

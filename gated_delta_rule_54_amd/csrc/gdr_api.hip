@@ -108,16 +108,18 @@ BwdPlan plan_seq_bwd(const Shape& s) {
   return w;
 }
 
-gdr_status hip_fail(hipError_t e) {
-  g_last_hip_error = hipGetErrorString(e);
-  return GDR_ERR_HIP;
-}
+gdr_status hip_fail(hipError_t e) { return gdr::record_hip_error(e); }
 
 template <typename T> T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
 }  // namespace
+
+gdr_status gdr::record_hip_error(hipError_t e) {
+  g_last_hip_error = hipGetErrorString(e);
+  return GDR_ERR_HIP;
+}
 
 extern "C" {
 
@@ -146,6 +148,17 @@ gdr_status gdr_forward_workspace(const gdr_problem* p, size_t* bytes) {
   if ((st = resolve_algo(p, false, &algo)) != GDR_OK) return st;
   const Shape s = shape_of(p);
   *bytes = (algo == GDR_ALGO_CHUNKED && s.B > 0 && s.T > 0) ? gdr::chunk_fwd_workspace(s, chunk_of(p)) : 0;
+  return GDR_OK;
+}
+
+gdr_status gdr_keeps_chunks(const gdr_problem* p, int* keeps) {
+  gdr_status st = check_problem(p);
+  if (st != GDR_OK) return st;
+  if (!keeps) return GDR_ERR_NULL_ARG;
+  int algo;
+  if ((st = resolve_algo(p, false, &algo)) != GDR_OK) return st;
+  const Shape s = shape_of(p);
+  *keeps = (algo == GDR_ALGO_CHUNKED && !s.channelwise && gdr::chunk_uses_f16(s, chunk_of(p))) ? 1 : 0;
   return GDR_OK;
 }
 

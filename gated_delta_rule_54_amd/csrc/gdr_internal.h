@@ -2,10 +2,15 @@
 // translation units.  Shapes here are already validated.
 #pragma once
 
+#include <gdr.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace gdr {
+
+// Keeps the text of a failed HIP call for gdr_last_hip_error() (this
+// thread) and returns GDR_ERR_HIP.
+gdr_status record_hip_error(hipError_t e);
 
 // Brackets one kernel launch with profiling events when gdr_profile_enable
 // is on for this thread (no-op otherwise).

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 3
+#define GDR_ABI_VERSION 4
 
 typedef enum gdr_status {
   GDR_OK = 0,
@@ -81,9 +81,20 @@ typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
  *     kernel; the MLX page's "sequential" VJP).  Every shape is supported.
  *   CHUNKED: tokens grouped in chunks of chunk_size; the work inside a chunk
  *     runs as dense matrix-core products (the MLX page's "chunked" VJP).
- *     Scalar gate only; bf16 io uses fp16 matrix-core operands with fp32
- *     accumulation (Dk = 128), fp32 io uses fp32 matrix-core operands.
- *   AUTO: CHUNKED when supported and T > 64, else SEQUENTIAL. */
+ *     Scalar gate: bf16 io uses fp16 matrix-core operands with fp32
+ *     accumulation (Dk = 128, chunk_size 32 or 64), every other shape fp32
+ *     matrix-core operands.  Channelwise gate: bf16 io, Dk = 128,
+ *     chunk_size 32 or 64 only (see below).
+ *   AUTO: CHUNKED when supported and T > 64, else SEQUENTIAL.
+ *
+ * Range of the fp16 chunked path.  Its matrix-core operands (normalised
+ * q / k, v and dout rows, T = (I + A)^-1, the chunk states it keeps) are
+ * fp16, whose finite range is +-65504; accumulation and the carried state
+ * are fp32.  bf16 inputs convert to fp16 exactly inside that range.  A
+ * v or dout element beyond it (or a T entry beyond it, possible only with
+ * beta outside (0, 1)) overflows to +-Inf in its operand, and the outputs
+ * that depend on it come out non-finite (Inf or NaN), never finite and
+ * wrong.  Inputs of that size need the SEQUENTIAL algorithm or fp32 io. */
 typedef enum gdr_algo {
   GDR_ALGO_AUTO = 0,
   GDR_ALGO_SEQUENTIAL = 1,
@@ -99,8 +110,10 @@ typedef enum gdr_algo {
  * and with GDR_CHANNELWISE (then a has g's per-channel shape). */
 /* GDR_SAVE_CHUNKS: keep the forward's per-chunk work for the VJP (what a
  * training step's autograd saves), on the chunked algorithm with bf16 io,
- * Dk = Dv = 128, chunk_size 32 or 64 and a scalar gate; elsewhere the flag
- * changes nothing.  gdr_forward then needs gdr_backward_workspace(p) bytes
+ * Dk = Dv = 128, chunk_size 32 or 64 and a scalar gate; elsewhere (the
+ * SEQUENTIAL algorithm, also when AUTO picks it; fp32 io; Dk = 16; the
+ * channelwise gate) both calls ignore the flag, and gdr_keeps_chunks tells
+ * which case a problem is.  gdr_forward then needs gdr_backward_workspace(p) bytes
  * of workspace (gdr_forward_workspace reports that size) and leaves the
  * chunk images (normalised q/k, gates, T = (I + A)^-1, P) and every
  * chunk's entry state there; gdr_backward with the same problem, the same
@@ -126,6 +139,13 @@ typedef struct gdr_problem {
  * runs the sequential VJP inside every chunk, all chunks in parallel, from
  * chunk states the chunk chains store.  AUTO picks the chunked kernels there
  * when T > 64. */
+
+/* *keeps = 1 when GDR_SAVE_CHUNKS takes effect for problem *p (whether or
+ * not the flag is set in p->flags), i.e. when gdr_forward with the flag
+ * leaves its chunks in the workspace for gdr_backward; else 0, and both
+ * calls ignore the flag.  Returns the validation status of the problem;
+ * *keeps is written only on GDR_OK. */
+gdr_status gdr_keeps_chunks(const gdr_problem* p, int* keeps);
 
 /* Workspace bytes the call needs for problem *p (0 is possible).  Returns
  * the same validation status gdr_forward/gdr_backward would for the shape

@@ -13,23 +13,25 @@ from gated_delta_rule_54_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def header_functions():
-    txt = open(os.path.join(ROOT, "include", "gdr.h")).read()
+def header_functions(name="gdr.h"):
+    txt = open(os.path.join(ROOT, "include", name)).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return set(re.findall(r"\b(gdr_[a-z0-9_]+)\s*\(", txt))
 
 
 def test_every_declared_symbol_is_exported():
-    declared = header_functions()
-    assert declared == set(B.SYMBOLS)
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert headers == ["gdr.h", "gdr_calib.h"]
+    assert header_functions("gdr.h") == set(B.SYMBOLS)
+    assert header_functions("gdr_calib.h") == set(B.CALIB_SYMBOLS)
     lib = B.lib()
-    for name in declared:
+    for name in B.SYMBOLS + B.CALIB_SYMBOLS:
         assert hasattr(lib, name), name
 
 
 def test_abi_version_and_status_strings():
     lib = B.lib()
-    assert lib.gdr_abi_version() == 3
+    assert lib.gdr_abi_version() == 4
     for s in range(7):
         assert len(lib.gdr_status_str(s)) > 0
     assert lib.gdr_status_str(99) == b"unknown gdr_status"
@@ -212,3 +214,64 @@ def test_binding_shape_checks():
     B._check_shapes(1, 9, Hk, Hv, D, D, 3, False, rag)
     with pytest.raises(ValueError, match="h0"):
         B._check_shapes(1, 9, Hk, Hv, D, D, 2, False, rag)
+
+
+def keeps(p):
+    n = ctypes.c_int(-1)
+    st = B.lib().gdr_keeps_chunks(ctypes.byref(p), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,kept", [
+    (dict(B=4, T=4096, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=0), 1),        # AUTO, T > 64: chunked fp16
+    (dict(B=4, T=4096, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=2, chunk_size=32), 1),
+    (dict(B=1, T=64, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=0), 0),          # AUTO picks sequential
+    (dict(B=1, T=8, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=0), 0),
+    (dict(B=1, T=512, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=1), 0),         # sequential
+    (dict(B=1, T=512, Hk=2, Hv=4, Dk=128, Dv=128, io_dtype=0, algo=2), 0),           # fp32 io
+    (dict(B=1, T=512, Hk=2, Hv=4, Dk=16, Dv=16, io_dtype=1, algo=2), 0),             # Dk = 16
+    (dict(B=1, T=512, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=2, chunk_size=16), 0),
+    (dict(B=1, T=512, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=2, flags=3), 0),  # channelwise
+])
+def test_keeps_chunks_query(kw, kept):
+    for flags in (kw.get("flags", 1), kw.get("flags", 1) | 8):
+        st, n = keeps(prob(**dict(kw, flags=flags)))
+        assert st == 0 and n == kept
+
+
+def test_keeps_chunks_query_validates():
+    assert keeps(prob(Hv=3))[0] == 2
+    assert B.lib().gdr_keeps_chunks(None, None) == 1
+    p = prob()
+    assert B.lib().gdr_keeps_chunks(ctypes.byref(p), None) == 1
+
+
+def test_saved_chunks_only_where_kept():
+    """Where the library ignores GDR_SAVE_CHUNKS, the forward with and without
+    the flag needs the same workspace and the binding keeps nothing; where it
+    honours it, the forward needs the backward's workspace."""
+    for kw in (dict(T=64, algo=0), dict(T=512, algo=1), dict(T=200, algo=2, io_dtype=0, Dk=128, Dv=128),
+               dict(T=200, algo=2, flags=3, Dk=128, Dv=128, io_dtype=1)):
+        base = dict(B=1, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, flags=1)
+        base.update(kw)
+        p0, p1 = prob(**base), prob(**dict(base, flags=base["flags"] | 8))
+        assert keeps(p1) == (0, 0)
+        assert fwd_ws(p0) == fwd_ws(p1)
+        assert bwd_ws(p0) == bwd_ws(p1)
+    p1 = prob(B=1, T=200, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, flags=9, algo=2)
+    assert keeps(p1) == (0, 1)
+    assert fwd_ws(p1) == bwd_ws(p1)
+    assert fwd_ws(p1)[1] > fwd_ws(prob(B=1, T=200, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, flags=1, algo=2))[1]
+
+
+def test_calib_entry_points_validate():
+    lib = B.lib()
+    fl = ctypes.c_double(0)
+    assert lib.gdr_calib_copy(None, FAKE, 16, None) == 1
+    assert lib.gdr_calib_copy(FAKE, FAKE + 16, 0, None) == 2
+    assert lib.gdr_calib_copy(FAKE, FAKE + 16, 24, None) == 2
+    assert lib.gdr_calib_copy(FAKE + 8, FAKE, 16, None) == 4
+    assert lib.gdr_calib_mfma(None, 1, 1, ctypes.byref(fl), None) == 1
+    assert lib.gdr_calib_mfma(FAKE, 0, 1, ctypes.byref(fl), None) == 2
+    assert lib.gdr_calib_mfma(FAKE, 1, -1, ctypes.byref(fl), None) == 2
+    assert lib.gdr_calib_mfma(FAKE + 4, 1, 1, ctypes.byref(fl), None) == 4

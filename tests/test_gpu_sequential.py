@@ -236,8 +236,9 @@ def test_hand_worked_examples(io, D, algo):
     recurrence and every gradient), no L2 norm: the HIP path against the
     hand-derived values directly.  The channelwise case is skipped on the
     fp32 chunked path (scalar gate only); with bf16 io only cases whose
-    inputs bf16 holds exactly run (the channelwise one, through the fp16
-    matrix-core kernels when chunked), at 5e-3."""
+    inputs bf16 holds exactly run (the channelwise one and the bf16-exact
+    scalar one with its VJP, through the fp16 matrix-core kernels when
+    chunked), at 5e-3."""
     import os
     import yaml
     from gated_delta_rule_54_amd.synth import round_bf16
@@ -282,7 +283,8 @@ def test_hand_worked_examples(io, D, algo):
                                  dev(pad_rows(a("dout"), (1, T, 1)), io_dtype(io)), None, **kw)
         torch.cuda.synchronize()
         want = {"dq": pad_rows(a("dq"), (1, T, 1)), "dk": pad_rows(a("dk"), (1, T, 1)),
-                "dv": pad_rows(a("dv"), (1, T, 1)), "dg": pad_rows(a("dg"), (1, T, 1)),
+                "dv": pad_rows(a("dv"), (1, T, 1)),
+                "dg": pad_rows(a("dg"), (1, T, 1)) if cw else a("dg").reshape(1, T, 1),
                 "dbeta": a("dbeta").reshape(1, T, 1), "dh0": np.zeros((1, 1, D, D), np.float32)}
         want["dh0"][0, 0, :2, :2] = a("dh0")
         for key, x in zip(GRAD_NAMES, grads):

@@ -441,17 +441,20 @@ def test_p16_fused_gates_autograd_of_the_textbook_form():
 
 
 def test_p17_hand_worked_examples():
-    """Two examples worked by hand on 2x2 states (tests/golden/
+    """Three examples worked by hand on 2x2 states (tests/golden/
     hand_worked_2x2.yaml, derivations in the file): a two-token scalar-gate
-    forward, and a one-token channelwise forward with its full VJP, which
-    fixes the key-channel side of the per-channel decay ([ET] summary) and
-    every gradient's sign and index."""
+    forward; a one-token channelwise forward with its full VJP, which fixes
+    the key-channel side of the per-channel decay ([ET] summary) and every
+    gradient's sign and index; and a two-token scalar-gate forward with its
+    full VJP whose inputs are exact in bf16 (so the bf16 matrix-core path
+    meets it too), which fixes the scalar dg and the carry of dH between
+    tokens."""
     import os
     import yaml
     path = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_2x2.yaml")
     with open(path) as fh:
         cases = yaml.safe_load(fh)
-    assert set(cases) == {"scalar_two_tokens", "channelwise_one_token_with_vjp"}
+    assert set(cases) == {"scalar_two_tokens", "channelwise_one_token_with_vjp", "scalar_two_tokens_bf16_with_vjp"}
     for name, c in cases.items():
         cw = c["channelwise"]
         a = lambda key: np.asarray(c[key], dtype=np.float64)
