@@ -59,6 +59,8 @@ KERNELS = [
     (r"seq_bwd_kernel", "seq_bwd"),
     (r"seq_fwd_kernel", "seq_fwd"),
     (r"decode_kernel", "decode"),
+    (r"calib_copy_kernel", "calib_copy"),
+    (r"calib_mfma_kernel", "calib_mfma"),
 ]
 COPY_PATTERN = r"neg_kernel"
 
