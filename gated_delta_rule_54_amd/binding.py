@@ -23,7 +23,7 @@ ALGOS = {"auto": GDR_ALGO_AUTO, "sequential": GDR_ALGO_SEQUENTIAL,
 
 # Every symbol include/gdr.h declares.
 SYMBOLS = ("gdr_keeps_chunks", "gdr_forward_workspace", "gdr_backward_workspace", "gdr_forward",
-           "gdr_backward", "gdr_forward_varlen", "gdr_backward_varlen",
+           "gdr_backward", "gdr_forward_noalloc", "gdr_forward_varlen", "gdr_backward_varlen",
            "gdr_profile_enable", "gdr_profile_read",
            "gdr_status_str", "gdr_last_hip_error", "gdr_abi_version")
 # Every symbol include/gdr_calib.h declares (device ceilings for the benchmark).
@@ -72,6 +72,7 @@ def lib():
         L.gdr_forward.argtypes = [P, vp, vp, vp, fp, fp, fp, vp, fp, vp, sz, vp]
         L.gdr_backward.argtypes = [P, vp, vp, vp, fp, fp, fp, vp, fp,
                                    vp, vp, vp, fp, fp, fp, vp, sz, vp]
+        L.gdr_forward_noalloc.argtypes = [P, vp, vp, vp, fp, fp, fp, vp, fp, vp]
         L.gdr_forward_varlen.argtypes = [P, vp, vp, vp, vp, fp, fp, fp, vp, fp, vp, sz, vp]
         L.gdr_backward_varlen.argtypes = [P, vp, vp, vp, vp, fp, fp, fp, vp, fp,
                                           vp, vp, vp, fp, fp, fp, vp, sz, vp]
@@ -79,7 +80,8 @@ def lib():
         L.gdr_calib_mfma.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(ctypes.c_double), vp]
         for name in ("gdr_keeps_chunks", "gdr_calib_copy", "gdr_calib_mfma",
                      "gdr_forward_workspace", "gdr_backward_workspace",
-                     "gdr_forward", "gdr_backward", "gdr_forward_varlen", "gdr_backward_varlen"):
+                     "gdr_forward", "gdr_backward", "gdr_forward_noalloc", "gdr_forward_varlen",
+                     "gdr_backward_varlen"):
             getattr(L, name).restype = ctypes.c_int
         L.gdr_profile_enable.argtypes = [ctypes.c_int]
         L.gdr_profile_enable.restype = ctypes.c_int
@@ -306,6 +308,36 @@ def gdr_forward(q, k, v, g, beta, h0=None, *, use_qk_l2norm=True, channelwise=Fa
         raise GdrError(st, "gdr_forward")
     if save_for_backward:
         return o, ht, SavedChunks(ws if keep else None, _save_key(prob), keep)
+    return o, ht
+
+
+def gdr_forward_noalloc(q, k, v, g, beta, h0=None, *, o=None, ht=None, use_qk_l2norm=True, channelwise=False,
+                        algo="auto", chunk_size=0, out_dtype=torch.float32, stream=None, fused_gates=False):
+    """gdr_forward with the library's fixed device scratch as workspace (the
+    C call allocates nothing).  ``o`` and ``ht`` may be given (then nothing is
+    allocated here either: ``ht`` may be ``h0``); otherwise they are created.
+    Returns (o, ht)."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype)
+    for t, n in ((g, "g"), (beta, "beta"), (h0, "h0")):
+        _check(t, n, torch.float32)
+    if o is None:
+        o = torch.empty((B, T, Hv, Dv), dtype=out_dtype, device=q.device)
+    if ht is None:
+        ht = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=q.device)
+    _check(o, "o", out_dtype)
+    _check(ht, "ht", torch.float32)
+    _check_shapes(B, T, Hk, Hv, Dk, Dv, B, channelwise, dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0, ht=ht))
+    if tuple(o.shape) != (B, T, Hv, Dv):
+        raise ValueError(f"o has shape {tuple(o.shape)}, expected {(B, T, Hv, Dv)}")
+    prob = make_problem(B, T, Hk, Hv, Dk, Dv, q.dtype, out_dtype, use_qk_l2norm, channelwise, algo, chunk_size,
+                        fused_gates, False)
+    st = lib().gdr_forward_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                                   _ptr(o), _ptr(ht), _stream(stream))
+    if st != GDR_OK:
+        raise GdrError(st, "gdr_forward_noalloc")
     return o, ht
 
 

@@ -6,6 +6,7 @@
 
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "gdr_internal.h"
@@ -112,6 +113,43 @@ gdr_status hip_fail(hipError_t e) { return gdr::record_hip_error(e); }
 
 template <typename T> T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+// ---- fixed device scratch for gdr_forward_noalloc -------------------------
+// A file-scope device array holds the workspace of the allocation-free
+// forward.  Every GPU the library runs on keeps its own copy until the
+// process ends.  Host code never passes the array's name (a host-side
+// stand-in) to a kernel or copy: it uses the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device on that device's first call.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(GDR_NOALLOC_SCRATCH_BYTES);
+__device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's scratch address (looked up once per device, with that
+// device current).
+gdr_status device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return gdr::record_hip_error(e);
+  if (dev < 0 || dev >= kMaxDevices) return GDR_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return gdr::record_hip_error(e);
+    if (!p) return GDR_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDR_OK;
 }
 
 }  // namespace
@@ -268,6 +306,20 @@ gdr_status gdr_forward(const gdr_problem* p, const void* q, const void* k, const
                        const float* g, const float* beta, const float* h0, void* o, float* ht,
                        void* ws, size_t ws_bytes, void* hip_stream) {
   return forward_impl(p, nullptr, false, q, k, v, g, beta, h0, o, ht, ws, ws_bytes, hip_stream);
+}
+
+gdr_status gdr_forward_noalloc(const gdr_problem* p, const void* q, const void* k, const void* v,
+                               const float* g, const float* beta, const float* h0, void* o, float* ht,
+                               void* hip_stream) {
+  gdr_status st = check_problem(p);
+  if (st != GDR_OK) return st;
+  if (p->flags & GDR_SAVE_CHUNKS) return GDR_ERR_UNSUPPORTED;  // the scratch is not the caller's to keep
+  size_t need = 0;
+  if ((st = gdr_forward_workspace(p, &need)) != GDR_OK) return st;
+  if (need > kScratchBytes) return GDR_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (need > 0 && (st = device_scratch(&ws)) != GDR_OK) return st;
+  return forward_impl(p, nullptr, false, q, k, v, g, beta, h0, o, ht, ws, need, hip_stream);
 }
 
 gdr_status gdr_forward_varlen(const gdr_problem* p, const int64_t* cu_seqlens, const void* q, const void* k,

@@ -174,6 +174,24 @@ gdr_status gdr_backward(const gdr_problem* p, const void* q, const void* k,
                         float* dh0, void* ws, size_t ws_bytes,
                         void* hip_stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): gdr_forward with the workspace taken from a fixed scratch
+ * array of GDR_NOALLOC_SCRATCH_BYTES (64 MiB) that the library keeps on
+ * every GPU it runs on until the process ends.  The call allocates and
+ * frees nothing; the caller still owns q .. ht.  Limits: problems whose
+ * gdr_forward_workspace exceeds the scratch return
+ * GDR_ERR_WORKSPACE_TOO_SMALL before anything is launched (the chunked path
+ * needs about 1.1 MiB per 64 tokens of each sequence at Hk = 16, Hv = 32,
+ * D = 128; the sequential path needs none); GDR_SAVE_CHUNKS returns
+ * GDR_ERR_UNSUPPORTED.  All calls on one GPU share that GPU's scratch, so
+ * calls that overlap on one GPU (concurrent streams, threads) race: order
+ * them on one stream.  The stream must belong to the current device. */
+#define GDR_NOALLOC_SCRATCH_BYTES (64u << 20)
+gdr_status gdr_forward_noalloc(const gdr_problem* p, const void* q, const void* k,
+                               const void* v, const float* g, const float* beta,
+                               const float* h0, void* o, float* ht, void* hip_stream);
+
 /* Ragged (packed) batches: p->B sequences of different lengths laid end to
  * end along the token axis, for prefill of a batch of prompts.  cu_seqlens
  * (device memory, int64, B + 1 entries, 8-byte aligned) holds the row

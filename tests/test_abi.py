@@ -275,3 +275,16 @@ def test_calib_entry_points_validate():
     assert lib.gdr_calib_mfma(FAKE, 0, 1, ctypes.byref(fl), None) == 2
     assert lib.gdr_calib_mfma(FAKE, 1, -1, ctypes.byref(fl), None) == 2
     assert lib.gdr_calib_mfma(FAKE + 4, 1, 1, ctypes.byref(fl), None) == 4
+
+
+def test_noalloc_forward_validates_before_touching_the_device():
+    """gdr_forward_noalloc refuses a problem beyond its fixed scratch and the
+    GDR_SAVE_CHUNKS flag during validation (no device call is made)."""
+    lib = B.lib()
+    args = [FAKE] * 8 + [None]
+    big = prob(B=8, T=4096, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=2)
+    assert fwd_ws(big)[1] > (64 << 20)
+    assert lib.gdr_forward_noalloc(ctypes.byref(big), *args) == 5
+    assert lib.gdr_forward_noalloc(ctypes.byref(prob(flags=9)), *args) == 3
+    assert lib.gdr_forward_noalloc(ctypes.byref(prob(Hv=3)), *args) == 2
+    assert lib.gdr_forward_noalloc(None, *args) == 1
