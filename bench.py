@@ -186,7 +186,7 @@ def bench_chunked(torch, gdr, steps, warmup, fused_gates=False, saved=True):
     return ms, wall, kernels
 
 
-def bench_decode(torch, gdr, graph=True):
+def bench_decode(torch, gdr, graph=True, legs=("rotated", "single_buffer_cache_warm")):
     """B=8 single-token steps, state updated in place, rotating over
     DEC_BUFFERS independent states so a step's 16 MiB state is not served
     from the 256 MB last-level cache.  Per step: the kernel time from the
@@ -210,6 +210,8 @@ def bench_decode(torch, gdr, graph=True):
 
     out = {}
     for label, buffers in (("rotated", DEC_BUFFERS), ("single_buffer_cache_warm", 1)):
+        if label not in legs:
+            continue
         run(32, buffers)
         torch.cuda.synchronize()
         gdr.gdr_profile_enable(True)
@@ -614,10 +616,12 @@ def variants(torch, gdr, args, tokens):
 
 def calibration(torch, gdr):
     """Measured ceilings of this GPU (include/gdr_calib.h): a streaming copy
-    of 16 MiB (served partly by the last-level cache) and of 512 MiB (beyond
-    it: HBM), read + write bytes per second from the library's events around
-    each launch; and a loop of independent fp16 16x16x32 matrix-core products
-    on register operands (enough waves to fill every SIMD)."""
+    of 16 MiB (the same buffers every call: partly served by the last-level
+    cache), of 16 MiB rotating over 32 buffer pairs (the decode step's
+    traffic shape, from HBM) and of 512 MiB (HBM), read + write bytes per
+    second from the library's events around each launch; and a loop of
+    independent fp16 16x16x32 matrix-core products on register operands
+    (enough waves to fill every SIMD)."""
     out = {}
     for mib, reps in ((16, 50), (512, 10)):
         n = mib << 20
@@ -635,6 +639,24 @@ def calibration(torch, gdr):
         out[f"copy_{mib}MiB"] = {"us": round(us, 2), "GBps": round(2 * n / (us * 1e-6) / 1e9, 1),
                                  "frac_hbm_peak": round(2 * n / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         del src, dst
+    # the decode step's traffic shape: 16 MiB read + 16 MiB written per
+    # launch, rotating over 32 buffer pairs (1 GiB, beyond the last-level
+    # cache) as the decode leg rotates its states
+    n = 16 << 20
+    bufs = [(torch.ones(n // 4, dtype=torch.float32, device="cuda"),
+             torch.empty(n // 4, dtype=torch.float32, device="cuda")) for _ in range(DEC_BUFFERS)]
+    for sb, db in bufs:
+        gdr.gdr_calib_copy(sb, db)
+    torch.cuda.synchronize()
+    gdr.gdr_profile_enable(True)
+    for i in range(DEC_STEPS):
+        gdr.gdr_calib_copy(*bufs[i % DEC_BUFFERS])
+    ms, cnt = gdr.gdr_profile_read()["calib_copy"]
+    gdr.gdr_profile_enable(False)
+    us = 1000.0 * ms / cnt
+    out["copy_16MiB_rotated_32"] = {"us": round(us, 2), "GBps": round(2 * n / (us * 1e-6) / 1e9, 1),
+                                    "frac_hbm_peak": round(2 * n / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del bufs
     wgs, iters = 4096, 4096
     buf = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
     gdr.gdr_calib_mfma(buf, wgs, 64)
@@ -667,6 +689,8 @@ def main():
     ap.add_argument("--only-calibration", action="store_true",
                     help="run only the calibration leg (copy and matrix-core ceilings)")
     ap.add_argument("--no-graph", action="store_true", help="decode leg without the replayed HIP graph")
+    ap.add_argument("--decode-rotated-only", action="store_true",
+                    help="decode leg: only the rotated (HBM) steps, so that a kernel trace holds those alone")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy this many MiB once with a plain elementwise kernel "
                          "(reference for HBM byte counters)")
@@ -686,7 +710,8 @@ def main():
     gdr.lib()  # fail loudly if the library was not built
 
     if args.only_decode:
-        print(json.dumps({"decode": bench_decode(torch, gdr, graph=not args.no_graph)}), flush=True)
+        legs = ("rotated",) if args.decode_rotated_only else ("rotated", "single_buffer_cache_warm")
+        print(json.dumps({"decode": bench_decode(torch, gdr, graph=not args.no_graph, legs=legs)}), flush=True)
         copy_calibration(torch, args.copy_calibration_mib)
         return
     if args.only_calibration:

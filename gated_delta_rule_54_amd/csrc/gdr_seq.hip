@@ -219,6 +219,24 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(Dims d, SeqFwdArgs a) {
     len = a.cu[b + 1] - tb;
     len = len < 0 ? 0 : (len > d.T ? d.T : len);
   }
+  // The token's rows first: their loads are issued ahead of the state's,
+  // so the sums that need no state (|k|^2, |q|^2, k.q) are formed while the
+  // state is still arriving.
+  const int64_t krow = (tb * d.Hk + kh) * D + i0;
+  const int64_t vrow = (tb * d.Hv + hv) * D + j0;
+  const int64_t grow = tb * d.Hv + hv;
+  float k[RPL], q[RPL], v[4], al[CW ? RPL : 1], beta = 0.f;
+  if (len > 0) {  // the same for every thread of the block
+    ld_rows<RPL, TI>(static_cast<const TI*>(a.k) + krow, k);
+    ld_rows<RPL, TI>(static_cast<const TI*>(a.q) + krow, q);
+    ld4<TI>(static_cast<const TI*>(a.v) + vrow, v);
+    if constexpr (CW) {
+      ld_rows<RPL, float>(a.g + grow * D + i0, al);
+    } else {
+      al[0] = a.g[grow];
+    }
+    beta = a.beta[grow];
+  }
   float h[RPL][4];
 #pragma unroll
   for (int m = 0; m < RPL; ++m) {
@@ -229,29 +247,26 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(Dims d, SeqFwdArgs a) {
       h[m][0] = h[m][1] = h[m][2] = h[m][3] = 0.f;
     }
   }
-  if (len > 0) {  // the same for every thread of the block
-    const int64_t krow = (tb * d.Hk + kh) * D + i0;
-    const int64_t vrow = (tb * d.Hv + hv) * D + j0;
-    const int64_t grow = tb * d.Hv + hv;
-    float k[RPL], q[RPL], v[4], al[CW ? RPL : 1];
-    ld_rows<RPL, TI>(static_cast<const TI*>(a.k) + krow, k);
-    ld_rows<RPL, TI>(static_cast<const TI*>(a.q) + krow, q);
-    ld4<TI>(static_cast<const TI*>(a.v) + vrow, v);
+  if (len > 0) {
     if constexpr (CW) {
-      ld_rows<RPL, float>(a.g + grow * D + i0, al);
 #pragma unroll
       for (int m = 0; m < RPL; ++m) al[m] = d.fg ? fg_alpha(al[m]) : expf(al[m]);
     } else {
-      al[0] = d.fg ? fg_alpha(a.g[grow]) : expf(a.g[grow]);
+      al[0] = d.fg ? fg_alpha(al[0]) : expf(al[0]);
     }
-    const float beta = d.fg ? fg_beta(a.beta[grow]) : a.beta[grow];
+    beta = d.fg ? fg_beta(beta) : beta;
     // this wave's halves of the sums over Dk
     float x[NV] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // |k|^2 |q|^2 k.q p[4] r[4]
 #pragma unroll
-    for (int m = 0; m < RPL; ++m) {
+    for (int m = 0; m < RPL; ++m) {  // needs no state
       x[0] += k[m] * k[m];
       x[1] += q[m] * q[m];
       x[2] += k[m] * q[m];
+    }
+#pragma unroll
+    for (int n = 0; n < 3; ++n) x[n] = xsum<NCG, 64>(x[n]);
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
       const float am = CW ? al[CW ? m : 0] : al[0];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -262,7 +277,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(Dims d, SeqFwdArgs a) {
       }
     }
 #pragma unroll
-    for (int n = 0; n < NV; ++n) x[n] = xsum<NCG, 64>(x[n]);
+    for (int n = 3; n < NV; ++n) x[n] = xsum<NCG, 64>(x[n]);
     if (rg == 0) {
 #pragma unroll
       for (int n = 0; n < NV; ++n) part[w][cg][n] = x[n];
