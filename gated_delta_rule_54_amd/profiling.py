@@ -62,7 +62,7 @@ KERNELS = [
     (r"calib_copy_kernel", "calib_copy"),
     (r"calib_mfma_kernel", "calib_mfma"),
 ]
-COPY_PATTERN = r"neg_kernel"
+COPY_PATTERN = r"calib_copy_kernel"
 
 
 def src_digest():
