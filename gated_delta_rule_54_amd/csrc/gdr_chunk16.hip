@@ -83,7 +83,6 @@ struct K16 {
   int64_t B, T;
   int Hk, Hv, NC, l2;
   int fg;                  // fused gate activation: g, beta hold pre-activations
-  int gi;                  // v-head within its k-head group (gradient launches)
   const int64_t* cu;       // ragged batch: sequence b is rows cu[b] .. cu[b+1) (null: rows b*T .. b*T+T)
 };
 
@@ -1033,12 +1032,14 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
 // ---------------------------------------------------------------------------
 // grad16: all gradients of one chunk except dv and dH, given its entry state
 // H0 and the gradient dH at its end (both [Dk][Dv] fp16).  Eight waves.  One
-// launch per v-head of a k-head group (v-head gi of every group), in order:
-// dq_hat / dk_hat of the group are summed in fp32 in a running buffer
-// (FIRST stores, MID adds), and the launch of the group's last v-head adds
-// its share, applies the L2-norm VJP and writes dq, dk (LAST; ONLY when the
-// group has one v-head).  The sum order is fixed, so results are
-// reproducible.
+// workgroup per (chunk, k-head, b) walks the v-heads of the k-head group one
+// after the other (GROUP; ONLY when the group has one v-head): the key image
+// is loaded once, each v-head's dq_hat / dk_hat share is added in fp32 to
+// sums held in registers, and after the last v-head the L2-norm VJP is
+// applied and dq, dk are written.  The sum order is fixed, so results are
+// reproducible.  With fewer such workgroups than CUs, SPLIT runs one
+// workgroup per (chunk, v-head, b) and stores each v-head's share for the
+// epilogue kernel, which sums the group and applies the norm VJP.
 //   Phase A  wave w owns the 16-column value strip jw = 16w .. 16w+15 and
 //            chains in registers Y = K H0, X = K dH, U = T RHS,
 //            dU = lam X + P^T dO, dRHS = T^T dU; it writes dRHS, dO and U
@@ -1071,8 +1072,23 @@ __device__ __forceinline__ void mma_rows(f32x4 (&acc)[NO], const _Float16* A, in
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// With ON, x passes through an empty asm statement, so the compiler cannot
+// treat what is derived from it as loop invariant: addresses built from the
+// lane index inside a loop are rebuilt there instead of being held in
+// registers across the whole loop body.
+template <bool ON>
+__device__ __forceinline__ int opaque_v(int x) {
+  if constexpr (ON) asm volatile("" : "+v"(x));
+  return x;
+}
+template <bool ON>
+__device__ __forceinline__ int opaque_s(int x) {
+  if constexpr (ON) asm volatile("" : "+s"(x));
+  return x;
+}
 
-enum GradMode { kFirst = 0, kMid = 1, kLast = 2, kOnly = 3, kSplit = 4 };
+
+enum GradMode { kOnly = 0, kSplit = 1, kGroup = 2 };
 
 template <int C, typename TO, int MODE>
 __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
@@ -1098,427 +1114,397 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   // L2-norm VJP row partials q_hat . dq_hat, k_hat . dk_hat, after the dq / dk output tiles
   float (*sN)[NW][C] = reinterpret_cast<float (*)[NW][C]>(xb + 2 * C * LDQ);
 
-  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-  // kSplit: one launch for all v-heads (blockIdx.y = v-head), each storing
-  // its own dq_hat / dk_hat rows for the epilogue kernel
-  // Launches after a group's first walk the grid backwards: the running sums
-  // and key images the previous launch touched last are the likeliest to
-  // still be cached (about 5 us less for the later launch at B=4, T=4096)
-  int c = blockIdx.x, yy = blockIdx.y;
-  int64_t b = blockIdx.z;
-  if constexpr (MODE == kMid || MODE == kLast) {
-    c = gridDim.x - 1 - c;
-    yy = gridDim.y - 1 - yy;
-    b = gridDim.z - 1 - b;
-  }
-  const int hv = MODE == kSplit ? yy : yy * (a.Hv / a.Hk) + a.gi;
-  const int kh = MODE == kSplit ? hv / (a.Hv / a.Hk) : yy;
+  const int tid0 = threadIdx.x, w0 = wave_id();
+  // kSplit: blockIdx.y = v-head, each storing its own dq_hat / dk_hat rows
+  // for the epilogue kernel; otherwise blockIdx.y = k-head
+  const int c = blockIdx.x, yy = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  // kGroup: one workgroup walks all v-heads of its k-head in order, with
+  // the group sums of dq_hat / dk_hat kept in registers and the key image
+  // loaded once
+  constexpr bool GROUP = MODE == kGroup;
+  const int ngi = GROUP ? a.Hv / a.Hk : 1;
+  const int kh = MODE == kSplit ? yy / (a.Hv / a.Hk) : yy;
   const int64_t t0 = static_cast<int64_t>(c) * C;
   const SeqSpan sp = seq_span(a, b);
   if (t0 >= sp.len) return;  // past the end of a shorter sequence of a ragged batch
   const int L = static_cast<int>(sp.len - t0 < C ? sp.len - t0 : C);
-  const int64_t cbase = (b * a.Hv + hv) * a.NC + c;
-  const int jw = 16 * w + c16;         // phase A value column
-  const int i2 = 16 * w + c16;         // phase 1/2 and dq/dk key row
-  const bool qact = w * DPW < NQ;      // this wave owns C x C tiles
-  const int qr = (w * DPW) / NT, qc0 = (w * DPW) % NT;
 
-  dma<IM::CHK, 512>(make_rsrc(a.cimg + cbase * static_cast<int64_t>(IM::CHK), IM::CHK), 0, img, tid, w);
   dma<IM::KEY, 512>(make_rsrc(a.kimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(IM::KEY), IM::KEY), 0,
-                    img + IM::CHK, tid, w);
-  // H0 / dH: this lane's chained strips (rows 16ti + 4g + e, column jw), as
-  // stored by the chain kernels; the row fragments of phases 1 / 2 come from
-  // the transposed copy Hs written from these strips
-  const rsrc_t hr = make_rsrc(a.hst + cbase * static_cast<int64_t>(DK * DK), DK * DK * 2);
-  const rsrc_t dhr = make_rsrc(a.dhst + cbase * static_cast<int64_t>(DK * DK), DK * DK * 2);
-  f16x8 h0f[NTK / 2], dhf[NTK / 2];
-#pragma unroll
-  for (int kb = 0; kb < NTK / 2; ++kb) {
-    h0f[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(hr, frag_off(w, kb), 0, 0));
-    dhf[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(dhr, frag_off(w, kb), 0, 0));
-  }
-  // Hs[j][i] <- strips (rows i of column j = jw)
-  auto put_state = [&](const f16x8 (&f)[NTK / 2]) {
-#pragma unroll
-    for (int kb = 0; kb < NTK / 2; ++kb) {
-      *reinterpret_cast<f16x4*>(Hs + jw * LDK + 32 * kb + 4 * g) = f16x4{f[kb][0], f[kb][1], f[kb][2], f[kb][3]};
-      *reinterpret_cast<f16x4*>(Hs + jw * LDK + 32 * kb + 16 + 4 * g) = f16x4{f[kb][4], f[kb][5], f[kb][6], f[kb][7]};
-    }
-  };
-  // raw v / dO rows of the chunk, packed [C][DK] bf16, in the strip buffers
-  const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
-  const int64_t seq0 = (sp.t0 + t0) * a.Hv * DK;
-  dma_rows<C, DK * 2, 512>(make_rsrc(a.v + seq0, static_cast<uint32_t>(L) * rowv), rowv, hv * DK * 2, L,
-                           reinterpret_cast<char*>(xb), tid, w);
-  dma_rows<C, DK * 2, 512>(make_rsrc(a.dout + seq0, static_cast<uint32_t>(L) * rowv), rowv, hv * DK * 2, L,
-                           reinterpret_cast<char*>(xb + C * DK), tid, w);
-  for (int e = tid; e < NW * C; e += 512) sGc[e / C][e % C] = 0.f;
-  wait_all();
-  __syncthreads();
-  const float* gam = reinterpret_cast<const float*>(img);
-  const float* lam = gam + C;
-  const float* bet = gam + 2 * C;
-  const float* G2 = gam + 3 * C;
-  const _Float16* Ts = reinterpret_cast<const _Float16*>(img + IM::GT);
-  const _Float16* Ps = Ts + C * LDC;
+                    img + IM::CHK, tid0, w0);
   const _Float16* Ks = reinterpret_cast<const _Float16*>(img + IM::CHK);
   const _Float16* Qs = Ks + C * LDK;
-  const float gamC = gam[L - 1];
-  // strip tiles, transposed (X[j][r]): dRHS then dU | dO then RHS | U
-  _Float16* X0 = xb;
-  _Float16* X1b = xb + XT;
-  _Float16* X2b = xb + 2 * XT;
-  // this lane's strip rows 16tr + 4g .. +3 of column jw into X[jw][.]
-  auto put_strip_t = [&](_Float16* X, const f32x4 (&x)[NT]) {
+  float dqv[NT][4], dkv[NT][4];  // this v-head's (kGroup: the group's) dq_hat / dk_hat, rows 16rt + 4g + e, column i2
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dqv[rt][e] = dkv[rt][e] = 0.f;
+#pragma unroll 1
+  for (int gi = 0; gi < ngi; ++gi) {
+    const int tid = opaque_v<GROUP>(tid0), w = opaque_s<GROUP>(w0), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int jw = 16 * w + c16;         // phase A value column
+    const int i2 = 16 * w + c16;         // phase 1/2 and dq/dk key row
+    const bool qact = w * DPW < NQ;      // this wave owns C x C tiles
+    const int qr = (w * DPW) / NT, qc0 = (w * DPW) % NT;
+    const int hv = MODE == kSplit ? yy : kh * (a.Hv / a.Hk) + gi;
+    const int64_t cbase = (b * a.Hv + hv) * a.NC + c;
+    dma<IM::CHK, 512>(make_rsrc(a.cimg + cbase * static_cast<int64_t>(IM::CHK), IM::CHK), 0, img, tid, w);
+    // H0 / dH: this lane's chained strips (rows 16ti + 4g + e, column jw), as
+    // stored by the chain kernels; the row fragments of phases 1 / 2 come from
+    // the transposed copy Hs written from these strips
+    const rsrc_t hr = make_rsrc(a.hst + cbase * static_cast<int64_t>(DK * DK), DK * DK * 2);
+    const rsrc_t dhr = make_rsrc(a.dhst + cbase * static_cast<int64_t>(DK * DK), DK * DK * 2);
+    f16x8 h0f[NTK / 2], dhf[NTK / 2];
+#pragma unroll
+    for (int kb = 0; kb < NTK / 2; ++kb) {
+      h0f[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(hr, frag_off(w, kb), 0, 0));
+      dhf[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(dhr, frag_off(w, kb), 0, 0));
+    }
+    // Hs[j][i] <- strips (rows i of column j = jw)
+    auto put_state = [&](const f16x8 (&f)[NTK / 2]) {
+#pragma unroll
+      for (int kb = 0; kb < NTK / 2; ++kb) {
+        *reinterpret_cast<f16x4*>(Hs + jw * LDK + 32 * kb + 4 * g) = f16x4{f[kb][0], f[kb][1], f[kb][2], f[kb][3]};
+        *reinterpret_cast<f16x4*>(Hs + jw * LDK + 32 * kb + 16 + 4 * g) = f16x4{f[kb][4], f[kb][5], f[kb][6], f[kb][7]};
+      }
+    };
+    // raw v / dO rows of the chunk, packed [C][DK] bf16, in the strip buffers
+    const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
+    const int64_t seq0 = (sp.t0 + t0) * a.Hv * DK;
+    dma_rows<C, DK * 2, 512>(make_rsrc(a.v + seq0, static_cast<uint32_t>(L) * rowv), rowv, hv * DK * 2, L,
+                             reinterpret_cast<char*>(xb), tid, w);
+    dma_rows<C, DK * 2, 512>(make_rsrc(a.dout + seq0, static_cast<uint32_t>(L) * rowv), rowv, hv * DK * 2, L,
+                             reinterpret_cast<char*>(xb + C * DK), tid, w);
+    for (int e = tid; e < NW * C; e += 512) sGc[e / C][e % C] = 0.f;
+    wait_all();
+    __syncthreads();
+    const float* gam = reinterpret_cast<const float*>(img);
+    const float* lam = gam + C;
+    const float* bet = gam + 2 * C;
+    const float* G2 = gam + 3 * C;
+    const _Float16* Ts = reinterpret_cast<const _Float16*>(img + IM::GT);
+    const _Float16* Ps = Ts + C * LDC;
+    const float gamC = gam[L - 1];
+    // strip tiles, transposed (X[j][r]): dRHS then dU | dO then RHS | U
+    _Float16* X0 = xb;
+    _Float16* X1b = xb + XT;
+    _Float16* X2b = xb + 2 * XT;
+    // this lane's strip rows 16tr + 4g .. +3 of column jw into X[jw][.]
+    auto put_strip_t = [&](_Float16* X, const f32x4 (&x)[NT]) {
+#pragma unroll
+      for (int tr = 0; tr < NT; ++tr)
+        *reinterpret_cast<f16x4*>(X + jw * LDR + 16 * tr + 4 * g) =
+            f16x4{static_cast<_Float16>(x[tr][0]), static_cast<_Float16>(x[tr][1]), static_cast<_Float16>(x[tr][2]),
+                  static_cast<_Float16>(x[tr][3])};
+    };
+
+    // ---- phase A
+    put_state(h0f);
+    float hh = 0.f;  // this lane's part of <dH, H0>
+#pragma unroll
+    for (int kb = 0; kb < NTK / 2; ++kb) {
+#pragma unroll
+      for (int p2 = 0; p2 < 4; ++p2)
+        hh = __builtin_amdgcn_fdot2(f16x2{h0f[kb][2 * p2], h0f[kb][2 * p2 + 1]},
+                                    f16x2{dhf[kb][2 * p2], dhf[kb][2 * p2 + 1]}, hh, false);
+    }
+    f32x4 y[NT], du[NT], u[NT], dr[NT], rhs[NT], dov[NT];
+    f16x4 vraw[NT], draw[NT];
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) {
+      vraw[tr] = tr4(xb, DK, 16 * tr + 4 * g, 16 * w);
+      draw[tr] = tr4(xb + C * DK, DK, 16 * tr + 4 * g, 16 * w);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) y[t] = du[t] = u[t] = dr[t] = zero4();
+    mma_chain_rows2<NT, NTK>(y, du, Ks, LDK, h0f, dhf);
+    lds_barrier();  // every wave holds its v / dO strips: the strip tiles may be overwritten
+    f32x4 psb[NT], psy[NT];
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) {
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * tr + 4 * g);
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(lam + 16 * tr + 4 * g);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
+      float vv[4], dd[4];
+      bf16x4_to_f32(vv, vraw[tr]);
+      bf16x4_to_f32(dd, draw[tr]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float vmy = vv[e] - gv[e] * y[tr][e];
+        psb[tr][e] = vmy;  // completed below once dRHS is known
+        rhs[tr][e] = bv[e] * vmy;
+        du[tr][e] *= lv[e];
+        dov[tr][e] = dd[e];
+      }
+    }
+    f16x8 bf[NT / 2];
+    chain_frags<NT>(bf, rhs);
+    mma_chain_rows<NT, NT>(u, Ts, LDC, bf);
+    chain_frags<NT>(bf, dov);
+    mma_chain_rows_t<NT, NT>(du, Ps, LDC, bf);
+    chain_frags<NT>(bf, du);
+    mma_chain_rows_t<NT, NT>(dr, Ts, LDC, bf);
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr)
-      *reinterpret_cast<f16x4*>(X + jw * LDR + 16 * tr + 4 * g) =
-          f16x4{static_cast<_Float16>(x[tr][0]), static_cast<_Float16>(x[tr][1]), static_cast<_Float16>(x[tr][2]),
-                static_cast<_Float16>(x[tr][3])};
-  };
-
-  // ---- phase A
-  put_state(h0f);
-  float hh = 0.f;  // this lane's part of <dH, H0>
-#pragma unroll
-  for (int kb = 0; kb < NTK / 2; ++kb) {
-#pragma unroll
-    for (int p2 = 0; p2 < 4; ++p2)
-      hh = __builtin_amdgcn_fdot2(f16x2{h0f[kb][2 * p2], h0f[kb][2 * p2 + 1]},
-                                  f16x2{dhf[kb][2 * p2], dhf[kb][2 * p2 + 1]}, hh, false);
-  }
-  f32x4 y[NT], du[NT], u[NT], dr[NT], rhs[NT], dov[NT];
-  f16x4 vraw[NT], draw[NT];
-#pragma unroll
-  for (int tr = 0; tr < NT; ++tr) {
-    vraw[tr] = tr4(xb, DK, 16 * tr + 4 * g, 16 * w);
-    draw[tr] = tr4(xb + C * DK, DK, 16 * tr + 4 * g, 16 * w);
-  }
-#pragma unroll
-  for (int t = 0; t < NT; ++t) y[t] = du[t] = u[t] = dr[t] = zero4();
-  mma_chain_rows2<NT, NTK>(y, du, Ks, LDK, h0f, dhf);
-  lds_barrier();  // every wave holds its v / dO strips: the strip tiles may be overwritten
-  f32x4 psb[NT], psy[NT];
-#pragma unroll
-  for (int tr = 0; tr < NT; ++tr) {
-    const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * tr + 4 * g);
-    const f32x4 lv = *reinterpret_cast<const f32x4*>(lam + 16 * tr + 4 * g);
-    const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
-    float vv[4], dd[4];
-    bf16x4_to_f32(vv, vraw[tr]);
-    bf16x4_to_f32(dd, draw[tr]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float vmy = vv[e] - gv[e] * y[tr][e];
-      psb[tr][e] = vmy;  // completed below once dRHS is known
-      rhs[tr][e] = bv[e] * vmy;
-      du[tr][e] *= lv[e];
-      dov[tr][e] = dd[e];
-    }
-  }
-  f16x8 bf[NT / 2];
-  chain_frags<NT>(bf, rhs);
-  mma_chain_rows<NT, NT>(u, Ts, LDC, bf);
-  chain_frags<NT>(bf, dov);
-  mma_chain_rows_t<NT, NT>(du, Ps, LDC, bf);
-  chain_frags<NT>(bf, du);
-  mma_chain_rows_t<NT, NT>(dr, Ts, LDC, bf);
-#pragma unroll
-  for (int tr = 0; tr < NT; ++tr)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      psb[tr][e] *= dr[tr][e];
-      psy[tr][e] = dr[tr][e] * y[tr][e];
-    }
-  put_strip_t(X0, dr);
-  put_strip_t(X1b, dov);
-  put_strip_t(X2b, u);
-  // This wave's shares of dbeta_r and dG_r (rows 16tr + 4g + e, summed over
-  // its 16 value columns) start the per-wave row sums sB / sG:
-  // dbeta_r = sum_j dRHS (V - gam Y);  dG_r = -beta gam sum_j dRHS Y + ...
-#pragma unroll
-  for (int tr = 0; tr < NT; ++tr) {
-    const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * tr + 4 * g);
-    const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
-    f32x4 rb, rg;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      rb[e] = row16_sum(psb[tr][e]);
-      rg[e] = -bv[e] * gv[e] * row16_sum(psy[tr][e]);
-    }
-    if (c16 == 0) {
-      *reinterpret_cast<f32x4*>(&sB[w][16 * tr + 4 * g]) = rb;
-      *reinterpret_cast<f32x4*>(&sG[w][16 * tr + 4 * g]) = rg;
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 1: X1 = dRHS H0^T, X2 = dO H0^T, dP = dO U^T
-  f32x4 x1[NT], x2[NT], x3[NT], dP[DPW], dT[DPW];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) x1[t] = x2[t] = x3[t] = zero4();
-#pragma unroll
-  for (int t = 0; t < DPW; ++t) dP[t] = dT[t] = zero4();
-#pragma unroll
-  for (int ks = 0; ks < DK / 32; ++ks) {
-    const f16x8 bfr = frag_t(Hs, LDK, 32 * ks, 16 * w);  // H0[i2][32ks + 8g ..]
-    f16x8 a1[NT], a2[NT];
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt) {
-      a1[rt] = frag_t(X0, LDR, 32 * ks, 16 * rt);
-      a2[rt] = frag_t(X1b, LDR, 32 * ks, 16 * rt);
-    }
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt) {
-      x1[rt] = F16Op::mma(a1[rt], bfr, x1[rt]);
-      x2[rt] = F16Op::mma(a2[rt], bfr, x2[rt]);
-    }
-  }
-  if (qact) {
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) {
-      const f16x8 af = frag_t(X1b, LDR, 32 * ks, 16 * qr);
-#pragma unroll
-      for (int t = 0; t < DPW; ++t) dP[t] = F16Op::mma(af, frag_t(X2b, LDR, 32 * ks, 16 * (qc0 + t)), dP[t]);
-    }
-  }
-  __syncthreads();
-  put_strip_t(X0, du);
-  put_strip_t(X1b, rhs);
-  put_state(dhf);
-  __syncthreads();
-  // ---- phase 2: X3 = U dH^T, dT = dU RHS^T
-#pragma unroll
-  for (int ks = 0; ks < DK / 32; ++ks) {
-    const f16x8 bfr = frag_t(Hs, LDK, 32 * ks, 16 * w);  // dH[i2][32ks + 8g ..]
-    f16x8 a3[NT];
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt) a3[rt] = frag_t(X2b, LDR, 32 * ks, 16 * rt);
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt) x3[rt] = F16Op::mma(a3[rt], bfr, x3[rt]);
-  }
-  if (qact) {
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) {
-      const f16x8 af = frag_t(X0, LDR, 32 * ks, 16 * qr);
-#pragma unroll
-      for (int t = 0; t < DPW; ++t) dT[t] = F16Op::mma(af, frag_t(X1b, LDR, 32 * ks, 16 * (qc0 + t)), dT[t]);
-    }
-  }
-  __syncthreads();
-
-  // Loads used after the products, issued now: the group's running sums of
-  // dq_hat / dk_hat (earlier v-heads; stored per (b, chunk, k-head) in this
-  // kernel's own lane order, 16 bytes per lane and row tile).
-  const int64_t ptile = ((b * a.NC + c) * a.Hk + kh) * static_cast<int64_t>(C * DK);
-  const rsrc_t pqr = make_rsrc(a.pdq + ptile, C * DK * 4);
-  const rsrc_t pkr = make_rsrc(a.pdk + ptile, C * DK * 4);
-  auto poff = [&](int rt) { return static_cast<uint32_t>(((w * NT + rt) * 64 + lane) * 16); };
-  u32x4 pq[NT], pk[NT];
-  if constexpr (MODE == kMid || MODE == kLast) {
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt) {
-      pq[rt] = __builtin_amdgcn_raw_buffer_load_b128(pqr, poff(rt), 0, 0);
-      pk[rt] = __builtin_amdgcn_raw_buffer_load_b128(pkr, poff(rt), 0, 0);
-    }
-  }
-
-  // ---- C x C stage on the tiles (qr, qc0 + t)
-  _Float16* dTT = xb;              // dTT[s'][s] = dT[s][s']
-  _Float16* M1s = dTT + C * LDC;
-  _Float16* dPm = M1s + C * LDC;   // dPm[r][s]
-  _Float16* dPmT = dPm + C * LDC;  // dPmT[s][r]
-  _Float16* dAs = dPmT + C * LDC;  // symmetric dAm + dAm^T
-  float rgc[4] = {0.f, 0.f, 0.f, 0.f}, rbc[4] = {0.f, 0.f, 0.f, 0.f};
-  if (qact) {
-#pragma unroll
-    for (int t = 0; t < DPW; ++t) {
-      const int s2 = 16 * (qc0 + t) + c16;
-      f16x4 t4, p4;
-      float col = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * qr + 4 * g + e;
-        t4[e] = static_cast<_Float16>(dT[t][e]);
-        const float pv = static_cast<float>(Ps[r * LDC + s2]);  // P_rs
-        const float m = s2 <= r ? __builtin_amdgcn_exp2f(G2[r] - G2[s2]) : 0.f;
-        const float dpp = dP[t][e] * pv;
-        rgc[e] += dpp;
-        col += dpp;
-        p4[e] = static_cast<_Float16>(dP[t][e] * m);
-        dPm[r * LDC + s2] = p4[e];
+        psb[tr][e] *= dr[tr][e];
+        psy[tr][e] = dr[tr][e] * y[tr][e];
       }
-      *reinterpret_cast<f16x4*>(dTT + s2 * LDC + 16 * qr + 4 * g) = t4;
-      *reinterpret_cast<f16x4*>(dPmT + s2 * LDC + 16 * qr + 4 * g) = p4;
-      col = xsum<16, 64>(col);
-      if (lane < 16) sGc[w][s2] += col;
-    }
-  }
-  __syncthreads();
-  if (qact) {
-    f32x4 m1[DPW];
+    put_strip_t(X0, dr);
+    put_strip_t(X1b, dov);
+    put_strip_t(X2b, u);
+    // This wave's shares of dbeta_r and dG_r (rows 16tr + 4g + e, summed over
+    // its 16 value columns) start the per-wave row sums sB / sG:
+    // dbeta_r = sum_j dRHS (V - gam Y);  dG_r = -beta gam sum_j dRHS Y + ...
 #pragma unroll
-    for (int t = 0; t < DPW; ++t) m1[t] = zero4();
-    mma_cols_t<DPW, C>(m1, Ts, LDC, 16 * qr, dTT, LDC, 16 * qc0);
-#pragma unroll
-    for (int t = 0; t < DPW; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        M1s[(16 * qr + 4 * g + e) * LDC + 16 * (qc0 + t) + c16] = static_cast<_Float16>(m1[t][e]);
-  }
-  __syncthreads();
-  if (qact) {
-    f32x4 da[DPW], kk[DPW];
-#pragma unroll
-    for (int t = 0; t < DPW; ++t) da[t] = kk[t] = zero4();
-    mma_cols<DPW, C>(da, M1s, LDC, 16 * qr, Ts, LDC, 16 * qc0);
-    mma_cols<DPW, DK>(kk, Ks, LDK, 16 * qr, Ks, LDK, 16 * qc0);
-#pragma unroll
-    for (int t = 0; t < DPW; ++t) {
-      const int s2 = 16 * (qc0 + t) + c16;
-      float col = 0.f;
+    for (int tr = 0; tr < NT; ++tr) {
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * tr + 4 * g);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
+      f32x4 rb, rg;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * qr + 4 * g + e;
-        const float ex = s2 < r ? __builtin_amdgcn_exp2f(G2[r] - G2[s2]) : 0.f;
-        const float dav = -da[t][e] * ex;
-        const float dam = dav * bet[r];
-        const float ag = dam * kk[t][e];
-        rbc[e] += dav * kk[t][e];
-        rgc[e] += ag;
-        col += ag;
-        if (s2 < r) {
-          dAs[r * LDC + s2] = static_cast<_Float16>(dam);
-          dAs[s2 * LDC + r] = static_cast<_Float16>(dam);
-        } else if (s2 == r) {
-          dAs[r * LDC + r] = static_cast<_Float16>(0.f);
+        rb[e] = row16_sum(psb[tr][e]);
+        rg[e] = -bv[e] * gv[e] * row16_sum(psy[tr][e]);
+      }
+      if (c16 == 0) {
+        *reinterpret_cast<f32x4*>(&sB[w][16 * tr + 4 * g]) = rb;
+        *reinterpret_cast<f32x4*>(&sG[w][16 * tr + 4 * g]) = rg;
+      }
+    }
+    __syncthreads();
+
+    // ---- phase 1: X1 = dRHS H0^T, X2 = dO H0^T, dP = dO U^T
+    f32x4 x1[NT], x2[NT], x3[NT], dP[DPW], dT[DPW];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) x1[t] = x2[t] = x3[t] = zero4();
+#pragma unroll
+    for (int t = 0; t < DPW; ++t) dP[t] = dT[t] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      const f16x8 bfr = frag_t(Hs, LDK, 32 * ks, 16 * w);  // H0[i2][32ks + 8g ..]
+      f16x8 a1[NT], a2[NT];
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        a1[rt] = frag_t(X0, LDR, 32 * ks, 16 * rt);
+        a2[rt] = frag_t(X1b, LDR, 32 * ks, 16 * rt);
+      }
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        x1[rt] = F16Op::mma(a1[rt], bfr, x1[rt]);
+        x2[rt] = F16Op::mma(a2[rt], bfr, x2[rt]);
+      }
+    }
+    if (qact) {
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) {
+        const f16x8 af = frag_t(X1b, LDR, 32 * ks, 16 * qr);
+#pragma unroll
+        for (int t = 0; t < DPW; ++t) dP[t] = F16Op::mma(af, frag_t(X2b, LDR, 32 * ks, 16 * (qc0 + t)), dP[t]);
+      }
+    }
+    __syncthreads();
+    put_strip_t(X0, du);
+    put_strip_t(X1b, rhs);
+    put_state(dhf);
+    __syncthreads();
+    // ---- phase 2: X3 = U dH^T, dT = dU RHS^T
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      const f16x8 bfr = frag_t(Hs, LDK, 32 * ks, 16 * w);  // dH[i2][32ks + 8g ..]
+      f16x8 a3[NT];
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) a3[rt] = frag_t(X2b, LDR, 32 * ks, 16 * rt);
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) x3[rt] = F16Op::mma(a3[rt], bfr, x3[rt]);
+    }
+    if (qact) {
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) {
+        const f16x8 af = frag_t(X0, LDR, 32 * ks, 16 * qr);
+#pragma unroll
+        for (int t = 0; t < DPW; ++t) dT[t] = F16Op::mma(af, frag_t(X1b, LDR, 32 * ks, 16 * (qc0 + t)), dT[t]);
+      }
+    }
+    __syncthreads();
+
+    // ---- C x C stage on the tiles (qr, qc0 + t)
+    _Float16* dTT = xb;              // dTT[s'][s] = dT[s][s']
+    _Float16* M1s = dTT + C * LDC;
+    _Float16* dPm = M1s + C * LDC;   // dPm[r][s]
+    _Float16* dPmT = dPm + C * LDC;  // dPmT[s][r]
+    _Float16* dAs = dPmT + C * LDC;  // symmetric dAm + dAm^T
+    float rgc[4] = {0.f, 0.f, 0.f, 0.f}, rbc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (qact) {
+#pragma unroll
+      for (int t = 0; t < DPW; ++t) {
+        const int s2 = 16 * (qc0 + t) + c16;
+        f16x4 t4, p4;
+        float col = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * qr + 4 * g + e;
+          t4[e] = static_cast<_Float16>(dT[t][e]);
+          const float pv = static_cast<float>(Ps[r * LDC + s2]);  // P_rs
+          const float m = s2 <= r ? __builtin_amdgcn_exp2f(G2[r] - G2[s2]) : 0.f;
+          const float dpp = dP[t][e] * pv;
+          rgc[e] += dpp;
+          col += dpp;
+          p4[e] = static_cast<_Float16>(dP[t][e] * m);
+          dPm[r * LDC + s2] = p4[e];
+        }
+        *reinterpret_cast<f16x4*>(dTT + s2 * LDC + 16 * qr + 4 * g) = t4;
+        *reinterpret_cast<f16x4*>(dPmT + s2 * LDC + 16 * qr + 4 * g) = p4;
+        col = xsum<16, 64>(col);
+        if (lane < 16) sGc[w][s2] += col;
+      }
+    }
+    __syncthreads();
+    if (qact) {
+      f32x4 m1[DPW];
+#pragma unroll
+      for (int t = 0; t < DPW; ++t) m1[t] = zero4();
+      mma_cols_t<DPW, C>(m1, Ts, LDC, 16 * qr, dTT, LDC, 16 * qc0);
+#pragma unroll
+      for (int t = 0; t < DPW; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          M1s[(16 * qr + 4 * g + e) * LDC + 16 * (qc0 + t) + c16] = static_cast<_Float16>(m1[t][e]);
+    }
+    __syncthreads();
+    if (qact) {
+      f32x4 da[DPW], kk[DPW];
+#pragma unroll
+      for (int t = 0; t < DPW; ++t) da[t] = kk[t] = zero4();
+      mma_cols<DPW, C>(da, M1s, LDC, 16 * qr, Ts, LDC, 16 * qc0);
+      mma_cols<DPW, DK>(kk, Ks, LDK, 16 * qr, Ks, LDK, 16 * qc0);
+#pragma unroll
+      for (int t = 0; t < DPW; ++t) {
+        const int s2 = 16 * (qc0 + t) + c16;
+        float col = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * qr + 4 * g + e;
+          const float ex = s2 < r ? __builtin_amdgcn_exp2f(G2[r] - G2[s2]) : 0.f;
+          const float dav = -da[t][e] * ex;
+          const float dam = dav * bet[r];
+          const float ag = dam * kk[t][e];
+          rbc[e] += dav * kk[t][e];
+          rgc[e] += ag;
+          col += ag;
+          if (s2 < r) {
+            dAs[r * LDC + s2] = static_cast<_Float16>(dam);
+            dAs[s2 * LDC + r] = static_cast<_Float16>(dam);
+          } else if (s2 == r) {
+            dAs[r * LDC + r] = static_cast<_Float16>(0.f);
+          }
+        }
+        col = xsum<16, 64>(col);
+        if (lane < 16) sGc[w][s2] += col;
+      }
+      f32x4 rg, rb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rg[e] = row16_sum(rgc[e]);
+        rb[e] = row16_sum(rbc[e]);
+      }
+      if (c16 == 0) {
+        f32x4* pg = reinterpret_cast<f32x4*>(&sG[w][16 * qr + 4 * g]);
+        f32x4* pb = reinterpret_cast<f32x4*>(&sB[w][16 * qr + 4 * g]);
+        *pg = *pg + rg;
+        *pb = *pb + rb;
+      }
+    }
+    __syncthreads();
+
+    // ---- dq_hat, dk_hat on Dk tile w; X2 / X3 terms of dG
+    f32x4 dq[NT], dk[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dq[t] = dk[t] = zero4();
+    mma_rows<NT, C>(dq, dPm, LDC, Ks, LDK, 16 * w);
+    mma_rows<NT, C>(dk, dPmT, LDC, Qs, LDK, 16 * w);
+    mma_rows<NT, C>(dk, dAs, LDC, Ks, LDK, 16 * w);
+    float gcx = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * rt + 4 * g);
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(lam + 16 * rt + 4 * g);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * rt + 4 * g);
+      f32x4 rgx;
+      const f16x4 qn4 = tr4(Qs, LDK, 16 * rt + 4 * g, 16 * w);  // Qn[16rt + 4g + e][i2]
+      const f16x4 kn4 = tr4(Ks, LDK, 16 * rt + 4 * g, 16 * w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float qn = static_cast<float>(qn4[e]);
+        const float kn = static_cast<float>(kn4[e]);
+        const float t3 = lv[e] * kn * x3[rt][e];
+        gcx += t3;
+        rgx[e] = row16_sum(gv[e] * qn * x2[rt][e] - t3);
+        dqv[rt][e] += dq[rt][e] + gv[e] * x2[rt][e];
+        dkv[rt][e] += dk[rt][e] + lv[e] * x3[rt][e] - bv[e] * gv[e] * x1[rt][e];
+      }
+      if (c16 == 0) {
+        f32x4* pg = reinterpret_cast<f32x4*>(&sG[w][16 * rt + 4 * g]);
+        *pg = *pg + rgx;
+      }
+    }
+    if constexpr (MODE == kSplit) {  // rows (b * T + t) * Hv + hv of [B * T * Hv][DK]; rows >= L dropped
+      const uint32_t rowp = static_cast<uint32_t>(a.Hv) * DK * 4;
+      const int64_t prow = (b * a.T + t0) * a.Hv + hv;
+      const rsrc_t sq = make_rsrc(a.pdq + prow * DK, static_cast<uint32_t>(L) * rowp);
+      const rsrc_t sk = make_rsrc(a.pdk + prow * DK, static_cast<uint32_t>(L) * rowp);
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t off = (16 * rt + 4 * g + e) * rowp + i2 * 4;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dqv[rt][e]), sq, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dkv[rt][e]), sk, off, 0, 0);
+        }
+    }
+    hh = xsum<1, 64>(hh);
+    gcx = xsum<1, 64>(gcx);
+    if (lane == 0) {
+      red[0][w] = hh;
+      red[1][w] = gcx;
+    }
+    __syncthreads();
+    if (w == 0) {
+      const int r = lane;
+      float dG = 0.f, dB = 0.f;
+      if (r < C) {
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+          dG += sG[w2][r] - sGc[w2][r];
+          dB += sB[w2][r];
         }
       }
-      col = xsum<16, 64>(col);
-      if (lane < 16) sGc[w][s2] += col;
-    }
-    f32x4 rg, rb;
+      if (r == L - 1) {
+        float hs = 0.f, xs = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      rg[e] = row16_sum(rgc[e]);
-      rb[e] = row16_sum(rbc[e]);
-    }
-    if (c16 == 0) {
-      f32x4* pg = reinterpret_cast<f32x4*>(&sG[w][16 * qr + 4 * g]);
-      f32x4* pb = reinterpret_cast<f32x4*>(&sB[w][16 * qr + 4 * g]);
-      *pg = *pg + rg;
-      *pb = *pb + rb;
-    }
-  }
-  __syncthreads();
-
-  // ---- dq_hat, dk_hat on Dk tile w; X2 / X3 terms of dG
-  f32x4 dq[NT], dk[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) dq[t] = dk[t] = zero4();
-  mma_rows<NT, C>(dq, dPm, LDC, Ks, LDK, 16 * w);
-  mma_rows<NT, C>(dk, dPmT, LDC, Qs, LDK, 16 * w);
-  mma_rows<NT, C>(dk, dAs, LDC, Ks, LDK, 16 * w);
-  float dqv[NT][4], dkv[NT][4];
-  float gcx = 0.f;
-#pragma unroll
-  for (int rt = 0; rt < NT; ++rt) {
-    const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * rt + 4 * g);
-    const f32x4 lv = *reinterpret_cast<const f32x4*>(lam + 16 * rt + 4 * g);
-    const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * rt + 4 * g);
-    f32x4 rgx;
-    const f16x4 qn4 = tr4(Qs, LDK, 16 * rt + 4 * g, 16 * w);  // Qn[16rt + 4g + e][i2]
-    const f16x4 kn4 = tr4(Ks, LDK, 16 * rt + 4 * g, 16 * w);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float qn = static_cast<float>(qn4[e]);
-      const float kn = static_cast<float>(kn4[e]);
-      const float t3 = lv[e] * kn * x3[rt][e];
-      gcx += t3;
-      rgx[e] = row16_sum(gv[e] * qn * x2[rt][e] - t3);
-      dqv[rt][e] = dq[rt][e] + gv[e] * x2[rt][e];
-      dkv[rt][e] = dk[rt][e] + lv[e] * x3[rt][e] - bv[e] * gv[e] * x1[rt][e];
-    }
-    if (c16 == 0) {
-      f32x4* pg = reinterpret_cast<f32x4*>(&sG[w][16 * rt + 4 * g]);
-      *pg = *pg + rgx;
-    }
-  }
-  // ---- group sums of dq_hat / dk_hat (rows 16rt + 4g + e, column i2)
-  if constexpr (MODE == kMid || MODE == kLast) {
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dqv[rt][e] += __uint_as_float(pq[rt][e]);
-        dkv[rt][e] += __uint_as_float(pk[rt][e]);
+        for (int w2 = 0; w2 < NW; ++w2) {
+          hs += red[0][w2];
+          xs += red[1][w2];
+        }
+        dG += gamC * hs + xs;
       }
-  }
-  if constexpr (MODE == kSplit) {  // rows (b * T + t) * Hv + hv of [B * T * Hv][DK]; rows >= L dropped
-    const uint32_t rowp = static_cast<uint32_t>(a.Hv) * DK * 4;
-    const int64_t prow = (b * a.T + t0) * a.Hv + hv;
-    const rsrc_t sq = make_rsrc(a.pdq + prow * DK, static_cast<uint32_t>(L) * rowp);
-    const rsrc_t sk = make_rsrc(a.pdk + prow * DK, static_cast<uint32_t>(L) * rowp);
+      if (r >= L) dG = 0.f;
+      float x = dG;  // dg_t = sum_{r >= t} dG_r
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t off = (16 * rt + 4 * g + e) * rowp + i2 * 4;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dqv[rt][e]), sq, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dkv[rt][e]), sk, off, 0, 0);
+      for (int off = 1; off < 64; off <<= 1) {
+        const float yv = __shfl_down(x, off, 64);
+        if (lane + off < 64) x += yv;
       }
-  }
-  if constexpr (MODE == kFirst || MODE == kMid) {
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt) {
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(dqv[rt][0]), __float_as_uint(dqv[rt][1]),
-                                                   __float_as_uint(dqv[rt][2]), __float_as_uint(dqv[rt][3])},
-                                             pqr, poff(rt), 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(dkv[rt][0]), __float_as_uint(dkv[rt][1]),
-                                                   __float_as_uint(dkv[rt][2]), __float_as_uint(dkv[rt][3])},
-                                             pkr, poff(rt), 0, 0);
-    }
-  }
-  hh = xsum<1, 64>(hh);
-  gcx = xsum<1, 64>(gcx);
-  if (lane == 0) {
-    red[0][w] = hh;
-    red[1][w] = gcx;
-  }
-  __syncthreads();
-  if (w == 0) {
-    const int r = lane;
-    float dG = 0.f, dB = 0.f;
-    if (r < C) {
-#pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) {
-        dG += sG[w2][r] - sGc[w2][r];
-        dB += sB[w2][r];
+      if (r < L) {
+        const int64_t row = (sp.t0 + t0 + r) * a.Hv + hv;
+        a.dg[row] = a.fg ? x * fg_dlog_alpha(a.g[row]) : x;
+        a.dbeta[row] = a.fg ? dB * fg_dbeta(a.beta[row]) : dB;
       }
     }
-    if (r == L - 1) {
-      float hs = 0.f, xs = 0.f;
-#pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) {
-        hs += red[0][w2];
-        xs += red[1][w2];
-      }
-      dG += gamC * hs + xs;
-    }
-    if (r >= L) dG = 0.f;
-    float x = dG;  // dg_t = sum_{r >= t} dG_r
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float yv = __shfl_down(x, off, 64);
-      if (lane + off < 64) x += yv;
-    }
-    if (r < L) {
-      const int64_t row = (sp.t0 + t0 + r) * a.Hv + hv;
-      a.dg[row] = a.fg ? x * fg_dlog_alpha(a.g[row]) : x;
-      a.dbeta[row] = a.fg ? dB * fg_dbeta(a.beta[row]) : dB;
-    }
+    if constexpr (GROUP) __syncthreads();  // the next v-head reloads the chunk image, strips and row sums
   }
-  if constexpr (MODE == kLast || MODE == kOnly) {
+  if constexpr (MODE != kSplit) {
+    const int tid = tid0, w = w0, lane = tid & 63, g = lane >> 4, c16 = lane & 15, i2 = 16 * w + c16;
     // L2-norm VJP of the group's sums: with x_hat = r x and
     // r = (|x|^2 + eps)^(-1/2), dx = r (dx_hat - x_hat (x_hat . dx_hat)) (the
     // Megatron-LM page's fold of the norm into the kernel, differentiated);
@@ -2266,14 +2252,13 @@ constexpr size_t kAlign = 256;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Ws16 {
-  size_t kimg, cimg, hst, dhst, pdq, pdk, total;  // pdq / pdk: group running sums (Hv > Hk)
+  size_t kimg, cimg, hst, dhst, pdq, pdk, total;  // pdq / pdk: per-v-head dq_hat / dk_hat rows (split gradient)
 };
 
-// The v-heads of a k-head group run their gradient work as consecutive
-// launches (a running sum of dq_hat / dk_hat, the L2-norm VJP in the last)
-// when one launch fills the GPU; with fewer (chunk, k-head, b) workgroups
-// than CUs they run as one launch over every v-head, and the epilogue kernel
-// sums the group and applies the norm VJP.
+// A k-head group's v-heads share one gradient workgroup per (chunk, k-head,
+// b) when that gives at least one workgroup per CU; with fewer, the gradient
+// launch runs one workgroup per v-head and the epilogue kernel sums the
+// group and applies the norm VJP.
 constexpr int kCUs = 256;
 bool grad_split(const Shape& s, int C) {
   const int64_t nc = (s.T + C - 1) / C;
@@ -2290,12 +2275,12 @@ Ws16 plan16(const Shape& s, bool bwd) {
   w.kimg = off; off = up(off + nk * IM::KEY);
   w.cimg = off; off = up(off + nv * IM::CHK);
   if (bwd) {
-    // running-sum tiles per (b, chunk, k-head), or with a split gradient
-    // launch the rows of every v-head ([B * T * Hv][DK] <= B * nc * C * Hv rows)
-    const size_t rows = static_cast<size_t>(s.B) * nc * C * (grad_split(s, C) ? s.Hv : s.Hk);
+    // with a split gradient launch, the dq_hat / dk_hat rows of every v-head
+    // ([B * T * Hv][DK] <= B * nc * C * Hv rows)
+    const size_t rows = static_cast<size_t>(s.B) * nc * C * s.Hv;
     w.hst = off;  off = up(off + nv * DK * DK * 2);
     w.dhst = off; off = up(off + nv * DK * DK * 2);
-    if (s.Hv > s.Hk) {
+    if (grad_split(s, C)) {
       w.pdq = off;  off = up(off + rows * DK * 4);
       w.pdk = off;  off = up(off + rows * DK * 4);
     }
@@ -2321,7 +2306,7 @@ K16 args16(const Shape& s, int C, void* ws, const Ws16& w) {
   if (w.hst || w.dhst) {
     a.hst = reinterpret_cast<_Float16*>(base + w.hst);
     a.dhst = reinterpret_cast<_Float16*>(base + w.dhst);
-    if (s.Hv > s.Hk) {
+    if (w.pdq) {
       a.pdq = reinterpret_cast<float*>(base + w.pdq);
       a.pdk = reinterpret_cast<float*>(base + w.pdk);
     }
@@ -2365,22 +2350,13 @@ hipError_t grad16(const Shape& s, K16 a, hipStream_t st) {
     EpiArgs ea{a.q, a.k, a.pdq, a.pdk, nullptr, nullptr, 1, a.dq, a.dk, a.dbeta, a.dg, a.g, a.beta, a.cu};
     return launch_bwd_epilogue(s, ea, st);
   }
-  for (int gi = 0; gi < grp; ++gi) {
-    a.gi = gi;
-    const dim3 grid(a.NC, a.Hk, static_cast<unsigned>(a.B));
-    ProfScope ps("chunk_grad", st);
-    if (grp == 1)
-      hipLaunchKernelGGL((grad16_kernel<C, TO, kOnly>), grid, dim3(512), 0, st, a);
-    else if (gi == 0)
-      hipLaunchKernelGGL((grad16_kernel<C, TO, kFirst>), grid, dim3(512), 0, st, a);
-    else if (gi + 1 < grp)
-      hipLaunchKernelGGL((grad16_kernel<C, TO, kMid>), grid, dim3(512), 0, st, a);
-    else
-      hipLaunchKernelGGL((grad16_kernel<C, TO, kLast>), grid, dim3(512), 0, st, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  ProfScope ps("chunk_grad", st);
+  const dim3 grid(a.NC, a.Hk, static_cast<unsigned>(a.B));
+  if (grp == 1)
+    hipLaunchKernelGGL((grad16_kernel<C, TO, kOnly>), grid, dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((grad16_kernel<C, TO, kGroup>), grid, dim3(512), 0, st, a);
+  return hipGetLastError();
 }
 
 template <int C, typename TO>

@@ -93,10 +93,11 @@ def test_chunked_vjp_sweep(B, T):
 
 @pytest.mark.parametrize("B,T,Hk,Hv,C", [(2, 500, 16, 64, 64), (1, 1000, 16, 48, 32)])
 def test_chunked_vjp_group_launches(B, T, Hk, Hv, C):
-    """The gradient work of a k-head group as consecutive launches (the
-    (chunk, k-head, b) grid fills the GPU): GQA 1:4 and 1:3, so the launches
-    in the middle add to the group's running sum, ragged last chunk, h0 and
-    dht nonzero; sampled groups against the oracle."""
+    """The gradient work of a k-head group in one workgroup per (chunk,
+    k-head, b) (that grid fills the GPU): GQA 1:4 and 1:3, so the workgroup
+    walks four or three v-heads and the middle ones add to the group sums it
+    holds, ragged last chunk, h0 and dht nonzero; sampled groups against the
+    oracle."""
     x = make_inputs(3100 + T + Hv, B, T, Hk, Hv, 128, 128, io_dtype="bf16", h0_std=0.02)
     dht = (0.1 * np.random.default_rng(T + Hv).standard_normal((B, Hv, 128, 128))).astype(np.float32)
     check_bwd(x, "bf16", dht=dht, heads=[(0, 0), (B - 1, Hk - 1)], algo=("chunked", C))
@@ -166,8 +167,8 @@ def test_bf16_outputs_small(save):
 
 def test_bf16_outputs_benchmark_shape():
     """The benchmark's step: B=4, T=4096, Hk=16, Hv=32, D=128, C=64, bf16 io
-    and outputs, the forward saving its chunks for the VJP (gradient work as
-    consecutive launches, the last one writing bf16 dq / dk through LDS);
+    and outputs, the forward saving its chunks for the VJP (one gradient
+    workgroup per k-head group, writing bf16 dq / dk through LDS);
     two sampled (b, k-head) groups against the oracle."""
     x = make_inputs(3400, 4, 4096, 16, 32, 128, 128, io_dtype="bf16")  # zero h0, as benchmarked
     assert x["h0"] is None

@@ -83,8 +83,8 @@ def test_ragged_chunked_saved_chunks():
 
 def test_ragged_chunked_vjp_group_launches():
     """A ragged batch whose (chunk, k-head, sequence) grid fills the GPU, so
-    the gradient work of a k-head group runs as consecutive launches with a
-    running sum (Hk=32, Hv=64): empty, 1-token and ragged-chunk sequences."""
+    one gradient workgroup walks the v-heads of its k-head group (Hk=32,
+    Hv=64): empty, 1-token and ragged-chunk sequences."""
     run_and_check([0, 1, 130, 200], "bf16", "chunked", 64, seed=7, Hk=32, Hv=64)
 
 
