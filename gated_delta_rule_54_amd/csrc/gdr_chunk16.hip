@@ -1102,7 +1102,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   constexpr int NQ = NT * NT;                    // C x C tiles
   constexpr int DPW = NQ >= NW ? NQ / NW : 1;    // C x C tiles per wave, all in one row tile
   static_assert(5 * C * LDC <= XB, "C x C stage buffers alias the strip buffers");
-  static_assert(2 * C * DK <= XB, "raw v / dO tiles fit the strip buffers");
+  static_assert(2 * C * DK <= DK * LDK, "raw v / dO tiles fit the state buffer");
   static_assert(2 * C * LDQ * 2 + 4 * NW * C * 4 <= XB * 2, "dq / dk tiles and norm partials fit the strip buffers");
   __shared__ __align__(16) char img[IM::CHK + IM::KEY];
   __shared__ __align__(16) _Float16 xb[XB];
@@ -1134,6 +1134,18 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
                     img + IM::CHK, tid0, w0);
   const _Float16* Ks = reinterpret_cast<const _Float16*>(img + IM::CHK);
   const _Float16* Qs = Ks + C * LDK;
+  // raw v / dO rows of a v-head's chunk, packed [C][DK] bf16, in the state
+  // buffer Hs, which holds them until phase A has taken its strips; the next
+  // v-head's rows are requested as soon as phase 2 has read dH from Hs
+  const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
+  const int64_t seq0 = (sp.t0 + t0) * a.Hv * DK;
+  auto load_vdo = [&](int hvx, int tid, int w) {
+    dma_rows<C, DK * 2, 512>(make_rsrc(a.v + seq0, static_cast<uint32_t>(L) * rowv), rowv, hvx * DK * 2, L,
+                             reinterpret_cast<char*>(Hs), tid, w);
+    dma_rows<C, DK * 2, 512>(make_rsrc(a.dout + seq0, static_cast<uint32_t>(L) * rowv), rowv, hvx * DK * 2, L,
+                             reinterpret_cast<char*>(Hs + C * DK), tid, w);
+  };
+  load_vdo(MODE == kSplit ? yy : kh * (a.Hv / a.Hk), tid0, w0);
   float dqv[NT][4], dkv[NT][4];  // this v-head's (kGroup: the group's) dq_hat / dk_hat, rows 16rt + 4g + e, column i2
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt)
@@ -1168,16 +1180,11 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
         *reinterpret_cast<f16x4*>(Hs + jw * LDK + 32 * kb + 16 + 4 * g) = f16x4{f[kb][4], f[kb][5], f[kb][6], f[kb][7]};
       }
     };
-    // raw v / dO rows of the chunk, packed [C][DK] bf16, in the strip buffers
-    const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
-    const int64_t seq0 = (sp.t0 + t0) * a.Hv * DK;
-    dma_rows<C, DK * 2, 512>(make_rsrc(a.v + seq0, static_cast<uint32_t>(L) * rowv), rowv, hv * DK * 2, L,
-                             reinterpret_cast<char*>(xb), tid, w);
-    dma_rows<C, DK * 2, 512>(make_rsrc(a.dout + seq0, static_cast<uint32_t>(L) * rowv), rowv, hv * DK * 2, L,
-                             reinterpret_cast<char*>(xb + C * DK), tid, w);
-    for (int e = tid; e < NW * C; e += 512) sGc[e / C][e % C] = 0.f;
     wait_all();
     __syncthreads();
+    // column sums of this v-head: each wave clears its own row (wave 0 reads
+    // all rows for the previous v-head's dg before it passes the barrier above)
+    if (lane < C) sGc[w][lane] = 0.f;
     const float* gam = reinterpret_cast<const float*>(img);
     const float* lam = gam + C;
     const float* bet = gam + 2 * C;
@@ -1199,7 +1206,6 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     };
 
     // ---- phase A
-    put_state(h0f);
     float hh = 0.f;  // this lane's part of <dH, H0>
 #pragma unroll
     for (int kb = 0; kb < NTK / 2; ++kb) {
@@ -1212,13 +1218,14 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     f16x4 vraw[NT], draw[NT];
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr) {
-      vraw[tr] = tr4(xb, DK, 16 * tr + 4 * g, 16 * w);
-      draw[tr] = tr4(xb + C * DK, DK, 16 * tr + 4 * g, 16 * w);
+      vraw[tr] = tr4(Hs, DK, 16 * tr + 4 * g, 16 * w);
+      draw[tr] = tr4(Hs + C * DK, DK, 16 * tr + 4 * g, 16 * w);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) y[t] = du[t] = u[t] = dr[t] = zero4();
     mma_chain_rows2<NT, NTK>(y, du, Ks, LDK, h0f, dhf);
-    lds_barrier();  // every wave holds its v / dO strips: the strip tiles may be overwritten
+    lds_barrier();  // every wave holds its v / dO strips: Hs may take H0
+    put_state(h0f);
     f32x4 psb[NT], psy[NT];
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr) {
@@ -1327,6 +1334,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       }
     }
     __syncthreads();
+    if (gi + 1 < ngi) load_vdo(hv + 1, tid, w);  // Hs is free until the next v-head's phase A
 
     // ---- C x C stage on the tiles (qr, qc0 + t)
     _Float16* dTT = xb;              // dTT[s'][s] = dT[s][s']
@@ -1501,7 +1509,6 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
         a.dbeta[row] = a.fg ? dB * fg_dbeta(a.beta[row]) : dB;
       }
     }
-    if constexpr (GROUP) __syncthreads();  // the next v-head reloads the chunk image, strips and row sums
   }
   if constexpr (MODE != kSplit) {
     const int tid = tid0, w = w0, lane = tid & 63, g = lane >> 4, c16 = lane & 15, i2 = 16 * w + c16;
