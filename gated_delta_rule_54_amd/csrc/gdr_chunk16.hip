@@ -1145,7 +1145,28 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     dma_rows<C, DK * 2, 512>(make_rsrc(a.dout + seq0, static_cast<uint32_t>(L) * rowv), rowv, hvx * DK * 2, L,
                              reinterpret_cast<char*>(Hs + C * DK), tid, w);
   };
-  load_vdo(MODE == kSplit ? yy : kh * (a.Hv / a.Hk), tid0, w0);
+  // a v-head's chunk image (into img) and this lane's chained strips of its
+  // H0 / dH (rows 16ti + 4g + e, column jw, as the chain kernels store them;
+  // the row fragments of phases 1 / 2 come from the transposed copy Hs
+  // written from these strips); the next v-head's are requested once its
+  // predecessor's last products are done
+  auto load_cimg = [&](int hvx, int tid, int w) {
+    const int64_t cb = (b * a.Hv + hvx) * a.NC + c;
+    dma<IM::CHK, 512>(make_rsrc(a.cimg + cb * static_cast<int64_t>(IM::CHK), IM::CHK), 0, img, tid, w);
+  };
+  auto load_states = [&](f16x8 (&h0f)[NTK / 2], f16x8 (&dhf)[NTK / 2], int hvx, int w) {
+    const int64_t cb = (b * a.Hv + hvx) * a.NC + c;
+    const rsrc_t hr = make_rsrc(a.hst + cb * static_cast<int64_t>(DK * DK), DK * DK * 2);
+    const rsrc_t dhr = make_rsrc(a.dhst + cb * static_cast<int64_t>(DK * DK), DK * DK * 2);
+#pragma unroll
+    for (int kb = 0; kb < NTK / 2; ++kb) {
+      h0f[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(hr, frag_off(w, kb), 0, 0));
+      dhf[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(dhr, frag_off(w, kb), 0, 0));
+    }
+  };
+  const int hv0 = MODE == kSplit ? yy : kh * (a.Hv / a.Hk);
+  load_vdo(hv0, tid0, w0);
+  load_cimg(hv0, tid0, w0);
   float dqv[NT][4], dkv[NT][4];  // this v-head's (kGroup: the group's) dq_hat / dk_hat, rows 16rt + 4g + e, column i2
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt)
@@ -1158,20 +1179,9 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     const int i2 = 16 * w + c16;         // phase 1/2 and dq/dk key row
     const bool qact = w * DPW < NQ;      // this wave owns C x C tiles
     const int qr = (w * DPW) / NT, qc0 = (w * DPW) % NT;
-    const int hv = MODE == kSplit ? yy : kh * (a.Hv / a.Hk) + gi;
-    const int64_t cbase = (b * a.Hv + hv) * a.NC + c;
-    dma<IM::CHK, 512>(make_rsrc(a.cimg + cbase * static_cast<int64_t>(IM::CHK), IM::CHK), 0, img, tid, w);
-    // H0 / dH: this lane's chained strips (rows 16ti + 4g + e, column jw), as
-    // stored by the chain kernels; the row fragments of phases 1 / 2 come from
-    // the transposed copy Hs written from these strips
-    const rsrc_t hr = make_rsrc(a.hst + cbase * static_cast<int64_t>(DK * DK), DK * DK * 2);
-    const rsrc_t dhr = make_rsrc(a.dhst + cbase * static_cast<int64_t>(DK * DK), DK * DK * 2);
+    const int hv = hv0 + gi;
     f16x8 h0f[NTK / 2], dhf[NTK / 2];
-#pragma unroll
-    for (int kb = 0; kb < NTK / 2; ++kb) {
-      h0f[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(hr, frag_off(w, kb), 0, 0));
-      dhf[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(dhr, frag_off(w, kb), 0, 0));
-    }
+    load_states(h0f, dhf, hv, w);
     // Hs[j][i] <- strips (rows i of column j = jw)
     auto put_state = [&](const f16x8 (&f)[NTK / 2]) {
 #pragma unroll
@@ -1477,6 +1487,8 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       red[1][w] = gcx;
     }
     __syncthreads();
+    // every wave is past its last read of the chunk image and of h0f / dhf
+    if (gi + 1 < ngi) load_cimg(hv + 1, tid, w);
     if (w == 0) {
       const int r = lane;
       float dG = 0.f, dB = 0.f;
