@@ -196,14 +196,16 @@ __global__ __launch_bounds__(64) void seq_fwd_kernel(Dims d, SeqFwdArgs a) {
   }
 }
 
-// Decode step (T = 1, Dk = Dv = 128): NW waves per 128 x 32 state slice,
-// wave w owning rows (128/NW)w .. (128/NW)(w+1) - 1 (128/(8 NW) rows x 4
-// columns per lane), so each wave issues 1/NW of the state loads and stores
-// of seq_fwd_kernel; the sums over Dk (|k|^2, |q|^2, k.q, p, r) add the
-// waves' parts through LDS.
-template <typename TI, typename TO, bool CW, int NW>
+// Decode step (T = 1, Dk = Dv = 128): NW waves per 128 x BV state slice,
+// wave w owning rows (128/NW)w .. (128/NW)(w+1) - 1 (lanes: BV/4 column
+// groups of 4 columns x 64/(BV/4) row groups of 128/NW/(64/(BV/4)) rows), so
+// each wave issues 1/NW of the slice's state loads and stores; the sums over
+// Dk (|k|^2, |q|^2, k.q, p, r) add the lanes' parts by butterfly and, with
+// more than one wave, the waves' parts through LDS.
+template <typename TI, typename TO, bool CW, int NW, int BV = 32>
 __global__ __launch_bounds__(64 * NW) void decode_kernel(Dims d, SeqFwdArgs a) {
-  constexpr int D = 128, BV = 32, NCG = 8, RPL = D / NW / 8, NV = 11;
+  constexpr int D = 128, NCG = BV / 4, RG = 64 / NCG, RPL = D / NW / RG, NV = 11;
+  static_assert(RPL >= 1 && NCG * RG == 64, "slice shape");
   __shared__ float part[NW][NCG][NV + 1];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int cg = lane % NCG, rg = lane / NCG;
@@ -278,17 +280,19 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(Dims d, SeqFwdArgs a) {
     }
 #pragma unroll
     for (int n = 3; n < NV; ++n) x[n] = xsum<NCG, 64>(x[n]);
-    if (rg == 0) {
+    if constexpr (NW > 1) {
+      if (rg == 0) {
 #pragma unroll
-      for (int n = 0; n < NV; ++n) part[w][cg][n] = x[n];
-    }
-    __syncthreads();
+        for (int n = 0; n < NV; ++n) part[w][cg][n] = x[n];
+      }
+      __syncthreads();
 #pragma unroll
-    for (int n = 0; n < NV; ++n) {  // all waves' parts in one order (every wave gets the same sums)
-      float t = 0.f;
+      for (int n = 0; n < NV; ++n) {  // all waves' parts in one order (every wave gets the same sums)
+        float t = 0.f;
 #pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) t += part[w2][cg][n];
-      x[n] = t;
+        for (int w2 = 0; w2 < NW; ++w2) t += part[w2][cg][n];
+        x[n] = t;
+      }
     }
     const float rk = d.l2 ? rsqrtf(x[0] + kL2Eps) : 1.f;
     const float rq = d.l2 ? rsqrtf(x[1] + kL2Eps) : 1.f;
@@ -753,7 +757,12 @@ __global__ __launch_bounds__(256) void epilogue128_kernel(Dims d, EpiArgs a) {
 Dims dims_of(const Shape& s) { return Dims{s.B, s.T, s.Hk, s.Hv, s.l2norm ? 1 : 0, s.fused_gates ? 1 : 0}; }
 
 template <int D> constexpr int fwd_bv() { return D == 16 ? 16 : 32; }
-constexpr int kDecWaves = 2;  // waves per decode slice (1, 4 and 8 measured slower at B=8, Hv=32)
+// Decode slices at B=8, Hv=32 (rocprofv3 kernel durations on rotated state
+// buffers, us): 32 columns x 2 waves 8.36 (chosen); 32 x 1: 8.64, 32 x 4:
+// 8.87; 64 x 2: 8.57, 64 x 4: 8.58, 64 x 8: 8.69; 128 x 4: 8.90, 128 x 8:
+// 8.93, 128 x 16: 8.90; 16 columns (half a 128-byte line per row) x 1, 2, 4:
+// 12.2 - 13.3.
+constexpr int kDecWaves = 2, kDecCols = 32;
 // with fewer slices than CUs (B=1, Hv=32: 3.45 vs 3.66 us per step with 2 waves, 3.82 with 8)
 constexpr int kDecSmallGrid = 256, kDecWavesSmall = 4;
 template <int D> constexpr int bwd_bv() { return D == 16 ? 16 : 32; }
@@ -770,7 +779,8 @@ hipError_t fwd_go(const Shape& s, const SeqFwdArgs& a, hipStream_t st) {
                            dims_of(s), a);
         return hipGetLastError();
       }
-      hipLaunchKernelGGL((decode_kernel<TI, TO, CW, kDecWaves>), grid, dim3(64 * kDecWaves), 0, st, dims_of(s), a);
+      hipLaunchKernelGGL((decode_kernel<TI, TO, CW, kDecWaves, kDecCols>),
+                         dim3(D / kDecCols, s.Hv, static_cast<unsigned>(s.B)), dim3(64 * kDecWaves), 0, st, dims_of(s), a);
       return hipGetLastError();
     }
   }
