@@ -540,28 +540,43 @@ def host_cpu_share():
     return max(1, min(16, n))
 
 
-def cpu_baseline():
+def oracle_pool():
+    """The oracle's worker processes, one per host CPU of this GPU's share,
+    forked before anything touches the GPU (they inherit the workload's
+    inputs).  They wait idle until cpu_baseline hands them work after the
+    GPU legs: the workers hold about 1 GB of fp64 states each, and freeing
+    that much memory stalls the host for seconds, which would starve the
+    GPU of launches if any timing followed."""
+    import multiprocessing as mp
+    from gated_delta_rule_54_amd.synth import make_inputs
+    global _GROUP_INPUTS
+    _GROUP_INPUTS = make_inputs(2, B, T, HK, HV, D, D, io_dtype="bf16")
+    cores = host_cpu_share()
+    return mp.get_context("fork").Pool(cores), cores
+
+
+def cpu_baseline(pool, cores):
     """The fp64 oracle (forward + VJP, numpy, one BLAS thread per process)
     timed on the host: a sample of the headline workload's (b, k-head)
     groups (each = the Hv/Hk v-heads of one k-head over all T tokens), one
-    group per worker process, all workers at once; whole-workload tokens/s
-    from the sample's wall time.  Also the oracle's single-thread seconds on
-    the tiny case (B=1, T=64, Hk=Hv=2, D=16, fp32, fwd + VJP) and on the
-    decode case (B=8, Hk=16, Hv=32, D=128, 256 tokens, forward).  Must run
-    before anything touches the GPU: the pool is forked."""
-    import multiprocessing as mp
+    group per worker process of oracle_pool, all workers at once;
+    whole-workload tokens/s from the sample's wall time.  Also the oracle's
+    single-thread seconds on the tiny case (B=1, T=64, Hk=Hv=2, D=16, fp32,
+    fwd + VJP) and on the decode case (B=8, Hk=16, Hv=32, D=128, 256 tokens,
+    forward)."""
     from threadpoolctl import threadpool_limits
     from gated_delta_rule_54_amd.synth import make_inputs
     from oracle import gdr_oracle as orc
     global _GROUP_INPUTS
-    _GROUP_INPUTS = make_inputs(2, B, T, HK, HV, D, D, io_dtype="bf16")
-    cores = host_cpu_share()
     n_groups = B * HK
     sample = min(n_groups, cores)
-    with mp.get_context("fork").Pool(cores) as pool:
+    try:
         w0 = time.perf_counter()
         secs = pool.map(_oracle_group, range(sample), chunksize=1)
         wall = time.perf_counter() - w0
+    finally:
+        pool.terminate()
+        pool.join()
     _GROUP_INPUTS = None
     whole = wall * n_groups / sample  # the sample is one round of the pool
     single = {}
@@ -700,10 +715,11 @@ def main():
               "(the path has no multi-GPU mode).", file=sys.stderr)
         sys.exit(2)
 
-    # the oracle's worker pool is forked before anything touches the GPU
-    cpu = None
+    # the oracle's worker pool is forked before anything touches the GPU and
+    # given its work after the last GPU leg
+    pool = None
     if not (args.no_cpu_baseline or args.only_decode or args.only_calibration):
-        cpu = cpu_baseline()
+        pool = oracle_pool()
 
     import torch
     import gated_delta_rule_54_amd as gdr
@@ -802,7 +818,7 @@ def main():
         line["decode"] = bench_decode(torch, gdr, graph=not args.no_graph)
     if not args.no_calibration:
         line["calibration"] = calibration(torch, gdr)
-    line["cpu_baseline"] = cpu
+    line["cpu_baseline"] = cpu_baseline(*pool) if pool is not None else None
     print(json.dumps(line), flush=True)
     copy_calibration(torch, args.copy_calibration_mib)
 
