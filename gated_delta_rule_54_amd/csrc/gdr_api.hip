@@ -172,6 +172,7 @@ const char* gdr_status_str(gdr_status s) {
     case GDR_ERR_BAD_ALIGNMENT: return "pointer not 16-byte aligned (workspace: 256-byte)";
     case GDR_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the size query returned";
     case GDR_ERR_HIP: return "HIP error (see gdr_last_hip_error)";
+    case GDR_STATUS_MAX_ENUM: break;
   }
   return "unknown gdr_status";
 }

@@ -958,7 +958,6 @@ CArgs base_args(const Shape& s, int C) {
 template <typename F>
 hipError_t with_cfg(const Shape& s, int C, F&& f) {
   auto go = [&](auto cfg) -> hipError_t {
-    using CF = decltype(cfg);
     auto by_out = [&](auto ti) -> hipError_t {
       return s.out_bf16 ? f(cfg, ti, std::common_type<bf16_t>{}) : f(cfg, ti, std::common_type<float>{});
     };

@@ -293,25 +293,9 @@ __device__ __forceinline__ void load_strip(f32x4 (&x)[NT], const bf16_t* base, i
     }
 }
 
-// This lane's strip rows 16tr + 4g + e of a bf16 tensor through buffer r
-// (rows rowb bytes apart, voff = byte offset of row 4g at the lane's
-// column), one raw bf16 per word so that nothing waits for the loads until
-// the values are used; rows past the buffer end read 0.
-template <int NT>
-__device__ __forceinline__ void load_strip_buf(uint32_t (&x)[NT][4], rsrc_t r, uint32_t voff, uint32_t rowb) {
-#pragma unroll
-  for (int tr = 0; tr < NT; ++tr)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[tr][e] = __builtin_amdgcn_raw_buffer_load_b16(r, voff + (16 * tr + e) * rowb, 0, 0);
-}
-
-__device__ __forceinline__ void unpack_strip(float (&x)[4], const uint32_t (&w)[4]) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e] << 16);
-}
-
-// Stores this lane's strip rows (as load_strip_buf) as TO; rows past the
-// buffer end are dropped.
+// Stores this lane's strip rows 16tr + 4g + e as TO through buffer r (rows
+// rowb bytes apart, voff = byte offset of row 4g at the lane's column);
+// rows past the buffer end are dropped.
 template <typename TO, int NT>
 __device__ __forceinline__ void store_strip_buf(rsrc_t r, uint32_t voff, uint32_t rowb, const f32x4 (&x)[NT]) {
 #pragma unroll

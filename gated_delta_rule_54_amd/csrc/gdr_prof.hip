@@ -47,14 +47,22 @@ thread_local Profiler g_prof;
 ProfScope::ProfScope(const char* name, hipStream_t st) : stream_(st), active_(g_prof.on) {
   if (!active_) return;
   Pending p{name, g_prof.get(), g_prof.get()};
-  if (p.start) hipEventRecord(p.start, st);
+  // an event that could not be recorded is returned to the pool, and a pair
+  // missing either event is never read back
+  if (p.start && hipEventRecord(p.start, st) != hipSuccess) {
+    g_prof.free_events.push_back(p.start);
+    p.start = nullptr;
+  }
   g_prof.pending.push_back(p);
 }
 
 ProfScope::~ProfScope() {
   if (!active_ || g_prof.pending.empty()) return;
   Pending& p = g_prof.pending.back();
-  if (p.stop) hipEventRecord(p.stop, stream_);
+  if (p.stop && hipEventRecord(p.stop, stream_) != hipSuccess) {
+    g_prof.free_events.push_back(p.stop);
+    p.stop = nullptr;
+  }
 }
 
 }  // namespace gdr

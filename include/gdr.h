@@ -71,7 +71,11 @@ typedef enum gdr_status {
   GDR_ERR_UNSUPPORTED = 3,         /* a valid problem this build cannot run */
   GDR_ERR_BAD_ALIGNMENT = 4,       /* pointer not 16 B (workspace 256 B)    */
   GDR_ERR_WORKSPACE_TOO_SMALL = 5, /* ws_bytes below the *_workspace size   */
-  GDR_ERR_HIP = 6                  /* a HIP launch or copy failed           */
+  GDR_ERR_HIP = 6,                 /* a HIP launch or copy failed           */
+  /* Never returned.  Widens the type's range to every non-negative int, so
+   * any status value a caller passes back (gdr_status_str) is a value of
+   * the type in C++ as in C. */
+  GDR_STATUS_MAX_ENUM = 0x7fffffff
 } gdr_status;
 
 typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
