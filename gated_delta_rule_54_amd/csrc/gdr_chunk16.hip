@@ -75,6 +75,7 @@ struct K16 {
   void* dv;
   float* dh0;
   char *kimg, *cimg;       // [B][Hk][NC] key images, [B][Hv][NC] chunk images
+  char* pkimg;             // channelwise VJP: [B][Hk][NC] unscaled key images (K_hat | Q_hat, norm factors)
   _Float16 *hst, *dhst;    // [B][Hv][NC][DK][DK]: chunk-entry H, chunk-end dH
   float *pdq, *pdk;        // dq_hat / dk_hat over a group's v-heads: running-sum tiles per (b, chunk, k-head)
                            // in the gradient kernel's lane order, or, split launch, rows [B][T][Hv][DK]
@@ -1929,6 +1930,11 @@ __global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
       dkl[e] = __builtin_bit_cast(uint4, okl);
     }
   }
+  if (a.pkimg && hv % (a.Hv / a.Hk) == 0) {  // the k-head's unscaled key image, for the VJP
+    char* pim = a.pkimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(Img<C>::KEY);
+    write_tile<C, UK, NTH, true>(pim, [&](int r, int u) { return ld8(Ks + r * LDK + 8 * u); });
+    write_tile<C, UK, NTH, true>(pim + Img<C>::KN, [&](int r, int u) { return ld8(Qs + r * LDK + 8 * u); });
+  }
   __syncthreads();  // Kn, Qn and G2 are no longer read: their space takes A, T and P
 
   for (int e = tid; e < 2 * CSZ / 16; e += NTH)  // fp16 T and P tiles start at zero
@@ -2249,6 +2255,618 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwdh16_kernel(K16 a) {
 }
 
 // ---------------------------------------------------------------------------
+// cwgrad16: all gradients of one chunk except dH for the channelwise gate
+// (the per-key-channel decay of the page "Two-pass optimization for
+// channelwise gated delta rule kernel"), one workgroup of eight waves per
+// (chunk, k-head, b) walking the group's v-heads in order (as grad16's group
+// walk: dq_hat / dk_hat summed in registers, the L2-norm VJP after the last
+// v-head).  With G_r the per-channel running sum of g over the chunk,
+// W_rs = e^{G_r - G_s} per channel (<= 1 for s <= r), Kg = K o e^G and
+// Kl = K o e^{G_C - G}, per v-head:
+//   Phase A  Y = Kg H0, RHS = beta (V - Y), U = T RHS,
+//            dU = Kl dH + P^T dO, dRHS = T^T dU; dv = beta dRHS;
+//            dbeta_r gets dRHS_r . (V - Y)_r
+//   Phase 1  X1 = dRHS H0^T, X2 = dO H0^T, dP = dO U^T
+//   Phase 2  X3 = U dH^T, dT = dU RHS^T
+//   C x C    dA = -T^T dT T^T (s < r); dP masked to s <= r
+//   then per channel (the decay differs per channel, so the chunk-local
+//   sums carry W inside them):
+//     dq_r   = e^{G_r} X2_r + sum_{s<=r} dP_rs W_rs k_s
+//     dk+_r  = beta_r (-e^{G_r} X1_r + a_r),  a_r = sum_{s<r} dA_rs W_rs k_s
+//     dk-_s  = e^{G_C - G_s} X3_s + sum_{r>=s} dP_rs W_rs q_r
+//              + sum_{r>s} dA_rs beta_r W_rs k_r
+//     dk = dk+ + dk-,  dbeta_r += k_r . a_r,
+//     dG = q o dq + k o (dk+ - dk-), and at the last valid row also
+//       sum_r k_r o (e^{G_C - G_r} X3_r) + e^{G_C} o rowsum(H0 o dH),
+//     dg_t = sum_{r >= t} dG_r.
+//   Blocks of these sums below the 16-row diagonal blocks run as 16x16x16
+//   fp16 matrix-core products with W split at a block boundary, both
+//   factors <= 1: about the last row l of the column block for the row
+//   sums (k_s e^{G_l - G_s}, then e^{G_r - G_l}), about the first row b of
+//   the row block for the column sums (q_r e^{G_r - G_b}, then
+//   e^{G_b - G_s}).  Diagonal blocks are summed exactly in fp32 with one
+//   exponential per pair (arguments clamped at 0 where the mask is zero).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mma16x16x16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+template <int C, typename TO>
+__global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
+  using IM = ImgCW<C>;
+  using IP = Img<C>;
+  constexpr int NW = 8, LDC = IM::LDC, NT = C / 16;
+  constexpr int LDR = C + 8;                   // pitch of the transposed strip tiles X[j][r]
+  constexpr int XT = DK * LDR, XB = 3 * XT;
+  constexpr int LDQ = DK + 8;                  // pitch of the dq / dk output tiles
+  constexpr int NQ = NT * NT;
+  constexpr int DPW = NQ >= NW ? NQ / NW : 1;  // C x C tiles per wave, all in one row tile
+  constexpr int LDG = C + 4;                   // pitch (floats) of G2T[i][r]
+  constexpr uint32_t KXB = 2 * IM::KN > DK * LDG * 4 ? 2 * IM::KN : DK * LDG * 4;
+  static_assert(6 * C * LDC <= XB, "C x C buffers alias the strip buffers");
+  static_assert(IP::KEY <= DK * LDK * 2, "the plain key image fits the state buffer");
+  static_assert(2 * C * DK <= DK * LDK, "raw v / dO tiles fit the state buffer");
+  static_assert(2 * C * LDQ * 2 + 4 * NW * C * 4 <= XB * 2, "dq / dk tiles and norm partials fit the strip buffers");
+  __shared__ __align__(16) char cimg[IM::CHK];     // beta | e^{G_C} | T | P
+  __shared__ __align__(16) char kx[KXB];           // Kg | Kl (phase A), then G2T
+  __shared__ __align__(16) _Float16 xb[XB];
+  __shared__ __align__(16) _Float16 Hs[DK * LDK];  // v / dO rows, H0, dH as Hs[j][i], then K_hat | Q_hat
+  __shared__ __align__(16) float sB[NW][C];        // per-wave parts of dbeta
+  __shared__ __align__(16) float sQ[4][DK];        // running gate sums of the row quarters
+  __shared__ __align__(16) float sDot[2][C];
+  float (*sN)[NW][C] = reinterpret_cast<float (*)[NW][C]>(xb + 2 * C * LDQ);
+
+  const int tid0 = threadIdx.x, w0 = wave_id();
+  const int c = blockIdx.x, kh = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int grp = a.Hv / a.Hk;
+  const int64_t t0 = static_cast<int64_t>(c) * C;
+  const SeqSpan sp = seq_span(a, b);
+  if (t0 >= sp.len) return;  // past the end of a shorter sequence of a ragged batch
+  const int L = static_cast<int>(sp.len - t0 < C ? sp.len - t0 : C);
+  const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
+  const int64_t seq0 = (sp.t0 + t0) * a.Hv * DK;
+  const float* bet = reinterpret_cast<const float*>(cimg);
+  const float* eGC = bet + C;
+  const _Float16* Ts = reinterpret_cast<const _Float16*>(cimg + IM::GT);
+  const _Float16* Ps = Ts + C * LDC;
+  const _Float16* Kg = reinterpret_cast<const _Float16*>(kx);
+  const _Float16* Kl = Kg + C * LDK;
+  float* G2T = reinterpret_cast<float*>(kx);  // log2(e) G[r][i] at G2T[i * LDG + r]
+  const _Float16* Ks = Hs;                    // plain key image: K_hat | Q_hat, norm factors in the row pads
+  const _Float16* Qs = Hs + C * LDK;
+  _Float16* X0 = xb;
+  _Float16* X1b = xb + XT;
+  _Float16* X2b = xb + 2 * XT;
+  _Float16* dTT = xb;  // C x C tiles, after phase 2
+  _Float16* M1s = dTT + C * LDC;
+  _Float16* dPm = M1s + C * LDC;   // dP, s <= r            [r][s]
+  _Float16* dPmT = dPm + C * LDC;  //                       [s][r]
+  _Float16* dAm = dPmT + C * LDC;  // dA, s < r             [r][s]
+  _Float16* dAmT = dAm + C * LDC;  //                       [s][r]
+
+  float dqv[NT][4], dkv[NT][4];  // the group's dq_hat / dk_hat, rows 16rt + 4g + e, column i2
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dqv[rt][e] = dkv[rt][e] = 0.f;
+#pragma unroll 1
+  for (int gi = 0; gi < grp; ++gi) {
+    const int tid = opaque_v<true>(tid0), w = opaque_s<true>(w0), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int jw = 16 * w + c16;  // phase A value column
+    const int i2 = 16 * w + c16;  // key channel of phases 1 / 2 and of the per-channel sums
+    const bool qact = w * DPW < NQ;
+    const int qr = (w * DPW) / NT, qc0 = (w * DPW) % NT;
+    const int hv = kh * grp + gi;
+    const int64_t cb = (b * a.Hv + hv) * a.NC + c;
+    {
+      const char* kim = a.kimg + cb * static_cast<int64_t>(IM::KEY);  // Kg | Qg | Kl
+      dma<IM::CHK, 512>(make_rsrc(a.cimg + cb * static_cast<int64_t>(IM::CHK), IM::CHK), 0, cimg, tid, w);
+      dma<IM::KN, 512>(make_rsrc(kim, IM::KN), 0, kx, tid, w);
+      dma<IM::KN, 512>(make_rsrc(kim + 2 * IM::KN, IM::KN), 0, kx + IM::KN, tid, w);
+      dma_rows<C, DK * 2, 512>(make_rsrc(a.v + seq0, static_cast<uint32_t>(L) * rowv), rowv, hv * DK * 2, L,
+                               reinterpret_cast<char*>(Hs), tid, w);
+      dma_rows<C, DK * 2, 512>(make_rsrc(a.dout + seq0, static_cast<uint32_t>(L) * rowv), rowv, hv * DK * 2, L,
+                               reinterpret_cast<char*>(Hs + C * DK), tid, w);
+    }
+    // this lane's chained strips of H0 / dH (rows 16ti + 4g + e, column jw)
+    f16x8 h0f[NTK / 2], dhf[NTK / 2];
+    {
+      const rsrc_t hr = make_rsrc(a.hst + cb * static_cast<int64_t>(DK * DK), DK * DK * 2);
+      const rsrc_t dhr = make_rsrc(a.dhst + cb * static_cast<int64_t>(DK * DK), DK * DK * 2);
+#pragma unroll
+      for (int kb = 0; kb < NTK / 2; ++kb) {
+        h0f[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(hr, frag_off(w, kb), 0, 0));
+        dhf[kb] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(dhr, frag_off(w, kb), 0, 0));
+      }
+    }
+    auto put_state = [&](const f16x8 (&f)[NTK / 2]) {  // Hs[j][i] <- strips
+#pragma unroll
+      for (int kb = 0; kb < NTK / 2; ++kb) {
+        *reinterpret_cast<f16x4*>(Hs + jw * LDK + 32 * kb + 4 * g) = f16x4{f[kb][0], f[kb][1], f[kb][2], f[kb][3]};
+        *reinterpret_cast<f16x4*>(Hs + jw * LDK + 32 * kb + 16 + 4 * g) = f16x4{f[kb][4], f[kb][5], f[kb][6], f[kb][7]};
+      }
+    };
+    auto put_strip_t = [&](_Float16* X, const f32x4 (&x)[NT]) {  // rows 16tr + 4g .. +3 of column jw
+#pragma unroll
+      for (int tr = 0; tr < NT; ++tr)
+        *reinterpret_cast<f16x4*>(X + jw * LDR + 16 * tr + 4 * g) =
+            f16x4{static_cast<_Float16>(x[tr][0]), static_cast<_Float16>(x[tr][1]), static_cast<_Float16>(x[tr][2]),
+                  static_cast<_Float16>(x[tr][3])};
+    };
+    wait_all();
+    __syncthreads();
+
+    // ---- phase A
+    f32x4 y[NT], du[NT], u[NT], dr[NT], rhs[NT], dov[NT];
+    f16x4 vraw[NT], draw[NT];
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) {
+      vraw[tr] = tr4(Hs, DK, 16 * tr + 4 * g, 16 * w);
+      draw[tr] = tr4(Hs + C * DK, DK, 16 * tr + 4 * g, 16 * w);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) y[t] = du[t] = u[t] = dr[t] = zero4();
+    mma_chain_rows<NT, NTK>(y, Kg, LDK, h0f);
+    mma_chain_rows<NT, NTK>(du, Kl, LDK, dhf);
+    lds_barrier();  // every wave holds its v / dO strips: Hs may take H0
+    put_state(h0f);
+    f32x4 psb[NT];
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) {
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
+      float vv[4], dd[4];
+      bf16x4_to_f32(vv, vraw[tr]);
+      bf16x4_to_f32(dd, draw[tr]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float vmy = vv[e] - y[tr][e];
+        psb[tr][e] = vmy;
+        rhs[tr][e] = bv[e] * vmy;
+        dov[tr][e] = dd[e];
+      }
+    }
+    f16x8 bf[NT / 2];
+    chain_frags<NT>(bf, rhs);
+    mma_chain_rows<NT, NT>(u, Ts, LDC, bf);
+    chain_frags<NT>(bf, dov);
+    mma_chain_rows_t<NT, NT>(du, Ps, LDC, bf);
+    chain_frags<NT>(bf, du);
+    mma_chain_rows_t<NT, NT>(dr, Ts, LDC, bf);
+    {  // dv = beta dRHS; rows past the sequence's end are dropped by the buffer extent
+      const uint32_t rowo = static_cast<uint32_t>(a.Hv) * DK * sizeof(TO);
+      const rsrc_t ovr = make_rsrc(static_cast<char*>(a.dv) + (sp.t0 + t0) * rowo, static_cast<uint32_t>(L) * rowo);
+      f32x4 dvs[NT];
+#pragma unroll
+      for (int tr = 0; tr < NT; ++tr) {
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dvs[tr][e] = bv[e] * dr[tr][e];
+      }
+      store_strip_buf<TO, NT>(ovr, 4 * g * rowo + (hv * DK + jw) * static_cast<uint32_t>(sizeof(TO)), rowo, dvs);
+    }
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) {
+      f32x4 rb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rb[e] = row16_sum(psb[tr][e] * dr[tr][e]);
+      if (c16 == 0) *reinterpret_cast<f32x4*>(&sB[w][16 * tr + 4 * g]) = rb;
+    }
+    put_strip_t(X0, dr);
+    put_strip_t(X1b, dov);
+    put_strip_t(X2b, u);
+    __syncthreads();
+
+    // ---- phase 1: X1 = dRHS H0^T, X2 = dO H0^T, dP = dO U^T; the H0 row
+    // fragments stay for rowsum(H0 o dH) in phase 2
+    f32x4 x1[NT], x2[NT], x3[NT], dP[DPW], dT[DPW];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) x1[t] = x2[t] = x3[t] = zero4();
+#pragma unroll
+    for (int t = 0; t < DPW; ++t) dP[t] = dT[t] = zero4();
+    f16x8 h0k[DK / 32];
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      const f16x8 bfr = frag_t(Hs, LDK, 32 * ks, 16 * w);  // H0[i2][32ks + 8g ..]
+      h0k[ks] = bfr;
+      f16x8 a1[NT], a2[NT];
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        a1[rt] = frag_t(X0, LDR, 32 * ks, 16 * rt);
+        a2[rt] = frag_t(X1b, LDR, 32 * ks, 16 * rt);
+      }
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        x1[rt] = F16Op::mma(a1[rt], bfr, x1[rt]);
+        x2[rt] = F16Op::mma(a2[rt], bfr, x2[rt]);
+      }
+    }
+    if (qact) {
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) {
+        const f16x8 af = frag_t(X1b, LDR, 32 * ks, 16 * qr);
+#pragma unroll
+        for (int t = 0; t < DPW; ++t) dP[t] = F16Op::mma(af, frag_t(X2b, LDR, 32 * ks, 16 * (qc0 + t)), dP[t]);
+      }
+    }
+    __syncthreads();
+    put_strip_t(X0, du);
+    put_strip_t(X1b, rhs);
+    put_state(dhf);
+    __syncthreads();
+    // ---- phase 2: X3 = U dH^T, dT = dU RHS^T
+    float hd = 0.f;  // this lane's part of sum_j H0[i2][j] dH[i2][j]
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      const f16x8 bfr = frag_t(Hs, LDK, 32 * ks, 16 * w);  // dH[i2][32ks + 8g ..]
+#pragma unroll
+      for (int p2 = 0; p2 < 4; ++p2)
+        hd = __builtin_amdgcn_fdot2(f16x2{h0k[ks][2 * p2], h0k[ks][2 * p2 + 1]}, f16x2{bfr[2 * p2], bfr[2 * p2 + 1]},
+                                    hd, false);
+      f16x8 a3[NT];
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) a3[rt] = frag_t(X2b, LDR, 32 * ks, 16 * rt);
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) x3[rt] = F16Op::mma(a3[rt], bfr, x3[rt]);
+    }
+    if (qact) {
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) {
+        const f16x8 af = frag_t(X0, LDR, 32 * ks, 16 * qr);
+#pragma unroll
+        for (int t = 0; t < DPW; ++t) dT[t] = F16Op::mma(af, frag_t(X1b, LDR, 32 * ks, 16 * (qc0 + t)), dT[t]);
+      }
+    }
+    hd = xsum<16, 64>(hd);
+    __syncthreads();
+
+    // ---- Kg / Kl and the states are done: the plain key image goes to Hs,
+    // the running gate sums (log2 units, channel-major) to kx
+    dma<IP::KEY, 512>(make_rsrc(a.pkimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(IP::KEY), IP::KEY), 0,
+                      reinterpret_cast<char*>(Hs), tid, w);
+    constexpr int RQ = C / 4;  // rows per quarter; thread -> channel tid % DK, quarter tid / DK
+    const int gch = tid & (DK - 1), gq = tid >> 7;
+    float grun[RQ];
+    {
+      const float* gp = a.g + ((sp.t0 + t0 + gq * RQ) * a.Hv + hv) * DK + gch;
+      const int64_t rs = static_cast<int64_t>(a.Hv) * DK;
+      float run = 0.f;
+#pragma unroll
+      for (int j = 0; j < RQ; ++j) {
+        float gj = 0.f;
+        if (gq * RQ + j < L) gj = a.fg ? fg_log_alpha(gp[j * rs]) : gp[j * rs];
+        run += gj;
+        grun[j] = run;
+      }
+      sQ[gq][gch] = run;
+    }
+    // C x C stage, part 1: dT transposed, dP masked (and transposed)
+    if (qact) {
+#pragma unroll
+      for (int t = 0; t < DPW; ++t) {
+        const int s2 = 16 * (qc0 + t) + c16;
+        f16x4 t4, p4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * qr + 4 * g + e;
+          t4[e] = static_cast<_Float16>(dT[t][e]);
+          p4[e] = static_cast<_Float16>(s2 <= r ? dP[t][e] : 0.f);
+          dPm[r * LDC + s2] = p4[e];
+        }
+        *reinterpret_cast<f16x4*>(dTT + s2 * LDC + 16 * qr + 4 * g) = t4;
+        *reinterpret_cast<f16x4*>(dPmT + s2 * LDC + 16 * qr + 4 * g) = p4;
+      }
+    }
+    __syncthreads();
+    {
+      float base = 0.f;
+      for (int q2 = 0; q2 < gq; ++q2) base += sQ[q2][gch];
+#pragma unroll
+      for (int j = 0; j < RQ; j += 4)
+        *reinterpret_cast<f32x4*>(G2T + gch * LDG + gq * RQ + j) =
+            f32x4{(grun[j] + base) * kLog2e, (grun[j + 1] + base) * kLog2e, (grun[j + 2] + base) * kLog2e,
+                  (grun[j + 3] + base) * kLog2e};
+    }
+    if (qact) {
+      f32x4 m1[DPW];
+#pragma unroll
+      for (int t = 0; t < DPW; ++t) m1[t] = zero4();
+      mma_cols_t<DPW, C>(m1, Ts, LDC, 16 * qr, dTT, LDC, 16 * qc0);
+#pragma unroll
+      for (int t = 0; t < DPW; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          M1s[(16 * qr + 4 * g + e) * LDC + 16 * (qc0 + t) + c16] = static_cast<_Float16>(m1[t][e]);
+    }
+    __syncthreads();
+    // ---- the per-channel sums start from the products with the states
+    float G2r[NT][4];  // log2(e) G at this lane's rows, channel i2
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(G2T + i2 * LDG + 16 * rt + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) G2r[rt][e] = gv[e];
+    }
+    const float G2C = G2T[i2 * LDG + L - 1];
+    float dq[NT][4], dkp[NT][4], dkm[NT][4], ta[NT][4];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * rt + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float eg = __builtin_amdgcn_exp2f(G2r[rt][e]);
+        dq[rt][e] = eg * x2[rt][e];
+        dkp[rt][e] = -bv[e] * eg * x1[rt][e];
+        dkm[rt][e] = __builtin_amdgcn_exp2f(G2C - G2r[rt][e]) * x3[rt][e];
+        ta[rt][e] = 0.f;
+      }
+    }
+    // C x C stage, part 2: dA = -T^T dT T^T below the diagonal
+    if (qact) {
+      f32x4 da[DPW];
+#pragma unroll
+      for (int t = 0; t < DPW; ++t) da[t] = zero4();
+      mma_cols<DPW, C>(da, M1s, LDC, 16 * qr, Ts, LDC, 16 * qc0);
+#pragma unroll
+      for (int t = 0; t < DPW; ++t) {
+        const int s2 = 16 * (qc0 + t) + c16;
+        f16x4 a4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * qr + 4 * g + e;
+          a4[e] = static_cast<_Float16>(s2 < r ? -da[t][e] : 0.f);
+          dAm[r * LDC + s2] = a4[e];
+        }
+        *reinterpret_cast<f16x4*>(dAmT + s2 * LDC + 16 * qr + 4 * g) = a4;
+      }
+    }
+    wait_all();  // the plain key image
+    __syncthreads();
+
+    // ---- row sums: dq += sum_{s<=r} dP_rs W_rs k_s, a += sum_{s<r} dA_rs W_rs k_s
+#pragma unroll
+    for (int S = 0; S + 1 < NT; ++S) {  // blocks below the diagonal, about the last row of column block S
+      const float g2l = G2T[i2 * LDG + 16 * S + 15];
+      const f16x4 kq = tr4(Ks, LDK, 16 * S + 4 * g, 16 * w);
+      const f32x4 g2s = *reinterpret_cast<const f32x4*>(G2T + i2 * LDG + 16 * S + 4 * g);
+      f16x4 bk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        bk[i] = static_cast<_Float16>(static_cast<float>(kq[i]) * __builtin_amdgcn_exp2f(g2l - g2s[i]));
+#pragma unroll
+      for (int R = S + 1; R < NT; ++R) {
+        const f16x4 ap = *reinterpret_cast<const f16x4*>(dPm + (16 * R + c16) * LDC + 16 * S + 4 * g);
+        const f16x4 aa = *reinterpret_cast<const f16x4*>(dAm + (16 * R + c16) * LDC + 16 * S + 4 * g);
+        const f32x4 tp = mma16x16x16(ap, bk, zero4());
+        const f32x4 tq = mma16x16x16(aa, bk, zero4());
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sc = __builtin_amdgcn_exp2f(G2r[R][e] - g2l);
+          dq[R][e] += sc * tp[e];
+          ta[R][e] += sc * tq[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int R = 0; R < NT; ++R) {  // diagonal blocks, one exponential per pair
+#pragma unroll 1
+      for (int sq = 0; sq < 4; ++sq) {
+        const f16x4 kq = tr4(Ks, LDK, 16 * R + 4 * sq, 16 * w);
+        const f32x4 g2s = *reinterpret_cast<const f32x4*>(G2T + i2 * LDG + 16 * R + 4 * sq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * R + 4 * g + e;
+          const f16x4 pq = *reinterpret_cast<const f16x4*>(dPm + r * LDC + 16 * R + 4 * sq);
+          const f16x4 aq = *reinterpret_cast<const f16x4*>(dAm + r * LDC + 16 * R + 4 * sq);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float wk =
+                static_cast<float>(kq[i]) * __builtin_amdgcn_exp2f(fminf(G2r[R][e] - g2s[i], 0.f));
+            dq[R][e] += static_cast<float>(pq[i]) * wk;
+            ta[R][e] += static_cast<float>(aq[i]) * wk;
+          }
+        }
+      }
+    }
+    // ---- the last row's sum_r k_r o (e^{G_C - G_r} X3_r), before the column sums join dk-
+    float kl3 = 0.f;
+    float qn[NT][4], kn[NT][4];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      const f16x4 q4 = tr4(Qs, LDK, 16 * rt + 4 * g, 16 * w);
+      const f16x4 k4 = tr4(Ks, LDK, 16 * rt + 4 * g, 16 * w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qn[rt][e] = static_cast<float>(q4[e]);
+        kn[rt][e] = static_cast<float>(k4[e]);
+        kl3 += kn[rt][e] * dkm[rt][e];
+      }
+    }
+    kl3 = xsum<16, 64>(kl3);
+    // ---- column sums: dk- += sum_{r>=s} dP_rs W_rs q_r + sum_{r>s} dA_rs beta_r W_rs k_r
+#pragma unroll
+    for (int R = 1; R < NT; ++R) {  // blocks below the diagonal, about the first row of row block R
+      const float g2b = G2T[i2 * LDG + 16 * R];
+      const f16x4 q4 = tr4(Qs, LDK, 16 * R + 4 * g, 16 * w);
+      const f16x4 k4 = tr4(Ks, LDK, 16 * R + 4 * g, 16 * w);
+      const f32x4 g2v = *reinterpret_cast<const f32x4*>(G2T + i2 * LDG + 16 * R + 4 * g);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * R + 4 * g);
+      f16x4 bq, bkb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f = __builtin_amdgcn_exp2f(g2v[i] - g2b);
+        bq[i] = static_cast<_Float16>(static_cast<float>(q4[i]) * f);
+        bkb[i] = static_cast<_Float16>(bv[i] * static_cast<float>(k4[i]) * f);
+      }
+#pragma unroll
+      for (int S = 0; S < R; ++S) {
+        const f16x4 ap = *reinterpret_cast<const f16x4*>(dPmT + (16 * S + c16) * LDC + 16 * R + 4 * g);
+        const f16x4 aa = *reinterpret_cast<const f16x4*>(dAmT + (16 * S + c16) * LDC + 16 * R + 4 * g);
+        f32x4 tp = mma16x16x16(ap, bq, zero4());
+        tp = mma16x16x16(aa, bkb, tp);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dkm[S][e] += __builtin_amdgcn_exp2f(g2b - G2r[S][e]) * tp[e];
+      }
+    }
+#pragma unroll
+    for (int R = 0; R < NT; ++R) {  // diagonal blocks, one exponential per pair
+#pragma unroll 1
+      for (int rq = 0; rq < 4; ++rq) {
+        const f16x4 q4 = tr4(Qs, LDK, 16 * R + 4 * rq, 16 * w);
+        const f16x4 k4 = tr4(Ks, LDK, 16 * R + 4 * rq, 16 * w);
+        const f32x4 g2v = *reinterpret_cast<const f32x4*>(G2T + i2 * LDG + 16 * R + 4 * rq);
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * R + 4 * rq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s = 16 * R + 4 * g + e;
+          const f16x4 pq = *reinterpret_cast<const f16x4*>(dPmT + s * LDC + 16 * R + 4 * rq);
+          const f16x4 aq = *reinterpret_cast<const f16x4*>(dAmT + s * LDC + 16 * R + 4 * rq);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float f = __builtin_amdgcn_exp2f(fminf(g2v[i] - G2r[R][e], 0.f));
+            dkm[R][e] += f * (static_cast<float>(pq[i]) * static_cast<float>(q4[i]) +
+                              static_cast<float>(aq[i]) * bv[i] * static_cast<float>(k4[i]));
+          }
+        }
+      }
+    }
+
+    // ---- dk, dG, dg, dbeta of this v-head
+    float dG[NT][4];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * rt + 4 * g);
+      f32x4 rb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * g + e;
+        rb[e] = row16_sum(kn[rt][e] * ta[rt][e]);
+        dkp[rt][e] += bv[e] * ta[rt][e];
+        float x = qn[rt][e] * dq[rt][e] + kn[rt][e] * (dkp[rt][e] - dkm[rt][e]);
+        if (r == L - 1) x += kl3 + eGC[i2] * hd;
+        dG[rt][e] = r < L ? x : 0.f;
+        dqv[rt][e] += dq[rt][e];
+        dkv[rt][e] += dkp[rt][e] + dkm[rt][e];
+      }
+      if (c16 == 0) {
+        f32x4* pb = reinterpret_cast<f32x4*>(&sB[w][16 * rt + 4 * g]);
+        *pb = *pb + rb;
+      }
+    }
+    {  // dg_t = sum_{r >= t} dG_r per channel: rows 16rt + 4g + e live in
+       // lanes c16 + 16g; suffix within the lane, across the lane groups,
+       // then across the row tiles
+      float tot[NT];
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 3; e >= 0; --e) {
+          s += dG[rt][e];
+          dG[rt][e] = s;
+        }
+        float v1 = __shfl_down(s, 16, 64), v2 = __shfl_down(s, 32, 64), v3 = __shfl_down(s, 48, 64);
+        const float after = (g < 3 ? v1 : 0.f) + (g < 2 ? v2 : 0.f) + (g < 1 ? v3 : 0.f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dG[rt][e] += after;
+        tot[rt] = xsum<16, 64>(s);
+      }
+      float later = 0.f;
+#pragma unroll
+      for (int rt = NT - 1; rt >= 0; --rt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rt + 4 * g + e;
+          if (r < L) {
+            const int64_t idx = ((sp.t0 + t0 + r) * a.Hv + hv) * DK + i2;
+            const float x = dG[rt][e] + later;
+            a.dg[idx] = a.fg ? x * fg_dlog_alpha(a.g[idx]) : x;
+          }
+        }
+        later += tot[rt];
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+      const int r = lane;
+      if (r < L) {
+        float dB = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) dB += sB[w2][r];
+        const int64_t row = (sp.t0 + t0 + r) * a.Hv + hv;
+        a.dbeta[row] = a.fg ? dB * fg_dbeta(a.beta[row]) : dB;
+      }
+    }
+  }
+  {  // L2-norm VJP of the group's sums (x_hat and the norm factors from the plain key image), dq, dk
+    const int tid = tid0, w = w0, lane = tid & 63, g = lane >> 4, c16 = lane & 15, i2 = 16 * w + c16;
+    if (a.l2) {
+      float xq[NT][4], xk[NT][4];
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        const f16x4 q4 = tr4(Qs, LDK, 16 * rt + 4 * g, 16 * w);
+        const f16x4 k4 = tr4(Ks, LDK, 16 * rt + 4 * g, 16 * w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xq[rt][e] = static_cast<float>(q4[e]);
+          xk[rt][e] = static_cast<float>(k4[e]);
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float s1 = row16_sum(xq[rt][e] * dqv[rt][e]);
+          const float s3 = row16_sum(xk[rt][e] * dkv[rt][e]);
+          if (c16 == 0) {
+            const int r = 16 * rt + 4 * g + e;
+            sN[0][w][r] = s1;
+            sN[1][w][r] = s3;
+          }
+        }
+      }
+      __syncthreads();
+      if (tid < 2 * C) {
+        const int m = tid / C, r = tid % C;
+        float sum = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) sum += sN[m][w2][r];
+        sDot[m][r] = sum;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        const f32x4 qd = *reinterpret_cast<const f32x4*>(&sDot[0][16 * rt + 4 * g]);
+        const f32x4 kd = *reinterpret_cast<const f32x4*>(&sDot[1][16 * rt + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rt + 4 * g + e;
+          const float rq = *reinterpret_cast<const float*>(Qs + r * LDK + DK);
+          const float rk = *reinterpret_cast<const float*>(Ks + r * LDK + DK);
+          dqv[rt][e] = rq * (dqv[rt][e] - xq[rt][e] * qd[e]);
+          dkv[rt][e] = rk * (dkv[rt][e] - xk[rt][e] * kd[e]);
+        }
+      }
+    }
+    const uint32_t rowo = static_cast<uint32_t>(a.Hk) * DK * sizeof(TO);
+    const int64_t seqo = (sp.t0 + t0) * a.Hk * DK * static_cast<int64_t>(sizeof(TO));
+    const rsrc_t oqr = make_rsrc(static_cast<char*>(a.dq) + seqo, static_cast<uint32_t>(L) * rowo);
+    const rsrc_t okr = make_rsrc(static_cast<char*>(a.dk) + seqo, static_cast<uint32_t>(L) * rowo);
+    f32x4 oq[NT], ok[NT];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        oq[rt][e] = dqv[rt][e];
+        ok[rt][e] = dkv[rt][e];
+      }
+    const uint32_t voffo = 4 * g * rowo + (kh * DK + i2) * static_cast<uint32_t>(sizeof(TO));
+    store_strip_buf<TO, NT>(oqr, voffo, rowo, oq);
+    store_strip_buf<TO, NT>(okr, voffo, rowo, ok);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 constexpr size_t kAlign = 256;
@@ -2444,32 +3062,25 @@ hipError_t fwd_cw(const Shape& s, const ChunkFwdArgs& x, void* ws, hipStream_t s
   return hipGetLastError();
 }
 
-// Channelwise VJP: the chunk images, every chunk's entry state (forward
-// chain), every chunk's end gradient and dh0 (reverse chain), then the
-// sequential VJP inside every chunk from those two states, all chunks in
-// parallel (partial sums per value slice), and the epilogue (slice and
-// group sums, L2-norm VJP, dq / dk / dbeta / dg).
+// Channelwise VJP: the chunk images (and each k-head's unscaled key image),
+// every chunk's entry state (forward chain), every chunk's end gradient and
+// dh0 (reverse chain), then every chunk's gradients from those two states
+// (cwgrad16: dq, dk, dv, dg, dbeta).
 struct WsCW {
-  size_t kimg, cimg, hst, dhst, pdq, pdk, pdb, pdg, ckpt, scratch, total;
+  size_t kimg, cimg, hst, dhst, pkimg, total;
 };
 
 template <int C>
 WsCW plan_cw_bwd(const Shape& s) {
   using IM = ImgCW<C>;
   const size_t nv = static_cast<size_t>(s.B) * s.Hv * static_cast<size_t>((s.T + C - 1) / C);
-  const size_t ns = static_cast<size_t>(seq_bwd_slices(s)), rows = static_cast<size_t>(s.B * s.T * s.Hv);
   WsCW w{};
   size_t off = 0;
   w.kimg = off;    off = up(off + nv * IM::KEY);
   w.cimg = off;    off = up(off + nv * IM::CHK);
   w.hst = off;     off = up(off + nv * DK * DK * 2);
   w.dhst = off;    off = up(off + nv * DK * DK * 2);
-  w.pdq = off;     off = up(off + ns * rows * DK * 4);
-  w.pdk = off;     off = up(off + ns * rows * DK * 4);
-  w.pdb = off;     off = up(off + ns * rows * 4);
-  w.pdg = off;     off = up(off + ns * rows * DK * 4);
-  w.ckpt = off;    off = up(off + seq_bwd_chunk_ckpt_floats(s, C) * 4);
-  w.scratch = off; off = up(off + seq_bwd_chunk_scratch_floats(s, C) * 4);
+  w.pkimg = off;   off = up(off + static_cast<size_t>(s.B) * s.Hk * ((s.T + C - 1) / C) * Img<C>::KEY);
   w.total = off;
   return w;
 }
@@ -2493,6 +3104,7 @@ hipError_t bwd_cw(const Shape& s, const ChunkBwdArgs& x, void* ws, hipStream_t s
   a.h0 = x.h0;
   a.dht = x.dht;
   a.dh0 = x.dh0;
+  a.pkimg = static_cast<char*>(ws) + w.pkimg;
   const dim3 chains(static_cast<unsigned>(2 * a.Hv * a.B));
   {
     ProfScope ps("chunk_prep_cw", st);
@@ -2512,15 +3124,18 @@ hipError_t bwd_cw(const Shape& s, const ChunkBwdArgs& x, void* ws, hipStream_t s
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  char* base = static_cast<char*>(ws);
-  auto fp = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
-  SeqBwdArgs sa{x.q, x.k, x.v, x.dout, x.g, x.beta, x.h0, x.dht, x.dv, nullptr, fp(w.ckpt), fp(w.scratch),
-                fp(w.pdq), fp(w.pdk), fp(w.pdb), fp(w.pdg), x.cu, a.hst, a.dhst, C, a.NC};
-  hipError_t e = launch_seq_bwd_chunks(s, sa, st);
-  if (e != hipSuccess) return e;
-  EpiArgs ea{x.q, x.k, sa.part_dq, sa.part_dk, sa.part_db, sa.part_dg, seq_bwd_slices(s), x.dq, x.dk, x.dbeta,
-             x.dg, x.g, x.beta, x.cu};
-  return launch_bwd_epilogue(s, ea, st);
+  a.dq = x.dq;
+  a.dk = x.dk;
+  a.dv = x.dv;
+  a.dg = x.dg;
+  a.dbeta = x.dbeta;
+  ProfScope ps("chunk_grad_cw", st);
+  const dim3 grid(a.NC, a.Hk, static_cast<unsigned>(a.B));
+  if (s.out_bf16)
+    hipLaunchKernelGGL((cwgrad16_kernel<C, bf16_t>), grid, dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((cwgrad16_kernel<C, float>), grid, dim3(512), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace

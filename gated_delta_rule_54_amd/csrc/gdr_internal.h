@@ -58,17 +58,8 @@ struct SeqBwdArgs {
   float* part_db;    // [NS][B][T][Hv]
   float* part_dg;    // [NS][B][T][Hv] or [NS][B][T][Hv][D]
   const int64_t* cu; // ragged batch row offsets [B + 1], or null (partials stay [B][T])
-  // chunk mode (launch_seq_bwd_chunks): per-chunk entry states and end
-  // gradients, [B][Hv][NC][128 x 128] fp16 in chained-fragment order
-  const _Float16 *hst, *dhst;
-  int C, NC;
 };
 hipError_t launch_seq_bwd(const Shape& s, const SeqBwdArgs& a, hipStream_t st);
-// The same VJP with every chunk of C tokens in its own workgroups (chunk
-// mode; Dk = Dv = 128): ckpt / scratch sized by the two functions below.
-size_t seq_bwd_chunk_ckpt_floats(const Shape& s, int C);
-size_t seq_bwd_chunk_scratch_floats(const Shape& s, int C);
-hipError_t launch_seq_bwd_chunks(const Shape& s, const SeqBwdArgs& a, hipStream_t st);
 
 // ---- backward epilogue (shared by both paths) ------------------------------
 // Sums per-slice / per-v-head partials in a fixed order, applies the L2-norm

@@ -334,57 +334,23 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(Dims d, SeqFwdArgs a) {
 //   dH  = diag(alpha) dD
 // dq, dk, dbeta, dg sum over value columns, so each slice writes partial
 // sums that the epilogue adds in slice order.
-//
-// CHK (chunk mode, Dk = Dv = 128): one workgroup per (value slice, chunk)
-// covers only the chunk's tokens, starting from the chunk's entry state and
-// its end gradient as the chunk chains stored them (fp16, chained-fragment
-// order); the chunks of a sequence then run in parallel.  dh0 comes from the
-// reverse chain instead.
-typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
-
-// The lane's rows i0 .. i0 + RPL - 1, columns j0 .. j0 + 3 of a [128][128]
-// fp16 state in chained-fragment order: entry (wg, kb, lane', e) (8 halves
-// per lane and fragment) holds row 32kb + 16(e/4) + 4(lane'/16) + e%4 and
-// column 16wg + lane'%16, so 4 aligned rows of one column are 8 bytes.
-template <int RPL>
-__device__ __forceinline__ void load_state_frag(const _Float16* st, int i0, int j0, float (&h)[RPL][4]) {
-#pragma unroll
-  for (int m4 = 0; m4 < RPL / 4; ++m4) {
-    const int i = i0 + 4 * m4, kb = i >> 5, r32 = i & 31, hi = r32 >> 4, q = (r32 & 15) >> 2;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = j0 + e;
-      const h16x4 v = *reinterpret_cast<const h16x4*>(st + (((j >> 4) * 4 + kb) * 64 + 16 * q + (j & 15)) * 8 + 4 * hi);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) h[4 * m4 + r][e] = static_cast<float>(v[r]);
-    }
-  }
-}
-
-template <int D, int BV, typename TI, typename TO, bool CW, bool CHK>
+template <int D, int BV, typename TI, typename TO, bool CW>
 __global__ __launch_bounds__(64) void seq_bwd_kernel(Dims d, SeqBwdArgs a, int nck, int ns) {
   using L = Lay<D, BV>;
   constexpr int RPL = L::RPL;
-  static_assert(!CHK || (D == 128 && BV == 32), "chunk mode reads the 128 x 128 fragment-order states");
   const int lane = threadIdx.x;
   const int cg = lane % L::NCG, rg = lane / L::NCG;
-  const int slice = CHK ? static_cast<int>(blockIdx.x) % ns : static_cast<int>(blockIdx.x), hv = blockIdx.y;
-  const int cidx = CHK ? static_cast<int>(blockIdx.x) / ns : 0;
+  const int slice = static_cast<int>(blockIdx.x), hv = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int kh = hv / (d.Hv / d.Hk);
   const int j0 = slice * BV + cg * 4;
   const int i0 = rg * RPL;
   const int64_t hbase = ((b * d.Hv + hv) * D + i0) * D + j0;
-  const int64_t wg = CHK ? ((b * d.Hv + hv) * ns + slice) * a.NC + cidx : (b * d.Hv + hv) * ns + slice;
+  const int64_t wg = (b * d.Hv + hv) * ns + slice;
   float* ck = a.ckpt + wg * static_cast<int64_t>(nck) * D * BV;
   float* sc = a.scratch + wg * static_cast<int64_t>(kSeqSeg) * D * BV;
   auto lane_ptr = [&](float* base, int64_t idx, int m) {  // lane-private float4 slot
     return base + ((idx * RPL + m) * 64 + lane) * 4;
-  };
-  // chunk mode keeps the replayed states in fp16 (the chunk's entry state is
-  // already fp16): a lane-private 4-half slot in the same per-wave region
-  auto lane_ptr16 = [&](float* base, int64_t idx, int m) {
-    return reinterpret_cast<_Float16*>(base) + ((idx * RPL + m) * 64 + lane) * 4;
   };
 
   // sequence b: token rows tb .. tb + len - 1 (ragged: offsets cu, lengths
@@ -395,23 +361,13 @@ __global__ __launch_bounds__(64) void seq_bwd_kernel(Dims d, SeqBwdArgs a, int n
     slen = a.cu[b + 1] - tb;
     slen = slen < 0 ? 0 : (slen > d.T ? d.T : slen);
   }
-  int64_t t_beg = 0, t_end = slen;  // tokens of this workgroup
-  if constexpr (CHK) {
-    t_beg = static_cast<int64_t>(cidx) * a.C;
-    if (t_beg >= slen) return;  // past the end of a shorter sequence
-    t_end = t_beg + a.C < slen ? t_beg + a.C : slen;
-  }
+  const int64_t t_beg = 0, t_end = slen;  // tokens of this workgroup
   const int nckb = static_cast<int>((t_end - t_beg + kSeqSeg - 1) / kSeqSeg);
-  const int64_t cstate = ((b * d.Hv + hv) * a.NC + cidx) * static_cast<int64_t>(D * D);  // chunk mode
   float h[RPL][4];
-  if constexpr (CHK) {
-    load_state_frag<RPL>(a.hst + cstate, i0, j0, h);
-  } else {
 #pragma unroll
-    for (int m = 0; m < RPL; ++m) {
-      if (a.h0) ld4<float>(a.h0 + hbase + m * D, h[m]);
-      else h[m][0] = h[m][1] = h[m][2] = h[m][3] = 0.f;
-    }
+  for (int m = 0; m < RPL; ++m) {
+    if (a.h0) ld4<float>(a.h0 + hbase + m * D, h[m]);
+    else h[m][0] = h[m][1] = h[m][2] = h[m][3] = 0.f;
   }
   // phase 1: checkpoints at the start of every segment (the tokens of the
   // last segment need no forward pass here: phase 2 replays them)
@@ -429,14 +385,10 @@ __global__ __launch_bounds__(64) void seq_bwd_kernel(Dims d, SeqBwdArgs a, int n
 
   // phase 2: reverse
   float dH[RPL][4];
-  if constexpr (CHK) {
-    load_state_frag<RPL>(a.dhst + cstate, i0, j0, dH);
-  } else {
 #pragma unroll
-    for (int m = 0; m < RPL; ++m) {
-      if (a.dht) ld4<float>(a.dht + hbase + m * D, dH[m]);
-      else dH[m][0] = dH[m][1] = dH[m][2] = dH[m][3] = 0.f;
-    }
+  for (int m = 0; m < RPL; ++m) {
+    if (a.dht) ld4<float>(a.dht + hbase + m * D, dH[m]);
+    else dH[m][0] = dH[m][1] = dH[m][2] = dH[m][3] = 0.f;
   }
   for (int c = nckb - 1; c >= 0; --c) {
     const int64_t t0 = t_beg + static_cast<int64_t>(c) * kSeqSeg;
@@ -445,14 +397,7 @@ __global__ __launch_bounds__(64) void seq_bwd_kernel(Dims d, SeqBwdArgs a, int n
     for (int m = 0; m < RPL; ++m) ld4<float>(lane_ptr(ck, c, m), h[m]);
     for (int tau = 0; tau < len; ++tau) {
 #pragma unroll
-      for (int m = 0; m < RPL; ++m) {
-        if constexpr (CHK)
-          *reinterpret_cast<h16x4*>(lane_ptr16(sc, tau, m)) =
-              h16x4{static_cast<_Float16>(h[m][0]), static_cast<_Float16>(h[m][1]), static_cast<_Float16>(h[m][2]),
-                    static_cast<_Float16>(h[m][3])};
-        else
-          st4<float>(lane_ptr(sc, tau, m), h[m]);
-      }
+      for (int m = 0; m < RPL; ++m) st4<float>(lane_ptr(sc, tau, m), h[m]);
       Tok<RPL, CW> x;
       load_tok<D, L, TI, CW, false, false>(x, d, a.q, a.k, a.v, nullptr, a.g, a.beta, tb + t0 + tau, kh, hv, i0,
                                            j0);
@@ -467,13 +412,7 @@ __global__ __launch_bounds__(64) void seq_bwd_kernel(Dims d, SeqBwdArgs a, int n
 #pragma unroll
       for (int m = 0; m < RPL; ++m) {
         float hp[4];
-        if constexpr (CHK) {
-          const h16x4 v = *reinterpret_cast<const h16x4*>(lane_ptr16(sc, tau, m));
-          hp[0] = static_cast<float>(v[0]); hp[1] = static_cast<float>(v[1]);
-          hp[2] = static_cast<float>(v[2]); hp[3] = static_cast<float>(v[3]);
-        } else {
-          ld4<float>(lane_ptr(sc, tau, m), hp);
-        }
+        ld4<float>(lane_ptr(sc, tau, m), hp);
         const float am = alpha_of(x, m);
 #pragma unroll
         for (int e = 0; e < 4; ++e) Dm[m][e] = am * hp[e];
@@ -556,7 +495,7 @@ __global__ __launch_bounds__(64) void seq_bwd_kernel(Dims d, SeqBwdArgs a, int n
       }
     }
   }
-  if (!CHK && a.dh0) {
+  if (a.dh0) {
 #pragma unroll
     for (int m = 0; m < RPL; ++m) st4<float>(a.dh0 + hbase + m * D, dH[m]);
   }
@@ -794,23 +733,8 @@ hipError_t bwd_go(const Shape& s, const SeqBwdArgs& a, hipStream_t st) {
   const int nck = static_cast<int>((s.T + kSeqSeg - 1) / kSeqSeg);
   dim3 grid(D / BV, s.Hv, static_cast<unsigned>(s.B));
   ProfScope ps("seq_bwd", st);
-  hipLaunchKernelGGL((seq_bwd_kernel<D, BV, TI, TO, CW, false>), grid, dim3(64), 0, st, dims_of(s), a, nck, D / BV);
+  hipLaunchKernelGGL((seq_bwd_kernel<D, BV, TI, TO, CW>), grid, dim3(64), 0, st, dims_of(s), a, nck, D / BV);
   return hipGetLastError();
-}
-
-// Chunk mode: grid (slices x chunks, Hv, B); D = 128 only.
-template <int D, typename TI, typename TO, bool CW>
-hipError_t bwd_chunks_go(const Shape& s, const SeqBwdArgs& a, hipStream_t st) {
-  if constexpr (D != 128) {
-    return hipErrorInvalidValue;
-  } else {
-    constexpr int BV = bwd_bv<D>();
-    dim3 grid((D / BV) * a.NC, s.Hv, static_cast<unsigned>(s.B));
-    ProfScope ps("seq_bwd_chunks", st);
-    hipLaunchKernelGGL((seq_bwd_kernel<D, BV, TI, TO, CW, true>), grid, dim3(64), 0, st, dims_of(s), a,
-                       a.C / kSeqSeg, D / BV);
-    return hipGetLastError();
-  }
 }
 
 template <int D, typename TI, typename TO, bool CW>
@@ -853,11 +777,6 @@ template <int D, typename TI, typename TO, bool CW> struct FwdF {
 template <int D, typename TI, typename TO, bool CW> struct BwdF {
   static hipError_t run(const Shape& s, const SeqBwdArgs& a, hipStream_t st) { return bwd_go<D, TI, TO, CW>(s, a, st); }
 };
-template <int D, typename TI, typename TO, bool CW> struct BwdChunksF {
-  static hipError_t run(const Shape& s, const SeqBwdArgs& a, hipStream_t st) {
-    return bwd_chunks_go<D, TI, TO, CW>(s, a, st);
-  }
-};
 template <int D, typename TI, typename TO, bool CW> struct EpiF {
   static hipError_t run(const Shape& s, const EpiArgs& a, hipStream_t st) { return epi_go<D, TI, TO, CW>(s, a, st); }
 };
@@ -883,18 +802,6 @@ hipError_t launch_seq_bwd(const Shape& s, const SeqBwdArgs& a, hipStream_t st) {
 }
 hipError_t launch_bwd_epilogue(const Shape& s, const EpiArgs& a, hipStream_t st) {
   return dispatch<EpiF>(s, a, st);
-}
-
-size_t seq_bwd_chunk_ckpt_floats(const Shape& s, int C) {
-  const int64_t nc = (s.T + C - 1) / C;
-  return static_cast<size_t>(s.B * s.Hv * nc) * (C / kSeqSeg) * s.D * s.D;
-}
-size_t seq_bwd_chunk_scratch_floats(const Shape& s, int C) {
-  const int64_t nc = (s.T + C - 1) / C;
-  return static_cast<size_t>(s.B * s.Hv * nc) * kSeqSeg * s.D * s.D;
-}
-hipError_t launch_seq_bwd_chunks(const Shape& s, const SeqBwdArgs& a, hipStream_t st) {
-  return dispatch<BwdChunksF>(s, a, st);
 }
 
 }  // namespace gdr

@@ -48,6 +48,7 @@ KERNELS = [
     (r"cwchain16_kernel<\d+, [^,]+, true, false>", "chunk_fwd_cw"),
     (r"cwchain16_kernel<\d+, [^,]+, false, true>", "chunk_states_cw"),
     (r"cwdh16_kernel", "chunk_dh_cw"),
+    (r"cwgrad16_kernel", "chunk_grad_cw"),
     (r"prep16_kernel", "chunk_prep"),
     (r"chain16_kernel<\d+, [^,]+, true, false>", "chunk_fwd"),
     (r"chain16_kernel<\d+, [^,]+, true, true>", "chunk_fwd_save"),
@@ -55,7 +56,6 @@ KERNELS = [
     (r"dh16_kernel", "chunk_dh"),
     (r"grad16_kernel", "chunk_grad"),
     (r"epilogue128_kernel", "bwd_epilogue"),
-    (r"seq_bwd_kernel<[^>]*, true>", "seq_bwd_chunks"),
     (r"seq_bwd_kernel", "seq_bwd"),
     (r"seq_fwd_kernel", "seq_fwd"),
     (r"decode_kernel", "decode"),

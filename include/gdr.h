@@ -140,9 +140,10 @@ typedef struct gdr_problem {
 } gdr_problem;
 /* With GDR_CHANNELWISE, GDR_ALGO_CHUNKED is supported with bf16 io,
  * Dk = Dv = 128 and chunk_size 32 or 64 (else GDR_ERR_UNSUPPORTED); its VJP
- * runs the sequential VJP inside every chunk, all chunks in parallel, from
- * chunk states the chunk chains store.  AUTO picks the chunked kernels there
- * when T > 64. */
+ * forms each chunk's gradients from the chunk states the chunk chains store,
+ * the per-channel decay carried inside the chunk-local sums (matrix cores
+ * below the diagonal blocks, exact fp32 sums on them).  AUTO picks the
+ * chunked kernels there when T > 64. */
 
 /* *keeps = 1 when GDR_SAVE_CHUNKS takes effect for problem *p (whether or
  * not the flag is set in p->flags), i.e. when gdr_forward with the flag

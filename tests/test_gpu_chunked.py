@@ -293,8 +293,9 @@ def test_saved_chunks_match_stateless(T, C):
 @pytest.mark.parametrize("T,C", [(1, 64), (50, 64), (64, 64), (200, 64), (97, 32), (130, 32)])
 def test_channelwise_chunked_vjp(T, C):
     """Channelwise gates on the chunked VJP (chunk states from the chains,
-    the sequential VJP inside every chunk): ragged last chunk, GQA 2:4, h0
-    and dht nonzero, bf16 io, D=128."""
+    then every chunk's gradients with the per-channel decay inside the
+    chunk-local sums): ragged last chunk, GQA 2:4, h0 and dht nonzero, bf16
+    io, D=128."""
     x = make_inputs(1900 + T + C, 2, T, 2, 4, 128, 128, io_dtype="bf16", channelwise=True, h0_std=0.02)
     dht = (0.1 * np.random.default_rng(T + C).standard_normal((2, 4, 128, 128))).astype(np.float32)
     check_bwd(x, "bf16", cw=True, dht=dht, algo=("chunked", C))
