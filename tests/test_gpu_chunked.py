@@ -310,6 +310,22 @@ def test_channelwise_chunked_vjp_fused_gates_and_strong_decay():
     check_bwd(y, "bf16", cw=True, algo=("chunked", 64))
 
 
+@pytest.mark.parametrize("Hk,Hv,C,l2", [(1, 3, 64, True), (2, 8, 32, True), (1, 4, 64, False)])
+def test_channelwise_chunked_vjp_group_walk(Hk, Hv, C, l2):
+    """The channelwise gradient workgroup walks a k-head's v-heads in order
+    (GQA 1:3 and 1:4, both chunk sizes), summing dq_hat / dk_hat before the
+    L2-norm VJP, or with the norm flag off (then the rows of q and k are unit
+    vectors already, as in the forward tests); ragged last chunk, h0 and dht
+    nonzero."""
+    x = make_inputs(1970 + Hv + C, 2, 150, Hk, Hv, 128, 128, io_dtype="bf16", channelwise=True, h0_std=0.02)
+    if not l2:
+        for n in ("q", "k"):
+            u = x[n] / np.linalg.norm(x[n].astype(np.float64), axis=-1, keepdims=True)
+            x[n] = round_bf16(u.astype(np.float32))
+    dht = (0.1 * np.random.default_rng(Hv + C).standard_normal((2, Hv, 128, 128))).astype(np.float32)
+    check_bwd(x, "bf16", l2=l2, cw=True, dht=dht, algo=("chunked", C))
+
+
 def test_channelwise_chunked_vjp_prefill_t2048():
     """B=1, Hk=16, Hv=32, T=2048 (the channelwise prefill shape), sampled
     k-head groups against the oracle."""
