@@ -2284,8 +2284,9 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwdh16_kernel(K16 a) {
 //   factors <= 1: about the last row l of the column block for the row
 //   sums (k_s e^{G_l - G_s}, then e^{G_r - G_l}), about the first row b of
 //   the row block for the column sums (q_r e^{G_r - G_b}, then
-//   e^{G_b - G_s}).  Diagonal blocks are summed exactly in fp32 with one
-//   exponential per pair (arguments clamped at 0 where the mask is zero).
+//   e^{G_b - G_s}).  Diagonal blocks are summed in fp32 with W split about
+//   their first row o (e^{G_r - G_o} e^{G_o - G_s}) when the chunk's gates
+//   keep every such factor within 2^96, else with one exponential per pair.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ f32x4 mma16x16x16(f16x4 a, f16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
@@ -2526,7 +2527,7 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
                       reinterpret_cast<char*>(Hs), tid, w);
     constexpr int RQ = C / 4;  // rows per quarter; thread -> channel tid % DK, quarter tid / DK
     const int gch = tid & (DK - 1), gq = tid >> 7;
-    float grun[RQ];
+    float grun[RQ], gspan = 0.f;
     {
       const float* gp = a.g + ((sp.t0 + t0 + gq * RQ) * a.Hv + hv) * DK + gch;
       const int64_t rs = static_cast<int64_t>(a.Hv) * DK;
@@ -2536,9 +2537,11 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
         float gj = 0.f;
         if (gq * RQ + j < L) gj = a.fg ? fg_log_alpha(gp[j * rs]) : gp[j * rs];
         run += gj;
+        gspan += fabsf(gj);
         grun[j] = run;
       }
       sQ[gq][gch] = run;
+      gspan *= kLog2e;  // bound on the span of G over this quarter of the rows, log2 units
     }
     // C x C stage, part 1: dT transposed, dP masked (and transposed)
     if (qact) {
@@ -2557,7 +2560,11 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
         *reinterpret_cast<f16x4*>(dPmT + s2 * LDC + 16 * qr + 4 * g) = p4;
       }
     }
-    __syncthreads();
+    // The diagonal blocks split W about their first row o when every factor
+    // e^{G_o - G_s} of the chunk stays within 2^96 (a quarter of the rows is
+    // at most one 16-row block); else one exponential per pair.
+    constexpr float kSpan = 96.f;
+    const bool exact = __syncthreads_or(gspan > kSpan * RQ / 16);
     {
       float base = 0.f;
       for (int q2 = 0; q2 < gq; ++q2) base += sQ[q2][gch];
@@ -2647,6 +2654,40 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
         }
       }
     }
+    if (!exact) {
+#pragma unroll
+      for (int R = 0; R < NT; ++R) {  // diagonal blocks about their first row o: W = e^{G_r - G_o} e^{G_o - G_s}
+        const float g2o = G2T[i2 * LDG + 16 * R];
+        float ar[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ar[e] = __builtin_amdgcn_exp2f(G2r[R][e] - g2o);
+        float sp4[4] = {0.f, 0.f, 0.f, 0.f}, sa4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+        for (int sq = 0; sq < 4; ++sq) {
+          const f16x4 kq = tr4(Ks, LDK, 16 * R + 4 * sq, 16 * w);
+          const f32x4 g2s = *reinterpret_cast<const f32x4*>(G2T + i2 * LDG + 16 * R + 4 * sq);
+          float kb[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kb[i] = static_cast<float>(kq[i]) * __builtin_amdgcn_exp2f(g2o - g2s[i]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * R + 4 * g + e;
+            const f16x4 pq = *reinterpret_cast<const f16x4*>(dPm + r * LDC + 16 * R + 4 * sq);
+            const f16x4 aq = *reinterpret_cast<const f16x4*>(dAm + r * LDC + 16 * R + 4 * sq);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              sp4[e] += static_cast<float>(pq[i]) * kb[i];
+              sa4[e] += static_cast<float>(aq[i]) * kb[i];
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dq[R][e] += ar[e] * sp4[e];
+          ta[R][e] += ar[e] * sa4[e];
+        }
+      }
+    } else {
 #pragma unroll
     for (int R = 0; R < NT; ++R) {  // diagonal blocks, one exponential per pair
 #pragma unroll 1
@@ -2660,27 +2701,23 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
           const f16x4 aq = *reinterpret_cast<const f16x4*>(dAm + r * LDC + 16 * R + 4 * sq);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float wk =
-                static_cast<float>(kq[i]) * __builtin_amdgcn_exp2f(fminf(G2r[R][e] - g2s[i], 0.f));
+            const float wk = 4 * sq + i <= 4 * g + e
+                                 ? static_cast<float>(kq[i]) * __builtin_amdgcn_exp2f(G2r[R][e] - g2s[i])
+                                 : 0.f;
             dq[R][e] += static_cast<float>(pq[i]) * wk;
             ta[R][e] += static_cast<float>(aq[i]) * wk;
           }
         }
       }
     }
+    }
     // ---- the last row's sum_r k_r o (e^{G_C - G_r} X3_r), before the column sums join dk-
     float kl3 = 0.f;
-    float qn[NT][4], kn[NT][4];
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
-      const f16x4 q4 = tr4(Qs, LDK, 16 * rt + 4 * g, 16 * w);
       const f16x4 k4 = tr4(Ks, LDK, 16 * rt + 4 * g, 16 * w);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qn[rt][e] = static_cast<float>(q4[e]);
-        kn[rt][e] = static_cast<float>(k4[e]);
-        kl3 += kn[rt][e] * dkm[rt][e];
-      }
+      for (int e = 0; e < 4; ++e) kl3 += static_cast<float>(k4[e]) * dkm[rt][e];
     }
     kl3 = xsum<16, 64>(kl3);
     // ---- column sums: dk- += sum_{r>=s} dP_rs W_rs q_r + sum_{r>s} dA_rs beta_r W_rs k_r
@@ -2708,6 +2745,39 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
         for (int e = 0; e < 4; ++e) dkm[S][e] += __builtin_amdgcn_exp2f(g2b - G2r[S][e]) * tp[e];
       }
     }
+    if (!exact) {
+#pragma unroll
+      for (int R = 0; R < NT; ++R) {  // diagonal blocks about their first row o
+        const float g2o = G2T[i2 * LDG + 16 * R];
+        float bs[4], acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bs[e] = __builtin_amdgcn_exp2f(g2o - G2r[R][e]);
+#pragma unroll 1
+        for (int rq = 0; rq < 4; ++rq) {
+          const f16x4 q4 = tr4(Qs, LDK, 16 * R + 4 * rq, 16 * w);
+          const f16x4 k4 = tr4(Ks, LDK, 16 * R + 4 * rq, 16 * w);
+          const f32x4 g2v = *reinterpret_cast<const f32x4*>(G2T + i2 * LDG + 16 * R + 4 * rq);
+          const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * R + 4 * rq);
+          float qa[4], ka[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float f = __builtin_amdgcn_exp2f(g2v[i] - g2o);
+            qa[i] = static_cast<float>(q4[i]) * f;
+            ka[i] = bv[i] * static_cast<float>(k4[i]) * f;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int s = 16 * R + 4 * g + e;
+            const f16x4 pq = *reinterpret_cast<const f16x4*>(dPmT + s * LDC + 16 * R + 4 * rq);
+            const f16x4 aq = *reinterpret_cast<const f16x4*>(dAmT + s * LDC + 16 * R + 4 * rq);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[e] += static_cast<float>(pq[i]) * qa[i] + static_cast<float>(aq[i]) * ka[i];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dkm[R][e] += bs[e] * acc[e];
+      }
+    } else {
 #pragma unroll
     for (int R = 0; R < NT; ++R) {  // diagonal blocks, one exponential per pair
 #pragma unroll 1
@@ -2723,12 +2793,13 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
           const f16x4 aq = *reinterpret_cast<const f16x4*>(dAmT + s * LDC + 16 * R + 4 * rq);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float f = __builtin_amdgcn_exp2f(fminf(g2v[i] - G2r[R][e], 0.f));
+            const float f = 4 * rq + i >= 4 * g + e ? __builtin_amdgcn_exp2f(g2v[i] - G2r[R][e]) : 0.f;
             dkm[R][e] += f * (static_cast<float>(pq[i]) * static_cast<float>(q4[i]) +
                               static_cast<float>(aq[i]) * bv[i] * static_cast<float>(k4[i]));
           }
         }
       }
+    }
     }
 
     // ---- dk, dG, dg, dbeta of this v-head
@@ -2736,13 +2807,16 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
       const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * rt + 4 * g);
+      const f16x4 q4 = tr4(Qs, LDK, 16 * rt + 4 * g, 16 * w);
+      const f16x4 k4 = tr4(Ks, LDK, 16 * rt + 4 * g, 16 * w);
       f32x4 rb;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rt + 4 * g + e;
-        rb[e] = row16_sum(kn[rt][e] * ta[rt][e]);
+        const float qn = static_cast<float>(q4[e]), kn = static_cast<float>(k4[e]);
+        rb[e] = row16_sum(kn * ta[rt][e]);
         dkp[rt][e] += bv[e] * ta[rt][e];
-        float x = qn[rt][e] * dq[rt][e] + kn[rt][e] * (dkp[rt][e] - dkm[rt][e]);
+        float x = qn * dq[rt][e] + kn * (dkp[rt][e] - dkm[rt][e]);
         if (r == L - 1) x += kl3 + eGC[i2] * hd;
         dG[rt][e] = r < L ? x : 0.f;
         dqv[rt][e] += dq[rt][e];
