@@ -2656,35 +2656,25 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
     }
     if (!exact) {
 #pragma unroll
-      for (int R = 0; R < NT; ++R) {  // diagonal blocks about their first row o: W = e^{G_r - G_o} e^{G_o - G_s}
+      for (int R = 0; R < NT; ++R) {  // diagonal blocks about their first row o: W = e^{G_r - G_o} e^{G_o - G_s},
+        // the second factor (up to 2^96) inside fp32 matrix-core products; product kk
+        // of lane group g sums over s = 16R + 4g + kk, the rows this lane holds
         const float g2o = G2T[i2 * LDG + 16 * R];
-        float ar[4];
+        const f16x4 kq = tr4(Ks, LDK, 16 * R + 4 * g, 16 * w);
+        const f16x4 ap = *reinterpret_cast<const f16x4*>(dPm + (16 * R + c16) * LDC + 16 * R + 4 * g);
+        const f16x4 aa = *reinterpret_cast<const f16x4*>(dAm + (16 * R + c16) * LDC + 16 * R + 4 * g);
+        f32x4 tp = zero4(), tq = zero4();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ar[e] = __builtin_amdgcn_exp2f(G2r[R][e] - g2o);
-        float sp4[4] = {0.f, 0.f, 0.f, 0.f}, sa4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-        for (int sq = 0; sq < 4; ++sq) {
-          const f16x4 kq = tr4(Ks, LDK, 16 * R + 4 * sq, 16 * w);
-          const f32x4 g2s = *reinterpret_cast<const f32x4*>(G2T + i2 * LDG + 16 * R + 4 * sq);
-          float kb[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) kb[i] = static_cast<float>(kq[i]) * __builtin_amdgcn_exp2f(g2o - g2s[i]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * R + 4 * g + e;
-            const f16x4 pq = *reinterpret_cast<const f16x4*>(dPm + r * LDC + 16 * R + 4 * sq);
-            const f16x4 aq = *reinterpret_cast<const f16x4*>(dAm + r * LDC + 16 * R + 4 * sq);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              sp4[e] += static_cast<float>(pq[i]) * kb[i];
-              sa4[e] += static_cast<float>(aq[i]) * kb[i];
-            }
-          }
+        for (int kk = 0; kk < 4; ++kk) {
+          const float kb = static_cast<float>(kq[kk]) * __builtin_amdgcn_exp2f(g2o - G2r[R][kk]);
+          tp = F32Op::mma(static_cast<float>(ap[kk]), kb, tp);
+          tq = F32Op::mma(static_cast<float>(aa[kk]), kb, tq);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          dq[R][e] += ar[e] * sp4[e];
-          ta[R][e] += ar[e] * sa4[e];
+          const float ar = __builtin_amdgcn_exp2f(G2r[R][e] - g2o);
+          dq[R][e] += ar * tp[e];
+          ta[R][e] += ar * tq[e];
         }
       }
     } else {
@@ -2747,35 +2737,23 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
     }
     if (!exact) {
 #pragma unroll
-      for (int R = 0; R < NT; ++R) {  // diagonal blocks about their first row o
+      for (int R = 0; R < NT; ++R) {  // diagonal blocks about their first row o, as fp32 products over
+        // r = 16R + 4g + kk with e^{G_r - G_o} on the right operand, e^{G_o - G_s} after
         const float g2o = G2T[i2 * LDG + 16 * R];
-        float bs[4], acc[4] = {0.f, 0.f, 0.f, 0.f};
+        const f16x4 q4 = tr4(Qs, LDK, 16 * R + 4 * g, 16 * w);
+        const f16x4 k4 = tr4(Ks, LDK, 16 * R + 4 * g, 16 * w);
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * R + 4 * g);
+        const f16x4 ap = *reinterpret_cast<const f16x4*>(dPmT + (16 * R + c16) * LDC + 16 * R + 4 * g);
+        const f16x4 aa = *reinterpret_cast<const f16x4*>(dAmT + (16 * R + c16) * LDC + 16 * R + 4 * g);
+        f32x4 acc = zero4();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bs[e] = __builtin_amdgcn_exp2f(g2o - G2r[R][e]);
-#pragma unroll 1
-        for (int rq = 0; rq < 4; ++rq) {
-          const f16x4 q4 = tr4(Qs, LDK, 16 * R + 4 * rq, 16 * w);
-          const f16x4 k4 = tr4(Ks, LDK, 16 * R + 4 * rq, 16 * w);
-          const f32x4 g2v = *reinterpret_cast<const f32x4*>(G2T + i2 * LDG + 16 * R + 4 * rq);
-          const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * R + 4 * rq);
-          float qa[4], ka[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float f = __builtin_amdgcn_exp2f(g2v[i] - g2o);
-            qa[i] = static_cast<float>(q4[i]) * f;
-            ka[i] = bv[i] * static_cast<float>(k4[i]) * f;
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int s = 16 * R + 4 * g + e;
-            const f16x4 pq = *reinterpret_cast<const f16x4*>(dPmT + s * LDC + 16 * R + 4 * rq);
-            const f16x4 aq = *reinterpret_cast<const f16x4*>(dAmT + s * LDC + 16 * R + 4 * rq);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[e] += static_cast<float>(pq[i]) * qa[i] + static_cast<float>(aq[i]) * ka[i];
-          }
+        for (int kk = 0; kk < 4; ++kk) {
+          const float f = __builtin_amdgcn_exp2f(G2r[R][kk] - g2o);
+          acc = F32Op::mma(static_cast<float>(ap[kk]), static_cast<float>(q4[kk]) * f, acc);
+          acc = F32Op::mma(static_cast<float>(aa[kk]), bv[kk] * static_cast<float>(k4[kk]) * f, acc);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dkm[R][e] += bs[e] * acc[e];
+        for (int e = 0; e < 4; ++e) dkm[R][e] += __builtin_amdgcn_exp2f(g2o - G2r[R][e]) * acc[e];
       }
     } else {
 #pragma unroll
