@@ -200,17 +200,29 @@ __device__ __forceinline__ void chain_frags(f16x8 (&bf)[NT / 2], const f32x4 (&x
                    static_cast<_Float16>(x[2 * kb + 1][2]), static_cast<_Float16>(x[2 * kb + 1][3])};
 }
 
+// Zero pattern of a square C x C operand by 16-row blocks: products of
+// row tile t with the k-block pair kb (columns 32kb .. 32kb + 31) that only
+// meet zero blocks are skipped.  kLower: A is zero above its diagonal blocks
+// (T, P, the masked dP); kUpper: zero below them (their transposes).
+enum Tri { kFull = 0, kLower = 1, kUpper = 2 };
+template <int TRI>
+__device__ __forceinline__ constexpr bool tri_skip(int t, int kb) {
+  return (TRI == kLower && 2 * kb > t) || (TRI == kUpper && 2 * kb + 1 < t);
+}
+
 // acc[t] += A[16t : 16t+16, 0 : 16 NT] X for t < NO, X chained as bf.
-template <int NO, int NT>
+template <int NO, int NT, int TRI = kFull>
 __device__ __forceinline__ void mma_chain_rows(f32x4 (&acc)[NO], const _Float16* A, int ld, const f16x8 (&bf)[NT / 2]) {
   const int m = lane_id() & 15;
 #pragma unroll
   for (int kb = 0; kb < NT / 2; ++kb) {
     f16x8 af[NO];
 #pragma unroll
-    for (int t = 0; t < NO; ++t) af[t] = perm_frag(A, ld, 16 * t + m, kb);
+    for (int t = 0; t < NO; ++t)
+      if (!tri_skip<TRI>(t, kb)) af[t] = perm_frag(A, ld, 16 * t + m, kb);
 #pragma unroll
-    for (int t = 0; t < NO; ++t) acc[t] = F16Op::mma(af[t], bf[kb], acc[t]);
+    for (int t = 0; t < NO; ++t)
+      if (!tri_skip<TRI>(t, kb)) acc[t] = F16Op::mma(af[t], bf[kb], acc[t]);
   }
 }
 
@@ -232,17 +244,19 @@ __device__ __forceinline__ void mma_chain_rows2(f32x4 (&acc1)[NO], f32x4 (&acc2)
   }
 }
 
-// mma_chain_rows with A = M^T, M row-major [16 NT][ld].
-template <int NO, int NT>
+// mma_chain_rows with A = M^T, M row-major [16 NT][ld] (TRI describes A).
+template <int NO, int NT, int TRI = kFull>
 __device__ __forceinline__ void mma_chain_rows_t(f32x4 (&acc)[NO], const _Float16* M, int ld,
                                                  const f16x8 (&bf)[NT / 2]) {
 #pragma unroll
   for (int kb = 0; kb < NT / 2; ++kb) {
     f16x8 af[NO];
 #pragma unroll
-    for (int t = 0; t < NO; ++t) af[t] = perm_frag_t(M, ld, 16 * t, kb);
+    for (int t = 0; t < NO; ++t)
+      if (!tri_skip<TRI>(t, kb)) af[t] = perm_frag_t(M, ld, 16 * t, kb);
 #pragma unroll
-    for (int t = 0; t < NO; ++t) acc[t] = F16Op::mma(af[t], bf[kb], acc[t]);
+    for (int t = 0; t < NO; ++t)
+      if (!tri_skip<TRI>(t, kb)) acc[t] = F16Op::mma(af[t], bf[kb], acc[t]);
   }
 }
 
@@ -828,10 +842,10 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void chain16_kernel(K16 a) {
     }
     f16x8 bf[NT / 2];
     chain_frags<NT>(bf, rhs);
-    mma_chain_rows<NT, NT>(u, Tm, LDC, bf);
+    mma_chain_rows<NT, NT, kLower>(u, Tm, LDC, bf);
     if constexpr (WRITE_O) {
       chain_frags<NT>(bf, u);
-      mma_chain_rows<NT, NT>(o, Pm, LDC, bf);
+      mma_chain_rows<NT, NT, kLower>(o, Pm, LDC, bf);
     }
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr) {
@@ -978,9 +992,9 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
     }
     f16x8 bf[NT / 2];
     chain_frags<NT>(bf, dof);
-    mma_chain_rows_t<NT, NT>(du, Pm, LDC, bf);
+    mma_chain_rows_t<NT, NT, kUpper>(du, Pm, LDC, bf);
     chain_frags<NT>(bf, du);
-    mma_chain_rows_t<NT, NT>(dr, Tm, LDC, bf);
+    mma_chain_rows_t<NT, NT, kUpper>(dr, Tm, LDC, bf);
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr) {
       const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
@@ -1040,7 +1054,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
 // ---------------------------------------------------------------------------
 // acc[t] += A[16t : 16t+16, 0:K] Bm[0:K, n0 : n0+16], Bm row-major; the B
 // fragment is shared.
-template <int NO, int K>
+template <int NO, int K, int TRI = kFull>
 __device__ __forceinline__ void mma_rows(f32x4 (&acc)[NO], const _Float16* A, int lda, const _Float16* Bm, int ldb,
                                          int n0) {
   const int r = lane_id() & 15, kl = (lane_id() >> 4) * 8;
@@ -1049,9 +1063,11 @@ __device__ __forceinline__ void mma_rows(f32x4 (&acc)[NO], const _Float16* A, in
     const f16x8 bfr = frag_t(Bm, ldb, k0, n0);
     f16x8 af[NO];
 #pragma unroll
-    for (int t = 0; t < NO; ++t) af[t] = ld8(A + (16 * t + r) * lda + k0 + kl);
+    for (int t = 0; t < NO; ++t)
+      if (!tri_skip<TRI>(t, k0 / 32)) af[t] = ld8(A + (16 * t + r) * lda + k0 + kl);
 #pragma unroll
-    for (int t = 0; t < NO; ++t) acc[t] = F16Op::mma(af[t], bfr, acc[t]);
+    for (int t = 0; t < NO; ++t)
+      if (!tri_skip<TRI>(t, k0 / 32)) acc[t] = F16Op::mma(af[t], bfr, acc[t]);
   }
 }
 
@@ -1241,11 +1257,11 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     }
     f16x8 bf[NT / 2];
     chain_frags<NT>(bf, rhs);
-    mma_chain_rows<NT, NT>(u, Ts, LDC, bf);
+    mma_chain_rows<NT, NT, kLower>(u, Ts, LDC, bf);
     chain_frags<NT>(bf, dov);
-    mma_chain_rows_t<NT, NT>(du, Ps, LDC, bf);
+    mma_chain_rows_t<NT, NT, kUpper>(du, Ps, LDC, bf);
     chain_frags<NT>(bf, du);
-    mma_chain_rows_t<NT, NT>(dr, Ts, LDC, bf);
+    mma_chain_rows_t<NT, NT, kUpper>(dr, Ts, LDC, bf);
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr)
 #pragma unroll
@@ -1424,8 +1440,8 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     f32x4 dq[NT], dk[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) dq[t] = dk[t] = zero4();
-    mma_rows<NT, C>(dq, dPm, LDC, Ks, LDK, 16 * w);
-    mma_rows<NT, C>(dk, dPmT, LDC, Qs, LDK, 16 * w);
+    mma_rows<NT, C, kLower>(dq, dPm, LDC, Ks, LDK, 16 * w);
+    mma_rows<NT, C, kUpper>(dk, dPmT, LDC, Qs, LDK, 16 * w);
     mma_rows<NT, C>(dk, dAs, LDC, Ks, LDK, 16 * w);
     float gcx = 0.f;
 #pragma unroll
@@ -2095,9 +2111,9 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
     }
     f16x8 bf[NT / 2];
     chain_frags<NT>(bf, rhs);
-    mma_chain_rows<NT, NT>(u, Tm, LDC, bf);
+    mma_chain_rows<NT, NT, kLower>(u, Tm, LDC, bf);
     chain_frags<NT>(bf, u);
-    if constexpr (WRITE_O) mma_chain_rows<NT, NT>(o, Pm, LDC, bf);
+    if constexpr (WRITE_O) mma_chain_rows<NT, NT, kLower>(o, Pm, LDC, bf);
 #pragma unroll
     for (int ti = 0; ti < NTK; ++ti) {
       const f32x4 dec = *reinterpret_cast<const f32x4*>(gC + 16 * ti + 4 * g);
@@ -2221,9 +2237,9 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwdh16_kernel(K16 a) {
     }
     f16x8 bf[NT / 2], bo[NT / 2];
     chain_frags<NT>(bo, dof);
-    mma_chain_rows_t<NT, NT>(du, Pm, LDC, bo);
+    mma_chain_rows_t<NT, NT, kUpper>(du, Pm, LDC, bo);
     chain_frags<NT>(bf, du);
-    mma_chain_rows_t<NT, NT>(dr, Tm, LDC, bf);
+    mma_chain_rows_t<NT, NT, kUpper>(dr, Tm, LDC, bf);
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr) {
       const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
@@ -2429,11 +2445,11 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
     }
     f16x8 bf[NT / 2];
     chain_frags<NT>(bf, rhs);
-    mma_chain_rows<NT, NT>(u, Ts, LDC, bf);
+    mma_chain_rows<NT, NT, kLower>(u, Ts, LDC, bf);
     chain_frags<NT>(bf, dov);
-    mma_chain_rows_t<NT, NT>(du, Ps, LDC, bf);
+    mma_chain_rows_t<NT, NT, kUpper>(du, Ps, LDC, bf);
     chain_frags<NT>(bf, du);
-    mma_chain_rows_t<NT, NT>(dr, Ts, LDC, bf);
+    mma_chain_rows_t<NT, NT, kUpper>(dr, Ts, LDC, bf);
     {  // dv = beta dRHS; rows past the sequence's end are dropped by the buffer extent
       const uint32_t rowo = static_cast<uint32_t>(a.Hv) * DK * sizeof(TO);
       const rsrc_t ovr = make_rsrc(static_cast<char*>(a.dv) + (sp.t0 + t0) * rowo, static_cast<uint32_t>(L) * rowo);
