@@ -177,6 +177,43 @@ __device__ __forceinline__ f16x8 frag_t(const _Float16* M, int ld, int k0, int n
   return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Key-ordered tiles.  The key images store each row's columns in the order
+// the chained fragments consume them: 16-byte unit 4kb + g of a row holds
+// the columns 32kb + 4g .. +3 and 32kb + 16 + 4g .. +3 (the row pad, unit
+// DK / 8, is unchanged).  An A fragment of a chained product is then one
+// 16-byte read (plain 8-byte pairs read at half the rate), and a transposed
+// read names its four columns from the unit order.
+__device__ __forceinline__ f16x8 key_unit(const _Float16* row, int u) {  // unit u < DK / 8 of a natural row
+  const int kb = u >> 2, g = u & 3;
+  const f16x4 lo = *reinterpret_cast<const f16x4*>(row + 32 * kb + 4 * g);
+  const f16x4 hi = *reinterpret_cast<const f16x4*>(row + 32 * kb + 16 + 4 * g);
+  return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// perm_frag of a key-ordered A.
+__device__ __forceinline__ f16x8 kfrag(const _Float16* A, int ld, int m, int kb) {
+  return ld8(A + m * ld + 32 * kb + 8 * (lane_id() >> 4));
+}
+// tr4 of a key-ordered M (n0 a multiple of 16): lane p of the group names
+// the unit half holding natural columns n0 + 4(p % 4) .. +3, so it receives
+// natural column n0 + p of rows k0 .. k0 + 3, as tr4 does on a natural M.
+__device__ __forceinline__ f16x4 tr4k(const _Float16* M, int ld, int k0, int n0) {
+  const int p = lane_id() & 15;
+  const _Float16* src = M + (k0 + (p >> 2)) * ld + (n0 & ~31) + 8 * (p & 3) + 4 * ((n0 >> 4) & 1);
+  return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src));
+}
+__device__ __forceinline__ f16x8 perm_frag_tk(const _Float16* M, int ld, int m0, int kb) {
+  const int g = lane_id() >> 4;
+  const f16x4 lo = tr4k(M, ld, 32 * kb + 4 * g, m0);
+  const f16x4 hi = tr4k(M, ld, 32 * kb + 16 + 4 * g, m0);
+  return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ f16x8 frag_tk(const _Float16* M, int ld, int k0, int n0) {
+  const int g = lane_id() >> 4;
+  const f16x4 lo = tr4k(M, ld, k0 + 8 * g, n0);
+  const f16x4 hi = tr4k(M, ld, k0 + 8 * g + 4, n0);
+  return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 // Four bf16 values carried as the 16-bit halves of a transpose-read result,
 // widened to fp32.  The halves are taken from the two 32-bit words: a
 // bit_cast of a single vector element would read the vector's first element.
@@ -211,7 +248,7 @@ __device__ __forceinline__ constexpr bool tri_skip(int t, int kb) {
 }
 
 // acc[t] += A[16t : 16t+16, 0 : 16 NT] X for t < NO, X chained as bf.
-template <int NO, int NT, int TRI = kFull>
+template <int NO, int NT, int TRI = kFull, bool KP = false>
 __device__ __forceinline__ void mma_chain_rows(f32x4 (&acc)[NO], const _Float16* A, int ld, const f16x8 (&bf)[NT / 2]) {
   const int m = lane_id() & 15;
 #pragma unroll
@@ -219,7 +256,7 @@ __device__ __forceinline__ void mma_chain_rows(f32x4 (&acc)[NO], const _Float16*
     f16x8 af[NO];
 #pragma unroll
     for (int t = 0; t < NO; ++t)
-      if (!tri_skip<TRI>(t, kb)) af[t] = perm_frag(A, ld, 16 * t + m, kb);
+      if (!tri_skip<TRI>(t, kb)) af[t] = KP ? kfrag(A, ld, 16 * t + m, kb) : perm_frag(A, ld, 16 * t + m, kb);
 #pragma unroll
     for (int t = 0; t < NO; ++t)
       if (!tri_skip<TRI>(t, kb)) acc[t] = F16Op::mma(af[t], bf[kb], acc[t]);
@@ -227,7 +264,7 @@ __device__ __forceinline__ void mma_chain_rows(f32x4 (&acc)[NO], const _Float16*
 }
 
 // mma_chain_rows for two chained operands sharing A: acc1 += A X1, acc2 += A X2.
-template <int NO, int NT>
+template <int NO, int NT, bool KP = false>
 __device__ __forceinline__ void mma_chain_rows2(f32x4 (&acc1)[NO], f32x4 (&acc2)[NO], const _Float16* A, int ld,
                                                 const f16x8 (&bf1)[NT / 2], const f16x8 (&bf2)[NT / 2]) {
   const int m = lane_id() & 15;
@@ -235,7 +272,7 @@ __device__ __forceinline__ void mma_chain_rows2(f32x4 (&acc1)[NO], f32x4 (&acc2)
   for (int kb = 0; kb < NT / 2; ++kb) {
     f16x8 af[NO];
 #pragma unroll
-    for (int t = 0; t < NO; ++t) af[t] = perm_frag(A, ld, 16 * t + m, kb);
+    for (int t = 0; t < NO; ++t) af[t] = KP ? kfrag(A, ld, 16 * t + m, kb) : perm_frag(A, ld, 16 * t + m, kb);
 #pragma unroll
     for (int t = 0; t < NO; ++t) {
       acc1[t] = F16Op::mma(af[t], bf1[kb], acc1[t]);
@@ -244,8 +281,8 @@ __device__ __forceinline__ void mma_chain_rows2(f32x4 (&acc1)[NO], f32x4 (&acc2)
   }
 }
 
-// mma_chain_rows with A = M^T, M row-major [16 NT][ld] (TRI describes A).
-template <int NO, int NT, int TRI = kFull>
+// mma_chain_rows with A = M^T, M row-major [16 NT][ld] (TRI describes A; KP: M key-ordered).
+template <int NO, int NT, int TRI = kFull, bool KP = false>
 __device__ __forceinline__ void mma_chain_rows_t(f32x4 (&acc)[NO], const _Float16* M, int ld,
                                                  const f16x8 (&bf)[NT / 2]) {
 #pragma unroll
@@ -253,7 +290,7 @@ __device__ __forceinline__ void mma_chain_rows_t(f32x4 (&acc)[NO], const _Float1
     f16x8 af[NO];
 #pragma unroll
     for (int t = 0; t < NO; ++t)
-      if (!tri_skip<TRI>(t, kb)) af[t] = perm_frag_t(M, ld, 16 * t, kb);
+      if (!tri_skip<TRI>(t, kb)) af[t] = KP ? perm_frag_tk(M, ld, 16 * t, kb) : perm_frag_t(M, ld, 16 * t, kb);
 #pragma unroll
     for (int t = 0; t < NO; ++t)
       if (!tri_skip<TRI>(t, kb)) acc[t] = F16Op::mma(af[t], bf[kb], acc[t]);
@@ -530,8 +567,8 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
   constexpr int UK = DK / 8 + 1;  // 16-byte units per [*][LDK] row
   if (hv % grp == 0) {
     char* kim = a.kimg + ((b * a.Hk + kh) * a.NC + c) * static_cast<int64_t>(IM::KEY);
-    write_tile<C, UK, NTH, true>(kim, [&](int r, int u) { return ld8(Ks + r * LDK + 8 * u); });
-    write_tile<C, UK, NTH, true>(kim + IM::KN, [&](int r, int u) { return ld8(Qs + r * LDK + 8 * u); });
+    write_tile<C, UK, NTH, true>(kim, [&](int r, int u) { return u < DK / 8 ? key_unit(Ks + r * LDK, u) : ld8(Ks + r * LDK + 8 * u); });
+    write_tile<C, UK, NTH, true>(kim + IM::KN, [&](int r, int u) { return u < DK / 8 ? key_unit(Qs + r * LDK, u) : ld8(Qs + r * LDK + 8 * u); });
   }
   __syncthreads();
   // A from registers into the Kn space (only its lower tiles are read)
@@ -815,11 +852,11 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void chain16_kernel(K16 a) {
     f32x4 y[NT], u[NT], o[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) y[t] = u[t] = zero4();
-    mma_chain_rows<NT, NTK>(y, Kn, LDK, hf);
+    mma_chain_rows<NT, NTK, kFull, true>(y, Kn, LDK, hf);
     if constexpr (WRITE_O) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) o[t] = zero4();
-      mma_chain_rows<NT, NTK>(o, Qn, LDK, hf);
+      mma_chain_rows<NT, NTK, kFull, true>(o, Qn, LDK, hf);
     }
     if constexpr (STORE_H) {  // entry state of chunk c
       const rsrc_t hr = make_rsrc(a.hst + ((p.b * a.Hv + p.hv) * a.NC + c) * static_cast<int64_t>(DK * DK), DK * DK * 2);
@@ -857,7 +894,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void chain16_kernel(K16 a) {
     const float gc = gam[rows_of(c) - 1];
 #pragma unroll
     for (int ti = 0; ti < NTK; ++ti) h[ti] = h[ti] * gc;
-    mma_chain_rows_t<NTK, NT>(h, Kn, LDK, bf);
+    mma_chain_rows_t<NTK, NT, kFull, true>(h, Kn, LDK, bf);
     if constexpr (WRITE_O) put_strip<TO, NT>(os, 16 * w + c16, o);
     lds_barrier();
   };
@@ -969,7 +1006,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
     f32x4 du[NT], dr[NT], dvv[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) du[t] = dr[t] = zero4();
-    mma_chain_rows<NT, NTK>(du, Kn, LDK, hf);
+    mma_chain_rows<NT, NTK, kFull, true>(du, Kn, LDK, hf);
     {  // gradient at this chunk's end
       const rsrc_t hr = make_rsrc(a.dhst + ((p.b * a.Hv + p.hv) * a.NC + c) * static_cast<int64_t>(DK * DK), DK * DK * 2);
 #pragma unroll
@@ -1010,9 +1047,9 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
 #pragma unroll
     for (int ti = 0; ti < NTK; ++ti) dh[ti] = dh[ti] * gc;
     chain_frags<NT>(bf, gdo);
-    mma_chain_rows_t<NTK, NT>(dh, Qn, LDK, bf);
+    mma_chain_rows_t<NTK, NT, kFull, true>(dh, Qn, LDK, bf);
     chain_frags<NT>(bf, dr);
-    mma_chain_rows_t<NTK, NT>(dh, Kn, LDK, bf);
+    mma_chain_rows_t<NTK, NT, kFull, true>(dh, Kn, LDK, bf);
     lds_barrier();
   };
   // chunks NC-1, NC-2, ... alternate between the two buffers
@@ -1054,13 +1091,13 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
 // ---------------------------------------------------------------------------
 // acc[t] += A[16t : 16t+16, 0:K] Bm[0:K, n0 : n0+16], Bm row-major; the B
 // fragment is shared.
-template <int NO, int K, int TRI = kFull>
+template <int NO, int K, int TRI = kFull, bool KP = false>
 __device__ __forceinline__ void mma_rows(f32x4 (&acc)[NO], const _Float16* A, int lda, const _Float16* Bm, int ldb,
                                          int n0) {
   const int r = lane_id() & 15, kl = (lane_id() >> 4) * 8;
 #pragma unroll
   for (int k0 = 0; k0 < K; k0 += 32) {
-    const f16x8 bfr = frag_t(Bm, ldb, k0, n0);
+    const f16x8 bfr = KP ? frag_tk(Bm, ldb, k0, n0) : frag_t(Bm, ldb, k0, n0);
     f16x8 af[NO];
 #pragma unroll
     for (int t = 0; t < NO; ++t)
@@ -1234,7 +1271,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) y[t] = du[t] = u[t] = dr[t] = zero4();
-    mma_chain_rows2<NT, NTK>(y, du, Ks, LDK, h0f, dhf);
+    mma_chain_rows2<NT, NTK, true>(y, du, Ks, LDK, h0f, dhf);
     lds_barrier();  // every wave holds its v / dO strips: Hs may take H0
     put_state(h0f);
     f32x4 psb[NT], psy[NT];
@@ -1440,9 +1477,9 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     f32x4 dq[NT], dk[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) dq[t] = dk[t] = zero4();
-    mma_rows<NT, C, kLower>(dq, dPm, LDC, Ks, LDK, 16 * w);
-    mma_rows<NT, C, kUpper>(dk, dPmT, LDC, Qs, LDK, 16 * w);
-    mma_rows<NT, C>(dk, dAs, LDC, Ks, LDK, 16 * w);
+    mma_rows<NT, C, kLower, true>(dq, dPm, LDC, Ks, LDK, 16 * w);
+    mma_rows<NT, C, kUpper, true>(dk, dPmT, LDC, Qs, LDK, 16 * w);
+    mma_rows<NT, C, kFull, true>(dk, dAs, LDC, Ks, LDK, 16 * w);
     float gcx = 0.f;
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
@@ -1450,8 +1487,8 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       const f32x4 lv = *reinterpret_cast<const f32x4*>(lam + 16 * rt + 4 * g);
       const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * rt + 4 * g);
       f32x4 rgx;
-      const f16x4 qn4 = tr4(Qs, LDK, 16 * rt + 4 * g, 16 * w);  // Qn[16rt + 4g + e][i2]
-      const f16x4 kn4 = tr4(Ks, LDK, 16 * rt + 4 * g, 16 * w);
+      const f16x4 qn4 = tr4k(Qs, LDK, 16 * rt + 4 * g, 16 * w);  // Qn[16rt + 4g + e][i2]
+      const f16x4 kn4 = tr4k(Ks, LDK, 16 * rt + 4 * g, 16 * w);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float qn = static_cast<float>(qn4[e]);
@@ -1533,8 +1570,8 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       float xq[NT][4], xk[NT][4];  // q_hat / k_hat at this lane's rows 16rt + 4g + e, column i2
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) {
-        const f16x4 q4 = tr4(Qs, LDK, 16 * rt + 4 * g, 16 * w);
-        const f16x4 k4 = tr4(Ks, LDK, 16 * rt + 4 * g, 16 * w);
+        const f16x4 q4 = tr4k(Qs, LDK, 16 * rt + 4 * g, 16 * w);
+        const f16x4 k4 = tr4k(Ks, LDK, 16 * rt + 4 * g, 16 * w);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           xq[rt][e] = static_cast<float>(q4[e]);
@@ -1929,10 +1966,18 @@ __global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
         dkg[e] = dqg[e] = dkl[e] = uint4{0u, 0u, 0u, 0u};
         continue;
       }
+      // key-ordered unit u: natural columns n .. n + 3 and n + 16 .. n + 19
+      const int n = 32 * (u >> 2) + 4 * (u & 3);
       float gx[8], ge[8];
-      ld8f(gx, G2 + r * LDG + 8 * u);
-      ld8f(ge, G2 + (C - 1) * LDG + 8 * u);
-      const f16x8 kv = ld8(Ks + r * LDK + 8 * u), qv = ld8(Qs + r * LDK + 8 * u);
+      {
+        const float4 a0 = *reinterpret_cast<const float4*>(G2 + r * LDG + n);
+        const float4 a1 = *reinterpret_cast<const float4*>(G2 + r * LDG + n + 16);
+        const float4 b0 = *reinterpret_cast<const float4*>(G2 + (C - 1) * LDG + n);
+        const float4 b1 = *reinterpret_cast<const float4*>(G2 + (C - 1) * LDG + n + 16);
+        gx[0] = a0.x; gx[1] = a0.y; gx[2] = a0.z; gx[3] = a0.w; gx[4] = a1.x; gx[5] = a1.y; gx[6] = a1.z; gx[7] = a1.w;
+        ge[0] = b0.x; ge[1] = b0.y; ge[2] = b0.z; ge[3] = b0.w; ge[4] = b1.x; ge[5] = b1.y; ge[6] = b1.z; ge[7] = b1.w;
+      }
+      const f16x8 kv = key_unit(Ks + r * LDK, u), qv = key_unit(Qs + r * LDK, u);
       f16x8 okg, oqg, okl;
 #pragma unroll
       for (int q2 = 0; q2 < 8; ++q2) {
@@ -2098,8 +2143,8 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
     f32x4 y[NT], u[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) y[t] = u[t] = o[t] = zero4();
-    mma_chain_rows<NT, NTK>(y, Kg, LDK, hf);
-    if constexpr (WRITE_O) mma_chain_rows<NT, NTK>(o, Qg, LDK, hf);
+    mma_chain_rows<NT, NTK, kFull, true>(y, Kg, LDK, hf);
+    if constexpr (WRITE_O) mma_chain_rows<NT, NTK, kFull, true>(o, Qg, LDK, hf);
     f32x4 rhs[NT];
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr) {
@@ -2120,7 +2165,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) h[ti][e] *= dec[e];
     }
-    mma_chain_rows_t<NTK, NT>(h, Kl, LDK, bf);
+    mma_chain_rows_t<NTK, NT, kFull, true>(h, Kl, LDK, bf);
     lds_barrier();
   };
   for (int c = 0; c < nc; c += 2) {
@@ -2227,7 +2272,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwdh16_kernel(K16 a) {
     f32x4 du[NT], dr[NT], dof[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) du[t] = dr[t] = zero4();
-    mma_chain_rows<NT, NTK>(du, Kl, LDK, hf);
+    mma_chain_rows<NT, NTK, kFull, true>(du, Kl, LDK, hf);
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr) {
       float x[4];
@@ -2252,9 +2297,9 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwdh16_kernel(K16 a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) dh[ti][e] *= dec[e];
     }
-    mma_chain_rows_t<NTK, NT>(dh, Qg, LDK, bo);
+    mma_chain_rows_t<NTK, NT, kFull, true>(dh, Qg, LDK, bo);
     chain_frags<NT>(bf, dr);
-    mma_chain_rows_t<NTK, NT>(dh, Kg, LDK, bf);
+    mma_chain_rows_t<NTK, NT, kFull, true>(dh, Kg, LDK, bf);
     lds_barrier();
   };
   // chunks nc-1, nc-2, ... alternate between the two buffers
@@ -2424,8 +2469,8 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) y[t] = du[t] = u[t] = dr[t] = zero4();
-    mma_chain_rows<NT, NTK>(y, Kg, LDK, h0f);
-    mma_chain_rows<NT, NTK>(du, Kl, LDK, dhf);
+    mma_chain_rows<NT, NTK, kFull, true>(y, Kg, LDK, h0f);
+    mma_chain_rows<NT, NTK, kFull, true>(du, Kl, LDK, dhf);
     lds_barrier();  // every wave holds its v / dO strips: Hs may take H0
     put_state(h0f);
     f32x4 psb[NT];
