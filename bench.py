@@ -103,7 +103,8 @@ def design_bytes_per_token_head(name, d=D, c=C, grp=HV // HK, saved=True):
     for the forward and, unless the forward saved its chunks for the VJP,
     once more for the VJP; chunk_grad covers a whole k-head group per
     workgroup (the key image once, both v-heads' chunk images, states, v and
-    dout rows; dq, dk written once)."""
+    dout rows, dv rows; dq, dk written once); chunk_dh reads dout and writes
+    the chunk-end gradients."""
     im = image_bytes(d, c)
     kq = 2 * d * 2 / grp     # k and q rows, bf16
     vec = d * 2              # one bf16 row of v / o / do
@@ -115,8 +116,8 @@ def design_bytes_per_token_head(name, d=D, c=C, grp=HV // HK, saved=True):
         "chunk_fwd": im["KEY"] / (c * grp) + im["CHK"] / c + 2 * vec,
         "chunk_fwd_save": im["KEY"] / (c * grp) + im["CHK"] / c + 2 * vec + st,
         "chunk_states": im["KN"] / (c * grp) + (im["GT"] + im["TM"]) / c + vec + st,
-        "chunk_dh": im["KEY"] / (c * grp) + im["CHK"] / c + 2 * vec + st,
-        "chunk_grad": im["KEY"] / (c * grp) + im["CHK"] / c + 2 * st + 2 * vec + gates + 2 * d * 2 / grp,
+        "chunk_dh": im["KEY"] / (c * grp) + im["CHK"] / c + vec + st,
+        "chunk_grad": im["KEY"] / (c * grp) + im["CHK"] / c + 2 * st + 3 * vec + gates + 2 * d * 2 / grp,
     }.get(name)
 
 

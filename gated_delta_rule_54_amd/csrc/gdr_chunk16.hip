@@ -913,9 +913,10 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void chain16_kernel(K16 a) {
 // ---------------------------------------------------------------------------
 // dh16: reverse pass carrying dH.  Per chunk and compute wave:
 //   dU   = lam (Kn dH) + P^T dO           (16 + 8 MFMA, chained)
-//   dRHS = T^T dU                         (8, chained);  dv = beta dRHS
+//   dRHS = T^T dU                         (8, chained)
 //   dH   = gam_C dH + Qn^T (gam dO) - Kn^T (beta gam dRHS)   (16 + 16, chained)
-// Every chunk's incoming dH (the gradient at its end) is stored for grad16.
+// Every chunk's incoming dH (the gradient at its end) is stored for grad16,
+// which also forms dv = beta dRHS.
 // ---------------------------------------------------------------------------
 template <int C, typename TO>
 __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
@@ -924,11 +925,8 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
   constexpr uint32_t CB = IM::CHK;  // gates | T | P
   constexpr uint32_t KB = IM::KEY;  // Kn | Qn
   constexpr uint32_t VB = C * BV * 2;
-  constexpr uint32_t OB = OutTile<TO>::template bytes<C>();
   __shared__ __align__(16) char bufA[CB + KB + VB];
   __shared__ __align__(16) char bufB[CB + KB + VB];
-  __shared__ __align__(16) char osA[OB];
-  __shared__ __align__(16) char osB[OB];
 
   const int w = wave_id(), lane = lane_id(), g = lane >> 4, c16 = lane & 15;
   const ChainPos p = chain_pos(a);
@@ -947,21 +945,18 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
     return make_rsrc(p0, static_cast<uint32_t>(rows_of(c)) * rowb);
   };
   const uint32_t rowv = static_cast<uint32_t>(a.Hv) * DK * 2;
-  const uint32_t rowo = static_cast<uint32_t>(a.Hv) * DK * sizeof(TO);
 
   if (w == NCW) {  // ---- producer wave: chunks NC-1, NC-2, ...
     const char* kim0 = a.kimg + (p.b * a.Hk + p.kh) * a.NC * static_cast<int64_t>(IM::KEY);
     const char* cim0 = a.cimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::CHK);
     const uint32_t colv = (p.hv * DK + p.half * BV) * 2;
-    const uint32_t colo = (p.hv * DK + p.half * BV) * static_cast<uint32_t>(sizeof(TO));
     auto stage = [&](int c, char* buf) {
       dma<CB, 64>(make_rsrc(cim0 + c * static_cast<int64_t>(IM::CHK), CB), 0, buf, lane, 0);
       dma<KB, 64>(make_rsrc(kim0 + c * static_cast<int64_t>(IM::KEY), KB), 0, buf + CB, lane, 0);
       dma_rows<C, BV * 2, 64>(seq_rsrc(a.dout, 2, c, rowv), rowv, colv, rows_of(c), buf + CB + KB, lane, 0);
     };
-    auto pstep = [&](int c, char* nxt, const char* os_prev) __attribute__((always_inline)) {
+    auto pstep = [&](int c, char* nxt) __attribute__((always_inline)) {
       if (c > 0) stage(c - 1, nxt);
-      if (c + 1 < nc) flush_tile<TO, C>(os_prev, seq_rsrc(a.dv, sizeof(TO), c + 1, rowo), rowo, colo);
       wait_all();
       lds_barrier();
     };
@@ -969,10 +964,9 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
     wait_all();
     lds_barrier();
     for (int i = 0; i < nc; i += 2) {
-      pstep(nc - 1 - i, bufB, osB);
-      if (i + 1 < nc) pstep(nc - 2 - i, bufA, osA);
+      pstep(nc - 1 - i, bufB);
+      if (i + 1 < nc) pstep(nc - 2 - i, bufA);
     }
-    flush_tile<TO, C>(((nc - 1) & 1) ? osB : osA, seq_rsrc(a.dv, sizeof(TO), 0, rowo), rowo, colo);
     return;
   }
 
@@ -991,7 +985,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
   }
   lds_barrier();
 
-  auto step = [&](int c, const char* cur, char* os) __attribute__((always_inline)) {
+  auto step = [&](int c, const char* cur) __attribute__((always_inline)) {
     const float* gam = reinterpret_cast<const float*>(cur);
     const float* lam = gam + C;
     const float* bet = gam + 2 * C;
@@ -1003,7 +997,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
 
     f16x8 hf[NTK / 2];
     chain_frags<NTK>(hf, dh);
-    f32x4 du[NT], dr[NT], dvv[NT];
+    f32x4 du[NT], dr[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) du[t] = dr[t] = zero4();
     mma_chain_rows<NT, NTK, kFull, true>(du, Kn, LDK, hf);
@@ -1037,12 +1031,8 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
       const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
       const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * tr + 4 * g);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dvv[tr][e] = bv[e] * dr[tr][e];
-        dr[tr][e] = -gv[e] * dvv[tr][e];
-      }
+      for (int e = 0; e < 4; ++e) dr[tr][e] = -gv[e] * bv[e] * dr[tr][e];
     }
-    put_strip<TO, NT>(os, 16 * w + c16, dvv);
     const float gc = gam[rows_of(c) - 1];
 #pragma unroll
     for (int ti = 0; ti < NTK; ++ti) dh[ti] = dh[ti] * gc;
@@ -1054,8 +1044,8 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
   };
   // chunks NC-1, NC-2, ... alternate between the two buffers
   for (int i = 0; i < nc; i += 2) {
-    step(nc - 1 - i, bufA, osA);
-    if (i + 1 < nc) step(nc - 2 - i, bufB, osB);
+    step(nc - 1 - i, bufA);
+    if (i + 1 < nc) step(nc - 2 - i, bufB);
   }
   if (a.dh0) {
 #pragma unroll
@@ -1066,7 +1056,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
 }
 
 // ---------------------------------------------------------------------------
-// grad16: all gradients of one chunk except dv and dH, given its entry state
+// grad16: all gradients of one chunk except dH, given its entry state
 // H0 and the gradient dH at its end (both [Dk][Dv] fp16).  Eight waves.  One
 // workgroup per (chunk, k-head, b) walks the v-heads of the k-head group one
 // after the other (GROUP; ONLY when the group has one v-head): the key image
@@ -1078,8 +1068,9 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
 // epilogue kernel, which sums the group and applies the norm VJP.
 //   Phase A  wave w owns the 16-column value strip jw = 16w .. 16w+15 and
 //            chains in registers Y = K H0, X = K dH, U = T RHS,
-//            dU = lam X + P^T dO, dRHS = T^T dU; it writes dRHS, dO and U
-//            (then dU, RHS) as row-major [C][Dv] copies to LDS.
+//            dU = lam X + P^T dO, dRHS = T^T dU; it stores dv = beta dRHS
+//            and writes dRHS, dO and U (then dU, RHS) as row-major [C][Dv]
+//            copies to LDS.
 //   Phase 1  X1 = dRHS H0^T, X2 = dO H0^T (wave w: Dk tile w, all rows),
 //            dP = dO U^T (C x C tiles dealt to the waves).
 //   Phase 2  X3 = U dH^T, dT = dU RHS^T.
@@ -1299,6 +1290,18 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     mma_chain_rows_t<NT, NT, kUpper>(du, Ps, LDC, bf);
     chain_frags<NT>(bf, du);
     mma_chain_rows_t<NT, NT, kUpper>(dr, Ts, LDC, bf);
+    {  // dv = beta dRHS; rows past the sequence's end are dropped by the buffer extent
+      const uint32_t rowo = static_cast<uint32_t>(a.Hv) * DK * sizeof(TO);
+      const rsrc_t ovr = make_rsrc(static_cast<char*>(a.dv) + (sp.t0 + t0) * rowo, static_cast<uint32_t>(L) * rowo);
+      f32x4 dvs[NT];
+#pragma unroll
+      for (int tr = 0; tr < NT; ++tr) {
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dvs[tr][e] = bv[e] * dr[tr][e];
+      }
+      store_strip_buf<TO, NT>(ovr, 4 * g * rowo + (hv * DK + jw) * static_cast<uint32_t>(sizeof(TO)), rowo, dvs);
+    }
 #pragma unroll
     for (int tr = 0; tr < NT; ++tr)
 #pragma unroll
