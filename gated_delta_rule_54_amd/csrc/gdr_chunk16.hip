@@ -47,13 +47,17 @@ namespace {
 
 constexpr int DK = 128;       // key dim == value dim
 constexpr int LDK = DK + 8;   // pitch (halves) of [*][DK] tiles
-constexpr int BV = 64;        // value columns per chain workgroup
 constexpr int NTK = DK / 16;  // 16-row tiles of a state strip
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void;
+// LDS address of a generic pointer into a __shared__ array: its low 32 bits
+// (the shared aperture's base is 4 GB aligned), with no null check.
+__device__ __forceinline__ lds_void lds_addr(const void* p) {
+  return (lds_void)(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
+}
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Byte sizes of the images (all multiples of 16).
@@ -123,7 +127,7 @@ __device__ __forceinline__ void dma(rsrc_t r, uint32_t off, char* dst, int tid, 
 #pragma unroll
   for (int u = 0; u < (N16 + NTH - 1) / NTH; ++u) {
     if (N16 % NTH == 0 || NTH * u + tid < N16)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void)(dst + 16 * (NTH * u + 64 * w)), 16, off + 16 * tid,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_addr(dst + 16 * (NTH * u + 64 * w)), 16, off + 16 * tid,
                                                16 * NTH * u, 0, 0);
   }
 }
@@ -364,21 +368,21 @@ __device__ __forceinline__ void store_strip_buf(rsrc_t r, uint32_t voff, uint32_
     }
 }
 
-// Chain workgroup -> (b, v-head, value half).  Workgroups are dealt to the
-// eight XCDs round robin; the remap puts the 2 * Hv / Hk workgroups that read
-// one key image (and the 2 that read one chunk image) on the same XCD, so
-// they share its L2.
+// Chain workgroup -> (b, v-head, value slice), nsl slices per v-head.
+// Workgroups are dealt to the eight XCDs round robin; the remap puts the
+// nsl * Hv / Hk workgroups that read one key image (and the nsl that read
+// one chunk image) on the same XCD, so they share its L2.
 struct ChainPos {
-  int half, hv, kh;
+  int slice, hv, kh;
   int64_t b;
 };
-__device__ __forceinline__ ChainPos chain_pos(const K16& a) {
+__device__ __forceinline__ ChainPos chain_pos(const K16& a, int nsl) {
   const int nb = gridDim.x, l0 = blockIdx.x;
   const int lg = (nb % 8 == 0) ? (l0 % 8) * (nb / 8) + l0 / 8 : l0;
   ChainPos p;
-  p.half = lg & 1;
-  p.hv = (lg >> 1) % a.Hv;
-  p.b = (lg >> 1) / a.Hv;
+  p.slice = lg % nsl;
+  p.hv = (lg / nsl) % a.Hv;
+  p.b = (lg / nsl) / a.Hv;
   p.kh = p.hv / (a.Hv / a.Hk);
   return p;
 }
@@ -655,18 +659,23 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
 }
 
 // ---------------------------------------------------------------------------
-// Chain kernels: four compute waves and one producer wave per workgroup.
-// The compute waves own the state in MFMA accumulators and touch only LDS;
-// the producer wave issues all bulk global traffic of the chunk loop: it
-// copies the next chunk's images and the rows of v / dO for this value half
-// (C x 64 bf16) into LDS by buffer_load ... lds, and stores the previous
-// chunk's o / dv from an LDS tile [C][LDO] (written from the accumulators)
-// as 16-byte rows.  One barrier per chunk; a wave stalled on memory issue
-// never holds up the matrix cores.  Chunk states (H for the VJP, dH) leave
-// the compute waves as four 16-byte stores per lane in chained-fragment
-// order (see frag_off).
+// Chain kernels: NCW compute waves (16 value columns each: a value slice of
+// BV = 16 NCW columns) and one producer wave per workgroup, one workgroup
+// per (b, v-head, slice).  The compute waves own the state in MFMA
+// accumulators and touch only LDS; the producer wave issues all bulk global
+// traffic of the chunk loop: it copies the next chunk's images and the rows
+// of v / dO for this slice (C x BV bf16) into LDS by buffer_load ... lds,
+// and stores the previous chunk's o from an LDS tile [C][LDO] (written from
+// the accumulators) as 16-byte rows.  One barrier per chunk; a wave stalled
+// on memory issue never holds up the matrix cores.  Chunk states (H for the
+// VJP, dH) leave the compute waves as four 16-byte stores per lane in
+// chained-fragment order (see frag_off).  The launch takes the widest slice
+// whose grid still covers every CU (NCW = 4 from B Hv >= CUs / 2, e.g. B = 4,
+// Hv = 32 on 256 CUs; 1 at B = 1): a workgroup's time per chunk is set by its compute
+// waves' own chain of products, so narrower slices finish a small batch
+// sooner, and by the copy of the next chunk when every CU is copying, so a
+// full grid keeps the widest slices (fewest copies of each image).
 // ---------------------------------------------------------------------------
-constexpr int NCW = 4;  // compute waves of a chain workgroup; wave NCW is the producer
 
 // Workgroup barrier that orders LDS accesses only (global stores in flight
 // stay in flight).
@@ -698,7 +707,7 @@ __device__ __forceinline__ void dma_rows(rsrc_t r, uint32_t rowb, uint32_t col0,
     const int e = NTH * u + tid;
     const int row = e / UPR, cu = e % UPR;
     const int rr = row < L ? row : L - 1;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void)(dst + 16 * (NTH * u + 64 * w)), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_addr(dst + 16 * (NTH * u + 64 * w)), 16,
                                              rr * rowb + col0 + 16 * cu, 0, 0, 0);
   }
 }
@@ -711,19 +720,19 @@ __device__ __forceinline__ void tile_col4_bf16(float (&x)[4], const uint16_t* M,
   bf16x4_to_f32(x, tr4(reinterpret_cast<const _Float16*>(M), ld, r0, c0));
 }
 
-// Output tile of one chunk and value half: [C][LDO] elements of TO.
-template <typename TO>
+// Output tile of one chunk and value slice of BVX columns: [C][LDO] elements of TO.
+template <typename TO, int BVX>
 struct OutTile {
-  static constexpr int LDO = std::is_same_v<TO, float> ? BV + 4 : BV + 8;
-  static constexpr int UPR = BV * static_cast<int>(sizeof(TO)) / 16;  // 16-byte units per row
+  static constexpr int LDO = std::is_same_v<TO, float> ? BVX + 4 : BVX + 8;
+  static constexpr int UPR = BVX * static_cast<int>(sizeof(TO)) / 16;  // 16-byte units per row
   template <int C>
   static constexpr uint32_t bytes() { return C * LDO * sizeof(TO); }
 };
 
 // This lane's strip rows 16tr + 4g + e of column col into the output tile.
-template <typename TO, int NT>
+template <typename TO, int NT, int BVX>
 __device__ __forceinline__ void put_strip(char* os, int col, const f32x4 (&x)[NT]) {
-  constexpr int LDO = OutTile<TO>::LDO;
+  constexpr int LDO = OutTile<TO, BVX>::LDO;
   const int g = lane_id() >> 4;
 #pragma unroll
   for (int tr = 0; tr < NT; ++tr)
@@ -739,9 +748,9 @@ __device__ __forceinline__ void put_strip(char* os, int col, const f32x4 (&x)[NT
 
 // One wave stores the output tile's rows to buffer r (rows rowb bytes apart
 // from byte col0); rows past the buffer end are dropped.
-template <typename TO, int C>
+template <typename TO, int C, int BVX>
 __device__ __forceinline__ void flush_tile(const char* os, rsrc_t r, uint32_t rowb, uint32_t col0) {
-  constexpr int LDO = OutTile<TO>::LDO, UPR = OutTile<TO>::UPR, N16 = C * UPR;
+  constexpr int LDO = OutTile<TO, BVX>::LDO, UPR = OutTile<TO, BVX>::UPR, N16 = C * UPR;
   static_assert(N16 % 64 == 0, "whole wave rounds");
   const int lane = lane_id();
 #pragma unroll
@@ -760,26 +769,27 @@ __device__ __forceinline__ void flush_tile(const char* os, rsrc_t r, uint32_t ro
 //   O = gam Z + P U             (8, chained)
 //   H = gam_C H + Kn^T (lam U)  (16, chained)
 // ---------------------------------------------------------------------------
-template <int C, typename TO, bool WRITE_O, bool STORE_H>
+template <int C, typename TO, bool WRITE_O, bool STORE_H, int NCW>
 __global__ __launch_bounds__(64 * (NCW + 1)) void chain16_kernel(K16 a) {
+  constexpr int BV = 16 * NCW, NSL = DK / BV;  // value columns of a workgroup, workgroups per v-head
   using IM = Img<C>;
   constexpr int NT = C / 16, LDC = IM::LDC;
   constexpr uint32_t CB = WRITE_O ? IM::CHK : IM::GT + IM::TM;  // gates | T (| P)
   constexpr uint32_t KB = WRITE_O ? IM::KEY : IM::KN;           // Kn (| Qn)
   constexpr uint32_t VB = C * BV * 2;                           // v tile [C][BV] bf16
-  constexpr uint32_t OB = WRITE_O ? OutTile<TO>::template bytes<C>() : 16;
+  constexpr uint32_t OB = WRITE_O ? OutTile<TO, BV>::template bytes<C>() : 16;
   __shared__ __align__(16) char bufA[CB + KB + VB];
   __shared__ __align__(16) char bufB[CB + KB + VB];
   __shared__ __align__(16) char osA[OB];
   __shared__ __align__(16) char osB[OB];
 
   const int w = wave_id(), lane = lane_id(), g = lane >> 4, c16 = lane & 15;
-  const ChainPos p = chain_pos(a);
+  const ChainPos p = chain_pos(a, NSL);
   const SeqSpan sp = seq_span(a, p.b);
   const int nc = static_cast<int>((sp.len + C - 1) / C);
   if (nc == 0) {  // empty sequence of a ragged batch: the state passes through
     if (w < NCW && a.ht) {
-      const int64_t base = (p.b * a.Hv + p.hv) * DK * DK + p.half * BV + 16 * w + c16;
+      const int64_t base = (p.b * a.Hv + p.hv) * DK * DK + p.slice * BV + 16 * w + c16;
       for (int i = 0; i < DK; ++i) a.ht[base + i * DK] = a.h0 ? a.h0[base + i * DK] : 0.f;
     }
     return;
@@ -795,8 +805,8 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void chain16_kernel(K16 a) {
   if (w == NCW) {  // ---- producer wave
     const char* kim0 = a.kimg + (p.b * a.Hk + p.kh) * a.NC * static_cast<int64_t>(IM::KEY);
     const char* cim0 = a.cimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::CHK);
-    const uint32_t colv = (p.hv * DK + p.half * BV) * 2;
-    const uint32_t colo = (p.hv * DK + p.half * BV) * static_cast<uint32_t>(sizeof(TO));
+    const uint32_t colv = (p.hv * DK + p.slice * BV) * 2;
+    const uint32_t colo = (p.hv * DK + p.slice * BV) * static_cast<uint32_t>(sizeof(TO));
     auto stage = [&](int c, char* buf) {
       dma<CB, 64>(make_rsrc(cim0 + c * static_cast<int64_t>(IM::CHK), CB), 0, buf, lane, 0);
       dma<KB, 64>(make_rsrc(kim0 + c * static_cast<int64_t>(IM::KEY), KB), 0, buf + CB, lane, 0);
@@ -805,7 +815,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void chain16_kernel(K16 a) {
     auto pstep = [&](int c, char* nxt, const char* os_prev) __attribute__((always_inline)) {
       if (c + 1 < nc) stage(c + 1, nxt);
       if constexpr (WRITE_O) {
-        if (c > 0) flush_tile<TO, C>(os_prev, seq_rsrc(a.o, sizeof(TO), c - 1, rowo), rowo, colo);
+        if (c > 0) flush_tile<TO, C, BV>(os_prev, seq_rsrc(a.o, sizeof(TO), c - 1, rowo), rowo, colo);
       }
       wait_all();
       lds_barrier();
@@ -818,13 +828,13 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void chain16_kernel(K16 a) {
       if (c + 1 < nc) pstep(c + 1, bufA, osA);
     }
     if constexpr (WRITE_O)
-      flush_tile<TO, C>(((nc - 1) & 1) ? osB : osA, seq_rsrc(a.o, sizeof(TO), nc - 1, rowo), rowo, colo);
+      flush_tile<TO, C, BV>(((nc - 1) & 1) ? osB : osA, seq_rsrc(a.o, sizeof(TO), nc - 1, rowo), rowo, colo);
     return;
   }
 
   // ---- compute waves
-  const int jcol = p.half * BV + 16 * w + c16;  // this lane's state column
-  const int wg = p.half * NCW + w;              // column group of the chunk-state layout
+  const int jcol = p.slice * BV + 16 * w + c16;  // this lane's state column
+  const int wg = p.slice * NCW + w;              // column group of the chunk-state layout
   const int64_t hbase = (p.b * a.Hv + p.hv) * DK * DK + jcol;
   f32x4 h[NTK];
 #pragma unroll
@@ -895,7 +905,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void chain16_kernel(K16 a) {
 #pragma unroll
     for (int ti = 0; ti < NTK; ++ti) h[ti] = h[ti] * gc;
     mma_chain_rows_t<NTK, NT, kFull, true>(h, Kn, LDK, bf);
-    if constexpr (WRITE_O) put_strip<TO, NT>(os, 16 * w + c16, o);
+    if constexpr (WRITE_O) put_strip<TO, NT, BV>(os, 16 * w + c16, o);
     lds_barrier();
   };
   for (int c = 0; c < nc; c += 2) {
@@ -918,8 +928,9 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void chain16_kernel(K16 a) {
 // Every chunk's incoming dH (the gradient at its end) is stored for grad16,
 // which also forms dv = beta dRHS.
 // ---------------------------------------------------------------------------
-template <int C, typename TO>
+template <int C, typename TO, int NCW>
 __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
+  constexpr int BV = 16 * NCW, NSL = DK / BV;
   using IM = Img<C>;
   constexpr int NT = C / 16, LDC = IM::LDC;
   constexpr uint32_t CB = IM::CHK;  // gates | T | P
@@ -929,12 +940,12 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
   __shared__ __align__(16) char bufB[CB + KB + VB];
 
   const int w = wave_id(), lane = lane_id(), g = lane >> 4, c16 = lane & 15;
-  const ChainPos p = chain_pos(a);
+  const ChainPos p = chain_pos(a, NSL);
   const SeqSpan sp = seq_span(a, p.b);
   const int nc = static_cast<int>((sp.len + C - 1) / C);
   if (nc == 0) {  // empty sequence of a ragged batch: the state passes through
     if (w < NCW && a.dh0) {
-      const int64_t base = (p.b * a.Hv + p.hv) * DK * DK + p.half * BV + 16 * w + c16;
+      const int64_t base = (p.b * a.Hv + p.hv) * DK * DK + p.slice * BV + 16 * w + c16;
       for (int i = 0; i < DK; ++i) a.dh0[base + i * DK] = a.dht ? a.dht[base + i * DK] : 0.f;
     }
     return;
@@ -949,7 +960,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
   if (w == NCW) {  // ---- producer wave: chunks NC-1, NC-2, ...
     const char* kim0 = a.kimg + (p.b * a.Hk + p.kh) * a.NC * static_cast<int64_t>(IM::KEY);
     const char* cim0 = a.cimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::CHK);
-    const uint32_t colv = (p.hv * DK + p.half * BV) * 2;
+    const uint32_t colv = (p.hv * DK + p.slice * BV) * 2;
     auto stage = [&](int c, char* buf) {
       dma<CB, 64>(make_rsrc(cim0 + c * static_cast<int64_t>(IM::CHK), CB), 0, buf, lane, 0);
       dma<KB, 64>(make_rsrc(kim0 + c * static_cast<int64_t>(IM::KEY), KB), 0, buf + CB, lane, 0);
@@ -971,8 +982,8 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void dh16_kernel(K16 a) {
   }
 
   // ---- compute waves
-  const int jcol = p.half * BV + 16 * w + c16;
-  const int wg = p.half * NCW + w;
+  const int jcol = p.slice * BV + 16 * w + c16;
+  const int wg = p.slice * NCW + w;
   const int64_t hbase = (p.b * a.Hv + p.hv) * DK * DK + jcol;
   f32x4 dh[NTK];
 #pragma unroll
@@ -2054,8 +2065,9 @@ __global__ __launch_bounds__(512) void cwprep16_kernel(K16 a) {
 // The chunk's o leaves the compute waves as 2-byte stores (their LDS share
 // holds the three key tiles).  STORE_H: every chunk's entry state is stored
 // for the VJP (fp16, chained-fragment order); WRITE_O false: no outputs.
-template <int C, typename TO, bool WRITE_O, bool STORE_H>
+template <int C, typename TO, bool WRITE_O, bool STORE_H, int NCW>
 __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
+  constexpr int BV = 16 * NCW, NSL = DK / BV;
   using IM = ImgCW<C>;
   constexpr int NT = C / 16, LDC = IM::LDC;
   constexpr uint32_t CB = IM::CHK, KB = IM::KEY, VB = C * BV * 2;
@@ -2063,12 +2075,12 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
   __shared__ __align__(16) char bufB[CB + KB + VB];
 
   const int w = wave_id(), lane = lane_id(), g = lane >> 4, c16 = lane & 15;
-  const ChainPos p = chain_pos(a);
+  const ChainPos p = chain_pos(a, NSL);
   const SeqSpan sp = seq_span(a, p.b);
   const int nc = static_cast<int>((sp.len + C - 1) / C);
   if (nc == 0) {  // empty sequence of a ragged batch: the state passes through
     if (w < NCW && a.ht) {
-      const int64_t base = (p.b * a.Hv + p.hv) * DK * DK + p.half * BV + 16 * w + c16;
+      const int64_t base = (p.b * a.Hv + p.hv) * DK * DK + p.slice * BV + 16 * w + c16;
       for (int i = 0; i < DK; ++i) a.ht[base + i * DK] = a.h0 ? a.h0[base + i * DK] : 0.f;
     }
     return;
@@ -2084,7 +2096,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
   if (w == NCW) {  // ---- producer wave
     const char* kim0 = a.kimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::KEY);
     const char* cim0 = a.cimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::CHK);
-    const uint32_t colv = (p.hv * DK + p.half * BV) * 2;
+    const uint32_t colv = (p.hv * DK + p.slice * BV) * 2;
     auto stage = [&](int c, char* buf) {
       dma<CB, 64>(make_rsrc(cim0 + c * static_cast<int64_t>(IM::CHK), CB), 0, buf, lane, 0);
       dma<KB, 64>(make_rsrc(kim0 + c * static_cast<int64_t>(IM::KEY), KB), 0, buf + CB, lane, 0);
@@ -2107,8 +2119,8 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
   }
 
   // ---- compute waves
-  const int jcol = p.half * BV + 16 * w + c16;
-  const int wg = p.half * NCW + w;  // column group of the chunk-state layout
+  const int jcol = p.slice * BV + 16 * w + c16;
+  const int wg = p.slice * NCW + w;  // column group of the chunk-state layout
   const int64_t hbase = (p.b * a.Hv + p.hv) * DK * DK + jcol;
   const uint32_t voffo = 4 * g * rowo + (p.hv * DK + jcol) * static_cast<uint32_t>(sizeof(TO));
   f32x4 h[NTK];
@@ -2190,8 +2202,9 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwchain16_kernel(K16 a) {
 //   dU = Kl dH + P^T dO,  dRHS = T^T dU,
 //   dH = diag(e^{G_C}) dH + Qg^T dO - Kg^T (beta dRHS).
 // (dv and the other gradients come from the per-chunk VJP.)
-template <int C>
+template <int C, int NCW>
 __global__ __launch_bounds__(64 * (NCW + 1)) void cwdh16_kernel(K16 a) {
+  constexpr int BV = 16 * NCW, NSL = DK / BV;
   using IM = ImgCW<C>;
   constexpr int NT = C / 16, LDC = IM::LDC;
   constexpr uint32_t CB = IM::CHK, KB = IM::KEY, VB = C * BV * 2;
@@ -2199,12 +2212,12 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwdh16_kernel(K16 a) {
   __shared__ __align__(16) char bufB[CB + KB + VB];
 
   const int w = wave_id(), lane = lane_id(), g = lane >> 4, c16 = lane & 15;
-  const ChainPos p = chain_pos(a);
+  const ChainPos p = chain_pos(a, NSL);
   const SeqSpan sp = seq_span(a, p.b);
   const int nc = static_cast<int>((sp.len + C - 1) / C);
   if (nc == 0) {  // empty sequence of a ragged batch: the gradient passes through
     if (w < NCW && a.dh0) {
-      const int64_t base = (p.b * a.Hv + p.hv) * DK * DK + p.half * BV + 16 * w + c16;
+      const int64_t base = (p.b * a.Hv + p.hv) * DK * DK + p.slice * BV + 16 * w + c16;
       for (int i = 0; i < DK; ++i) a.dh0[base + i * DK] = a.dht ? a.dht[base + i * DK] : 0.f;
     }
     return;
@@ -2215,7 +2228,7 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwdh16_kernel(K16 a) {
   if (w == NCW) {  // ---- producer wave: chunks nc-1, nc-2, ...
     const char* kim0 = a.kimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::KEY);
     const char* cim0 = a.cimg + (p.b * a.Hv + p.hv) * a.NC * static_cast<int64_t>(IM::CHK);
-    const uint32_t colv = (p.hv * DK + p.half * BV) * 2;
+    const uint32_t colv = (p.hv * DK + p.slice * BV) * 2;
     auto stage = [&](int c, char* buf) {
       const char* p0 = reinterpret_cast<const char*>(a.dout) + (sp.t0 + static_cast<int64_t>(c) * C) * rowv;
       dma<CB, 64>(make_rsrc(cim0 + c * static_cast<int64_t>(IM::CHK), CB), 0, buf, lane, 0);
@@ -2240,8 +2253,8 @@ __global__ __launch_bounds__(64 * (NCW + 1)) void cwdh16_kernel(K16 a) {
   }
 
   // ---- compute waves
-  const int jcol = p.half * BV + 16 * w + c16;
-  const int wg = p.half * NCW + w;
+  const int jcol = p.slice * BV + 16 * w + c16;
+  const int wg = p.slice * NCW + w;
   const int64_t hbase = (p.b * a.Hv + p.hv) * DK * DK + jcol;
   f32x4 dh[NTK];
 #pragma unroll
@@ -3051,6 +3064,38 @@ K16 args16(const Shape& s, int C, void* ws, const Ws16& w) {
   return a;
 }
 
+// Compute waves per chain workgroup (16 value columns each): the widest
+// slice whose grid of (b, v-head, slice) workgroups still covers every CU
+// of the current device.
+int chain_waves(const K16& a) {
+  static int ncu[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 4;
+  if (ncu[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    ncu[dev] = n;
+  }
+  const int64_t heads = static_cast<int64_t>(a.Hv) * a.B;
+  if (heads * (DK / 64) >= ncu[dev]) return 4;
+  if (heads * (DK / 32) >= ncu[dev]) return 2;
+  return 1;
+}
+
+// Calls f(std::integral_constant<int, NW>) for the chain workgroup shape nw.
+template <typename F>
+void with_chain_waves(int nw, F&& f) {
+  if (nw == 4)
+    f(std::integral_constant<int, 4>{});
+  else if (nw == 2)
+    f(std::integral_constant<int, 2>{});
+  else
+    f(std::integral_constant<int, 1>{});
+}
+
+// Grid of a chain launch with NW compute waves per workgroup.
+dim3 chain_grid(const K16& a, int nw) { return dim3(static_cast<unsigned>(DK / (16 * nw) * a.Hv * a.B)); }
+
 template <int C>
 hipError_t prep16(const K16& a, hipStream_t st) {
   ProfScope ps("chunk_prep", st);
@@ -3061,15 +3106,20 @@ hipError_t prep16(const K16& a, hipStream_t st) {
 template <int C, typename TO, bool WO, bool SH>
 hipError_t chain16(const K16& a, hipStream_t st) {
   ProfScope ps(WO ? (SH ? "chunk_fwd_save" : "chunk_fwd") : "chunk_states", st);
-  hipLaunchKernelGGL((chain16_kernel<C, TO, WO, SH>), dim3(static_cast<unsigned>(2 * a.Hv * a.B)), dim3(64 * (NCW + 1)),
-                     0, st, a);
+  with_chain_waves(chain_waves(a), [&](auto nw) {
+    constexpr int NW = decltype(nw)::value;
+    hipLaunchKernelGGL((chain16_kernel<C, TO, WO, SH, NW>), chain_grid(a, NW), dim3(64 * (NW + 1)), 0, st, a);
+  });
   return hipGetLastError();
 }
 
 template <int C, typename TO>
 hipError_t dh16(const K16& a, hipStream_t st) {
   ProfScope ps("chunk_dh", st);
-  hipLaunchKernelGGL((dh16_kernel<C, TO>), dim3(static_cast<unsigned>(2 * a.Hv * a.B)), dim3(64 * (NCW + 1)), 0, st, a);
+  with_chain_waves(chain_waves(a), [&](auto nw) {
+    constexpr int NW = decltype(nw)::value;
+    hipLaunchKernelGGL((dh16_kernel<C, TO, NW>), chain_grid(a, NW), dim3(64 * (NW + 1)), 0, st, a);
+  });
   return hipGetLastError();
 }
 
@@ -3173,8 +3223,10 @@ hipError_t fwd_cw(const Shape& s, const ChunkFwdArgs& x, void* ws, hipStream_t s
     if (e != hipSuccess) return e;
   }
   ProfScope ps("chunk_fwd_cw", st);
-  hipLaunchKernelGGL((cwchain16_kernel<C, TO, true, false>), dim3(static_cast<unsigned>(2 * a.Hv * a.B)),
-                     dim3(64 * (NCW + 1)), 0, st, a);
+  with_chain_waves(chain_waves(a), [&](auto nw) {
+    constexpr int NW = decltype(nw)::value;
+    hipLaunchKernelGGL((cwchain16_kernel<C, TO, true, false, NW>), chain_grid(a, NW), dim3(64 * (NW + 1)), 0, st, a);
+  });
   return hipGetLastError();
 }
 
@@ -3221,7 +3273,7 @@ hipError_t bwd_cw(const Shape& s, const ChunkBwdArgs& x, void* ws, hipStream_t s
   a.dht = x.dht;
   a.dh0 = x.dh0;
   a.pkimg = static_cast<char*>(ws) + w.pkimg;
-  const dim3 chains(static_cast<unsigned>(2 * a.Hv * a.B));
+  const int nw = chain_waves(a);
   {
     ProfScope ps("chunk_prep_cw", st);
     hipLaunchKernelGGL((cwprep16_kernel<C>), dim3(a.NC, a.Hv, static_cast<unsigned>(a.B)), dim3(512), 0, st, a);
@@ -3230,13 +3282,19 @@ hipError_t bwd_cw(const Shape& s, const ChunkBwdArgs& x, void* ws, hipStream_t s
   }
   {
     ProfScope ps("chunk_states_cw", st);
-    hipLaunchKernelGGL((cwchain16_kernel<C, bf16_t, false, true>), chains, dim3(64 * (NCW + 1)), 0, st, a);
+    with_chain_waves(nw, [&](auto w) {
+      constexpr int NW = decltype(w)::value;
+      hipLaunchKernelGGL((cwchain16_kernel<C, bf16_t, false, true, NW>), chain_grid(a, NW), dim3(64 * (NW + 1)), 0, st, a);
+    });
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
     ProfScope ps("chunk_dh_cw", st);
-    hipLaunchKernelGGL((cwdh16_kernel<C>), chains, dim3(64 * (NCW + 1)), 0, st, a);
+    with_chain_waves(nw, [&](auto w) {
+      constexpr int NW = decltype(w)::value;
+      hipLaunchKernelGGL((cwdh16_kernel<C, NW>), chain_grid(a, NW), dim3(64 * (NW + 1)), 0, st, a);
+    });
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -103,6 +103,22 @@ def test_chunked_vjp_group_launches(B, T, Hk, Hv, C):
     check_bwd(x, "bf16", dht=dht, heads=[(0, 0), (B - 1, Hk - 1)], algo=("chunked", C))
 
 
+@pytest.mark.parametrize("cw", [False, True])
+@pytest.mark.parametrize("B", [1, 2, 4])
+def test_chain_slice_widths(B, cw):
+    """The chain kernels' value slice follows the grid: on a 256-CU GPU,
+    Hv=32 takes one compute wave per workgroup (16 columns, 8 workgroups
+    per v-head) at B=1, two at B=2 and four at B=4.  Forward and VJP (scalar
+    and channelwise gates, ragged last chunk, h0 and dht nonzero) on sampled
+    (b, k-head) groups against the oracle."""
+    Hk, Hv, T = 16, 32, 200
+    x = make_inputs(3200 + B + 10 * cw, B, T, Hk, Hv, 128, 128, io_dtype="bf16", h0_std=0.02, channelwise=cw)
+    dht = (0.1 * np.random.default_rng(B + 10 * cw).standard_normal((B, Hv, 128, 128))).astype(np.float32)
+    heads = [(0, 0), (B - 1, Hk - 1)]
+    check_fwd(x, "bf16", h0=True, heads=heads, algo=("chunked", 64), cw=cw)
+    check_bwd(x, "bf16", cw=cw, dht=dht, heads=heads, algo=("chunked", 64))
+
+
 @pytest.mark.parametrize("Hk,Hv", [(2, 8), (1, 3)])
 def test_chunked_vjp_split_group(Hk, Hv):
     """The gradient work of every v-head in one launch with the epilogue
