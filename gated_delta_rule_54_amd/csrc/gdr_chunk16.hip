@@ -369,16 +369,24 @@ __device__ __forceinline__ void store_strip_buf(rsrc_t r, uint32_t voff, uint32_
 }
 
 // Chain workgroup -> (b, v-head, value slice), nsl slices per v-head.
-// Workgroups are dealt to the eight XCDs round robin; the remap puts the
-// nsl * Hv / Hk workgroups that read one key image (and the nsl that read
-// one chunk image) on the same XCD, so they share its L2.
+// Workgroups are dealt to the eight XCDs round robin.  The remap keeps the
+// gs = nsl * Hv / Hk workgroups of a (b, k-head) group, which read one key
+// image (and the nsl that read one chunk image), on one XCD, so they share
+// its L2, and deals the groups to the XCDs in turn, so every XCD holds an
+// eighth of every sequence's groups (a ragged batch's long sequences do not
+// pile onto one XCD).
 struct ChainPos {
   int slice, hv, kh;
   int64_t b;
 };
 __device__ __forceinline__ ChainPos chain_pos(const K16& a, int nsl) {
   const int nb = gridDim.x, l0 = blockIdx.x;
-  const int lg = (nb % 8 == 0) ? (l0 % 8) * (nb / 8) + l0 / 8 : l0;
+  const int gs = nsl * (a.Hv / a.Hk);
+  int lg = l0;
+  if (nb % (8 * gs) == 0) {
+    const int x = l0 % 8, slot = l0 / 8;  // XCD, and the workgroup's place in its list
+    lg = (x + 8 * (slot / gs)) * gs + slot % gs;
+  }
   ChainPos p;
   p.slice = lg % nsl;
   p.hv = (lg / nsl) % a.Hv;
