@@ -10,6 +10,7 @@
 //            writes the chunk's operands as fp16 "images": byte-exact copies
 //            of the padded LDS tiles the other kernels read.
 //              key image   per (b, k-head, chunk):  Kn [C][136] | Qn [C][136]
+//                          (columns in chained-fragment order: see key_unit)
 //              chunk image per (b, v-head, chunk):  gam | lam | beta | log2(e) G
 //                          (4 x C fp32) | T | P, each C x C tile [C][C+8]
 //            Normalisation and gate math thus happen once per chunk instead
@@ -17,20 +18,22 @@
 //            transposed (Kn^T, Qn^T, T^T, P^T) read it from the row-major
 //            copy with ds_read_b64_tr_b16, so the images hold each tile once
 //            and forward and VJP share one image format.
-//   chain16  per (b, v-head, 64-column value half): the sequential pass over
-//            chunks.  Wave w owns a 16-column strip of the state in MFMA
+//   chain16  per (b, v-head, value slice of 16, 32 or 64 columns): the
+//            sequential pass over chunks.  Wave w owns a 16-column strip of the state in MFMA
 //            accumulators.  Each chunk's images are copied into one of two LDS
 //            buffers by buffer_load_dwordx4 ... lds (no registers, no ALU)
 //            while the previous chunk computes; one barrier per chunk.
 //   dh16     the reverse pass carrying dH, same structure.
-//   grad16   per (b, v-head, chunk), parallel: every remaining gradient.
+//   grad16   per (b, k-head, chunk), parallel: every remaining gradient, the
+//            k-head's v-heads in turn.
 //
 // Chained operands: a C x 16 (or 128 x 16) strip held in accumulators is fed
 // back as the B operand of the next product that contracts over its rows by
 // relabelling that product's k index, so that lane group g supplies rows
 // {4g..4g+3, 16+4g..16+4g+3} of each 32-row block - exactly the rows its
 // accumulators hold.  The LDS-side A operand is read with the same
-// relabelling (two 8-byte reads per fragment).
+// relabelling: one 16-byte read per fragment from the key images, which are
+// stored in that order, two 8-byte reads from T and P.
 //
 // Global traffic of the chain kernels goes through buffer resources whose
 // extent ends at the chunk's last valid row: loads past it return 0 and
