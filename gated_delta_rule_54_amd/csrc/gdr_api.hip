@@ -66,7 +66,15 @@ int chunk_of(const gdr_problem* p) { return p->chunk_size ? p->chunk_size : 64; 
 
 constexpr bool kChunkedBackward = true;
 
-// SEQUENTIAL or CHUNKED for this call; CHUNKED needs a scalar gate.
+// Shortest T at which AUTO takes the chunked kernels: below it the
+// sequential kernels' per-token cost is under the chunked pipeline's fixed
+// cost (measured on MI355X, HIP events, B in {1, 4, 8}: forward 16 vs 19-26
+// us sequential against chunked at T = 8, 26-32 vs 19-27 at T = 16; scalar
+// VJP 34-50 vs 39-57 at T = 4, 38-59 vs 54-78 at T = 8; channelwise VJP
+// 66-76 vs 68-78 at T = 8, 117-134 vs 69-79 at T = 16).
+constexpr int kAutoChunkedFwdT = 12, kAutoChunkedBwdT = 6, kAutoChunkedBwdTChannelwise = 10;
+
+// SEQUENTIAL or CHUNKED for this call.
 gdr_status resolve_algo(const gdr_problem* p, bool backward, int* algo, bool ragged = false) {
   // channelwise gates: chunked kernels on the fp16 matrix-core path only
   // (bf16 io, Dk = 128, C >= 32).  Ragged batches: the chunked kernels on
@@ -79,7 +87,9 @@ gdr_status resolve_algo(const gdr_problem* p, bool backward, int* algo, bool rag
     if (!chunk_ok) return GDR_ERR_UNSUPPORTED;
     *algo = GDR_ALGO_CHUNKED;
   } else if (p->algo == GDR_ALGO_AUTO) {
-    if (chunk_ok && (p->T > 64 || !seq_ok)) *algo = GDR_ALGO_CHUNKED;
+    const int64_t t_min = !backward ? kAutoChunkedFwdT
+                          : (p->flags & GDR_CHANNELWISE) ? kAutoChunkedBwdTChannelwise : kAutoChunkedBwdT;
+    if (chunk_ok && (p->T >= t_min || !seq_ok)) *algo = GDR_ALGO_CHUNKED;
     else if (seq_ok) *algo = GDR_ALGO_SEQUENTIAL;
     else return GDR_ERR_UNSUPPORTED;
   } else {
@@ -87,6 +97,25 @@ gdr_status resolve_algo(const gdr_problem* p, bool backward, int* algo, bool rag
     *algo = GDR_ALGO_SEQUENTIAL;
   }
   return GDR_OK;
+}
+
+// Whether gdr_forward with GDR_SAVE_CHUNKS leaves its chunks for the VJP of
+// problem p: the forward's algorithm is the chunked one on its fp16 path with
+// a scalar gate.  AUTO's forward and backward can choose different
+// algorithms for one T, so the backward honours the flag only where this
+// holds (elsewhere both calls ignore it).
+bool forward_keeps_chunks(const gdr_problem* p, bool ragged = false) {
+  int algo;
+  if (resolve_algo(p, false, &algo, ragged) != GDR_OK) return false;
+  const Shape s = shape_of(p);
+  return algo == GDR_ALGO_CHUNKED && !s.channelwise && gdr::chunk_uses_f16(s, chunk_of(p));
+}
+
+// The shape of a backward call: GDR_SAVE_CHUNKS only where the forward keeps chunks.
+Shape backward_shape(const gdr_problem* p, bool ragged = false) {
+  Shape s = shape_of(p);
+  if (s.save_chunks && !forward_keeps_chunks(p, ragged)) s.save_chunks = false;
+  return s;
 }
 
 // ---- workspace plans: byte offsets of each carved buffer -----------------
@@ -196,8 +225,7 @@ gdr_status gdr_keeps_chunks(const gdr_problem* p, int* keeps) {
   if (!keeps) return GDR_ERR_NULL_ARG;
   int algo;
   if ((st = resolve_algo(p, false, &algo)) != GDR_OK) return st;
-  const Shape s = shape_of(p);
-  *keeps = (algo == GDR_ALGO_CHUNKED && !s.channelwise && gdr::chunk_uses_f16(s, chunk_of(p))) ? 1 : 0;
+  *keeps = forward_keeps_chunks(p) ? 1 : 0;
   return GDR_OK;
 }
 
@@ -207,7 +235,7 @@ gdr_status gdr_backward_workspace(const gdr_problem* p, size_t* bytes) {
   if (!bytes) return GDR_ERR_NULL_ARG;
   int algo;
   if ((st = resolve_algo(p, true, &algo)) != GDR_OK) return st;
-  const Shape s = shape_of(p);
+  const Shape s = backward_shape(p);
   *bytes = (s.B == 0 || s.T == 0) ? 0
            : algo == GDR_ALGO_CHUNKED ? gdr::chunk_bwd_workspace(s, chunk_of(p)) : plan_seq_bwd(s).total;
   return GDR_OK;
@@ -259,7 +287,7 @@ gdr_status backward_impl(const gdr_problem* p, const int64_t* cu, bool ragged, c
                          void* ws, size_t ws_bytes, void* hip_stream) {
   gdr_status st = check_problem(p);
   if (st != GDR_OK) return st;
-  const Shape s = shape_of(p);
+  const Shape s = backward_shape(p, ragged);
   const bool empty = s.B == 0 || s.T == 0;
   if (!empty && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
     return GDR_ERR_NULL_ARG;

@@ -89,7 +89,10 @@ typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
  *     accumulation (Dk = 128, chunk_size 32 or 64), every other shape fp32
  *     matrix-core operands.  Channelwise gate: bf16 io, Dk = 128,
  *     chunk_size 32 or 64 only (see below).
- *   AUTO: CHUNKED when supported and T > 64, else SEQUENTIAL.
+ *   AUTO: CHUNKED when supported and T is at least 12 (gdr_forward), 6
+ *     (gdr_backward) or 10 (gdr_backward with GDR_CHANNELWISE), else
+ *     SEQUENTIAL: below those lengths the sequential kernels are the faster
+ *     of the two on MI355X.
  *
  * Range of the fp16 chunked path.  Its matrix-core operands (normalised
  * q / k, v and dout rows, T = (I + A)^-1, the chunk states it keeps) are
@@ -142,8 +145,8 @@ typedef struct gdr_problem {
  * Dk = Dv = 128 and chunk_size 32 or 64 (else GDR_ERR_UNSUPPORTED); its VJP
  * forms each chunk's gradients from the chunk states the chunk chains store,
  * the per-channel decay carried inside the chunk-local sums (matrix cores
- * below the diagonal blocks, exact fp32 sums on them).  AUTO picks the
- * chunked kernels there when T > 64. */
+ * below the diagonal blocks, matrix cores or exact fp32 sums on them).
+ * AUTO picks the chunked kernels there from the lengths given above. */
 
 /* *keeps = 1 when GDR_SAVE_CHUNKS takes effect for problem *p (whether or
  * not the flag is set in p->flags), i.e. when gdr_forward with the flag

@@ -142,7 +142,8 @@ def test_channelwise_chunked_support():
     st, n = fwd_ws(prob(algo=0, **cw))
     assert st == 0 and n > 0                                      # AUTO -> chunked
     assert bwd_ws(prob(algo=0, **cw)) == bwd_ws(prob(algo=2, **cw))
-    assert fwd_ws(prob(algo=0, **dict(cw, T=64))) == (0, 0)       # short: sequential
+    assert fwd_ws(prob(algo=0, **dict(cw, T=11))) == (0, 0)       # short: sequential
+    assert fwd_ws(prob(algo=0, **dict(cw, T=12)))[1] > 0          # AUTO's shortest chunked forward
     assert fwd_ws(prob(algo=0, flags=3, T=256)) == (0, 0)         # fp32: sequential
 
 
@@ -223,9 +224,11 @@ def keeps(p):
 
 
 @pytest.mark.parametrize("kw,kept", [
-    (dict(B=4, T=4096, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=0), 1),        # AUTO, T > 64: chunked fp16
+    (dict(B=4, T=4096, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=0), 1),        # AUTO: chunked fp16
     (dict(B=4, T=4096, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=2, chunk_size=32), 1),
-    (dict(B=1, T=64, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=0), 0),          # AUTO picks sequential
+    (dict(B=1, T=64, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=0), 1),
+    (dict(B=1, T=12, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=0), 1),          # AUTO's shortest chunked forward
+    (dict(B=1, T=11, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=0), 0),          # AUTO picks sequential
     (dict(B=1, T=8, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=0), 0),
     (dict(B=1, T=512, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, algo=1), 0),         # sequential
     (dict(B=1, T=512, Hk=2, Hv=4, Dk=128, Dv=128, io_dtype=0, algo=2), 0),           # fp32 io
@@ -250,7 +253,8 @@ def test_saved_chunks_only_where_kept():
     """Where the library ignores GDR_SAVE_CHUNKS, the forward with and without
     the flag needs the same workspace and the binding keeps nothing; where it
     honours it, the forward needs the backward's workspace."""
-    for kw in (dict(T=64, algo=0), dict(T=512, algo=1), dict(T=200, algo=2, io_dtype=0, Dk=128, Dv=128),
+    # AUTO at T = 8 and 10: the forward runs the sequential kernels, the backward the chunked ones
+    for kw in (dict(T=8, algo=0), dict(T=10, algo=0), dict(T=512, algo=1), dict(T=200, algo=2, io_dtype=0, Dk=128, Dv=128),
                dict(T=200, algo=2, flags=3, Dk=128, Dv=128, io_dtype=1)):
         base = dict(B=1, Hk=16, Hv=32, Dk=128, Dv=128, io_dtype=1, flags=1)
         base.update(kw)

@@ -254,18 +254,19 @@ def test_fp16_range_of_the_chunked_path():
 
 # ---------------------------------------------------------------- saved chunks
 
-@pytest.mark.parametrize("case", ["auto_T64", "sequential", "fp32_chunked", "channelwise"])
+@pytest.mark.parametrize("case", ["auto_T8", "sequential", "fp32_chunked", "channelwise"])
 def test_save_for_backward_where_ignored(case):
     """save_for_backward=True on problems where the library keeps no chunks
-    (AUTO at T=64 picks the sequential kernels; the sequential algorithm;
-    fp32 io; the channelwise gate): the backward runs the stateless VJP and
-    gives exactly what it gives without the flag."""
-    T = 64 if case == "auto_T64" else 130
+    (AUTO's forward at T=8 picks the sequential kernels, its backward the
+    chunked ones; the sequential algorithm; fp32 io; the channelwise gate):
+    the backward runs the stateless VJP and gives exactly what it gives
+    without the flag."""
+    T = 8 if case == "auto_T8" else 130
     io = "f32" if case == "fp32_chunked" else "bf16"
     cw = case == "channelwise"
     x = make_inputs(31, 1, T, 2, 4, 128, 128, io_dtype=io, channelwise=cw, h0_std=0.02)
     t = to_dev(x, io)
-    kw = dict(algo={"auto_T64": "auto", "sequential": "sequential"}.get(case, "chunked"), channelwise=cw)
+    kw = dict(algo={"auto_T8": "auto", "sequential": "sequential"}.get(case, "chunked"), channelwise=cw)
     o, ht, sv = gdr.gdr_forward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], save_for_backward=True, **kw)
     assert not sv.kept
     g1 = gdr.gdr_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"], t["do"], saved=sv, **kw)
