@@ -68,11 +68,15 @@ constexpr bool kChunkedBackward = true;
 
 // Shortest T at which AUTO takes the chunked kernels: below it the
 // sequential kernels' per-token cost is under the chunked pipeline's fixed
-// cost (measured on MI355X, HIP events, B in {1, 4, 8}: forward 16 vs 19-26
-// us sequential against chunked at T = 8, 26-32 vs 19-27 at T = 16; scalar
-// VJP 34-50 vs 39-57 at T = 4, 38-59 vs 54-78 at T = 8; channelwise VJP
-// 66-76 vs 68-78 at T = 8, 117-134 vs 69-79 at T = 16).
-constexpr int kAutoChunkedFwdT = 12, kAutoChunkedBwdT = 6, kAutoChunkedBwdTChannelwise = 10;
+// cost.  Measured on MI355X (HIP events, B in {1, 4, 8}, Hv = 32, D = 128):
+// on the fp16 path the forward takes 16 vs 19-26 us sequential against
+// chunked at T = 8 and 26-32 vs 19-27 at T = 16; the scalar VJP 34-50 vs
+// 39-57 at T = 4 and 54-78 vs 38-59 at T = 8; the channelwise VJP 66-76 vs
+// 68-78 at T = 8 and 117-134 vs 69-79 at T = 16.  On the fp32 path (fp32 io
+// or D = 16) the chunked pipeline costs more: forward 43 vs 63 us at T = 32,
+// 82-98 vs 64-94 at T = 64; VJP 182-205 vs 206-260 at T = 32, 368-405 vs
+// 214-276 at T = 64.
+constexpr int kAutoChunkedFwdT = 12, kAutoChunkedBwdT = 6, kAutoChunkedBwdTChannelwise = 10, kAutoChunkedF32T = 64;
 
 // SEQUENTIAL or CHUNKED for this call.
 gdr_status resolve_algo(const gdr_problem* p, bool backward, int* algo, bool ragged = false) {
@@ -87,8 +91,10 @@ gdr_status resolve_algo(const gdr_problem* p, bool backward, int* algo, bool rag
     if (!chunk_ok) return GDR_ERR_UNSUPPORTED;
     *algo = GDR_ALGO_CHUNKED;
   } else if (p->algo == GDR_ALGO_AUTO) {
-    const int64_t t_min = !backward ? kAutoChunkedFwdT
-                          : (p->flags & GDR_CHANNELWISE) ? kAutoChunkedBwdTChannelwise : kAutoChunkedBwdT;
+    const int64_t t_min = !f16                          ? kAutoChunkedF32T
+                          : !backward                    ? kAutoChunkedFwdT
+                          : (p->flags & GDR_CHANNELWISE) ? kAutoChunkedBwdTChannelwise
+                                                         : kAutoChunkedBwdT;
     if (chunk_ok && (p->T >= t_min || !seq_ok)) *algo = GDR_ALGO_CHUNKED;
     else if (seq_ok) *algo = GDR_ALGO_SEQUENTIAL;
     else return GDR_ERR_UNSUPPORTED;

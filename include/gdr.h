@@ -90,9 +90,9 @@ typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
  *     matrix-core operands.  Channelwise gate: bf16 io, Dk = 128,
  *     chunk_size 32 or 64 only (see below).
  *   AUTO: CHUNKED when supported and T is at least 12 (gdr_forward), 6
- *     (gdr_backward) or 10 (gdr_backward with GDR_CHANNELWISE), else
- *     SEQUENTIAL: below those lengths the sequential kernels are the faster
- *     of the two on MI355X.
+ *     (gdr_backward) or 10 (gdr_backward with GDR_CHANNELWISE) on the fp16
+ *     matrix-core path, 64 on the fp32 one, else SEQUENTIAL: below those
+ *     lengths the sequential kernels are the faster of the two on MI355X.
  *
  * Range of the fp16 chunked path.  Its matrix-core operands (normalised
  * q / k, v and dout rows, T = (I + A)^-1, the chunk states it keeps) are
