@@ -45,14 +45,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # demangled kernel name pattern -> library timing name
 KERNELS = [
     (r"cwprep16_kernel", "chunk_prep_cw"),
-    (r"cwchain16_kernel<\d+, [^,]+, true, false>", "chunk_fwd_cw"),
-    (r"cwchain16_kernel<\d+, [^,]+, false, true>", "chunk_states_cw"),
+    (r"cwchain16_kernel<\d+, [^,]+, true, false(?:, \d+)?>", "chunk_fwd_cw"),
+    (r"cwchain16_kernel<\d+, [^,]+, false, true(?:, \d+)?>", "chunk_states_cw"),
     (r"cwdh16_kernel", "chunk_dh_cw"),
     (r"cwgrad16_kernel", "chunk_grad_cw"),
     (r"prep16_kernel", "chunk_prep"),
-    (r"chain16_kernel<\d+, [^,]+, true, false>", "chunk_fwd"),
-    (r"chain16_kernel<\d+, [^,]+, true, true>", "chunk_fwd_save"),
-    (r"chain16_kernel<\d+, [^,]+, false, true>", "chunk_states"),
+    (r"chain16_kernel<\d+, [^,]+, true, false(?:, \d+)?>", "chunk_fwd"),
+    (r"chain16_kernel<\d+, [^,]+, true, true(?:, \d+)?>", "chunk_fwd_save"),
+    (r"chain16_kernel<\d+, [^,]+, false, true(?:, \d+)?>", "chunk_states"),
     (r"dh16_kernel", "chunk_dh"),
     (r"grad16_kernel", "chunk_grad"),
     (r"epilogue128_kernel", "bwd_epilogue"),
