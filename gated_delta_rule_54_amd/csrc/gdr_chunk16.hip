@@ -371,13 +371,70 @@ __device__ __forceinline__ void store_strip_buf(rsrc_t r, uint32_t voff, uint32_
     }
 }
 
+// The sequence of rank r when the sequences of a ragged batch of at most 64
+// are ordered by decreasing length (equal lengths by index).  Lane j holds
+// sequence j's length; each lane counts the sequences ahead of its own.
+constexpr int kMaxRankedSeqs = 64;
+__device__ __forceinline__ int64_t seq_by_length(const K16& a, int r) {
+  const int lane = lane_id(), nb = static_cast<int>(a.B);
+  const int len = lane < nb ? static_cast<int>(seq_span(a, lane).len) : -1;
+  int rank = 0;
+  for (int j = 0; j < nb; ++j) {
+    const int lj = __builtin_amdgcn_readlane(len, j);
+    rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
+  }
+  const unsigned long long m = __ballot(lane < nb && rank == r);
+  return m ? __builtin_ctzll(m) : r;  // exactly one lane matches for 0 <= r < B
+}
+
+// Chunk c of sequence b for the workgroup of an (NC, heads, B) grid.
+// Without a ragged batch, or with more than 64 sequences, block (x, z) is
+// chunk x of sequence z (possibly past its end).  A ragged batch of at most
+// 64 numbers its chunks in sequence order and block (x, z) takes chunk
+// x + NC z of that list: the blocks past the batch's last chunk are then
+// the last ones dispatched (they get c = NC, past every sequence's end)
+// instead of holding a CU between real chunks, which costs the gradient
+// kernels (one workgroup per CU) about 15% on a ragged batch of half-empty
+// rows; the prep kernels, four and two workgroups per CU, keep the plain
+// order, which measured slightly faster for them.
+struct ChunkPos {
+  int c;
+  int64_t b;
+};
+__device__ __forceinline__ ChunkPos chunk_pos(const K16& a, int C) {
+  ChunkPos p{static_cast<int>(blockIdx.x), static_cast<int64_t>(blockIdx.z)};
+  if (!a.cu || a.B > kMaxRankedSeqs) return p;
+  const int lane = lane_id(), nb = static_cast<int>(a.B);
+  const int nch = lane < nb ? static_cast<int>((seq_span(a, lane).len + C - 1) / C) : 0;
+  int incl = nch;  // chunks of sequences 0 .. lane
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  const int excl = incl - nch;
+  const int idx = static_cast<int>(blockIdx.x) + a.NC * static_cast<int>(blockIdx.z);
+  const unsigned long long m = __ballot(lane < nb && excl <= idx && idx < incl);
+  if (!m) {
+    p.c = a.NC;
+    p.b = 0;
+    return p;
+  }
+  const int bb = __builtin_ctzll(m);
+  p.b = bb;
+  p.c = idx - __builtin_amdgcn_readlane(excl, bb);
+  return p;
+}
+
 // Chain workgroup -> (b, v-head, value slice), nsl slices per v-head.
 // Workgroups are dealt to the eight XCDs round robin.  The remap keeps the
 // gs = nsl * Hv / Hk workgroups of a (b, k-head) group, which read one key
 // image (and the nsl that read one chunk image), on one XCD, so they share
 // its L2, and deals the groups to the XCDs in turn, so every XCD holds an
 // eighth of every sequence's groups (a ragged batch's long sequences do not
-// pile onto one XCD).
+// pile onto one XCD).  A ragged batch of at most 64 sequences takes them
+// longest first (the dispatch order follows the block index), so the chains
+// that end last are short ones.
 struct ChainPos {
   int slice, hv, kh;
   int64_t b;
@@ -394,6 +451,7 @@ __device__ __forceinline__ ChainPos chain_pos(const K16& a, int nsl) {
   p.slice = lg % nsl;
   p.hv = (lg / nsl) % a.Hv;
   p.b = (lg / nsl) / a.Hv;
+  if (a.cu && a.B <= kMaxRankedSeqs) p.b = seq_by_length(a, static_cast<int>(p.b));
   p.kh = p.hv / (a.Hv / a.Hk);
   return p;
 }
@@ -1168,8 +1226,9 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   const int tid0 = threadIdx.x, w0 = wave_id();
   // kSplit: blockIdx.y = v-head, each storing its own dq_hat / dk_hat rows
   // for the epilogue kernel; otherwise blockIdx.y = k-head
-  const int c = blockIdx.x, yy = blockIdx.y;
-  const int64_t b = blockIdx.z;
+  const ChunkPos cp = chunk_pos(a, C);
+  const int c = cp.c, yy = blockIdx.y;
+  const int64_t b = cp.b;
   // kGroup: one workgroup walks all v-heads of its k-head in order, with
   // the group sums of dq_hat / dk_hat kept in registers and the key image
   // loaded once
@@ -2406,8 +2465,9 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
   float (*sN)[NW][C] = reinterpret_cast<float (*)[NW][C]>(xb + 2 * C * LDQ);
 
   const int tid0 = threadIdx.x, w0 = wave_id();
-  const int c = blockIdx.x, kh = blockIdx.y;
-  const int64_t b = blockIdx.z;
+  const ChunkPos cp = chunk_pos(a, C);
+  const int c = cp.c, kh = blockIdx.y;
+  const int64_t b = cp.b;
   const int grp = a.Hv / a.Hk;
   const int64_t t0 = static_cast<int64_t>(c) * C;
   const SeqSpan sp = seq_span(a, b);

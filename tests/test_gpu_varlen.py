@@ -88,6 +88,18 @@ def test_ragged_chunked_vjp_group_launches():
     run_and_check([0, 1, 130, 200], "bf16", "chunked", 64, seed=7, Hk=32, Hv=64)
 
 
+@pytest.mark.parametrize("n,cw", [(64, False), (65, False), (64, True)])
+def test_ragged_chunked_many_sequences(n, cw):
+    """64 sequences, the most for which the kernels rank the chain
+    workgroups by length and number the gradient workgroups by the batch's
+    chunk list, and 65, which keep the plain block order: lengths 0 to 150
+    (empty, one-token, whole- and part-chunk sequences) on Hk=2, Hv=4."""
+    rng = np.random.default_rng(n)
+    lens = [int(x) for x in rng.integers(0, 151, size=n)]
+    lens[:4] = [0, 1, 64, 150]
+    run_and_check(lens, "bf16", "chunked", 64, cw=cw, seed=n)
+
+
 def test_ragged_bf16_outputs_benchmark_heads():
     """The ragged prefill leg's launch configuration: Hk=16, Hv=32, D=128,
     C=64, bf16 io and outputs, the forward saving its chunks for the VJP, on
