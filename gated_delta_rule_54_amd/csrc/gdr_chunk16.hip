@@ -1292,6 +1292,14 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     const int hv = hv0 + gi;
     f16x8 h0f[NTK / 2], dhf[NTK / 2];
     load_states(h0f, dhf, hv, w);
+    // fused gates: wave 0's lane r takes row r's pre-activation g and beta
+    // now, for the dg / dbeta it forms at the end of this v-head
+    float fgg = 0.f, fgb = 0.f;
+    if (a.fg && w == 0 && lane < L) {
+      const int64_t row = (sp.t0 + t0 + lane) * a.Hv + hv;
+      fgg = a.g[row];
+      fgb = a.beta[row];
+    }
     // Hs[j][i] <- strips (rows i of column j = jw)
     auto put_state = [&](const f16x8 (&f)[NTK / 2]) {
 #pragma unroll
@@ -1639,8 +1647,8 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       }
       if (r < L) {
         const int64_t row = (sp.t0 + t0 + r) * a.Hv + hv;
-        a.dg[row] = a.fg ? x * fg_dlog_alpha(a.g[row]) : x;
-        a.dbeta[row] = a.fg ? dB * fg_dbeta(a.beta[row]) : dB;
+        a.dg[row] = a.fg ? x * fg_dlog_alpha(fgg) : x;
+        a.dbeta[row] = a.fg ? dB * fg_dbeta(fgb) : dB;
       }
     }
   }
