@@ -30,6 +30,17 @@ total and average duration), and
     python -m gated_delta_rule_54_amd.profiling mfma DIR_M/m_results.db --md profiles/<name>.md
 
 the matrix-core busy fraction and executed matrix-core FLOPs per launch.
+
+and two runs of the same command with the wave-state counters (at most
+eight SQ counters a run)
+
+    rocprofv3 --pmc SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU \
+        SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_SCA -d DIR_S1 -o s -- python3 bench.py ...
+    rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_MFMA SQ_INSTS_SALU SQ_LDS_BANK_CONFLICT \
+        SQ_LDS_IDX_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES -d DIR_S2 -o s -- python3 bench.py ...
+    python -m gated_delta_rule_54_amd.profiling sq DIR_S1/s_results.db DIR_S2/s_results.db --md profiles/<name>.md
+
+give each kernel's wave time split by what its waves were doing.
 """
 
 import argparse
@@ -197,6 +208,56 @@ def mfma(args):
     print(text)
 
 
+def sq(args):
+    """Wave-state shares per kernel from SQ counter runs: each counter is
+    summed over the dispatch's counter instances and averaged over the
+    kernel's launches; the cycle counters share one unit (quad-cycles), so
+    ACTIVE_INST_* and WAIT_* over SQ_WAVE_CYCLES are the fractions of the
+    waves' resident time spent issuing that kind of instruction or waiting
+    (on memory, LDS or a barrier: WAIT_ANY; for an issue slot:
+    WAIT_INST_ANY).  The instruction counts are per launch."""
+    vals = collections.defaultdict(dict)
+    for db in args.dbs:
+        con = sqlite3.connect(db)
+        for (cn,) in con.execute("select distinct counter_name from pmc_events"):
+            for lab, (v, n) in per_kernel(db, cn).items():
+                if lab != "copy":
+                    vals[lab][cn] = (v, n)
+    cols = [("issuing", "SQ_ACTIVE_INST_ANY"), ("VALU", "SQ_ACTIVE_INST_VALU"), ("LDS", "SQ_ACTIVE_INST_LDS"),
+            ("VMEM", "SQ_ACTIVE_INST_VMEM"), ("scalar", "SQ_ACTIVE_INST_SCA"), ("waiting", "SQ_WAIT_ANY"),
+            ("waiting for issue", "SQ_WAIT_INST_ANY")]
+    lines = ["# Wave states per kernel launch (rocprofv3 SQ counters)", ""]
+    if args.command:
+        lines += ["Commands (from the repository root on one MI355X, library built):", "", "```", args.command,
+                  "```", ""]
+    lines += ["Shares of SQ_WAVE_CYCLES (the waves' resident time): issuing any instruction, issuing each "
+              "kind, waiting (memory, LDS, barriers), waiting for an issue slot.  Bank conflicts: "
+              "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (share of the LDS's active cycles lost to "
+              "conflicts).  Instructions: millions per launch over all waves.", "",
+              "| kernel | launches | " + " | ".join(c for c, _ in cols) +
+              " | LDS bank conflicts | VALU / LDS / MFMA / SALU instructions (M) |",
+              "|---|---:|" + "---:|" * (len(cols) + 2)]
+    for lab in sorted(vals):
+        d = vals[lab]
+        if "SQ_WAVE_CYCLES" not in d:
+            continue
+        wc = d["SQ_WAVE_CYCLES"][0]
+        row = [lab, str(d["SQ_WAVE_CYCLES"][1])]
+        for _, cn in cols:
+            row.append(f"{100.0 * d[cn][0] / wc:.0f}%" if cn in d and wc else "")
+        bc, la = d.get("SQ_LDS_BANK_CONFLICT"), d.get("SQ_LDS_IDX_ACTIVE")
+        row.append(f"{100.0 * bc[0] / la[0]:.0f}%" if bc and la and la[0] else "")
+        ins = [d.get(k) for k in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA", "SQ_INSTS_SALU")]
+        row.append(" / ".join(f"{x[0] / 1e6:.1f}" if x else "-" for x in ins))
+        lines.append("| " + " | ".join(row) + " |")
+    lines += ["", f"Kernel sources digest: `{src_digest()}`", ""]
+    text = "\n".join(lines)
+    if args.md:
+        with open(args.md, "w") as fh:
+            fh.write(text)
+    print(text)
+
+
 def trace(args):
     con = sqlite3.connect(args.db)
     rows = con.execute("select name, total_calls, total_duration, average, percentage from top_kernels "
@@ -256,8 +317,12 @@ def main():
     m.add_argument("--md", default=None)
     m.add_argument("--command", default="")
     m.add_argument("--simds", type=int, default=1024, help="SIMDs on the GPU (MI355X: 256 CUs x 4)")
+    q = sub.add_parser("sq")
+    q.add_argument("dbs", nargs="+")
+    q.add_argument("--md", default=None)
+    q.add_argument("--command", default="")
     args = ap.parse_args()
-    {"traffic": traffic, "trace": trace, "mfma": mfma}[args.cmd](args)
+    {"traffic": traffic, "trace": trace, "mfma": mfma, "sq": sq}[args.cmd](args)
 
 
 if __name__ == "__main__":
