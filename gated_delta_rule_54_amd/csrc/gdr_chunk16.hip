@@ -1401,23 +1401,24 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     put_strip_t(X0, dr);
     put_strip_t(X1b, dov);
     put_strip_t(X2b, u);
-    // This wave's shares of dbeta_r and dG_r (rows 16tr + 4g + e, summed over
-    // its 16 value columns) start the per-wave row sums sB / sG:
+    // This wave's shares of dbeta_r and dG_r (summed over its 16 value
+    // columns) start the per-wave row sums sB / sG:
     // dbeta_r = sum_j dRHS (V - gam Y);  dG_r = -beta gam sum_j dRHS Y + ...
+    // Lane c16 of group g sums row rs = 16 (k / 4) + 4 g + k % 4, its value
+    // k = 4 tr + e of the row sums below (k = c16 NT / 4).
+    const int ks = c16 * NT / 4, rs = 16 * (ks >> 2) + 4 * g + (ks & 3);
+    {
+      float vb[4 * NT], vy[4 * NT];
 #pragma unroll
-    for (int tr = 0; tr < NT; ++tr) {
-      const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * tr + 4 * g);
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
-      f32x4 rb, rg;
+      for (int tr = 0; tr < NT; ++tr)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        rb[e] = row16_sum(psb[tr][e]);
-        rg[e] = -bv[e] * gv[e] * row16_sum(psy[tr][e]);
-      }
-      if (c16 == 0) {
-        *reinterpret_cast<f32x4*>(&sB[w][16 * tr + 4 * g]) = rb;
-        *reinterpret_cast<f32x4*>(&sG[w][16 * tr + 4 * g]) = rg;
-      }
+        for (int e = 0; e < 4; ++e) {
+          vb[4 * tr + e] = psb[tr][e];
+          vy[4 * tr + e] = psy[tr][e];
+        }
+      const float sb = row16_scatter(vb), sy = row16_scatter(vy);
+      sB[w][rs] = sb;
+      sG[w][rs] = -bet[rs] * gam[rs] * sy;
     }
     __syncthreads();
 
@@ -1573,12 +1574,12 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     mma_rows<NT, C, kUpper, true>(dk, dPmT, LDC, Qs, LDK, 16 * w);
     mma_rows<NT, C, kFull, true>(dk, dAs, LDC, Ks, LDK, 16 * w);
     float gcx = 0.f;
+    float vx[4 * NT];  // this lane's terms of dG_r (rows 16rt + 4g + e), summed over the wave's 16 keys below
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
       const f32x4 gv = *reinterpret_cast<const f32x4*>(gam + 16 * rt + 4 * g);
       const f32x4 lv = *reinterpret_cast<const f32x4*>(lam + 16 * rt + 4 * g);
       const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * rt + 4 * g);
-      f32x4 rgx;
       const f16x4 qn4 = tr4k(Qs, LDK, 16 * rt + 4 * g, 16 * w);  // Qn[16rt + 4g + e][i2]
       const f16x4 kn4 = tr4k(Ks, LDK, 16 * rt + 4 * g, 16 * w);
 #pragma unroll
@@ -1587,15 +1588,12 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
         const float kn = static_cast<float>(kn4[e]);
         const float t3 = lv[e] * kn * x3[rt][e];
         gcx += t3;
-        rgx[e] = row16_sum(gv[e] * qn * x2[rt][e] - t3);
+        vx[4 * rt + e] = gv[e] * qn * x2[rt][e] - t3;
         dqv[rt][e] += dq[rt][e] + gv[e] * x2[rt][e];
         dkv[rt][e] += dk[rt][e] + lv[e] * x3[rt][e] - bv[e] * gv[e] * x1[rt][e];
       }
-      if (c16 == 0) {
-        f32x4* pg = reinterpret_cast<f32x4*>(&sG[w][16 * rt + 4 * g]);
-        *pg = *pg + rgx;
-      }
     }
+    sG[w][rs] += row16_scatter(vx);
     if constexpr (MODE == kSplit) {  // rows (b * T + t) * Hv + hv of [B * T * Hv][DK]; rows >= L dropped
       const uint32_t rowp = static_cast<uint32_t>(a.Hv) * DK * 4;
       const int64_t prow = (b * a.T + t0) * a.Hv + hv;
@@ -1670,18 +1668,18 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
           xk[rt][e] = static_cast<float>(k4[e]);
         }
       }
+      {
+        float v1[4 * NT], v3[4 * NT];
 #pragma unroll
-      for (int rt = 0; rt < NT; ++rt) {
+        for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float s1 = row16_sum(xq[rt][e] * dqv[rt][e]);
-          const float s3 = row16_sum(xk[rt][e] * dkv[rt][e]);
-          if (c16 == 0) {
-            const int r = 16 * rt + 4 * g + e;
-            sN[0][w][r] = s1;
-            sN[1][w][r] = s3;
+          for (int e = 0; e < 4; ++e) {
+            v1[4 * rt + e] = xq[rt][e] * dqv[rt][e];
+            v3[4 * rt + e] = xk[rt][e] * dkv[rt][e];
           }
-        }
+        const int ks = c16 * NT / 4, rs = 16 * (ks >> 2) + 4 * g + (ks & 3);  // the row lane c16 of group g sums
+        sN[0][w][rs] = row16_scatter(v1);
+        sN[1][w][rs] = row16_scatter(v3);
       }
       __syncthreads();
       if (tid < 2 * C) {

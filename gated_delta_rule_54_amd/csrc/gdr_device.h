@@ -88,4 +88,44 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// N (16 or 8) sums over the 16 lanes of a DPP row at once: lane j of the
+// row ends with the sum of every lane's v[j N / 16].  Recursive halving: at
+// each step a lane pairs with its mirror in the row, its mirror in the
+// half-row, its mirror in the quad, then its neighbour; the lane whose bit
+// (3, 2, 1, 0 of its row position) is set keeps the upper half of its
+// values, the other the lower, and each adds the half its partner gave up
+// (with N = 8 the neighbours, holding the same value, just add).  15 adds
+// and 30 selects for N = 16, against 64 adds for sixteen full row sums; the
+// order of additions is fixed.
+template <int H, int CTRL>
+__device__ __forceinline__ void row16_halve(const float* in, float* out, bool hi) {
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const float keep = hi ? in[k + H] : in[k];
+    const float give = hi ? in[k] : in[k + H];
+    out[k] = keep + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, give), CTRL, 0xf, 0xf,
+                                                                       true));
+  }
+}
+template <int N>
+__device__ __forceinline__ float row16_scatter(const float (&v)[N]) {
+  static_assert(N == 16 || N == 8, "16 or 8 values per lane");
+  const int j = threadIdx.x & 15;
+  float a[8], b[4], c[2];
+  if constexpr (N == 16) {
+    row16_halve<8, 0x140>(v, a, (j & 8) != 0);  // row_mirror: lane 15 - j
+    row16_halve<4, 0x141>(a, b, (j & 4) != 0);  // row_half_mirror: lane 7 - j in its half
+  } else {
+    row16_halve<4, 0x140>(v, b, (j & 8) != 0);
+  }
+  row16_halve<2, (N == 16 ? 0x1b : 0x141)>(b, c, (j & (N == 16 ? 2 : 4)) != 0);
+  float d[1];
+  row16_halve<1, (N == 16 ? 0xb1 : 0x1b)>(c, d, (j & (N == 16 ? 1 : 2)) != 0);
+  if constexpr (N == 16) {
+    return d[0];
+  } else {  // quad_perm [1, 0, 3, 2]: the neighbour holds the same value
+    return d[0] + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, d[0]), 0xb1, 0xf, 0xf, true));
+  }
+}
+
 }  // namespace gdr
