@@ -352,16 +352,34 @@ __device__ __forceinline__ void load_strip(f32x4 (&x)[NT], const bf16_t* base, i
     }
 }
 
+// With ON, x passes through an empty asm statement, so the compiler cannot
+// treat what is derived from it as loop invariant: addresses built from the
+// lane index inside a loop are rebuilt there instead of being held in
+// registers across the whole loop body.
+template <bool ON>
+__device__ __forceinline__ int opaque_v(int x) {
+  if constexpr (ON) asm volatile("" : "+v"(x));
+  return x;
+}
+template <bool ON>
+__device__ __forceinline__ int opaque_s(int x) {
+  if constexpr (ON) asm volatile("" : "+s"(x));
+  return x;
+}
+
 // Stores this lane's strip rows 16tr + 4g + e as TO through buffer r (rows
 // rowb bytes apart, voff = byte offset of row 4g at the lane's column);
-// rows past the buffer end are dropped.
+// rows past the buffer end are dropped.  voff is held as is, so each store
+// adds one uniform row offset to it (left free, the compiler folds the
+// lane's row into a multiply by rowb at every store).
 template <typename TO, int NT>
 __device__ __forceinline__ void store_strip_buf(rsrc_t r, uint32_t voff, uint32_t rowb, const f32x4 (&x)[NT]) {
+  const uint32_t v0 = static_cast<uint32_t>(opaque_v<true>(static_cast<int>(voff)));
 #pragma unroll
   for (int tr = 0; tr < NT; ++tr)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t off = voff + (16 * tr + e) * rowb;
+      const uint32_t off = v0 + (16 * tr + e) * rowb;
       if constexpr (std::is_same_v<TO, float>) {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[tr][e]), r, off, 0, 0);
       } else {
@@ -1180,22 +1198,6 @@ __device__ __forceinline__ void mma_rows(f32x4 (&acc)[NO], const _Float16* A, in
 }
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-// With ON, x passes through an empty asm statement, so the compiler cannot
-// treat what is derived from it as loop invariant: addresses built from the
-// lane index inside a loop are rebuilt there instead of being held in
-// registers across the whole loop body.
-template <bool ON>
-__device__ __forceinline__ int opaque_v(int x) {
-  if constexpr (ON) asm volatile("" : "+v"(x));
-  return x;
-}
-template <bool ON>
-__device__ __forceinline__ int opaque_s(int x) {
-  if constexpr (ON) asm volatile("" : "+s"(x));
-  return x;
-}
-
 
 enum GradMode { kOnly = 0, kSplit = 1, kGroup = 2 };
 
@@ -2600,12 +2602,16 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
       }
       store_strip_buf<TO, NT>(ovr, 4 * g * rowo + (hv * DK + jw) * static_cast<uint32_t>(sizeof(TO)), rowo, dvs);
     }
+    // lane c16 of group g sums row rs = 16 (k / 4) + 4 g + k % 4 of the
+    // row sums over the wave's 16 columns, its value k = 4 tr + e (k = c16 NT / 4)
+    const int ks = c16 * NT / 4, rs = 16 * (ks >> 2) + 4 * g + (ks & 3);
+    {
+      float vb[4 * NT];
 #pragma unroll
-    for (int tr = 0; tr < NT; ++tr) {
-      f32x4 rb;
+      for (int tr = 0; tr < NT; ++tr)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rb[e] = row16_sum(psb[tr][e] * dr[tr][e]);
-      if (c16 == 0) *reinterpret_cast<f32x4*>(&sB[w][16 * tr + 4 * g]) = rb;
+        for (int e = 0; e < 4; ++e) vb[4 * tr + e] = psb[tr][e] * dr[tr][e];
+      sB[w][rs] = row16_scatter(vb);
     }
     put_strip_t(X0, dr);
     put_strip_t(X1b, dov);
@@ -2936,17 +2942,17 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
 
     // ---- dk, dG, dg, dbeta of this v-head
     float dG[NT][4];
+    float vb[4 * NT];  // this lane's terms of dbeta_r, summed over the wave's 16 keys below
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
       const f32x4 bv = *reinterpret_cast<const f32x4*>(bet + 16 * rt + 4 * g);
       const f16x4 q4 = tr4(Qs, LDK, 16 * rt + 4 * g, 16 * w);
       const f16x4 k4 = tr4(Ks, LDK, 16 * rt + 4 * g, 16 * w);
-      f32x4 rb;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rt + 4 * g + e;
         const float qn = static_cast<float>(q4[e]), kn = static_cast<float>(k4[e]);
-        rb[e] = row16_sum(kn * ta[rt][e]);
+        vb[4 * rt + e] = kn * ta[rt][e];
         dkp[rt][e] += bv[e] * ta[rt][e];
         float x = qn * dq[rt][e] + kn * (dkp[rt][e] - dkm[rt][e]);
         if (r == L - 1) x += kl3 + eGC[i2] * hd;
@@ -2954,11 +2960,8 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
         dqv[rt][e] += dq[rt][e];
         dkv[rt][e] += dkp[rt][e] + dkm[rt][e];
       }
-      if (c16 == 0) {
-        f32x4* pb = reinterpret_cast<f32x4*>(&sB[w][16 * rt + 4 * g]);
-        *pb = *pb + rb;
-      }
     }
+    sB[w][rs] += row16_scatter(vb);
     {  // dg_t = sum_{r >= t} dG_r per channel: rows 16rt + 4g + e live in
        // lanes c16 + 16g; suffix within the lane, across the lane groups,
        // then across the row tiles
@@ -3018,18 +3021,18 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
           xk[rt][e] = static_cast<float>(k4[e]);
         }
       }
+      {
+        float v1[4 * NT], v3[4 * NT];
 #pragma unroll
-      for (int rt = 0; rt < NT; ++rt) {
+        for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float s1 = row16_sum(xq[rt][e] * dqv[rt][e]);
-          const float s3 = row16_sum(xk[rt][e] * dkv[rt][e]);
-          if (c16 == 0) {
-            const int r = 16 * rt + 4 * g + e;
-            sN[0][w][r] = s1;
-            sN[1][w][r] = s3;
+          for (int e = 0; e < 4; ++e) {
+            v1[4 * rt + e] = xq[rt][e] * dqv[rt][e];
+            v3[4 * rt + e] = xk[rt][e] * dkv[rt][e];
           }
-        }
+        const int ks = c16 * NT / 4, rs = 16 * (ks >> 2) + 4 * g + (ks & 3);  // the row lane c16 of group g sums
+        sN[0][w][rs] = row16_scatter(v1);
+        sN[1][w][rs] = row16_scatter(v3);
       }
       __syncthreads();
       if (tid < 2 * C) {
