@@ -1197,6 +1197,23 @@ __device__ __forceinline__ void mma_rows(f32x4 (&acc)[NO], const _Float16* A, in
   }
 }
 
+// mma_rows with A = M^T (A[m][k] = M[k][m], M row-major; transposed reads).
+template <int NO, int K, int TRI = kFull, bool KP = false>
+__device__ __forceinline__ void mma_rows_ta(f32x4 (&acc)[NO], const _Float16* M, int ldm, const _Float16* Bm, int ldb,
+                                            int n0) {
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const f16x8 bfr = KP ? frag_tk(Bm, ldb, k0, n0) : frag_t(Bm, ldb, k0, n0);
+    f16x8 af[NO];
+#pragma unroll
+    for (int t = 0; t < NO; ++t)
+      if (!tri_skip<TRI>(t, k0 / 32)) af[t] = frag_t(M, ldm, k0, 16 * t);
+#pragma unroll
+    for (int t = 0; t < NO; ++t)
+      if (!tri_skip<TRI>(t, k0 / 32)) acc[t] = F16Op::mma(af[t], bfr, acc[t]);
+  }
+}
+
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 enum GradMode { kOnly = 0, kSplit = 1, kGroup = 2 };
@@ -1212,7 +1229,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   constexpr int LDQ = DK + 8;                    // pitch of the dq / dk output tiles
   constexpr int NQ = NT * NT;                    // C x C tiles
   constexpr int DPW = NQ >= NW ? NQ / NW : 1;    // C x C tiles per wave, all in one row tile
-  static_assert(5 * C * LDC <= XB, "C x C stage buffers alias the strip buffers");
+  static_assert(4 * C * LDC <= XB, "C x C stage buffers alias the strip buffers");
   static_assert(2 * C * DK <= DK * LDK, "raw v / dO tiles fit the state buffer");
   static_assert(2 * C * LDQ * 2 + 4 * NW * C * 4 <= XB * 2, "dq / dk tiles and norm partials fit the strip buffers");
   __shared__ __align__(16) char img[IM::CHK + IM::KEY];
@@ -1480,11 +1497,13 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     if (gi + 1 < ngi) load_vdo(hv + 1, tid, w);  // Hs is free until the next v-head's phase A
 
     // ---- C x C stage on the tiles (qr, qc0 + t)
+    // [C][LDC] fp16 tiles, each stored transposed by 8-byte rows of four
+    // (a lane's four rows 16qr + 4g + e of one column) and read transposed
+    // where the products want the untransposed matrix
     _Float16* dTT = xb;              // dTT[s'][s] = dT[s][s']
-    _Float16* M1s = dTT + C * LDC;
-    _Float16* dPm = M1s + C * LDC;   // dPm[r][s]
-    _Float16* dPmT = dPm + C * LDC;  // dPmT[s][r]
-    _Float16* dAs = dPmT + C * LDC;  // symmetric dAm + dAm^T
+    _Float16* M1T = dTT + C * LDC;   // M1T[s][r] = M1[r][s], M1 = T^T dT
+    _Float16* dPmT = M1T + C * LDC;  // dPmT[s][r] = dPm[r][s]
+    _Float16* dAmT = dPmT + C * LDC; // dAmT[s][r] = dAm[r][s] (strictly upper)
     float rgc[4] = {0.f, 0.f, 0.f, 0.f}, rbc[4] = {0.f, 0.f, 0.f, 0.f};
     if (qact) {
 #pragma unroll
@@ -1502,7 +1521,6 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
           rgc[e] += dpp;
           col += dpp;
           p4[e] = static_cast<_Float16>(dP[t][e] * m);
-          dPm[r * LDC + s2] = p4[e];
         }
         *reinterpret_cast<f16x4*>(dTT + s2 * LDC + 16 * qr + 4 * g) = t4;
         *reinterpret_cast<f16x4*>(dPmT + s2 * LDC + 16 * qr + 4 * g) = p4;
@@ -1518,21 +1536,22 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       mma_cols_t<DPW, C>(m1, Ts, LDC, 16 * qr, dTT, LDC, 16 * qc0);
 #pragma unroll
       for (int t = 0; t < DPW; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          M1s[(16 * qr + 4 * g + e) * LDC + 16 * (qc0 + t) + c16] = static_cast<_Float16>(m1[t][e]);
+        *reinterpret_cast<f16x4*>(M1T + (16 * (qc0 + t) + c16) * LDC + 16 * qr + 4 * g) =
+            f16x4{static_cast<_Float16>(m1[t][0]), static_cast<_Float16>(m1[t][1]), static_cast<_Float16>(m1[t][2]),
+                  static_cast<_Float16>(m1[t][3])};
     }
     __syncthreads();
     if (qact) {
       f32x4 da[DPW], kk[DPW];
 #pragma unroll
       for (int t = 0; t < DPW; ++t) da[t] = kk[t] = zero4();
-      mma_cols<DPW, C>(da, M1s, LDC, 16 * qr, Ts, LDC, 16 * qc0);
+      mma_cols_t<DPW, C>(da, M1T, LDC, 16 * qr, Ts, LDC, 16 * qc0);
       mma_cols<DPW, DK>(kk, Ks, LDK, 16 * qr, Ks, LDK, 16 * qc0);
 #pragma unroll
       for (int t = 0; t < DPW; ++t) {
         const int s2 = 16 * (qc0 + t) + c16;
         float col = 0.f;
+        f16x4 a4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * qr + 4 * g + e;
@@ -1543,13 +1562,9 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
           rbc[e] += dav * kk[t][e];
           rgc[e] += ag;
           col += ag;
-          if (s2 < r) {
-            dAs[r * LDC + s2] = static_cast<_Float16>(dam);
-            dAs[s2 * LDC + r] = static_cast<_Float16>(dam);
-          } else if (s2 == r) {
-            dAs[r * LDC + r] = static_cast<_Float16>(0.f);
-          }
+          a4[e] = static_cast<_Float16>(s2 < r ? dam : 0.f);
         }
+        *reinterpret_cast<f16x4*>(dAmT + s2 * LDC + 16 * qr + 4 * g) = a4;
         col = xsum<16, 64>(col);
         if (lane < 16) sGc[w][s2] += col;
       }
@@ -1572,9 +1587,10 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     f32x4 dq[NT], dk[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) dq[t] = dk[t] = zero4();
-    mma_rows<NT, C, kLower, true>(dq, dPm, LDC, Ks, LDK, 16 * w);
-    mma_rows<NT, C, kUpper, true>(dk, dPmT, LDC, Qs, LDK, 16 * w);
-    mma_rows<NT, C, kFull, true>(dk, dAs, LDC, Ks, LDK, 16 * w);
+    mma_rows_ta<NT, C, kLower, true>(dq, dPmT, LDC, Ks, LDK, 16 * w);   // dPm K
+    mma_rows<NT, C, kUpper, true>(dk, dPmT, LDC, Qs, LDK, 16 * w);      // dPm^T Q
+    mma_rows_ta<NT, C, kLower, true>(dk, dAmT, LDC, Ks, LDK, 16 * w);   // dAm K
+    mma_rows<NT, C, kUpper, true>(dk, dAmT, LDC, Ks, LDK, 16 * w);      // dAm^T K
     float gcx = 0.f;
     float vx[4 * NT];  // this lane's terms of dG_r (rows 16rt + 4g + e), summed over the wave's 16 keys below
 #pragma unroll
