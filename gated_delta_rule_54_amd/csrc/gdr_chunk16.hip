@@ -1533,7 +1533,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
         }
         *reinterpret_cast<f16x4*>(dTT + s2 * LDC + 16 * qr + 4 * g) = t4;
         *reinterpret_cast<f16x4*>(dPmT + s2 * LDC + 16 * qr + 4 * g) = p4;
-        col = xsum<16, 64>(col);
+        col = rows4_sum(col);
         if (lane < 16) sGc[w][s2] += col;
       }
     }
@@ -1574,7 +1574,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
           a4[e] = static_cast<_Float16>(s2 < r ? dam : 0.f);
         }
         *reinterpret_cast<f16x4*>(dAmT + s2 * LDC + 16 * qr + 4 * g) = a4;
-        col = xsum<16, 64>(col);
+        col = rows4_sum(col);
         if (lane < 16) sGc[w][s2] += col;
       }
       f32x4 rg, rb;
@@ -1635,8 +1635,8 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dkv[rt][e]), sk, off, 0, 0);
         }
     }
-    hh = xsum<1, 64>(hh);
-    gcx = xsum<1, 64>(gcx);
+    hh = rows4_sum(row16_sum(hh));
+    gcx = rows4_sum(row16_sum(gcx));
     if (lane == 0) {
       red[0][w] = hh;
       red[1][w] = gcx;

@@ -128,4 +128,21 @@ __device__ __forceinline__ float row16_scatter(const float (&v)[N]) {
   }
 }
 
+// Sum over the four 16-lane rows (lanes j, j ^ 16, j ^ 32, j ^ 48): every
+// lane ends with its row position's total.  gfx950's row swaps exchange
+// odd and even rows, then the two halves of the wave, on the VALU (no LDS
+// crossbar); the two lanes of a pair add the same two values.  The swaps'
+// results are copied out element by element before use (a bit cast taken
+// directly of the second element reads the first).
+__device__ __forceinline__ float rows4_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned a0 = a[0], a1 = a[1];
+  const float y = __uint_as_float(a0) + __uint_as_float(a1);
+  const unsigned v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  const unsigned b0 = b[0], b1 = b[1];
+  return __uint_as_float(b0) + __uint_as_float(b1);
+}
+
 }  // namespace gdr
