@@ -2576,6 +2576,14 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
             f16x4{static_cast<_Float16>(x[tr][0]), static_cast<_Float16>(x[tr][1]), static_cast<_Float16>(x[tr][2]),
                   static_cast<_Float16>(x[tr][3])};
     };
+    // the same from the strip's chained fragments (already fp16)
+    auto put_frags_t = [&](_Float16* X, const f16x8 (&f)[NT / 2]) {
+#pragma unroll
+      for (int kb = 0; kb < NT / 2; ++kb) {
+        *reinterpret_cast<f16x4*>(X + jw * LDR + 32 * kb + 4 * g) = f16x4{f[kb][0], f[kb][1], f[kb][2], f[kb][3]};
+        *reinterpret_cast<f16x4*>(X + jw * LDR + 32 * kb + 16 + 4 * g) = f16x4{f[kb][4], f[kb][5], f[kb][6], f[kb][7]};
+      }
+    };
     wait_all();
     __syncthreads();
 
@@ -2608,13 +2616,14 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
         dov[tr][e] = dd[e];
       }
     }
-    f16x8 bf[NT / 2];
-    chain_frags<NT>(bf, rhs);
-    mma_chain_rows<NT, NT, kLower>(u, Ts, LDC, bf);
-    chain_frags<NT>(bf, dov);
-    mma_chain_rows_t<NT, NT, kUpper>(du, Ps, LDC, bf);
-    chain_frags<NT>(bf, du);
-    mma_chain_rows_t<NT, NT, kUpper>(dr, Ts, LDC, bf);
+    // RHS, dO and dU as chained fragments, kept (fp16) for the strip tiles
+    f16x8 frhs[NT / 2], fdo[NT / 2], fdu[NT / 2];
+    chain_frags<NT>(frhs, rhs);
+    mma_chain_rows<NT, NT, kLower>(u, Ts, LDC, frhs);
+    chain_frags<NT>(fdo, dov);
+    mma_chain_rows_t<NT, NT, kUpper>(du, Ps, LDC, fdo);
+    chain_frags<NT>(fdu, du);
+    mma_chain_rows_t<NT, NT, kUpper>(dr, Ts, LDC, fdu);
     {  // dv = beta dRHS; rows past the sequence's end are dropped by the buffer extent
       const uint32_t rowo = static_cast<uint32_t>(a.Hv) * DK * sizeof(TO);
       const rsrc_t ovr = make_rsrc(static_cast<char*>(a.dv) + (sp.t0 + t0) * rowo, static_cast<uint32_t>(L) * rowo);
@@ -2639,7 +2648,7 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
       sB[w][rs] = row16_scatter(vb);
     }
     put_strip_t(X0, dr);
-    put_strip_t(X1b, dov);
+    put_frags_t(X1b, fdo);
     put_strip_t(X2b, u);
     __syncthreads();
 
@@ -2676,8 +2685,8 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
       }
     }
     __syncthreads();
-    put_strip_t(X0, du);
-    put_strip_t(X1b, rhs);
+    put_frags_t(X0, fdu);
+    put_frags_t(X1b, frhs);
     put_state(dhf);
     __syncthreads();
     // ---- phase 2: X3 = U dH^T, dT = dU RHS^T
