@@ -2712,7 +2712,7 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
         for (int t = 0; t < DPW; ++t) dT[t] = F16Op::mma(af, frag_t(X1b, LDR, 32 * ks, 16 * (qc0 + t)), dT[t]);
       }
     }
-    hd = xsum<16, 64>(hd);
+    hd = rows4_sum(hd);
     __syncthreads();
 
     // ---- Kg / Kl and the states are done: the plain key image goes to Hs,
@@ -2903,7 +2903,7 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) kl3 += static_cast<float>(k4[e]) * dkm[rt][e];
     }
-    kl3 = xsum<16, 64>(kl3);
+    kl3 = rows4_sum(kl3);
     // ---- column sums: dk- += sum_{r>=s} dP_rs W_rs q_r + sum_{r>s} dA_rs beta_r W_rs k_r
 #pragma unroll
     for (int R = 1; R < NT; ++R) {  // blocks below the diagonal, about the first row of row block R
@@ -3012,7 +3012,7 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
         const float after = (g < 3 ? v1 : 0.f) + (g < 2 ? v2 : 0.f) + (g < 1 ? v3 : 0.f);
 #pragma unroll
         for (int e = 0; e < 4; ++e) dG[rt][e] += after;
-        tot[rt] = xsum<16, 64>(s);
+        tot[rt] = rows4_sum(s);
       }
       float later = 0.f;
 #pragma unroll
