@@ -1297,6 +1297,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
   load_vdo(hv0, tid0, w0);
   load_cimg(hv0, tid0, w0);
   float dqv[NT][4], dkv[NT][4];  // this v-head's (kGroup: the group's) dq_hat / dk_hat, rows 16rt + 4g + e, column i2
+  f32x4 kk[DPW];  // K_hat K_hat^T on this wave's C x C tiles, the same for every v-head of the group
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
@@ -1551,11 +1552,15 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     }
     __syncthreads();
     if (qact) {
-      f32x4 da[DPW], kk[DPW];
+      f32x4 da[DPW];
 #pragma unroll
-      for (int t = 0; t < DPW; ++t) da[t] = kk[t] = zero4();
+      for (int t = 0; t < DPW; ++t) da[t] = zero4();
       mma_cols_t<DPW, C>(da, M1T, LDC, 16 * qr, Ts, LDC, 16 * qc0);
-      mma_cols<DPW, DK>(kk, Ks, LDK, 16 * qr, Ks, LDK, 16 * qc0);
+      if (gi == 0) {
+#pragma unroll
+        for (int t = 0; t < DPW; ++t) kk[t] = zero4();
+        mma_cols<DPW, DK>(kk, Ks, LDK, 16 * qr, Ks, LDK, 16 * qc0);
+      }
 #pragma unroll
       for (int t = 0; t < DPW; ++t) {
         const int s2 = 16 * (qc0 + t) + c16;
