@@ -1515,18 +1515,23 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     _Float16* dPmT = M1T + C * LDC;  // dPmT[s][r] = dPm[r][s]
     _Float16* dAmT = dPmT + C * LDC; // dAmT[s][r] = dAm[r][s] (strictly upper)
     float rgc[4] = {0.f, 0.f, 0.f, 0.f}, rbc[4] = {0.f, 0.f, 0.f, 0.f};
+    // this lane's rows 16qr + 4g + e: their log2 gates and betas
+    const f32x4 g2q = *reinterpret_cast<const f32x4*>(G2 + 16 * qr + 4 * g);
+    const f32x4 btq = *reinterpret_cast<const f32x4*>(bet + 16 * qr + 4 * g);
     if (qact) {
 #pragma unroll
       for (int t = 0; t < DPW; ++t) {
         const int s2 = 16 * (qc0 + t) + c16;
+        const float g2s = G2[s2];
+        const f16x4 p4s = tr4(Ps, LDC, 16 * qr + 4 * g, 16 * (qc0 + t));  // P_rs, rows r of column s2
         f16x4 t4, p4;
         float col = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * qr + 4 * g + e;
           t4[e] = static_cast<_Float16>(dT[t][e]);
-          const float pv = static_cast<float>(Ps[r * LDC + s2]);  // P_rs
-          const float m = s2 <= r ? __builtin_amdgcn_exp2f(G2[r] - G2[s2]) : 0.f;
+          const float pv = static_cast<float>(p4s[e]);
+          const float m = s2 <= r ? __builtin_amdgcn_exp2f(g2q[e] - g2s) : 0.f;
           const float dpp = dP[t][e] * pv;
           rgc[e] += dpp;
           col += dpp;
@@ -1564,14 +1569,15 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
 #pragma unroll
       for (int t = 0; t < DPW; ++t) {
         const int s2 = 16 * (qc0 + t) + c16;
+        const float g2s = G2[s2];
         float col = 0.f;
         f16x4 a4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * qr + 4 * g + e;
-          const float ex = s2 < r ? __builtin_amdgcn_exp2f(G2[r] - G2[s2]) : 0.f;
+          const float ex = s2 < r ? __builtin_amdgcn_exp2f(g2q[e] - g2s) : 0.f;
           const float dav = -da[t][e] * ex;
-          const float dam = dav * bet[r];
+          const float dam = dav * btq[e];
           const float ag = dam * kk[t][e];
           rbc[e] += dav * kk[t][e];
           rgc[e] += ag;
