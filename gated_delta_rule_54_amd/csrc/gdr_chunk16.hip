@@ -645,11 +645,15 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
       kk = F16Op::mma(ka[ks], kb[ks], kk);
       qk = F16Op::mma(qa[ks], kb[ks], qk);
     }
+    const int s2 = 16 * tc + c16;
+    const float g2s = G2[s2];
+    const f32x4 g2r = *reinterpret_cast<const f32x4*>(G2 + 16 * tr + 4 * g);  // rows 16tr + 4g + e
+    const f32x4 btr = *reinterpret_cast<const f32x4*>(bet + 16 * tr + 4 * g);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 16 * tr + 4 * g + e, s2 = 16 * tc + c16;
-      const float ex = s2 <= r ? __builtin_amdgcn_exp2f(G2[r] - G2[s2]) : 0.f;
-      areg[it][e] = s2 < r ? bet[r] * ex * kk[e] : 0.f;
+      const int r = 16 * tr + 4 * g + e;
+      const float ex = s2 <= r ? __builtin_amdgcn_exp2f(g2r[e] - g2s) : 0.f;
+      areg[it][e] = s2 < r ? btr[e] * ex * kk[e] : 0.f;
       preg[it][e] = static_cast<_Float16>(ex * qk[e]);
     }
   }
@@ -693,11 +697,13 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
       const int j = i - d;
       f32x4 m = zero4();
       for (int k = j; k < i; ++k) {
+        // product q takes k = 16k + 4g + q: this lane's four A values are one
+        // 16-byte read
+        const f32x4 av = *reinterpret_cast<const f32x4*>(A + (16 * i + c16) * LDA + 16 * k + 4 * g);
 #pragma unroll
-        for (int k0 = 0; k0 < 16; k0 += 4) {
-          const float av = A[(16 * i + c16) * LDA + 16 * k + k0 + g];
-          const float bv = Tf[(16 * k + k0 + g) * LDA + 16 * j + c16];
-          m = F32Op::mma(av, bv, m);
+        for (int q = 0; q < 4; ++q) {
+          const float bv = Tf[(16 * k + 4 * g + q) * LDA + 16 * j + c16];
+          m = F32Op::mma(av[q], bv, m);
         }
       }
       // T_ij = -T_ii m; m's accumulators supply B(k = 4g + e, n) directly
