@@ -94,8 +94,8 @@ __device__ __forceinline__ float row16_sum(float x) {
 // half-row, its mirror in the quad, then its neighbour; the lane whose bit
 // (3, 2, 1, 0 of its row position) is set keeps the upper half of its
 // values, the other the lower, and each adds the half its partner gave up
-// (with N = 8 the neighbours, holding the same value, just add).  15 adds
-// and 30 selects for N = 16, against 64 adds for sixteen full row sums; the
+// (with N = 8 the neighbours, holding the same value, just add).  27 adds
+// and 6 selects for N = 16, against 64 adds for sixteen full row sums; the
 // order of additions is fixed.
 template <int H, int CTRL>
 __device__ __forceinline__ void row16_halve(const float* in, float* out, bool hi) {
@@ -107,18 +107,84 @@ __device__ __forceinline__ void row16_halve(const float* in, float* out, bool hi
                                                                        true));
   }
 }
+// The first two halving steps split the row by bit 3, then bit 2 of the
+// lane's row position: whole DPP banks of four lanes, so the bank mask picks
+// the lanes an add writes.  The lower banks add their own and their
+// partner's v[k], the upper banks v[k + H], into one register: two adds per
+// pair and no selects (the builtins take a bank mask only on a move, whose
+// add then needs the selects again).  The leading s_nop gives the wait
+// states a DPP read needs after a VALU write of its source, which the
+// compiler's hazard pass does not check inside inline asm.  Each add is
+// partner + own, the same sum as the selecting form.
+__device__ __forceinline__ void row16_halve8_mirror(const float* in, float* out) {
+  asm("s_nop 4\n"
+      "v_add_f32_dpp %0, %8, %8 row_mirror row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %0, %16, %16 row_mirror row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %1, %9, %9 row_mirror row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %1, %17, %17 row_mirror row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %2, %10, %10 row_mirror row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %2, %18, %18 row_mirror row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %3, %11, %11 row_mirror row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %3, %19, %19 row_mirror row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %4, %12, %12 row_mirror row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %4, %20, %20 row_mirror row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %5, %13, %13 row_mirror row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %5, %21, %21 row_mirror row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %6, %14, %14 row_mirror row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %6, %22, %22 row_mirror row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %7, %15, %15 row_mirror row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %7, %23, %23 row_mirror row_mask:0xf bank_mask:0xc\n"
+      : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4]), "=&v"(out[5]), "=&v"(out[6]), "=&v"(out[7])
+      : "v"(in[0]), "v"(in[1]), "v"(in[2]), "v"(in[3]), "v"(in[4]), "v"(in[5]), "v"(in[6]), "v"(in[7]), "v"(in[8]), "v"(in[9]), "v"(in[10]), "v"(in[11]), "v"(in[12]), "v"(in[13]), "v"(in[14]), "v"(in[15]));
+}
+__device__ __forceinline__ void row16_halve4_mirror(const float* in, float* out) {
+  asm("s_nop 4\n"
+      "v_add_f32_dpp %0, %4, %4 row_mirror row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %0, %8, %8 row_mirror row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %1, %5, %5 row_mirror row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %1, %9, %9 row_mirror row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %2, %6, %6 row_mirror row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %2, %10, %10 row_mirror row_mask:0xf bank_mask:0xc\n"
+      "v_add_f32_dpp %3, %7, %7 row_mirror row_mask:0xf bank_mask:0x3\n"
+      "v_add_f32_dpp %3, %11, %11 row_mirror row_mask:0xf bank_mask:0xc\n"
+      : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])
+      : "v"(in[0]), "v"(in[1]), "v"(in[2]), "v"(in[3]), "v"(in[4]), "v"(in[5]), "v"(in[6]), "v"(in[7]));
+}
+__device__ __forceinline__ void row16_halve4_half_mirror(const float* in, float* out) {
+  asm("s_nop 4\n"
+      "v_add_f32_dpp %0, %4, %4 row_half_mirror row_mask:0xf bank_mask:0x5\n"
+      "v_add_f32_dpp %0, %8, %8 row_half_mirror row_mask:0xf bank_mask:0xa\n"
+      "v_add_f32_dpp %1, %5, %5 row_half_mirror row_mask:0xf bank_mask:0x5\n"
+      "v_add_f32_dpp %1, %9, %9 row_half_mirror row_mask:0xf bank_mask:0xa\n"
+      "v_add_f32_dpp %2, %6, %6 row_half_mirror row_mask:0xf bank_mask:0x5\n"
+      "v_add_f32_dpp %2, %10, %10 row_half_mirror row_mask:0xf bank_mask:0xa\n"
+      "v_add_f32_dpp %3, %7, %7 row_half_mirror row_mask:0xf bank_mask:0x5\n"
+      "v_add_f32_dpp %3, %11, %11 row_half_mirror row_mask:0xf bank_mask:0xa\n"
+      : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])
+      : "v"(in[0]), "v"(in[1]), "v"(in[2]), "v"(in[3]), "v"(in[4]), "v"(in[5]), "v"(in[6]), "v"(in[7]));
+}
+__device__ __forceinline__ void row16_halve2_half_mirror(const float* in, float* out) {
+  asm("s_nop 4\n"
+      "v_add_f32_dpp %0, %2, %2 row_half_mirror row_mask:0xf bank_mask:0x5\n"
+      "v_add_f32_dpp %0, %4, %4 row_half_mirror row_mask:0xf bank_mask:0xa\n"
+      "v_add_f32_dpp %1, %3, %3 row_half_mirror row_mask:0xf bank_mask:0x5\n"
+      "v_add_f32_dpp %1, %5, %5 row_half_mirror row_mask:0xf bank_mask:0xa\n"
+      : "=&v"(out[0]), "=&v"(out[1])
+      : "v"(in[0]), "v"(in[1]), "v"(in[2]), "v"(in[3]));
+}
 template <int N>
 __device__ __forceinline__ float row16_scatter(const float (&v)[N]) {
   static_assert(N == 16 || N == 8, "16 or 8 values per lane");
   const int j = threadIdx.x & 15;
   float a[8], b[4], c[2];
   if constexpr (N == 16) {
-    row16_halve<8, 0x140>(v, a, (j & 8) != 0);  // row_mirror: lane 15 - j
-    row16_halve<4, 0x141>(a, b, (j & 4) != 0);  // row_half_mirror: lane 7 - j in its half
+    row16_halve8_mirror(v, a);       // row_mirror: lane 15 - j
+    row16_halve4_half_mirror(a, b);  // row_half_mirror: lane 7 - j in its half
+    row16_halve<2, 0x1b>(b, c, (j & 2) != 0);
   } else {
-    row16_halve<4, 0x140>(v, b, (j & 8) != 0);
+    row16_halve4_mirror(v, b);
+    row16_halve2_half_mirror(b, c);
   }
-  row16_halve<2, (N == 16 ? 0x1b : 0x141)>(b, c, (j & (N == 16 ? 2 : 4)) != 0);
   float d[1];
   row16_halve<1, (N == 16 ? 0xb1 : 0x1b)>(c, d, (j & (N == 16 ? 1 : 2)) != 0);
   if constexpr (N == 16) {
