@@ -1318,11 +1318,11 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     const int hv = hv0 + gi;
     f16x8 h0f[NTK / 2], dhf[NTK / 2];
     load_states(h0f, dhf, hv, w);
-    // fused gates: wave 0's lane r takes row r's pre-activation g and beta
-    // now, for the dg / dbeta it forms at the end of this v-head
+    // fused gates: wave 0's lane 63 - r takes row r's pre-activation g and
+    // beta now, for the dg / dbeta it forms at the end of this v-head
     float fgg = 0.f, fgb = 0.f;
-    if (a.fg && w == 0 && lane < L) {
-      const int64_t row = (sp.t0 + t0 + lane) * a.Hv + hv;
+    if (a.fg && w == 0 && 63 - lane < L) {
+      const int64_t row = (sp.t0 + t0 + 63 - lane) * a.Hv + hv;
       fgg = a.g[row];
       fgb = a.beta[row];
     }
@@ -1661,8 +1661,8 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     __syncthreads();
     // every wave is past its last read of the chunk image and of h0f / dhf
     if (gi + 1 < ngi) load_cimg(hv + 1, tid, w);
-    if (w == 0) {
-      const int r = lane;
+    if (w == 0) {  // lane 63 - r takes row r, so that a prefix sum in lane order sums rows >= r
+      const int r = 63 - lane;
       float dG = 0.f, dB = 0.f;
       if (r < C) {
 #pragma unroll
@@ -1681,12 +1681,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
         dG += gamC * hs + xs;
       }
       if (r >= L) dG = 0.f;
-      float x = dG;  // dg_t = sum_{r >= t} dG_r
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float yv = __shfl_down(x, off, 64);
-        if (lane + off < 64) x += yv;
-      }
+      const float x = wave_prefix_sum(dG);  // dg_t = sum_{r >= t} dG_r
       if (r < L) {
         const int64_t row = (sp.t0 + t0 + r) * a.Hv + hv;
         a.dg[row] = a.fg ? x * fg_dlog_alpha(fgg) : x;

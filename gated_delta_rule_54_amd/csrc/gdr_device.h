@@ -194,6 +194,21 @@ __device__ __forceinline__ float row16_scatter(const float (&v)[N]) {
   }
 }
 
+// Inclusive prefix sum over the wave's 64 lanes in lane order: shifts by 1,
+// 2, 4 and 8 lanes inside each 16-lane row (a lane whose source lies before
+// the row's start adds 0), then the totals of the rows below carried up by
+// the broadcasts of lanes 15 (to rows 1 and 3) and 31 (to rows 2 and 3).
+// Every step is a DPP add on the VALU; no LDS crossbar.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false));
+  return x;
+}
+
 // Sum over the four 16-lane rows (lanes j, j ^ 16, j ^ 32, j ^ 48): every
 // lane ends with its row position's total.  gfx950's row swaps exchange
 // odd and even rows, then the two halves of the wave, on the VALU (no LDS
