@@ -1524,6 +1524,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     // this lane's rows 16qr + 4g + e: their log2 gates and betas
     const f32x4 g2q = *reinterpret_cast<const f32x4*>(G2 + 16 * qr + 4 * g);
     const f32x4 btq = *reinterpret_cast<const f32x4*>(bet + 16 * qr + 4 * g);
+    float colp[DPW];  // this lane's share of column s2's sum of dP * P, finished in the dA stage
     if (qact) {
 #pragma unroll
       for (int t = 0; t < DPW; ++t) {
@@ -1545,8 +1546,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
         }
         *reinterpret_cast<f16x4*>(dTT + s2 * LDC + 16 * qr + 4 * g) = t4;
         *reinterpret_cast<f16x4*>(dPmT + s2 * LDC + 16 * qr + 4 * g) = p4;
-        col = rows4_sum(col);
-        if (lane < 16) sGc[w][s2] += col;
+        colp[t] = col;  // reduced over the rows with the dA stage's share
       }
     }
     __syncthreads();
@@ -1576,7 +1576,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
       for (int t = 0; t < DPW; ++t) {
         const int s2 = 16 * (qc0 + t) + c16;
         const float g2s = G2[s2];
-        float col = 0.f;
+        float col = colp[t];
         f16x4 a4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
