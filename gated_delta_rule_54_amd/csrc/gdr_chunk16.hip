@@ -3020,11 +3020,21 @@ __global__ __launch_bounds__(512) void cwgrad16_kernel(K16 a) {
           s += dG[rt][e];
           dG[rt][e] = s;
         }
-        float v1 = __shfl_down(s, 16, 64), v2 = __shfl_down(s, 32, 64), v3 = __shfl_down(s, 48, 64);
-        const float after = (g < 3 ? v1 : 0.f) + (g < 2 ? v2 : 0.f) + (g < 1 ? v3 : 0.f);
+        // the lane groups above g: the odd neighbour (row swap), then the
+        // upper pair of groups (half swap); each swap's two results hold the
+        // lane's own value and its partner's (the even row, or the lower
+        // half, finds its partner's in the second)
+        const unsigned su = __float_as_uint(s);
+        const auto pa = __builtin_amdgcn_permlane16_swap(su, su, false, false);
+        const unsigned pa0 = pa[0], pa1 = pa[1];
+        const float pair = __uint_as_float(pa0) + __uint_as_float(pa1);
+        const unsigned pu = __float_as_uint(pair);
+        const auto pb = __builtin_amdgcn_permlane32_swap(pu, pu, false, false);
+        const unsigned pb0 = pb[0], pb1 = pb[1];
+        const float after = ((g & 1) == 0 ? __uint_as_float(pa1) : 0.f) + (g < 2 ? __uint_as_float(pb1) : 0.f);
 #pragma unroll
         for (int e = 0; e < 4; ++e) dG[rt][e] += after;
-        tot[rt] = rows4_sum(s);
+        tot[rt] = __uint_as_float(pb0) + __uint_as_float(pb1);  // all four groups
       }
       float later = 0.f;
 #pragma unroll
