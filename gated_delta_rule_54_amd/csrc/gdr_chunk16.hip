@@ -1525,6 +1525,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
     const f32x4 g2q = *reinterpret_cast<const f32x4*>(G2 + 16 * qr + 4 * g);
     const f32x4 btq = *reinterpret_cast<const f32x4*>(bet + 16 * qr + 4 * g);
     float colp[DPW];  // this lane's share of column s2's sum of dP * P, finished in the dA stage
+    float mx[DPW][4];  // exp2(G2_r - G2_s) on and below the diagonal, kept for the dA stage
     if (qact) {
 #pragma unroll
       for (int t = 0; t < DPW; ++t) {
@@ -1539,6 +1540,7 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
           t4[e] = static_cast<_Float16>(dT[t][e]);
           const float pv = static_cast<float>(p4s[e]);
           const float m = s2 <= r ? __builtin_amdgcn_exp2f(g2q[e] - g2s) : 0.f;
+          mx[t][e] = m;
           const float dpp = dP[t][e] * pv;
           rgc[e] += dpp;
           col += dpp;
@@ -1575,13 +1577,12 @@ __global__ __launch_bounds__(512) void grad16_kernel(K16 a) {
 #pragma unroll
       for (int t = 0; t < DPW; ++t) {
         const int s2 = 16 * (qc0 + t) + c16;
-        const float g2s = G2[s2];
         float col = colp[t];
         f16x4 a4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * qr + 4 * g + e;
-          const float ex = s2 < r ? __builtin_amdgcn_exp2f(g2q[e] - g2s) : 0.f;
+          const float ex = s2 < r ? mx[t][e] : 0.f;
           const float dav = -da[t][e] * ex;
           const float dam = dav * btq[e];
           const float ag = dam * kk[t][e];
