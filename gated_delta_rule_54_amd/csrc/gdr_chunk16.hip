@@ -597,14 +597,9 @@ __global__ __launch_bounds__(512) void prep16_kernel(K16 a) {
     }
     norm_rows<C, NV, NTH>(Ks, kr, a.l2);
     norm_rows<C, NV, NTH>(Qs, qr, a.l2);
-    if (tid < 64) {  // running sum G over the chunk (g = 0 past the end)
-      float x = gv;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-      }
-      const float gc = __shfl(x, L - 1, 64);
+    if (tid < 64) {  // running sum G over the chunk (g = 0 past the end), then G at the last row
+      const float x = wave_prefix_sum(gv);
+      const float gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), L - 1));
       if (lane < C) {
         G2[lane] = x * kLog2e;
         gam[lane] = expf(x);
