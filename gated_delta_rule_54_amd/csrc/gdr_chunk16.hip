@@ -506,7 +506,11 @@ __device__ __forceinline__ void norm_rows(_Float16* dst, const uint4 (&raw)[NV],
 #pragma unroll
     for (int i = 0; i < 8; ++i) ss += x[u][i] * x[u][i];
   }
-  ss = xsum<1, TPR>(ss);
+  if constexpr (TPR == 8 || TPR == 16) {
+    ss = group_sum_dpp<TPR>(ss);
+  } else {
+    ss = xsum<1, TPR>(ss);
+  }
   const float rn = l2 ? rsqrtf(ss + kL2Eps) : 1.f;
 #pragma unroll
   for (int u = 0; u < NV; ++u) {

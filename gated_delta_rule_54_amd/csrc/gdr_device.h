@@ -76,6 +76,22 @@ __device__ __forceinline__ float xsum(float x) {
   return x;
 }
 
+// Sum over aligned groups of N (8 or 16) lanes by DPP adds on the VALU: the
+// neighbour, the other pair of the quad, then the mirror in the half-row
+// (and for N = 16 in the row); once a group's quads (halves) hold equal
+// values, the mirror reaches the other quad (half).  The additions and
+// their order are those of the xor butterfly xsum<1, N>.
+template <int N>
+__device__ __forceinline__ float group_sum_dpp(float x) {
+  static_assert(N == 8 || N == 16, "8 or 16 lanes");
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xb1, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4e, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xf, 0xf, true));
+  if constexpr (N == 16)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xf, 0xf, true));
+  return x;
+}
+
 // Sum over the 16 lanes of a DPP row (lanes 16k .. 16k+15): four row
 // rotations; every lane of the row ends with the same total.  A rotation
 // never reads outside the row, so bound_ctrl changes nothing but lets the
