@@ -424,12 +424,7 @@ __device__ __forceinline__ ChunkPos chunk_pos(const K16& a, int C) {
   if (!a.cu || a.B > kMaxRankedSeqs) return p;
   const int lane = lane_id(), nb = static_cast<int>(a.B);
   const int nch = lane < nb ? static_cast<int>((seq_span(a, lane).len + C - 1) / C) : 0;
-  int incl = nch;  // chunks of sequences 0 .. lane
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
+  const int incl = wave_prefix_sum(nch);  // chunks of sequences 0 .. lane
   const int excl = incl - nch;
   const int idx = static_cast<int>(blockIdx.x) + a.NC * static_cast<int>(blockIdx.z);
   const unsigned long long m = __ballot(lane < nb && excl <= idx && idx < incl);

@@ -225,6 +225,17 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
   return x;
 }
 
+// The same prefix sum over integers.
+__device__ __forceinline__ int wave_prefix_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+  return x;
+}
+
 // Sum over the four 16-lane rows (lanes j, j ^ 16, j ^ 32, j ^ 48): every
 // lane ends with its row position's total.  gfx950's row swaps exchange
 // odd and even rows, then the two halves of the wave, on the VALU (no LDS
